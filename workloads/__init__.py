@@ -1,0 +1,18 @@
+"""Seeded synthetic inputs and the layer lists of the measured workloads.
+
+This package holds no arithmetic of the convolution method: it draws random
+numbers, casts them to the storage type and describes layer shapes. Both the
+GPU path (tests, benchmark) and the CPU oracle consume the same bytes from it.
+"""
+from .inputs import (  # noqa: F401
+    ConvSpec,
+    PoolSpec,
+    conv1_single,
+    conv2_stem,
+    conv3_pointwise,
+    conv4_ifnet_block,
+    conv5_resnet18d,
+    conv_flops,
+    random_conv_case,
+    to_storage,
+)
