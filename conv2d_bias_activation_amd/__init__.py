@@ -1,0 +1,224 @@
+"""Fused conv2d (+bias, activation, residual) and pools for MI355X (gfx950).
+
+A thin ctypes binding over the C ABI of ``libconv2d_fused.so``
+(include/conv2d_fused.h). PyTorch supplies device memory and the current HIP
+stream; every step of the computation runs in the library's HIP kernels. The
+binding only checks tensor shapes, dtypes and devices, derives the sizes the C
+ABI takes, allocates outputs when none are given and raises on an error code.
+There is no fallback: if the library is not built, importing the ops raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["conv2d_fused", "maxpool3x3s2", "avgpool2x2", "out_dim", "check_args", "plan",
+           "last_error", "library_path", "Conv2dError", "ACT_NONE", "ACT_RELU", "ACT_SILU",
+           "ACT_PRELU", "RES_BEFORE_ACT", "LAYOUT_NHWC", "LAYOUT_NCHW", "DTYPE_F32",
+           "DTYPE_BF16", "DTYPE_F16"]
+
+# Codes of include/conv2d_fused.h
+LAYOUT_NHWC, LAYOUT_NCHW = 0, 1
+DTYPE_F32, DTYPE_BF16, DTYPE_F16 = 0, 1, 2
+ACT_NONE, ACT_RELU, ACT_SILU, ACT_PRELU = 0, 1, 2, 3
+RES_BEFORE_ACT = 0x100
+OK, EINVAL, EUNSUPPORTED, EHIP = 0, -1, -2, -3
+
+_ACTS = {"none": ACT_NONE, "relu": ACT_RELU, "silu": ACT_SILU, "prelu": ACT_PRELU}
+_LAYOUTS = {"nhwc": LAYOUT_NHWC, "nchw": LAYOUT_NCHW}
+_DTYPES = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16, torch.float16: DTYPE_F16}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libconv2d_fused.so")
+
+# Every exported symbol of the C ABI, with (restype, argtypes).
+_vp, _fp, _i, _cp = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_char_p
+SIGNATURES = {
+    "conv2d_fused": (_i, [_vp, _vp, _fp, _fp, _vp, _vp] + [_i] * 12 + [_vp]),
+    "maxpool3x3s2": (_i, [_vp, _vp] + [_i] * 6 + [_vp]),
+    "avgpool2x2": (_i, [_vp, _vp] + [_i] * 6 + [_vp]),
+    "conv2d_out_dim": (_i, [_i] * 4),
+    "conv2d_check_args": (_i, [_vp, _vp, _fp, _fp, _vp, _vp] + [_i] * 12),
+    "conv2d_plan": (_i, [_i] * 12 + [_cp, _i]),
+    "conv2d_last_error": (_cp, []),
+    "conv2d_abi_version": (_i, []),
+}
+
+_lib = None
+
+
+class Conv2dError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"conv2d library error {code}: {msg}")
+        self.code = code
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"{_LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
+            "(hipcc --offload-arch=gfx950)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def last_error() -> str:
+    return _load().conv2d_last_error().decode()
+
+
+def _check(rc):
+    if rc != OK:
+        raise Conv2dError(rc, last_error())
+
+
+def out_dim(n_in: int, k: int, stride: int, pad: int) -> int:
+    return _load().conv2d_out_dim(n_in, k, stride, pad)
+
+
+def _act_code(act, res_before_act):
+    code = _ACTS[act] if isinstance(act, str) else int(act)
+    return code | (RES_BEFORE_ACT if res_before_act else 0)
+
+
+def _stream_handle(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dims(x, w, layout):
+    if x.dim() != 4 or w.dim() != 4:
+        raise ValueError("x and w must be 4-D")
+    if layout == "nhwc":
+        N, H, W, Cin = x.shape
+        Cout, kh, kw, wc = w.shape
+    else:
+        N, Cin, H, W = x.shape
+        Cout, wc, kh, kw = w.shape
+    if wc != Cin:
+        raise ValueError(f"weight has {wc} input channels, x has {Cin}")
+    return N, H, W, Cin, Cout, kh, kw
+
+
+def _require(t, name, dtype, device):
+    if t is None:
+        return
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def conv2d_fused(x, w, bias=None, alpha=None, residual=None, *, stride=1, pad=0, act="none",
+                 res_before_act=False, layout="nhwc", out=None, stream=None):
+    """y = epilogue(conv(x, w)) on the GPU; see include/conv2d_fused.h.
+
+    x, w, residual, out: CUDA tensors of one storage dtype (float32, bfloat16 or
+    float16), contiguous, in ``layout`` ("nhwc" with OHWI weights or "nchw" with
+    OIHW weights). bias, alpha: float32 [Cout] or None. Returns y.
+    """
+    lib = _load()
+    lay = _LAYOUTS[layout]
+    dt = _DTYPES.get(x.dtype)
+    if dt is None:
+        raise ValueError(f"unsupported dtype {x.dtype}")
+    N, H, W, Cin, Cout, kh, kw = _dims(x, w, layout)
+    OH, OW = out_dim(H, kh, stride, pad), out_dim(W, kw, stride, pad)
+    if OH < 1 or OW < 1:
+        raise ValueError("the kernel does not fit the padded input")
+    yshape = (N, OH, OW, Cout) if layout == "nhwc" else (N, Cout, OH, OW)
+    dev = x.device
+    _require(x, "x", x.dtype, dev)
+    _require(w, "w", x.dtype, dev)
+    _require(residual, "residual", x.dtype, dev)
+    _require(bias, "bias", torch.float32, dev)
+    _require(alpha, "alpha", torch.float32, dev)
+    for t, name in ((bias, "bias"), (alpha, "alpha")):
+        if t is not None and tuple(t.shape) != (Cout,):
+            raise ValueError(f"{name} must have shape ({Cout},)")
+    if residual is not None and tuple(residual.shape) != yshape:
+        raise ValueError(f"residual must have shape {yshape}")
+    if out is None:
+        out = torch.empty(yshape, dtype=x.dtype, device=dev)
+    else:
+        _require(out, "out", x.dtype, dev)
+        if tuple(out.shape) != yshape:
+            raise ValueError(f"out must have shape {yshape}")
+    rc = lib.conv2d_fused(_ptr(x), _ptr(w), _ptr(bias), _ptr(alpha), _ptr(residual), _ptr(out),
+                          N, H, W, Cin, Cout, kh, kw, stride, pad,
+                          _act_code(act, res_before_act), lay, dt, _stream_handle(stream))
+    _check(rc)
+    return out
+
+
+def _pool(fn_name, x, layout, out, stream, oh_of):
+    lib = _load()
+    lay = _LAYOUTS[layout]
+    dt = _DTYPES.get(x.dtype)
+    if dt is None:
+        raise ValueError(f"unsupported dtype {x.dtype}")
+    if x.dim() != 4:
+        raise ValueError("x must be 4-D")
+    _require(x, "x", x.dtype, x.device)
+    if layout == "nhwc":
+        N, H, W, C = x.shape
+    else:
+        N, C, H, W = x.shape
+    OH, OW = oh_of(H), oh_of(W)
+    yshape = (N, OH, OW, C) if layout == "nhwc" else (N, C, OH, OW)
+    if out is None:
+        if OH < 1 or OW < 1:
+            raise ValueError("input too small")
+        out = torch.empty(yshape, dtype=x.dtype, device=x.device)
+    else:
+        _require(out, "out", x.dtype, x.device)
+        if tuple(out.shape) != yshape:
+            raise ValueError(f"out must have shape {yshape}")
+    rc = getattr(lib, fn_name)(_ptr(x), _ptr(out), N, H, W, C, lay, dt, _stream_handle(stream))
+    _check(rc)
+    return out
+
+
+def maxpool3x3s2(x, *, layout="nhwc", out=None, stream=None):
+    """3x3 stride-2 pad-1 max pool on the GPU (bit-exact)."""
+    return _pool("maxpool3x3s2", x, layout, out, stream, lambda n: (n - 1) // 2 + 1)
+
+
+def avgpool2x2(x, *, layout="nhwc", out=None, stream=None):
+    """2x2 stride-2 average pool on the GPU (bit-exact, fixed summation order)."""
+    return _pool("avgpool2x2", x, layout, out, stream, lambda n: n // 2)
+
+
+def check_args(x_ptr, w_ptr, bias_ptr, alpha_ptr, res_ptr, y_ptr, N, H, W, Cin, Cout, kh, kw,
+               stride, pad, act, layout, dtype):
+    """Host-only validation (no GPU needed); returns the C status code."""
+    return _load().conv2d_check_args(x_ptr, w_ptr, bias_ptr, alpha_ptr, res_ptr, y_ptr, N, H, W,
+                                     Cin, Cout, kh, kw, stride, pad, act, layout, dtype)
+
+
+def plan(N, H, W, Cin, Cout, kh, kw, stride, pad, act, layout, dtype) -> str:
+    """Name of the kernel variant conv2d_fused picks for a shape (host only)."""
+    buf = ctypes.create_string_buffer(256)
+    n = _load().conv2d_plan(N, H, W, Cin, Cout, kh, kw, stride, pad, act, layout, dtype, buf, 256)
+    _check(n if n < 0 else OK)
+    return buf.value.decode()

@@ -1,0 +1,309 @@
+// C ABI of the library: argument validation, kernel-variant choice and launch.
+// Declarations and the contract of every entry point: include/conv2d_fused.h.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace {
+
+using namespace c2d;
+
+thread_local std::string g_err;
+
+int set_error(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int set_ok() {
+    g_err.clear();
+    return CONV2D_OK;
+}
+
+int dtype_bytes(int dtype) {
+    switch (dtype) {
+    case CONV2D_DTYPE_F32:
+        return 4;
+    case CONV2D_DTYPE_BF16:
+    case CONV2D_DTYPE_F16:
+        return 2;
+    default:
+        return 0;
+    }
+}
+
+const char *dtype_name(int dtype) {
+    switch (dtype) {
+    case CONV2D_DTYPE_F32:
+        return "f32";
+    case CONV2D_DTYPE_BF16:
+        return "bf16";
+    case CONV2D_DTYPE_F16:
+        return "f16";
+    default:
+        return "?";
+    }
+}
+
+int out_dim(int in, int k, int s, int p) {
+    if (in <= 0 || k <= 0 || s <= 0 || p < 0) return -1;
+    long long span = (long long)in + 2ll * p - k;
+    if (span < 0) return -1;
+    long long o = span / s + 1;
+    return o > 0x7fffffff ? -1 : (int)o;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool overlap(const void *a, long long abytes, const void *b, long long bbytes) {
+    if (!a || !b) return false;
+    uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
+}
+
+constexpr long long kMaxElems = 0x7fffffffll;
+
+// Validates conv2d_fused's arguments; fills the derived geometry into `a`.
+int check_conv(const void *x, const void *w, const float *alpha, const void *residual,
+               const void *y, int N, int H, int W, int Cin, int Cout, int kh, int kw,
+               int stride, int pad, int act, int layout, int dtype, ConvArgs *a) {
+    if (!x || !w || !y) return set_error(CONV2D_EINVAL, "x, w and y must not be null");
+    if (N <= 0 || H <= 0 || W <= 0 || Cin <= 0 || Cout <= 0 || kh <= 0 || kw <= 0)
+        return set_error(CONV2D_EINVAL, "sizes must be positive (N=%d H=%d W=%d Cin=%d Cout=%d kh=%d kw=%d)",
+                         N, H, W, Cin, Cout, kh, kw);
+    if (stride != 1 && stride != 2) return set_error(CONV2D_EINVAL, "stride must be 1 or 2 (got %d)", stride);
+    if (pad < 0) return set_error(CONV2D_EINVAL, "pad must be >= 0 (got %d)", pad);
+    if (layout != CONV2D_LAYOUT_NHWC && layout != CONV2D_LAYOUT_NCHW)
+        return set_error(CONV2D_EINVAL, "unknown layout %d", layout);
+    if (!dtype_bytes(dtype)) return set_error(CONV2D_EINVAL, "unknown dtype %d", dtype);
+    int code = act & 0xff;
+    if (code > CONV2D_ACT_PRELU || (act & ~(0xff | CONV2D_RES_BEFORE_ACT)))
+        return set_error(CONV2D_EINVAL, "unknown activation flags 0x%x", act);
+    if (code == CONV2D_ACT_PRELU && !alpha) return set_error(CONV2D_EINVAL, "PRELU needs alpha");
+    int OH = out_dim(H, kh, stride, pad), OW = out_dim(W, kw, stride, pad);
+    if (OH < 1 || OW < 1)
+        return set_error(CONV2D_EINVAL, "kernel %dx%d does not fit the padded %dx%d input", kh, kw, H, W);
+    long long xe = (long long)N * H * W * Cin;
+    long long we = (long long)Cout * kh * kw * Cin;
+    long long ye = (long long)N * OH * OW * Cout;
+    long long m = (long long)N * OH * OW;
+    if (xe > kMaxElems || we > kMaxElems || ye > kMaxElems || m > kMaxElems)
+        return set_error(CONV2D_EUNSUPPORTED, "tensors of 2^31 or more elements are not supported");
+    int eb = dtype_bytes(dtype);
+    if (overlap(y, ye * eb, x, xe * eb)) return set_error(CONV2D_EINVAL, "y overlaps x");
+    if (overlap(y, ye * eb, residual, ye * eb)) return set_error(CONV2D_EINVAL, "y overlaps the residual");
+    a->x = x;
+    a->w = w;
+    a->alpha = alpha;
+    a->res = residual;
+    a->y = const_cast<void *>(y);
+    a->N = N;
+    a->H = H;
+    a->W = W;
+    a->Cin = Cin;
+    a->Cout = Cout;
+    a->kh = kh;
+    a->kw = kw;
+    a->stride = stride;
+    a->pad = pad;
+    a->OH = OH;
+    a->OW = OW;
+    a->M = (int)m;
+    a->K = (int)we / Cout;
+    a->act = code;
+    a->res_before_act = (act & CONV2D_RES_BEFORE_ACT) ? 1 : 0;
+    a->vec_out = aligned16(y) && (!residual || aligned16(residual));
+    return CONV2D_OK;
+}
+
+enum Family { FAM_DIRECT = 0, FAM_IGEMM = 1 };
+
+struct Plan {
+    int family;
+    IgemmPlan ig;
+};
+
+const char *tile_name(int t) {
+    switch (t) {
+    case IGEMM_TILE_128x128:
+        return "128x128";
+    case IGEMM_TILE_128x64:
+        return "128x64";
+    case IGEMM_TILE_64x64:
+        return "64x64";
+    case IGEMM_TILE_256x32:
+        return "256x32";
+    default:
+        return "?";
+    }
+}
+
+// Tile choice: the fewest "rounds" of 256 workgroups (one per CU), weighted by how
+// efficiently each tile shape feeds the matrix cores.
+int choose_tile(const ConvArgs &a) {
+    struct Cand {
+        int tile, bm, bn;
+        double eff;
+    } cands[] = {{IGEMM_TILE_128x128, 128, 128, 1.0},
+                 {IGEMM_TILE_128x64, 128, 64, 0.8},
+                 {IGEMM_TILE_256x32, 256, 32, 0.7},
+                 {IGEMM_TILE_64x64, 64, 64, 0.6}};
+    int best = IGEMM_TILE_128x128;
+    double best_cost = 1e300;
+    for (const Cand &c : cands) {
+        long long tm = (a.M + c.bm - 1) / c.bm, tn = (a.Cout + c.bn - 1) / c.bn;
+        long long tiles = tm * tn;
+        long long rounds = (tiles + 255) / 256;
+        double cost = (double)rounds * c.bm * c.bn / c.eff;
+        if (cost < best_cost) {
+            best_cost = cost;
+            best = c.tile;
+        }
+    }
+    return best;
+}
+
+Plan make_plan(const ConvArgs &a, int layout, int dtype) {
+    Plan p{};
+    const int ve = 16 / dtype_bytes(dtype);
+    if (a.Cin <= 4) {
+        p.family = FAM_DIRECT;
+        return p;
+    }
+    p.family = FAM_IGEMM;
+    p.ig.nchw = layout == CONV2D_LAYOUT_NCHW;
+    p.ig.avec = !p.ig.nchw && (a.Cin % ve) == 0 && aligned16(a.x) && aligned16(a.w);
+    p.ig.bvec = (a.K % ve) == 0 && aligned16(a.w);
+    p.ig.tile = choose_tile(a);
+    return p;
+}
+
+int describe(const Plan &p, int layout, int dtype, char *buf, int cap) {
+    char tmp[160];
+    if (p.family == FAM_DIRECT) {
+        snprintf(tmp, sizeof tmp, "direct_%s %s cob32", layout == CONV2D_LAYOUT_NCHW ? "nchw" : "nhwc",
+                 dtype_name(dtype));
+    } else {
+        snprintf(tmp, sizeof tmp, "igemm_%s%s %s %s splitk=1", p.ig.nchw ? "nchw" : "nhwc",
+                 p.ig.avec ? "_vec" : "_gather", dtype_name(dtype), tile_name(p.ig.tile));
+    }
+    int n = (int)strlen(tmp);
+    if (buf && cap > 0) {
+        strncpy(buf, tmp, (size_t)cap - 1);
+        buf[cap - 1] = 0;
+    }
+    return n;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+    return set_error(CONV2D_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int check_pool(const void *x, const void *y, int N, int H, int W, int C, int layout, int dtype,
+               int OH, int OW, const char *name) {
+    if (!x || !y) return set_error(CONV2D_EINVAL, "%s: x and y must not be null", name);
+    if (N <= 0 || H <= 0 || W <= 0 || C <= 0)
+        return set_error(CONV2D_EINVAL, "%s: sizes must be positive", name);
+    if (layout != CONV2D_LAYOUT_NHWC && layout != CONV2D_LAYOUT_NCHW)
+        return set_error(CONV2D_EINVAL, "%s: unknown layout %d", name, layout);
+    if (!dtype_bytes(dtype)) return set_error(CONV2D_EINVAL, "%s: unknown dtype %d", name, dtype);
+    if (OH < 1 || OW < 1) return set_error(CONV2D_EINVAL, "%s: input too small", name);
+    long long xe = (long long)N * H * W * C, ye = (long long)N * OH * OW * C;
+    if (xe > kMaxElems) return set_error(CONV2D_EUNSUPPORTED, "%s: tensor too large", name);
+    int eb = dtype_bytes(dtype);
+    if (overlap(y, ye * eb, x, xe * eb)) return set_error(CONV2D_EINVAL, "%s: y overlaps x", name);
+    return CONV2D_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int conv2d_abi_version(void) { return 1; }
+
+const char *conv2d_last_error(void) { return g_err.c_str(); }
+
+int conv2d_out_dim(int in, int k, int stride, int pad) { return out_dim(in, k, stride, pad); }
+
+int conv2d_check_args(const void *x, const void *w, const float *bias, const float *alpha,
+                      const void *residual, const void *y, int N, int H, int W, int Cin,
+                      int Cout, int kh, int kw, int stride, int pad, int act, int layout,
+                      int dtype) {
+    (void)bias;
+    ConvArgs a{};
+    int rc = check_conv(x, w, alpha, residual, y, N, H, W, Cin, Cout, kh, kw, stride, pad, act,
+                        layout, dtype, &a);
+    return rc ? rc : set_ok();
+}
+
+int conv2d_plan(int N, int H, int W, int Cin, int Cout, int kh, int kw, int stride, int pad,
+                int act, int layout, int dtype, char *buf, int cap) {
+    // Stand-in addresses (never dereferenced): aligned, non-overlapping.
+    const void *px = (const void *)(uintptr_t)0x100000000ull;
+    const void *pw = (const void *)(uintptr_t)0x900000000ull;
+    const void *py = (const void *)(uintptr_t)0x1100000000ull;
+    const float *pa = (const float *)(uintptr_t)0x1900000000ull;
+    ConvArgs a{};
+    int rc = check_conv(px, pw, pa, nullptr, py, N, H, W, Cin, Cout, kh, kw, stride, pad, act,
+                        layout, dtype, &a);
+    if (rc) return rc;
+    set_ok();
+    return describe(make_plan(a, layout, dtype), layout, dtype, buf, cap);
+}
+
+int conv2d_fused(const void *x, const void *w, const float *bias, const float *alpha,
+                 const void *residual, void *y, int N, int H, int W, int Cin, int Cout, int kh,
+                 int kw, int stride, int pad, int act, int layout, int dtype, void *stream) {
+    ConvArgs a{};
+    int rc = check_conv(x, w, alpha, residual, y, N, H, W, Cin, Cout, kh, kw, stride, pad, act,
+                        layout, dtype, &a);
+    if (rc) return rc;
+    a.bias = bias;
+    if ((act & 0xff) != CONV2D_ACT_PRELU) a.alpha = nullptr;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    Plan p = make_plan(a, layout, dtype);
+    hipError_t e;
+    if (p.family == FAM_DIRECT)
+        e = launch_direct(a, dtype, layout == CONV2D_LAYOUT_NCHW, st);
+    else
+        e = launch_igemm(a, dtype, p.ig, st);
+    if (e != hipSuccess) return hip_fail(e, "conv2d_fused launch");
+    return set_ok();
+}
+
+int maxpool3x3s2(const void *x, void *y, int N, int H, int W, int C, int layout, int dtype,
+                 void *stream) {
+    int OH = out_dim(H, 3, 2, 1), OW = out_dim(W, 3, 2, 1);
+    int rc = check_pool(x, y, N, H, W, C, layout, dtype, OH, OW, "maxpool3x3s2");
+    if (rc) return rc;
+    int ve = 16 / dtype_bytes(dtype);
+    bool vec = layout == CONV2D_LAYOUT_NHWC && (C % ve) == 0 && aligned16(x) && aligned16(y);
+    hipError_t e = launch_maxpool(x, y, N, H, W, C, layout == CONV2D_LAYOUT_NCHW, dtype, vec,
+                                  static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "maxpool3x3s2 launch");
+    return set_ok();
+}
+
+int avgpool2x2(const void *x, void *y, int N, int H, int W, int C, int layout, int dtype,
+               void *stream) {
+    int rc = check_pool(x, y, N, H, W, C, layout, dtype, H / 2, W / 2, "avgpool2x2");
+    if (rc) return rc;
+    int ve = 16 / dtype_bytes(dtype);
+    bool vec = layout == CONV2D_LAYOUT_NHWC && (C % ve) == 0 && aligned16(x) && aligned16(y);
+    hipError_t e = launch_avgpool(x, y, N, H, W, C, layout == CONV2D_LAYOUT_NCHW, dtype, vec,
+                                  static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "avgpool2x2 launch");
+    return set_ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,79 @@
+// Shared device helpers of the fused conv2d library (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/conv2d_fused.h"
+
+namespace c2d {
+
+typedef __bf16 bf16;
+typedef _Float16 f16;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Everything a conv kernel needs, passed by value.
+struct ConvArgs {
+    const void *x;
+    const void *w;
+    const float *bias;   // may be null
+    const float *alpha;  // may be null unless PReLU
+    const void *res;     // may be null
+    void *y;
+    int N, H, W, Cin, Cout, kh, kw, stride, pad, OH, OW;
+    int M;    // N*OH*OW output pixels (GEMM rows)
+    int K;    // Cin*kh*kw (GEMM depth)
+    int act;  // CONV2D_ACT_* (low byte only)
+    int res_before_act;
+    int vec_out;  // y and residual are 16-byte aligned
+};
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16 v) { return (float)v; }
+__device__ __forceinline__ float to_f32(f16 v) { return (float)v; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+// Casts to the 16-bit types round to nearest-even (gfx950 v_cvt_pk_bf16_f32 and
+// v_cvt_f16_f32 under the default rounding mode).
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return (bf16)v; }
+template <> __device__ __forceinline__ f16 from_f32<f16>(float v) { return (f16)v; }
+
+// Activation of the epilogue: ReLU, SiLU v/(1+exp(-v)) or per-channel PReLU.
+__device__ __forceinline__ float activate(int act, float v, float alpha) {
+    switch (act) {
+    case CONV2D_ACT_RELU:
+        return v > 0.0f ? v : 0.0f;
+    case CONV2D_ACT_SILU:
+        // exp(-v) overflows to +inf for v < -88, giving v * 0 = -0: the exact value
+        // there is below 1e-36 in magnitude.
+        return v * __builtin_amdgcn_rcpf(1.0f + __expf(-v));
+    case CONV2D_ACT_PRELU:
+        return v >= 0.0f ? v : alpha * v;
+    default:
+        return v;
+    }
+}
+
+// bias, residual (before or after the activation) and activation of one output.
+__device__ __forceinline__ float epilogue(float acc, float bias, float alpha, float r,
+                                          bool has_res, int act, bool res_before) {
+    float v = acc + bias;
+    if (has_res && res_before) v += r;
+    v = activate(act, v, alpha);
+    if (has_res && !res_before) v += r;
+    return v;
+}
+
+// Maps a hardware workgroup id to a logical tile id so that each of the 8 XCDs
+// (which take workgroups round-robin and each own an L2) runs one contiguous run
+// of logical tiles, which then share input rows and weights in that L2.
+__device__ __forceinline__ int xcd_remap(int g, int total) {
+    const int nx = 8;
+    int q = total / nx, r = total % nx;
+    int x = g % nx, i = g / nx;
+    return x * q + (x < r ? x : r) + i;
+}
+
+}  // namespace c2d

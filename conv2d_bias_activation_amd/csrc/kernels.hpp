@@ -1,0 +1,36 @@
+// Host-side launchers of the library's kernels (one per kernel family).
+#pragma once
+
+#include "common.hpp"
+
+namespace c2d {
+
+enum IgemmTile {
+    IGEMM_TILE_128x128 = 0,
+    IGEMM_TILE_128x64 = 1,
+    IGEMM_TILE_64x64 = 2,
+    IGEMM_TILE_256x32 = 3,
+};
+
+struct IgemmPlan {
+    int tile;   // IgemmTile
+    bool nchw;  // channel-first layout
+    bool avec;  // channel-last, Cin a multiple of the 16-byte vector, x and w aligned
+    bool bvec;  // K a multiple of the 16-byte vector, w aligned
+};
+
+// MFMA implicit GEMM, any k/stride/pad, both layouts, f32/bf16/f16 storage.
+hipError_t launch_igemm(const ConvArgs &a, int dtype, const IgemmPlan &p, hipStream_t st);
+
+// Direct convolution on the vector ALUs for few input channels (the image stem):
+// one thread per output pixel and a block of output channels.
+hipError_t launch_direct(const ConvArgs &a, int dtype, bool nchw, hipStream_t st);
+
+// Pools (layout: CONV2D_LAYOUT_*). vec: C a multiple of the 16-byte vector and
+// both pointers aligned (channel-last only).
+hipError_t launch_maxpool(const void *x, void *y, int N, int H, int W, int C, bool nchw,
+                          int dtype, bool vec, hipStream_t st);
+hipError_t launch_avgpool(const void *x, void *y, int N, int H, int W, int C, bool nchw,
+                          int dtype, bool vec, hipStream_t st);
+
+}  // namespace c2d

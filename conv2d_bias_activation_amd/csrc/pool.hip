@@ -1,0 +1,259 @@
+// 3x3/s2/p1 max pool and 2x2/s2 average pool (inferencelayer page, `MAXPOOL_SRC`
+// and `AVGPOOL_SRC`). Both only move data: each output reads its window once and is
+// written once, so the kernels are laid out for coalesced 16-byte accesses along
+// channels (channel-last) or along the row (channel-first).
+//
+// Max: the largest in-range tap, compared in fp32 after an exact widening, so the
+// stored value is bit-identical to an input (the first largest in row-major tap
+// order; an all-NaN window gives -inf). Average: ((x00 + x01) + x10) + x11 in fp32,
+// in that order, then times 0.25 and one rounding to the storage type.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace c2d {
+
+template <typename T> struct Vec16 {
+    static constexpr int n = 16 / (int)sizeof(T);
+    T v[16 / sizeof(T)];
+};
+
+template <typename T> __device__ __forceinline__ Vec16<T> load16(const T *p) {
+    Vec16<T> r;
+    u32x4 t = *reinterpret_cast<const u32x4 *>(p);
+    __builtin_memcpy(r.v, &t, 16);
+    return r;
+}
+template <typename T> __device__ __forceinline__ void store16(T *p, const Vec16<T> &r) {
+    u32x4 t;
+    __builtin_memcpy(&t, r.v, 16);
+    *reinterpret_cast<u32x4 *>(p) = t;
+}
+
+// channel-last, one thread per (output pixel, 16-byte channel vector)
+template <typename T>
+__global__ __launch_bounds__(256) void maxpool_nhwc_vec(const T *__restrict__ x, T *__restrict__ y,
+                                                        int N, int H, int W, int C, int OH, int OW) {
+    constexpr int VE = Vec16<T>::n;
+    const int CV = C / VE;
+    const long long total = (long long)N * OH * OW * CV;
+    for (long long it = blockIdx.x * 256ll + threadIdx.x; it < total; it += (long long)gridDim.x * 256) {
+        int cv = (int)(it % CV);
+        long long p = it / CV;
+        int ow = (int)(p % OW);
+        long long q = p / OW;
+        int oh = (int)(q % OH);
+        int n = (int)(q / OH);
+        float best[VE];
+        Vec16<T> out;
+#pragma unroll
+        for (int e = 0; e < VE; ++e) {
+            best[e] = -__builtin_inff();
+            out.v[e] = from_f32<T>(-__builtin_inff());
+        }
+        for (int dy = 0; dy < 3; ++dy) {
+            int iy = 2 * oh + dy - 1;
+            if ((unsigned)iy >= (unsigned)H) continue;
+            for (int dx = 0; dx < 3; ++dx) {
+                int ix = 2 * ow + dx - 1;
+                if ((unsigned)ix >= (unsigned)W) continue;
+                Vec16<T> v = load16(x + (((size_t)n * H + iy) * W + ix) * C + cv * VE);
+#pragma unroll
+                for (int e = 0; e < VE; ++e) {
+                    float f = to_f32(v.v[e]);
+                    if (f > best[e]) {
+                        best[e] = f;
+                        out.v[e] = v.v[e];
+                    }
+                }
+            }
+        }
+        store16(y + (((size_t)n * OH + oh) * OW + ow) * C + cv * VE, out);
+    }
+}
+
+// any layout, one thread per output element (channel-first: consecutive threads
+// walk along the output row)
+template <typename T, bool NCHW>
+__global__ __launch_bounds__(256) void maxpool_scalar(const T *__restrict__ x, T *__restrict__ y,
+                                                      int N, int H, int W, int C, int OH, int OW) {
+    const long long total = (long long)N * OH * OW * C;
+    for (long long it = blockIdx.x * 256ll + threadIdx.x; it < total; it += (long long)gridDim.x * 256) {
+        int n, c, oh, ow;
+        if (NCHW) {
+            ow = (int)(it % OW);
+            long long q = it / OW;
+            oh = (int)(q % OH);
+            q /= OH;
+            c = (int)(q % C);
+            n = (int)(q / C);
+        } else {
+            c = (int)(it % C);
+            long long q = it / C;
+            ow = (int)(q % OW);
+            q /= OW;
+            oh = (int)(q % OH);
+            n = (int)(q / OH);
+        }
+        float best = -__builtin_inff();
+        T out = from_f32<T>(-__builtin_inff());
+        for (int dy = 0; dy < 3; ++dy) {
+            int iy = 2 * oh + dy - 1;
+            if ((unsigned)iy >= (unsigned)H) continue;
+            for (int dx = 0; dx < 3; ++dx) {
+                int ix = 2 * ow + dx - 1;
+                if ((unsigned)ix >= (unsigned)W) continue;
+                size_t off = NCHW ? (((size_t)n * C + c) * H + iy) * W + ix
+                                  : (((size_t)n * H + iy) * W + ix) * C + c;
+                T v = x[off];
+                float f = to_f32(v);
+                if (f > best) {
+                    best = f;
+                    out = v;
+                }
+            }
+        }
+        y[it] = out;
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void avgpool_nhwc_vec(const T *__restrict__ x, T *__restrict__ y,
+                                                        int N, int H, int W, int C, int OH, int OW) {
+    constexpr int VE = Vec16<T>::n;
+    const int CV = C / VE;
+    const long long total = (long long)N * OH * OW * CV;
+    for (long long it = blockIdx.x * 256ll + threadIdx.x; it < total; it += (long long)gridDim.x * 256) {
+        int cv = (int)(it % CV);
+        long long p = it / CV;
+        int ow = (int)(p % OW);
+        long long q = p / OW;
+        int oh = (int)(q % OH);
+        int n = (int)(q / OH);
+        const T *b = x + (((size_t)n * H + 2 * oh) * W + 2 * ow) * C + cv * VE;
+        Vec16<T> v00 = load16(b), v01 = load16(b + C);
+        Vec16<T> v10 = load16(b + (size_t)W * C), v11 = load16(b + (size_t)W * C + C);
+        Vec16<T> out;
+#pragma unroll
+        for (int e = 0; e < VE; ++e) {
+            float s = to_f32(v00.v[e]) + to_f32(v01.v[e]);
+            s = s + to_f32(v10.v[e]);
+            s = s + to_f32(v11.v[e]);
+            out.v[e] = from_f32<T>(s * 0.25f);
+        }
+        store16(y + (((size_t)n * OH + oh) * OW + ow) * C + cv * VE, out);
+    }
+}
+
+template <typename T, bool NCHW>
+__global__ __launch_bounds__(256) void avgpool_scalar(const T *__restrict__ x, T *__restrict__ y,
+                                                      int N, int H, int W, int C, int OH, int OW) {
+    const long long total = (long long)N * OH * OW * C;
+    for (long long it = blockIdx.x * 256ll + threadIdx.x; it < total; it += (long long)gridDim.x * 256) {
+        int n, c, oh, ow;
+        if (NCHW) {
+            ow = (int)(it % OW);
+            long long q = it / OW;
+            oh = (int)(q % OH);
+            q /= OH;
+            c = (int)(q % C);
+            n = (int)(q / C);
+        } else {
+            c = (int)(it % C);
+            long long q = it / C;
+            ow = (int)(q % OW);
+            q /= OW;
+            oh = (int)(q % OH);
+            n = (int)(q / OH);
+        }
+        size_t b, dx, dy;
+        if (NCHW) {
+            b = (((size_t)n * C + c) * H + 2 * oh) * W + 2 * ow;
+            dx = 1;
+            dy = W;
+        } else {
+            b = (((size_t)n * H + 2 * oh) * W + 2 * ow) * C + c;
+            dx = C;
+            dy = (size_t)W * C;
+        }
+        float s = to_f32(x[b]) + to_f32(x[b + dx]);
+        s = s + to_f32(x[b + dy]);
+        s = s + to_f32(x[b + dy + dx]);
+        y[it] = from_f32<T>(s * 0.25f);
+    }
+}
+
+static unsigned pool_grid(long long items) {
+    long long g = (items + 255) / 256;
+    const long long cap = 256 * 64;  // enough waves to fill 256 CUs; the loop strides the rest
+    return (unsigned)(g < 1 ? 1 : (g > cap ? cap : g));
+}
+
+template <typename T>
+static hipError_t maxpool_t(const void *x, void *y, int N, int H, int W, int C, bool nchw,
+                            bool vec, hipStream_t st) {
+    int OH = (H - 1) / 2 + 1, OW = (W - 1) / 2 + 1;
+    const T *xp = static_cast<const T *>(x);
+    T *yp = static_cast<T *>(y);
+    if (!nchw && vec) {
+        long long items = (long long)N * OH * OW * (C / Vec16<T>::n);
+        hipLaunchKernelGGL(maxpool_nhwc_vec<T>, dim3(pool_grid(items)), dim3(256), 0, st, xp, yp, N, H,
+                           W, C, OH, OW);
+    } else if (nchw) {
+        hipLaunchKernelGGL((maxpool_scalar<T, true>), dim3(pool_grid((long long)N * OH * OW * C)), dim3(256),
+                           0, st, xp, yp, N, H, W, C, OH, OW);
+    } else {
+        hipLaunchKernelGGL((maxpool_scalar<T, false>), dim3(pool_grid((long long)N * OH * OW * C)), dim3(256),
+                           0, st, xp, yp, N, H, W, C, OH, OW);
+    }
+    return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t avgpool_t(const void *x, void *y, int N, int H, int W, int C, bool nchw,
+                            bool vec, hipStream_t st) {
+    int OH = H / 2, OW = W / 2;
+    const T *xp = static_cast<const T *>(x);
+    T *yp = static_cast<T *>(y);
+    if (!nchw && vec) {
+        long long items = (long long)N * OH * OW * (C / Vec16<T>::n);
+        hipLaunchKernelGGL(avgpool_nhwc_vec<T>, dim3(pool_grid(items)), dim3(256), 0, st, xp, yp, N, H,
+                           W, C, OH, OW);
+    } else if (nchw) {
+        hipLaunchKernelGGL((avgpool_scalar<T, true>), dim3(pool_grid((long long)N * OH * OW * C)), dim3(256),
+                           0, st, xp, yp, N, H, W, C, OH, OW);
+    } else {
+        hipLaunchKernelGGL((avgpool_scalar<T, false>), dim3(pool_grid((long long)N * OH * OW * C)), dim3(256),
+                           0, st, xp, yp, N, H, W, C, OH, OW);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_maxpool(const void *x, void *y, int N, int H, int W, int C, bool nchw, int dtype,
+                          bool vec, hipStream_t st) {
+    switch (dtype) {
+    case CONV2D_DTYPE_F32:
+        return maxpool_t<float>(x, y, N, H, W, C, nchw, vec, st);
+    case CONV2D_DTYPE_BF16:
+        return maxpool_t<bf16>(x, y, N, H, W, C, nchw, vec, st);
+    case CONV2D_DTYPE_F16:
+        return maxpool_t<f16>(x, y, N, H, W, C, nchw, vec, st);
+    default:
+        return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_avgpool(const void *x, void *y, int N, int H, int W, int C, bool nchw, int dtype,
+                          bool vec, hipStream_t st) {
+    switch (dtype) {
+    case CONV2D_DTYPE_F32:
+        return avgpool_t<float>(x, y, N, H, W, C, nchw, vec, st);
+    case CONV2D_DTYPE_BF16:
+        return avgpool_t<bf16>(x, y, N, H, W, C, nchw, vec, st);
+    case CONV2D_DTYPE_F16:
+        return avgpool_t<f16>(x, y, N, H, W, C, nchw, vec, st);
+    default:
+        return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace c2d

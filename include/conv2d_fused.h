@@ -1,0 +1,165 @@
+/*
+ * conv2d_fused.h - C ABI of the fused 2-D convolution library for MI355X (gfx950).
+ *
+ * The layer is the one the inferencelayer page (docs.rs, src/rtdetr_gpu.rs:
+ * `conv()`, `IM2COL_SRC`, `ADDACT_SRC`, `MAXPOOL_SRC`, `AVGPOOL_SRC`) and the
+ * framecast page (package/rt.js: `wgslConv`) state: a k x k zero-padded
+ * cross-correlation lowered to a GEMM over im2col patches, with bias, an
+ * activation and an optional residual add applied in the GEMM epilogue, plus
+ * the 3x3/s2/p1 max pool and the 2x2/s2 average pool that sit beside it.
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are DEVICE pointers owned by the caller (for example
+ *    torch tensors' data_ptr()). The library never frees them, never keeps them
+ *    after the call returns, and writes only the output tensor.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Every call only
+ *    enqueues kernels on that stream and returns; it never synchronises. A
+ *    device fault therefore surfaces at the caller's next synchronisation.
+ *  - Arguments are validated on the host before anything is launched: a call
+ *    that returns an error has written nothing.
+ *  - Return value: CONV2D_OK (0) or a negative CONV2D_E* code; the message of
+ *    the last error on the calling thread is returned by conv2d_last_error().
+ *  - Tensors are dense and contiguous. Every tensor must hold fewer than 2^31
+ *    elements (CONV2D_EUNSUPPORTED otherwise).
+ *  - The output may not overlap the input or the residual (CONV2D_EINVAL).
+ *  - Calls on different streams may run concurrently, except that split-K
+ *    launches of conv2d_fused on one device share one library-owned scratch
+ *    buffer: callers that run conv2d_fused on several streams of one device at
+ *    once must serialise those calls.
+ */
+#ifndef CONV2D_FUSED_H
+#define CONV2D_FUSED_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Memory layouts. NHWC: x [N][H][W][Cin], w [Cout][kh][kw][Cin] (OHWI), residual and
+ * y [N][OH][OW][Cout]. NCHW: x [N][Cin][H][W], w [Cout][Cin][kh][kw] (OIHW), residual
+ * and y [N][Cout][OH][OW]. */
+#define CONV2D_LAYOUT_NHWC 0
+#define CONV2D_LAYOUT_NCHW 1
+
+/* Storage types of x, w, residual and y. Arithmetic is always fp32 accumulate;
+ * results are rounded to the storage type to nearest-even. bias and alpha are
+ * always fp32 (framecast `wgslConv` keeps them fp32 under f16 storage). */
+#define CONV2D_DTYPE_F32 0
+#define CONV2D_DTYPE_BF16 1
+#define CONV2D_DTYPE_F16 2
+
+/* Activation, in the low byte of `act`:
+ *   NONE  v
+ *   RELU  max(v, 0)                      (inferencelayer `ADDACT_SRC`)
+ *   SILU  v / (1 + exp(-v))              (inferencelayer `ADDACT_SRC`,
+ *                                         rlx-wgpu `apply_activation_host`)
+ *   PRELU v >= 0 ? v : alpha[co] * v     (framecast `wgslConv`, one slope per
+ *                                         output channel)
+ * OR-ed with CONV2D_RES_BEFORE_ACT, a residual is added before the activation
+ * (y = act(conv + bias + r), the ResNet block sum that inferencelayer's
+ * `encoder_maps` sends through `addact(.., relu)`); without it a residual is
+ * added after the activation (y = act(conv + bias) + r, framecast `wgslConv`). */
+#define CONV2D_ACT_NONE 0
+#define CONV2D_ACT_RELU 1
+#define CONV2D_ACT_SILU 2
+#define CONV2D_ACT_PRELU 3
+#define CONV2D_RES_BEFORE_ACT 0x100
+
+/* Status codes. */
+#define CONV2D_OK 0
+#define CONV2D_EINVAL (-1)      /* bad argument: null required pointer, size <= 0, stride
+                                   not 1 or 2, pad < 0, no output fits, unknown code,
+                                   PRELU without alpha, output overlapping an input */
+#define CONV2D_EUNSUPPORTED (-2) /* valid but not handled (a tensor of 2^31 or more
+                                   elements) */
+#define CONV2D_EHIP (-3)        /* the HIP runtime failed (no device, launch failure,
+                                   scratch allocation failure) */
+
+/*
+ * y = epilogue(conv(x, w)) for one layer.
+ *
+ * Source: inferencelayer page, `conv()` (output size (h + 2*pad - kh)/stride + 1,
+ * im2col in (dy, dx, c) order with zero fill, GEMM with bias + activation in the
+ * epilogue); framecast page, `wgslConv` (bias, per-channel PReLU, residual added
+ * after the activation).
+ *
+ * x        [N,H,W,Cin] or [N,Cin,H,W] in `dtype` (required)
+ * w        [Cout,kh,kw,Cin] or [Cout,Cin,kh,kw] in `dtype` (required)
+ * bias     fp32 [Cout], or NULL for no bias
+ * alpha    fp32 [Cout]; required when the activation is PRELU, ignored otherwise
+ * residual y's shape, layout and dtype, or NULL for none
+ * y        [N,OH,OW,Cout] or [N,Cout,OH,OW] in `dtype`, OH = (H + 2*pad - kh)/stride
+ *          + 1 (floor), OW likewise (required)
+ * stride   1 or 2; pad >= 0 (zero padding on all four sides); kh, kw >= 1
+ * act      CONV2D_ACT_* optionally OR-ed with CONV2D_RES_BEFORE_ACT
+ * layout   CONV2D_LAYOUT_*; dtype CONV2D_DTYPE_*
+ * stream   hipStream_t or NULL
+ *
+ * Accumulation is fp32 in any order; the result is rounded once to `dtype`.
+ * Some shapes run as split-K, which needs a device scratch buffer that the
+ * library allocates once per device on first use and keeps until the process
+ * ends (CONV2D_EHIP if that allocation fails).
+ */
+int conv2d_fused(const void *x, const void *w, const float *bias, const float *alpha,
+                 const void *residual, void *y, int N, int H, int W, int Cin, int Cout, int kh,
+                 int kw, int stride, int pad, int act, int layout, int dtype, void *stream);
+
+/*
+ * 3x3 max pool, stride 2, padding 1 with -infinity (out-of-range taps never win).
+ * Source: inferencelayer page, `MAXPOOL_SRC` and the max-pool step of
+ * `encoder_maps` (output (h + 2 - 3)/2 + 1).
+ *
+ * x [N,H,W,C] or [N,C,H,W] in `dtype`; y [N,OH,OW,C] or [N,C,OH,OW] with
+ * OH = (H - 1)/2 + 1 (floor), OW likewise. The result is bit-exactly one of the
+ * input values (the first largest in row-major tap order; NaN inputs are
+ * skipped unless every tap is NaN, in which case -infinity is written).
+ */
+int maxpool3x3s2(const void *x, void *y, int N, int H, int W, int C, int layout, int dtype,
+                 void *stream);
+
+/*
+ * 2x2 average pool, stride 2, no padding.
+ * Source: inferencelayer page, `AVGPOOL_SRC` (the sum of the four taps taken
+ * left to right, then times 0.25) and the ResNet-D shortcut of `encoder_maps`.
+ *
+ * x [N,H,W,C] or [N,C,H,W] in `dtype` (H, W >= 2); y [N,H/2,W/2,C] or
+ * [N,C,H/2,W/2] (floor: an odd last row or column is dropped). Computed in fp32
+ * as ((x00 + x01) + x10) + x11, times 0.25, then rounded once to `dtype`, so the
+ * result is bit-exact and reproducible.
+ */
+int avgpool2x2(const void *x, void *y, int N, int H, int W, int C, int layout, int dtype,
+               void *stream);
+
+/* floor((in + 2*pad - k)/stride) + 1, or -1 if in, k, stride <= 0, pad < 0 or the
+ * kernel does not fit the padded input (inferencelayer `conv()`). Host only. */
+int conv2d_out_dim(int in, int k, int stride, int pad);
+
+/* Host-only validation of conv2d_fused's arguments, without launching anything
+ * and without touching the GPU: returns what conv2d_fused would return before
+ * its launch (CONV2D_OK, CONV2D_EINVAL or CONV2D_EUNSUPPORTED). Pointers are only
+ * compared, never dereferenced. */
+int conv2d_check_args(const void *x, const void *w, const float *bias, const float *alpha,
+                      const void *residual, const void *y, int N, int H, int W, int Cin,
+                      int Cout, int kh, int kw, int stride, int pad, int act, int layout,
+                      int dtype);
+
+/* Host-only: writes into buf (capacity cap bytes, NUL-terminated) the name of the
+ * kernel variant conv2d_fused would launch for this shape, e.g.
+ * "igemm_nhwc_vec bf16 128x128 splitk=1". Returns the name's length, or a
+ * negative CONV2D_E* code for invalid arguments. */
+int conv2d_plan(int N, int H, int W, int Cin, int Cout, int kh, int kw, int stride, int pad,
+                int act, int layout, int dtype, char *buf, int cap);
+
+/* Message of the last error on the calling thread ("" if none). The pointer stays
+ * valid until the thread's next call into the library. */
+const char *conv2d_last_error(void);
+
+/* ABI version of this header: 1. */
+int conv2d_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CONV2D_FUSED_H */

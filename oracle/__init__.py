@@ -49,6 +49,8 @@ def _bind(lib):
     dp = ctypes.POINTER(ctypes.c_double)
     fp = ctypes.POINTER(ctypes.c_float)
     i = ctypes.c_int
+    lib.oracle_threads.argtypes = []
+    lib.oracle_threads.restype = i
     lib.oracle_out_dim.argtypes = [i, i, i, i]
     lib.oracle_out_dim.restype = i
     lib.oracle_conv2d_nchw.argtypes = [dp, dp, dp, dp, dp, dp] + [i] * 11
@@ -79,6 +81,11 @@ def _f64(a):
 def _act_flags(act, res_before_act):
     code = _ACT_NAMES[act] if isinstance(act, str) else int(act)
     return code | (RES_BEFORE_ACT if res_before_act else 0)
+
+
+def threads() -> int:
+    """Threads the oracle uses by default (OpenMP's maximum)."""
+    return int(_load().oracle_threads())
 
 
 def out_dim(n_in: int, k: int, stride: int, pad: int) -> int:

@@ -68,6 +68,9 @@ static int threads_to_use(int requested) {
 #endif
 }
 
+/* Number of threads a call with nthreads = 0 uses. */
+int oracle_threads(void) { return threads_to_use(0); }
+
 int oracle_out_dim(int in, int k, int stride, int pad) {
     if (in <= 0 || k <= 0 || stride <= 0 || pad < 0) return -1;
     int span = in + 2 * pad - k;

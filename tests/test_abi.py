@@ -1,0 +1,83 @@
+"""The C ABI without a GPU: the library loads, exports what the header declares, and the
+host-only entry points validate arguments (CPU only; no kernel is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch  # noqa: F401  (loads the HIP runtime the library binds to)
+
+import conv2d_bias_activation_amd as c2d
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "conv2d_fused.h")
+
+# stand-in device addresses: never dereferenced by the host-only calls
+X, Wp, Y, R, A = (ctypes.c_void_p(v << 32) for v in (1, 9, 17, 25, 33))
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(c2d.library_path())
+    names = _declared()
+    assert {"conv2d_fused", "maxpool3x3s2", "avgpool2x2"} <= names
+    for name in names:
+        assert hasattr(lib, name), name
+    assert names == set(c2d.SIGNATURES)
+    assert c2d._load().conv2d_abi_version() == 1
+
+
+def test_out_dim():
+    assert c2d.out_dim(640, 3, 2, 1) == 320
+    assert c2d.out_dim(32, 3, 1, 1) == 32
+    assert c2d.out_dim(80, 1, 1, 0) == 80
+    assert c2d.out_dim(2, 3, 1, 0) == -1
+    assert c2d.out_dim(5, 3, 0, 1) == -1
+
+
+def _check(**kw):
+    a = dict(x=X, w=Wp, bias=None, alpha=None, res=None, y=Y, N=1, H=8, W=8, Cin=16, Cout=16,
+             kh=3, kw=3, stride=1, pad=1, act=c2d.ACT_RELU, layout=c2d.LAYOUT_NHWC,
+             dtype=c2d.DTYPE_BF16)
+    a.update(kw)
+    return c2d.check_args(a["x"], a["w"], a["bias"], a["alpha"], a["res"], a["y"], a["N"], a["H"],
+                          a["W"], a["Cin"], a["Cout"], a["kh"], a["kw"], a["stride"], a["pad"],
+                          a["act"], a["layout"], a["dtype"])
+
+
+def test_check_args_accepts_valid():
+    assert _check() == c2d.OK
+    assert _check(act=c2d.ACT_PRELU, alpha=A) == c2d.OK
+    assert _check(res=R, act=c2d.ACT_RELU | c2d.RES_BEFORE_ACT) == c2d.OK
+    assert _check(layout=c2d.LAYOUT_NCHW, dtype=c2d.DTYPE_F16, stride=2) == c2d.OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), c2d.EINVAL), (dict(w=None), c2d.EINVAL), (dict(y=None), c2d.EINVAL),
+    (dict(N=0), c2d.EINVAL), (dict(Cin=-1), c2d.EINVAL), (dict(stride=3), c2d.EINVAL),
+    (dict(stride=0), c2d.EINVAL), (dict(pad=-1), c2d.EINVAL), (dict(kh=11, pad=0), c2d.EINVAL),
+    (dict(act=7), c2d.EINVAL), (dict(act=0x200), c2d.EINVAL), (dict(act=c2d.ACT_PRELU), c2d.EINVAL),
+    (dict(layout=2), c2d.EINVAL), (dict(dtype=5), c2d.EINVAL), (dict(y=X), c2d.EINVAL),
+    (dict(res=Y), c2d.EINVAL), (dict(N=4, H=2048, W=2048, Cin=256), c2d.EUNSUPPORTED),
+])
+def test_check_args_rejects(kw, code):
+    assert _check(**kw) == code
+    assert c2d.last_error() != ""
+
+
+def test_plan_names_a_kernel_for_every_workload_shape():
+    bf16, f16, f32 = c2d.DTYPE_BF16, c2d.DTYPE_F16, c2d.DTYPE_F32
+    shapes = [(1, 32, 32, 16, 32, 3, 3, 1, 1, 1, 0, f32), (1, 640, 640, 3, 32, 3, 3, 2, 1, 2, 0, f32),
+              (4, 80, 80, 512, 256, 1, 1, 1, 0, 1, 0, bf16), (1, 68, 120, 240, 240, 3, 3, 1, 1, 3, 1, f16),
+              (4, 40, 40, 256, 256, 3, 3, 1, 1, 1, 0, bf16)]
+    for s in shapes:
+        name = c2d.plan(*s)
+        assert name and ("igemm" in name or "direct" in name), name
+    assert c2d.plan(1, 640, 640, 3, 32, 3, 3, 2, 1, 2, 0, bf16).startswith("direct")
+    with pytest.raises(c2d.Conv2dError):
+        c2d.plan(1, 8, 8, 4, 4, 3, 3, 5, 1, 0, 0, bf16)
