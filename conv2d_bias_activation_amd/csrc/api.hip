@@ -126,11 +126,12 @@ int check_conv(const void *x, const void *w, const float *alpha, const void *res
     return CONV2D_OK;
 }
 
-enum Family { FAM_DIRECT = 0, FAM_IGEMM = 1 };
+enum Family { FAM_DIRECT = 0, FAM_IGEMM = 1, FAM_NHWC = 2 };
 
 struct Plan {
     int family;
     IgemmPlan ig;
+    NhwcPlan nh;
 };
 
 const char *tile_name(int t) {
@@ -173,11 +174,48 @@ int choose_tile(const ConvArgs &a) {
     return best;
 }
 
+const char *nhwc_tile_name(int t) {
+    static const char *names[NHWC_TILE_COUNT] = {"256x128w8", "128x128", "128x64", "256x64w8",
+                                                 "256x32",    "64x64",   "128x128w8", "128x256w8"};
+    return (t >= 0 && t < NHWC_TILE_COUNT) ? names[t] : "?";
+}
+
+// Channel-last 16-bit layers. Tile shapes from measurements on MI355X (ResNet-style
+// layer shapes): 8-wave 128x128 tiles while there are enough of them to occupy the
+// GPU, 64x64 tiles for the small-M deep layers (more workgroups in flight beat
+// bigger tiles there), 128x256 for wide pointwise layers, 128x64 for narrow outputs.
+NhwcPlan plan_nhwc(const ConvArgs &a) {
+    NhwcPlan p{};
+    auto tiles = [&](int bm, int bn) {
+        return (long long)((a.M + bm - 1) / bm) * ((a.Cout + bn - 1) / bn);
+    };
+    if (a.Cout <= 64)
+        p.tile = NHWC_TILE_128x64;
+    else if (a.Cout >= 256 && a.K >= 256 && a.kh * a.kw == 1 && tiles(128, 256) >= 100)
+        p.tile = NHWC_TILE_128x256_W8;
+    else if (tiles(128, 128) >= 160)
+        p.tile = NHWC_TILE_128x128_W8;
+    else
+        p.tile = NHWC_TILE_64x64;
+    p.tap_inner = (a.Cin % 64) == 0;
+    return p;
+}
+
 Plan make_plan(const ConvArgs &a, int layout, int dtype) {
     Plan p{};
     const int ve = 16 / dtype_bytes(dtype);
     if (a.Cin <= 4) {
         p.family = FAM_DIRECT;
+        return p;
+    }
+    const long long xbytes = (long long)a.N * a.H * a.W * a.Cin * dtype_bytes(dtype);
+    const long long wbytes = (long long)a.Cout * a.K * dtype_bytes(dtype);
+    const long long ybytes = (long long)a.M * a.Cout * dtype_bytes(dtype);
+    if (layout == CONV2D_LAYOUT_NHWC && dtype != CONV2D_DTYPE_F32 && (a.Cin % 8) == 0 &&
+        aligned16(a.x) && aligned16(a.w) && xbytes < (1ll << 31) && wbytes < (1ll << 31) &&
+        ybytes < (1ll << 31)) {
+        p.family = FAM_NHWC;
+        p.nh = plan_nhwc(a);
         return p;
     }
     p.family = FAM_IGEMM;
@@ -193,8 +231,11 @@ int describe(const Plan &p, int layout, int dtype, char *buf, int cap) {
     if (p.family == FAM_DIRECT) {
         snprintf(tmp, sizeof tmp, "direct_%s %s cob32", layout == CONV2D_LAYOUT_NCHW ? "nchw" : "nhwc",
                  dtype_name(dtype));
+    } else if (p.family == FAM_NHWC) {
+        snprintf(tmp, sizeof tmp, "igemm_nhwc_pipe%s %s %s", p.nh.tap_inner ? "_tapinner" : "",
+                 dtype_name(dtype), nhwc_tile_name(p.nh.tile));
     } else {
-        snprintf(tmp, sizeof tmp, "igemm_%s%s %s %s splitk=1", p.ig.nchw ? "nchw" : "nhwc",
+        snprintf(tmp, sizeof tmp, "igemm_%s%s %s %s", p.ig.nchw ? "nchw" : "nhwc",
                  p.ig.avec ? "_vec" : "_gather", dtype_name(dtype), tile_name(p.ig.tile));
     }
     int n = (int)strlen(tmp);
@@ -273,10 +314,13 @@ int conv2d_fused(const void *x, const void *w, const float *bias, const float *a
     hipStream_t st = static_cast<hipStream_t>(stream);
     Plan p = make_plan(a, layout, dtype);
     hipError_t e;
-    if (p.family == FAM_DIRECT)
+    if (p.family == FAM_DIRECT) {
         e = launch_direct(a, dtype, layout == CONV2D_LAYOUT_NCHW, st);
-    else
+    } else if (p.family == FAM_NHWC) {
+        e = launch_igemm_nhwc(a, dtype, p.nh, st);
+    } else {
         e = launch_igemm(a, dtype, p.ig, st);
+    }
     if (e != hipSuccess) return hip_fail(e, "conv2d_fused launch");
     return set_ok();
 }

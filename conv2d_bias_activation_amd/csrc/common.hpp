@@ -11,6 +11,7 @@ namespace c2d {
 typedef __bf16 bf16;
 typedef _Float16 f16;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Everything a conv kernel needs, passed by value.

@@ -13,39 +13,11 @@
 // K order follows the weight layout so that B is a plain row-major [Cout][K]
 // matrix: channel-last (OHWI) weights give k = (ky*kw + kx)*Cin + ci, the pages'
 // (dy, dx, c) order; channel-first (OIHW) weights give k = (ci*kh + ky)*kw + kx.
-#include "common.hpp"
+#include "igemm_common.hpp"
 #include "kernels.hpp"
 
 namespace c2d {
 
-// One 16x16 output block per instruction; every lane holds KPL consecutive k of
-// one A row (lane % 16) and one B column (lane % 16); lane / 16 picks which KPL-run
-// of the instruction's 4*KPL k values. The fp32 result: lane holds rows
-// 4*(lane/16) + i, i < 4, of column lane % 16.
-template <typename T> struct Mfma;
-template <> struct Mfma<bf16> {
-    static constexpr int KPL = 8;
-    typedef __bf16 vec __attribute__((ext_vector_type(8)));
-    __device__ static f32x4 run(vec a, vec b, f32x4 c) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-    }
-};
-template <> struct Mfma<f16> {
-    static constexpr int KPL = 8;
-    typedef _Float16 vec __attribute__((ext_vector_type(8)));
-    __device__ static f32x4 run(vec a, vec b, f32x4 c) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-    }
-};
-template <> struct Mfma<float> {
-    static constexpr int KPL = 1;
-    typedef float vec;
-    __device__ static f32x4 run(vec a, vec b, f32x4 c) {
-        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-    }
-};
-
-template <int A, int B> struct cmax { static constexpr int v = A > B ? A : B; };
 
 // T: storage type. BM x BN tile per 256-thread workgroup, waves arranged WGM x WGN.
 // NCHW: channel-first layout. AVEC: channel-last with Cin a multiple of the 16-byte
@@ -285,89 +257,7 @@ __global__ __launch_bounds__(256) void igemm_kernel(ConvArgs a, int tiles_n) {
             }
     __syncthreads();
 
-    const T *__restrict__ res = static_cast<const T *>(a.res);
-    T *__restrict__ y = static_cast<T *>(a.y);
-    const bool has_res = res != nullptr;
-    const bool pre = a.res_before_act != 0;
-    const int act = a.act;
-    const int Cout = a.Cout;
-
-    if constexpr (!NCHW) {
-        if ((Cout % VE) == 0 && a.vec_out) {
-            constexpr int CV = BN / VE;
-            for (int it = tid; it < BM * CV; it += 256) {
-                int row = it / CV, cv = it % CV;
-                int m = m0 + row, co = n0 + cv * VE;
-                if (m >= a.M || co >= Cout) continue;
-                size_t o = (size_t)m * Cout + co;
-                T rv[VE];
-                if (has_res) {
-                    u32x4 t = *reinterpret_cast<const u32x4 *>(res + o);
-                    __builtin_memcpy(rv, &t, 16);
-                }
-                T out[VE];
-#pragma unroll
-                for (int e = 0; e < VE; ++e) {
-                    float b = a.bias ? a.bias[co + e] : 0.0f;
-                    float al = a.alpha ? a.alpha[co + e] : 0.0f;
-                    float r = has_res ? to_f32(rv[e]) : 0.0f;
-                    out[e] = from_f32<T>(epilogue(sC[row * LDC + cv * VE + e], b, al, r, has_res, act, pre));
-                }
-                u32x4 t;
-                __builtin_memcpy(&t, out, 16);
-                *reinterpret_cast<u32x4 *>(y + o) = t;
-            }
-        } else {
-            for (int it = tid; it < BM * BN; it += 256) {
-                int row = it / BN, col = it % BN;
-                int m = m0 + row, co = n0 + col;
-                if (m >= a.M || co >= Cout) continue;
-                size_t o = (size_t)m * Cout + co;
-                float b = a.bias ? a.bias[co] : 0.0f;
-                float al = a.alpha ? a.alpha[co] : 0.0f;
-                float r = has_res ? to_f32(res[o]) : 0.0f;
-                y[o] = from_f32<T>(epilogue(sC[row * LDC + col], b, al, r, has_res, act, pre));
-            }
-        }
-    } else {
-        constexpr int RV = BM / VE;
-        const bool plane_aligned = (OHW % VE) == 0 && a.vec_out;
-        for (int it = tid; it < BN * RV; it += 256) {
-            int col = it / RV, rv = it % RV;
-            int co = n0 + col, mb = m0 + rv * VE;
-            if (co >= Cout || mb >= a.M) continue;
-            float b = a.bias ? a.bias[co] : 0.0f;
-            float al = a.alpha ? a.alpha[co] : 0.0f;
-            int n = mb / OHW, pix = mb - n * OHW;
-            size_t o = ((size_t)n * Cout + co) * OHW + pix;
-            if (plane_aligned && (pix % VE) == 0 && mb + VE <= a.M) {
-                // the VE pixels are consecutive in one plane and 16-byte aligned
-                T rvv[VE];
-                if (has_res) {
-                    u32x4 t = *reinterpret_cast<const u32x4 *>(res + o);
-                    __builtin_memcpy(rvv, &t, 16);
-                }
-                T out[VE];
-#pragma unroll
-                for (int e = 0; e < VE; ++e) {
-                    float r = has_res ? to_f32(rvv[e]) : 0.0f;
-                    out[e] = from_f32<T>(epilogue(sC[(rv * VE + e) * LDC + col], b, al, r, has_res, act, pre));
-                }
-                u32x4 t;
-                __builtin_memcpy(&t, out, 16);
-                *reinterpret_cast<u32x4 *>(y + o) = t;
-            } else {
-                for (int e = 0; e < VE; ++e) {
-                    int m = mb + e;
-                    if (m >= a.M) break;
-                    int n2 = m / OHW, pix2 = m - n2 * OHW;
-                    size_t o2 = ((size_t)n2 * Cout + co) * OHW + pix2;
-                    float r = has_res ? to_f32(res[o2]) : 0.0f;
-                    y[o2] = from_f32<T>(epilogue(sC[(rv * VE + e) * LDC + col], b, al, r, has_res, act, pre));
-                }
-            }
-        }
-    }
+    store_tile<T, BM, BN, LDC, NCHW>(sC, a, m0, n0, tid);
 }
 
 template <typename T, int BM, int BN, int WGM, int WGN, bool NCHW, bool AVEC, bool BVEC>

@@ -1,0 +1,315 @@
+// Channel-last implicit-GEMM convolution on CDNA4 matrix cores, pipelined.
+//
+// Same GEMM as the general kernel (m = output pixel, k = (tap, input channel),
+// n = output channel; inferencelayer page, `conv()`: im2col + `enc_gemm3` with bias
+// and activation in the epilogue), built for throughput on gfx950:
+//
+//  * K steps of 64: every thread moves whole 16-byte channel runs (8 x 16-bit) of
+//    the patch matrix A and of the weight B with buffer loads. A padding tap, a row
+//    past the last pixel or a column past the last channel gets an out-of-range
+//    buffer offset, which the hardware answers with zeros: no branches in the loop.
+//  * LDS rows are 128 bytes with the 16-byte chunks XOR-swizzled by row (chunk
+//    position p holds logical chunk p ^ (row % 8)), so neither the 16-byte stores
+//    nor the matrix-core operand reads of 16 consecutive rows hit the same banks.
+//  * The loads go straight from memory into LDS (buffer_load ... lds: each lane's
+//    16 bytes land at the wave's LDS base + 16 * lane, which is exactly the swizzled
+//    row layout above), through a ring of NS LDS stages with one barrier per step:
+//    NS = 3 keeps two K steps in flight while the matrix cores work on a third.
+//  * When Cin is a multiple of 64 the K loop takes the taps innermost, so the patch
+//    rows of consecutive steps are the same pixels shifted by one tap and mostly
+//    hit in the vector L1 cache.
+#include "igemm_common.hpp"
+#include "kernels.hpp"
+
+namespace c2d {
+
+namespace {
+
+__device__ __forceinline__ __attribute__((address_space(3))) void *lds_ptr(void *p) {
+    return (__attribute__((address_space(3))) void *)p;
+}
+
+}  // namespace
+
+// s_waitcnt with only the vector-memory counter limited (expcnt and lgkmcnt at their
+// maxima, so they impose no wait).
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier without a memory fence: the LDS data it publishes is complete
+// either through the explicit vmcnt wait before it (direct-to-LDS loads) or because
+// the readers' operands were consumed. The empty asm statements keep the compiler
+// from moving memory accesses across it.
+__device__ __forceinline__ void barrier_nofence() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <typename T, int BM, int BN, int WGM, int WGN, int NS, bool TAP_INNER>
+__global__ __launch_bounds__(64 * WGM * WGN) void igemm_nhwc_kernel(ConvArgs a, int tiles_n) {
+    constexpr int NW = WGM * WGN;        // waves per workgroup (4 or 8)
+    constexpr int BK = 64;               // k per step (elements)
+    constexpr int ROWB = 128;            // bytes per LDS row (BK 16-bit values)
+    constexpr int FM = BM / (32 * WGM);  // 32x32 blocks per wave along M
+    constexpr int FN = BN / (32 * WGN);
+    static_assert((NW == 4 || NW == 8) && FM >= 1 && FN >= 1, "4 or 8 waves");
+    constexpr int RR = 8 * NW;           // rows per load round (8 per wave)
+    static_assert(BM % RR == 0 && BN % RR == 0, "whole load rounds");
+    static_assert(NS == 2 || NS == 3, "LDS stages");
+    constexpr int LA = BM / RR;          // 16-byte A loads per thread per step
+    constexpr int LB = BN / RR;
+    constexpr int L = LA + LB;
+    constexpr int STAGE = (BM + BN) * ROWB;
+    constexpr int WN = FN * 32;          // columns per wave
+    constexpr int WLD = WN + 4;          // row stride of a wave's epilogue slice (floats)
+    constexpr int SLICE = 16 * WLD * 4;  // bytes
+    constexpr int SPS = STAGE / SLICE;   // slices per stage array
+    static_assert(SPS * 2 >= NW, "epilogue slices fit in two stages");
+    // One array per stage: distinct objects let the compiler see that the direct-to-LDS
+    // loads into one stage never alias the operand reads from another, so it keeps the
+    // explicit vmcnt waits instead of draining every load before each read.
+    __shared__ __attribute__((aligned(1024))) char st0[STAGE];
+    __shared__ __attribute__((aligned(1024))) char st1[STAGE];
+    __shared__ __attribute__((aligned(1024))) char st2[NS == 3 ? STAGE : 16];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave % WGM, wn = wave / WGM;
+
+    const int tile = xcd_remap(blockIdx.x, gridDim.x);
+    const int m0 = (tile / tiles_n) * BM;
+    const int n0 = (tile % tiles_n) * BN;
+
+    const int H = a.H, W = a.W, Cin = a.Cin, kh = a.kh, kw = a.kw, K = a.K;
+    const int OW = a.OW, OHW = a.OH * a.OW;
+    const int nsteps = (K + BK - 1) / BK;
+
+    const __amdgpu_buffer_rsrc_t rx =
+        make_rsrc(a.x, (uint32_t)((size_t)a.N * H * W * Cin * sizeof(T)));
+    const __amdgpu_buffer_rsrc_t rw =
+        make_rsrc(a.w, (uint32_t)((size_t)a.Cout * K * sizeof(T)));
+
+    // This thread's loads: rows (j*NW + wave)*8 + lrow, LDS chunk position pch (= the
+    // lane's slot in the wave's 1 KiB), which holds the row's logical 16-byte chunk
+    // c = pch ^ ((row / 2) % 8) (k offset 8c within the step; NW is even, so this is
+    // the same for every j). With that swizzle the 16 rows read by one quarter-wave
+    // occupy 16 distinct 16-byte bank groups.
+    const int lrow = lane >> 3;
+    const int pch = lane & 7;
+    const int c = pch ^ ((wave * 4 + (lane >> 4)) & 7);
+
+    int a_pix[LA], a_ih[LA], a_iw[LA];
+    bool a_ok[LA];
+#pragma unroll
+    for (int j = 0; j < LA; ++j) {
+        int m = m0 + (j * NW + wave) * 8 + lrow;
+        a_ok[j] = m < a.M;
+        int mm = a_ok[j] ? m : 0;
+        int n = mm / OHW, pix = mm - n * OHW;
+        int oh = pix / OW, ow = pix - oh * OW;
+        a_pix[j] = n * H * W;
+        a_ih[j] = oh * a.stride - a.pad;
+        a_iw[j] = ow * a.stride - a.pad;
+    }
+    int b_off[LB];
+    bool b_ok[LB];
+#pragma unroll
+    for (int j = 0; j < LB; ++j) {
+        int co = n0 + (j * NW + wave) * 8 + lrow;
+        b_ok[j] = co < a.Cout;
+        b_off[j] = (b_ok[j] ? co : 0) * K;
+    }
+
+    // k state of this thread's chunk at the next step to load
+    int ky = 0, kx = 0, ci = c * 8;
+    if constexpr (!TAP_INNER) {
+        int tap = ci / Cin;
+        ci -= tap * Cin;
+        ky = tap / kw;
+        kx = tap - ky * kw;
+    }
+
+    // Issues one step's loads into LDS stage `stage`. A step past this slice (live
+    // false) still issues them, with out-of-range offsets (no memory traffic), so every
+    // step adds exactly L to the vector-memory counter and the waits below are exact.
+    auto issue = [&](char *stage, bool live) {
+        char *sA = stage;
+        char *sB = sA + BM * ROWB;
+        const bool kin = live && ky < kh;
+#pragma unroll
+        for (int j = 0; j < LA; ++j) {
+            int iy = a_ih[j] + ky, ix = a_iw[j] + kx;
+            bool ok = a_ok[j] && kin && (unsigned)iy < (unsigned)H && (unsigned)ix < (unsigned)W;
+            uint32_t off = (uint32_t)((a_pix[j] + iy * W + ix) * Cin + ci) * (uint32_t)sizeof(T);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lds_ptr(sA + (j * NW + wave) * 1024), 16,
+                                                     (int)(ok ? off : kOOB), 0, 0, 0);
+        }
+        const int kk = (ky * kw + kx) * Cin + ci;
+#pragma unroll
+        for (int j = 0; j < LB; ++j) {
+            uint32_t off = (uint32_t)(b_off[j] + kk) * (uint32_t)sizeof(T);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lds_ptr(sB + (j * NW + wave) * 1024), 16,
+                                                     (int)((b_ok[j] && kin) ? off : kOOB), 0, 0, 0);
+        }
+        if constexpr (TAP_INNER) {
+            if (++kx == kw) {
+                kx = 0;
+                if (++ky == kh) {
+                    ky = 0;
+                    ci += BK;
+                }
+            }
+        } else {
+            ci += BK;
+            while (ci >= Cin) {
+                ci -= Cin;
+                if (++kx == kw) {
+                    kx = 0;
+                    ++ky;
+                }
+            }
+        }
+    };
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    typedef typename Mfma32<T>::vec vec;
+    const int rl = lane & 31, kq = lane >> 5, sw = (rl >> 1) & 7;
+    auto compute = [&](const char *stage) {
+        const char *sA = stage;
+        const char *sB = sA + BM * ROWB;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int chunk = ((ks * 2 + kq) ^ sw) * 16;
+            vec fa[FM], fb[FN];
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                fa[i] = *reinterpret_cast<const vec *>(sA + (wm * FM * 32 + i * 32 + rl) * ROWB + chunk);
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                fb[j] = *reinterpret_cast<const vec *>(sB + (wn * FN * 32 + j * 32 + rl) * ROWB + chunk);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) acc[i][j] = Mfma32<T>::run(fa[i], fb[j], acc[i][j]);
+        }
+    };
+
+    // Ring of NS stages; step s lives in stage s % NS. One step: wait for this wave's
+    // loads of the step, barrier (every wave's have landed and every wave is done with
+    // the previous step's stage), matrix cores on this step, then refill the previous
+    // step's stage (so the matrix cores start right after the barrier).
+    auto step = [&](const char *cur, char *refill, bool live_refill) {
+        if constexpr (NS == 3)
+            wait_vmcnt<L>();
+        else
+            wait_vmcnt<0>();
+        barrier_nofence();
+        compute(cur);
+        issue(refill, live_refill);
+    };
+    if constexpr (NS == 3) {
+        issue(st0, nsteps > 0);
+        issue(st1, nsteps > 1);
+        for (int s = 0; s < nsteps; s += 3) {
+            step(st0, st2, s + 2 < nsteps);
+            if (s + 1 >= nsteps) break;
+            step(st1, st0, s + 3 < nsteps);
+            if (s + 2 >= nsteps) break;
+            step(st2, st1, s + 4 < nsteps);
+        }
+    } else {
+        issue(st0, nsteps > 0);
+        for (int s = 0; s < nsteps; s += 2) {
+            step(st0, st1, s + 1 < nsteps);
+            if (s + 1 >= nsteps) break;
+            step(st1, st0, s + 2 < nsteps);
+        }
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+
+    // Epilogue, each wave over its own rows through its slice of stage 0 (LDS phase,
+    // then global phase; see wave_epilogue_nhwc32).
+    float *slice = reinterpret_cast<float *>(wave < SPS ? st0 + wave * SLICE : st1 + (wave - SPS) * SLICE);
+    wave_epilogue_nhwc32<T, FM, FN, WLD>(acc, slice, a, m0 + wm * FM * 32, n0 + wn * WN, lane,
+                                         (uint32_t)((size_t)a.M * a.Cout * sizeof(T)));
+}
+
+namespace {
+
+// Tile shapes: (BM, BN) per workgroup, waves WGM x WGN, LDS stages.
+struct TileCfg {
+    int bm, bn, wgm, wgn, ns;
+};
+constexpr TileCfg kTiles[NHWC_TILE_COUNT] = {
+    {256, 128, 4, 2, 2},  // NHWC_TILE_256x128_W8
+    {128, 128, 2, 2, 3},  // NHWC_TILE_128x128
+    {128, 64, 2, 2, 3},   // NHWC_TILE_128x64
+    {256, 64, 4, 2, 3},   // NHWC_TILE_256x64_W8
+    {256, 32, 4, 1, 3},   // NHWC_TILE_256x32
+    {64, 64, 2, 2, 3},    // NHWC_TILE_64x64
+    {128, 128, 2, 4, 3},  // NHWC_TILE_128x128_W8
+    {128, 256, 2, 4, 2},  // NHWC_TILE_128x256_W8
+};
+
+template <typename T, int TILE>
+hipError_t launch_t(const ConvArgs &a, const NhwcPlan &p, hipStream_t st) {
+    constexpr TileCfg c = kTiles[TILE];
+    const long long tiles_m = (a.M + c.bm - 1) / c.bm;
+    const int tiles_n = (a.Cout + c.bn - 1) / c.bn;
+    if (tiles_m * tiles_n > 0x7fffffffll) return hipErrorInvalidValue;
+    dim3 grid((unsigned)(tiles_m * tiles_n));
+    dim3 block(64 * c.wgm * c.wgn);
+    if (p.tap_inner)
+        hipLaunchKernelGGL((igemm_nhwc_kernel<T, c.bm, c.bn, c.wgm, c.wgn, c.ns, true>), grid, block, 0, st, a, tiles_n);
+    else
+        hipLaunchKernelGGL((igemm_nhwc_kernel<T, c.bm, c.bn, c.wgm, c.wgn, c.ns, false>), grid, block, 0, st, a, tiles_n);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_dtype(const ConvArgs &a, const NhwcPlan &p, hipStream_t st) {
+    switch (p.tile) {
+    case 0: return launch_t<T, 0>(a, p, st);
+    case 1: return launch_t<T, 1>(a, p, st);
+    case 2: return launch_t<T, 2>(a, p, st);
+    case 3: return launch_t<T, 3>(a, p, st);
+    case 4: return launch_t<T, 4>(a, p, st);
+    case 5: return launch_t<T, 5>(a, p, st);
+    case 6: return launch_t<T, 6>(a, p, st);
+    case 7: return launch_t<T, 7>(a, p, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+int nhwc_tile_bm(int tile) { return (tile >= 0 && tile < NHWC_TILE_COUNT) ? kTiles[tile].bm : 0; }
+int nhwc_tile_bn(int tile) { return (tile >= 0 && tile < NHWC_TILE_COUNT) ? kTiles[tile].bn : 0; }
+int nhwc_tile_waves(int tile) {
+    return (tile >= 0 && tile < NHWC_TILE_COUNT) ? kTiles[tile].wgm * kTiles[tile].wgn : 0;
+}
+
+hipError_t launch_igemm_nhwc(const ConvArgs &a, int dtype, const NhwcPlan &p, hipStream_t st) {
+    switch (dtype) {
+    case CONV2D_DTYPE_BF16:
+        return launch_dtype<bf16>(a, p, st);
+    case CONV2D_DTYPE_F16:
+        return launch_dtype<f16>(a, p, st);
+    default:
+        return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace c2d

@@ -22,6 +22,31 @@ struct IgemmPlan {
 // MFMA implicit GEMM, any k/stride/pad, both layouts, f32/bf16/f16 storage.
 hipError_t launch_igemm(const ConvArgs &a, int dtype, const IgemmPlan &p, hipStream_t st);
 
+enum NhwcTile {
+    NHWC_TILE_256x128_W8 = 0,
+    NHWC_TILE_128x128 = 1,
+    NHWC_TILE_128x64 = 2,
+    NHWC_TILE_256x64_W8 = 3,
+    NHWC_TILE_256x32 = 4,
+    NHWC_TILE_64x64 = 5,
+    NHWC_TILE_128x128_W8 = 6,
+    NHWC_TILE_128x256_W8 = 7,
+    NHWC_TILE_COUNT = 8,
+};
+
+struct NhwcPlan {
+    int tile;        // NhwcTile
+    bool tap_inner;  // Cin % 64 == 0: taps innermost in the K loop
+};
+
+int nhwc_tile_bm(int tile);
+int nhwc_tile_bn(int tile);
+int nhwc_tile_waves(int tile);
+
+// Pipelined channel-last MFMA implicit GEMM (bf16/f16, Cin % 8 == 0, x, w and y
+// under 2 GiB, x and w 16-byte aligned).
+hipError_t launch_igemm_nhwc(const ConvArgs &a, int dtype, const NhwcPlan &p, hipStream_t st);
+
 // Direct convolution on the vector ALUs for few input channels (the image stem):
 // one thread per output pixel and a block of output channels.
 hipError_t launch_direct(const ConvArgs &a, int dtype, bool nchw, hipStream_t st);

@@ -22,10 +22,8 @@
  *  - Tensors are dense and contiguous. Every tensor must hold fewer than 2^31
  *    elements (CONV2D_EUNSUPPORTED otherwise).
  *  - The output may not overlap the input or the residual (CONV2D_EINVAL).
- *  - Calls on different streams may run concurrently, except that split-K
- *    launches of conv2d_fused on one device share one library-owned scratch
- *    buffer: callers that run conv2d_fused on several streams of one device at
- *    once must serialise those calls.
+ *  - The library keeps no state between calls besides the last-error message,
+ *    so calls on different streams may run concurrently.
  */
 #ifndef CONV2D_FUSED_H
 #define CONV2D_FUSED_H
@@ -73,8 +71,7 @@ extern "C" {
                                    PRELU without alpha, output overlapping an input */
 #define CONV2D_EUNSUPPORTED (-2) /* valid but not handled (a tensor of 2^31 or more
                                    elements) */
-#define CONV2D_EHIP (-3)        /* the HIP runtime failed (no device, launch failure,
-                                   scratch allocation failure) */
+#define CONV2D_EHIP (-3)        /* the HIP runtime failed (no device, launch failure) */
 
 /*
  * y = epilogue(conv(x, w)) for one layer.
@@ -97,9 +94,7 @@ extern "C" {
  * stream   hipStream_t or NULL
  *
  * Accumulation is fp32 in any order; the result is rounded once to `dtype`.
- * Some shapes run as split-K, which needs a device scratch buffer that the
- * library allocates once per device on first use and keeps until the process
- * ends (CONV2D_EHIP if that allocation fails).
+ * The library allocates nothing.
  */
 int conv2d_fused(const void *x, const void *w, const float *bias, const float *alpha,
                  const void *residual, void *y, int N, int H, int W, int Cin, int Cout, int kh,
@@ -146,7 +141,7 @@ int conv2d_check_args(const void *x, const void *w, const float *bias, const flo
 
 /* Host-only: writes into buf (capacity cap bytes, NUL-terminated) the name of the
  * kernel variant conv2d_fused would launch for this shape, e.g.
- * "igemm_nhwc_vec bf16 128x128 splitk=1". Returns the name's length, or a
+ * "igemm_nhwc_pipe_tapinner bf16 128x128w8". Returns the name's length, or a
  * negative CONV2D_E* code for invalid arguments. */
 int conv2d_plan(int N, int H, int W, int Cin, int Cout, int kh, int kw, int stride, int pad,
                 int act, int layout, int dtype, char *buf, int cap);

@@ -58,6 +58,14 @@ SWEEP = [
     (1, 2, 3, 16, 8, 3, 2, 2, "relu", None, "nhwc", "f16"),     # padding wider than input
     (4, 7, 9, 8, 1, 3, 1, 1, "silu", None, "nhwc", "bf16"),     # one output channel
     (1, 11, 13, 1, 5, 3, 1, 1, "relu", None, "nchw", "bf16"),   # one input channel
+    # few output tiles, deep K
+    (1, 10, 10, 256, 256, 3, 1, 1, "relu", "pre", "nhwc", "bf16"),
+    (2, 9, 7, 72, 200, 3, 2, 1, "silu", "post", "nhwc", "f16"),  # Cin % 64 != 0, K tail
+    (1, 6, 6, 512, 64, 3, 1, 1, "none", None, "nhwc", "bf16"),
+    (1, 7, 9, 320, 40, 3, 2, 1, "prelu", "post", "nhwc", "bf16"),
+    (3, 5, 5, 128, 96, 1, 1, 0, "relu", None, "nhwc", "f16"),
+    (2, 12, 12, 256, 512, 3, 2, 1, "relu", None, "nhwc", "bf16"),
+    (1, 64, 64, 64, 64, 3, 1, 1, "relu", "pre", "nhwc", "bf16"),  # many tiles, taps innermost
 ]
 
 
@@ -237,6 +245,18 @@ def test_conv5_resnet18d_per_layer_full():
 
 def test_conv5_resnet18d_end_to_end_full():
     _end_to_end("resnet", wl.conv5_resnet18d())
+
+
+def test_repeatable():
+    """Every output is one fixed-order fp32 sum: repeated calls agree bit for bit."""
+    x, spec, r = wl.random_conv_case(11, n=1, h=20, w=20, cin=512, cout=512, k=3, stride=1, pad=1,
+                                     act="relu", layout="nhwc", dtype="bf16", residual=True,
+                                     res_before_act=True)
+    ys = [_gpu_conv(x, spec, r, "nhwc") for _ in range(4)]
+    torch.cuda.synchronize()
+    for y in ys[1:]:
+        assert bits_equal(y, ys[0])
+    gate(to64(ys[0]), _oracle_conv(x, spec, r, "nhwc"), "bf16")
 
 
 def test_batch_equals_separate_runs():
