@@ -18,6 +18,8 @@
 //  * When Cin is a multiple of 64 the K loop takes the taps innermost, so the patch
 //    rows of consecutive steps are the same pixels shifted by one tap and mostly
 //    hit in the vector L1 cache.
+#include <utility>
+
 #include "igemm_common.hpp"
 #include "kernels.hpp"
 
@@ -49,7 +51,9 @@ __device__ __forceinline__ void barrier_nofence() {
 }
 
 template <typename T, int BM, int BN, int WGM, int WGN, int NS, bool TAP_INNER>
-__global__ __launch_bounds__(64 * WGM * WGN) void igemm_nhwc_kernel(ConvArgs a, int tiles_n) {
+__global__ __launch_bounds__(64 * WGM * WGN) void igemm_nhwc_kernel(ConvArgs a, int tiles_n,
+                                                                   int steps_per_split,
+                                                                   float *partials) {
     constexpr int NW = WGM * WGN;        // waves per workgroup (4 or 8)
     constexpr int BK = 64;               // k per step (elements)
     constexpr int ROWB = 128;            // bytes per LDS row (BK 16-bit values)
@@ -58,7 +62,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void igemm_nhwc_kernel(ConvArgs a, 
     static_assert((NW == 4 || NW == 8) && FM >= 1 && FN >= 1, "4 or 8 waves");
     constexpr int RR = 8 * NW;           // rows per load round (8 per wave)
     static_assert(BM % RR == 0 && BN % RR == 0, "whole load rounds");
-    static_assert(NS == 2 || NS == 3, "LDS stages");
+    static_assert(NS >= 2 && NS <= 6, "LDS stages");
     constexpr int LA = BM / RR;          // 16-byte A loads per thread per step
     constexpr int LB = BN / RR;
     constexpr int L = LA + LB;
@@ -73,7 +77,19 @@ __global__ __launch_bounds__(64 * WGM * WGN) void igemm_nhwc_kernel(ConvArgs a, 
     // explicit vmcnt waits instead of draining every load before each read.
     __shared__ __attribute__((aligned(1024))) char st0[STAGE];
     __shared__ __attribute__((aligned(1024))) char st1[STAGE];
-    __shared__ __attribute__((aligned(1024))) char st2[NS == 3 ? STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) char st2[NS > 2 ? STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) char st3[NS > 3 ? STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) char st4[NS > 4 ? STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) char st5[NS > 5 ? STAGE : 16];
+    auto stage_ptr = [&](auto idx) -> char * {
+        constexpr int I = decltype(idx)::value;
+        if constexpr (I == 0) return st0;
+        else if constexpr (I == 1) return st1;
+        else if constexpr (I == 2) return st2;
+        else if constexpr (I == 3) return st3;
+        else if constexpr (I == 4) return st4;
+        else return st5;
+    };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -86,7 +102,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void igemm_nhwc_kernel(ConvArgs a, 
 
     const int H = a.H, W = a.W, Cin = a.Cin, kh = a.kh, kw = a.kw, K = a.K;
     const int OW = a.OW, OHW = a.OH * a.OW;
-    const int nsteps = (K + BK - 1) / BK;
+    // Split-K (gridDim.y slices): this workgroup takes K steps [s_begin, s_end).
+    const int nsteps_all = (K + BK - 1) / BK;
+    const int s_begin = blockIdx.y * steps_per_split;
+    const int nsteps = max(0, min(nsteps_all, s_begin + steps_per_split) - s_begin);
 
     const __amdgpu_buffer_rsrc_t rx =
         make_rsrc(a.x, (uint32_t)((size_t)a.N * H * W * Cin * sizeof(T)));
@@ -125,10 +144,17 @@ __global__ __launch_bounds__(64 * WGM * WGN) void igemm_nhwc_kernel(ConvArgs a, 
     }
 
     // k state of this thread's chunk at the next step to load
-    int ky = 0, kx = 0, ci = c * 8;
-    if constexpr (!TAP_INNER) {
-        int tap = ci / Cin;
-        ci -= tap * Cin;
+    int ky, kx, ci;
+    if constexpr (TAP_INNER) {
+        const int taps = kh * kw;
+        const int cb = s_begin / taps, tap = s_begin - cb * taps;
+        ky = tap / kw;
+        kx = tap - ky * kw;
+        ci = cb * BK + c * 8;
+    } else {
+        const int k = s_begin * BK + c * 8;
+        const int tap = k / Cin;
+        ci = k - tap * Cin;
         ky = tap / kw;
         kx = tap - ky * kw;
     }
@@ -205,36 +231,26 @@ __global__ __launch_bounds__(64 * WGM * WGN) void igemm_nhwc_kernel(ConvArgs a, 
         }
     };
 
-    // Ring of NS stages; step s lives in stage s % NS. One step: wait for this wave's
-    // loads of the step, barrier (every wave's have landed and every wave is done with
-    // the previous step's stage), matrix cores on this step, then refill the previous
-    // step's stage (so the matrix cores start right after the barrier).
-    auto step = [&](const char *cur, char *refill, bool live_refill) {
-        if constexpr (NS == 3)
-            wait_vmcnt<L>();
-        else
-            wait_vmcnt<0>();
+    // Ring of NS stages; step s lives in stage s % NS and is loaded NS-1 steps ahead.
+    // One step: wait for this wave's loads of the step (the NS-2 younger steps stay in
+    // flight), barrier (every wave's have landed and every wave is done with the
+    // previous step's stage), matrix cores on this step, then refill the previous
+    // step's stage with step s+NS-1 (so the matrix cores start right after the barrier).
+    auto step = [&](auto idx, int s) {
+        constexpr int I = decltype(idx)::value;
+        wait_vmcnt<(NS - 2) * L>();
         barrier_nofence();
-        compute(cur);
-        issue(refill, live_refill);
+        compute(stage_ptr(std::integral_constant<int, I>{}));
+        issue(stage_ptr(std::integral_constant<int, (I + NS - 1) % NS>{}), s + NS - 1 < nsteps);
     };
-    if constexpr (NS == 3) {
-        issue(st0, nsteps > 0);
-        issue(st1, nsteps > 1);
-        for (int s = 0; s < nsteps; s += 3) {
-            step(st0, st2, s + 2 < nsteps);
-            if (s + 1 >= nsteps) break;
-            step(st1, st0, s + 3 < nsteps);
-            if (s + 2 >= nsteps) break;
-            step(st2, st1, s + 4 < nsteps);
-        }
-    } else {
-        issue(st0, nsteps > 0);
-        for (int s = 0; s < nsteps; s += 2) {
-            step(st0, st1, s + 1 < nsteps);
-            if (s + 1 >= nsteps) break;
-            step(st1, st0, s + 2 < nsteps);
-        }
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+        (issue(stage_ptr(std::integral_constant<int, I>{}), I < nsteps), ...);
+    }(std::make_integer_sequence<int, NS - 1>{});
+    for (int s0 = 0; s0 < nsteps; s0 += NS) {
+        bool done = false;
+        [&]<int... I>(std::integer_sequence<int, I...>) {
+            ((done = done || s0 + I >= nsteps, done ? void() : step(std::integral_constant<int, I>{}, s0 + I)), ...);
+        }(std::make_integer_sequence<int, NS>{});
     }
     wait_vmcnt<0>();
     __syncthreads();
@@ -242,8 +258,76 @@ __global__ __launch_bounds__(64 * WGM * WGN) void igemm_nhwc_kernel(ConvArgs a, 
     // Epilogue, each wave over its own rows through its slice of stage 0 (LDS phase,
     // then global phase; see wave_epilogue_nhwc32).
     float *slice = reinterpret_cast<float *>(wave < SPS ? st0 + wave * SLICE : st1 + (wave - SPS) * SLICE);
+    float *part = gridDim.y > 1 ? partials + (size_t)blockIdx.y * a.M * a.Cout : nullptr;
     wave_epilogue_nhwc32<T, FM, FN, WLD>(acc, slice, a, m0 + wm * FM * 32, n0 + wn * WN, lane,
-                                         (uint32_t)((size_t)a.M * a.Cout * sizeof(T)));
+                                         (uint32_t)((size_t)a.M * a.Cout * sizeof(T)), part);
+}
+
+// Second pass of a split-K launch: per 16-byte output run, the fp32 slices are
+// added in slice order (so the result does not depend on scheduling), then bias,
+// residual and activation, and one rounding to T.
+template <typename T>
+__global__ __launch_bounds__(256) void splitk_epilogue_kernel(ConvArgs a, const float *partials,
+                                                              int splits) {
+    constexpr int VE = 16 / (int)sizeof(T);
+    const int runs_per_row = a.Cout / VE;
+    const long long total = (long long)a.M * runs_per_row;
+    const size_t slice = (size_t)a.M * a.Cout;
+    const T *__restrict__ res = static_cast<const T *>(a.res);
+    T *__restrict__ y = static_cast<T *>(a.y);
+    const bool has_res = res != nullptr, pre = a.res_before_act != 0;
+    for (long long it = blockIdx.x * 256ll + threadIdx.x; it < total; it += (long long)gridDim.x * 256) {
+        const int m = (int)(it / runs_per_row);
+        const int co = (int)(it - (long long)m * runs_per_row) * VE;
+        const size_t o = (size_t)m * a.Cout + co;
+        float v[VE];
+#pragma unroll
+        for (int e = 0; e < VE; e += 4) {
+            f32x4 t = *reinterpret_cast<const f32x4 *>(partials + o + e);
+            v[e] = t[0];
+            v[e + 1] = t[1];
+            v[e + 2] = t[2];
+            v[e + 3] = t[3];
+        }
+        for (int sidx = 1; sidx < splits; ++sidx) {
+#pragma unroll
+            for (int e = 0; e < VE; e += 4) {
+                f32x4 t = *reinterpret_cast<const f32x4 *>(partials + sidx * slice + o + e);
+                v[e] += t[0];
+                v[e + 1] += t[1];
+                v[e + 2] += t[2];
+                v[e + 3] += t[3];
+            }
+        }
+        float bv[VE], av[VE];
+        T rv[VE], out[VE];
+#pragma unroll
+        for (int e = 0; e < VE; ++e) {
+            bv[e] = a.bias ? a.bias[co + e] : 0.0f;
+            av[e] = a.alpha ? a.alpha[co + e] : 0.0f;
+        }
+        if (has_res) {
+            u32x4 t = *reinterpret_cast<const u32x4 *>(res + o);
+            __builtin_memcpy(rv, &t, 16);
+        }
+        switch (a.act) {
+        case CONV2D_ACT_RELU:
+            epilogue_vec<T, CONV2D_ACT_RELU, VE>(v, bv, av, rv, has_res, pre, out);
+            break;
+        case CONV2D_ACT_SILU:
+            epilogue_vec<T, CONV2D_ACT_SILU, VE>(v, bv, av, rv, has_res, pre, out);
+            break;
+        case CONV2D_ACT_PRELU:
+            epilogue_vec<T, CONV2D_ACT_PRELU, VE>(v, bv, av, rv, has_res, pre, out);
+            break;
+        default:
+            epilogue_vec<T, CONV2D_ACT_NONE, VE>(v, bv, av, rv, has_res, pre, out);
+            break;
+        }
+        u32x4 t;
+        __builtin_memcpy(&t, out, 16);
+        *reinterpret_cast<u32x4 *>(y + o) = t;
+    }
 }
 
 namespace {
@@ -261,34 +345,55 @@ constexpr TileCfg kTiles[NHWC_TILE_COUNT] = {
     {64, 64, 2, 2, 3},    // NHWC_TILE_64x64
     {128, 128, 2, 4, 3},  // NHWC_TILE_128x128_W8
     {128, 256, 2, 4, 2},  // NHWC_TILE_128x256_W8
+    {64, 64, 2, 2, 6},    // NHWC_TILE_64x64_D6
+    {128, 64, 2, 2, 5},   // NHWC_TILE_128x64_D5
+    {128, 128, 2, 4, 4},  // NHWC_TILE_128x128_W8_D4
+    {64, 128, 2, 2, 5},   // NHWC_TILE_64x128_D5
 };
 
 template <typename T, int TILE>
-hipError_t launch_t(const ConvArgs &a, const NhwcPlan &p, hipStream_t st) {
+hipError_t launch_t(const ConvArgs &a, const NhwcPlan &p, float *partials, hipStream_t st) {
     constexpr TileCfg c = kTiles[TILE];
     const long long tiles_m = (a.M + c.bm - 1) / c.bm;
     const int tiles_n = (a.Cout + c.bn - 1) / c.bn;
     if (tiles_m * tiles_n > 0x7fffffffll) return hipErrorInvalidValue;
-    dim3 grid((unsigned)(tiles_m * tiles_n));
+    const int splits = p.splits > 1 ? p.splits : 1;
+    const int nsteps = (a.K + 63) / 64;
+    const int per = (nsteps + splits - 1) / splits;
+    dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)splits);
     dim3 block(64 * c.wgm * c.wgn);
     if (p.tap_inner)
-        hipLaunchKernelGGL((igemm_nhwc_kernel<T, c.bm, c.bn, c.wgm, c.wgn, c.ns, true>), grid, block, 0, st, a, tiles_n);
+        hipLaunchKernelGGL((igemm_nhwc_kernel<T, c.bm, c.bn, c.wgm, c.wgn, c.ns, true>), grid, block, 0, st, a,
+                           tiles_n, per, partials);
     else
-        hipLaunchKernelGGL((igemm_nhwc_kernel<T, c.bm, c.bn, c.wgm, c.wgn, c.ns, false>), grid, block, 0, st, a, tiles_n);
+        hipLaunchKernelGGL((igemm_nhwc_kernel<T, c.bm, c.bn, c.wgm, c.wgn, c.ns, false>), grid, block, 0, st, a,
+                           tiles_n, per, partials);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || splits == 1) return e;
+    constexpr int VE = 16 / (int)sizeof(T);
+    long long runs = (long long)a.M * (a.Cout / VE);
+    long long blocks = (runs + 255) / 256;
+    if (blocks > 256 * 32) blocks = 256 * 32;
+    hipLaunchKernelGGL(splitk_epilogue_kernel<T>, dim3((unsigned)blocks), dim3(256), 0, st, a,
+                       (const float *)partials, splits);
     return hipGetLastError();
 }
 
 template <typename T>
-hipError_t launch_dtype(const ConvArgs &a, const NhwcPlan &p, hipStream_t st) {
+hipError_t launch_dtype(const ConvArgs &a, const NhwcPlan &p, float *partials, hipStream_t st) {
     switch (p.tile) {
-    case 0: return launch_t<T, 0>(a, p, st);
-    case 1: return launch_t<T, 1>(a, p, st);
-    case 2: return launch_t<T, 2>(a, p, st);
-    case 3: return launch_t<T, 3>(a, p, st);
-    case 4: return launch_t<T, 4>(a, p, st);
-    case 5: return launch_t<T, 5>(a, p, st);
-    case 6: return launch_t<T, 6>(a, p, st);
-    case 7: return launch_t<T, 7>(a, p, st);
+    case 0: return launch_t<T, 0>(a, p, partials, st);
+    case 1: return launch_t<T, 1>(a, p, partials, st);
+    case 2: return launch_t<T, 2>(a, p, partials, st);
+    case 3: return launch_t<T, 3>(a, p, partials, st);
+    case 4: return launch_t<T, 4>(a, p, partials, st);
+    case 5: return launch_t<T, 5>(a, p, partials, st);
+    case 6: return launch_t<T, 6>(a, p, partials, st);
+    case 7: return launch_t<T, 7>(a, p, partials, st);
+    case 8: return launch_t<T, 8>(a, p, partials, st);
+    case 9: return launch_t<T, 9>(a, p, partials, st);
+    case 10: return launch_t<T, 10>(a, p, partials, st);
+    case 11: return launch_t<T, 11>(a, p, partials, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -301,12 +406,13 @@ int nhwc_tile_waves(int tile) {
     return (tile >= 0 && tile < NHWC_TILE_COUNT) ? kTiles[tile].wgm * kTiles[tile].wgn : 0;
 }
 
-hipError_t launch_igemm_nhwc(const ConvArgs &a, int dtype, const NhwcPlan &p, hipStream_t st) {
+hipError_t launch_igemm_nhwc(const ConvArgs &a, int dtype, const NhwcPlan &p, float *partials,
+                             hipStream_t st) {
     switch (dtype) {
     case CONV2D_DTYPE_BF16:
-        return launch_dtype<bf16>(a, p, st);
+        return launch_dtype<bf16>(a, p, partials, st);
     case CONV2D_DTYPE_F16:
-        return launch_dtype<f16>(a, p, st);
+        return launch_dtype<f16>(a, p, partials, st);
     default:
         return hipErrorInvalidValue;
     }

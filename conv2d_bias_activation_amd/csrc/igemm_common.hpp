@@ -273,10 +273,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint3
 // out-of-range offsets the hardware ignores, so there are no per-element branches:
 // bias and slopes once per lane, then every residual load, then the math and the
 // 16-byte stores, all in flight together. `out_bytes` bounds y (and the residual).
+// With `part` non-null the wave stores its fp32 sums there instead ([M][Cout] fp32,
+// one K slice of a split-K launch) and applies nothing; a separate pass adds the
+// slices and runs the epilogue.
 template <typename T, int FM, int FN, int WLD>
 __device__ __forceinline__ void wave_epilogue_nhwc32(const f32x16 (&acc)[FM][FN], float *slice,
                                                      const ConvArgs &a, int mrow0, int ncol0,
-                                                     int lane, uint32_t out_bytes) {
+                                                     int lane, uint32_t out_bytes,
+                                                     float *part = nullptr) {
     constexpr int VE = 16 / (int)sizeof(T);
     constexpr int WN = FN * 32;
     constexpr int CPR = WN / VE;  // VE-wide runs per row
@@ -318,9 +322,26 @@ __device__ __forceinline__ void wave_epilogue_nhwc32(const f32x16 (&acc)[FM][FN]
             __builtin_amdgcn_wave_barrier();
         }
 
-    const bool has_res = a.res != nullptr, pre = a.res_before_act != 0;
     const int Cout = a.Cout;
     const int co = ncol0 + cc * VE;
+    if (part) {
+        // split-K slice: raw fp32 sums (only used when Cout % VE == 0)
+        const __amdgpu_buffer_rsrc_t rp = make_rsrc(part, (uint32_t)((size_t)a.M * Cout * 4));
+#pragma unroll
+        for (int q = 0; q < NH; ++q)
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                const int m = mrow0 + q * 16 + rsub + p * RPP;
+                const uint32_t o = (m < a.M && co < Cout) ? ((uint32_t)m * (uint32_t)Cout + (uint32_t)co) * 4u : kOOB;
+#pragma unroll
+                for (int e = 0; e < VE; e += 4) {
+                    u32x4 t = __builtin_bit_cast(u32x4, f32x4{v[q][p][e], v[q][p][e + 1], v[q][p][e + 2], v[q][p][e + 3]});
+                    __builtin_amdgcn_raw_buffer_store_b128(t, rp, (int)(o == kOOB ? kOOB : o + e * 4u), 0, 0);
+                }
+            }
+        return;
+    }
+    const bool has_res = a.res != nullptr, pre = a.res_before_act != 0;
     const bool vec = a.vec_out && (Cout % VE) == 0;
     const __amdgpu_buffer_rsrc_t rbias = make_rsrc(a.bias, a.bias ? (uint32_t)Cout * 4u : 0u);
     const __amdgpu_buffer_rsrc_t ralpha = make_rsrc(a.alpha, a.alpha ? (uint32_t)Cout * 4u : 0u);

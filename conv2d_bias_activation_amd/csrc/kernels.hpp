@@ -31,11 +31,16 @@ enum NhwcTile {
     NHWC_TILE_64x64 = 5,
     NHWC_TILE_128x128_W8 = 6,
     NHWC_TILE_128x256_W8 = 7,
-    NHWC_TILE_COUNT = 8,
+    NHWC_TILE_64x64_D6 = 8,
+    NHWC_TILE_128x64_D5 = 9,
+    NHWC_TILE_128x128_W8_D4 = 10,
+    NHWC_TILE_64x128_D5 = 11,
+    NHWC_TILE_COUNT = 12,
 };
 
 struct NhwcPlan {
     int tile;        // NhwcTile
+    int splits;      // K slices; > 1 needs splits * M * Cout floats of scratch
     bool tap_inner;  // Cin % 64 == 0: taps innermost in the K loop
 };
 
@@ -44,8 +49,11 @@ int nhwc_tile_bn(int tile);
 int nhwc_tile_waves(int tile);
 
 // Pipelined channel-last MFMA implicit GEMM (bf16/f16, Cin % 8 == 0, x, w and y
-// under 2 GiB, x and w 16-byte aligned).
-hipError_t launch_igemm_nhwc(const ConvArgs &a, int dtype, const NhwcPlan &p, hipStream_t st);
+// under 2 GiB, x and w 16-byte aligned). With p.splits > 1 (needs Cout % 8 == 0 and
+// 16-byte aligned y and residual), the GEMM writes fp32 partial sums of each K
+// slice to `partials` and a second kernel adds them and applies the epilogue.
+hipError_t launch_igemm_nhwc(const ConvArgs &a, int dtype, const NhwcPlan &p, float *partials,
+                             hipStream_t st);
 
 // Direct convolution on the vector ALUs for few input channels (the image stem):
 // one thread per output pixel and a block of output channels.

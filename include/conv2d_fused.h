@@ -22,8 +22,13 @@
  *  - Tensors are dense and contiguous. Every tensor must hold fewer than 2^31
  *    elements (CONV2D_EUNSUPPORTED otherwise).
  *  - The output may not overlap the input or the residual (CONV2D_EINVAL).
- *  - The library keeps no state between calls besides the last-error message,
- *    so calls on different streams may run concurrently.
+ *  - State kept between calls: the last-error message (per thread) and, per
+ *    device, one 64 MiB scratch buffer for split-K partial sums that the library
+ *    allocates on the first call that needs it and keeps until the process ends.
+ *    Split-K calls on one device all use that buffer: callers that run
+ *    conv2d_fused on several streams of one device at the same time must
+ *    serialise those calls. (Under HIP graph capture, make one call on each device
+ *    before capturing, so the allocation does not happen inside the capture.)
  */
 #ifndef CONV2D_FUSED_H
 #define CONV2D_FUSED_H
@@ -71,7 +76,8 @@ extern "C" {
                                    PRELU without alpha, output overlapping an input */
 #define CONV2D_EUNSUPPORTED (-2) /* valid but not handled (a tensor of 2^31 or more
                                    elements) */
-#define CONV2D_EHIP (-3)        /* the HIP runtime failed (no device, launch failure) */
+#define CONV2D_EHIP (-3)        /* the HIP runtime failed (no device, launch failure,
+                                   scratch allocation failure) */
 
 /*
  * y = epilogue(conv(x, w)) for one layer.
@@ -94,7 +100,10 @@ extern "C" {
  * stream   hipStream_t or NULL
  *
  * Accumulation is fp32 in any order; the result is rounded once to `dtype`.
- * The library allocates nothing.
+ * Layers with a deep K and few output tiles run as split-K: fp32 partial sums of
+ * K slices go to the library's per-device scratch buffer and a second kernel adds
+ * them in slice order and applies the epilogue (CONV2D_EHIP if the one-time
+ * scratch allocation fails).
  */
 int conv2d_fused(const void *x, const void *w, const float *bias, const float *alpha,
                  const void *residual, void *y, int N, int H, int W, int Cin, int Cout, int kh,
@@ -141,7 +150,7 @@ int conv2d_check_args(const void *x, const void *w, const float *bias, const flo
 
 /* Host-only: writes into buf (capacity cap bytes, NUL-terminated) the name of the
  * kernel variant conv2d_fused would launch for this shape, e.g.
- * "igemm_nhwc_pipe_tapinner bf16 128x128w8". Returns the name's length, or a
+ * "igemm_nhwc_pipe_tapinner bf16 128x128w8 splitk=1". Returns the name's length, or a
  * negative CONV2D_E* code for invalid arguments. */
 int conv2d_plan(int N, int H, int W, int Cin, int Cout, int kh, int kw, int stride, int pad,
                 int act, int layout, int dtype, char *buf, int cap);

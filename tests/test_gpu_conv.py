@@ -58,7 +58,10 @@ SWEEP = [
     (1, 2, 3, 16, 8, 3, 2, 2, "relu", None, "nhwc", "f16"),     # padding wider than input
     (4, 7, 9, 8, 1, 3, 1, 1, "silu", None, "nhwc", "bf16"),     # one output channel
     (1, 11, 13, 1, 5, 3, 1, 1, "relu", None, "nchw", "bf16"),   # one input channel
-    # few output tiles, deep K
+    # few output tiles, deep K (split-K: fp32 slices, then a second pass for the epilogue)
+    (1, 10, 10, 512, 512, 3, 1, 1, "relu", "pre", "nhwc", "bf16"),
+    (2, 7, 9, 384, 64, 3, 1, 1, "prelu", "post", "nhwc", "f16"),
+    (1, 9, 11, 512, 200, 3, 1, 1, "silu", None, "nhwc", "bf16"),
     (1, 10, 10, 256, 256, 3, 1, 1, "relu", "pre", "nhwc", "bf16"),
     (2, 9, 7, 72, 200, 3, 2, 1, "silu", "post", "nhwc", "f16"),  # Cin % 64 != 0, K tail
     (1, 6, 6, 512, 64, 3, 1, 1, "none", None, "nhwc", "bf16"),
@@ -248,10 +251,12 @@ def test_conv5_resnet18d_end_to_end_full():
 
 
 def test_repeatable():
-    """Every output is one fixed-order fp32 sum: repeated calls agree bit for bit."""
+    """Every output is one fixed-order fp32 sum (split-K slices are added in slice
+    order): repeated calls agree bit for bit."""
     x, spec, r = wl.random_conv_case(11, n=1, h=20, w=20, cin=512, cout=512, k=3, stride=1, pad=1,
                                      act="relu", layout="nhwc", dtype="bf16", residual=True,
                                      res_before_act=True)
+    assert "splitk=1" not in c2d.plan(1, 20, 20, 512, 512, 3, 3, 1, 1, 0x101, 0, 1)
     ys = [_gpu_conv(x, spec, r, "nhwc") for _ in range(4)]
     torch.cuda.synchronize()
     for y in ys[1:]:
