@@ -29,6 +29,15 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16/f16 matrix peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
+# name -> (builder, config description)
+WORKLOADS = {
+    "resnet18d": ("conv5_resnet18d", "resnet18d_backbone_4x640x640_nhwc_bf16"),
+    "ifnet": ("conv4_ifnet_block", "ifnet_convblock_8x_conv3x3_240ch_68x120_nchw_f16"),
+    "pointwise": ("conv3_pointwise", "conv1x1_512to256_relu_4x80x80_nhwc_bf16"),
+    "stem_bf16": ("conv2_stem_bf16", "stem_conv3x3s2_3to32_silu_maxpool_1x640x640_nhwc_bf16"),
+    "stem_f32": ("conv2_stem", "stem_conv3x3s2_3to32_silu_maxpool_1x640x640_nhwc_f32"),
+}
+
 
 def parse():
     p = argparse.ArgumentParser()
@@ -38,8 +47,10 @@ def parse():
     p.add_argument("--mode", choices=["graph", "eager"], default="graph",
                    help="replay one captured HIP graph per step, or launch eagerly")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--layer-reps", type=int, default=10)
+    p.add_argument("--layer-reps", type=int, default=20)
     p.add_argument("--layers-out", default=None, help="write per-layer timings (JSON) here")
+    p.add_argument("--workload", choices=list(WORKLOADS), default="resnet18d",
+                   help="the backbone (default; the headline) or one of the other layer configs")
     return p.parse_args()
 
 
@@ -56,30 +67,39 @@ class Net:
         self.work = work
         self.t = {"x": work.x.to(dev)}
         self.layers = []
-        dt = c2d.DTYPE_BF16
+        dt = {"f32": c2d.DTYPE_F32, "bf16": c2d.DTYPE_BF16, "f16": c2d.DTYPE_F16}[work.dtype]
+        esz = 4 if work.dtype == "f32" else 2
+        nchw = work.layout == "nchw"
+        lay = c2d.LAYOUT_NCHW if nchw else c2d.LAYOUT_NHWC
         for spec in work.layers:
             src = self.t[spec.src]
-            n, h, w, c = src.shape
+            if nchw:
+                n, c, h, w = src.shape
+            else:
+                n, h, w, c = src.shape
             if hasattr(spec, "cin"):
                 oh = c2d.out_dim(h, spec.k, spec.stride, spec.pad)
                 ow = c2d.out_dim(w, spec.k, spec.stride, spec.pad)
-                out = torch.empty((n, oh, ow, spec.cout), dtype=src.dtype, device=dev)
+                oshape = (n, spec.cout, oh, ow) if nchw else (n, oh, ow, spec.cout)
+                out = torch.empty(oshape, dtype=src.dtype, device=dev)
                 wdev = spec.w.to(dev)
                 bdev = spec.bias.to(dev)
+                adev = spec.alpha.to(dev) if spec.alpha is not None else None
                 res = self.t[spec.res] if spec.res else None
                 act = {"none": 0, "relu": 1, "silu": 2, "prelu": 3}[spec.act]
                 act |= c2d.RES_BEFORE_ACT if spec.res_before_act else 0
-                keep = (wdev, bdev)
+                keep = (wdev, bdev, adev)
                 args = [ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(wdev.data_ptr()),
-                        ctypes.c_void_p(bdev.data_ptr()), None,
+                        ctypes.c_void_p(bdev.data_ptr()),
+                        ctypes.c_void_p(adev.data_ptr()) if adev is not None else None,
                         ctypes.c_void_p(res.data_ptr()) if res is not None else None,
                         ctypes.c_void_p(out.data_ptr()), n, h, w, c, spec.cout, spec.k, spec.k,
-                        spec.stride, spec.pad, act, c2d.LAYOUT_NHWC, dt]
+                        spec.stride, spec.pad, act, lay, dt]
                 flops = 2 * n * oh * ow * spec.cout * c * spec.k * spec.k
-                nbytes = 2 * (src.numel() + spec.w.numel() + out.numel() +
-                              (res.numel() if res is not None else 0)) + 4 * spec.cout
+                nbytes = esz * (src.numel() + spec.w.numel() + out.numel() +
+                                (res.numel() if res is not None else 0)) + 4 * spec.cout * (2 if adev is not None else 1)
                 plan = c2d.plan(n, h, w, c, spec.cout, spec.k, spec.k, spec.stride, spec.pad, act,
-                                c2d.LAYOUT_NHWC, dt)
+                                lay, dt)
                 self.layers.append(dict(name=spec.name, fn=self.lib.conv2d_fused, args=args,
                                         flops=flops, bytes=nbytes, plan=plan, keep=keep))
             else:
@@ -89,11 +109,12 @@ class Net:
                 else:
                     oh, ow, fn = h // 2, w // 2, self.lib.avgpool2x2
                     plan = "avgpool2x2"
-                out = torch.empty((n, oh, ow, c), dtype=src.dtype, device=dev)
+                out = torch.empty((n, c, oh, ow) if nchw else (n, oh, ow, c), dtype=src.dtype,
+                                  device=dev)
                 args = [ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(out.data_ptr()), n, h, w,
-                        c, c2d.LAYOUT_NHWC, dt]
+                        c, lay, dt]
                 self.layers.append(dict(name=spec.name, fn=fn, args=args, flops=0,
-                                        bytes=2 * (src.numel() + out.numel()), plan=plan, keep=()))
+                                        bytes=esz * (src.numel() + out.numel()), plan=plan, keep=()))
             self.t[spec.out] = out
         self.flops = sum(L["flops"] for L in self.layers)
         self.out_name = work.layers[-1].out
@@ -144,22 +165,22 @@ def time_steps(torch, net, steps, warmup, mode):
 
 
 def time_layers(torch, net, reps):
-    """Per-layer average durations (ms) from events between back-to-back launches."""
+    """Per-layer average launch durations (ms): each layer is launched `reps` times back to
+    back between one pair of HIP events on the launch stream, while a preceding spin keeps
+    the GPU busy until the host has queued them, so no launch or event gap is counted."""
     stream = torch.cuda.current_stream()
     h = ctypes.c_void_p(stream.cuda_stream)
-    n = len(net.layers)
-    tot = [0.0] * n
-    for _ in range(reps):
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
-        prefill(torch, ms=10.0)
-        ev[0].record(stream)
-        for i, L in enumerate(net.layers):
+    out = []
+    for L in net.layers:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        prefill(torch, ms=2.0)
+        e0.record(stream)
+        for _ in range(reps):
             net.run_layer(L, h)
-            ev[i + 1].record(stream)
+        e1.record(stream)
         torch.cuda.synchronize()
-        for i in range(n):
-            tot[i] += ev[i].elapsed_time(ev[i + 1])
-    return [t / reps for t in tot]
+        out.append(e0.elapsed_time(e1) / reps)
+    return out
 
 
 def kernel_source_hash():
@@ -189,36 +210,42 @@ def measured_traffic(plan, launches_bytes):
     return k.get("bytes_per_launch")
 
 
-def cpu_baseline(work):
-    """The oracle (fp64 direct loops, all host threads) on one image of the same backbone."""
+def cpu_baseline(min_seconds=10.0):
+    """The oracle (fp64 direct loops, all host threads) on a bounded sample of the same
+    backbone: one-image forwards (the full 22-conv chain at 640x640, pools included),
+    repeated until at least `min_seconds` of CPU work."""
     import numpy as np
+    import torch
 
     import oracle
     import workloads as wl
 
     one = wl.conv5_resnet18d(n=1)
-    t = {"x": one.x.to(__import__("torch").float64).numpy()}
     flops = 0
+    runs = 0
     t0 = time.perf_counter()
-    for spec in one.layers:
-        src = t[spec.src]
-        if isinstance(spec, wl.ConvSpec):
-            r = t[spec.res] if spec.res else None
-            y = oracle.conv2d(src, spec.w.double().numpy(), spec.bias.double().numpy(), None, r,
-                              stride=spec.stride, pad=spec.pad, act=spec.act,
-                              res_before_act=spec.res_before_act)
-            n, h, w, c = src.shape
-            flops += 2 * n * y.shape[1] * y.shape[2] * spec.cout * c * spec.k * spec.k
-            t[spec.out] = oracle.quantize(y, "bf16")
-        elif spec.kind == "max":
-            t[spec.out] = oracle.maxpool3x3s2(src)
-        else:
-            t[spec.out] = oracle.quantize(oracle.avgpool2x2(src).astype(np.float64), "bf16")
+    while runs == 0 or time.perf_counter() - t0 < min_seconds:
+        t = {"x": one.x.to(torch.float64).numpy()}
+        for spec in one.layers:
+            src = t[spec.src]
+            if isinstance(spec, wl.ConvSpec):
+                r = t[spec.res] if spec.res else None
+                y = oracle.conv2d(src, spec.w.double().numpy(), spec.bias.double().numpy(), None, r,
+                                  stride=spec.stride, pad=spec.pad, act=spec.act,
+                                  res_before_act=spec.res_before_act)
+                n, h, w, c = src.shape
+                flops += 2 * n * y.shape[1] * y.shape[2] * spec.cout * c * spec.k * spec.k
+                t[spec.out] = oracle.quantize(y, "bf16")
+            elif spec.kind == "max":
+                t[spec.out] = oracle.maxpool3x3s2(src)
+            else:
+                t[spec.out] = oracle.quantize(oracle.avgpool2x2(src).astype(np.float64), "bf16")
+        runs += 1
     dt = time.perf_counter() - t0
     return dict(value=round(flops / dt / 1e12, 6), unit="TFLOP/s", cores=oracle.threads(),
                 kind="oracle",
-                sample=f"one of the 4 images: full 22-conv forward in fp64 ({flops / 1e9:.2f} GFLOP, "
-                       f"{dt:.1f} s)")
+                sample=f"{runs} one-image forwards of the backbone (640x640, 22 convs + 4 pools) "
+                       f"in fp64: {flops / 1e9:.1f} GFLOP in {dt:.1f} s")
 
 
 def main():
@@ -233,7 +260,8 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    work = wl.conv5_resnet18d()
+    builder, config_name = WORKLOADS[args.workload]
+    work = getattr(wl, builder)()
     net = Net(work, dev)
     ms, graph = time_steps(torch, net, args.steps, args.warmup, args.mode)
     value = net.flops / (ms * 1e-3) / 1e12
@@ -246,7 +274,13 @@ def main():
         g["flops"] += L["flops"]
         g["bytes"] += L["bytes"]
         g["launches"] += 1
-    dom_plan = max(groups, key=lambda k: groups[k]["ms"])
+    # The dominant kernel: the single-kernel launch group with the most time per step
+    # (a split-K layer runs two kernels per call, a channel-first layer three, so
+    # neither group is one kernel).
+    single = [k for k in groups if ("splitk=1" in k or "splitk" not in k) and "+" not in k]
+    if not single:
+        single = list(groups)
+    dom_plan = max(single, key=lambda k: groups[k]["ms"])
     g = groups[dom_plan]
     avg_ms = g["ms"] / g["launches"]
     if g["flops"] > 0:
@@ -275,7 +309,7 @@ def main():
         with open(args.layers_out, "w") as f:
             json.dump(dict(step_ms=ms, sum_layer_ms=sum(layer_ms), layers=rows), f, indent=1)
 
-    cpu = None if args.no_cpu_baseline else cpu_baseline(work)
+    cpu = None if (args.no_cpu_baseline or args.workload != "resnet18d") else cpu_baseline()
     line = {
         "metric": "conv TFLOP/s (2*N*OH*OW*Cout*Cin*kh*kw) and % of MFMA/HBM roofline, 1 GPU",
         "value": round(value, 3),
@@ -287,11 +321,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded PCG64: x~U[0,1] image, He-normal weights, bias~U[-0.1,0.1])",
-        "config": {"workload": "resnet18d_backbone_4x640x640_nhwc_bf16", "global_batch": 4,
-                   "image": "640x640x3", "convs": 22, "pools": 4, "gflop_per_step": round(net.flops / 1e9, 3),
-                   "launch": args.mode},
+        "dtype": work.dtype,
+        "data": "synthetic: seeded PCG64 tensors with the shapes and value ranges of the pages' layers (workloads/inputs.py)",
+        "config": {"workload": config_name, "global_batch": int(work.x.shape[0]),
+                   "convs": sum(1 for L in net.layers if L["flops"]),
+                   "pools": sum(1 for L in net.layers if not L["flops"]),
+                   "gflop_per_step": round(net.flops / 1e9, 3), "launch": args.mode},
         "roofline": roof,
         "cpu_baseline": cpu,
     }

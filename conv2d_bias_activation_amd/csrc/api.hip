@@ -127,7 +127,7 @@ int check_conv(const void *x, const void *w, const float *alpha, const void *res
     return CONV2D_OK;
 }
 
-enum Family { FAM_DIRECT = 0, FAM_IGEMM = 1, FAM_NHWC = 2 };
+enum Family { FAM_DIRECT = 0, FAM_IGEMM = 1, FAM_NHWC = 2, FAM_NCHW_VIA_NHWC = 3 };
 
 struct Plan {
     int family;
@@ -135,8 +135,9 @@ struct Plan {
     NhwcPlan nh;
 };
 
-// Split-K scratch: fp32 partial sums, one buffer per device, allocated on the first
-// split-K call and kept until the process ends.
+// Library scratch, one buffer per device, allocated on the first call that needs it
+// and kept until the process ends: split-K fp32 partial sums, or the channel-last
+// copies of a channel-first layer's input and weight.
 constexpr size_t kScratchBytes = 64ull << 20;
 constexpr int kMaxDevices = 64;
 float *g_scratch[kMaxDevices];
@@ -210,6 +211,8 @@ const char *nhwc_tile_name(int t) {
 // layer shapes): 8-wave 128x128 tiles while there are enough of them to occupy the
 // GPU, 64x64 tiles for the small-M deep layers (more workgroups in flight beat
 // bigger tiles there), 128x256 for wide pointwise layers, 128x64 for narrow outputs.
+size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
+
 NhwcPlan plan_nhwc(const ConvArgs &a) {
     NhwcPlan p{};
     auto tiles = [&](int bm, int bn) {
@@ -253,6 +256,16 @@ Plan make_plan(const ConvArgs &a, int layout, int dtype) {
         p.nh = plan_nhwc(a);
         return p;
     }
+    // Channel-first 16-bit layers: channel-last copies of x and w in the scratch, the
+    // channel-last kernel, and an epilogue that writes the channel-first output.
+    if (layout == CONV2D_LAYOUT_NCHW && dtype != CONV2D_DTYPE_F32 && (a.Cin % 8) == 0 &&
+        round256((size_t)xbytes) + round256((size_t)wbytes) <= kScratchBytes && ybytes < (1ll << 31)) {
+        p.family = FAM_NCHW_VIA_NHWC;
+        p.nh = plan_nhwc(a);
+        p.nh.splits = 1;
+        p.nh.nchw_out = true;
+        return p;
+    }
     p.family = FAM_IGEMM;
     p.ig.nchw = layout == CONV2D_LAYOUT_NCHW;
     p.ig.avec = !p.ig.nchw && (a.Cin % ve) == 0 && aligned16(a.x) && aligned16(a.w);
@@ -266,8 +279,9 @@ int describe(const Plan &p, int layout, int dtype, char *buf, int cap) {
     if (p.family == FAM_DIRECT) {
         snprintf(tmp, sizeof tmp, "direct_%s %s cob32", layout == CONV2D_LAYOUT_NCHW ? "nchw" : "nhwc",
                  dtype_name(dtype));
-    } else if (p.family == FAM_NHWC) {
-        snprintf(tmp, sizeof tmp, "igemm_nhwc_pipe%s %s %s splitk=%d", p.nh.tap_inner ? "_tapinner" : "",
+    } else if (p.family == FAM_NHWC || p.family == FAM_NCHW_VIA_NHWC) {
+        snprintf(tmp, sizeof tmp, "%sigemm_nhwc_pipe%s %s %s splitk=%d",
+                 p.family == FAM_NCHW_VIA_NHWC ? "to_nhwc+" : "", p.nh.tap_inner ? "_tapinner" : "",
                  dtype_name(dtype), nhwc_tile_name(p.nh.tile), p.nh.splits);
     } else {
         snprintf(tmp, sizeof tmp, "igemm_%s%s %s %s", p.ig.nchw ? "nchw" : "nhwc",
@@ -358,6 +372,20 @@ int conv2d_fused(const void *x, const void *w, const float *bias, const float *a
             if (rc) return rc;
         }
         e = launch_igemm_nhwc(a, dtype, p.nh, scratch, st);
+    } else if (p.family == FAM_NCHW_VIA_NHWC) {
+        float *scratch = nullptr;
+        rc = get_scratch(&scratch);
+        if (rc) return rc;
+        const int eb = dtype_bytes(dtype);
+        char *xs = reinterpret_cast<char *>(scratch);
+        char *ws = xs + round256((size_t)a.N * a.H * a.W * a.Cin * eb);
+        e = launch_to_channel_last(a.x, xs, a.N, a.Cin, a.H * a.W, a.w, ws, a.Cout, a.kh * a.kw, dtype, st);
+        if (e == hipSuccess) {
+            ConvArgs b = a;
+            b.x = xs;
+            b.w = ws;
+            e = launch_igemm_nhwc(b, dtype, p.nh, nullptr, st);
+        }
     } else {
         e = launch_igemm(a, dtype, p.ig, st);
     }

@@ -50,7 +50,8 @@ __device__ __forceinline__ void barrier_nofence() {
     asm volatile("" ::: "memory");
 }
 
-template <typename T, int BM, int BN, int WGM, int WGN, int NS, bool TAP_INNER>
+template <typename T, int BM, int BN, int WGM, int WGN, int NS, bool TAP_INNER, bool SPLIT,
+          bool NCHW_OUT>
 __global__ __launch_bounds__(64 * WGM * WGN) void igemm_nhwc_kernel(ConvArgs a, int tiles_n,
                                                                    int steps_per_split,
                                                                    float *partials) {
@@ -258,9 +259,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void igemm_nhwc_kernel(ConvArgs a, 
     // Epilogue, each wave over its own rows through its slice of stage 0 (LDS phase,
     // then global phase; see wave_epilogue_nhwc32).
     float *slice = reinterpret_cast<float *>(wave < SPS ? st0 + wave * SLICE : st1 + (wave - SPS) * SLICE);
-    float *part = gridDim.y > 1 ? partials + (size_t)blockIdx.y * a.M * a.Cout : nullptr;
-    wave_epilogue_nhwc32<T, FM, FN, WLD>(acc, slice, a, m0 + wm * FM * 32, n0 + wn * WN, lane,
-                                         (uint32_t)((size_t)a.M * a.Cout * sizeof(T)), part);
+    const uint32_t out_bytes = (uint32_t)((size_t)a.M * a.Cout * sizeof(T));
+    if constexpr (NCHW_OUT) {
+        wave_epilogue_nchw32<T, FM, FN, WLD>(acc, slice, a, m0 + wm * FM * 32, n0 + wn * WN, lane, out_bytes);
+    } else {
+        float *part = SPLIT ? partials + (size_t)blockIdx.y * a.M * a.Cout : nullptr;
+        wave_epilogue_nhwc32<T, FM, FN, WLD>(acc, slice, a, m0 + wm * FM * 32, n0 + wn * WN, lane, out_bytes,
+                                             part);
+    }
 }
 
 // Second pass of a split-K launch: per 16-byte output run, the fp32 slices are
@@ -362,12 +368,29 @@ hipError_t launch_t(const ConvArgs &a, const NhwcPlan &p, float *partials, hipSt
     const int per = (nsteps + splits - 1) / splits;
     dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)splits);
     dim3 block(64 * c.wgm * c.wgn);
-    if (p.tap_inner)
-        hipLaunchKernelGGL((igemm_nhwc_kernel<T, c.bm, c.bn, c.wgm, c.wgn, c.ns, true>), grid, block, 0, st, a,
-                           tiles_n, per, partials);
-    else
-        hipLaunchKernelGGL((igemm_nhwc_kernel<T, c.bm, c.bn, c.wgm, c.wgn, c.ns, false>), grid, block, 0, st, a,
-                           tiles_n, per, partials);
+    if (p.nchw_out) {
+        if (splits > 1) return hipErrorInvalidValue;  // split-K writes channel-last only
+        if (p.tap_inner)
+            hipLaunchKernelGGL((igemm_nhwc_kernel<T, c.bm, c.bn, c.wgm, c.wgn, c.ns, true, false, true>), grid,
+                               block, 0, st, a, tiles_n, per, partials);
+        else
+            hipLaunchKernelGGL((igemm_nhwc_kernel<T, c.bm, c.bn, c.wgm, c.wgn, c.ns, false, false, true>), grid,
+                               block, 0, st, a, tiles_n, per, partials);
+    } else if (p.tap_inner) {
+        if (splits > 1)
+            hipLaunchKernelGGL((igemm_nhwc_kernel<T, c.bm, c.bn, c.wgm, c.wgn, c.ns, true, true, false>), grid,
+                               block, 0, st, a, tiles_n, per, partials);
+        else
+            hipLaunchKernelGGL((igemm_nhwc_kernel<T, c.bm, c.bn, c.wgm, c.wgn, c.ns, true, false, false>), grid,
+                               block, 0, st, a, tiles_n, per, partials);
+    } else {
+        if (splits > 1)
+            hipLaunchKernelGGL((igemm_nhwc_kernel<T, c.bm, c.bn, c.wgm, c.wgn, c.ns, false, true, false>), grid,
+                               block, 0, st, a, tiles_n, per, partials);
+        else
+            hipLaunchKernelGGL((igemm_nhwc_kernel<T, c.bm, c.bn, c.wgm, c.wgn, c.ns, false, false, false>), grid,
+                               block, 0, st, a, tiles_n, per, partials);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || splits == 1) return e;
     constexpr int VE = 16 / (int)sizeof(T);

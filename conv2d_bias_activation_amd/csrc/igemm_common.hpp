@@ -421,4 +421,133 @@ __device__ __forceinline__ void wave_epilogue_nhwc32(const f32x16 (&acc)[FM][FN]
     }
 }
 
+// The same epilogue for channel-first output (y and the residual are [N][Cout][OH*OW]):
+// each lane reads back one output channel over 8 consecutive pixels, which are one
+// 16-byte run of an output plane when OH*OW is a multiple of 8 (runs start at pixels
+// that are multiples of 8, so they never cross a plane). Otherwise every element is
+// addressed on its own.
+template <typename T, int FM, int FN, int WLD>
+__device__ __forceinline__ void wave_epilogue_nchw32(const f32x16 (&acc)[FM][FN], float *slice,
+                                                     const ConvArgs &a, int mrow0, int ncol0,
+                                                     int lane, uint32_t out_bytes) {
+    static_assert(sizeof(T) == 2, "16-bit storage");
+    constexpr int WN = FN * 32;
+    constexpr int NH = FM * 2;
+    const int col = lane & 31, hi = lane >> 5;
+    float v[NH][FN][8];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int g = 0; g < 2; ++g)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        slice[(g * 8 + hi * 4 + r) * WLD + j * 32 + col] = acc[i][j][(2 * h + g) * 4 + r];
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int t = 0; t < FN; ++t) {
+                const int idx = lane + 64 * t, c = idx % WN, rg = idx / WN;
+#pragma unroll
+                for (int r = 0; r < 8; ++r) v[i * 2 + h][t][r] = slice[(rg * 8 + r) * WLD + c];
+            }
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            __builtin_amdgcn_wave_barrier();
+        }
+
+    const bool has_res = a.res != nullptr, pre = a.res_before_act != 0;
+    const int Cout = a.Cout, OHW = a.OH * a.OW;
+    const bool vec = a.vec_out && (OHW % 8) == 0;
+    const __amdgpu_buffer_rsrc_t rbias = make_rsrc(a.bias, a.bias ? (uint32_t)Cout * 4u : 0u);
+    const __amdgpu_buffer_rsrc_t ralpha = make_rsrc(a.alpha, a.alpha ? (uint32_t)Cout * 4u : 0u);
+    const __amdgpu_buffer_rsrc_t rres = make_rsrc(a.res, has_res ? out_bytes : 0u);
+    const __amdgpu_buffer_rsrc_t ry = make_rsrc(a.y, out_bytes);
+    float bv[FN], av[FN];
+    uint32_t off[NH][FN];
+    T rv[NH][FN][8];
+#pragma unroll
+    for (int t = 0; t < FN; ++t) {
+        const int idx = lane + 64 * t, co = ncol0 + idx % WN;
+        const uint32_t bo = co < Cout ? (uint32_t)co * 4u : kOOB;
+        bv[t] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rbias, (int)bo, 0, 0));
+        av[t] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ralpha, (int)bo, 0, 0));
+    }
+#pragma unroll
+    for (int q = 0; q < NH; ++q)
+#pragma unroll
+        for (int t = 0; t < FN; ++t) {
+            const int idx = lane + 64 * t, co = ncol0 + idx % WN;
+            const int m = mrow0 + q * 16 + (idx / WN) * 8;
+            const int n = m / OHW, pix = m - n * OHW;
+            off[q][t] = (m < a.M && co < Cout)
+                            ? (((uint32_t)n * (uint32_t)Cout + (uint32_t)co) * (uint32_t)OHW + (uint32_t)pix) * 2u
+                            : kOOB;
+            if (vec) {
+                u32x4 tt = __builtin_amdgcn_raw_buffer_load_b128(rres, (int)off[q][t], 0, 0);
+                __builtin_memcpy(rv[q][t], &tt, 16);
+            } else {
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    const int mr = m + r, nr = mr / OHW, pr = mr - nr * OHW;
+                    const uint32_t o = (mr < a.M && co < Cout)
+                        ? (((uint32_t)nr * (uint32_t)Cout + (uint32_t)co) * (uint32_t)OHW + (uint32_t)pr) * 2u
+                        : kOOB;
+                    uint16_t u = __builtin_amdgcn_raw_buffer_load_b16(rres, (int)o, 0, 0);
+                    __builtin_memcpy(&rv[q][t][r], &u, 2);
+                }
+            }
+        }
+    auto finish = [&](auto act_tag) {
+        constexpr int ACT = decltype(act_tag)::value;
+#pragma unroll
+        for (int q = 0; q < NH; ++q)
+#pragma unroll
+            for (int t = 0; t < FN; ++t) {
+                float b8[8], a8[8];
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    b8[r] = bv[t];
+                    a8[r] = av[t];
+                }
+                T out[8];
+                epilogue_vec<T, ACT, 8>(v[q][t], b8, a8, rv[q][t], has_res, pre, out);
+                if (vec) {
+                    u32x4 tt;
+                    __builtin_memcpy(&tt, out, 16);
+                    __builtin_amdgcn_raw_buffer_store_b128(tt, ry, (int)off[q][t], 0, 0);
+                } else {
+                    const int idx = lane + 64 * t, co = ncol0 + idx % WN;
+                    const int m = mrow0 + q * 16 + (idx / WN) * 8;
+#pragma unroll
+                    for (int r = 0; r < 8; ++r) {
+                        const int mr = m + r, nr = mr / OHW, pr = mr - nr * OHW;
+                        const uint32_t o = (mr < a.M && co < Cout)
+                            ? (((uint32_t)nr * (uint32_t)Cout + (uint32_t)co) * (uint32_t)OHW + (uint32_t)pr) * 2u
+                            : kOOB;
+                        uint16_t u;
+                        __builtin_memcpy(&u, &out[r], 2);
+                        __builtin_amdgcn_raw_buffer_store_b16(u, ry, (int)o, 0, 0);
+                    }
+                }
+            }
+    };
+    switch (a.act) {
+    case CONV2D_ACT_RELU:
+        finish(std::integral_constant<int, CONV2D_ACT_RELU>{});
+        break;
+    case CONV2D_ACT_SILU:
+        finish(std::integral_constant<int, CONV2D_ACT_SILU>{});
+        break;
+    case CONV2D_ACT_PRELU:
+        finish(std::integral_constant<int, CONV2D_ACT_PRELU>{});
+        break;
+    default:
+        finish(std::integral_constant<int, CONV2D_ACT_NONE>{});
+        break;
+    }
+}
+
 }  // namespace c2d

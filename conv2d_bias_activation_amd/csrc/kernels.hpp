@@ -42,7 +42,12 @@ struct NhwcPlan {
     int tile;        // NhwcTile
     int splits;      // K slices; > 1 needs splits * M * Cout floats of scratch
     bool tap_inner;  // Cin % 64 == 0: taps innermost in the K loop
+    bool nchw_out;   // y and the residual are channel-first (x and w still channel-last)
 };
+
+// Channel-first input and OIHW weight to channel-last copies (16-bit types).
+hipError_t launch_to_channel_last(const void *x, void *x_nhwc, int N, int C, int HW, const void *w,
+                                  void *w_ohwi, int Cout, int taps, int dtype, hipStream_t st);
 
 int nhwc_tile_bm(int tile);
 int nhwc_tile_bn(int tile);

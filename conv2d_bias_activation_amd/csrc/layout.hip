@@ -1,0 +1,74 @@
+// Layout conversion for channel-first layers: the input map NCHW -> NHWC and the
+// weight OIHW -> OHWI, so that a channel-first call can run on the channel-last
+// matrix-core kernel (whose patch rows and weight rows are then contiguous channel
+// runs). Both are pure data movement.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace c2d {
+
+// One 64-channel x 64-pixel tile per 256-thread block: rows of pixels are read
+// along the NCHW plane, written to LDS, and leave as rows of channels.
+template <typename T>
+__global__ __launch_bounds__(256) void nchw_to_nhwc_kernel(const T *__restrict__ x, T *__restrict__ y,
+                                                           int C, int HW) {
+    __shared__ T tile[64][64 + 2];
+    const int n = blockIdx.z;
+    const int c0 = blockIdx.y * 64, p0 = blockIdx.x * 64;
+    const T *xn = x + (size_t)n * C * HW;
+    T *yn = y + (size_t)n * HW * C;
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    for (int c = ty; c < 64; c += 4) {
+        const int cc = c0 + c, pp = p0 + tx;
+        tile[c][tx] = (cc < C && pp < HW) ? xn[(size_t)cc * HW + pp] : from_f32<T>(0.0f);
+    }
+    __syncthreads();
+    for (int p = ty; p < 64; p += 4) {
+        const int pp = p0 + p, cc = c0 + tx;
+        if (pp < HW && cc < C) yn[(size_t)pp * C + cc] = tile[tx][p];
+    }
+}
+
+// w[co][ci][t] -> w2[co][t][ci], t = ky*kw + kx; one thread per element.
+template <typename T>
+__global__ __launch_bounds__(256) void oihw_to_ohwi_kernel(const T *__restrict__ w, T *__restrict__ w2,
+                                                           int Cout, int Cin, int taps) {
+    const long long total = (long long)Cout * Cin * taps;
+    for (long long i = blockIdx.x * 256ll + threadIdx.x; i < total; i += (long long)gridDim.x * 256) {
+        const int ci = (int)(i % Cin);
+        const long long r = i / Cin;
+        const int t = (int)(r % taps);
+        const int co = (int)(r / taps);
+        w2[i] = w[((size_t)co * Cin + ci) * taps + t];
+    }
+}
+
+template <typename T>
+static hipError_t to_nhwc_t(const void *x, void *y, int N, int C, int HW, const void *w, void *w2,
+                            int Cout, int taps, hipStream_t st) {
+    dim3 grid((HW + 63) / 64, (C + 63) / 64, N);
+    hipLaunchKernelGGL(nchw_to_nhwc_kernel<T>, grid, dim3(256), 0, st, static_cast<const T *>(x),
+                       static_cast<T *>(y), C, HW);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    long long total = (long long)Cout * C * taps;
+    long long blocks = (total + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    hipLaunchKernelGGL(oihw_to_ohwi_kernel<T>, dim3((unsigned)blocks), dim3(256), 0, st,
+                       static_cast<const T *>(w), static_cast<T *>(w2), Cout, C, taps);
+    return hipGetLastError();
+}
+
+hipError_t launch_to_channel_last(const void *x, void *x_nhwc, int N, int C, int HW, const void *w,
+                                  void *w_ohwi, int Cout, int taps, int dtype, hipStream_t st) {
+    switch (dtype) {
+    case CONV2D_DTYPE_BF16:
+        return to_nhwc_t<bf16>(x, x_nhwc, N, C, HW, w, w_ohwi, Cout, taps, st);
+    case CONV2D_DTYPE_F16:
+        return to_nhwc_t<f16>(x, x_nhwc, N, C, HW, w, w_ohwi, Cout, taps, st);
+    default:
+        return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace c2d

@@ -58,6 +58,11 @@ SWEEP = [
     (1, 2, 3, 16, 8, 3, 2, 2, "relu", None, "nhwc", "f16"),     # padding wider than input
     (4, 7, 9, 8, 1, 3, 1, 1, "silu", None, "nhwc", "bf16"),     # one output channel
     (1, 11, 13, 1, 5, 3, 1, 1, "relu", None, "nchw", "bf16"),   # one input channel
+    # channel-first through channel-last copies + the matrix-core kernel
+    (2, 9, 7, 64, 40, 3, 1, 1, "prelu", "post", "nchw", "f16"),  # 63 pixels: per-element stores
+    (1, 16, 16, 128, 96, 3, 2, 1, "relu", "pre", "nchw", "bf16"),
+    (3, 12, 12, 72, 200, 1, 1, 0, "silu", None, "nchw", "f16"),
+    (1, 17, 30, 240, 240, 3, 1, 1, "prelu", "post", "nchw", "f16"),  # IFNet conv, reduced frame
     # few output tiles, deep K (split-K: fp32 slices, then a second pass for the epilogue)
     (1, 10, 10, 512, 512, 3, 1, 1, "relu", "pre", "nhwc", "bf16"),
     (2, 7, 9, 384, 64, 3, 1, 1, "prelu", "post", "nhwc", "f16"),

@@ -9,6 +9,7 @@ from .inputs import (  # noqa: F401
     PoolSpec,
     conv1_single,
     conv2_stem,
+    conv2_stem_bf16,
     conv3_pointwise,
     conv4_ifnet_block,
     conv5_resnet18d,

@@ -123,6 +123,11 @@ def conv2_stem(dtype: str = "f32", seed: int = 1, n: int = 1, hw: int = 640) -> 
                     dtype, x, [conv, pool])
 
 
+def conv2_stem_bf16(seed: int = 1) -> Workload:
+    """The stem workload with bf16 storage."""
+    return conv2_stem("bf16", seed)
+
+
 def conv3_pointwise(seed: int = 2, n: int = 4, hw: int = 80) -> Workload:
     """1x1 conv 512->256 + bias + ReLU, NHWC bf16, x ~ N(0,1), w ~ N(0, 1/512)."""
     rng = np.random.default_rng(seed)
