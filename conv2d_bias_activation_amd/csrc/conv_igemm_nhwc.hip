@@ -25,14 +25,6 @@
 
 namespace c2d {
 
-namespace {
-
-__device__ __forceinline__ __attribute__((address_space(3))) void *lds_ptr(void *p) {
-    return (__attribute__((address_space(3))) void *)p;
-}
-
-}  // namespace
-
 // s_waitcnt with only the vector-memory counter limited (expcnt and lgkmcnt at their
 // maxima, so they impose no wait).
 template <int N> __device__ __forceinline__ void wait_vmcnt() {
@@ -94,7 +86,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void igemm_nhwc_kernel(ConvArgs a, 
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave % WGM, wn = wave / WGM;
 
     const int tile = xcd_remap(blockIdx.x, gridDim.x);
@@ -108,10 +100,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void igemm_nhwc_kernel(ConvArgs a, 
     const int s_begin = blockIdx.y * steps_per_split;
     const int nsteps = max(0, min(nsteps_all, s_begin + steps_per_split) - s_begin);
 
-    const __amdgpu_buffer_rsrc_t rx =
-        make_rsrc(a.x, (uint32_t)((size_t)a.N * H * W * Cin * sizeof(T)));
-    const __amdgpu_buffer_rsrc_t rw =
-        make_rsrc(a.w, (uint32_t)((size_t)a.Cout * K * sizeof(T)));
+    const i32x4 rx = rsrc_words(a.x, (uint32_t)((size_t)a.N * H * W * Cin * sizeof(T)));
+    const i32x4 rw = rsrc_words(a.w, (uint32_t)((size_t)a.Cout * K * sizeof(T)));
 
     // This thread's loads: rows (j*NW + wave)*8 + lrow, LDS chunk position pch (= the
     // lane's slot in the wave's 1 KiB), which holds the row's logical 16-byte chunk
@@ -172,15 +162,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void igemm_nhwc_kernel(ConvArgs a, 
             int iy = a_ih[j] + ky, ix = a_iw[j] + kx;
             bool ok = a_ok[j] && kin && (unsigned)iy < (unsigned)H && (unsigned)ix < (unsigned)W;
             uint32_t off = (uint32_t)((a_pix[j] + iy * W + ix) * Cin + ci) * (uint32_t)sizeof(T);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lds_ptr(sA + (j * NW + wave) * 1024), 16,
-                                                     (int)(ok ? off : kOOB), 0, 0, 0);
+            dma_b128(rx, ok ? off : kOOB, lds_addr(sA + (j * NW + wave) * 1024));
         }
         const int kk = (ky * kw + kx) * Cin + ci;
 #pragma unroll
         for (int j = 0; j < LB; ++j) {
             uint32_t off = (uint32_t)(b_off[j] + kk) * (uint32_t)sizeof(T);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lds_ptr(sB + (j * NW + wave) * 1024), 16,
-                                                     (int)((b_ok[j] && kin) ? off : kOOB), 0, 0, 0);
+            dma_b128(rw, (b_ok[j] && kin) ? off : kOOB, lds_addr(sB + (j * NW + wave) * 1024));
         }
         if constexpr (TAP_INNER) {
             if (++kx == kw) {
@@ -212,23 +200,32 @@ __global__ __launch_bounds__(64 * WGM * WGN) void igemm_nhwc_kernel(ConvArgs a, 
 
     typedef typename Mfma32<T>::vec vec;
     const int rl = lane & 31, kq = lane >> 5, sw = (rl >> 1) & 7;
+    // One step's matrix-core work. The operand reads of sub-step ks+1 are issued
+    // before the products of sub-step ks, so LDS latency overlaps the matrix cores.
     auto compute = [&](const char *stage) {
         const char *sA = stage;
         const char *sB = sA + BM * ROWB;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
+        vec fa[2][FM], fb[2][FN];
+        auto read = [&](int ks, vec(&xa)[FM], vec(&xb)[FN]) {
             const int chunk = ((ks * 2 + kq) ^ sw) * 16;
-            vec fa[FM], fb[FN];
 #pragma unroll
             for (int i = 0; i < FM; ++i)
-                fa[i] = *reinterpret_cast<const vec *>(sA + (wm * FM * 32 + i * 32 + rl) * ROWB + chunk);
+                xa[i] = *reinterpret_cast<const vec *>(sA + (wm * FM * 32 + i * 32 + rl) * ROWB + chunk);
 #pragma unroll
             for (int j = 0; j < FN; ++j)
-                fb[j] = *reinterpret_cast<const vec *>(sB + (wn * FN * 32 + j * 32 + rl) * ROWB + chunk);
+                xb[j] = *reinterpret_cast<const vec *>(sB + (wn * FN * 32 + j * 32 + rl) * ROWB + chunk);
+        };
+        read(0, fa[0], fb[0]);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            if (ks < 3) read(ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+            // keep the scheduler from sinking those reads below the products
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int j = 0; j < FN; ++j) acc[i][j] = Mfma32<T>::run(fa[i], fb[j], acc[i][j]);
+                for (int j = 0; j < FN; ++j) acc[i][j] = Mfma32<T>::run(fa[ks & 1][i], fb[ks & 1][j], acc[i][j]);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 

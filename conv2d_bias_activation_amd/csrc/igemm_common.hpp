@@ -265,6 +265,27 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint3
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (int)bytes, 0x00020000);
 }
 
+// The same descriptor as four words, for the direct-to-LDS load below.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 rsrc_words(const void *p, uint32_t bytes) {
+    const uint64_t a = (uint64_t)p;
+    return i32x4{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), (int)bytes, 0x00020000};
+}
+
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
+}
+
+// Direct-to-LDS 16-byte buffer load: lane i's 16 bytes from `voff` land at LDS address
+// lds + 16*i (lds must be wave-uniform). Issued as inline assembly so that the
+// compiler, which cannot tell which LDS bytes such a load writes, does not drain every
+// outstanding load before each later LDS read: the caller owns the vmcnt waits and
+// barriers that order these loads before the reads of their data.
+__device__ __forceinline__ void dma_b128(i32x4 rsrc, uint32_t voff, uint32_t lds) {
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds) : "memory");
+}
+
 // Fused epilogue of one wave's (FM*32) x (FN*32) block of 32x32 matrix-core
 // accumulators, channel-last output (rows mrow0.. are pixels, columns ncol0.. output
 // channels). Phase 1 touches only LDS: 16 rows at a time go through the wave's
