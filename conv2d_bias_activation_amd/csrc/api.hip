@@ -4,6 +4,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 #include <string>
 
@@ -127,12 +128,13 @@ int check_conv(const void *x, const void *w, const float *alpha, const void *res
     return CONV2D_OK;
 }
 
-enum Family { FAM_DIRECT = 0, FAM_IGEMM = 1, FAM_NHWC = 2, FAM_NCHW_VIA_NHWC = 3 };
+enum Family { FAM_DIRECT = 0, FAM_IGEMM = 1, FAM_NHWC = 2, FAM_NCHW_VIA_NHWC = 3, FAM_HALO = 4 };
 
 struct Plan {
     int family;
     IgemmPlan ig;
     NhwcPlan nh;
+    HaloPlan halo;
 };
 
 // Library scratch, one buffer per device, allocated on the first call that needs it
@@ -157,6 +159,24 @@ int get_scratch(float **out) {
         g_scratch[dev] = static_cast<float *>(p);
     }
     *out = g_scratch[dev];
+    return CONV2D_OK;
+}
+
+// Compute units of the current device (queried once per device).
+std::atomic<int> g_cus[kMaxDevices];
+
+int device_cus(int *out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return set_error(CONV2D_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return set_error(CONV2D_EHIP, "device index %d out of range", dev);
+    int n = g_cus[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess || n <= 0) return set_error(CONV2D_EHIP, "compute unit count: %s", hipGetErrorString(e));
+        g_cus[dev].store(n, std::memory_order_relaxed);
+    }
+    *out = n;
     return CONV2D_OK;
 }
 
@@ -202,8 +222,8 @@ int choose_tile(const ConvArgs &a) {
 
 const char *nhwc_tile_name(int t) {
     static const char *names[NHWC_TILE_COUNT] = {
-        "256x128w8", "128x128",    "128x64",      "256x64w8",       "256x32",      "64x64",
-        "128x128w8", "128x256w8",  "64x64d6",     "128x64d5",       "128x128w8d4", "64x128d5"};
+        "256x128w8", "128x128",  "128x64",   "256x64w8",    "256x32",   "64x64",   "128x128w8",
+        "128x256w8", "64x64d6",  "128x64d5", "128x128w8d4", "64x128d5", "64x64d4", "256x128w8d3"};
     return (t >= 0 && t < NHWC_TILE_COUNT) ? names[t] : "?";
 }
 
@@ -239,6 +259,33 @@ NhwcPlan plan_nhwc(const ConvArgs &a) {
     return p;
 }
 
+// Halo-tile kernel for narrow 3x3 stride-1 layers: 32 output channels per wave, and
+// the tile height with the least work per CU over one GPU's 256 CUs, counting a tile
+// of TH rows as TH + 4 (its two halo rows and a fixed cost, from MI355X timings of
+// the ResNet stem and stage-1 layers); ties go to the taller tile.
+HaloPlan plan_halo(const ConvArgs &a) {
+    HaloPlan p{};
+    p.wn = a.Cout <= 32 ? 1 : 2;
+    const int ths[2] = {p.wn == 1 ? (a.Cin <= 32 ? 16 : 8) : 8, p.wn == 1 ? 8 : 4};
+    long long best = 0;
+    for (int th : ths) {
+        const long long nt = (long long)a.N * ((a.W + 31) / 32) * ((a.H + th - 1) / th);
+        const long long cost = (nt + 255) / 256 * (th + 4);
+        if (p.th == 0 || cost < best) {
+            best = cost;
+            p.th = th;
+        }
+    }
+    p.grid_cap = 256;
+    return p;
+}
+
+bool halo_fits(const ConvArgs &a, int layout, int dtype) {
+    return layout == CONV2D_LAYOUT_NHWC && dtype != CONV2D_DTYPE_F32 && a.kh == 3 && a.kw == 3 &&
+           a.stride == 1 && a.pad == 1 && (a.Cin == 16 || a.Cin == 32 || a.Cin == 64) && a.Cout <= 64 &&
+           (a.Cout % 8) == 0 && a.vec_out && aligned16(a.x) && aligned16(a.w);
+}
+
 Plan make_plan(const ConvArgs &a, int layout, int dtype) {
     Plan p{};
     const int ve = 16 / dtype_bytes(dtype);
@@ -249,6 +296,11 @@ Plan make_plan(const ConvArgs &a, int layout, int dtype) {
     const long long xbytes = (long long)a.N * a.H * a.W * a.Cin * dtype_bytes(dtype);
     const long long wbytes = (long long)a.Cout * a.K * dtype_bytes(dtype);
     const long long ybytes = (long long)a.M * a.Cout * dtype_bytes(dtype);
+    if (halo_fits(a, layout, dtype) && xbytes < (1ll << 31) && ybytes < (1ll << 31)) {
+        p.family = FAM_HALO;
+        p.halo = plan_halo(a);
+        return p;
+    }
     if (layout == CONV2D_LAYOUT_NHWC && dtype != CONV2D_DTYPE_F32 && (a.Cin % 8) == 0 &&
         aligned16(a.x) && aligned16(a.w) && xbytes < (1ll << 31) && wbytes < (1ll << 31) &&
         ybytes < (1ll << 31)) {
@@ -279,6 +331,8 @@ int describe(const Plan &p, int layout, int dtype, char *buf, int cap) {
     if (p.family == FAM_DIRECT) {
         snprintf(tmp, sizeof tmp, "direct_%s %s cob32", layout == CONV2D_LAYOUT_NCHW ? "nchw" : "nhwc",
                  dtype_name(dtype));
+    } else if (p.family == FAM_HALO) {
+        snprintf(tmp, sizeof tmp, "halo3x3_nhwc %s th%d co%d", dtype_name(dtype), p.halo.th, 32 * p.halo.wn);
     } else if (p.family == FAM_NHWC || p.family == FAM_NCHW_VIA_NHWC) {
         snprintf(tmp, sizeof tmp, "%sigemm_nhwc_pipe%s %s %s splitk=%d",
                  p.family == FAM_NCHW_VIA_NHWC ? "to_nhwc+" : "", p.nh.tap_inner ? "_tapinner" : "",
@@ -365,6 +419,10 @@ int conv2d_fused(const void *x, const void *w, const float *bias, const float *a
     hipError_t e;
     if (p.family == FAM_DIRECT) {
         e = launch_direct(a, dtype, layout == CONV2D_LAYOUT_NCHW, st);
+    } else if (p.family == FAM_HALO) {
+        rc = device_cus(&p.halo.grid_cap);
+        if (rc) return rc;
+        e = launch_halo3x3(a, dtype, p.halo, st);
     } else if (p.family == FAM_NHWC) {
         float *scratch = nullptr;
         if (p.nh.splits > 1) {

@@ -352,6 +352,8 @@ constexpr TileCfg kTiles[NHWC_TILE_COUNT] = {
     {128, 64, 2, 2, 5},   // NHWC_TILE_128x64_D5
     {128, 128, 2, 4, 4},  // NHWC_TILE_128x128_W8_D4
     {64, 128, 2, 2, 5},   // NHWC_TILE_64x128_D5
+    {64, 64, 2, 2, 4},    // NHWC_TILE_64x64_D4
+    {256, 128, 4, 2, 3},  // NHWC_TILE_256x128_W8_D3
 };
 
 template <typename T, int TILE>
@@ -414,6 +416,8 @@ hipError_t launch_dtype(const ConvArgs &a, const NhwcPlan &p, float *partials, h
     case 9: return launch_t<T, 9>(a, p, partials, st);
     case 10: return launch_t<T, 10>(a, p, partials, st);
     case 11: return launch_t<T, 11>(a, p, partials, st);
+    case 12: return launch_t<T, 12>(a, p, partials, st);
+    case 13: return launch_t<T, 13>(a, p, partials, st);
     default: return hipErrorInvalidValue;
     }
 }

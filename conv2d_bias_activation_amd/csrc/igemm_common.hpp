@@ -297,11 +297,15 @@ __device__ __forceinline__ void dma_b128(i32x4 rsrc, uint32_t voff, uint32_t lds
 // With `part` non-null the wave stores its fp32 sums there instead ([M][Cout] fp32,
 // one K slice of a split-K launch) and applies nothing; a separate pass adds the
 // slices and runs the epilogue.
-template <typename T, int FM, int FN, int WLD>
-__device__ __forceinline__ void wave_epilogue_nhwc32(const f32x16 (&acc)[FM][FN], float *slice,
-                                                     const ConvArgs &a, int mrow0, int ncol0,
-                                                     int lane, uint32_t out_bytes,
-                                                     float *part = nullptr) {
+//
+// `rowof(r)` maps the wave's local row r (0 <= r < FM*32) to its output pixel m, or -1
+// for a row that has no pixel (past the end of the map or of a tile row). `mid()` runs
+// after every global load of the epilogue has been issued and before the first store.
+template <typename T, int FM, int FN, int WLD, typename RowOf, typename Mid>
+__device__ __forceinline__ void wave_epilogue_nhwc32_rows(const f32x16 (&acc)[FM][FN], float *slice,
+                                                          const ConvArgs &a, RowOf rowof, int ncol0,
+                                                          int lane, uint32_t out_bytes, float *part,
+                                                          Mid mid) {
     constexpr int VE = 16 / (int)sizeof(T);
     constexpr int WN = FN * 32;
     constexpr int CPR = WN / VE;  // VE-wide runs per row
@@ -347,13 +351,14 @@ __device__ __forceinline__ void wave_epilogue_nhwc32(const f32x16 (&acc)[FM][FN]
     const int co = ncol0 + cc * VE;
     if (part) {
         // split-K slice: raw fp32 sums (only used when Cout % VE == 0)
+        mid();
         const __amdgpu_buffer_rsrc_t rp = make_rsrc(part, (uint32_t)((size_t)a.M * Cout * 4));
 #pragma unroll
         for (int q = 0; q < NH; ++q)
 #pragma unroll
             for (int p = 0; p < NP; ++p) {
-                const int m = mrow0 + q * 16 + rsub + p * RPP;
-                const uint32_t o = (m < a.M && co < Cout) ? ((uint32_t)m * (uint32_t)Cout + (uint32_t)co) * 4u : kOOB;
+                const int m = rowof(q * 16 + rsub + p * RPP);
+                const uint32_t o = (m >= 0 && co < Cout) ? ((uint32_t)m * (uint32_t)Cout + (uint32_t)co) * 4u : kOOB;
 #pragma unroll
                 for (int e = 0; e < VE; e += 4) {
                     u32x4 t = __builtin_bit_cast(u32x4, f32x4{v[q][p][e], v[q][p][e + 1], v[q][p][e + 2], v[q][p][e + 3]});
@@ -381,9 +386,9 @@ __device__ __forceinline__ void wave_epilogue_nhwc32(const f32x16 (&acc)[FM][FN]
     for (int q = 0; q < NH; ++q)
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
-            const int m = mrow0 + q * 16 + rsub + p * RPP;
-            off[q][p] = (m < a.M && co < Cout) ? ((uint32_t)m * (uint32_t)Cout + (uint32_t)co) * (uint32_t)sizeof(T)
-                                               : kOOB;
+            const int m = rowof(q * 16 + rsub + p * RPP);
+            off[q][p] = (m >= 0 && co < Cout) ? ((uint32_t)m * (uint32_t)Cout + (uint32_t)co) * (uint32_t)sizeof(T)
+                                              : kOOB;
         }
     T rv[NH][NP][VE];
 #pragma unroll
@@ -403,6 +408,7 @@ __device__ __forceinline__ void wave_epilogue_nhwc32(const f32x16 (&acc)[FM][FN]
                 }
             }
         }
+    mid();
     auto finish = [&](auto act_tag) {
         constexpr int ACT = decltype(act_tag)::value;
 #pragma unroll
@@ -440,6 +446,18 @@ __device__ __forceinline__ void wave_epilogue_nhwc32(const f32x16 (&acc)[FM][FN]
         finish(std::integral_constant<int, CONV2D_ACT_NONE>{});
         break;
     }
+}
+
+// Rows mrow0, mrow0+1, ... of the GEMM (pixels in order); rows at or past M have none.
+template <typename T, int FM, int FN, int WLD>
+__device__ __forceinline__ void wave_epilogue_nhwc32(const f32x16 (&acc)[FM][FN], float *slice,
+                                                     const ConvArgs &a, int mrow0, int ncol0,
+                                                     int lane, uint32_t out_bytes,
+                                                     float *part = nullptr) {
+    const int M = a.M;
+    wave_epilogue_nhwc32_rows<T, FM, FN, WLD>(
+        acc, slice, a, [=](int r) { return mrow0 + r < M ? mrow0 + r : -1; }, ncol0, lane, out_bytes, part,
+        [] {});
 }
 
 // The same epilogue for channel-first output (y and the residual are [N][Cout][OH*OW]):

@@ -35,7 +35,9 @@ enum NhwcTile {
     NHWC_TILE_128x64_D5 = 9,
     NHWC_TILE_128x128_W8_D4 = 10,
     NHWC_TILE_64x128_D5 = 11,
-    NHWC_TILE_COUNT = 12,
+    NHWC_TILE_64x64_D4 = 12,
+    NHWC_TILE_256x128_W8_D3 = 13,
+    NHWC_TILE_COUNT = 14,
 };
 
 struct NhwcPlan {
@@ -59,6 +61,18 @@ int nhwc_tile_waves(int tile);
 // slice to `partials` and a second kernel adds them and applies the epilogue.
 hipError_t launch_igemm_nhwc(const ConvArgs &a, int dtype, const NhwcPlan &p, float *partials,
                              hipStream_t st);
+
+struct HaloPlan {
+    int th;        // output rows per 32-pixel-wide tile
+    int wn;        // waves along the output channels (32 channels each): 1 or 2
+    int grid_cap;  // persistent workgroups (one per CU)
+};
+
+// 3x3 stride-1 pad-1 channel-last 16-bit convolution with halo tiles and weights held
+// in registers: Cin 16, 32 or 64, Cout <= 32 * p.wn with Cout % 8 == 0, x and w
+// 16-byte aligned, y and the residual 16-byte aligned (a.vec_out), tensors under
+// 2 GiB. (p.wn, p.th) in {(1, 8), (1, 16) for Cin <= 32, (2, 4), (2, 8)}.
+hipError_t launch_halo3x3(const ConvArgs &a, int dtype, const HaloPlan &p, hipStream_t st);
 
 // Direct convolution on the vector ALUs for few input channels (the image stem):
 // one thread per output pixel and a block of output channels.

@@ -92,6 +92,40 @@ def test_sweep(case):
     gate(to64(y), _oracle_conv(x, spec, r, layout), dtype, what=str(case))
 
 
+# Narrow 3x3 stride-1 layers on the halo-tile kernel: ragged tile rows and columns,
+# partial channel blocks, every epilogue, and enough tiles that each persistent
+# workgroup walks several (both halo buffers, the prefetch of tiles past the end).
+# (n, h, w, cin, cout, act, residual, dtype)
+HALO = [
+    (1, 9, 11, 16, 16, "relu", None, "bf16"),
+    (2, 37, 45, 32, 32, "silu", None, "bf16"),
+    (2, 37, 45, 32, 64, "prelu", "post", "f16"),
+    (1, 70, 100, 64, 64, "relu", "pre", "bf16"),
+    (2, 33, 65, 64, 24, "none", "post", "bf16"),
+    (3, 8, 32, 16, 40, "relu", "pre", "f16"),
+    (1, 1, 1, 32, 32, "relu", None, "bf16"),
+    (1, 130, 66, 32, 8, "silu", None, "bf16"),
+    (4, 256, 256, 16, 32, "relu", None, "bf16"),
+    (2, 150, 200, 64, 64, "prelu", "pre", "f16"),
+    (2, 160, 160, 32, 48, "silu", "post", "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", HALO, ids=lambda c: "-".join(map(str, c)))
+def test_halo(case):
+    n, h, w, cin, cout, act, res, dtype = case
+    seed = zlib.crc32(repr(case).encode())
+    x, spec, r = wl.random_conv_case(seed, n=n, h=h, w=w, cin=cin, cout=cout, k=3, stride=1, pad=1,
+                                     act=act, layout="nhwc", dtype=dtype, residual=res is not None,
+                                     res_before_act=res == "pre")
+    plan = c2d.plan(n, h, w, cin, cout, 3, 3, 1, 1, 0, 0, {"bf16": 1, "f16": 2}[dtype])
+    print(f"case {case} plan {plan}", flush=True)
+    assert plan.startswith("halo3x3"), plan
+    y = _gpu_conv(x, spec, r, "nhwc")
+    torch.cuda.synchronize()
+    gate(to64(y), _oracle_conv(x, spec, r, "nhwc"), dtype, what=str(case))
+
+
 @pytest.mark.parametrize("layout", ["nhwc", "nchw"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_delta_kernel_is_identity(layout, dtype):
