@@ -266,7 +266,8 @@ NhwcPlan plan_nhwc(const ConvArgs &a) {
 HaloPlan plan_halo(const ConvArgs &a) {
     HaloPlan p{};
     p.wn = a.Cout <= 32 ? 1 : 2;
-    const int ths[2] = {p.wn == 1 ? (a.Cin <= 32 ? 16 : 8) : 8, p.wn == 1 ? 8 : 4};
+    // 64-channel layers split k over wave pairs: half the waves along the tile rows
+    const int ths[2] = {a.Cin == 64 ? (p.wn == 1 ? 8 : 4) : (p.wn == 1 ? 16 : 8), p.wn == 1 ? (a.Cin == 64 ? 4 : 8) : 4};
     long long best = 0;
     for (int th : ths) {
         const long long nt = (long long)a.N * ((a.W + 31) / 32) * ((a.H + th - 1) / th);

@@ -10,12 +10,14 @@
 // WebGPU page's convolution shader). Input bytes move HBM -> LDS about
 // (TH+2)*34/(TH*32) times instead of nine times.
 //
-//  * Weights stay in registers: with Cin <= 64 one wave's 32 output channels over
-//    all 9*Cin k are 9*Cin/16 operand fragments of 4 VGPRs (144 VGPRs at Cin 64),
-//    loaded once per workgroup.
+//  * Weights stay in registers: one wave's 32 output channels over its share of the
+//    9*Cin k are 9*Cin/(16*WK) operand fragments of 4 VGPRs (72 VGPRs at Cin 32, or
+//    at Cin 64 with k split over a pair of waves). A workgroup copies the weights
+//    into LDS once, in fragment order, and every wave reads its fragments from there.
 //  * Workgroups are persistent: each walks tiles t = k*G + r (r its XCD-grouped
 //    index among G), with the halo of tile k+2 loading into the buffer tile k just
-//    released while tile k's epilogue and tile k+1's products run.
+//    released while tile k's epilogue and tile k+1's products run. Bias and slopes
+//    stay in registers; a tile's residual loads go out before its products.
 //  * The halo copy goes straight from memory into LDS (16-byte direct-to-LDS loads,
 //    out-of-image pixels as out-of-range offsets that read zeros). A pixel takes
 //    Cin/8 + 1 16-byte slots (the last one is padding), an odd number of 16-byte
@@ -43,13 +45,15 @@ __device__ __forceinline__ void halo_barrier() {
 }  // namespace
 
 // CIN input channels (16, 32 or 64); TH output rows per tile (tiles are TH x 32);
-// WN waves along the output channels (32 each), 8 / WN waves along the tile rows.
-template <typename T, int CIN, int TH, int WN>
+// WN waves along the output channels (32 each); WK waves along k (each takes CIN/WK
+// of the input channels of every tap and the pair adds their sums through LDS);
+// 8 / (WN * WK) waves along the tile rows.
+template <typename T, int CIN, int TH, int WN, int WK>
 __global__ __launch_bounds__(512) void halo3x3_kernel(ConvArgs a, int tiles_w, int tiles_h, int ntiles) {
     constexpr int NW = 8;
-    constexpr int WM = NW / WN;
+    constexpr int WM = NW / (WN * WK);
     constexpr int FM = TH / WM;               // 32-pixel tile rows per wave
-    static_assert(FM >= 1 && FM * WM == TH, "tile rows split evenly over the waves");
+    static_assert(WM >= 1 && FM >= 1 && FM * WM == TH, "tile rows split evenly over the waves");
     constexpr int TW = 32, HW = TW + 2, HR = TH + 2;
     constexpr int CPX = CIN / 8;              // 16-byte chunks of channels per pixel
     static_assert(CPX == 2 || CPX == 4 || CPX == 8, "Cin 16, 32 or 64");
@@ -59,33 +63,66 @@ __global__ __launch_bounds__(512) void halo3x3_kernel(ConvArgs a, int tiles_w, i
     constexpr int NDW = (NQ * SPX + 64 * NW - 1) / (64 * NW);  // loads per lane per halo
     constexpr int HBUF = NDW * NW * 1024;
     constexpr int KC = CIN / 16;              // 16-wide k steps per tap
-    constexpr int KS = 9 * KC;
+    static_assert(KC % WK == 0, "k split");
+    constexpr int KCW = KC / WK;              // of them per wave
+    constexpr int KSW = 9 * KCW;              // k steps per wave
+    constexpr int WBYTES = WN * WK * KSW * 1024;            // weights in operand order
+    constexpr int NDWW = (WBYTES + NW * 1024 - 1) / (NW * 1024);
+    constexpr int RING = cmax<2 * HBUF, NDWW * NW * 1024>::v;
+    constexpr int NHW = 2 / WK;               // 16-row halves of each block this wave stores
+    constexpr int NH = FM * NHW;
+    constexpr int XCH = WK == 2 ? NW * FM * 2 * 1024 : 16;  // per wave: FM x 8 floats per lane
     constexpr int WLD = 32 + 4;
     constexpr int SLICE = 16 * WLD * 4;
-    __shared__ __attribute__((aligned(1024))) char hb0[HBUF];
-    __shared__ __attribute__((aligned(1024))) char hb1[HBUF];
+    constexpr int VE = 8;                     // 16-bit values per 16-byte run
+    __shared__ __attribute__((aligned(1024))) char ring[RING];
+    __shared__ __attribute__((aligned(1024))) char xch[XCH];
     __shared__ __attribute__((aligned(16))) char slices[NW * SLICE];
+    char *const hb0 = ring;
+    char *const hb1 = ring + HBUF;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wm = wave % WM, wn = wave / WM;
+    const int wm = wave % WM, wk = (wave / WM) % WK, wn = wave / (WM * WK);
     const int rl = lane & 31, hi = lane >> 5;
+    const int cc = lane & 3, rsub = lane >> 2;  // epilogue: 16-byte run cc of row rsub
     const int H = a.H, W = a.W, Cout = a.Cout;
-
-    // This wave's weights: output channel co = 32*wn + rl, k step s -> tap s / KC,
-    // channels 16*(s % KC) + 8*hi .. +8 (the B operand layout).
     typedef typename Mfma32<T>::vec vec;
-    vec bw[KS];
-    {
-        const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.w, (uint32_t)((size_t)Cout * 9 * CIN * sizeof(T)));
-        const int co = wn * 32 + rl;
+
+    // Weights, once per workgroup: staged in LDS in operand order ([wn][wk][k step]
+    // [lane] x 16 bytes: output channel 32*wn + lane % 32, channels 8*(lane/32).. of
+    // the wave's k step), then each wave takes its KSW fragments into registers.
+    // Bias and slopes of the lane's epilogue run stay in registers too.
+    const i32x4 rwt = rsrc_words(a.w, (uint32_t)((size_t)Cout * 9 * CIN * sizeof(T)));
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            const uint32_t off =
-                co < Cout ? (uint32_t)((co * 9 + s / KC) * CIN + (s % KC) * 16 + hi * 8) * (uint32_t)sizeof(T) : kOOB;
-            bw[s] = __builtin_bit_cast(vec, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)off, 0, 0));
+    for (int d = 0; d < NDWW; ++d) {
+        const int rest = d * NW + wave;
+        const int sw = rest % KSW, wkk = (rest / KSW) % WK, wnn = rest / (KSW * WK);
+        const int co = wnn * 32 + rl, tap = sw / KCW, ci = (wkk * KCW + sw % KCW) * 16 + hi * 8;
+        const bool ok = wnn < WN && co < Cout;
+        dma_b128(rwt, ok ? (uint32_t)((co * 9 + tap) * CIN + ci) * (uint32_t)sizeof(T) : kOOB,
+                 lds_addr(ring + rest * 1024));
+    }
+    float bv[VE], av[VE];
+    {
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.bias, a.bias ? (uint32_t)Cout * 4u : 0u);
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.alpha, a.alpha ? (uint32_t)Cout * 4u : 0u);
+        const int co = wn * 32 + cc * VE;
+#pragma unroll
+        for (int e = 0; e < VE; ++e) {
+            const uint32_t off = co + e < Cout ? (uint32_t)(co + e) * 4u : kOOB;
+            bv[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, (int)off, 0, 0));
+            av[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ra, (int)off, 0, 0));
         }
     }
+    halo_wait_vmcnt<0>();
+    halo_barrier();
+    vec bw[KSW];
+#pragma unroll
+    for (int sw = 0; sw < KSW; ++sw)
+        bw[sw] = *reinterpret_cast<const vec *>(ring + (((wn * WK + wk) * KSW + sw) * 64 + lane) * 16);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): fragments in registers before the ring is reused
+    halo_barrier();
 
     // Tile order: G workgroups, the ones on one XCD (blockIdx % 8) take a contiguous
     // run of each round's G tiles, so neighbouring tiles share halo rows in one L2.
@@ -113,62 +150,137 @@ __global__ __launch_bounds__(512) void halo3x3_kernel(ConvArgs a, int tiles_w, i
         }
     };
 
-    f32x16 acc[FM][1];
+    f32x16 acc[FM];
     auto compute = [&](const char *buf) {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][0][e] = 0.0f;
-        // A operand of tile row wm*FM+i at k step s: pixel (row + ky, rl + kx) of the
-        // halo, chunk 2*(s % KC) + hi.
-        const char *base = buf + ((wm * FM) * HW + rl) * PSTR + hi * 16;
-        auto read = [&](int s, vec(&fa)[FM]) {
-            const int tap = s / KC, ky = tap / 3, kx = tap % 3;
+            for (int e = 0; e < 16; ++e) acc[i][e] = 0.0f;
+        // A operand of tile row wm*FM+i at the wave's k step sw: pixel (row + ky, rl + kx)
+        // of the halo, 16-channel chunk wk*KCW + sw % KCW, 8-channel half hi.
+        const char *base = buf + ((wm * FM) * HW + rl) * PSTR + hi * 16 + wk * KCW * 32;
+        auto read = [&](int sw, vec(&fa)[FM]) {
+            const int tap = sw / KCW, ky = tap / 3, kx = tap % 3;
 #pragma unroll
             for (int i = 0; i < FM; ++i)
-                fa[i] = *reinterpret_cast<const vec *>(base + ((i + ky) * HW + kx) * PSTR + (s % KC) * 32);
+                fa[i] = *reinterpret_cast<const vec *>(base + ((i + ky) * HW + kx) * PSTR + (sw % KCW) * 32);
         };
         vec fa[2][FM];
         read(0, fa[0]);
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            if (s + 1 < KS) read(s + 1, fa[(s + 1) & 1]);
+        for (int sw = 0; sw < KSW; ++sw) {
+            if (sw + 1 < KSW) read(sw + 1, fa[(sw + 1) & 1]);
+            // keep the scheduler from sinking those reads below the products
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int i = 0; i < FM; ++i) acc[i][0] = Mfma32<T>::run(fa[s & 1][i], bw[s], acc[i][0]);
+            for (int i = 0; i < FM; ++i) acc[i] = Mfma32<T>::run(fa[sw & 1][i], bw[sw], acc[i]);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
 
-    float *slice = reinterpret_cast<float *>(slices + wave * SLICE);
+    // Epilogue rows: the wave's q-th 16-row half (block i = q / NHW, half h) holds
+    // pixels 16h + 0..15 of tile row wm*FM + i; a lane finishes row rsub of each half,
+    // channels 32*wn + 8*cc .. +8.
+    const bool has_res = a.res != nullptr, pre = a.res_before_act != 0;
     const uint32_t out_bytes = (uint32_t)((size_t)a.M * Cout * sizeof(T));
+    const __amdgpu_buffer_rsrc_t rres = make_rsrc(a.res, has_res ? out_bytes : 0u);
+    const __amdgpu_buffer_rsrc_t ry = make_rsrc(a.y, out_bytes);
+    const int co_run = wn * 32 + cc * VE;
+    auto half_of = [&](int q) { return WK == 2 ? wk : q % NHW; };
+    auto out_off = [&](int t, int q) -> uint32_t {
+        const int tx = t % tiles_w, rr = t / tiles_w;
+        const int ty = rr % tiles_h, n = rr / tiles_h;
+        const int oy = ty * TH + wm * FM + q / NHW, ox = tx * TW + 16 * half_of(q) + rsub;
+        return (oy < H && ox < W && co_run < Cout)
+                   ? ((uint32_t)((n * H + oy) * W + ox) * (uint32_t)Cout + (uint32_t)co_run) * (uint32_t)sizeof(T)
+                   : kOOB;
+    };
+
+    float *slice = reinterpret_cast<float *>(slices + wave * SLICE);
+    float *mine = reinterpret_cast<float *>(xch + wave * (FM * 2 * 1024));
+    const float *theirs = reinterpret_cast<const float *>(xch + (WK == 2 ? (wave + (wk ? -WM : WM)) : wave) * (FM * 2 * 1024));
 
     // One tile. Its halo has landed for this wave (the wait in the previous tile's
-    // epilogue, or the prologue's): barrier (so it has for every wave), products,
-    // barrier (every wave is done reading buf), epilogue. Between the epilogue's loads
-    // and its stores, wait for all of this wave's loads (the residual and bias, the
+    // epilogue, or the prologue's): barrier (so it has for every wave), residual loads,
+    // products, [hand the partner the half it stores,] barrier (every wave is done
+    // reading buf), [add the partner's half,] epilogue. Between the epilogue's LDS
+    // phase and its stores, wait for all of this wave's loads (the residual, and the
     // halo of tile k+1, which has had this tile's products to arrive) and refill buf
-    // with tile k+2. Loads return in order, so issuing the refill only after that
-    // wait keeps the epilogue's own loads from queueing behind it.
+    // with tile k+2.
     auto tile = [&](char *buf, int k) {
         const int t = k * G + r;
         halo_barrier();
+        uint32_t off[NH];
+        u32x4 rv[NH];
+#pragma unroll
+        for (int q = 0; q < NH; ++q) {
+            off[q] = out_off(t, q);
+            rv[q] = has_res ? __builtin_amdgcn_raw_buffer_load_b128(rres, (int)off[q], 0, 0) : u32x4{0u, 0u, 0u, 0u};
+        }
         compute(buf);
+        if constexpr (WK == 2) {
+            const int hs = 1 - wk;  // the half the partner stores
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+                    *reinterpret_cast<f32x4 *>(mine + ((i * 2 + u) * 64 + lane) * 4) =
+                        f32x4{acc[i][8 * hs + 4 * u], acc[i][8 * hs + 4 * u + 1], acc[i][8 * hs + 4 * u + 2],
+                              acc[i][8 * hs + 4 * u + 3]};
+        }
         halo_barrier();
-        const int tx = t % tiles_w, rr = t / tiles_w;
-        const int ty = rr % tiles_h, n = rr / tiles_h;
-        const int oy0 = ty * TH + wm * FM, ox0 = tx * TW;
-        wave_epilogue_nhwc32_rows<T, FM, 1, WLD>(
-            acc, slice, a,
-            [=](int lr) {
-                const int oy = oy0 + lr / 32, ox = ox0 + lr % 32;
-                return (oy < H && ox < W) ? (n * H + oy) * W + ox : -1;
-            },
-            wn * 32, lane, out_bytes, nullptr,
-            [&] {
-                halo_wait_vmcnt<0>();
-                issue(buf, (k + 2) * G + r);
-            });
+        if constexpr (WK == 2) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const f32x4 o = *reinterpret_cast<const f32x4 *>(theirs + ((i * 2 + u) * 64 + lane) * 4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[i][8 * wk + 4 * u + e] += o[e];
+                }
+        }
+        // LDS phase: each 16-row half through the wave's slice, back as 8-channel runs.
+        float v[NH][VE];
+#pragma unroll
+        for (int q = 0; q < NH; ++q) {
+            const int i = q / NHW, h = half_of(q);
+#pragma unroll
+            for (int g = 0; g < 2; ++g)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) slice[(g * 8 + hi * 4 + e) * WLD + rl] = acc[i][(2 * h + g) * 4 + e];
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int e = 0; e < VE; e += 4) {
+                const f32x4 x = *reinterpret_cast<const f32x4 *>(slice + rsub * WLD + cc * VE + e);
+                v[q][e] = x[0];
+                v[q][e + 1] = x[1];
+                v[q][e + 2] = x[2];
+                v[q][e + 3] = x[3];
+            }
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            __builtin_amdgcn_wave_barrier();
+        }
+        halo_wait_vmcnt<0>();
+        issue(buf, (k + 2) * G + r);
+        auto finish = [&](auto act_tag) {
+            constexpr int ACT = decltype(act_tag)::value;
+#pragma unroll
+            for (int q = 0; q < NH; ++q) {
+                T rt[VE], out[VE];
+                __builtin_memcpy(rt, &rv[q], 16);
+                epilogue_vec<T, ACT, VE>(v[q], bv, av, rt, has_res, pre, out);
+                u32x4 o;
+                __builtin_memcpy(&o, out, 16);
+                __builtin_amdgcn_raw_buffer_store_b128(o, ry, (int)off[q], 0, 0);
+            }
+        };
+        switch (a.act) {
+        case CONV2D_ACT_RELU: finish(std::integral_constant<int, CONV2D_ACT_RELU>{}); break;
+        case CONV2D_ACT_SILU: finish(std::integral_constant<int, CONV2D_ACT_SILU>{}); break;
+        case CONV2D_ACT_PRELU: finish(std::integral_constant<int, CONV2D_ACT_PRELU>{}); break;
+        default: finish(std::integral_constant<int, CONV2D_ACT_NONE>{}); break;
+        }
     };
     issue(hb0, r);
     issue(hb1, G + r);
@@ -189,20 +301,25 @@ static hipError_t launch_halo_t(const ConvArgs &a, int grid_cap, hipStream_t st)
     const int ntiles = (int)nt;
     int grid = ntiles < grid_cap ? ntiles : grid_cap;
     if (grid > 8) grid -= grid % 8;
-    hipLaunchKernelGGL((halo3x3_kernel<T, CIN, TH, WN>), dim3(grid), dim3(512), 0, st, a, tiles_w, tiles_h,
+    constexpr int WK = CIN == 64 ? 2 : 1;
+    hipLaunchKernelGGL((halo3x3_kernel<T, CIN, TH, WN, WK>), dim3(grid), dim3(512), 0, st, a, tiles_w, tiles_h,
                        ntiles);
     return hipGetLastError();
 }
 
+// Tile heights per (Cin, waves along Cout): 64-channel layers split k over wave pairs,
+// which leaves 2 (WN = 2) or 4 (WN = 1) waves along the tile rows.
 template <typename T, int CIN>
 static hipError_t launch_halo_c(const ConvArgs &a, const HaloPlan &p, hipStream_t st) {
-    if (p.wn == 1) {
-        if (p.th == 8) return launch_halo_t<T, CIN, 8, 1>(a, p.grid_cap, st);
-        if constexpr (CIN <= 32)  // two (16+2) x 34-pixel halos of 64 channels exceed the LDS
-            if (p.th == 16) return launch_halo_t<T, CIN, 16, 1>(a, p.grid_cap, st);
-    } else if (p.wn == 2) {
-        if (p.th == 4) return launch_halo_t<T, CIN, 4, 2>(a, p.grid_cap, st);
-        if (p.th == 8) return launch_halo_t<T, CIN, 8, 2>(a, p.grid_cap, st);
+    if constexpr (CIN == 64) {
+        if (p.wn == 1 && p.th == 4) return launch_halo_t<T, CIN, 4, 1>(a, p.grid_cap, st);
+        if (p.wn == 1 && p.th == 8) return launch_halo_t<T, CIN, 8, 1>(a, p.grid_cap, st);
+        if (p.wn == 2 && p.th == 4) return launch_halo_t<T, CIN, 4, 2>(a, p.grid_cap, st);
+    } else {
+        if (p.wn == 1 && p.th == 8) return launch_halo_t<T, CIN, 8, 1>(a, p.grid_cap, st);
+        if (p.wn == 1 && p.th == 16) return launch_halo_t<T, CIN, 16, 1>(a, p.grid_cap, st);
+        if (p.wn == 2 && p.th == 4) return launch_halo_t<T, CIN, 4, 2>(a, p.grid_cap, st);
+        if (p.wn == 2 && p.th == 8) return launch_halo_t<T, CIN, 8, 2>(a, p.grid_cap, st);
     }
     return hipErrorInvalidValue;
 }

@@ -71,7 +71,8 @@ struct HaloPlan {
 // 3x3 stride-1 pad-1 channel-last 16-bit convolution with halo tiles and weights held
 // in registers: Cin 16, 32 or 64, Cout <= 32 * p.wn with Cout % 8 == 0, x and w
 // 16-byte aligned, y and the residual 16-byte aligned (a.vec_out), tensors under
-// 2 GiB. (p.wn, p.th) in {(1, 8), (1, 16) for Cin <= 32, (2, 4), (2, 8)}.
+// 2 GiB. (p.wn, p.th) in {(1, 8), (1, 16), (2, 4), (2, 8)} for Cin <= 32 and
+// {(1, 4), (1, 8), (2, 4)} for Cin 64.
 hipError_t launch_halo3x3(const ConvArgs &a, int dtype, const HaloPlan &p, hipStream_t st);
 
 // Direct convolution on the vector ALUs for few input channels (the image stem):
