@@ -259,22 +259,26 @@ NhwcPlan plan_nhwc(const ConvArgs &a) {
     return p;
 }
 
-// Halo-tile kernel for narrow 3x3 stride-1 layers: 32 output channels per wave, and
-// the tile height with the least work per CU over one GPU's 256 CUs, counting a tile
-// of TH rows as TH + 4 (its two halo rows and a fixed cost, from MI355X timings of
-// the ResNet stem and stage-1 layers); ties go to the taller tile.
+// Halo-tile kernel for narrow 3x3 stride-1 layers: one wave covers all the output
+// channels (32 or 64); tile height WM rows (one per wave along the rows: 8, or 4 when
+// k is split over wave pairs at Cin 64) or, for 32 channels, possibly 2*WM, taking
+// the height with the least work per CU over one GPU's 256 CUs, counting a tile of
+// TH rows as TH + 4 (its two halo rows and a fixed cost, from MI355X timings of the
+// ResNet stem and stage-1 layers); ties go to the taller tile.
 HaloPlan plan_halo(const ConvArgs &a) {
     HaloPlan p{};
-    p.wn = a.Cout <= 32 ? 1 : 2;
-    // 64-channel layers split k over wave pairs: half the waves along the tile rows
-    const int ths[2] = {a.Cin == 64 ? (p.wn == 1 ? 8 : 4) : (p.wn == 1 ? 16 : 8), p.wn == 1 ? (a.Cin == 64 ? 4 : 8) : 4};
-    long long best = 0;
-    for (int th : ths) {
-        const long long nt = (long long)a.N * ((a.W + 31) / 32) * ((a.H + th - 1) / th);
-        const long long cost = (nt + 255) / 256 * (th + 4);
-        if (p.th == 0 || cost < best) {
-            best = cost;
-            p.th = th;
+    p.fn = a.Cout <= 32 ? 1 : 2;
+    const int wm = a.Cin == 64 ? 4 : 8;
+    p.th = wm;
+    if (p.fn == 1) {
+        long long best = 0;
+        for (int th : {2 * wm, wm}) {
+            const long long nt = (long long)a.N * ((a.W + 31) / 32) * ((a.H + th - 1) / th);
+            const long long cost = (nt + 255) / 256 * (th + 4);
+            if (best == 0 || cost < best) {
+                best = cost;
+                p.th = th;
+            }
         }
     }
     p.grid_cap = 256;
@@ -333,7 +337,7 @@ int describe(const Plan &p, int layout, int dtype, char *buf, int cap) {
         snprintf(tmp, sizeof tmp, "direct_%s %s cob32", layout == CONV2D_LAYOUT_NCHW ? "nchw" : "nhwc",
                  dtype_name(dtype));
     } else if (p.family == FAM_HALO) {
-        snprintf(tmp, sizeof tmp, "halo3x3_nhwc %s th%d co%d", dtype_name(dtype), p.halo.th, 32 * p.halo.wn);
+        snprintf(tmp, sizeof tmp, "halo3x3_nhwc %s th%d co%d", dtype_name(dtype), p.halo.th, 32 * p.halo.fn);
     } else if (p.family == FAM_NHWC || p.family == FAM_NCHW_VIA_NHWC) {
         snprintf(tmp, sizeof tmp, "%sigemm_nhwc_pipe%s %s %s splitk=%d",
                  p.family == FAM_NCHW_VIA_NHWC ? "to_nhwc+" : "", p.nh.tap_inner ? "_tapinner" : "",

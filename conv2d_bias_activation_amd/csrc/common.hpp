@@ -2,17 +2,29 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 #include <stdint.h>
 
 #include "../../include/conv2d_fused.h"
 
 namespace c2d {
 
+// Launches kernel k and returns that launch's own status, not the thread's sticky last
+// error (which can still hold an earlier, unrelated failure of the host program).
+template <typename... P>
+inline hipError_t launch_kernel(void (*k)(P...), dim3 grid, dim3 block, size_t smem, hipStream_t st,
+                                std::type_identity_t<P>... args) {
+    void *ptrs[] = {static_cast<void *>(&args)...};
+    return hipLaunchKernel(reinterpret_cast<const void *>(k), grid, block, ptrs, smem, st);
+}
+
 typedef __bf16 bf16;
 typedef _Float16 f16;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Everything a conv kernel needs, passed by value.
 struct ConvArgs {

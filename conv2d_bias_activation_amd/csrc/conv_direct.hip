@@ -129,8 +129,7 @@ static hipError_t launch_direct_t(const ConvArgs &a, hipStream_t st) {
     if (cic > a.Cin) cic = a.Cin;
     size_t smem = (size_t)taps * cic * COB * sizeof(float);
     dim3 grid((a.M + 255) / 256, (a.Cout + COB - 1) / COB);
-    hipLaunchKernelGGL((direct_kernel<T, COB, NCHW>), grid, dim3(256), smem, st, a, cic);
-    return hipGetLastError();
+    return launch_kernel(direct_kernel<T, COB, NCHW>, grid, dim3(256), smem, st, a, cic);
 }
 
 hipError_t launch_direct(const ConvArgs &a, int dtype, bool nchw, hipStream_t st) {

@@ -10,10 +10,11 @@
 // WebGPU page's convolution shader). Input bytes move HBM -> LDS about
 // (TH+2)*34/(TH*32) times instead of nine times.
 //
-//  * Weights stay in registers: one wave's 32 output channels over its share of the
-//    9*Cin k are 9*Cin/(16*WK) operand fragments of 4 VGPRs (72 VGPRs at Cin 32, or
-//    at Cin 64 with k split over a pair of waves). A workgroup copies the weights
-//    into LDS once, in fragment order, and every wave reads its fragments from there.
+//  * Weights stay in registers: one wave's 32*FN output channels over its share of the
+//    9*Cin k are 9*Cin*FN/(16*WK) operand fragments of 4 VGPRs (72 per 32 channels at
+//    Cin 32, or at Cin 64 with k split over a pair of waves). A workgroup copies the
+//    weights into LDS once, in fragment order, and every wave reads its fragments
+//    from there. With FN = 2 every pixel operand read from LDS feeds two products.
 //  * Workgroups are persistent: each walks tiles t = k*G + r (r its XCD-grouped
 //    index among G), with the halo of tile k+2 loading into the buffer tile k just
 //    released while tile k's epilogue and tile k+1's products run. Bias and slopes
@@ -45,13 +46,13 @@ __device__ __forceinline__ void halo_barrier() {
 }  // namespace
 
 // CIN input channels (16, 32 or 64); TH output rows per tile (tiles are TH x 32);
-// WN waves along the output channels (32 each); WK waves along k (each takes CIN/WK
-// of the input channels of every tap and the pair adds their sums through LDS);
-// 8 / (WN * WK) waves along the tile rows.
-template <typename T, int CIN, int TH, int WN, int WK>
+// FN 32-channel output blocks per wave (the workgroup covers 32*FN channels); WK
+// waves along k (each takes CIN/WK of the input channels of every tap and the pair
+// adds their sums through LDS); 8 / WK waves along the tile rows.
+template <typename T, int CIN, int TH, int FN, int WK>
 __global__ __launch_bounds__(512) void halo3x3_kernel(ConvArgs a, int tiles_w, int tiles_h, int ntiles) {
     constexpr int NW = 8;
-    constexpr int WM = NW / (WN * WK);
+    constexpr int WM = NW / WK;
     constexpr int FM = TH / WM;               // 32-pixel tile rows per wave
     static_assert(WM >= 1 && FM >= 1 && FM * WM == TH, "tile rows split evenly over the waves");
     constexpr int TW = 32, HW = TW + 2, HR = TH + 2;
@@ -66,61 +67,60 @@ __global__ __launch_bounds__(512) void halo3x3_kernel(ConvArgs a, int tiles_w, i
     static_assert(KC % WK == 0, "k split");
     constexpr int KCW = KC / WK;              // of them per wave
     constexpr int KSW = 9 * KCW;              // k steps per wave
-    constexpr int WBYTES = WN * WK * KSW * 1024;            // weights in operand order
+    constexpr int WBYTES = WK * KSW * FN * 1024;  // weights in operand order
     constexpr int NDWW = (WBYTES + NW * 1024 - 1) / (NW * 1024);
     constexpr int RING = cmax<2 * HBUF, NDWW * NW * 1024>::v;
-    constexpr int NHW = 2 / WK;               // 16-row halves of each block this wave stores
-    constexpr int NH = FM * NHW;
-    constexpr int XCH = WK == 2 ? NW * FM * 2 * 1024 : 16;  // per wave: FM x 8 floats per lane
-    constexpr int WLD = 32 + 4;
-    constexpr int SLICE = 16 * WLD * 4;
-    constexpr int VE = 8;                     // 16-bit values per 16-byte run
+    constexpr int NG = 4 / WK;                // 4-channel groups of each block this wave stores
+    constexpr int NP = NG / 2;                // pairs of them: one 16-byte store per lane
+    constexpr int XBYTES = FM * FN * 2 * 1024;  // per wave: 8 floats per lane per block
+    constexpr int XCH = WK == 2 ? NW * XBYTES : 16;
     __shared__ __attribute__((aligned(1024))) char ring[RING];
     __shared__ __attribute__((aligned(1024))) char xch[XCH];
-    __shared__ __attribute__((aligned(16))) char slices[NW * SLICE];
+    __shared__ __attribute__((aligned(16))) float bal[2][32 * FN];  // bias, slopes (0 past Cout)
     char *const hb0 = ring;
     char *const hb1 = ring + HBUF;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wm = wave % WM, wk = (wave / WM) % WK, wn = wave / (WM * WK);
+    const int wm = wave % WM, wk = wave / WM;
     const int rl = lane & 31, hi = lane >> 5;
-    const int cc = lane & 3, rsub = lane >> 2;  // epilogue: 16-byte run cc of row rsub
     const int H = a.H, W = a.W, Cout = a.Cout;
     typedef typename Mfma32<T>::vec vec;
 
-    // Weights, once per workgroup: staged in LDS in operand order ([wn][wk][k step]
-    // [lane] x 16 bytes: output channel 32*wn + lane % 32, channels 8*(lane/32).. of
-    // the wave's k step), then each wave takes its KSW fragments into registers.
-    // Bias and slopes of the lane's epilogue run stay in registers too.
+    // Weights, once per workgroup: staged in LDS in operand order ([wk][k step][block j]
+    // [lane] x 16 bytes: output channel 32*j + lane % 32, channels 8*(lane/32).. of the
+    // wave's k step), then each wave takes its KSW*FN fragments into registers.
+    // The weights are the A operand and the pixels the B operand, so the sums come
+    // out with output channels along the rows: lane (rl, hi) holds channels
+    // 32*j + 8*g + 4*hi + 0..3, g < 4, of pixel rl, and the epilogue stores 4-channel
+    // runs straight from registers. The accumulators start from the bias; bias and
+    // slopes sit in a small LDS table.
     const i32x4 rwt = rsrc_words(a.w, (uint32_t)((size_t)Cout * 9 * CIN * sizeof(T)));
 #pragma unroll
     for (int d = 0; d < NDWW; ++d) {
         const int rest = d * NW + wave;
-        const int sw = rest % KSW, wkk = (rest / KSW) % WK, wnn = rest / (KSW * WK);
-        const int co = wnn * 32 + rl, tap = sw / KCW, ci = (wkk * KCW + sw % KCW) * 16 + hi * 8;
-        const bool ok = wnn < WN && co < Cout;
+        const int j = rest % FN, sw = (rest / FN) % KSW, wkk = rest / (FN * KSW);
+        const int co = j * 32 + rl, tap = sw / KCW, ci = (wkk * KCW + sw % KCW) * 16 + hi * 8;
+        const bool ok = wkk < WK && co < Cout;
         dma_b128(rwt, ok ? (uint32_t)((co * 9 + tap) * CIN + ci) * (uint32_t)sizeof(T) : kOOB,
                  lds_addr(ring + rest * 1024));
     }
-    float bv[VE], av[VE];
-    {
-        const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.bias, a.bias ? (uint32_t)Cout * 4u : 0u);
-        const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.alpha, a.alpha ? (uint32_t)Cout * 4u : 0u);
-        const int co = wn * 32 + cc * VE;
-#pragma unroll
-        for (int e = 0; e < VE; ++e) {
-            const uint32_t off = co + e < Cout ? (uint32_t)(co + e) * 4u : kOOB;
-            bv[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, (int)off, 0, 0));
-            av[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ra, (int)off, 0, 0));
-        }
+    // the wave stores channel groups g = g0 .. g0+NG-1 of each block (all four, or its
+    // half for k-split pairs)
+    const int g0 = WK == 2 ? 2 * wk : 0;
+    if (threadIdx.x < 32 * FN) {
+        const int co = threadIdx.x;
+        bal[0][co] = a.bias && co < Cout ? a.bias[co] : 0.0f;
+        bal[1][co] = a.alpha && co < Cout ? a.alpha[co] : 0.0f;
     }
     halo_wait_vmcnt<0>();
     halo_barrier();
-    vec bw[KSW];
+    vec bw[KSW][FN];
 #pragma unroll
     for (int sw = 0; sw < KSW; ++sw)
-        bw[sw] = *reinterpret_cast<const vec *>(ring + (((wn * WK + wk) * KSW + sw) * 64 + lane) * 16);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            bw[sw][j] = *reinterpret_cast<const vec *>(ring + (((wk * KSW + sw) * FN + j) * 64 + lane) * 16);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): fragments in registers before the ring is reused
     halo_barrier();
 
@@ -150,13 +150,24 @@ __global__ __launch_bounds__(512) void halo3x3_kernel(ConvArgs a, int tiles_w, i
         }
     };
 
-    f32x16 acc[FM];
+    f32x16 acc[FM][FN];
     auto compute = [&](const char *buf) {
+        // start from the bias (the first wave of a k-split pair), lane (rl, hi): channels
+        // 32*j + 8*g + 4*hi + 0..3 in elements 4g..4g+3
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+        for (int j = 0; j < FN; ++j) {
+            f32x16 b0;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][e] = 0.0f;
-        // A operand of tile row wm*FM+i at the wave's k step sw: pixel (row + ky, rl + kx)
+            for (int g = 0; g < 4; ++g) {
+                const f32x4 bq = (WK == 1 || wk == 0) ? *reinterpret_cast<const f32x4 *>(&bal[0][j * 32 + 8 * g + 4 * hi])
+                                                      : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) b0[4 * g + e] = bq[e];
+            }
+#pragma unroll
+            for (int i = 0; i < FM; ++i) acc[i][j] = b0;
+        }
+        // B operand of tile row wm*FM+i at the wave's k step sw: pixel (row + ky, rl + kx)
         // of the halo, 16-channel chunk wk*KCW + sw % KCW, 8-channel half hi.
         const char *base = buf + ((wm * FM) * HW + rl) * PSTR + hi * 16 + wk * KCW * 32;
         auto read = [&](int sw, vec(&fa)[FM]) {
@@ -173,113 +184,148 @@ __global__ __launch_bounds__(512) void halo3x3_kernel(ConvArgs a, int tiles_w, i
             // keep the scheduler from sinking those reads below the products
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int i = 0; i < FM; ++i) acc[i] = Mfma32<T>::run(fa[sw & 1][i], bw[sw], acc[i]);
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) acc[i][j] = Mfma32<T>::run(bw[sw][j], fa[sw & 1][i], acc[i][j]);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
 
-    // Epilogue rows: the wave's q-th 16-row half (block i = q / NHW, half h) holds
-    // pixels 16h + 0..15 of tile row wm*FM + i; a lane finishes row rsub of each half,
-    // channels 32*wn + 8*cc .. +8.
-    const bool has_res = a.res != nullptr, pre = a.res_before_act != 0;
+    // Epilogue: block (i, j) is tile row wm*FM + i, channels 32*j..; lane (rl, hi)
+    // holds pixel rl of the row, 4 channels 32*j + 8*g + 4*hi.. for each of its groups
+    // g. After the math, one lane-half swap per pair of groups (2p, 2p+1) (lanes 32..63
+    // of group 2p trade with lanes 0..31 of group 2p+1, v_permlane32_swap) leaves lane
+    // (rl, hi) with 8 consecutive channels 32*j + 16*p + 8*hi.. of its pixel, stored in
+    // one 16-byte access; the residual is loaded in that layout and swapped back. The
+    // residual mode (none / added before / after the activation) and the activation
+    // are template arguments of the store loop.
+    const bool has_res = a.res != nullptr;
+    const int res_mode = has_res ? (a.res_before_act ? 1 : 2) : 0;
     const uint32_t out_bytes = (uint32_t)((size_t)a.M * Cout * sizeof(T));
     const __amdgpu_buffer_rsrc_t rres = make_rsrc(a.res, has_res ? out_bytes : 0u);
     const __amdgpu_buffer_rsrc_t ry = make_rsrc(a.y, out_bytes);
-    const int co_run = wn * 32 + cc * VE;
-    auto half_of = [&](int q) { return WK == 2 ? wk : q % NHW; };
-    auto out_off = [&](int t, int q) -> uint32_t {
+    const int p0 = g0 / 2;
+    auto out_off = [&](int t, int i, int j, int pp) -> uint32_t {
         const int tx = t % tiles_w, rr = t / tiles_w;
         const int ty = rr % tiles_h, n = rr / tiles_h;
-        const int oy = ty * TH + wm * FM + q / NHW, ox = tx * TW + 16 * half_of(q) + rsub;
-        return (oy < H && ox < W && co_run < Cout)
-                   ? ((uint32_t)((n * H + oy) * W + ox) * (uint32_t)Cout + (uint32_t)co_run) * (uint32_t)sizeof(T)
+        const int oy = ty * TH + wm * FM + i, ox = tx * TW + rl;
+        const int co = j * 32 + 16 * (p0 + pp) + 8 * hi;
+        return (oy < H && ox < W && co < Cout)
+                   ? ((uint32_t)((n * H + oy) * W + ox) * (uint32_t)Cout + (uint32_t)co) * (uint32_t)sizeof(T)
                    : kOOB;
     };
+    // lanes 32..63 of lo trade with lanes 0..31 of hi, for each of the two dwords
+    auto swap_halves = [](u32x2 &lo, u32x2 &hi2) {
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+            const auto r2 = __builtin_amdgcn_permlane32_swap(lo[d], hi2[d], false, false);
+            lo[d] = r2[0];
+            hi2[d] = r2[1];
+        }
+    };
 
-    float *slice = reinterpret_cast<float *>(slices + wave * SLICE);
-    float *mine = reinterpret_cast<float *>(xch + wave * (FM * 2 * 1024));
-    const float *theirs = reinterpret_cast<const float *>(xch + (WK == 2 ? (wave + (wk ? -WM : WM)) : wave) * (FM * 2 * 1024));
+    float *mine = reinterpret_cast<float *>(xch + wave * XBYTES);
+    const float *theirs = reinterpret_cast<const float *>(xch + (WK == 2 ? (wave + (wk ? -WM : WM)) : wave) * XBYTES);
 
     // One tile. Its halo has landed for this wave (the wait in the previous tile's
     // epilogue, or the prologue's): barrier (so it has for every wave), residual loads,
-    // products, [hand the partner the half it stores,] barrier (every wave is done
-    // reading buf), [add the partner's half,] epilogue. Between the epilogue's LDS
-    // phase and its stores, wait for all of this wave's loads (the residual, and the
-    // halo of tile k+1, which has had this tile's products to arrive) and refill buf
-    // with tile k+2.
+    // products, [hand the partner the channel groups it stores,] barrier (every wave
+    // is done reading buf), [add the partner's sums,] wait for all of this wave's
+    // loads (the residual, and the halo of tile k+1, which has had this tile's
+    // products to arrive), refill buf with tile k+2, epilogue and stores.
     auto tile = [&](char *buf, int k) {
         const int t = k * G + r;
         halo_barrier();
-        uint32_t off[NH];
-        u32x4 rv[NH];
+        uint32_t off[FM][FN][NP];
+        u32x4 rv[FM][FN][NP];
 #pragma unroll
-        for (int q = 0; q < NH; ++q) {
-            off[q] = out_off(t, q);
-            rv[q] = has_res ? __builtin_amdgcn_raw_buffer_load_b128(rres, (int)off[q], 0, 0) : u32x4{0u, 0u, 0u, 0u};
-        }
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int pp = 0; pp < NP; ++pp) {
+                    off[i][j][pp] = out_off(t, i, j, pp);
+                    rv[i][j][pp] = has_res ? __builtin_amdgcn_raw_buffer_load_b128(rres, (int)off[i][j][pp], 0, 0)
+                                           : u32x4{0u, 0u, 0u, 0u};
+                }
         compute(buf);
         if constexpr (WK == 2) {
-            const int hs = 1 - wk;  // the half the partner stores
+            const int hs = 1 - wk;  // the channel groups (2hs, 2hs+1) the partner stores
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int u = 0; u < 2; ++u)
-                    *reinterpret_cast<f32x4 *>(mine + ((i * 2 + u) * 64 + lane) * 4) =
-                        f32x4{acc[i][8 * hs + 4 * u], acc[i][8 * hs + 4 * u + 1], acc[i][8 * hs + 4 * u + 2],
-                              acc[i][8 * hs + 4 * u + 3]};
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int u = 0; u < 2; ++u)
+                        *reinterpret_cast<f32x4 *>(mine + (((i * FN + j) * 2 + u) * 64 + lane) * 4) =
+                            f32x4{acc[i][j][8 * hs + 4 * u], acc[i][j][8 * hs + 4 * u + 1],
+                                  acc[i][j][8 * hs + 4 * u + 2], acc[i][j][8 * hs + 4 * u + 3]};
         }
         halo_barrier();
         if constexpr (WK == 2) {
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const f32x4 o = *reinterpret_cast<const f32x4 *>(theirs + ((i * 2 + u) * 64 + lane) * 4);
+                for (int j = 0; j < FN; ++j)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[i][8 * wk + 4 * u + e] += o[e];
-                }
-        }
-        // LDS phase: each 16-row half through the wave's slice, back as 8-channel runs.
-        float v[NH][VE];
+                    for (int u = 0; u < 2; ++u) {
+                        const f32x4 o =
+                            *reinterpret_cast<const f32x4 *>(theirs + (((i * FN + j) * 2 + u) * 64 + lane) * 4);
 #pragma unroll
-        for (int q = 0; q < NH; ++q) {
-            const int i = q / NHW, h = half_of(q);
-#pragma unroll
-            for (int g = 0; g < 2; ++g)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) slice[(g * 8 + hi * 4 + e) * WLD + rl] = acc[i][(2 * h + g) * 4 + e];
-            __builtin_amdgcn_s_waitcnt(0xC07F);
-            __builtin_amdgcn_wave_barrier();
-#pragma unroll
-            for (int e = 0; e < VE; e += 4) {
-                const f32x4 x = *reinterpret_cast<const f32x4 *>(slice + rsub * WLD + cc * VE + e);
-                v[q][e] = x[0];
-                v[q][e + 1] = x[1];
-                v[q][e + 2] = x[2];
-                v[q][e + 3] = x[3];
-            }
-            __builtin_amdgcn_s_waitcnt(0xC07F);
-            __builtin_amdgcn_wave_barrier();
+                        for (int e = 0; e < 4; ++e) acc[i][j][8 * wk + 4 * u + e] += o[e];
+                    }
         }
         halo_wait_vmcnt<0>();
         issue(buf, (k + 2) * G + r);
-        auto finish = [&](auto act_tag) {
+        auto finish = [&](auto act_tag, auto res_tag) {
             constexpr int ACT = decltype(act_tag)::value;
+            constexpr int RES = decltype(res_tag)::value;
 #pragma unroll
-            for (int q = 0; q < NH; ++q) {
-                T rt[VE], out[VE];
-                __builtin_memcpy(rt, &rv[q], 16);
-                epilogue_vec<T, ACT, VE>(v[q], bv, av, rt, has_res, pre, out);
-                u32x4 o;
-                __builtin_memcpy(&o, out, 16);
-                __builtin_amdgcn_raw_buffer_store_b128(o, ry, (int)off[q], 0, 0);
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int pp = 0; pp < NP; ++pp) {
+                        u32x2 q[2];  // the pair's two groups, 4 channels each, packed
+                        u32x2 rq[2] = {u32x2{rv[i][j][pp][0], rv[i][j][pp][1]}, u32x2{rv[i][j][pp][2], rv[i][j][pp][3]}};
+                        if constexpr (RES != 0) swap_halves(rq[0], rq[1]);
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) {
+                            const int g = 2 * pp + h;  // group within the wave's share
+                            T rt[4], out[4];
+                            __builtin_memcpy(rt, &rq[h], 8);
+                            f32x4 al{0.0f, 0.0f, 0.0f, 0.0f};
+                            if constexpr (ACT == CONV2D_ACT_PRELU)
+                                al = *reinterpret_cast<const f32x4 *>(&bal[1][j * 32 + 8 * (g0 + g) + 4 * hi]);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                float x = acc[i][j][4 * (g0 + g) + e];
+                                if constexpr (RES == 1) x += to_f32(rt[e]);
+                                if constexpr (ACT == CONV2D_ACT_RELU) x = __builtin_fmaxf(x, 0.0f);
+                                if constexpr (ACT == CONV2D_ACT_SILU) x = x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+                                if constexpr (ACT == CONV2D_ACT_PRELU) x = x >= 0.0f ? x : al[e] * x;
+                                if constexpr (RES == 2) x += to_f32(rt[e]);
+                                out[e] = from_f32<T>(x);
+                            }
+                            __builtin_memcpy(&q[h], out, 8);
+                        }
+                        swap_halves(q[0], q[1]);
+                        __builtin_amdgcn_raw_buffer_store_b128(u32x4{q[0][0], q[0][1], q[1][0], q[1][1]}, ry,
+                                                               (int)off[i][j][pp], 0, 0);
+                    }
+        };
+        auto with_res = [&](auto act_tag) {
+            switch (res_mode) {
+            case 1: finish(act_tag, std::integral_constant<int, 1>{}); break;
+            case 2: finish(act_tag, std::integral_constant<int, 2>{}); break;
+            default: finish(act_tag, std::integral_constant<int, 0>{}); break;
             }
         };
         switch (a.act) {
-        case CONV2D_ACT_RELU: finish(std::integral_constant<int, CONV2D_ACT_RELU>{}); break;
-        case CONV2D_ACT_SILU: finish(std::integral_constant<int, CONV2D_ACT_SILU>{}); break;
-        case CONV2D_ACT_PRELU: finish(std::integral_constant<int, CONV2D_ACT_PRELU>{}); break;
-        default: finish(std::integral_constant<int, CONV2D_ACT_NONE>{}); break;
+        case CONV2D_ACT_RELU: with_res(std::integral_constant<int, CONV2D_ACT_RELU>{}); break;
+        case CONV2D_ACT_SILU: with_res(std::integral_constant<int, CONV2D_ACT_SILU>{}); break;
+        case CONV2D_ACT_PRELU: with_res(std::integral_constant<int, CONV2D_ACT_PRELU>{}); break;
+        default: with_res(std::integral_constant<int, CONV2D_ACT_NONE>{}); break;
         }
     };
     issue(hb0, r);
@@ -293,7 +339,7 @@ __global__ __launch_bounds__(512) void halo3x3_kernel(ConvArgs a, int tiles_w, i
     halo_wait_vmcnt<0>();
 }
 
-template <typename T, int CIN, int TH, int WN>
+template <typename T, int CIN, int TH, int FN>
 static hipError_t launch_halo_t(const ConvArgs &a, int grid_cap, hipStream_t st) {
     const int tiles_w = (a.W + 31) / 32, tiles_h = (a.H + TH - 1) / TH;
     const long long nt = (long long)a.N * tiles_w * tiles_h;
@@ -302,25 +348,19 @@ static hipError_t launch_halo_t(const ConvArgs &a, int grid_cap, hipStream_t st)
     int grid = ntiles < grid_cap ? ntiles : grid_cap;
     if (grid > 8) grid -= grid % 8;
     constexpr int WK = CIN == 64 ? 2 : 1;
-    hipLaunchKernelGGL((halo3x3_kernel<T, CIN, TH, WN, WK>), dim3(grid), dim3(512), 0, st, a, tiles_w, tiles_h,
-                       ntiles);
-    return hipGetLastError();
+    return launch_kernel(halo3x3_kernel<T, CIN, TH, FN, WK>, dim3(grid), dim3(512), 0, st, a, tiles_w, tiles_h,
+                         ntiles);
 }
 
-// Tile heights per (Cin, waves along Cout): 64-channel layers split k over wave pairs,
-// which leaves 2 (WN = 2) or 4 (WN = 1) waves along the tile rows.
+// Tile heights per (Cin, output blocks per wave): 64-channel layers split k over wave
+// pairs, which leaves 4 waves along the tile rows (8 otherwise); two 32-channel
+// output blocks per wave only with one tile row per wave (registers).
 template <typename T, int CIN>
 static hipError_t launch_halo_c(const ConvArgs &a, const HaloPlan &p, hipStream_t st) {
-    if constexpr (CIN == 64) {
-        if (p.wn == 1 && p.th == 4) return launch_halo_t<T, CIN, 4, 1>(a, p.grid_cap, st);
-        if (p.wn == 1 && p.th == 8) return launch_halo_t<T, CIN, 8, 1>(a, p.grid_cap, st);
-        if (p.wn == 2 && p.th == 4) return launch_halo_t<T, CIN, 4, 2>(a, p.grid_cap, st);
-    } else {
-        if (p.wn == 1 && p.th == 8) return launch_halo_t<T, CIN, 8, 1>(a, p.grid_cap, st);
-        if (p.wn == 1 && p.th == 16) return launch_halo_t<T, CIN, 16, 1>(a, p.grid_cap, st);
-        if (p.wn == 2 && p.th == 4) return launch_halo_t<T, CIN, 4, 2>(a, p.grid_cap, st);
-        if (p.wn == 2 && p.th == 8) return launch_halo_t<T, CIN, 8, 2>(a, p.grid_cap, st);
-    }
+    constexpr int WM = CIN == 64 ? 4 : 8;
+    if (p.fn == 1 && p.th == WM) return launch_halo_t<T, CIN, WM, 1>(a, p.grid_cap, st);
+    if (p.fn == 1 && p.th == 2 * WM) return launch_halo_t<T, CIN, 2 * WM, 1>(a, p.grid_cap, st);
+    if (p.fn == 2 && p.th == WM) return launch_halo_t<T, CIN, WM, 2>(a, p.grid_cap, st);
     return hipErrorInvalidValue;
 }
 

@@ -266,9 +266,8 @@ static hipError_t launch_igemm_t(const ConvArgs &a, hipStream_t st) {
     int tiles_n = (a.Cout + BN - 1) / BN;
     long long g = (long long)tiles_m * tiles_n;
     if (g > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((igemm_kernel<T, BM, BN, WGM, WGN, NCHW, AVEC, BVEC>), dim3((unsigned)g),
-                       dim3(256), 0, st, a, tiles_n);
-    return hipGetLastError();
+    return launch_kernel(igemm_kernel<T, BM, BN, WGM, WGN, NCHW, AVEC, BVEC>, dim3((unsigned)g), dim3(256), 0, st,
+                         a, tiles_n);
 }
 
 template <typename T, int BM, int BN, int WGM, int WGN>

@@ -367,38 +367,37 @@ hipError_t launch_t(const ConvArgs &a, const NhwcPlan &p, float *partials, hipSt
     const int per = (nsteps + splits - 1) / splits;
     dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)splits);
     dim3 block(64 * c.wgm * c.wgn);
+    hipError_t e;
     if (p.nchw_out) {
         if (splits > 1) return hipErrorInvalidValue;  // split-K writes channel-last only
         if (p.tap_inner)
-            hipLaunchKernelGGL((igemm_nhwc_kernel<T, c.bm, c.bn, c.wgm, c.wgn, c.ns, true, false, true>), grid,
-                               block, 0, st, a, tiles_n, per, partials);
+            e = launch_kernel(igemm_nhwc_kernel<T, c.bm, c.bn, c.wgm, c.wgn, c.ns, true, false, true>, grid, block, 0,
+                              st, a, tiles_n, per, partials);
         else
-            hipLaunchKernelGGL((igemm_nhwc_kernel<T, c.bm, c.bn, c.wgm, c.wgn, c.ns, false, false, true>), grid,
-                               block, 0, st, a, tiles_n, per, partials);
+            e = launch_kernel(igemm_nhwc_kernel<T, c.bm, c.bn, c.wgm, c.wgn, c.ns, false, false, true>, grid, block,
+                              0, st, a, tiles_n, per, partials);
     } else if (p.tap_inner) {
         if (splits > 1)
-            hipLaunchKernelGGL((igemm_nhwc_kernel<T, c.bm, c.bn, c.wgm, c.wgn, c.ns, true, true, false>), grid,
-                               block, 0, st, a, tiles_n, per, partials);
+            e = launch_kernel(igemm_nhwc_kernel<T, c.bm, c.bn, c.wgm, c.wgn, c.ns, true, true, false>, grid, block, 0,
+                              st, a, tiles_n, per, partials);
         else
-            hipLaunchKernelGGL((igemm_nhwc_kernel<T, c.bm, c.bn, c.wgm, c.wgn, c.ns, true, false, false>), grid,
-                               block, 0, st, a, tiles_n, per, partials);
+            e = launch_kernel(igemm_nhwc_kernel<T, c.bm, c.bn, c.wgm, c.wgn, c.ns, true, false, false>, grid, block,
+                              0, st, a, tiles_n, per, partials);
     } else {
         if (splits > 1)
-            hipLaunchKernelGGL((igemm_nhwc_kernel<T, c.bm, c.bn, c.wgm, c.wgn, c.ns, false, true, false>), grid,
-                               block, 0, st, a, tiles_n, per, partials);
+            e = launch_kernel(igemm_nhwc_kernel<T, c.bm, c.bn, c.wgm, c.wgn, c.ns, false, true, false>, grid, block,
+                              0, st, a, tiles_n, per, partials);
         else
-            hipLaunchKernelGGL((igemm_nhwc_kernel<T, c.bm, c.bn, c.wgm, c.wgn, c.ns, false, false, false>), grid,
-                               block, 0, st, a, tiles_n, per, partials);
+            e = launch_kernel(igemm_nhwc_kernel<T, c.bm, c.bn, c.wgm, c.wgn, c.ns, false, false, false>, grid, block,
+                              0, st, a, tiles_n, per, partials);
     }
-    hipError_t e = hipGetLastError();
     if (e != hipSuccess || splits == 1) return e;
     constexpr int VE = 16 / (int)sizeof(T);
     long long runs = (long long)a.M * (a.Cout / VE);
     long long blocks = (runs + 255) / 256;
     if (blocks > 256 * 32) blocks = 256 * 32;
-    hipLaunchKernelGGL(splitk_epilogue_kernel<T>, dim3((unsigned)blocks), dim3(256), 0, st, a,
-                       (const float *)partials, splits);
-    return hipGetLastError();
+    return launch_kernel(splitk_epilogue_kernel<T>, dim3((unsigned)blocks), dim3(256), 0, st, a,
+                         (const float *)partials, splits);
 }
 
 template <typename T>

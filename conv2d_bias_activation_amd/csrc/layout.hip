@@ -47,16 +47,14 @@ template <typename T>
 static hipError_t to_nhwc_t(const void *x, void *y, int N, int C, int HW, const void *w, void *w2,
                             int Cout, int taps, hipStream_t st) {
     dim3 grid((HW + 63) / 64, (C + 63) / 64, N);
-    hipLaunchKernelGGL(nchw_to_nhwc_kernel<T>, grid, dim3(256), 0, st, static_cast<const T *>(x),
-                       static_cast<T *>(y), C, HW);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_kernel(nchw_to_nhwc_kernel<T>, grid, dim3(256), 0, st, static_cast<const T *>(x),
+                                 static_cast<T *>(y), C, HW);
     if (e != hipSuccess) return e;
     long long total = (long long)Cout * C * taps;
     long long blocks = (total + 255) / 256;
     if (blocks > 8192) blocks = 8192;
-    hipLaunchKernelGGL(oihw_to_ohwi_kernel<T>, dim3((unsigned)blocks), dim3(256), 0, st,
-                       static_cast<const T *>(w), static_cast<T *>(w2), Cout, C, taps);
-    return hipGetLastError();
+    return launch_kernel(oihw_to_ohwi_kernel<T>, dim3((unsigned)blocks), dim3(256), 0, st,
+                         static_cast<const T *>(w), static_cast<T *>(w2), Cout, C, taps);
 }
 
 hipError_t launch_to_channel_last(const void *x, void *x_nhwc, int N, int C, int HW, const void *w,

@@ -196,16 +196,15 @@ static hipError_t maxpool_t(const void *x, void *y, int N, int H, int W, int C, 
     T *yp = static_cast<T *>(y);
     if (!nchw && vec) {
         long long items = (long long)N * OH * OW * (C / Vec16<T>::n);
-        hipLaunchKernelGGL(maxpool_nhwc_vec<T>, dim3(pool_grid(items)), dim3(256), 0, st, xp, yp, N, H,
-                           W, C, OH, OW);
+        return launch_kernel(maxpool_nhwc_vec<T>, dim3(pool_grid(items)), dim3(256), 0, st, xp, yp, N, H, W, C,
+                             OH, OW);
     } else if (nchw) {
-        hipLaunchKernelGGL((maxpool_scalar<T, true>), dim3(pool_grid((long long)N * OH * OW * C)), dim3(256),
-                           0, st, xp, yp, N, H, W, C, OH, OW);
+        return launch_kernel(maxpool_scalar<T, true>, dim3(pool_grid((long long)N * OH * OW * C)), dim3(256), 0,
+                             st, xp, yp, N, H, W, C, OH, OW);
     } else {
-        hipLaunchKernelGGL((maxpool_scalar<T, false>), dim3(pool_grid((long long)N * OH * OW * C)), dim3(256),
-                           0, st, xp, yp, N, H, W, C, OH, OW);
+        return launch_kernel(maxpool_scalar<T, false>, dim3(pool_grid((long long)N * OH * OW * C)), dim3(256), 0,
+                             st, xp, yp, N, H, W, C, OH, OW);
     }
-    return hipGetLastError();
 }
 
 template <typename T>
@@ -216,16 +215,15 @@ static hipError_t avgpool_t(const void *x, void *y, int N, int H, int W, int C, 
     T *yp = static_cast<T *>(y);
     if (!nchw && vec) {
         long long items = (long long)N * OH * OW * (C / Vec16<T>::n);
-        hipLaunchKernelGGL(avgpool_nhwc_vec<T>, dim3(pool_grid(items)), dim3(256), 0, st, xp, yp, N, H,
-                           W, C, OH, OW);
+        return launch_kernel(avgpool_nhwc_vec<T>, dim3(pool_grid(items)), dim3(256), 0, st, xp, yp, N, H, W, C,
+                             OH, OW);
     } else if (nchw) {
-        hipLaunchKernelGGL((avgpool_scalar<T, true>), dim3(pool_grid((long long)N * OH * OW * C)), dim3(256),
-                           0, st, xp, yp, N, H, W, C, OH, OW);
+        return launch_kernel(avgpool_scalar<T, true>, dim3(pool_grid((long long)N * OH * OW * C)), dim3(256), 0,
+                             st, xp, yp, N, H, W, C, OH, OW);
     } else {
-        hipLaunchKernelGGL((avgpool_scalar<T, false>), dim3(pool_grid((long long)N * OH * OW * C)), dim3(256),
-                           0, st, xp, yp, N, H, W, C, OH, OW);
+        return launch_kernel(avgpool_scalar<T, false>, dim3(pool_grid((long long)N * OH * OW * C)), dim3(256), 0,
+                             st, xp, yp, N, H, W, C, OH, OW);
     }
-    return hipGetLastError();
 }
 
 hipError_t launch_maxpool(const void *x, void *y, int N, int H, int W, int C, bool nchw, int dtype,
