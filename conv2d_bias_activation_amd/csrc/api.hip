@@ -260,28 +260,32 @@ NhwcPlan plan_nhwc(const ConvArgs &a) {
 }
 
 // Halo-tile kernel for narrow 3x3 stride-1 layers: one wave covers all the output
-// channels (32 or 64); tile height WM rows (one per wave along the rows: 8, or 4 when
-// k is split over wave pairs at Cin 64) or, for 32 channels, possibly 2*WM, taking
-// the height with the least work per CU over one GPU's 256 CUs, counting a tile of
-// TH rows as TH + 4 (its two halo rows and a fixed cost, from MI355X timings of the
-// ResNet stem and stage-1 layers); ties go to the taller tile.
+// channels (32 or 64). Cin <= 32: 4-wave workgroups, two per CU (their epilogues
+// overlap each other's products); Cin 64: 8-wave workgroups with k split over wave
+// pairs (a 4-wave one would have 2-row tiles, whose halo costs as much as the tile).
+// Tile height WM rows (one per wave along the rows) or, for 32 channels, possibly
+// 2*WM, taking the height with the least work per workgroup slot over one GPU's 256
+// CUs, counting a tile of TH rows as TH + 4 (its two halo rows and a fixed cost;
+// from MI355X timings of the ResNet stem and stage-1 layers); ties go to the taller.
 HaloPlan plan_halo(const ConvArgs &a) {
     HaloPlan p{};
     p.fn = a.Cout <= 32 ? 1 : 2;
-    const int wm = a.Cin == 64 ? 4 : 8;
+    p.waves = a.Cin == 64 ? 8 : 4;
+    const int wm = a.Cin == 64 ? p.waves / 2 : p.waves;
+    const int slots = 256 * (8 / p.waves);
     p.th = wm;
     if (p.fn == 1) {
         long long best = 0;
         for (int th : {2 * wm, wm}) {
             const long long nt = (long long)a.N * ((a.W + 31) / 32) * ((a.H + th - 1) / th);
-            const long long cost = (nt + 255) / 256 * (th + 4);
+            const long long cost = (nt + slots - 1) / slots * (th + 4);
             if (best == 0 || cost < best) {
                 best = cost;
                 p.th = th;
             }
         }
     }
-    p.grid_cap = 256;
+    p.grid_cap = slots;
     return p;
 }
 
@@ -337,7 +341,8 @@ int describe(const Plan &p, int layout, int dtype, char *buf, int cap) {
         snprintf(tmp, sizeof tmp, "direct_%s %s cob32", layout == CONV2D_LAYOUT_NCHW ? "nchw" : "nhwc",
                  dtype_name(dtype));
     } else if (p.family == FAM_HALO) {
-        snprintf(tmp, sizeof tmp, "halo3x3_nhwc %s th%d co%d", dtype_name(dtype), p.halo.th, 32 * p.halo.fn);
+        snprintf(tmp, sizeof tmp, "halo3x3_nhwc %s th%d co%d w%d", dtype_name(dtype), p.halo.th, 32 * p.halo.fn,
+                 p.halo.waves);
     } else if (p.family == FAM_NHWC || p.family == FAM_NCHW_VIA_NHWC) {
         snprintf(tmp, sizeof tmp, "%sigemm_nhwc_pipe%s %s %s splitk=%d",
                  p.family == FAM_NCHW_VIA_NHWC ? "to_nhwc+" : "", p.nh.tap_inner ? "_tapinner" : "",
@@ -425,8 +430,10 @@ int conv2d_fused(const void *x, const void *w, const float *bias, const float *a
     if (p.family == FAM_DIRECT) {
         e = launch_direct(a, dtype, layout == CONV2D_LAYOUT_NCHW, st);
     } else if (p.family == FAM_HALO) {
-        rc = device_cus(&p.halo.grid_cap);
+        int cus = 0;
+        rc = device_cus(&cus);
         if (rc) return rc;
+        p.halo.grid_cap = cus * (8 / p.halo.waves);
         e = launch_halo3x3(a, dtype, p.halo, st);
     } else if (p.family == FAM_NHWC) {
         float *scratch = nullptr;

@@ -13,8 +13,11 @@
 //  * Weights stay in registers: one wave's 32*FN output channels over its share of the
 //    9*Cin k are 9*Cin*FN/(16*WK) operand fragments of 4 VGPRs (72 per 32 channels at
 //    Cin 32, or at Cin 64 with k split over a pair of waves). A workgroup copies the
-//    weights into LDS once, in fragment order, and every wave reads its fragments
-//    from there. With FN = 2 every pixel operand read from LDS feeds two products.
+//    weights into LDS once, in fragment order and in chunks the size of the halo
+//    buffers, and every wave reads its fragments from there. With FN = 2 every pixel
+//    operand read from LDS feeds two products.
+//  * 4-wave workgroups run two to a CU: their tiles drift out of step, so one's
+//    epilogue (vector-memory and VALU bound) overlaps the other's products.
 //  * Workgroups are persistent: each walks tiles t = k*G + r (r its XCD-grouped
 //    index among G), with the halo of tile k+2 loading into the buffer tile k just
 //    released while tile k's epilogue and tile k+1's products run. Bias and slopes
@@ -48,10 +51,9 @@ __device__ __forceinline__ void halo_barrier() {
 // CIN input channels (16, 32 or 64); TH output rows per tile (tiles are TH x 32);
 // FN 32-channel output blocks per wave (the workgroup covers 32*FN channels); WK
 // waves along k (each takes CIN/WK of the input channels of every tap and the pair
-// adds their sums through LDS); 8 / WK waves along the tile rows.
-template <typename T, int CIN, int TH, int FN, int WK>
-__global__ __launch_bounds__(512) void halo3x3_kernel(ConvArgs a, int tiles_w, int tiles_h, int ntiles) {
-    constexpr int NW = 8;
+// adds their sums through LDS); NW / WK waves along the tile rows.
+template <typename T, int CIN, int TH, int FN, int WK, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void halo3x3_kernel(ConvArgs a, int tiles_w, int tiles_h, int ntiles) {
     constexpr int WM = NW / WK;
     constexpr int FM = TH / WM;               // 32-pixel tile rows per wave
     static_assert(WM >= 1 && FM >= 1 && FM * WM == TH, "tile rows split evenly over the waves");
@@ -67,9 +69,12 @@ __global__ __launch_bounds__(512) void halo3x3_kernel(ConvArgs a, int tiles_w, i
     static_assert(KC % WK == 0, "k split");
     constexpr int KCW = KC / WK;              // of them per wave
     constexpr int KSW = 9 * KCW;              // k steps per wave
-    constexpr int WBYTES = WK * KSW * FN * 1024;  // weights in operand order
-    constexpr int NDWW = (WBYTES + NW * 1024 - 1) / (NW * 1024);
-    constexpr int RING = cmax<2 * HBUF, NDWW * NW * 1024>::v;
+    constexpr int WUNITS = WK * KSW * FN;     // weights in operand order, 1 KiB units
+    constexpr int RING = 2 * HBUF;            // two halo buffers; weights pass through in chunks
+    constexpr int CUNITS = RING / 1024;       // units per chunk
+    constexpr int NCH = (WUNITS + CUNITS - 1) / CUNITS;
+    static_assert(CUNITS % NW == 0, "whole chunks per wave");
+    constexpr int NDWW = CUNITS / NW;         // loads per lane per chunk
     constexpr int NG = 4 / WK;                // 4-channel groups of each block this wave stores
     constexpr int NP = NG / 2;                // pairs of them: one 16-byte store per lane
     constexpr int XBYTES = FM * FN * 2 * 1024;  // per wave: 8 floats per lane per block
@@ -96,15 +101,17 @@ __global__ __launch_bounds__(512) void halo3x3_kernel(ConvArgs a, int tiles_w, i
     // runs straight from registers. The accumulators start from the bias; bias and
     // slopes sit in a small LDS table.
     const i32x4 rwt = rsrc_words(a.w, (uint32_t)((size_t)Cout * 9 * CIN * sizeof(T)));
+    auto stage_chunk = [&](int c) {
 #pragma unroll
-    for (int d = 0; d < NDWW; ++d) {
-        const int rest = d * NW + wave;
-        const int j = rest % FN, sw = (rest / FN) % KSW, wkk = rest / (FN * KSW);
-        const int co = j * 32 + rl, tap = sw / KCW, ci = (wkk * KCW + sw % KCW) * 16 + hi * 8;
-        const bool ok = wkk < WK && co < Cout;
-        dma_b128(rwt, ok ? (uint32_t)((co * 9 + tap) * CIN + ci) * (uint32_t)sizeof(T) : kOOB,
-                 lds_addr(ring + rest * 1024));
-    }
+        for (int d = 0; d < NDWW; ++d) {
+            const int slot = d * NW + wave, u = c * CUNITS + slot;
+            const int j = u % FN, sw = (u / FN) % KSW, wkk = u / (FN * KSW);
+            const int co = j * 32 + rl, tap = sw / KCW, ci = (wkk * KCW + sw % KCW) * 16 + hi * 8;
+            const bool ok = u < WUNITS && co < Cout;
+            dma_b128(rwt, ok ? (uint32_t)((co * 9 + tap) * CIN + ci) * (uint32_t)sizeof(T) : kOOB,
+                     lds_addr(ring + slot * 1024));
+        }
+    };
     // the wave stores channel groups g = g0 .. g0+NG-1 of each block (all four, or its
     // half for k-split pairs)
     const int g0 = WK == 2 ? 2 * wk : 0;
@@ -113,16 +120,23 @@ __global__ __launch_bounds__(512) void halo3x3_kernel(ConvArgs a, int tiles_w, i
         bal[0][co] = a.bias && co < Cout ? a.bias[co] : 0.0f;
         bal[1][co] = a.alpha && co < Cout ? a.alpha[co] : 0.0f;
     }
-    halo_wait_vmcnt<0>();
-    halo_barrier();
     vec bw[KSW][FN];
 #pragma unroll
-    for (int sw = 0; sw < KSW; ++sw)
+    for (int c = 0; c < NCH; ++c) {
+        stage_chunk(c);
+        halo_wait_vmcnt<0>();
+        halo_barrier();
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-            bw[sw][j] = *reinterpret_cast<const vec *>(ring + (((wk * KSW + sw) * FN + j) * 64 + lane) * 16);
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): fragments in registers before the ring is reused
-    halo_barrier();
+        for (int sw = 0; sw < KSW; ++sw)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int u = (wk * KSW + sw) * FN + j - c * CUNITS;
+                if (NCH == 1 || (u >= 0 && u < CUNITS))
+                    bw[sw][j] = *reinterpret_cast<const vec *>(ring + (u * 64 + lane) * 16);
+            }
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): fragments in registers before the ring is reused
+        halo_barrier();
+    }
 
     // Tile order: G workgroups, the ones on one XCD (blockIdx % 8) take a contiguous
     // run of each round's G tiles, so neighbouring tiles share halo rows in one L2.
@@ -339,7 +353,7 @@ __global__ __launch_bounds__(512) void halo3x3_kernel(ConvArgs a, int tiles_w, i
     halo_wait_vmcnt<0>();
 }
 
-template <typename T, int CIN, int TH, int FN>
+template <typename T, int CIN, int TH, int FN, int NW>
 static hipError_t launch_halo_t(const ConvArgs &a, int grid_cap, hipStream_t st) {
     const int tiles_w = (a.W + 31) / 32, tiles_h = (a.H + TH - 1) / TH;
     const long long nt = (long long)a.N * tiles_w * tiles_h;
@@ -348,19 +362,27 @@ static hipError_t launch_halo_t(const ConvArgs &a, int grid_cap, hipStream_t st)
     int grid = ntiles < grid_cap ? ntiles : grid_cap;
     if (grid > 8) grid -= grid % 8;
     constexpr int WK = CIN == 64 ? 2 : 1;
-    return launch_kernel(halo3x3_kernel<T, CIN, TH, FN, WK>, dim3(grid), dim3(512), 0, st, a, tiles_w, tiles_h,
-                         ntiles);
+    return launch_kernel(halo3x3_kernel<T, CIN, TH, FN, WK, NW>, dim3(grid), dim3(64 * NW), 0, st, a, tiles_w,
+                         tiles_h, ntiles);
 }
 
-// Tile heights per (Cin, output blocks per wave): 64-channel layers split k over wave
-// pairs, which leaves 4 waves along the tile rows (8 otherwise); two 32-channel
-// output blocks per wave only with one tile row per wave (registers).
+// Tile heights per (Cin, output blocks per wave, waves): 64-channel layers split k
+// over wave pairs, which leaves NW/2 waves along the tile rows (NW otherwise); two
+// 32-channel output blocks per wave only with one tile row per wave (registers).
+// 4-wave workgroups run two to a CU (p.grid_cap counts workgroups).
+template <typename T, int CIN, int NW>
+static hipError_t launch_halo_w(const ConvArgs &a, const HaloPlan &p, hipStream_t st) {
+    constexpr int WM = CIN == 64 ? NW / 2 : NW;
+    if (p.fn == 1 && p.th == WM) return launch_halo_t<T, CIN, WM, 1, NW>(a, p.grid_cap, st);
+    if (p.fn == 1 && p.th == 2 * WM) return launch_halo_t<T, CIN, 2 * WM, 1, NW>(a, p.grid_cap, st);
+    if (p.fn == 2 && p.th == WM) return launch_halo_t<T, CIN, WM, 2, NW>(a, p.grid_cap, st);
+    return hipErrorInvalidValue;
+}
+
 template <typename T, int CIN>
 static hipError_t launch_halo_c(const ConvArgs &a, const HaloPlan &p, hipStream_t st) {
-    constexpr int WM = CIN == 64 ? 4 : 8;
-    if (p.fn == 1 && p.th == WM) return launch_halo_t<T, CIN, WM, 1>(a, p.grid_cap, st);
-    if (p.fn == 1 && p.th == 2 * WM) return launch_halo_t<T, CIN, 2 * WM, 1>(a, p.grid_cap, st);
-    if (p.fn == 2 && p.th == WM) return launch_halo_t<T, CIN, WM, 2>(a, p.grid_cap, st);
+    if (p.waves == 8) return launch_halo_w<T, CIN, 8>(a, p, st);
+    if (p.waves == 4) return launch_halo_w<T, CIN, 4>(a, p, st);
     return hipErrorInvalidValue;
 }
 

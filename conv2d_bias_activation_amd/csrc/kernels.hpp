@@ -65,14 +65,15 @@ hipError_t launch_igemm_nhwc(const ConvArgs &a, int dtype, const NhwcPlan &p, fl
 struct HaloPlan {
     int th;        // output rows per 32-pixel-wide tile
     int fn;        // 32-channel output blocks per wave: 1 (Cout <= 32) or 2 (Cout <= 64)
-    int grid_cap;  // persistent workgroups (one per CU)
+    int waves;     // per workgroup: 8, or 4 (two workgroups per CU)
+    int grid_cap;  // persistent workgroups
 };
 
 // 3x3 stride-1 pad-1 channel-last 16-bit convolution with halo tiles and weights held
 // in registers: Cin 16, 32 or 64, Cout <= 32 * p.fn with Cout % 8 == 0, x and w
 // 16-byte aligned, y and the residual 16-byte aligned (a.vec_out), tensors under
-// 2 GiB. With WM = 8 (Cin <= 32) or 4 (Cin 64): p.th in {WM, 2*WM} for p.fn = 1,
-// p.th = WM for p.fn = 2.
+// 2 GiB. With WM = p.waves (Cin <= 32) or p.waves / 2 (Cin 64): p.th in {WM, 2*WM}
+// for p.fn = 1, p.th = WM for p.fn = 2.
 hipError_t launch_halo3x3(const ConvArgs &a, int dtype, const HaloPlan &p, hipStream_t st);
 
 // Direct convolution on the vector ALUs for few input channels (the image stem):

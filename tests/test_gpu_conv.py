@@ -108,6 +108,8 @@ HALO = [
     (4, 256, 256, 16, 32, "relu", None, "bf16"),
     (2, 150, 200, 64, 64, "prelu", "pre", "f16"),
     (2, 160, 160, 32, 48, "silu", "post", "bf16"),
+    (4, 256, 256, 64, 32, "relu", "pre", "bf16"),
+    (2, 64, 100, 16, 64, "silu", None, "f16"),
 ]
 
 
