@@ -128,7 +128,7 @@ int check_conv(const void *x, const void *w, const float *alpha, const void *res
     return CONV2D_OK;
 }
 
-enum Family { FAM_DIRECT = 0, FAM_IGEMM = 1, FAM_NHWC = 2, FAM_NCHW_VIA_NHWC = 3, FAM_HALO = 4 };
+enum Family { FAM_DIRECT = 0, FAM_IGEMM = 1, FAM_NHWC = 2, FAM_NCHW_VIA_NHWC = 3, FAM_HALO = 4, FAM_STEM = 5 };
 
 struct Plan {
     int family;
@@ -295,9 +295,21 @@ bool halo_fits(const ConvArgs &a, int layout, int dtype) {
            (a.Cout % 8) == 0 && a.vec_out && aligned16(a.x) && aligned16(a.w);
 }
 
+// Matrix-core stem kernel: 3-channel channel-last 16-bit image, 3x3, pad 1.
+bool stem_fits(const ConvArgs &a, int layout, int dtype) {
+    return layout == CONV2D_LAYOUT_NHWC && dtype != CONV2D_DTYPE_F32 && a.Cin == 3 && a.kh == 3 && a.kw == 3 &&
+           a.pad == 1 && (a.stride == 1 || a.stride == 2) && a.Cout <= 64 && (a.Cout % 8) == 0 && a.vec_out &&
+           aligned16(a.x) && (a.W % 8) == 0 && a.W <= 3000 && (long long)a.N * a.H * a.W * 6 < (1ll << 31) &&
+           (long long)a.M * a.Cout * 2 < (1ll << 31);
+}
+
 Plan make_plan(const ConvArgs &a, int layout, int dtype) {
     Plan p{};
     const int ve = 16 / dtype_bytes(dtype);
+    if (stem_fits(a, layout, dtype)) {
+        p.family = FAM_STEM;
+        return p;
+    }
     if (a.Cin <= 4) {
         p.family = FAM_DIRECT;
         return p;
@@ -340,6 +352,8 @@ int describe(const Plan &p, int layout, int dtype, char *buf, int cap) {
     if (p.family == FAM_DIRECT) {
         snprintf(tmp, sizeof tmp, "direct_%s %s cob32", layout == CONV2D_LAYOUT_NCHW ? "nchw" : "nhwc",
                  dtype_name(dtype));
+    } else if (p.family == FAM_STEM) {
+        snprintf(tmp, sizeof tmp, "stem3x3_mfma %s", dtype_name(dtype));
     } else if (p.family == FAM_HALO) {
         snprintf(tmp, sizeof tmp, "halo3x3_nhwc %s th%d co%d w%d", dtype_name(dtype), p.halo.th, 32 * p.halo.fn,
                  p.halo.waves);
@@ -429,6 +443,8 @@ int conv2d_fused(const void *x, const void *w, const float *bias, const float *a
     hipError_t e;
     if (p.family == FAM_DIRECT) {
         e = launch_direct(a, dtype, layout == CONV2D_LAYOUT_NCHW, st);
+    } else if (p.family == FAM_STEM) {
+        e = launch_stem3(a, dtype, st);
     } else if (p.family == FAM_HALO) {
         int cus = 0;
         rc = device_cus(&cus);

@@ -190,17 +190,21 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void halo3x3_kernel(ConvArgs a, in
             for (int i = 0; i < FM; ++i)
                 fa[i] = *reinterpret_cast<const vec *>(base + ((i + ky) * HW + kx) * PSTR + (sw % KCW) * 32);
         };
-        vec fa[2][FM];
-        read(0, fa[0]);
+        // operand reads run PF k steps ahead of the products
+        constexpr int PF = 2;
+        vec fa[PF + 1][FM];
+#pragma unroll
+        for (int sw = 0; sw < PF && sw < KSW; ++sw) read(sw, fa[sw]);
 #pragma unroll
         for (int sw = 0; sw < KSW; ++sw) {
-            if (sw + 1 < KSW) read(sw + 1, fa[(sw + 1) & 1]);
+            if (sw + PF < KSW) read(sw + PF, fa[(sw + PF) % (PF + 1)]);
             // keep the scheduler from sinking those reads below the products
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int j = 0; j < FN; ++j) acc[i][j] = Mfma32<T>::run(bw[sw][j], fa[sw & 1][i], acc[i][j]);
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = Mfma32<T>::run(bw[sw][j], fa[sw % (PF + 1)][i], acc[i][j]);
             __builtin_amdgcn_sched_barrier(0);
         }
     };

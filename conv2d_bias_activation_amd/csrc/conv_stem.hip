@@ -1,0 +1,244 @@
+// 3x3 convolution of a 3-channel channel-last 16-bit image (the stem conv of the
+// inferencelayer page's `encoder_maps`: stride 2, pad 1) on CDNA4 matrix cores.
+//
+// K = 27 is too thin for a tiled GEMM, and on the vector ALUs the 27 x Cout fp32
+// multiply-adds per pixel would cost more than moving the image and the feature map.
+// Here one 32x32x16 product pair covers 32 pixels x 32 output channels:
+//
+//  * K is laid out as the three 9-value image rows of the 3x3x3 patch (ky, then kx
+//    and channel, which is how both the image row and the OHWI weight row are stored):
+//    step 0 takes values 0..7 of patch row 0 (lanes 0-31) and of row 1 (lanes 32-63),
+//    step 1 values 0..7 of row 2 and, in lanes 32-63, the three leftover values 8 of
+//    rows 0-2 and five zeros. Weights are the A operand (built once per lane in that
+//    order), pixels the B operand.
+//  * A workgroup stages the input rows that its output rows need, whole, in LDS
+//    (16-byte loads, zero rows for padding, a zero pixel in front for the left pad).
+//    A lane's 8 consecutive values start 2-byte aligned, so it reads 5 dwords of the
+//    row and shifts them together in pairs (v_alignbit).
+//  * The epilogue is the channel-last one of the halo kernel: the accumulators start
+//    from the bias, channel groups are paired by a lane-half swap and stored as
+//    8-channel 16-byte runs.
+#include "igemm_common.hpp"
+#include "kernels.hpp"
+
+namespace c2d {
+
+// FN 32-channel output blocks (Cout <= 32*FN); RB output rows per workgroup; S stride.
+template <typename T, int FN, int RB, int S>
+__global__ __launch_bounds__(256) void stem3_kernel(ConvArgs a, int rstr) {
+    constexpr int NW = 4;
+    constexpr int RS = (RB - 1) * S + 3;  // input rows staged
+    extern __shared__ __attribute__((aligned(16))) char srow[];  // [RS][rstr] bytes
+    __shared__ __attribute__((aligned(16))) float bal[2][32 * FN];
+    typedef typename Mfma32<T>::vec vec;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int rl = lane & 31, hi = lane >> 5;
+    const int H = a.H, W = a.W, OH = a.OH, OW = a.OW, Cout = a.Cout;
+    const int rows_per_img = (OH + RB - 1) / RB;
+    const int n = blockIdx.x / rows_per_img;
+    const int oy0 = (blockIdx.x - n * rows_per_img) * RB;
+
+    // Weights as the A operand: lane (co = 32j + rl, hi), step 0: values 0..7 of patch
+    // row hi; step 1: values 0..7 of row 2 (hi = 0) or value 8 of rows 0, 1, 2 (hi = 1).
+    vec wa[2][FN];
+    {
+        const T *w = static_cast<const T *>(a.w);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int co = j * 32 + rl;
+            T v0[8], v1[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                v0[e] = co < Cout ? w[co * 27 + hi * 9 + e] : from_f32<T>(0.0f);
+                const int k1 = hi == 0 ? 18 + e : (e < 3 ? e * 9 + 8 : -1);
+                v1[e] = (co < Cout && k1 >= 0) ? w[co * 27 + k1] : from_f32<T>(0.0f);
+            }
+            __builtin_memcpy(&wa[0][j], v0, 16);
+            __builtin_memcpy(&wa[1][j], v1, 16);
+        }
+    }
+    if (threadIdx.x < 32 * FN) {
+        const int co = threadIdx.x;
+        bal[0][co] = a.bias && co < Cout ? a.bias[co] : 0.0f;
+        bal[1][co] = a.alpha && co < Cout ? a.alpha[co] : 0.0f;
+    }
+
+    // Stage input rows iy = oy0*S - 1 + r, r < RS: LDS row r = [16 zero bytes][W x 6
+    // bytes][zeros up to rstr]; the pixel at column ix starts at byte 16 + 6*ix.
+    {
+        const int row_bytes = W * 6;
+        const int chunks = rstr / 16;
+        const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint32_t)((size_t)a.N * H * row_bytes));
+        for (int i = threadIdx.x; i < RS * chunks; i += 256) {
+            const int r = i / chunks, c = i - r * chunks;
+            const int iy = oy0 * S - 1 + r;
+            const int b = c * 16 - 16;  // byte within the image row
+            u32x4 v = u32x4{0u, 0u, 0u, 0u};
+            if (b >= 0 && b < row_bytes && (unsigned)iy < (unsigned)H)
+                v = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)((size_t)(n * H + iy) * row_bytes + b), 0, 0);
+            *reinterpret_cast<u32x4 *>(srow + r * rstr + c * 16) = v;
+        }
+    }
+    __syncthreads();
+
+    const uint32_t out_bytes = (uint32_t)((size_t)a.M * Cout * sizeof(T));
+    const bool has_res = a.res != nullptr;
+    const int res_mode = has_res ? (a.res_before_act ? 1 : 2) : 0;
+    const __amdgpu_buffer_rsrc_t rres = make_rsrc(a.res, has_res ? out_bytes : 0u);
+    const __amdgpu_buffer_rsrc_t ry = make_rsrc(a.y, out_bytes);
+    auto swap_halves = [](u32x2 &lo, u32x2 &hi2) {
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+            const auto r2 = __builtin_amdgcn_permlane32_swap(lo[d], hi2[d], false, false);
+            lo[d] = r2[0];
+            hi2[d] = r2[1];
+        }
+    };
+
+    const int tasks_w = (OW + 31) / 32;
+    for (int task = wave; task < RB * tasks_w; task += NW) {
+        const int rr = task / tasks_w, ox0 = (task - rr * tasks_w) * 32;
+        const int oy = oy0 + rr, ox = ox0 + rl;
+        if (oy >= OH) break;
+        // The 9 values of patch row ky sit at bytes 16 + 6*(ox*S - 1) .. +18 of staged row
+        // rr*S + ky; read the 5 dwords from the one below that offset and shift. Lanes
+        // past the row end read the last pixel's patch (their outputs are not stored).
+        const int byte = 16 + 6 * ((ox < OW ? ox : OW - 1) * S - 1);
+        const int base = byte & ~3, sh = (byte & 3) * 8;
+        uint32_t pr[3][4], p8[3];
+#pragma unroll
+        for (int ky = 0; ky < 3; ++ky) {
+            const uint32_t *src = reinterpret_cast<const uint32_t *>(srow + (rr * S + ky) * rstr + base);
+            uint32_t d[5];
+#pragma unroll
+            for (int i = 0; i < 5; ++i) d[i] = src[i];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pr[ky][i] = __builtin_amdgcn_alignbit(d[i + 1], d[i], sh);
+            p8[ky] = (d[4] >> sh) & 0xffffu;
+        }
+        vec xb[2];
+        {
+            uint32_t b0[4], b1[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                b0[i] = hi ? pr[1][i] : pr[0][i];
+                b1[i] = hi ? 0u : pr[2][i];
+            }
+            if (hi) {
+                b1[0] = p8[0] | (p8[1] << 16);
+                b1[1] = p8[2];
+            }
+            __builtin_memcpy(&xb[0], b0, 16);
+            __builtin_memcpy(&xb[1], b1, 16);
+        }
+        f32x16 acc[FN];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const f32x4 bq = *reinterpret_cast<const f32x4 *>(&bal[0][j * 32 + 8 * g + 4 * hi]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[j][4 * g + e] = bq[e];
+            }
+            acc[j] = Mfma32<T>::run(wa[0][j], xb[0], acc[j]);
+            acc[j] = Mfma32<T>::run(wa[1][j], xb[1], acc[j]);
+        }
+        // Epilogue: lane (rl, hi) holds channels 32j + 8g + 4hi.. of pixel ox; pairs of
+        // groups become 8-channel runs 32j + 16p + 8hi.. after the lane-half swap.
+        const bool live = oy < OH && ox < OW;
+        uint32_t off[FN][2];
+        u32x4 rv[FN][2];
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp) {
+                const int co = j * 32 + 16 * pp + 8 * hi;
+                off[j][pp] = (live && co < Cout)
+                                 ? ((uint32_t)((n * OH + oy) * OW + ox) * (uint32_t)Cout + (uint32_t)co) *
+                                       (uint32_t)sizeof(T)
+                                 : kOOB;
+                rv[j][pp] = has_res ? __builtin_amdgcn_raw_buffer_load_b128(rres, (int)off[j][pp], 0, 0)
+                                    : u32x4{0u, 0u, 0u, 0u};
+            }
+        auto finish = [&](auto act_tag, auto res_tag) {
+            constexpr int ACT = decltype(act_tag)::value;
+            constexpr int RES = decltype(res_tag)::value;
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int pp = 0; pp < 2; ++pp) {
+                    u32x2 q[2];
+                    u32x2 rq[2] = {u32x2{rv[j][pp][0], rv[j][pp][1]}, u32x2{rv[j][pp][2], rv[j][pp][3]}};
+                    if constexpr (RES != 0) swap_halves(rq[0], rq[1]);
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const int g = 2 * pp + h;
+                        T rt[4], out[4];
+                        __builtin_memcpy(rt, &rq[h], 8);
+                        f32x4 al{0.0f, 0.0f, 0.0f, 0.0f};
+                        if constexpr (ACT == CONV2D_ACT_PRELU)
+                            al = *reinterpret_cast<const f32x4 *>(&bal[1][j * 32 + 8 * g + 4 * hi]);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            float x = acc[j][4 * g + e];
+                            if constexpr (RES == 1) x += to_f32(rt[e]);
+                            if constexpr (ACT == CONV2D_ACT_RELU) x = __builtin_fmaxf(x, 0.0f);
+                            if constexpr (ACT == CONV2D_ACT_SILU) x = x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+                            if constexpr (ACT == CONV2D_ACT_PRELU) x = x >= 0.0f ? x : al[e] * x;
+                            if constexpr (RES == 2) x += to_f32(rt[e]);
+                            out[e] = from_f32<T>(x);
+                        }
+                        __builtin_memcpy(&q[h], out, 8);
+                    }
+                    swap_halves(q[0], q[1]);
+                    __builtin_amdgcn_raw_buffer_store_b128(u32x4{q[0][0], q[0][1], q[1][0], q[1][1]}, ry,
+                                                           (int)off[j][pp], 0, 0);
+                }
+        };
+        auto with_res = [&](auto act_tag) {
+            switch (res_mode) {
+            case 1: finish(act_tag, std::integral_constant<int, 1>{}); break;
+            case 2: finish(act_tag, std::integral_constant<int, 2>{}); break;
+            default: finish(act_tag, std::integral_constant<int, 0>{}); break;
+            }
+        };
+        switch (a.act) {
+        case CONV2D_ACT_RELU: with_res(std::integral_constant<int, CONV2D_ACT_RELU>{}); break;
+        case CONV2D_ACT_SILU: with_res(std::integral_constant<int, CONV2D_ACT_SILU>{}); break;
+        case CONV2D_ACT_PRELU: with_res(std::integral_constant<int, CONV2D_ACT_PRELU>{}); break;
+        default: with_res(std::integral_constant<int, CONV2D_ACT_NONE>{}); break;
+        }
+    }
+}
+
+template <typename T, int FN, int S>
+static hipError_t launch_stem_t(const ConvArgs &a, hipStream_t st) {
+    constexpr int RB = 2;
+    constexpr int RS = (RB - 1) * S + 3;
+    // 16 zero bytes, the row, and the right pad pixel plus the dword read past it
+    const int rstr = ((16 + a.W * 6 + 8) + 15) / 16 * 16;
+    const size_t smem = (size_t)RS * rstr;
+    if (smem > 96 * 1024) return hipErrorInvalidValue;
+    const long long blocks = (long long)a.N * ((a.OH + RB - 1) / RB);
+    if (blocks > 0x7fffffffll) return hipErrorInvalidValue;
+    return launch_kernel(stem3_kernel<T, FN, RB, S>, dim3((unsigned)blocks), dim3(256), smem, st, a, rstr);
+}
+
+template <typename T>
+static hipError_t launch_stem_d(const ConvArgs &a, hipStream_t st) {
+    const int fn = a.Cout <= 32 ? 1 : 2;
+    if (a.stride == 2) return fn == 1 ? launch_stem_t<T, 1, 2>(a, st) : launch_stem_t<T, 2, 2>(a, st);
+    return fn == 1 ? launch_stem_t<T, 1, 1>(a, st) : launch_stem_t<T, 2, 1>(a, st);
+}
+
+hipError_t launch_stem3(const ConvArgs &a, int dtype, hipStream_t st) {
+    switch (dtype) {
+    case CONV2D_DTYPE_BF16: return launch_stem_d<bf16>(a, st);
+    case CONV2D_DTYPE_F16: return launch_stem_d<f16>(a, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace c2d

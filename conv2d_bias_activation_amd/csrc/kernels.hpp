@@ -76,6 +76,11 @@ struct HaloPlan {
 // for p.fn = 1, p.th = WM for p.fn = 2.
 hipError_t launch_halo3x3(const ConvArgs &a, int dtype, const HaloPlan &p, hipStream_t st);
 
+// 3x3 convolution of a 3-channel channel-last 16-bit image on the matrix cores:
+// stride 1 or 2, pad 1, Cout <= 64 with Cout % 8 == 0, W % 8 == 0 and W <= 3000, x
+// 16-byte aligned, y and the residual 16-byte aligned (a.vec_out), tensors under 2 GiB.
+hipError_t launch_stem3(const ConvArgs &a, int dtype, hipStream_t st);
+
 // Direct convolution on the vector ALUs for few input channels (the image stem):
 // one thread per output pixel and a block of output channels.
 hipError_t launch_direct(const ConvArgs &a, int dtype, bool nchw, hipStream_t st);

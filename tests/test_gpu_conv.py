@@ -128,6 +128,36 @@ def test_halo(case):
     gate(to64(y), _oracle_conv(x, spec, r, "nhwc"), dtype, what=str(case))
 
 
+# 3-channel images on the matrix-core stem kernel: stride 1 and 2, partial last
+# 32-pixel group of a row, partial channel blocks, single-row images, every epilogue.
+# (n, h, w, cout, stride, act, residual, dtype)
+STEM = [
+    (1, 17, 24, 32, 2, "relu", None, "bf16"),
+    (2, 32, 40, 64, 2, "silu", "post", "f16"),
+    (1, 21, 16, 32, 1, "prelu", "pre", "bf16"),
+    (3, 9, 8, 16, 1, "none", None, "bf16"),
+    (1, 64, 88, 48, 2, "relu", None, "bf16"),
+    (1, 1, 8, 32, 2, "relu", None, "bf16"),
+    (2, 130, 136, 64, 2, "relu", "pre", "bf16"),
+    (1, 40, 72, 24, 1, "silu", None, "f16"),
+]
+
+
+@pytest.mark.parametrize("case", STEM, ids=lambda c: "-".join(map(str, c)))
+def test_stem(case):
+    n, h, w, cout, s, act, res, dtype = case
+    seed = zlib.crc32(repr(case).encode())
+    x, spec, r = wl.random_conv_case(seed, n=n, h=h, w=w, cin=3, cout=cout, k=3, stride=s, pad=1,
+                                     act=act, layout="nhwc", dtype=dtype, residual=res is not None,
+                                     res_before_act=res == "pre", x_dist="uniform")
+    plan = c2d.plan(n, h, w, 3, cout, 3, 3, s, 1, 0, 0, {"bf16": 1, "f16": 2}[dtype])
+    print(f"case {case} plan {plan}", flush=True)
+    assert plan.startswith("stem3x3"), plan
+    y = _gpu_conv(x, spec, r, "nhwc")
+    torch.cuda.synchronize()
+    gate(to64(y), _oracle_conv(x, spec, r, "nhwc"), dtype, what=str(case))
+
+
 @pytest.mark.parametrize("layout", ["nhwc", "nchw"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_delta_kernel_is_identity(layout, dtype):
