@@ -12,6 +12,10 @@
 
 namespace c2d {
 
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_buffer_rsrc_bytes(const void *p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (int)bytes, 0x00020000);
+}
+
 template <typename T> struct Vec16 {
     static constexpr int n = 16 / (int)sizeof(T);
     T v[16 / sizeof(T)];
@@ -29,46 +33,53 @@ template <typename T> __device__ __forceinline__ void store16(T *p, const Vec16<
     *reinterpret_cast<u32x4 *>(p) = t;
 }
 
-// channel-last, one thread per (output pixel, 16-byte channel vector)
+// channel-last: blockIdx.y is an output row (n, oh), threads walk its (pixel, 16-byte
+// channel vector) items; the nine taps are buffer loads (an out-of-image tap gets an
+// out-of-range offset and is then ignored by the compare), all in flight together.
 template <typename T>
 __global__ __launch_bounds__(256) void maxpool_nhwc_vec(const T *__restrict__ x, T *__restrict__ y,
                                                         int N, int H, int W, int C, int OH, int OW) {
     constexpr int VE = Vec16<T>::n;
     const int CV = C / VE;
-    const long long total = (long long)N * OH * OW * CV;
-    for (long long it = blockIdx.x * 256ll + threadIdx.x; it < total; it += (long long)gridDim.x * 256) {
-        int cv = (int)(it % CV);
-        long long p = it / CV;
-        int ow = (int)(p % OW);
-        long long q = p / OW;
-        int oh = (int)(q % OH);
-        int n = (int)(q / OH);
-        float best[VE];
-        Vec16<T> out;
+    const int item = blockIdx.x * 256 + threadIdx.x;
+    if (item >= OW * CV) return;
+    const int row = blockIdx.y;  // n * OH + oh
+    const int n = row / OH, oh = row - n * OH;
+    const int ow = item / CV, cv = item - ow * CV;
+    const __amdgpu_buffer_rsrc_t rx = make_buffer_rsrc_bytes(x, (uint32_t)((size_t)N * H * W * C * sizeof(T)));
+    u32x4 v[9];
+    bool ok[9];
+#pragma unroll
+    for (int dy = 0; dy < 3; ++dy)
+#pragma unroll
+        for (int dx = 0; dx < 3; ++dx) {
+            const int iy = 2 * oh + dy - 1, ix = 2 * ow + dx - 1;
+            const bool in = (unsigned)iy < (unsigned)H && (unsigned)ix < (unsigned)W;
+            const uint32_t off = in ? (uint32_t)(((n * H + iy) * W + ix) * C + cv * VE) * (uint32_t)sizeof(T)
+                                    : 0xFFFFFFF0u;
+            v[dy * 3 + dx] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)off, 0, 0);
+            ok[dy * 3 + dx] = in;
+        }
+    float best[VE];
+    Vec16<T> out;
+#pragma unroll
+    for (int e = 0; e < VE; ++e) {
+        best[e] = -__builtin_inff();
+        out.v[e] = from_f32<T>(-__builtin_inff());
+    }
+#pragma unroll
+    for (int t = 0; t < 9; ++t) {
+        T tv[VE];
+        __builtin_memcpy(tv, &v[t], 16);
 #pragma unroll
         for (int e = 0; e < VE; ++e) {
-            best[e] = -__builtin_inff();
-            out.v[e] = from_f32<T>(-__builtin_inff());
+            const float f = to_f32(tv[e]);
+            const bool take = ok[t] && f > best[e];
+            best[e] = take ? f : best[e];
+            out.v[e] = take ? tv[e] : out.v[e];
         }
-        for (int dy = 0; dy < 3; ++dy) {
-            int iy = 2 * oh + dy - 1;
-            if ((unsigned)iy >= (unsigned)H) continue;
-            for (int dx = 0; dx < 3; ++dx) {
-                int ix = 2 * ow + dx - 1;
-                if ((unsigned)ix >= (unsigned)W) continue;
-                Vec16<T> v = load16(x + (((size_t)n * H + iy) * W + ix) * C + cv * VE);
-#pragma unroll
-                for (int e = 0; e < VE; ++e) {
-                    float f = to_f32(v.v[e]);
-                    if (f > best[e]) {
-                        best[e] = f;
-                        out.v[e] = v.v[e];
-                    }
-                }
-            }
-        }
-        store16(y + (((size_t)n * OH + oh) * OW + ow) * C + cv * VE, out);
     }
+    store16(y + ((size_t)row * OW + ow) * C + cv * VE, out);
 }
 
 // any layout, one thread per output element (channel-first: consecutive threads
@@ -116,32 +127,30 @@ __global__ __launch_bounds__(256) void maxpool_scalar(const T *__restrict__ x, T
     }
 }
 
+// channel-last: blockIdx.y is an output row (n, oh), threads walk its (pixel, 16-byte
+// channel vector) items (the window is always inside the image: OH = H/2, OW = W/2).
 template <typename T>
 __global__ __launch_bounds__(256) void avgpool_nhwc_vec(const T *__restrict__ x, T *__restrict__ y,
                                                         int N, int H, int W, int C, int OH, int OW) {
     constexpr int VE = Vec16<T>::n;
     const int CV = C / VE;
-    const long long total = (long long)N * OH * OW * CV;
-    for (long long it = blockIdx.x * 256ll + threadIdx.x; it < total; it += (long long)gridDim.x * 256) {
-        int cv = (int)(it % CV);
-        long long p = it / CV;
-        int ow = (int)(p % OW);
-        long long q = p / OW;
-        int oh = (int)(q % OH);
-        int n = (int)(q / OH);
-        const T *b = x + (((size_t)n * H + 2 * oh) * W + 2 * ow) * C + cv * VE;
-        Vec16<T> v00 = load16(b), v01 = load16(b + C);
-        Vec16<T> v10 = load16(b + (size_t)W * C), v11 = load16(b + (size_t)W * C + C);
-        Vec16<T> out;
+    const int item = blockIdx.x * 256 + threadIdx.x;
+    if (item >= OW * CV) return;
+    const int row = blockIdx.y;  // n * OH + oh
+    const int n = row / OH, oh = row - n * OH;
+    const int ow = item / CV, cv = item - ow * CV;
+    const T *b = x + ((size_t)(n * H + 2 * oh) * W + 2 * ow) * C + cv * VE;
+    Vec16<T> v00 = load16(b), v01 = load16(b + C);
+    Vec16<T> v10 = load16(b + (size_t)W * C), v11 = load16(b + (size_t)W * C + C);
+    Vec16<T> out;
 #pragma unroll
-        for (int e = 0; e < VE; ++e) {
-            float s = to_f32(v00.v[e]) + to_f32(v01.v[e]);
-            s = s + to_f32(v10.v[e]);
-            s = s + to_f32(v11.v[e]);
-            out.v[e] = from_f32<T>(s * 0.25f);
-        }
-        store16(y + (((size_t)n * OH + oh) * OW + ow) * C + cv * VE, out);
+    for (int e = 0; e < VE; ++e) {
+        float s = to_f32(v00.v[e]) + to_f32(v01.v[e]);
+        s = s + to_f32(v10.v[e]);
+        s = s + to_f32(v11.v[e]);
+        out.v[e] = from_f32<T>(s * 0.25f);
     }
+    store16(y + ((size_t)row * OW + ow) * C + cv * VE, out);
 }
 
 template <typename T, bool NCHW>
@@ -194,10 +203,11 @@ static hipError_t maxpool_t(const void *x, void *y, int N, int H, int W, int C, 
     int OH = (H - 1) / 2 + 1, OW = (W - 1) / 2 + 1;
     const T *xp = static_cast<const T *>(x);
     T *yp = static_cast<T *>(y);
-    if (!nchw && vec) {
-        long long items = (long long)N * OH * OW * (C / Vec16<T>::n);
-        return launch_kernel(maxpool_nhwc_vec<T>, dim3(pool_grid(items)), dim3(256), 0, st, xp, yp, N, H, W, C,
-                             OH, OW);
+    // the vector kernel takes one output row per grid row and 32-bit byte offsets
+    if (!nchw && vec && (long long)N * OH <= 65535 && (long long)N * H * W * C * (long long)sizeof(T) < (1ll << 31)) {
+        const int per_row = OW * (C / Vec16<T>::n);
+        return launch_kernel(maxpool_nhwc_vec<T>, dim3((unsigned)((per_row + 255) / 256), (unsigned)(N * OH)),
+                             dim3(256), 0, st, xp, yp, N, H, W, C, OH, OW);
     } else if (nchw) {
         return launch_kernel(maxpool_scalar<T, true>, dim3(pool_grid((long long)N * OH * OW * C)), dim3(256), 0,
                              st, xp, yp, N, H, W, C, OH, OW);
@@ -213,10 +223,10 @@ static hipError_t avgpool_t(const void *x, void *y, int N, int H, int W, int C, 
     int OH = H / 2, OW = W / 2;
     const T *xp = static_cast<const T *>(x);
     T *yp = static_cast<T *>(y);
-    if (!nchw && vec) {
-        long long items = (long long)N * OH * OW * (C / Vec16<T>::n);
-        return launch_kernel(avgpool_nhwc_vec<T>, dim3(pool_grid(items)), dim3(256), 0, st, xp, yp, N, H, W, C,
-                             OH, OW);
+    if (!nchw && vec && (long long)N * OH <= 65535 && OW > 0) {
+        const int per_row = OW * (C / Vec16<T>::n);
+        return launch_kernel(avgpool_nhwc_vec<T>, dim3((unsigned)((per_row + 255) / 256), (unsigned)(N * OH)),
+                             dim3(256), 0, st, xp, yp, N, H, W, C, OH, OW);
     } else if (nchw) {
         return launch_kernel(avgpool_scalar<T, true>, dim3(pool_grid((long long)N * OH * OW * C)), dim3(256), 0,
                              st, xp, yp, N, H, W, C, OH, OW);
