@@ -255,7 +255,7 @@ NhwcPlan plan_nhwc(const ConvArgs &a) {
     if (waves < 1200 && nsteps >= 48 && (a.Cout % 8) == 0 && a.vec_out &&
         3ull * a.M * a.Cout * 4 <= kScratchBytes)
         p.splits = 3;
-    p.tap_inner = (a.Cin % 64) == 0;
+    p.tap_inner = (a.Cin % 64) == 0 && a.kh * a.kw <= 32;  // tap masks are 32-bit
     return p;
 }
 

@@ -44,7 +44,7 @@ __device__ __forceinline__ void barrier_nofence() {
 
 template <typename T, int BM, int BN, int WGM, int WGN, int NS, bool TAP_INNER, bool SPLIT,
           bool NCHW_OUT>
-__global__ __launch_bounds__(64 * WGM * WGN) void igemm_nhwc_kernel(ConvArgs a, int tiles_n,
+__global__ __launch_bounds__(64 * WGM * WGN, 8 / (WGM * WGN)) void igemm_nhwc_kernel(ConvArgs a, int tiles_n,
                                                                    int steps_per_split,
                                                                    float *partials) {
     constexpr int NW = WGM * WGN;        // waves per workgroup (4 or 8)
@@ -136,12 +136,34 @@ __global__ __launch_bounds__(64 * WGM * WGN) void igemm_nhwc_kernel(ConvArgs a, 
 
     // k state of this thread's chunk at the next step to load
     int ky, kx, ci;
+    // Taps innermost: k step = (channel block cb, tap). Each row's byte offset at tap
+    // (0, 0) and a mask of its taps that fall inside the image are fixed per thread;
+    // a step then adds one wave-uniform offset, so a load costs a bit test, an add and
+    // a select (the address arithmetic was most of the step's instruction stream).
+    int cb = 0;
+    int a_base[LA], b_base[LB];
+    uint32_t a_mask[LA];
     if constexpr (TAP_INNER) {
         const int taps = kh * kw;
-        const int cb = s_begin / taps, tap = s_begin - cb * taps;
+        cb = s_begin / taps;
+        const int tap = s_begin - cb * taps;
         ky = tap / kw;
         kx = tap - ky * kw;
-        ci = cb * BK + c * 8;
+        ci = 0;
+#pragma unroll
+        for (int j = 0; j < LA; ++j) {
+            a_base[j] = ((a_pix[j] + a_ih[j] * W + a_iw[j]) * Cin + c * 8) * (int)sizeof(T);
+            uint32_t mk = 0;
+            for (int ty = 0; ty < kh; ++ty)
+                for (int tx = 0; tx < kw; ++tx) {
+                    const bool in = a_ok[j] && (unsigned)(a_ih[j] + ty) < (unsigned)H && (unsigned)(a_iw[j] + tx) < (unsigned)W;
+                    mk |= (in ? 1u : 0u) << (ty * kw + tx);
+                }
+            a_mask[j] = mk;
+        }
+        // a weight row past Cout gets a base of 2^31 bytes: every offset from it is out of range
+#pragma unroll
+        for (int j = 0; j < LB; ++j) b_base[j] = b_ok[j] ? (b_off[j] + c * 8) * (int)sizeof(T) : (int)0x80000000u;
     } else {
         const int k = s_begin * BK + c * 8;
         const int tap = k / Cin;
@@ -156,6 +178,28 @@ __global__ __launch_bounds__(64 * WGM * WGN) void igemm_nhwc_kernel(ConvArgs a, 
     auto issue = [&](char *stage, bool live) {
         char *sA = stage;
         char *sB = sA + BM * ROWB;
+        if constexpr (TAP_INNER) {
+            const int tap = ky * kw + kx;
+            const bool kin = live && cb * BK < Cin;
+            const int toff = ((ky * W + kx) * Cin + cb * BK) * (int)sizeof(T);
+            const int koff = (tap * Cin + cb * BK) * (int)sizeof(T);
+#pragma unroll
+            for (int j = 0; j < LA; ++j) {
+                const bool ok = kin && ((a_mask[j] >> tap) & 1u);
+                dma_b128(rx, ok ? (uint32_t)(a_base[j] + toff) : kOOB, lds_addr(sA + (j * NW + wave) * 1024));
+            }
+#pragma unroll
+            for (int j = 0; j < LB; ++j)
+                dma_b128(rw, kin ? (uint32_t)(b_base[j] + koff) : kOOB, lds_addr(sB + (j * NW + wave) * 1024));
+            if (++kx == kw) {
+                kx = 0;
+                if (++ky == kh) {
+                    ky = 0;
+                    ++cb;
+                }
+            }
+            return;
+        }
         const bool kin = live && ky < kh;
 #pragma unroll
         for (int j = 0; j < LA; ++j) {
@@ -170,22 +214,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void igemm_nhwc_kernel(ConvArgs a, 
             uint32_t off = (uint32_t)(b_off[j] + kk) * (uint32_t)sizeof(T);
             dma_b128(rw, (b_ok[j] && kin) ? off : kOOB, lds_addr(sB + (j * NW + wave) * 1024));
         }
-        if constexpr (TAP_INNER) {
+        ci += BK;
+        while (ci >= Cin) {
+            ci -= Cin;
             if (++kx == kw) {
                 kx = 0;
-                if (++ky == kh) {
-                    ky = 0;
-                    ci += BK;
-                }
-            }
-        } else {
-            ci += BK;
-            while (ci >= Cin) {
-                ci -= Cin;
-                if (++kx == kw) {
-                    kx = 0;
-                    ++ky;
-                }
+                ++ky;
             }
         }
     };

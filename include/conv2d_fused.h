@@ -22,13 +22,15 @@
  *  - Tensors are dense and contiguous. Every tensor must hold fewer than 2^31
  *    elements (CONV2D_EUNSUPPORTED otherwise).
  *  - The output may not overlap the input or the residual (CONV2D_EINVAL).
- *  - State kept between calls: the last-error message (per thread) and, per
- *    device, one 64 MiB scratch buffer for split-K partial sums that the library
- *    allocates on the first call that needs it and keeps until the process ends.
- *    Split-K calls on one device all use that buffer: callers that run
- *    conv2d_fused on several streams of one device at the same time must
- *    serialise those calls. (Under HIP graph capture, make one call on each device
- *    before capturing, so the allocation does not happen inside the capture.)
+ *  - State kept between calls: the last-error message (per thread), the compute
+ *    unit count of each device (queried once), and, per device, one 64 MiB
+ *    scratch buffer that the library allocates on the first call that needs it
+ *    and keeps until the process ends. It holds the fp32 partial sums of split-K
+ *    calls and the channel-last copies of x and w of 16-bit channel-first calls.
+ *    Such calls on one device all use that buffer: callers that run conv2d_fused
+ *    on several streams of one device at the same time must serialise those
+ *    calls. (Under HIP graph capture, make one call on each device before
+ *    capturing, so the allocation does not happen inside the capture.)
  */
 #ifndef CONV2D_FUSED_H
 #define CONV2D_FUSED_H
@@ -102,8 +104,9 @@ extern "C" {
  * Accumulation is fp32 in any order; the result is rounded once to `dtype`.
  * Layers with a deep K and few output tiles run as split-K: fp32 partial sums of
  * K slices go to the library's per-device scratch buffer and a second kernel adds
- * them in slice order and applies the epilogue (CONV2D_EHIP if the one-time
- * scratch allocation fails).
+ * them in slice order and applies the epilogue. 16-bit channel-first layers with
+ * Cin % 8 == 0 are first copied to channel-last form in that buffer. (Either
+ * returns CONV2D_EHIP if the one-time scratch allocation fails.)
  */
 int conv2d_fused(const void *x, const void *w, const float *bias, const float *alpha,
                  const void *residual, void *y, int N, int H, int W, int Cin, int Cout, int kh,

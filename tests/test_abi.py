@@ -72,12 +72,19 @@ def test_check_args_rejects(kw, code):
 
 def test_plan_names_a_kernel_for_every_workload_shape():
     bf16, f16, f32 = c2d.DTYPE_BF16, c2d.DTYPE_F16, c2d.DTYPE_F32
-    shapes = [(1, 32, 32, 16, 32, 3, 3, 1, 1, 1, 0, f32), (1, 640, 640, 3, 32, 3, 3, 2, 1, 2, 0, f32),
-              (4, 80, 80, 512, 256, 1, 1, 1, 0, 1, 0, bf16), (1, 68, 120, 240, 240, 3, 3, 1, 1, 3, 1, f16),
-              (4, 40, 40, 256, 256, 3, 3, 1, 1, 1, 0, bf16)]
-    for s in shapes:
+    # (shape, expected kernel family): the workload layers and the narrow/stem special cases
+    cases = [((1, 32, 32, 16, 32, 3, 3, 1, 1, 1, 0, f32), "igemm_nhwc_vec"),
+             ((1, 640, 640, 3, 32, 3, 3, 2, 1, 2, 0, f32), "direct_nhwc"),
+             ((1, 640, 640, 3, 32, 3, 3, 2, 1, 2, 0, bf16), "stem3x3_mfma"),
+             ((2, 23, 19, 3, 32, 3, 3, 2, 1, 2, 0, bf16), "direct_nhwc"),  # W % 8 != 0
+             ((4, 80, 80, 512, 256, 1, 1, 1, 0, 1, 0, bf16), "igemm_nhwc_pipe"),
+             ((1, 68, 120, 240, 240, 3, 3, 1, 1, 3, 1, f16), "to_nhwc+igemm_nhwc_pipe"),
+             ((4, 40, 40, 256, 256, 3, 3, 1, 1, 1, 0, bf16), "igemm_nhwc_pipe"),
+             ((4, 320, 320, 32, 64, 3, 3, 1, 1, 1, 0, bf16), "halo3x3_nhwc"),
+             ((4, 160, 160, 64, 64, 3, 3, 1, 1, 1, 0, bf16), "halo3x3_nhwc"),
+             ((4, 160, 160, 64, 128, 3, 3, 2, 1, 1, 0, bf16), "igemm_nhwc_pipe")]
+    for s, family in cases:
         name = c2d.plan(*s)
-        assert name and ("igemm" in name or "direct" in name), name
-    assert c2d.plan(1, 640, 640, 3, 32, 3, 3, 2, 1, 2, 0, bf16).startswith("direct")
+        assert name.startswith(family), (s, name)
     with pytest.raises(c2d.Conv2dError):
         c2d.plan(1, 8, 8, 4, 4, 3, 3, 5, 1, 0, 0, bf16)
