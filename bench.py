@@ -49,6 +49,15 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--layer-reps", type=int, default=20)
     p.add_argument("--layers-out", default=None, help="write per-layer timings (JSON) here")
+    # counter runs (rocprofv3 --pmc): launch one kernel group, or a plain copy of known size,
+    # and turn the two counters' per-dispatch values into profiles/traffic.json
+    p.add_argument("--launch-plan", default=None,
+                   help="only launch the workload's layers that run this plan (5 times each), then exit")
+    p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                   help="only run 10 device copies of MIB MiB (counter scale), then exit")
+    p.add_argument("--traffic-from", default=None, metavar="DIR",
+                   help="write profiles/traffic.json from DIR/{fetch,write,copy_fetch,copy_write} "
+                        "rocprofv3 --pmc outputs (FETCH_SIZE, WRITE_SIZE), then exit")
     p.add_argument("--workload", choices=list(WORKLOADS), default="resnet18d",
                    help="the backbone (default; the headline) or one of the other layer configs")
     return p.parse_args()
@@ -248,8 +257,52 @@ def cpu_baseline(min_seconds=10.0):
                        f"in fp64: {flops / 1e9:.1f} GFLOP in {dt:.1f} s")
 
 
+def pmc_per_dispatch(path, counter):
+    """{kernel name: (dispatches, mean value)} of one rocprofv3 --pmc counter CSV."""
+    import csv
+    import glob
+
+    files = glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {path}")
+    acc = {}
+    for row in csv.DictReader(open(files[0])):
+        if row["Counter_Name"] != counter:
+            continue
+        d = acc.setdefault(row["Kernel_Name"], {})
+        d[row["Dispatch_Id"]] = d.get(row["Dispatch_Id"], 0.0) + float(row["Counter_Value"])
+    return {k: (len(v), sum(v.values()) / len(v)) for k, v in acc.items()}
+
+
+def write_traffic(src, copy_mib, plan):
+    """HBM bytes per launch of `plan`'s kernel: FETCH_SIZE and WRITE_SIZE (KiB per dispatch),
+    each scaled by bytes / counter of a plain copy of copy_mib MiB read and written."""
+    known = copy_mib * 1024.0  # KiB
+    def busiest(path, counter):
+        d = pmc_per_dispatch(path, counter)
+        name = max(d, key=lambda k: d[k][0])  # the kernel launched most often in that run
+        return name, d[name][1]
+    _, cf = busiest(os.path.join(src, "copy_fetch"), "FETCH_SIZE")
+    _, cw = busiest(os.path.join(src, "copy_write"), "WRITE_SIZE")
+    kname, kf = busiest(os.path.join(src, "fetch"), "FETCH_SIZE")
+    _, kw = busiest(os.path.join(src, "write"), "WRITE_SIZE")
+    sf, sw = known / cf, known / cw
+    rec = dict(source_hash=kernel_source_hash(),
+               copy=dict(mib=copy_mib, fetch_kib=round(cf, 1), write_kib=round(cw, 1),
+                         fetch_scale=round(sf, 4), write_scale=round(sw, 4)),
+               kernels={plan: dict(kernel=kname, fetch_kib=round(kf, 1), write_kib=round(kw, 1),
+                                   bytes_per_launch=int(round((kf * sf + kw * sw) * 1024)))})
+    out = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
 def main():
     args = parse()
+    if args.traffic_from:
+        write_traffic(args.traffic_from, args.copy_probe or 256, args.launch_plan)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; multi-GPU runs are not "
                                    "part of this build", "n_gpus": args.gpus}))
@@ -260,9 +313,27 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_probe:
+        src = torch.ones(args.copy_probe << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        return
     builder, config_name = WORKLOADS[args.workload]
     work = getattr(wl, builder)()
     net = Net(work, dev)
+    if args.launch_plan:
+        h = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        chosen = [L for L in net.layers if L["plan"] == args.launch_plan]
+        if not chosen:
+            raise SystemExit(f"no layer runs plan {args.launch_plan!r}")
+        for _ in range(5):
+            for L in chosen:
+                net.run_layer(L, h)
+        torch.cuda.synchronize()
+        print(f"launched {len(chosen)} layers x 5 with plan {args.launch_plan}", flush=True)
+        return
     ms, graph = time_steps(torch, net, args.steps, args.warmup, args.mode)
     value = net.flops / (ms * 1e-3) / 1e12
 
