@@ -14,7 +14,8 @@ import os
 
 import torch
 
-__all__ = ["conv2d_fused", "maxpool3x3s2", "avgpool2x2", "out_dim", "check_args", "plan",
+__all__ = ["conv2d_fused", "conv2d_fused_maxpool3x3s2", "maxpool3x3s2", "avgpool2x2", "out_dim",
+           "check_args", "plan", "plan_maxpool",
            "last_error", "library_path", "Conv2dError", "ACT_NONE", "ACT_RELU", "ACT_SILU",
            "ACT_PRELU", "RES_BEFORE_ACT", "LAYOUT_NHWC", "LAYOUT_NCHW", "DTYPE_F32",
            "DTYPE_BF16", "DTYPE_F16"]
@@ -42,6 +43,8 @@ SIGNATURES = {
     "conv2d_out_dim": (_i, [_i] * 4),
     "conv2d_check_args": (_i, [_vp, _vp, _fp, _fp, _vp, _vp] + [_i] * 12),
     "conv2d_plan": (_i, [_i] * 12 + [_cp, _i]),
+    "conv2d_fused_maxpool3x3s2": (_i, [_vp, _vp, _fp, _fp, _vp] + [_i] * 12 + [_vp]),
+    "conv2d_fused_maxpool_plan": (_i, [_i] * 12 + [_cp, _i]),
     "conv2d_last_error": (_cp, []),
     "conv2d_abi_version": (_i, []),
 }
@@ -129,6 +132,36 @@ def _require(t, name, dtype, device):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _conv_args(x, w, bias, alpha, stride, pad, layout):
+    lay = _LAYOUTS[layout]
+    dt = _DTYPES.get(x.dtype)
+    if dt is None:
+        raise ValueError(f"unsupported dtype {x.dtype}")
+    dims = _dims(x, w, layout)
+    N, H, W, Cin, Cout, kh, kw = dims
+    OH, OW = out_dim(H, kh, stride, pad), out_dim(W, kw, stride, pad)
+    if OH < 1 or OW < 1:
+        raise ValueError("the kernel does not fit the padded input")
+    dev = x.device
+    _require(x, "x", x.dtype, dev)
+    _require(w, "w", x.dtype, dev)
+    _require(bias, "bias", torch.float32, dev)
+    _require(alpha, "alpha", torch.float32, dev)
+    for t, name in ((bias, "bias"), (alpha, "alpha")):
+        if t is not None and tuple(t.shape) != (Cout,):
+            raise ValueError(f"{name} must have shape ({Cout},)")
+    return lay, dt, dims, (OH, OW)
+
+
+def _out(out, shape, x):
+    if out is None:
+        return torch.empty(shape, dtype=x.dtype, device=x.device)
+    _require(out, "out", x.dtype, x.device)
+    if tuple(out.shape) != shape:
+        raise ValueError(f"out must have shape {shape}")
+    return out
+
+
 def conv2d_fused(x, w, bias=None, alpha=None, residual=None, *, stride=1, pad=0, act="none",
                  res_before_act=False, layout="nhwc", out=None, stream=None):
     """y = epilogue(conv(x, w)) on the GPU; see include/conv2d_fused.h.
@@ -138,35 +171,30 @@ def conv2d_fused(x, w, bias=None, alpha=None, residual=None, *, stride=1, pad=0,
     OIHW weights). bias, alpha: float32 [Cout] or None. Returns y.
     """
     lib = _load()
-    lay = _LAYOUTS[layout]
-    dt = _DTYPES.get(x.dtype)
-    if dt is None:
-        raise ValueError(f"unsupported dtype {x.dtype}")
-    N, H, W, Cin, Cout, kh, kw = _dims(x, w, layout)
-    OH, OW = out_dim(H, kh, stride, pad), out_dim(W, kw, stride, pad)
-    if OH < 1 or OW < 1:
-        raise ValueError("the kernel does not fit the padded input")
+    lay, dt, (N, H, W, Cin, Cout, kh, kw), (OH, OW) = _conv_args(x, w, bias, alpha, stride, pad, layout)
     yshape = (N, OH, OW, Cout) if layout == "nhwc" else (N, Cout, OH, OW)
-    dev = x.device
-    _require(x, "x", x.dtype, dev)
-    _require(w, "w", x.dtype, dev)
-    _require(residual, "residual", x.dtype, dev)
-    _require(bias, "bias", torch.float32, dev)
-    _require(alpha, "alpha", torch.float32, dev)
-    for t, name in ((bias, "bias"), (alpha, "alpha")):
-        if t is not None and tuple(t.shape) != (Cout,):
-            raise ValueError(f"{name} must have shape ({Cout},)")
+    _require(residual, "residual", x.dtype, x.device)
     if residual is not None and tuple(residual.shape) != yshape:
         raise ValueError(f"residual must have shape {yshape}")
-    if out is None:
-        out = torch.empty(yshape, dtype=x.dtype, device=dev)
-    else:
-        _require(out, "out", x.dtype, dev)
-        if tuple(out.shape) != yshape:
-            raise ValueError(f"out must have shape {yshape}")
+    out = _out(out, yshape, x)
     rc = lib.conv2d_fused(_ptr(x), _ptr(w), _ptr(bias), _ptr(alpha), _ptr(residual), _ptr(out),
                           N, H, W, Cin, Cout, kh, kw, stride, pad,
                           _act_code(act, res_before_act), lay, dt, _stream_handle(stream))
+    _check(rc)
+    return out
+
+
+def conv2d_fused_maxpool3x3s2(x, w, bias=None, alpha=None, *, stride=1, pad=0, act="none",
+                              layout="nhwc", out=None, stream=None):
+    """maxpool3x3s2(conv2d_fused(x, w, bias, alpha)) with only the pooled map written;
+    see include/conv2d_fused.h. Returns the pooled y."""
+    lib = _load()
+    lay, dt, (N, H, W, Cin, Cout, kh, kw), (OH, OW) = _conv_args(x, w, bias, alpha, stride, pad, layout)
+    PH, PW = (OH - 1) // 2 + 1, (OW - 1) // 2 + 1
+    out = _out(out, (N, PH, PW, Cout) if layout == "nhwc" else (N, Cout, PH, PW), x)
+    rc = lib.conv2d_fused_maxpool3x3s2(_ptr(x), _ptr(w), _ptr(bias), _ptr(alpha), _ptr(out),
+                                       N, H, W, Cin, Cout, kh, kw, stride, pad,
+                                       _act_code(act, False), lay, dt, _stream_handle(stream))
     _check(rc)
     return out
 
@@ -220,5 +248,14 @@ def plan(N, H, W, Cin, Cout, kh, kw, stride, pad, act, layout, dtype) -> str:
     """Name of the kernel variant conv2d_fused picks for a shape (host only)."""
     buf = ctypes.create_string_buffer(256)
     n = _load().conv2d_plan(N, H, W, Cin, Cout, kh, kw, stride, pad, act, layout, dtype, buf, 256)
+    _check(n if n < 0 else OK)
+    return buf.value.decode()
+
+
+def plan_maxpool(N, H, W, Cin, Cout, kh, kw, stride, pad, act, layout, dtype) -> str:
+    """Kernel variants conv2d_fused_maxpool3x3s2 picks for a shape (host only)."""
+    buf = ctypes.create_string_buffer(256)
+    n = _load().conv2d_fused_maxpool_plan(N, H, W, Cin, Cout, kh, kw, stride, pad, act, layout, dtype,
+                                          buf, 256)
     _check(n if n < 0 else OK)
     return buf.value.decode()

@@ -75,10 +75,11 @@ bool overlap(const void *a, long long abytes, const void *b, long long bbytes) {
 
 constexpr long long kMaxElems = 0x7fffffffll;
 
-// Validates conv2d_fused's arguments; fills the derived geometry into `a`.
+// Validates conv2d_fused's arguments; fills the derived geometry into `a`. With
+// pooled_y, y holds the 3x3 stride-2 max pool of the conv output instead.
 int check_conv(const void *x, const void *w, const float *alpha, const void *residual,
                const void *y, int N, int H, int W, int Cin, int Cout, int kh, int kw,
-               int stride, int pad, int act, int layout, int dtype, ConvArgs *a) {
+               int stride, int pad, int act, int layout, int dtype, ConvArgs *a, bool pooled_y = false) {
     if (!x || !w || !y) return set_error(CONV2D_EINVAL, "x, w and y must not be null");
     if (N <= 0 || H <= 0 || W <= 0 || Cin <= 0 || Cout <= 0 || kh <= 0 || kw <= 0)
         return set_error(CONV2D_EINVAL, "sizes must be positive (N=%d H=%d W=%d Cin=%d Cout=%d kh=%d kw=%d)",
@@ -102,8 +103,9 @@ int check_conv(const void *x, const void *w, const float *alpha, const void *res
     if (xe > kMaxElems || we > kMaxElems || ye > kMaxElems || m > kMaxElems)
         return set_error(CONV2D_EUNSUPPORTED, "tensors of 2^31 or more elements are not supported");
     int eb = dtype_bytes(dtype);
-    if (overlap(y, ye * eb, x, xe * eb)) return set_error(CONV2D_EINVAL, "y overlaps x");
-    if (overlap(y, ye * eb, residual, ye * eb)) return set_error(CONV2D_EINVAL, "y overlaps the residual");
+    const long long yb = pooled_y ? (long long)N * out_dim(OH, 3, 2, 1) * out_dim(OW, 3, 2, 1) * Cout * eb : ye * eb;
+    if (overlap(y, yb, x, xe * eb)) return set_error(CONV2D_EINVAL, "y overlaps x");
+    if (overlap(y, yb, residual, ye * eb)) return set_error(CONV2D_EINVAL, "y overlaps the residual");
     a->x = x;
     a->w = w;
     a->alpha = alpha;
@@ -303,9 +305,20 @@ bool stem_fits(const ConvArgs &a, int layout, int dtype) {
            (long long)a.M * a.Cout * 2 < (1ll << 31);
 }
 
-Plan make_plan(const ConvArgs &a, int layout, int dtype) {
+// The general MFMA implicit GEMM: any shape, layout and dtype, no scratch.
+Plan igemm_plan(const ConvArgs &a, int layout, int dtype) {
     Plan p{};
     const int ve = 16 / dtype_bytes(dtype);
+    p.family = FAM_IGEMM;
+    p.ig.nchw = layout == CONV2D_LAYOUT_NCHW;
+    p.ig.avec = !p.ig.nchw && (a.Cin % ve) == 0 && aligned16(a.x) && aligned16(a.w);
+    p.ig.bvec = (a.K % ve) == 0 && aligned16(a.w);
+    p.ig.tile = choose_tile(a);
+    return p;
+}
+
+Plan make_plan(const ConvArgs &a, int layout, int dtype) {
+    Plan p{};
     if (stem_fits(a, layout, dtype)) {
         p.family = FAM_STEM;
         return p;
@@ -339,12 +352,7 @@ Plan make_plan(const ConvArgs &a, int layout, int dtype) {
         p.nh.nchw_out = true;
         return p;
     }
-    p.family = FAM_IGEMM;
-    p.ig.nchw = layout == CONV2D_LAYOUT_NCHW;
-    p.ig.avec = !p.ig.nchw && (a.Cin % ve) == 0 && aligned16(a.x) && aligned16(a.w);
-    p.ig.bvec = (a.K % ve) == 0 && aligned16(a.w);
-    p.ig.tile = choose_tile(a);
-    return p;
+    return igemm_plan(a, layout, dtype);
 }
 
 int describe(const Plan &p, int layout, int dtype, char *buf, int cap) {
@@ -393,6 +401,82 @@ int check_pool(const void *x, const void *y, int N, int H, int W, int C, int lay
     return CONV2D_OK;
 }
 
+// Launches the kernels of plan p for a validated conv (y = a.y). Returns a status code.
+int launch_conv(const ConvArgs &a, const Plan &p, int layout, int dtype, hipStream_t st) {
+    hipError_t e;
+    int rc;
+    if (p.family == FAM_DIRECT) {
+        e = launch_direct(a, dtype, layout == CONV2D_LAYOUT_NCHW, st);
+    } else if (p.family == FAM_STEM) {
+        e = launch_stem3(a, dtype, st);
+    } else if (p.family == FAM_HALO) {
+        int cus = 0;
+        rc = device_cus(&cus);
+        if (rc) return rc;
+        HaloPlan h = p.halo;
+        h.grid_cap = cus * (8 / h.waves);
+        e = launch_halo3x3(a, dtype, h, st);
+    } else if (p.family == FAM_NHWC) {
+        float *scratch = nullptr;
+        if (p.nh.splits > 1) {
+            rc = get_scratch(&scratch);
+            if (rc) return rc;
+        }
+        e = launch_igemm_nhwc(a, dtype, p.nh, scratch, st);
+    } else if (p.family == FAM_NCHW_VIA_NHWC) {
+        float *scratch = nullptr;
+        rc = get_scratch(&scratch);
+        if (rc) return rc;
+        const int eb = dtype_bytes(dtype);
+        char *xs = reinterpret_cast<char *>(scratch);
+        char *ws = xs + round256((size_t)a.N * a.H * a.W * a.Cin * eb);
+        e = launch_to_channel_last(a.x, xs, a.N, a.Cin, a.H * a.W, a.w, ws, a.Cout, a.kh * a.kw, dtype, st);
+        if (e == hipSuccess) {
+            ConvArgs b = a;
+            b.x = xs;
+            b.w = ws;
+            e = launch_igemm_nhwc(b, dtype, p.nh, nullptr, st);
+        }
+    } else {
+        e = launch_igemm(a, dtype, p.ig, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "conv2d_fused launch");
+    return CONV2D_OK;
+}
+
+struct PoolFusion {
+    bool fused;      // the fused stem + pool kernel
+    Plan conv_plan;  // otherwise: this conv into the scratch, then the pool kernel
+};
+
+// Validates conv2d_fused_maxpool3x3s2's arguments (y is the pooled map) and picks the
+// fused kernel or the two-kernel path.
+int check_conv_pool(const void *x, const void *w, const float *alpha, const void *y, int N, int H, int W,
+                    int Cin, int Cout, int kh, int kw, int stride, int pad, int act, int layout, int dtype,
+                    ConvArgs *a, PoolFusion *f) {
+    if (act & CONV2D_RES_BEFORE_ACT)
+        return set_error(CONV2D_EINVAL, "conv2d_fused_maxpool3x3s2 takes no residual");
+    int rc = check_conv(x, w, alpha, nullptr, y, N, H, W, Cin, Cout, kh, kw, stride, pad, act, layout, dtype, a,
+                        true);
+    if (rc) return rc;
+    f->fused = stem_fits(*a, layout, dtype);
+    if (!f->fused) {
+        // the conv output goes to the library scratch, which the conv kernels then must
+        // not use themselves: no split-K, and channel-first layers on the general kernel
+        if ((long long)a->M * Cout * dtype_bytes(dtype) > (long long)kScratchBytes)
+            return set_error(CONV2D_EUNSUPPORTED,
+                             "conv2d_fused_maxpool3x3s2: the unpooled conv output (%lld bytes) exceeds the %zu-byte "
+                             "scratch; call conv2d_fused and maxpool3x3s2",
+                             (long long)a->M * Cout * dtype_bytes(dtype), kScratchBytes);
+        ConvArgs b = *a;
+        b.vec_out = true;  // the scratch is 256-byte aligned
+        f->conv_plan = make_plan(b, layout, dtype);
+        if (f->conv_plan.family == FAM_NCHW_VIA_NHWC) f->conv_plan = igemm_plan(b, layout, dtype);
+        if (f->conv_plan.family == FAM_NHWC) f->conv_plan.nh.splits = 1;
+    }
+    return CONV2D_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -438,45 +522,66 @@ int conv2d_fused(const void *x, const void *w, const float *bias, const float *a
     if (rc) return rc;
     a.bias = bias;
     if ((act & 0xff) != CONV2D_ACT_PRELU) a.alpha = nullptr;
+    rc = launch_conv(a, make_plan(a, layout, dtype), layout, dtype, static_cast<hipStream_t>(stream));
+    return rc ? rc : set_ok();
+}
+
+int conv2d_fused_maxpool3x3s2(const void *x, const void *w, const float *bias, const float *alpha, void *y,
+                              int N, int H, int W, int Cin, int Cout, int kh, int kw, int stride, int pad,
+                              int act, int layout, int dtype, void *stream) {
+    ConvArgs a{};
+    PoolFusion f{};
+    int rc = check_conv_pool(x, w, alpha, y, N, H, W, Cin, Cout, kh, kw, stride, pad, act, layout, dtype, &a, &f);
+    if (rc) return rc;
+    a.bias = bias;
+    if ((act & 0xff) != CONV2D_ACT_PRELU) a.alpha = nullptr;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    Plan p = make_plan(a, layout, dtype);
-    hipError_t e;
-    if (p.family == FAM_DIRECT) {
-        e = launch_direct(a, dtype, layout == CONV2D_LAYOUT_NCHW, st);
-    } else if (p.family == FAM_STEM) {
-        e = launch_stem3(a, dtype, st);
-    } else if (p.family == FAM_HALO) {
-        int cus = 0;
-        rc = device_cus(&cus);
-        if (rc) return rc;
-        p.halo.grid_cap = cus * (8 / p.halo.waves);
-        e = launch_halo3x3(a, dtype, p.halo, st);
-    } else if (p.family == FAM_NHWC) {
-        float *scratch = nullptr;
-        if (p.nh.splits > 1) {
-            rc = get_scratch(&scratch);
-            if (rc) return rc;
-        }
-        e = launch_igemm_nhwc(a, dtype, p.nh, scratch, st);
-    } else if (p.family == FAM_NCHW_VIA_NHWC) {
-        float *scratch = nullptr;
-        rc = get_scratch(&scratch);
-        if (rc) return rc;
-        const int eb = dtype_bytes(dtype);
-        char *xs = reinterpret_cast<char *>(scratch);
-        char *ws = xs + round256((size_t)a.N * a.H * a.W * a.Cin * eb);
-        e = launch_to_channel_last(a.x, xs, a.N, a.Cin, a.H * a.W, a.w, ws, a.Cout, a.kh * a.kw, dtype, st);
-        if (e == hipSuccess) {
-            ConvArgs b = a;
-            b.x = xs;
-            b.w = ws;
-            e = launch_igemm_nhwc(b, dtype, p.nh, nullptr, st);
-        }
-    } else {
-        e = launch_igemm(a, dtype, p.ig, st);
+    if (f.fused) {
+        hipError_t e = launch_stem3_maxpool(a, y, dtype, st);
+        if (e != hipSuccess) return hip_fail(e, "conv2d_fused_maxpool3x3s2 launch");
+        return set_ok();
     }
-    if (e != hipSuccess) return hip_fail(e, "conv2d_fused launch");
+    // unfused: the conv into the scratch buffer, then the pool kernel
+    float *scratch = nullptr;
+    rc = get_scratch(&scratch);
+    if (rc) return rc;
+    ConvArgs b = a;
+    b.y = scratch;
+    b.vec_out = true;
+    rc = launch_conv(b, f.conv_plan, layout, dtype, st);
+    if (rc) return rc;
+    const int ve = 16 / dtype_bytes(dtype);
+    const bool vec = layout == CONV2D_LAYOUT_NHWC && (Cout % ve) == 0 && aligned16(y);
+    hipError_t e = launch_maxpool(scratch, y, N, a.OH, a.OW, Cout, layout == CONV2D_LAYOUT_NCHW, dtype, vec, st);
+    if (e != hipSuccess) return hip_fail(e, "conv2d_fused_maxpool3x3s2 pool launch");
     return set_ok();
+}
+
+int conv2d_fused_maxpool_plan(int N, int H, int W, int Cin, int Cout, int kh, int kw, int stride, int pad,
+                              int act, int layout, int dtype, char *buf, int cap) {
+    const void *px = (const void *)(uintptr_t)0x100000000ull;
+    const void *pw = (const void *)(uintptr_t)0x900000000ull;
+    void *py = (void *)(uintptr_t)0x1100000000ull;
+    const float *pa = (const float *)(uintptr_t)0x1900000000ull;
+    ConvArgs a{};
+    PoolFusion f{};
+    int rc = check_conv_pool(px, pw, pa, py, N, H, W, Cin, Cout, kh, kw, stride, pad, act, layout, dtype, &a, &f);
+    if (rc) return rc;
+    set_ok();
+    char tmp[200];
+    if (f.fused) {
+        snprintf(tmp, sizeof tmp, "stem3x3_mfma %s fused with maxpool3x3s2", dtype_name(dtype));
+    } else {
+        char inner[160];
+        describe(f.conv_plan, layout, dtype, inner, sizeof inner);
+        snprintf(tmp, sizeof tmp, "%s then maxpool3x3s2", inner);
+    }
+    int n = (int)strlen(tmp);
+    if (buf && cap > 0) {
+        strncpy(buf, tmp, (size_t)cap - 1);
+        buf[cap - 1] = 0;
+    }
+    return n;
 }
 
 int maxpool3x3s2(const void *x, void *y, int N, int H, int W, int C, int layout, int dtype,

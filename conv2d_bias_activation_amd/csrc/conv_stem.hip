@@ -213,6 +213,233 @@ __global__ __launch_bounds__(256) void stem3_kernel(ConvArgs a, int rstr) {
     }
 }
 
+// The same convolution followed by a 3x3 stride-2 pad-1 max pool, written as one
+// kernel that stores only the pooled map (the stem conv + max-pool step of the
+// inferencelayer page's `encoder_maps`). Workgroup: one pooled row py of one image
+// and 4 column groups (one per wave). A group covers 32 conv columns c0 = 30g - 1 ..
+// c0 + 31 of the three conv rows 2py-1 .. 2py+1 (six products per 32 channels); lane
+// rl = 2k+1 (k < 15) is the centre of pooled column 15g + k, so every pool window lies
+// inside one group (groups overlap by two columns). Max over the three rows in
+// registers, over the columns from lanes rl-1 and rl+1 (ds_bpermute), taken in fp32
+// on the activated sums: rounding is monotone, so rounding the maximum equals the
+// maximum of the rounded conv outputs. Taps outside the conv map count as -inf.
+template <typename T, int FN, int S>
+__global__ __launch_bounds__(256) void stem3_pool_kernel(ConvArgs a, int PH, int PW, int groups, int rstr,
+                                                         int ixs_step) {
+    constexpr int NW = 4;
+    constexpr int RS = 2 * S + 3;  // input rows staged
+    extern __shared__ __attribute__((aligned(16))) char srow[];  // [RS][rstr] bytes
+    __shared__ __attribute__((aligned(16))) float bal[2][32 * FN];
+    typedef typename Mfma32<T>::vec vec;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int rl = lane & 31, hi = lane >> 5;
+    const int H = a.H, W = a.W, OH = a.OH, OW = a.OW, Cout = a.Cout;
+    const int segs = (groups + NW - 1) / NW;
+    const int seg = blockIdx.x % segs, py = (blockIdx.x / segs) % PH, n = blockIdx.x / (segs * PH);
+    const int g = seg * NW + wave;
+
+    vec wa[2][FN];
+    {
+        const T *w = static_cast<const T *>(a.w);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int co = j * 32 + rl;
+            T v0[8], v1[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                v0[e] = co < Cout ? w[co * 27 + hi * 9 + e] : from_f32<T>(0.0f);
+                const int k1 = hi == 0 ? 18 + e : (e < 3 ? e * 9 + 8 : -1);
+                v1[e] = (co < Cout && k1 >= 0) ? w[co * 27 + k1] : from_f32<T>(0.0f);
+            }
+            __builtin_memcpy(&wa[0][j], v0, 16);
+            __builtin_memcpy(&wa[1][j], v1, 16);
+        }
+    }
+    if (threadIdx.x < 32 * FN) {
+        const int co = threadIdx.x;
+        bal[0][co] = a.bias && co < Cout ? a.bias[co] : 0.0f;
+        bal[1][co] = a.alpha && co < Cout ? a.alpha[co] : 0.0f;
+    }
+
+    // Stage input rows iy = (2py-1)*S - 1 + r, r < RS, from column ixs = 120*S*seg - 8 on
+    // (a multiple of 8 pixels, so the copy moves aligned 16-byte chunks; 8 columns before
+    // the segment's first patch column): column ix sits at byte 6*(ix - ixs) of LDS row r,
+    // and columns outside the image (padding) read as zero.
+    const int ixs = seg * ixs_step - 8;
+    {
+        const int row_bytes = W * 6;
+        const int chunks = rstr / 16;
+        const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint32_t)((size_t)a.N * H * row_bytes));
+        for (int i = threadIdx.x; i < RS * chunks; i += 256) {
+            const int r = i / chunks, c = i - r * chunks;
+            const int iy = (2 * py - 1) * S - 1 + r;
+            const int b = ixs * 6 + c * 16;  // byte within the image row
+            u32x4 v = u32x4{0u, 0u, 0u, 0u};
+            if (b >= 0 && b < row_bytes && (unsigned)iy < (unsigned)H)
+                v = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)((size_t)(n * H + iy) * row_bytes + b), 0, 0);
+            *reinterpret_cast<u32x4 *>(srow + r * rstr + c * 16) = v;
+        }
+    }
+    __syncthreads();
+    if (g >= groups) return;
+
+    const int c0 = 30 * g - 1;
+    const int cc = c0 + rl;                  // this lane's conv column
+    const bool col_ok = cc >= 0 && cc < OW;
+    const int ccr = cc < 0 ? 0 : (cc < OW ? cc : OW - 1);  // column read for the patch
+    const int byte = 6 * (ccr * S - 1 - ixs);
+    const int base = byte & ~3, sh = (byte & 3) * 8;
+    float best[FN][16];
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) best[j][e] = -__builtin_inff();
+    auto act_max = [&](auto act_tag, const f32x16 (&acc)[FN], bool ok) {
+        constexpr int ACT = decltype(act_tag)::value;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                float x = acc[j][e];
+                if constexpr (ACT == CONV2D_ACT_RELU) x = __builtin_fmaxf(x, 0.0f);
+                if constexpr (ACT == CONV2D_ACT_SILU) x = x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+                if constexpr (ACT == CONV2D_ACT_PRELU) {
+                    const float al = bal[1][j * 32 + 8 * (e / 4) + 4 * hi + (e % 4)];
+                    x = x >= 0.0f ? x : al * x;
+                }
+                best[j][e] = ok ? __builtin_fmaxf(best[j][e], x) : best[j][e];
+            }
+    };
+#pragma unroll
+    for (int dr = 0; dr < 3; ++dr) {
+        const int oy = 2 * py - 1 + dr;
+        const bool row_ok = oy >= 0 && oy < OH;
+        const int r0 = (dr + (row_ok ? 0 : (oy < 0 ? 1 : -1))) * S;  // a clamped row when out of range
+        uint32_t pr[3][4], p8[3];
+#pragma unroll
+        for (int ky = 0; ky < 3; ++ky) {
+            const uint32_t *src = reinterpret_cast<const uint32_t *>(srow + (r0 + ky) * rstr + base);
+            uint32_t d[5];
+#pragma unroll
+            for (int i = 0; i < 5; ++i) d[i] = src[i];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pr[ky][i] = __builtin_amdgcn_alignbit(d[i + 1], d[i], sh);
+            p8[ky] = (d[4] >> sh) & 0xffffu;
+        }
+        vec xb[2];
+        {
+            uint32_t b0[4], b1[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                b0[i] = hi ? pr[1][i] : pr[0][i];
+                b1[i] = hi ? 0u : pr[2][i];
+            }
+            if (hi) {
+                b1[0] = p8[0] | (p8[1] << 16);
+                b1[1] = p8[2];
+            }
+            __builtin_memcpy(&xb[0], b0, 16);
+            __builtin_memcpy(&xb[1], b1, 16);
+        }
+        f32x16 acc[FN];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const f32x4 bq = *reinterpret_cast<const f32x4 *>(&bal[0][j * 32 + 8 * gq + 4 * hi]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[j][4 * gq + e] = bq[e];
+            }
+            acc[j] = Mfma32<T>::run(wa[0][j], xb[0], acc[j]);
+            acc[j] = Mfma32<T>::run(wa[1][j], xb[1], acc[j]);
+        }
+        const bool ok = row_ok && col_ok;
+        switch (a.act) {
+        case CONV2D_ACT_RELU: act_max(std::integral_constant<int, CONV2D_ACT_RELU>{}, acc, ok); break;
+        case CONV2D_ACT_SILU: act_max(std::integral_constant<int, CONV2D_ACT_SILU>{}, acc, ok); break;
+        case CONV2D_ACT_PRELU: act_max(std::integral_constant<int, CONV2D_ACT_PRELU>{}, acc, ok); break;
+        default: act_max(std::integral_constant<int, CONV2D_ACT_NONE>{}, acc, ok); break;
+        }
+    }
+    // column max with the neighbouring conv columns (same half of the wave)
+    const int left = (lane - 1) * 4, right = (lane + 1 < 64 ? lane + 1 : lane) * 4;
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int v = __builtin_bit_cast(int, best[j][e]);
+            const float l = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(left < 0 ? 0 : left, v));
+            const float r = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(right, v));
+            best[j][e] = __builtin_fmaxf(best[j][e], __builtin_fmaxf(l, r));
+        }
+    // pooled column of this lane (odd lanes below 30 are window centres)
+    const int px = 15 * g + (rl - 1) / 2;
+    const bool store = (rl & 1) && rl < 30 && px < PW;
+    const __amdgpu_buffer_rsrc_t ry = make_rsrc(a.y, (uint32_t)((size_t)a.N * PH * PW * Cout * sizeof(T)));
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+            u32x2 q[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                T out[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) out[e] = from_f32<T>(best[j][4 * (2 * pp + h) + e]);
+                __builtin_memcpy(&q[h], out, 8);
+            }
+#pragma unroll
+            for (int d = 0; d < 2; ++d) {
+                const auto r2 = __builtin_amdgcn_permlane32_swap(q[0][d], q[1][d], false, false);
+                q[0][d] = r2[0];
+                q[1][d] = r2[1];
+            }
+            const int co = j * 32 + 16 * pp + 8 * hi;
+            const uint32_t off = (store && co < Cout)
+                                     ? ((uint32_t)((n * PH + py) * PW + px) * (uint32_t)Cout + (uint32_t)co) *
+                                           (uint32_t)sizeof(T)
+                                     : kOOB;
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4{q[0][0], q[0][1], q[1][0], q[1][1]}, ry, (int)off, 0, 0);
+        }
+}
+
+template <typename T, int FN, int S>
+static hipError_t launch_stem_pool_t(const ConvArgs &a, void *y, hipStream_t st) {
+    constexpr int RS = 2 * S + 3;
+    const int PH = (a.OH - 1) / 2 + 1, PW = (a.OW - 1) / 2 + 1;
+    const int groups = (PW + 14) / 15;
+    const int segs = (groups + 3) / 4;
+    // a segment of 4 groups covers conv columns 120*seg - 1 .. 120*seg + 120, i.e. input
+    // columns (120*seg - 1)*S - 1 .. (120*seg + 120)*S + 1; staging starts 8 columns
+    // before 120*S*seg and reads 20 bytes from each patch row's first dword
+    const int ixs_step = 120 * S;  // a multiple of 8
+    const int rstr = (6 * (120 * S + 16) + 16 + 15) / 16 * 16;
+    const size_t smem = (size_t)RS * rstr;
+    const long long blocks = (long long)a.N * PH * segs;
+    if (blocks * 256 > 0xffffffffll || smem > 64 * 1024) return hipErrorInvalidValue;
+    ConvArgs b = a;
+    b.y = y;
+    return launch_kernel(stem3_pool_kernel<T, FN, S>, dim3((unsigned)blocks), dim3(256), smem, st, b, PH, PW,
+                         groups, rstr, ixs_step);
+}
+
+template <typename T>
+static hipError_t launch_stem_pool_d(const ConvArgs &a, void *y, hipStream_t st) {
+    const int fn = a.Cout <= 32 ? 1 : 2;
+    if (a.stride == 2) return fn == 1 ? launch_stem_pool_t<T, 1, 2>(a, y, st) : launch_stem_pool_t<T, 2, 2>(a, y, st);
+    return fn == 1 ? launch_stem_pool_t<T, 1, 1>(a, y, st) : launch_stem_pool_t<T, 2, 1>(a, y, st);
+}
+
+hipError_t launch_stem3_maxpool(const ConvArgs &a, void *y, int dtype, hipStream_t st) {
+    switch (dtype) {
+    case CONV2D_DTYPE_BF16: return launch_stem_pool_d<bf16>(a, y, st);
+    case CONV2D_DTYPE_F16: return launch_stem_pool_d<f16>(a, y, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 template <typename T, int FN, int S>
 static hipError_t launch_stem_t(const ConvArgs &a, hipStream_t st) {
     constexpr int RB = 2;

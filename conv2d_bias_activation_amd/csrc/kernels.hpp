@@ -81,6 +81,11 @@ hipError_t launch_halo3x3(const ConvArgs &a, int dtype, const HaloPlan &p, hipSt
 // 16-byte aligned, y and the residual 16-byte aligned (a.vec_out), tensors under 2 GiB.
 hipError_t launch_stem3(const ConvArgs &a, int dtype, hipStream_t st);
 
+// The same convolution followed by the 3x3 stride-2 pad-1 max pool in one kernel: only
+// the pooled map is written, to y ([N, PH, PW, Cout] with PH = (OH - 1) / 2 + 1, 16-byte
+// aligned); a.y and a.res are ignored. Same limits as launch_stem3 except the width.
+hipError_t launch_stem3_maxpool(const ConvArgs &a, void *y, int dtype, hipStream_t st);
+
 // Direct convolution on the vector ALUs for few input channels (the image stem):
 // one thread per output pixel and a block of output channels.
 hipError_t launch_direct(const ConvArgs &a, int dtype, bool nchw, hipStream_t st);

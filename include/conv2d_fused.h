@@ -26,7 +26,9 @@
  *    unit count of each device (queried once), and, per device, one 64 MiB
  *    scratch buffer that the library allocates on the first call that needs it
  *    and keeps until the process ends. It holds the fp32 partial sums of split-K
- *    calls and the channel-last copies of x and w of 16-bit channel-first calls.
+ *    calls, the channel-last copies of x and w of 16-bit channel-first calls and
+ *    the unpooled conv output of conv2d_fused_maxpool3x3s2 calls that run as two
+ *    kernels.
  *    Such calls on one device all use that buffer: callers that run conv2d_fused
  *    on several streams of one device at the same time must serialise those
  *    calls. (Under HIP graph capture, make one call on each device before
@@ -124,6 +126,34 @@ int conv2d_fused(const void *x, const void *w, const float *bias, const float *a
  */
 int maxpool3x3s2(const void *x, void *y, int N, int H, int W, int C, int layout, int dtype,
                  void *stream);
+
+/*
+ * y = maxpool3x3s2(conv2d_fused(x, w, bias, alpha, no residual)): the image stem
+ * conv and the max pool after it, with only the pooled map written.
+ * Source: inferencelayer page, `encoder_maps` (the stem conv followed by the 3x3
+ * stride-2 max pool) with `conv()` and `MAXPOOL_SRC` as above.
+ *
+ * Arguments as conv2d_fused (no residual; act may not carry CONV2D_RES_BEFORE_ACT),
+ * except y: [N,PH,PW,Cout] or [N,Cout,PH,PW] in `dtype` with PH = (OH - 1)/2 + 1,
+ * PW = (OW - 1)/2 + 1 and OH, OW the conv's output size. y may not overlap x.
+ *
+ * The max is taken on the activated fp32 values and then rounded; rounding is
+ * monotone, so this equals rounding first and pooling after. Channel-last 16-bit
+ * 3-channel 3x3 pad-1 convs (Cout <= 64, Cout % 8 == 0, W % 8 == 0, W <= 3000, x and
+ * y 16-byte aligned) run as one kernel that keeps the conv output on chip. Any
+ * other shape runs the conv into the library's per-device scratch buffer and then
+ * the pool kernel; that needs N*OH*OW*Cout elements of `dtype` to fit the 64 MiB
+ * buffer (CONV2D_EUNSUPPORTED otherwise), and it shares the buffer as conv2d_fused
+ * does.
+ */
+int conv2d_fused_maxpool3x3s2(const void *x, const void *w, const float *bias, const float *alpha,
+                              void *y, int N, int H, int W, int Cin, int Cout, int kh, int kw,
+                              int stride, int pad, int act, int layout, int dtype, void *stream);
+
+/* Host-only: the kernel variants conv2d_fused_maxpool3x3s2 would launch for this
+ * shape (as conv2d_plan), e.g. "stem3x3_mfma bf16 fused with maxpool3x3s2". */
+int conv2d_fused_maxpool_plan(int N, int H, int W, int Cin, int Cout, int kh, int kw, int stride,
+                              int pad, int act, int layout, int dtype, char *buf, int cap);
 
 /*
  * 2x2 average pool, stride 2, no padding.

@@ -88,3 +88,36 @@ def test_plan_names_a_kernel_for_every_workload_shape():
         assert name.startswith(family), (s, name)
     with pytest.raises(c2d.Conv2dError):
         c2d.plan(1, 8, 8, 4, 4, 3, 3, 5, 1, 0, 0, bf16)
+
+
+def test_conv_pool_plan_and_argument_checks():
+    """Host-only: which kernels conv2d_fused_maxpool3x3s2 picks, and what it rejects
+    before launching anything."""
+    bf16, f32 = c2d.DTYPE_BF16, c2d.DTYPE_F32
+    assert c2d.plan_maxpool(1, 640, 640, 3, 32, 3, 3, 2, 1, 2, 0, bf16) == "stem3x3_mfma bf16 fused with maxpool3x3s2"
+    assert c2d.plan_maxpool(1, 640, 640, 3, 32, 3, 3, 2, 1, 2, 0, f32).startswith("direct_nhwc")
+    assert c2d.plan_maxpool(1, 640, 640, 3, 32, 3, 3, 2, 1, 2, 0, f32).endswith("then maxpool3x3s2")
+    # channel-first 16-bit layers keep the scratch for the conv output: the general kernel
+    assert c2d.plan_maxpool(1, 17, 23, 40, 72, 3, 3, 2, 1, 1, 1, bf16).startswith("igemm_nchw")
+    # split-K is turned off for the same reason
+    assert "splitk=1" in c2d.plan_maxpool(1, 10, 10, 512, 512, 3, 3, 1, 1, 1, 0, bf16)
+    # an unpooled conv output over the 64 MiB scratch
+    with pytest.raises(c2d.Conv2dError) as e:
+        c2d.plan_maxpool(4, 640, 640, 64, 64, 3, 3, 1, 1, 1, 0, bf16)
+    assert e.value.code == c2d.EUNSUPPORTED
+    lib = c2d._load()
+    P = ctypes.c_void_p
+    x, w, y = P(0x100000000), P(0x900000000), P(0x1100000000)
+    # a residual-order flag: there is no residual in this entry point
+    rc = lib.conv2d_fused_maxpool3x3s2(x, w, None, None, y, 1, 16, 16, 3, 32, 3, 3, 2, 1,
+                                       1 | c2d.RES_BEFORE_ACT, 0, bf16, None)
+    assert rc == c2d.EINVAL
+    # pooled y overlapping x (1x16x16x3 bf16 = 1536 bytes)
+    rc = lib.conv2d_fused_maxpool3x3s2(x, w, None, None, P(0x100000000 + 1024), 1, 16, 16, 3, 32, 3, 3, 2, 1,
+                                       1, 0, bf16, None)
+    assert rc == c2d.EINVAL and "overlaps" in c2d.last_error()
+    # y just past x is fine for the check (the conv-size extent is not used)
+    assert lib.conv2d_check_args(x, w, None, None, None, P(0x100000000 + 1536), 1, 16, 16, 3, 32, 3, 3, 2, 1,
+                                 1, 0, bf16) == c2d.OK
+    rc = lib.conv2d_fused_maxpool3x3s2(x, w, None, None, y, 1, 16, 16, 3, 32, 3, 3, 3, 1, 1, 0, bf16, None)
+    assert rc == c2d.EINVAL  # stride 3

@@ -1,0 +1,135 @@
+"""GPU parity of conv2d_fused_maxpool3x3s2 (conv + 3x3/s2/p1 max pool in one call)
+against the CPU oracle, and bit for bit against the two-call path (needs an MI355X)."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from parity import bits_equal, gate, to64
+
+pytestmark = pytest.mark.gpu
+
+c2d = pytest.importorskip("conv2d_bias_activation_amd")
+DEV = torch.device("cuda")
+DT = {"f32": 0, "bf16": 1, "f16": 2}
+
+
+def _dev(t):
+    return None if t is None else t.to(DEV)
+
+
+def _fused(x, spec, layout):
+    return c2d.conv2d_fused_maxpool3x3s2(_dev(x), _dev(spec.w), _dev(spec.bias), _dev(spec.alpha),
+                                         stride=spec.stride, pad=spec.pad, act=spec.act, layout=layout)
+
+
+def _two_calls(x, spec, layout):
+    y = c2d.conv2d_fused(_dev(x), _dev(spec.w), _dev(spec.bias), _dev(spec.alpha), stride=spec.stride,
+                         pad=spec.pad, act=spec.act, layout=layout)
+    return c2d.maxpool3x3s2(y, layout=layout)
+
+
+def _oracle(x, spec, layout):
+    conv = oracle.conv2d(to64(x), to64(spec.w), to64(spec.bias) if spec.bias is not None else None,
+                         to64(spec.alpha) if spec.alpha is not None else None, None, stride=spec.stride,
+                         pad=spec.pad, act=spec.act, layout=layout)
+    return oracle.maxpool3x3s2(conv, layout=layout)
+
+
+def _check(x, spec, layout, dtype, what, want_fused, bitexact_vs_two_calls=True):
+    n, h, w = (x.shape[0], x.shape[1], x.shape[2]) if layout == "nhwc" else (x.shape[0], x.shape[2], x.shape[3])
+    args = (n, h, w, spec.cin, spec.cout, spec.k, spec.k, spec.stride, spec.pad, 0,
+            0 if layout == "nhwc" else 1, DT[dtype])
+    plan = c2d.plan_maxpool(*args)
+    print(f"case {what} plan {plan}", flush=True)
+    assert ("fused" in plan) == want_fused, plan
+    y = _fused(x, spec, layout)
+    torch.cuda.synchronize()
+    gate(to64(y), _oracle(x, spec, layout), dtype, what=what)
+    if bitexact_vs_two_calls:
+        # same conv kernel arithmetic; rounding is monotone, so pooling before or after
+        # the rounding gives the same bits
+        assert c2d.plan(*args) in plan, (c2d.plan(*args), plan)
+        y2 = _two_calls(x, spec, layout)
+        torch.cuda.synchronize()
+        assert bits_equal(y, y2), what
+
+
+# The 3-channel stem in one kernel: (n, h, w, cout, stride, act, dtype). Ragged pooled
+# widths (not a multiple of the 15 columns a wave pools, nor of the 4 waves), odd and
+# even conv sizes (the last pool window clipped or not), one-row images and the
+# narrowest width.
+FUSED = [
+    (1, 17, 24, 32, 2, "silu", "bf16"),
+    (2, 32, 40, 64, 2, "relu", "f16"),
+    (1, 21, 16, 32, 1, "prelu", "bf16"),
+    (3, 9, 8, 16, 1, "none", "bf16"),
+    (1, 64, 248, 48, 2, "relu", "bf16"),
+    (1, 1, 8, 32, 2, "relu", "bf16"),
+    (1, 2, 8, 32, 1, "silu", "f16"),
+    (2, 130, 136, 64, 2, "relu", "bf16"),
+    (1, 40, 488, 24, 1, "silu", "f16"),
+    (1, 61, 960, 32, 2, "prelu", "bf16"),
+    (2, 33, 1208, 8, 1, "relu", "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", FUSED, ids=lambda c: "-".join(map(str, c)))
+def test_fused_stem_maxpool(case):
+    n, h, w, cout, s, act, dtype = case
+    x, spec, _ = wl.random_conv_case(zlib.crc32(repr(case).encode()), n=n, h=h, w=w, cin=3, cout=cout, k=3,
+                                     stride=s, pad=1, act=act, layout="nhwc", dtype=dtype, x_dist="uniform")
+    _check(x, spec, "nhwc", dtype, str(case), want_fused=True)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_fused_stem_maxpool_full_image(dtype):
+    """The 640x640 stem conv (3 -> 32, stride 2, SiLU) and its max pool: 1x160x160x32."""
+    wk = wl.conv2_stem(dtype)
+    spec = wk.layers[0]
+    _check(wk.x, spec, "nhwc", dtype, f"stem 640x640 {dtype}", want_fused=True)
+
+
+# Shapes outside the fused kernel: the conv into the library scratch, then the pool.
+# (n, h, w, cin, cout, k, stride, pad, act, layout, dtype, same kernels as two calls)
+UNFUSED = [
+    (1, 23, 19, 3, 32, 3, 2, 1, "silu", "nhwc", "f32", True),     # fp32 stem: direct kernel
+    (1, 20, 22, 3, 32, 3, 2, 1, "relu", "nhwc", "bf16", True),    # W % 8 != 0
+    (2, 18, 16, 3, 72, 3, 2, 1, "relu", "nhwc", "bf16", True),    # Cout > 64
+    (2, 37, 45, 32, 64, 3, 1, 1, "relu", "nhwc", "bf16", True),   # halo kernel
+    (1, 30, 26, 64, 64, 3, 1, 1, "prelu", "nhwc", "f16", True),   # halo kernel, Cin 64
+    (2, 17, 23, 40, 72, 3, 2, 1, "relu", "nchw", "f16", False),   # channel-first: general kernel
+    (1, 16, 18, 3, 16, 3, 2, 1, "silu", "nchw", "f32", True),
+    (1, 10, 10, 512, 512, 3, 1, 1, "relu", "nhwc", "bf16", False),  # split-K turned off
+    (1, 12, 14, 16, 24, 5, 2, 2, "none", "nhwc", "bf16", True),
+]
+
+
+@pytest.mark.parametrize("case", UNFUSED, ids=lambda c: "-".join(map(str, c)))
+def test_two_kernel_path(case):
+    n, h, w, cin, cout, k, s, p, act, layout, dtype, same = case
+    x, spec, _ = wl.random_conv_case(zlib.crc32(repr(case).encode()), n=n, h=h, w=w, cin=cin, cout=cout, k=k,
+                                     stride=s, pad=p, act=act, layout=layout, dtype=dtype)
+    _check(x, spec, layout, dtype, str(case), want_fused=False, bitexact_vs_two_calls=same)
+
+
+def test_fused_writes_only_the_pooled_map():
+    """Guard bytes around y keep their value, and repeated calls give the same bits."""
+    x, spec, _ = wl.random_conv_case(11, n=2, h=50, w=64, cin=3, cout=32, k=3, stride=2, pad=1, act="relu",
+                                     layout="nhwc", dtype="bf16", x_dist="uniform")
+    ph, pw = (25 - 1) // 2 + 1, (32 - 1) // 2 + 1  # conv 25 x 32
+    numel = 2 * ph * pw * 32
+    buf = torch.full((numel + 2 * 4096,), 7.0, dtype=torch.bfloat16, device=DEV)
+    out = buf[4096:4096 + numel].view(2, ph, pw, 32)
+    c2d.conv2d_fused_maxpool3x3s2(_dev(x), _dev(spec.w), _dev(spec.bias), None, stride=2, pad=1, act="relu",
+                                  out=out)
+    first = out.clone()
+    c2d.conv2d_fused_maxpool3x3s2(_dev(x), _dev(spec.w), _dev(spec.bias), None, stride=2, pad=1, act="relu",
+                                  out=out)
+    torch.cuda.synchronize()
+    assert bits_equal(first, out)
+    assert torch.all(buf[:4096] == 7.0) and torch.all(buf[4096 + numel:] == 7.0)
+    gate(to64(out), _oracle(x, spec, "nhwc"), "bf16", what="guarded")
