@@ -444,9 +444,11 @@ int launch_conv(const ConvArgs &a, const Plan &p, int layout, int dtype, hipStre
     return CONV2D_OK;
 }
 
+enum PoolKernel { POOL_TWO_KERNELS = 0, POOL_FUSED_STEM = 1, POOL_FUSED_HALO = 2 };
+
 struct PoolFusion {
-    bool fused;      // the fused stem + pool kernel
-    Plan conv_plan;  // otherwise: this conv into the scratch, then the pool kernel
+    int kind;        // PoolKernel
+    Plan conv_plan;  // POOL_TWO_KERNELS: this conv into the scratch, then the pool kernel
 };
 
 // Validates conv2d_fused_maxpool3x3s2's arguments (y is the pooled map) and picks the
@@ -459,8 +461,11 @@ int check_conv_pool(const void *x, const void *w, const float *alpha, const void
     int rc = check_conv(x, w, alpha, nullptr, y, N, H, W, Cin, Cout, kh, kw, stride, pad, act, layout, dtype, a,
                         true);
     if (rc) return rc;
-    f->fused = stem_fits(*a, layout, dtype);
-    if (!f->fused) {
+    const long long xbytes = (long long)N * H * W * Cin * dtype_bytes(dtype);
+    f->kind = stem_fits(*a, layout, dtype) ? POOL_FUSED_STEM
+              : (halo_fits(*a, layout, dtype) && Cin <= 32 && xbytes < (1ll << 31)) ? POOL_FUSED_HALO
+                                                                                     : POOL_TWO_KERNELS;
+    if (f->kind == POOL_TWO_KERNELS) {
         // the conv output goes to the library scratch, which the conv kernels then must
         // not use themselves: no split-K, and channel-first layers on the general kernel
         if ((long long)a->M * Cout * dtype_bytes(dtype) > (long long)kScratchBytes)
@@ -536,8 +541,16 @@ int conv2d_fused_maxpool3x3s2(const void *x, const void *w, const float *bias, c
     a.bias = bias;
     if ((act & 0xff) != CONV2D_ACT_PRELU) a.alpha = nullptr;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (f.fused) {
-        hipError_t e = launch_stem3_maxpool(a, y, dtype, st);
+    if (f.kind != POOL_TWO_KERNELS) {
+        hipError_t e;
+        if (f.kind == POOL_FUSED_STEM) {
+            e = launch_stem3_maxpool(a, y, dtype, st);
+        } else {
+            int cus = 0;
+            rc = device_cus(&cus);
+            if (rc) return rc;
+            e = launch_halo3x3_maxpool(a, y, dtype, 2 * cus, st);
+        }
         if (e != hipSuccess) return hip_fail(e, "conv2d_fused_maxpool3x3s2 launch");
         return set_ok();
     }
@@ -569,8 +582,11 @@ int conv2d_fused_maxpool_plan(int N, int H, int W, int Cin, int Cout, int kh, in
     if (rc) return rc;
     set_ok();
     char tmp[200];
-    if (f.fused) {
+    if (f.kind == POOL_FUSED_STEM) {
         snprintf(tmp, sizeof tmp, "stem3x3_mfma %s fused with maxpool3x3s2", dtype_name(dtype));
+    } else if (f.kind == POOL_FUSED_HALO) {
+        snprintf(tmp, sizeof tmp, "halo3x3_nhwc %s th4 co%d w4 fused with maxpool3x3s2", dtype_name(dtype),
+                 Cout <= 32 ? 32 : 64);
     } else {
         char inner[160];
         describe(f.conv_plan, layout, dtype, inner, sizeof inner);

@@ -40,8 +40,13 @@ template <int N> __device__ __forceinline__ void halo_wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// Workgroup barrier. s_barrier alone does not wait for the wave's own LDS writes
+// (ds_write) to land, so lgkmcnt(0) comes first: the partial sums that a k-split
+// pair exchanges and the pooled rows are complete for every wave that passes it.
+// Direct-to-LDS loads are published by the explicit vmcnt waits instead.
 __device__ __forceinline__ void halo_barrier() {
     asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 }
@@ -52,8 +57,27 @@ __device__ __forceinline__ void halo_barrier() {
 // FN 32-channel output blocks per wave (the workgroup covers 32*FN channels); WK
 // waves along k (each takes CIN/WK of the input channels of every tap and the pair
 // adds their sums through LDS); NW / WK waves along the tile rows.
-template <typename T, int CIN, int TH, int FN, int WK, int NW>
-__global__ __launch_bounds__(64 * NW, 8 / NW) void halo3x3_kernel(ConvArgs a, int tiles_w, int tiles_h, int ntiles) {
+//
+// POOL: the 3x3 stride-2 pad-1 max pool of the output is written instead of the
+// output (p.y, [N, PH, PW, Cout]); TH = 4, one tile row per wave, no k split, no
+// residual. A tile is 4 conv rows 4ty.. by 32 conv columns 30tx - 1.. (columns
+// overlap by two, so pooled column 15tx + c is centred on lane 2c + 1 of every row,
+// c < 15) and gives pooled rows 2ty and 2ty + 1: rows 4ty-1..4ty+1 and 4ty+1..4ty+3.
+// Each workgroup walks one run of tiles down the image (ty = seg*L .. seg*L + L - 1),
+// carrying the activated, column-maxed last row of a tile in LDS into the next; a run
+// that does not start at the top first computes the last row of the tile above
+// (one wave's products). The max is taken on rounded values: rounding is monotone,
+// so this equals pooling the rounded conv output.
+struct HaloPool {
+    void *y;
+    int PH, PW;
+    int seg_len;  // tiles per run
+    int segs;     // runs per column of tiles
+};
+
+template <typename T, int CIN, int TH, int FN, int WK, int NW, bool POOL>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void halo3x3_kernel(ConvArgs a, int tiles_w, int tiles_h, int ntiles,
+                                                                  HaloPool pl) {
     constexpr int WM = NW / WK;
     constexpr int FM = TH / WM;               // 32-pixel tile rows per wave
     static_assert(WM >= 1 && FM >= 1 && FM * WM == TH, "tile rows split evenly over the waves");
@@ -79,8 +103,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void halo3x3_kernel(ConvArgs a, in
     constexpr int NP = NG / 2;                // pairs of them: one 16-byte store per lane
     constexpr int XBYTES = FM * FN * 2 * 1024;  // per wave: 8 floats per lane per block
     constexpr int XCH = WK == 2 ? NW * XBYTES : 16;
+    static_assert(!POOL || (TH == 4 && FM == 1 && WK == 1), "pooled tiles: 4 rows, one per wave");
+    // POOL: six rows of [64 lanes][FN * 32 values] in T: the tile's rows 0..2 and two
+    // carry rows (the last row of the tile before and of this one), by tile parity
+    constexpr int PROW = FN * 2 * 1024;
     __shared__ __attribute__((aligned(1024))) char ring[RING];
     __shared__ __attribute__((aligned(1024))) char xch[XCH];
+    __shared__ __attribute__((aligned(16))) char prow[POOL ? 6 * PROW : 16];
     __shared__ __attribute__((aligned(16))) float bal[2][32 * FN];  // bias, slopes (0 past Cout)
     char *const hb0 = ring;
     char *const hb1 = ring + HBUF;
@@ -140,18 +169,40 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void halo3x3_kernel(ConvArgs a, in
 
     // Tile order: G workgroups, the ones on one XCD (blockIdx % 8) take a contiguous
     // run of each round's G tiles, so neighbouring tiles share halo rows in one L2.
+    // POOL: workgroup = one run of tiles down one column of tiles.
     const int G = gridDim.x;
     const int r = (G % 8) == 0 ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
+    struct Geo {
+        int n, oy0, ox0;
+        bool live;  // a tile of this workgroup
+        bool pool;  // POOL: writes pooled rows (else only the carry row)
+    };
+    auto geo = [&](int k) -> Geo {
+        if constexpr (!POOL) {
+            const int t = k * G + r;
+            const bool live = t < ntiles;
+            const int tt = live ? t : 0;
+            const int tx = tt % tiles_w, rr = tt / tiles_w;
+            const int ty = rr % tiles_h, n = rr / tiles_h;
+            return Geo{n, ty * TH, tx * TW, live, false};
+        } else {
+            const int seg = blockIdx.x % pl.segs, rest = blockIdx.x / pl.segs;
+            const int tx = rest % tiles_w, n = rest / tiles_w;
+            const int first = seg * pl.seg_len - (seg > 0 ? 1 : 0);
+            const int end = (seg + 1) * pl.seg_len < tiles_h ? (seg + 1) * pl.seg_len : tiles_h;
+            const int ty = first + k;
+            const bool live = ty < end;
+            return Geo{n, (live ? ty : first) * TH, tx * 30 - 1, live, !(seg > 0 && k == 0)};
+        }
+    };
 
     const i32x4 rx = rsrc_words(a.x, (uint32_t)((size_t)a.N * H * W * CIN * sizeof(T)));
-    // Halo of tile t into buf; a t past the last tile issues the same number of
-    // loads with out-of-range offsets (no traffic), so the vmcnt waits stay exact.
-    auto issue = [&](char *buf, int t) {
-        const bool live = t < ntiles;
-        const int tt = live ? t : 0;
-        const int tx = tt % tiles_w, rr = tt / tiles_w;
-        const int ty = rr % tiles_h, n = rr / tiles_h;
-        const int oy0 = ty * TH, ox0 = tx * TW;
+    // Halo of the workgroup's tile k into buf; a k past its last tile issues the same
+    // number of loads with out-of-range offsets (no traffic), so the vmcnt waits stay exact.
+    auto issue = [&](char *buf, int k) {
+        const Geo g = geo(k);
+        const bool live = g.live;
+        const int n = g.n, oy0 = g.oy0, ox0 = g.ox0;
 #pragma unroll
         for (int d = 0; d < NDW; ++d) {
             const int slot = (d * NW + wave) * 64 + lane;
@@ -223,13 +274,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void halo3x3_kernel(ConvArgs a, in
     const __amdgpu_buffer_rsrc_t rres = make_rsrc(a.res, has_res ? out_bytes : 0u);
     const __amdgpu_buffer_rsrc_t ry = make_rsrc(a.y, out_bytes);
     const int p0 = g0 / 2;
-    auto out_off = [&](int t, int i, int j, int pp) -> uint32_t {
-        const int tx = t % tiles_w, rr = t / tiles_w;
-        const int ty = rr % tiles_h, n = rr / tiles_h;
-        const int oy = ty * TH + wm * FM + i, ox = tx * TW + rl;
+    auto out_off = [&](const Geo &g, int i, int j, int pp) -> uint32_t {
+        const int oy = g.oy0 + wm * FM + i, ox = g.ox0 + rl;
         const int co = j * 32 + 16 * (p0 + pp) + 8 * hi;
-        return (oy < H && ox < W && co < Cout)
-                   ? ((uint32_t)((n * H + oy) * W + ox) * (uint32_t)Cout + (uint32_t)co) * (uint32_t)sizeof(T)
+        return (g.live && oy < H && ox < W && co < Cout)
+                   ? ((uint32_t)((g.n * H + oy) * W + ox) * (uint32_t)Cout + (uint32_t)co) * (uint32_t)sizeof(T)
                    : kOOB;
     };
     // lanes 32..63 of lo trade with lanes 0..31 of hi, for each of the two dwords
@@ -242,6 +291,104 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void halo3x3_kernel(ConvArgs a, in
         }
     };
 
+    // POOL epilogue of tile k: this wave's conv row, activated, -inf outside the conv
+    // output, maxed with its left and right neighbour columns (lanes rl -/+ 1 of the
+    // same half) and rounded, goes to LDS row wm (the last wave's to the carry row of
+    // tile k + 1); then wave 0 maxes the carry row of tile k with rows 0 and 1 into
+    // pooled row 2ty, and wave 1 rows 1, 2 and the new carry into pooled row 2ty + 1.
+    const __amdgpu_buffer_rsrc_t rp =
+        make_rsrc(pl.y, POOL ? (uint32_t)((size_t)a.N * pl.PH * pl.PW * Cout * sizeof(T)) : 0u);
+    auto prow_at = [&](int row, int q) -> char * { return prow + row * PROW + (q * 64 + lane) * 16; };
+    auto pool_rows = [&](const Geo &tg, int k) {
+        const int oy = tg.oy0 + wm, ox = tg.ox0 + rl;
+        const bool valid = (unsigned)oy < (unsigned)H && (unsigned)ox < (unsigned)W;
+        auto act_all = [&](auto act_tag) {
+            constexpr int ACT = decltype(act_tag)::value;
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    float x = acc[0][j][e];
+                    if constexpr (ACT == CONV2D_ACT_RELU) x = __builtin_fmaxf(x, 0.0f);
+                    if constexpr (ACT == CONV2D_ACT_SILU) x = x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+                    if constexpr (ACT == CONV2D_ACT_PRELU) {
+                        const float al = bal[1][j * 32 + 8 * (e / 4) + 4 * hi + (e % 4)];
+                        x = x >= 0.0f ? x : al * x;
+                    }
+                    acc[0][j][e] = valid ? x : -__builtin_inff();
+                }
+        };
+        switch (a.act) {
+        case CONV2D_ACT_RELU: act_all(std::integral_constant<int, CONV2D_ACT_RELU>{}); break;
+        case CONV2D_ACT_SILU: act_all(std::integral_constant<int, CONV2D_ACT_SILU>{}); break;
+        case CONV2D_ACT_PRELU: act_all(std::integral_constant<int, CONV2D_ACT_PRELU>{}); break;
+        default: act_all(std::integral_constant<int, CONV2D_ACT_NONE>{}); break;
+        }
+        const int left = (lane == 0 ? 0 : lane - 1) * 4, right = (lane == 63 ? 63 : lane + 1) * 4;
+        const int row = wm == WM - 1 ? 4 + ((k + 1) & 1) : wm;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            T q[16];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                // through a scalar: this compiler lowers a bit cast applied directly to a
+                // vector element as a read of element 0
+                const float c = acc[0][j][e];
+                const int v = __builtin_bit_cast(int, c);
+                const float l = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(left, v));
+                const float rgt = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(right, v));
+                q[e] = from_f32<T>(__builtin_fmaxf(c, __builtin_fmaxf(l, rgt)));
+            }
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp) {
+                u32x4 w4;
+                __builtin_memcpy(&w4, &q[8 * pp], 16);
+                *reinterpret_cast<u32x4 *>(prow_at(row, j * 2 + pp)) = w4;
+            }
+        }
+        halo_barrier();
+        if (!tg.pool || wm > 1) return;
+        const int r0 = wm == 0 ? 4 + (k & 1) : 1, r1 = wm == 0 ? 0 : 2, r2 = wm == 0 ? 1 : 4 + ((k + 1) & 1);
+        const int py = tg.oy0 / 2 + wm, px = (tg.ox0 + 1) / 2 + (rl - 1) / 2;
+        const bool store = (rl & 1) && rl < 30 && px < pl.PW && py < pl.PH;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp) {
+                const u32x4 v0 = *reinterpret_cast<const u32x4 *>(prow_at(r0, j * 2 + pp));
+                const u32x4 v1 = *reinterpret_cast<const u32x4 *>(prow_at(r1, j * 2 + pp));
+                const u32x4 v2 = *reinterpret_cast<const u32x4 *>(prow_at(r2, j * 2 + pp));
+                T t0[8], t1[8], t2[8], m[8];
+                __builtin_memcpy(t0, &v0, 16);
+                __builtin_memcpy(t1, &v1, 16);
+                __builtin_memcpy(t2, &v2, 16);
+                // The max is taken in fp32 behind an empty asm: left to itself, this compiler
+                // turns an f16 max of this shape into v_max3_f16 and then packs two results
+                // with a plain OR, as if the instruction cleared the upper 16 bits of its
+                // destination, which it does not (the odd channel of each pair came out wrong).
+                auto wide = [](T v) {
+                    float f = to_f32(v);
+                    asm volatile("" : "+v"(f));
+                    return f;
+                };
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    m[e] = from_f32<T>(__builtin_fmaxf(wide(t0[e]), __builtin_fmaxf(wide(t1[e]), wide(t2[e]))));
+                // groups 2pp, 2pp+1 (4 channels each) -> 8 consecutive channels per lane half
+                u32x2 qq[2];
+                __builtin_memcpy(&qq[0], &m[0], 8);
+                __builtin_memcpy(&qq[1], &m[4], 8);
+                swap_halves(qq[0], qq[1]);
+                const int co = j * 32 + 16 * pp + 8 * hi;
+                const uint32_t off = (store && co < Cout)
+                                         ? ((uint32_t)((tg.n * pl.PH + py) * pl.PW + px) * (uint32_t)Cout +
+                                            (uint32_t)co) * (uint32_t)sizeof(T)
+                                         : kOOB;
+                __builtin_amdgcn_raw_buffer_store_b128(u32x4{qq[0][0], qq[0][1], qq[1][0], qq[1][1]}, rp, (int)off,
+                                                       0, 0);
+            }
+    };
+
     float *mine = reinterpret_cast<float *>(xch + wave * XBYTES);
     const float *theirs = reinterpret_cast<const float *>(xch + (WK == 2 ? (wave + (wk ? -WM : WM)) : wave) * XBYTES);
 
@@ -252,7 +399,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void halo3x3_kernel(ConvArgs a, in
     // loads (the residual, and the halo of tile k+1, which has had this tile's
     // products to arrive), refill buf with tile k+2, epilogue and stores.
     auto tile = [&](char *buf, int k) {
-        const int t = k * G + r;
+        const Geo tg = geo(k);
         halo_barrier();
         uint32_t off[FM][FN][NP];
         u32x4 rv[FM][FN][NP];
@@ -262,11 +409,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void halo3x3_kernel(ConvArgs a, in
             for (int j = 0; j < FN; ++j)
 #pragma unroll
                 for (int pp = 0; pp < NP; ++pp) {
-                    off[i][j][pp] = out_off(t, i, j, pp);
-                    rv[i][j][pp] = has_res ? __builtin_amdgcn_raw_buffer_load_b128(rres, (int)off[i][j][pp], 0, 0)
-                                           : u32x4{0u, 0u, 0u, 0u};
+                    off[i][j][pp] = out_off(tg, i, j, pp);
+                    rv[i][j][pp] = (!POOL && has_res) ? __builtin_amdgcn_raw_buffer_load_b128(rres, (int)off[i][j][pp], 0, 0)
+                                                      : u32x4{0u, 0u, 0u, 0u};
                 }
-        compute(buf);
+        // a carry-only tile needs the last row alone
+        if (!POOL || tg.pool || wm == WM - 1) compute(buf);
         if constexpr (WK == 2) {
             const int hs = 1 - wk;  // the channel groups (2hs, 2hs+1) the partner stores
 #pragma unroll
@@ -294,7 +442,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void halo3x3_kernel(ConvArgs a, in
                     }
         }
         halo_wait_vmcnt<0>();
-        issue(buf, (k + 2) * G + r);
+        issue(buf, k + 2);
+        if constexpr (POOL) {
+            pool_rows(tg, k);
+            return;
+        }
         auto finish = [&](auto act_tag, auto res_tag) {
             constexpr int ACT = decltype(act_tag)::value;
             constexpr int RES = decltype(res_tag)::value;
@@ -346,12 +498,24 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void halo3x3_kernel(ConvArgs a, in
         default: with_res(std::integral_constant<int, CONV2D_ACT_NONE>{}); break;
         }
     };
-    issue(hb0, r);
-    issue(hb1, G + r);
+    if constexpr (POOL) {
+        // the carry into a run's first tile: the row above the image
+        if (wm == 0) {
+            T ninf[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ninf[e] = from_f32<T>(-__builtin_inff());
+            u32x4 w4;
+            __builtin_memcpy(&w4, ninf, 16);
+#pragma unroll
+            for (int q = 0; q < 2 * FN; ++q) *reinterpret_cast<u32x4 *>(prow_at(4, q)) = w4;
+        }
+    }
+    issue(hb0, 0);
+    issue(hb1, 1);
     halo_wait_vmcnt<0>();
-    for (int k = 0; k * G + r < ntiles; k += 2) {
+    for (int k = 0; geo(k).live; k += 2) {
         tile(hb0, k);
-        if ((k + 1) * G + r >= ntiles) break;
+        if (!geo(k + 1).live) break;
         tile(hb1, k + 1);
     }
     halo_wait_vmcnt<0>();
@@ -366,8 +530,30 @@ static hipError_t launch_halo_t(const ConvArgs &a, int grid_cap, hipStream_t st)
     int grid = ntiles < grid_cap ? ntiles : grid_cap;
     if (grid > 8) grid -= grid % 8;
     constexpr int WK = CIN == 64 ? 2 : 1;
-    return launch_kernel(halo3x3_kernel<T, CIN, TH, FN, WK, NW>, dim3(grid), dim3(64 * NW), 0, st, a, tiles_w,
-                         tiles_h, ntiles);
+    return launch_kernel(halo3x3_kernel<T, CIN, TH, FN, WK, NW, false>, dim3(grid), dim3(64 * NW), 0, st, a,
+                         tiles_w, tiles_h, ntiles, HaloPool{});
+}
+
+// Pooled variant: runs of seg_len tiles, about two workgroups per CU (grid_cap slots).
+template <typename T, int CIN, int FN>
+static hipError_t launch_halo_pool_t(const ConvArgs &a, void *y, int grid_cap, hipStream_t st) {
+    HaloPool pl{};
+    pl.y = y;
+    pl.PH = (a.OH - 1) / 2 + 1;
+    pl.PW = (a.OW - 1) / 2 + 1;
+    const int tiles_w = (pl.PW + 14) / 15, tiles_h = (pl.PH + 1) / 2;
+    const long long cols = (long long)a.N * tiles_w;
+    // as many runs as fit the slots (a run that starts below the top adds one carry row)
+    const long long runs_per_col = cols >= grid_cap ? 1 : grid_cap / cols;
+    long long len = (tiles_h + runs_per_col - 1) / runs_per_col;
+    if (len < 2) len = 2;
+    if (len > tiles_h) len = tiles_h;
+    pl.seg_len = (int)len;
+    pl.segs = (int)((tiles_h + len - 1) / len);
+    const long long grid = cols * pl.segs;
+    if (grid > 0x7fffffffll || (long long)a.N * a.H * a.W * CIN >= (1ll << 30)) return hipErrorInvalidValue;
+    return launch_kernel(halo3x3_kernel<T, CIN, 4, FN, 1, 4, true>, dim3((unsigned)grid), dim3(256), 0, st, a,
+                         tiles_w, tiles_h, 0, pl);
 }
 
 // Tile heights per (Cin, output blocks per wave, waves): 64-channel layers split k
@@ -396,6 +582,25 @@ static hipError_t launch_halo_d(const ConvArgs &a, const HaloPlan &p, hipStream_
     case 16: return launch_halo_c<T, 16>(a, p, st);
     case 32: return launch_halo_c<T, 32>(a, p, st);
     case 64: return launch_halo_c<T, 64>(a, p, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename T>
+static hipError_t launch_halo_pool_d(const ConvArgs &a, void *y, int grid_cap, hipStream_t st) {
+    const bool fn1 = a.Cout <= 32;
+    switch (a.Cin) {
+    case 16: return fn1 ? launch_halo_pool_t<T, 16, 1>(a, y, grid_cap, st) : launch_halo_pool_t<T, 16, 2>(a, y, grid_cap, st);
+    case 32: return fn1 ? launch_halo_pool_t<T, 32, 1>(a, y, grid_cap, st) : launch_halo_pool_t<T, 32, 2>(a, y, grid_cap, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_halo3x3_maxpool(const ConvArgs &a, void *y, int dtype, int grid_cap, hipStream_t st) {
+    if (a.res) return hipErrorInvalidValue;
+    switch (dtype) {
+    case CONV2D_DTYPE_BF16: return launch_halo_pool_d<bf16>(a, y, grid_cap, st);
+    case CONV2D_DTYPE_F16: return launch_halo_pool_d<f16>(a, y, grid_cap, st);
     default: return hipErrorInvalidValue;
     }
 }

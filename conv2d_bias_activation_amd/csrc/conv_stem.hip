@@ -23,6 +23,38 @@
 
 namespace c2d {
 
+// B operands of one 32-pixel block from three staged input rows (row0, row0 + rstr,
+// row0 + 2*rstr), the patch row starting at byte base + sh/8 of each. Lanes 0-31 take
+// values 0..7 of rows 0 and 2; lanes 32-63 values 0..7 of row 1 and values 8 of rows
+// 0-2. Each lane reads only the dwords it uses (five for its first operand; five of row
+// 2, or the one dword holding value 8 of each row, for its second).
+template <typename V>
+__device__ __forceinline__ void stem_operands(const char *row0, int rstr, int base, int sh, int hi, V (&xb)[2]) {
+    const uint32_t *s0 = reinterpret_cast<const uint32_t *>(row0 + hi * rstr + base);
+    uint32_t d[5], e[5];
+#pragma unroll
+    for (int i = 0; i < 5; ++i) d[i] = s0[i];
+    // second operand: lanes 0-31 dwords 0..4 of row 2; lanes 32-63 dword 4 of rows 0, 1, 2
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+        const int off = hi ? (i < 3 ? i : 2) * rstr + 16 : 2 * rstr + 4 * i;
+        e[i] = *reinterpret_cast<const uint32_t *>(row0 + base + off);
+    }
+    uint32_t b0[4], b1[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        b0[i] = __builtin_amdgcn_alignbit(d[i + 1], d[i], sh);
+        b1[i] = __builtin_amdgcn_alignbit(e[i + 1], e[i], sh);
+    }
+    const uint32_t v8_0 = (e[0] >> sh) & 0xffffu, v8_1 = (e[1] >> sh) & 0xffffu, v8_2 = (e[2] >> sh) & 0xffffu;
+    b1[0] = hi ? (v8_0 | (v8_1 << 16)) : b1[0];
+    b1[1] = hi ? v8_2 : b1[1];
+    b1[2] = hi ? 0u : b1[2];
+    b1[3] = hi ? 0u : b1[3];
+    __builtin_memcpy(&xb[0], b0, 16);
+    __builtin_memcpy(&xb[1], b1, 16);
+}
+
 // FN 32-channel output blocks (Cout <= 32*FN); RB output rows per workgroup; S stride.
 template <typename T, int FN, int RB, int S>
 __global__ __launch_bounds__(256) void stem3_kernel(ConvArgs a, int rstr) {
@@ -107,32 +139,8 @@ __global__ __launch_bounds__(256) void stem3_kernel(ConvArgs a, int rstr) {
         // past the row end read the last pixel's patch (their outputs are not stored).
         const int byte = 16 + 6 * ((ox < OW ? ox : OW - 1) * S - 1);
         const int base = byte & ~3, sh = (byte & 3) * 8;
-        uint32_t pr[3][4], p8[3];
-#pragma unroll
-        for (int ky = 0; ky < 3; ++ky) {
-            const uint32_t *src = reinterpret_cast<const uint32_t *>(srow + (rr * S + ky) * rstr + base);
-            uint32_t d[5];
-#pragma unroll
-            for (int i = 0; i < 5; ++i) d[i] = src[i];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) pr[ky][i] = __builtin_amdgcn_alignbit(d[i + 1], d[i], sh);
-            p8[ky] = (d[4] >> sh) & 0xffffu;
-        }
         vec xb[2];
-        {
-            uint32_t b0[4], b1[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                b0[i] = hi ? pr[1][i] : pr[0][i];
-                b1[i] = hi ? 0u : pr[2][i];
-            }
-            if (hi) {
-                b1[0] = p8[0] | (p8[1] << 16);
-                b1[1] = p8[2];
-            }
-            __builtin_memcpy(&xb[0], b0, 16);
-            __builtin_memcpy(&xb[1], b1, 16);
-        }
+        stem_operands(srow + rr * S * rstr, rstr, base, sh, hi, xb);
         f32x16 acc[FN];
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
@@ -317,32 +325,8 @@ __global__ __launch_bounds__(256) void stem3_pool_kernel(ConvArgs a, int PH, int
         const int oy = 2 * py - 1 + dr;
         const bool row_ok = oy >= 0 && oy < OH;
         const int r0 = (dr + (row_ok ? 0 : (oy < 0 ? 1 : -1))) * S;  // a clamped row when out of range
-        uint32_t pr[3][4], p8[3];
-#pragma unroll
-        for (int ky = 0; ky < 3; ++ky) {
-            const uint32_t *src = reinterpret_cast<const uint32_t *>(srow + (r0 + ky) * rstr + base);
-            uint32_t d[5];
-#pragma unroll
-            for (int i = 0; i < 5; ++i) d[i] = src[i];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) pr[ky][i] = __builtin_amdgcn_alignbit(d[i + 1], d[i], sh);
-            p8[ky] = (d[4] >> sh) & 0xffffu;
-        }
         vec xb[2];
-        {
-            uint32_t b0[4], b1[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                b0[i] = hi ? pr[1][i] : pr[0][i];
-                b1[i] = hi ? 0u : pr[2][i];
-            }
-            if (hi) {
-                b1[0] = p8[0] | (p8[1] << 16);
-                b1[1] = p8[2];
-            }
-            __builtin_memcpy(&xb[0], b0, 16);
-            __builtin_memcpy(&xb[1], b1, 16);
-        }
+        stem_operands(srow + r0 * rstr, rstr, base, sh, hi, xb);
         f32x16 acc[FN];
 #pragma unroll
         for (int j = 0; j < FN; ++j) {

@@ -76,6 +76,11 @@ struct HaloPlan {
 // for p.fn = 1, p.th = WM for p.fn = 2.
 hipError_t launch_halo3x3(const ConvArgs &a, int dtype, const HaloPlan &p, hipStream_t st);
 
+// The same convolution for Cin 16 or 32 followed by the 3x3 stride-2 pad-1 max pool in
+// one kernel: only the pooled map is written, to y ([N, PH, PW, Cout], PH = (H-1)/2 + 1,
+// 16-byte aligned); no residual. About grid_cap workgroups of 4 waves (two per CU).
+hipError_t launch_halo3x3_maxpool(const ConvArgs &a, void *y, int dtype, int grid_cap, hipStream_t st);
+
 // 3x3 convolution of a 3-channel channel-last 16-bit image on the matrix cores:
 // stride 1 or 2, pad 1, Cout <= 64 with Cout % 8 == 0, W % 8 == 0 and W <= 3000, x
 // 16-byte aligned, y and the residual 16-byte aligned (a.vec_out), tensors under 2 GiB.

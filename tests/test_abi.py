@@ -95,6 +95,8 @@ def test_conv_pool_plan_and_argument_checks():
     before launching anything."""
     bf16, f32 = c2d.DTYPE_BF16, c2d.DTYPE_F32
     assert c2d.plan_maxpool(1, 640, 640, 3, 32, 3, 3, 2, 1, 2, 0, bf16) == "stem3x3_mfma bf16 fused with maxpool3x3s2"
+    assert c2d.plan_maxpool(4, 320, 320, 32, 64, 3, 3, 1, 1, 1, 0, bf16).endswith("fused with maxpool3x3s2")
+    assert c2d.plan_maxpool(4, 160, 160, 64, 64, 3, 3, 1, 1, 1, 0, bf16).endswith("then maxpool3x3s2")
     assert c2d.plan_maxpool(1, 640, 640, 3, 32, 3, 3, 2, 1, 2, 0, f32).startswith("direct_nhwc")
     assert c2d.plan_maxpool(1, 640, 640, 3, 32, 3, 3, 2, 1, 2, 0, f32).endswith("then maxpool3x3s2")
     # channel-first 16-bit layers keep the scratch for the conv output: the general kernel

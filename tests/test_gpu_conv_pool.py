@@ -50,9 +50,9 @@ def _check(x, spec, layout, dtype, what, want_fused, bitexact_vs_two_calls=True)
     torch.cuda.synchronize()
     gate(to64(y), _oracle(x, spec, layout), dtype, what=what)
     if bitexact_vs_two_calls:
-        # same conv kernel arithmetic; rounding is monotone, so pooling before or after
-        # the rounding gives the same bits
-        assert c2d.plan(*args) in plan, (c2d.plan(*args), plan)
+        # same conv kernel family (the per-pixel sums do not depend on the tiling);
+        # rounding is monotone, so pooling before or after the rounding gives the same bits
+        assert c2d.plan(*args).split()[0] == plan.split()[0], (c2d.plan(*args), plan)
         y2 = _two_calls(x, spec, layout)
         torch.cuda.synchronize()
         assert bits_equal(y, y2), what
@@ -93,13 +93,39 @@ def test_fused_stem_maxpool_full_image(dtype):
     _check(wk.x, spec, "nhwc", dtype, f"stem 640x640 {dtype}", want_fused=True)
 
 
+# Narrow 3x3 stride-1 layers (Cin 16 or 32) on the halo-tile kernel with the pool in its
+# epilogue: (n, h, w, cin, cout, act, dtype). Runs of tiles down the image with a carry
+# row between tiles, ragged pooled widths and heights, partial channel blocks, images
+# of one pixel, and the ResNet-D stem's third conv at full size.
+HALO_FUSED = [
+    (1, 9, 11, 16, 16, "relu", "bf16"),
+    (2, 37, 45, 32, 64, "prelu", "f16"),
+    (1, 1, 1, 32, 32, "relu", "bf16"),
+    (2, 33, 65, 16, 40, "silu", "bf16"),
+    (3, 8, 32, 32, 24, "none", "bf16"),
+    (1, 130, 66, 32, 64, "relu", "bf16"),
+    (2, 64, 100, 16, 64, "silu", "f16"),
+    (1, 320, 64, 32, 64, "relu", "bf16"),
+    (2, 4, 4, 32, 8, "prelu", "bf16"),
+    (4, 160, 160, 32, 64, "relu", "bf16"),
+    (4, 320, 320, 32, 64, "relu", "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", HALO_FUSED, ids=lambda c: "-".join(map(str, c)))
+def test_fused_halo_maxpool(case):
+    n, h, w, cin, cout, act, dtype = case
+    x, spec, _ = wl.random_conv_case(zlib.crc32(repr(case).encode()), n=n, h=h, w=w, cin=cin, cout=cout, k=3,
+                                     stride=1, pad=1, act=act, layout="nhwc", dtype=dtype)
+    _check(x, spec, "nhwc", dtype, str(case), want_fused=True)
+
+
 # Shapes outside the fused kernel: the conv into the library scratch, then the pool.
 # (n, h, w, cin, cout, k, stride, pad, act, layout, dtype, same kernels as two calls)
 UNFUSED = [
     (1, 23, 19, 3, 32, 3, 2, 1, "silu", "nhwc", "f32", True),     # fp32 stem: direct kernel
     (1, 20, 22, 3, 32, 3, 2, 1, "relu", "nhwc", "bf16", True),    # W % 8 != 0
     (2, 18, 16, 3, 72, 3, 2, 1, "relu", "nhwc", "bf16", True),    # Cout > 64
-    (2, 37, 45, 32, 64, 3, 1, 1, "relu", "nhwc", "bf16", True),   # halo kernel
     (1, 30, 26, 64, 64, 3, 1, 1, "prelu", "nhwc", "f16", True),   # halo kernel, Cin 64
     (2, 17, 23, 40, 72, 3, 2, 1, "relu", "nchw", "f16", False),   # channel-first: general kernel
     (1, 16, 18, 3, 16, 3, 2, 1, "silu", "nchw", "f32", True),
