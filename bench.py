@@ -44,8 +44,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--mode", choices=["graph", "eager"], default="graph",
-                   help="replay one captured HIP graph per step, or launch eagerly")
+    p.add_argument("--mode", choices=["stack", "graph", "eager"], default="stack",
+                   help="replay the library's stack graph (conv2d_stack_graph_*) per step, a torch-captured "
+                        "HIP graph of the same calls, or launch eagerly")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--layer-reps", type=int, default=20)
     p.add_argument("--layers-out", default=None, help="write per-layer timings (JSON) here")
@@ -131,13 +132,16 @@ class Net:
                         2 if adev is not None else 1)
                     plan = c2d.plan_maxpool(n, h, w, c, spec.cout, spec.k, spec.k, spec.stride, spec.pad,
                                             act, lay, dt)
+                    op = c2d.Op(c2d.OP_CONV_MAXPOOL, *[a.value if isinstance(a, ctypes.c_void_p) else a
+                                                       for a in args[:4] + [None] + args[4:5] + args[5:15]])
                     self.layers.append(dict(name=spec.name + "+" + nxt.name, fn=self.lib.conv2d_fused_maxpool3x3s2,
-                                            args=args, flops=flops, bytes=nbytes, plan=plan, keep=keep))
+                                            args=args, flops=flops, bytes=nbytes, plan=plan, keep=keep, op=op))
                     self.t[nxt.out] = out
                     skip.add(i + 1)
                     continue
+                op = c2d.Op(c2d.OP_CONV, *[a.value if isinstance(a, ctypes.c_void_p) else a for a in args[:16]])
                 self.layers.append(dict(name=spec.name, fn=self.lib.conv2d_fused, args=args,
-                                        flops=flops, bytes=nbytes, plan=plan, keep=keep))
+                                        flops=flops, bytes=nbytes, plan=plan, keep=keep, op=op))
             else:
                 if spec.kind == "max":
                     oh, ow, fn = (h - 1) // 2 + 1, (w - 1) // 2 + 1, self.lib.maxpool3x3s2
@@ -149,10 +153,13 @@ class Net:
                                   device=dev)
                 args = [ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(out.data_ptr()), n, h, w,
                         c, lay, dt]
+                op = c2d.Op(c2d.OP_MAXPOOL if spec.kind == "max" else c2d.OP_AVGPOOL, src.data_ptr(), None, None,
+                            None, None, out.data_ptr(), n, h, w, c, c, 0, 0, 0, 0, 0)
                 self.layers.append(dict(name=spec.name, fn=fn, args=args, flops=0,
-                                        bytes=esz * (src.numel() + out.numel()), plan=plan, keep=()))
+                                        bytes=esz * (src.numel() + out.numel()), plan=plan, keep=(), op=op))
             self.t[spec.out] = out
         self.flops = sum(L["flops"] for L in self.layers)
+        self.layout, self.dtype = lay, dt
         self.out_name = work.layers[-1].out
 
     def run_layer(self, L, stream_handle):
@@ -174,7 +181,14 @@ def prefill(torch, ms=20.0):
 def time_steps(torch, net, steps, warmup, mode):
     stream = torch.cuda.current_stream()
     graph = None
-    if mode == "graph":
+    if mode == "stack":
+        # the library's own stack graph: validated once, captured once, replayed per step
+        net.step(stream)
+        torch.cuda.synchronize()
+        graph = net.c2d.StackGraph([L["op"] for L in net.layers], layout=["nhwc", "nchw"][net.layout],
+                                   dtype=net.dtype)
+        run = lambda: graph.launch(stream)
+    elif mode == "graph":
         side = torch.cuda.Stream()
         side.wait_stream(stream)
         with torch.cuda.stream(side):
@@ -186,7 +200,10 @@ def time_steps(torch, net, steps, warmup, mode):
         with torch.cuda.graph(graph):
             net.step(torch.cuda.current_stream())
         torch.cuda.synchronize()
-    run = (lambda: graph.replay()) if graph is not None else (lambda: net.step(stream))
+    if mode == "graph":
+        run = lambda: graph.replay()
+    elif mode == "eager":
+        run = lambda: net.step(stream)
     for _ in range(warmup):
         run()
     torch.cuda.synchronize()

@@ -15,7 +15,8 @@ import os
 import torch
 
 __all__ = ["conv2d_fused", "conv2d_fused_maxpool3x3s2", "maxpool3x3s2", "avgpool2x2", "out_dim",
-           "check_args", "plan", "plan_maxpool",
+           "check_args", "plan", "plan_maxpool", "Op", "conv_op", "pool_op", "copy_op", "stack_check",
+           "stack_plan", "stack_run", "StackGraph",
            "last_error", "library_path", "Conv2dError", "ACT_NONE", "ACT_RELU", "ACT_SILU",
            "ACT_PRELU", "RES_BEFORE_ACT", "LAYOUT_NHWC", "LAYOUT_NCHW", "DTYPE_F32",
            "DTYPE_BF16", "DTYPE_F16"]
@@ -36,6 +37,19 @@ _LIB_PATH = os.path.join(_HERE, "libconv2d_fused.so")
 
 # Every exported symbol of the C ABI, with (restype, argtypes).
 _vp, _fp, _i, _cp = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_char_p
+OP_CONV, OP_CONV_MAXPOOL, OP_MAXPOOL, OP_AVGPOOL, OP_COPY = 0, 1, 2, 3, 4
+
+
+class Op(ctypes.Structure):
+    """One op of a stack (struct conv2d_op of include/conv2d_fused.h)."""
+    _fields_ = [("kind", ctypes.c_int), ("x", ctypes.c_void_p), ("w", ctypes.c_void_p),
+                ("bias", ctypes.c_void_p), ("alpha", ctypes.c_void_p), ("residual", ctypes.c_void_p),
+                ("y", ctypes.c_void_p)] + [(f, ctypes.c_int) for f in
+                                           ("N", "H", "W", "Cin", "Cout", "kh", "kw", "stride", "pad", "act")]
+
+
+_op_p = ctypes.POINTER(Op)
+
 SIGNATURES = {
     "conv2d_fused": (_i, [_vp, _vp, _fp, _fp, _vp, _vp] + [_i] * 12 + [_vp]),
     "maxpool3x3s2": (_i, [_vp, _vp] + [_i] * 6 + [_vp]),
@@ -45,6 +59,12 @@ SIGNATURES = {
     "conv2d_plan": (_i, [_i] * 12 + [_cp, _i]),
     "conv2d_fused_maxpool3x3s2": (_i, [_vp, _vp, _fp, _fp, _vp] + [_i] * 12 + [_vp]),
     "conv2d_fused_maxpool_plan": (_i, [_i] * 12 + [_cp, _i]),
+    "conv2d_stack_check": (_i, [_op_p, _i, _i, _i, ctypes.POINTER(ctypes.c_int)]),
+    "conv2d_stack_plan": (_i, [_op_p, _i, _i, _i, _i, _cp, _i]),
+    "conv2d_stack_run": (_i, [_op_p, _i, _i, _i, _vp]),
+    "conv2d_stack_graph_create": (_i, [_op_p, _i, _i, _i, ctypes.POINTER(ctypes.c_void_p)]),
+    "conv2d_stack_graph_launch": (_i, [_vp, _vp]),
+    "conv2d_stack_graph_destroy": (_i, [_vp]),
     "conv2d_last_error": (_cp, []),
     "conv2d_abi_version": (_i, []),
 }
@@ -259,3 +279,89 @@ def plan_maxpool(N, H, W, Cin, Cout, kh, kw, stride, pad, act, layout, dtype) ->
                                           buf, 256)
     _check(n if n < 0 else OK)
     return buf.value.decode()
+
+
+def _tensor_ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def conv_op(x, w, y, bias=None, alpha=None, residual=None, *, stride=1, pad=0, act="none",
+            res_before_act=False, layout="nhwc", pool=False):
+    """An Op for conv2d_fused (or, with pool=True, conv2d_fused_maxpool3x3s2) on these
+    tensors. The tensors must stay alive while the stack (or its graph) is in use."""
+    N, H, W, Cin, Cout, kh, kw = _dims(x, w, layout)
+    return Op(OP_CONV_MAXPOOL if pool else OP_CONV, _tensor_ptr(x), _tensor_ptr(w), _tensor_ptr(bias),
+              _tensor_ptr(alpha), _tensor_ptr(residual), _tensor_ptr(y), N, H, W, Cin, Cout, kh, kw, stride, pad,
+              _act_code(act, res_before_act))
+
+
+def _nhwc_dims(x, layout):
+    if layout == "nhwc":
+        return tuple(x.shape)
+    N, C, H, W = x.shape
+    return N, H, W, C
+
+
+def pool_op(kind, x, y, *, layout="nhwc"):
+    """An Op for maxpool3x3s2 (kind "max") or avgpool2x2 (kind "avg")."""
+    N, H, W, C = _nhwc_dims(x, layout)
+    return Op(OP_MAXPOOL if kind == "max" else OP_AVGPOOL, x.data_ptr(), None, None, None, None, y.data_ptr(),
+              N, H, W, C, C, 0, 0, 0, 0, 0)
+
+
+def copy_op(x, y):
+    """An Op that copies x into y (same element count; a snapshot inside a stack)."""
+    if x.numel() != y.numel() or x.dtype != y.dtype:
+        raise ValueError("copy needs tensors of one dtype and size")
+    return Op(OP_COPY, x.data_ptr(), None, None, None, None, y.data_ptr(), 1, 1, 1, x.numel(), 0, 0, 0, 0, 0, 0)
+
+
+def _op_array(ops):
+    arr = (Op * len(ops))(*ops)
+    return arr, len(ops)
+
+
+def stack_check(ops, layout="nhwc", dtype=DTYPE_BF16):
+    """Host-only validation of a stack: (status, index of the first bad op or -1)."""
+    arr, n = _op_array(ops)
+    bad = ctypes.c_int(-1)
+    rc = _load().conv2d_stack_check(arr, n, _LAYOUTS[layout], dtype, ctypes.byref(bad))
+    return rc, bad.value
+
+
+def stack_plan(ops, index, layout="nhwc", dtype=DTYPE_BF16) -> str:
+    arr, n = _op_array(ops)
+    buf = ctypes.create_string_buffer(256)
+    rc = _load().conv2d_stack_plan(arr, n, _LAYOUTS[layout], dtype, index, buf, 256)
+    _check(rc if rc < 0 else OK)
+    return buf.value.decode()
+
+
+def stack_run(ops, layout="nhwc", dtype=DTYPE_BF16, stream=None):
+    """Validate the whole stack, then enqueue its ops in order on the stream."""
+    arr, n = _op_array(ops)
+    _check(_load().conv2d_stack_run(arr, n, _LAYOUTS[layout], dtype, _stream_handle(stream)))
+
+
+class StackGraph:
+    """A stack recorded once into a HIP graph; launch() replays it on a stream."""
+
+    def __init__(self, ops, layout="nhwc", dtype=DTYPE_BF16):
+        arr, n = _op_array(ops)
+        h = ctypes.c_void_p()
+        _check(_load().conv2d_stack_graph_create(arr, n, _LAYOUTS[layout], dtype, ctypes.byref(h)))
+        self._h = h
+
+    def launch(self, stream=None):
+        _check(_load().conv2d_stack_graph_launch(self._h, _stream_handle(stream)))
+
+    def close(self):
+        if self._h:
+            _check(_load().conv2d_stack_graph_destroy(self._h))
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

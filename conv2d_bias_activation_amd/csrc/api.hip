@@ -6,7 +6,9 @@
 
 #include <atomic>
 #include <mutex>
+#include <new>
 #include <string>
+#include <vector>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -482,11 +484,208 @@ int check_conv_pool(const void *x, const void *w, const float *alpha, const void
     return CONV2D_OK;
 }
 
+// One validated op of a call or a stack: everything its launch needs, decided on
+// the host before anything is launched.
+struct OpPlan {
+    int kind;  // CONV2D_OP_*
+    int layout, dtype;
+    ConvArgs a;     // convs (a.y is the conv output, or the pooled map for the fused kernels)
+    Plan plan;      // CONV2D_OP_CONV
+    PoolFusion pf;  // CONV2D_OP_CONV_MAXPOOL
+    const void *x;  // pools, copy
+    void *y;
+    int N, H, W, C;
+    bool vec;      // pools: the 16-byte channel-last kernels
+    size_t bytes;  // copy
+};
+
+bool needs_scratch(const OpPlan &o) {
+    if (o.kind == CONV2D_OP_CONV)
+        return o.plan.family == FAM_NCHW_VIA_NHWC || (o.plan.family == FAM_NHWC && o.plan.nh.splits > 1);
+    return o.kind == CONV2D_OP_CONV_MAXPOOL && o.pf.kind == POOL_TWO_KERNELS;
+}
+
+int check_op(const conv2d_op &op, int layout, int dtype, OpPlan *o) {
+    *o = OpPlan{};
+    o->kind = op.kind;
+    o->layout = layout;
+    o->dtype = dtype;
+    switch (op.kind) {
+    case CONV2D_OP_CONV: {
+        int rc = check_conv(op.x, op.w, op.alpha, op.residual, op.y, op.N, op.H, op.W, op.Cin, op.Cout, op.kh,
+                            op.kw, op.stride, op.pad, op.act, layout, dtype, &o->a);
+        if (rc) return rc;
+        o->a.bias = op.bias;
+        if ((op.act & 0xff) != CONV2D_ACT_PRELU) o->a.alpha = nullptr;
+        o->plan = make_plan(o->a, layout, dtype);
+        return CONV2D_OK;
+    }
+    case CONV2D_OP_CONV_MAXPOOL: {
+        if (op.residual) return set_error(CONV2D_EINVAL, "conv2d_fused_maxpool3x3s2 takes no residual");
+        int rc = check_conv_pool(op.x, op.w, op.alpha, op.y, op.N, op.H, op.W, op.Cin, op.Cout, op.kh, op.kw,
+                                 op.stride, op.pad, op.act, layout, dtype, &o->a, &o->pf);
+        if (rc) return rc;
+        o->a.bias = op.bias;
+        if ((op.act & 0xff) != CONV2D_ACT_PRELU) o->a.alpha = nullptr;
+        return CONV2D_OK;
+    }
+    case CONV2D_OP_MAXPOOL:
+    case CONV2D_OP_AVGPOOL: {
+        const bool mx = op.kind == CONV2D_OP_MAXPOOL;
+        const int OH = mx ? out_dim(op.H, 3, 2, 1) : op.H / 2, OW = mx ? out_dim(op.W, 3, 2, 1) : op.W / 2;
+        int rc = check_pool(op.x, op.y, op.N, op.H, op.W, op.Cin, layout, dtype, OH, OW,
+                            mx ? "maxpool3x3s2" : "avgpool2x2");
+        if (rc) return rc;
+        const int ve = 16 / dtype_bytes(dtype);
+        o->x = op.x;
+        o->y = op.y;
+        o->N = op.N;
+        o->H = op.H;
+        o->W = op.W;
+        o->C = op.Cin;
+        o->vec = layout == CONV2D_LAYOUT_NHWC && (op.Cin % ve) == 0 && aligned16(op.x) && aligned16(op.y);
+        return CONV2D_OK;
+    }
+    case CONV2D_OP_COPY: {
+        if (!op.x || !op.y) return set_error(CONV2D_EINVAL, "copy: x and y must not be null");
+        if (op.N <= 0 || op.H <= 0 || op.W <= 0 || op.Cin <= 0)
+            return set_error(CONV2D_EINVAL, "copy: sizes must be positive");
+        if (!dtype_bytes(dtype)) return set_error(CONV2D_EINVAL, "copy: unknown dtype %d", dtype);
+        const long long e = (long long)op.N * op.H * op.W * op.Cin;
+        if (e > kMaxElems) return set_error(CONV2D_EUNSUPPORTED, "copy: tensor too large");
+        o->bytes = (size_t)e * dtype_bytes(dtype);
+        if (overlap(op.y, (long long)o->bytes, op.x, (long long)o->bytes))
+            return set_error(CONV2D_EINVAL, "copy: y overlaps x");
+        o->x = op.x;
+        o->y = op.y;
+        return CONV2D_OK;
+    }
+    default:
+        return set_error(CONV2D_EINVAL, "unknown op kind %d", op.kind);
+    }
+}
+
+int check_stack(const conv2d_op *ops, int n, int layout, int dtype, std::vector<OpPlan> *plans, int *bad) {
+    if (n < 0 || (n > 0 && !ops)) return set_error(CONV2D_EINVAL, "ops must hold n >= 0 entries");
+    plans->resize((size_t)n);
+    for (int i = 0; i < n; ++i) {
+        int rc = check_op(ops[i], layout, dtype, &(*plans)[(size_t)i]);
+        if (rc) {
+            if (bad) *bad = i;
+            return set_error(rc, "op %d: %s", i, g_err.c_str());
+        }
+    }
+    return CONV2D_OK;
+}
+
+// Host-side state the launches need (the scratch buffer, the CU count), fetched before
+// any launch so that a captured stack makes no allocation inside the capture.
+int prepare_stack(const std::vector<OpPlan> &plans) {
+    bool scratch = false;
+    for (const OpPlan &o : plans) scratch = scratch || needs_scratch(o);
+    if (scratch) {
+        float *p = nullptr;
+        int rc = get_scratch(&p);
+        if (rc) return rc;
+    }
+    int cus = 0;
+    return plans.empty() ? CONV2D_OK : device_cus(&cus);
+}
+
+int launch_op(const OpPlan &o, hipStream_t st) {
+    hipError_t e = hipSuccess;
+    const bool nchw = o.layout == CONV2D_LAYOUT_NCHW;
+    switch (o.kind) {
+    case CONV2D_OP_CONV:
+        return launch_conv(o.a, o.plan, o.layout, o.dtype, st);
+    case CONV2D_OP_CONV_MAXPOOL: {
+        const ConvArgs &a = o.a;
+        if (o.pf.kind == POOL_FUSED_STEM) {
+            e = launch_stem3_maxpool(a, a.y, o.dtype, st);
+        } else if (o.pf.kind == POOL_FUSED_HALO) {
+            int cus = 0;
+            int rc = device_cus(&cus);
+            if (rc) return rc;
+            e = launch_halo3x3_maxpool(a, a.y, o.dtype, 2 * cus, st);
+        } else {
+            // the conv into the scratch buffer, then the pool kernel
+            float *scratch = nullptr;
+            int rc = get_scratch(&scratch);
+            if (rc) return rc;
+            ConvArgs b = a;
+            b.y = scratch;
+            b.vec_out = true;
+            rc = launch_conv(b, o.pf.conv_plan, o.layout, o.dtype, st);
+            if (rc) return rc;
+            const int ve = 16 / dtype_bytes(o.dtype);
+            const bool vec = !nchw && (a.Cout % ve) == 0 && aligned16(a.y);
+            e = launch_maxpool(scratch, a.y, a.N, a.OH, a.OW, a.Cout, nchw, o.dtype, vec, st);
+        }
+        if (e != hipSuccess) return hip_fail(e, "conv2d_fused_maxpool3x3s2 launch");
+        return CONV2D_OK;
+    }
+    case CONV2D_OP_MAXPOOL:
+        e = launch_maxpool(o.x, o.y, o.N, o.H, o.W, o.C, nchw, o.dtype, o.vec, st);
+        return e == hipSuccess ? CONV2D_OK : hip_fail(e, "maxpool3x3s2 launch");
+    case CONV2D_OP_AVGPOOL:
+        e = launch_avgpool(o.x, o.y, o.N, o.H, o.W, o.C, nchw, o.dtype, o.vec, st);
+        return e == hipSuccess ? CONV2D_OK : hip_fail(e, "avgpool2x2 launch");
+    case CONV2D_OP_COPY:
+        e = launch_copy(o.x, o.y, o.bytes, st);
+        return e == hipSuccess ? CONV2D_OK : hip_fail(e, "copy launch");
+    default:
+        return set_error(CONV2D_EINVAL, "unknown op kind %d", o.kind);
+    }
+}
+
+int run_one(const conv2d_op &op, int layout, int dtype, void *stream) {
+    OpPlan o{};
+    int rc = check_op(op, layout, dtype, &o);
+    if (rc) return rc;
+    rc = launch_op(o, static_cast<hipStream_t>(stream));
+    return rc ? rc : set_ok();
+}
+
+int describe_op(const OpPlan &o, char *buf, int cap) {
+    char tmp[200];
+    switch (o.kind) {
+    case CONV2D_OP_CONV:
+        return describe(o.plan, o.layout, o.dtype, buf, cap);
+    case CONV2D_OP_CONV_MAXPOOL:
+        if (o.pf.kind == POOL_FUSED_STEM) {
+            snprintf(tmp, sizeof tmp, "stem3x3_mfma %s fused with maxpool3x3s2", dtype_name(o.dtype));
+        } else if (o.pf.kind == POOL_FUSED_HALO) {
+            snprintf(tmp, sizeof tmp, "halo3x3_nhwc %s th4 co%d w4 fused with maxpool3x3s2", dtype_name(o.dtype),
+                     o.a.Cout <= 32 ? 32 : 64);
+        } else {
+            char inner[160];
+            describe(o.pf.conv_plan, o.layout, o.dtype, inner, sizeof inner);
+            snprintf(tmp, sizeof tmp, "%s then maxpool3x3s2", inner);
+        }
+        break;
+    case CONV2D_OP_MAXPOOL:
+        snprintf(tmp, sizeof tmp, "maxpool3x3s2");
+        break;
+    case CONV2D_OP_AVGPOOL:
+        snprintf(tmp, sizeof tmp, "avgpool2x2");
+        break;
+    default:
+        snprintf(tmp, sizeof tmp, "copy");
+        break;
+    }
+    int n = (int)strlen(tmp);
+    if (buf && cap > 0) {
+        strncpy(buf, tmp, (size_t)cap - 1);
+        buf[cap - 1] = 0;
+    }
+    return n;
+}
+
 }  // namespace
 
 extern "C" {
 
-int conv2d_abi_version(void) { return 1; }
+int conv2d_abi_version(void) { return 2; }
 
 const char *conv2d_last_error(void) { return g_err.c_str(); }
 
@@ -521,53 +720,16 @@ int conv2d_plan(int N, int H, int W, int Cin, int Cout, int kh, int kw, int stri
 int conv2d_fused(const void *x, const void *w, const float *bias, const float *alpha,
                  const void *residual, void *y, int N, int H, int W, int Cin, int Cout, int kh,
                  int kw, int stride, int pad, int act, int layout, int dtype, void *stream) {
-    ConvArgs a{};
-    int rc = check_conv(x, w, alpha, residual, y, N, H, W, Cin, Cout, kh, kw, stride, pad, act,
-                        layout, dtype, &a);
-    if (rc) return rc;
-    a.bias = bias;
-    if ((act & 0xff) != CONV2D_ACT_PRELU) a.alpha = nullptr;
-    rc = launch_conv(a, make_plan(a, layout, dtype), layout, dtype, static_cast<hipStream_t>(stream));
-    return rc ? rc : set_ok();
+    const conv2d_op op{CONV2D_OP_CONV, x, w, bias, alpha, residual, y, N, H, W, Cin, Cout, kh, kw, stride, pad, act};
+    return run_one(op, layout, dtype, stream);
 }
 
 int conv2d_fused_maxpool3x3s2(const void *x, const void *w, const float *bias, const float *alpha, void *y,
                               int N, int H, int W, int Cin, int Cout, int kh, int kw, int stride, int pad,
                               int act, int layout, int dtype, void *stream) {
-    ConvArgs a{};
-    PoolFusion f{};
-    int rc = check_conv_pool(x, w, alpha, y, N, H, W, Cin, Cout, kh, kw, stride, pad, act, layout, dtype, &a, &f);
-    if (rc) return rc;
-    a.bias = bias;
-    if ((act & 0xff) != CONV2D_ACT_PRELU) a.alpha = nullptr;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    if (f.kind != POOL_TWO_KERNELS) {
-        hipError_t e;
-        if (f.kind == POOL_FUSED_STEM) {
-            e = launch_stem3_maxpool(a, y, dtype, st);
-        } else {
-            int cus = 0;
-            rc = device_cus(&cus);
-            if (rc) return rc;
-            e = launch_halo3x3_maxpool(a, y, dtype, 2 * cus, st);
-        }
-        if (e != hipSuccess) return hip_fail(e, "conv2d_fused_maxpool3x3s2 launch");
-        return set_ok();
-    }
-    // unfused: the conv into the scratch buffer, then the pool kernel
-    float *scratch = nullptr;
-    rc = get_scratch(&scratch);
-    if (rc) return rc;
-    ConvArgs b = a;
-    b.y = scratch;
-    b.vec_out = true;
-    rc = launch_conv(b, f.conv_plan, layout, dtype, st);
-    if (rc) return rc;
-    const int ve = 16 / dtype_bytes(dtype);
-    const bool vec = layout == CONV2D_LAYOUT_NHWC && (Cout % ve) == 0 && aligned16(y);
-    hipError_t e = launch_maxpool(scratch, y, N, a.OH, a.OW, Cout, layout == CONV2D_LAYOUT_NCHW, dtype, vec, st);
-    if (e != hipSuccess) return hip_fail(e, "conv2d_fused_maxpool3x3s2 pool launch");
-    return set_ok();
+    const conv2d_op op{CONV2D_OP_CONV_MAXPOOL, x, w, bias, alpha, nullptr, y, N, H, W, Cin, Cout, kh, kw,
+                       stride, pad, act};
+    return run_one(op, layout, dtype, stream);
 }
 
 int conv2d_fused_maxpool_plan(int N, int H, int W, int Cin, int Cout, int kh, int kw, int stride, int pad,
@@ -576,52 +738,127 @@ int conv2d_fused_maxpool_plan(int N, int H, int W, int Cin, int Cout, int kh, in
     const void *pw = (const void *)(uintptr_t)0x900000000ull;
     void *py = (void *)(uintptr_t)0x1100000000ull;
     const float *pa = (const float *)(uintptr_t)0x1900000000ull;
-    ConvArgs a{};
-    PoolFusion f{};
-    int rc = check_conv_pool(px, pw, pa, py, N, H, W, Cin, Cout, kh, kw, stride, pad, act, layout, dtype, &a, &f);
+    const conv2d_op op{CONV2D_OP_CONV_MAXPOOL, px, pw, nullptr, pa, nullptr, py, N, H, W, Cin, Cout, kh, kw,
+                       stride, pad, act};
+    OpPlan o{};
+    int rc = check_op(op, layout, dtype, &o);
     if (rc) return rc;
     set_ok();
-    char tmp[200];
-    if (f.kind == POOL_FUSED_STEM) {
-        snprintf(tmp, sizeof tmp, "stem3x3_mfma %s fused with maxpool3x3s2", dtype_name(dtype));
-    } else if (f.kind == POOL_FUSED_HALO) {
-        snprintf(tmp, sizeof tmp, "halo3x3_nhwc %s th4 co%d w4 fused with maxpool3x3s2", dtype_name(dtype),
-                 Cout <= 32 ? 32 : 64);
-    } else {
-        char inner[160];
-        describe(f.conv_plan, layout, dtype, inner, sizeof inner);
-        snprintf(tmp, sizeof tmp, "%s then maxpool3x3s2", inner);
-    }
-    int n = (int)strlen(tmp);
-    if (buf && cap > 0) {
-        strncpy(buf, tmp, (size_t)cap - 1);
-        buf[cap - 1] = 0;
-    }
-    return n;
+    return describe_op(o, buf, cap);
 }
 
 int maxpool3x3s2(const void *x, void *y, int N, int H, int W, int C, int layout, int dtype,
                  void *stream) {
-    int OH = out_dim(H, 3, 2, 1), OW = out_dim(W, 3, 2, 1);
-    int rc = check_pool(x, y, N, H, W, C, layout, dtype, OH, OW, "maxpool3x3s2");
-    if (rc) return rc;
-    int ve = 16 / dtype_bytes(dtype);
-    bool vec = layout == CONV2D_LAYOUT_NHWC && (C % ve) == 0 && aligned16(x) && aligned16(y);
-    hipError_t e = launch_maxpool(x, y, N, H, W, C, layout == CONV2D_LAYOUT_NCHW, dtype, vec,
-                                  static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail(e, "maxpool3x3s2 launch");
-    return set_ok();
+    const conv2d_op op{CONV2D_OP_MAXPOOL, x, nullptr, nullptr, nullptr, nullptr, y, N, H, W, C, C, 3, 3, 2, 1, 0};
+    return run_one(op, layout, dtype, stream);
 }
 
 int avgpool2x2(const void *x, void *y, int N, int H, int W, int C, int layout, int dtype,
                void *stream) {
-    int rc = check_pool(x, y, N, H, W, C, layout, dtype, H / 2, W / 2, "avgpool2x2");
+    const conv2d_op op{CONV2D_OP_AVGPOOL, x, nullptr, nullptr, nullptr, nullptr, y, N, H, W, C, C, 2, 2, 2, 0, 0};
+    return run_one(op, layout, dtype, stream);
+}
+
+int conv2d_stack_check(const conv2d_op *ops, int n, int layout, int dtype, int *bad_index) {
+    if (bad_index) *bad_index = -1;
+    std::vector<OpPlan> plans;
+    int rc = check_stack(ops, n, layout, dtype, &plans, bad_index);
+    return rc ? rc : set_ok();
+}
+
+int conv2d_stack_plan(const conv2d_op *ops, int n, int layout, int dtype, int index, char *buf, int cap) {
+    std::vector<OpPlan> plans;
+    int bad = -1;
+    int rc = check_stack(ops, n, layout, dtype, &plans, &bad);
     if (rc) return rc;
-    int ve = 16 / dtype_bytes(dtype);
-    bool vec = layout == CONV2D_LAYOUT_NHWC && (C % ve) == 0 && aligned16(x) && aligned16(y);
-    hipError_t e = launch_avgpool(x, y, N, H, W, C, layout == CONV2D_LAYOUT_NCHW, dtype, vec,
-                                  static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail(e, "avgpool2x2 launch");
+    if (index < 0 || index >= n) return set_error(CONV2D_EINVAL, "op index %d outside the stack of %d", index, n);
+    set_ok();
+    return describe_op(plans[(size_t)index], buf, cap);
+}
+
+int conv2d_stack_run(const conv2d_op *ops, int n, int layout, int dtype, void *stream) {
+    std::vector<OpPlan> plans;
+    int bad = -1;
+    int rc = check_stack(ops, n, layout, dtype, &plans, &bad);
+    if (rc) return rc;
+    rc = prepare_stack(plans);
+    if (rc) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    for (int i = 0; i < n; ++i) {
+        rc = launch_op(plans[(size_t)i], st);
+        if (rc) return set_error(rc, "op %d: %s", i, g_err.c_str());
+    }
+    return set_ok();
+}
+
+struct conv2d_graph {
+    hipGraph_t graph;
+    hipGraphExec_t exec;
+    int ops;
+};
+
+int conv2d_stack_graph_create(const conv2d_op *ops, int n, int layout, int dtype, conv2d_graph **out) {
+    if (!out) return set_error(CONV2D_EINVAL, "out must not be null");
+    *out = nullptr;
+    std::vector<OpPlan> plans;
+    int bad = -1;
+    int rc = check_stack(ops, n, layout, dtype, &plans, &bad);
+    if (rc) return rc;
+    // everything that may allocate or query the device happens before the capture
+    rc = prepare_stack(plans);
+    if (rc) return rc;
+    hipStream_t cs = nullptr;
+    hipError_t e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
+    if (e != hipSuccess) return hip_fail(e, "capture stream");
+    e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+    if (e != hipSuccess) {
+        (void)hipStreamDestroy(cs);
+        return hip_fail(e, "hipStreamBeginCapture");
+    }
+    int lrc = CONV2D_OK;
+    std::string lerr;
+    for (int i = 0; i < n && lrc == CONV2D_OK; ++i) {
+        lrc = launch_op(plans[(size_t)i], cs);
+        if (lrc) lerr = "op " + std::to_string(i) + ": " + g_err;
+    }
+    hipGraph_t g = nullptr;
+    e = hipStreamEndCapture(cs, &g);
+    (void)hipStreamDestroy(cs);
+    if (lrc) {
+        if (g) (void)hipGraphDestroy(g);
+        return set_error(lrc, "%s", lerr.c_str());
+    }
+    if (e != hipSuccess) return hip_fail(e, "hipStreamEndCapture");
+    hipGraphExec_t x = nullptr;
+    e = hipGraphInstantiate(&x, g, nullptr, nullptr, 0);
+    if (e != hipSuccess) {
+        (void)hipGraphDestroy(g);
+        return hip_fail(e, "hipGraphInstantiate");
+    }
+    conv2d_graph *h = new (std::nothrow) conv2d_graph{g, x, n};
+    if (!h) {
+        (void)hipGraphExecDestroy(x);
+        (void)hipGraphDestroy(g);
+        return set_error(CONV2D_EHIP, "out of host memory");
+    }
+    *out = h;
+    return set_ok();
+}
+
+int conv2d_stack_graph_launch(conv2d_graph *g, void *stream) {
+    if (!g) return set_error(CONV2D_EINVAL, "graph must not be null");
+    hipError_t e = hipGraphLaunch(g->exec, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "hipGraphLaunch");
+    return set_ok();
+}
+
+int conv2d_stack_graph_destroy(conv2d_graph *g) {
+    if (!g) return set_ok();
+    hipError_t e1 = hipGraphExecDestroy(g->exec);
+    hipError_t e2 = hipGraphDestroy(g->graph);
+    delete g;
+    if (e1 != hipSuccess) return hip_fail(e1, "hipGraphExecDestroy");
+    if (e2 != hipSuccess) return hip_fail(e2, "hipGraphDestroy");
     return set_ok();
 }
 

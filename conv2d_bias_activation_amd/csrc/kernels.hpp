@@ -95,6 +95,9 @@ hipError_t launch_stem3_maxpool(const ConvArgs &a, void *y, int dtype, hipStream
 // one thread per output pixel and a block of output channels.
 hipError_t launch_direct(const ConvArgs &a, int dtype, bool nchw, hipStream_t st);
 
+// y = x, `bytes` bytes (a snapshot inside a stream of layers).
+hipError_t launch_copy(const void *x, void *y, size_t bytes, hipStream_t st);
+
 // Pools (layout: CONV2D_LAYOUT_*). vec: C a multiple of the 16-byte vector and
 // both pointers aligned (channel-last only).
 hipError_t launch_maxpool(const void *x, void *y, int N, int H, int W, int C, bool nchw,

@@ -70,3 +70,30 @@ hipError_t launch_to_channel_last(const void *x, void *x_nhwc, int N, int C, int
 }
 
 }  // namespace c2d
+
+namespace c2d {
+
+// Byte copy for in-stream snapshots: 16-byte runs when both pointers and the size
+// allow it, bytes otherwise; a grid-stride loop over at most 8192 blocks.
+__global__ __launch_bounds__(256) void copy16_kernel(const u32x4 *__restrict__ x, u32x4 *__restrict__ y, size_t n) {
+    for (size_t i = blockIdx.x * 256ull + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) y[i] = x[i];
+}
+
+__global__ __launch_bounds__(256) void copy1_kernel(const uint8_t *__restrict__ x, uint8_t *__restrict__ y, size_t n) {
+    for (size_t i = blockIdx.x * 256ull + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) y[i] = x[i];
+}
+
+hipError_t launch_copy(const void *x, void *y, size_t bytes, hipStream_t st) {
+    if (bytes == 0) return hipSuccess;
+    const bool v16 = (((uintptr_t)x | (uintptr_t)y | bytes) & 15) == 0;
+    const size_t n = v16 ? bytes / 16 : bytes;
+    size_t blocks = (n + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    if (v16)
+        return launch_kernel(copy16_kernel, dim3((unsigned)blocks), dim3(256), 0, st, static_cast<const u32x4 *>(x),
+                             static_cast<u32x4 *>(y), n);
+    return launch_kernel(copy1_kernel, dim3((unsigned)blocks), dim3(256), 0, st, static_cast<const uint8_t *>(x),
+                         static_cast<uint8_t *>(y), n);
+}
+
+}  // namespace c2d

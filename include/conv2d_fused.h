@@ -188,11 +188,76 @@ int conv2d_check_args(const void *x, const void *w, const float *bias, const flo
 int conv2d_plan(int N, int H, int W, int Cin, int Cout, int kh, int kw, int stride, int pad,
                 int act, int layout, int dtype, char *buf, int cap);
 
+/*
+ * Stacks of layers: a list of ops run in order on one stream, like one call per op,
+ * but validated as a whole first (a stack that returns an error has launched
+ * nothing) and, optionally, captured once into a HIP graph and replayed. This is how
+ * the pages run a network section: inferencelayer's `Recorder` records a whole
+ * encoder into one submission, and framecast runs the eight convs of an IFNet block
+ * back to back, having first copied the block input aside because the ping-pong
+ * buffers reuse it, so that the last conv can add it as its residual. An op reads its
+ * inputs when its turn comes, so a later op sees what earlier ops wrote; a snapshot
+ * that a later op needs is an explicit CONV2D_OP_COPY.
+ *
+ * One op (fields that a kind does not use are ignored):
+ *   CONV2D_OP_CONV          conv2d_fused(x, w, bias, alpha, residual, y, N, H, W, Cin,
+ *                           Cout, kh, kw, stride, pad, act)
+ *   CONV2D_OP_CONV_MAXPOOL  conv2d_fused_maxpool3x3s2(x, w, bias, alpha, y, ...); residual
+ *                           must be NULL
+ *   CONV2D_OP_MAXPOOL       maxpool3x3s2(x, y, N, H, W, C = Cin)
+ *   CONV2D_OP_AVGPOOL       avgpool2x2(x, y, N, H, W, C = Cin)
+ *   CONV2D_OP_COPY          y = x, N*H*W*Cin elements of dtype (y may not overlap x)
+ * Layout and dtype are shared by the whole stack.
+ */
+#define CONV2D_OP_CONV 0
+#define CONV2D_OP_CONV_MAXPOOL 1
+#define CONV2D_OP_MAXPOOL 2
+#define CONV2D_OP_AVGPOOL 3
+#define CONV2D_OP_COPY 4
+
+typedef struct conv2d_op {
+    int kind;
+    const void *x;
+    const void *w;
+    const float *bias;
+    const float *alpha;
+    const void *residual;
+    void *y;
+    int N, H, W, Cin, Cout, kh, kw, stride, pad, act;
+} conv2d_op;
+
+/* Host-only validation of every op of a stack (ops[0..n-1]), without touching the GPU.
+ * Returns CONV2D_OK or the code of the first invalid op, whose index goes to
+ * *bad_index (-1 when the stack is valid or the list itself is invalid; bad_index may
+ * be NULL). */
+int conv2d_stack_check(const conv2d_op *ops, int n, int layout, int dtype, int *bad_index);
+
+/* Host-only: the kernel variants of op `index` of a stack, as conv2d_plan. */
+int conv2d_stack_plan(const conv2d_op *ops, int n, int layout, int dtype, int index, char *buf, int cap);
+
+/* Validates the whole stack, then enqueues its ops in order on `stream`. Same memory
+ * and scratch rules as the single calls. */
+int conv2d_stack_run(const conv2d_op *ops, int n, int layout, int dtype, void *stream);
+
+/* Validates the stack and records it once into a HIP graph (stream capture on a
+ * private stream; the scratch buffer, if an op needs it, is allocated before the
+ * capture). The graph holds the ops' pointers and sizes as given: every replay runs
+ * the same ops on the same buffers, which must stay allocated until the graph is
+ * destroyed. *out receives an opaque handle (NULL on error). */
+typedef struct conv2d_graph conv2d_graph;
+int conv2d_stack_graph_create(const conv2d_op *ops, int n, int layout, int dtype, conv2d_graph **out);
+
+/* Enqueues one replay of the graph on `stream` (asynchronous, like the other calls). */
+int conv2d_stack_graph_launch(conv2d_graph *g, void *stream);
+
+/* Frees the graph (NULL is allowed). The caller makes sure no replay is still running. */
+int conv2d_stack_graph_destroy(conv2d_graph *g);
+
 /* Message of the last error on the calling thread ("" if none). The pointer stays
  * valid until the thread's next call into the library. */
 const char *conv2d_last_error(void);
 
-/* ABI version of this header: 1. */
+/* ABI version of this header: 2 (1 plus the stack calls and the fused conv + max pool). */
 int conv2d_abi_version(void);
 
 #ifdef __cplusplus

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     for name in names:
         assert hasattr(lib, name), name
     assert names == set(c2d.SIGNATURES)
-    assert c2d._load().conv2d_abi_version() == 1
+    assert c2d._load().conv2d_abi_version() == 2
 
 
 def test_out_dim():
@@ -123,3 +123,36 @@ def test_conv_pool_plan_and_argument_checks():
                                  1, 0, bf16) == c2d.OK
     rc = lib.conv2d_fused_maxpool3x3s2(x, w, None, None, y, 1, 16, 16, 3, 32, 3, 3, 3, 1, 1, 0, bf16, None)
     assert rc == c2d.EINVAL  # stride 3
+
+
+def test_op_struct_layout_matches_the_header(tmp_path):
+    """ctypes' Op has the size and field offsets the C compiler gives struct conv2d_op."""
+    src = tmp_path / "layout.c"
+    fields = [f for f, _ in c2d.Op._fields_]
+    src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "conv2d_fused.h"\nint main(void) {\n'
+                   '  printf("%zu", sizeof(conv2d_op));\n' +
+                   "".join(f'  printf(" %zu", offsetof(conv2d_op, {f}));\n' for f in fields) + "  return 0;\n}\n")
+    import subprocess
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)], check=True)
+    got = [int(v) for v in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
+    want = [ctypes.sizeof(c2d.Op)] + [getattr(c2d.Op, f).offset for f in fields]
+    assert got == want
+
+
+def test_stack_check_names_the_bad_op():
+    P = ctypes.c_void_p
+    ok = c2d.Op(c2d.OP_CONV, 1 << 32, 9 << 32, None, None, None, 17 << 32, 1, 16, 16, 32, 32, 3, 3, 1, 1, 1)
+    pool = c2d.Op(c2d.OP_MAXPOOL, 17 << 32, None, None, None, None, 25 << 32, 1, 16, 16, 32, 32, 0, 0, 0, 0, 0)
+    copy = c2d.Op(c2d.OP_COPY, 1 << 32, None, None, None, None, 33 << 32, 1, 16, 16, 32, 0, 0, 0, 0, 0, 0)
+    assert c2d.stack_check([ok, pool, copy]) == (c2d.OK, -1)
+    bad = c2d.Op(c2d.OP_CONV, 1 << 32, 9 << 32, None, None, None, 17 << 32, 1, 16, 16, 32, 32, 3, 3, 5, 1, 1)
+    assert c2d.stack_check([ok, pool, bad, copy]) == (c2d.EINVAL, 2)
+    overlap = c2d.Op(c2d.OP_COPY, 1 << 32, None, None, None, None, (1 << 32) + 64, 1, 16, 16, 32, 0, 0, 0, 0, 0, 0)
+    assert c2d.stack_check([ok, overlap]) == (c2d.EINVAL, 1)
+    unknown = c2d.Op(9, 1 << 32, None, None, None, None, 17 << 32, 1, 1, 1, 1, 0, 0, 0, 0, 0, 0)
+    assert c2d.stack_check([unknown])[0] == c2d.EINVAL
+    assert c2d.stack_check([]) == (c2d.OK, -1)
+    assert c2d.stack_plan([ok, pool, copy], 1) == "maxpool3x3s2"
+    assert c2d.stack_plan([ok, pool, copy], 2) == "copy"
+    assert c2d.stack_plan([ok, pool, copy], 0) == c2d.plan(1, 16, 16, 32, 32, 3, 3, 1, 1, 1, 0, c2d.DTYPE_BF16)
