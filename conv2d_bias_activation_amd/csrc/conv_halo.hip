@@ -294,8 +294,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void halo3x3_kernel(ConvArgs a, in
     // POOL epilogue of tile k: this wave's conv row, activated, -inf outside the conv
     // output, maxed with its left and right neighbour columns (lanes rl -/+ 1 of the
     // same half) and rounded, goes to LDS row wm (the last wave's to the carry row of
-    // tile k + 1); then wave 0 maxes the carry row of tile k with rows 0 and 1 into
-    // pooled row 2ty, and wave 1 rows 1, 2 and the new carry into pooled row 2ty + 1.
+    // tile k + 1); then the even waves max the carry row of tile k with rows 0 and 1
+    // into pooled row 2ty, the odd waves rows 1, 2 and the new carry into pooled row
+    // 2ty + 1, each wave half of the channels.
     const __amdgpu_buffer_rsrc_t rp =
         make_rsrc(pl.y, POOL ? (uint32_t)((size_t)a.N * pl.PH * pl.PW * Cout * sizeof(T)) : 0u);
     auto prow_at = [&](int row, int q) -> char * { return prow + row * PROW + (q * 64 + lane) * 16; };
@@ -347,46 +348,48 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void halo3x3_kernel(ConvArgs a, in
             }
         }
         halo_barrier();
-        if (!tg.pool || wm > 1) return;
-        const int r0 = wm == 0 ? 4 + (k & 1) : 1, r1 = wm == 0 ? 0 : 2, r2 = wm == 0 ? 1 : 4 + ((k + 1) & 1);
-        const int py = tg.oy0 / 2 + wm, px = (tg.ox0 + 1) / 2 + (rl - 1) / 2;
+        if (!tg.pool) return;
+        // pooled row 2ty + (wave & 1): carry-in, rows 0, 1 (even) or rows 1, 2, carry-out
+        // (odd); the wave takes half of its 2*FN 8-channel quads
+        const int odd = wave & 1, qh = wave >> 1;
+        const int r0 = odd ? 1 : 4 + (k & 1), r1 = odd ? 2 : 0, r2 = odd ? 4 + ((k + 1) & 1) : 1;
+        const int py = tg.oy0 / 2 + odd, px = (tg.ox0 + 1) / 2 + (rl - 1) / 2;
         const bool store = (rl & 1) && rl < 30 && px < pl.PW && py < pl.PH;
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
+        for (int qq = 0; qq < FN; ++qq) {
+            const int q = qh * FN + qq, j = q >> 1, pp = q & 1;
+            const u32x4 v0 = *reinterpret_cast<const u32x4 *>(prow_at(r0, q));
+            const u32x4 v1 = *reinterpret_cast<const u32x4 *>(prow_at(r1, q));
+            const u32x4 v2 = *reinterpret_cast<const u32x4 *>(prow_at(r2, q));
+            T t0[8], t1[8], t2[8], m[8];
+            __builtin_memcpy(t0, &v0, 16);
+            __builtin_memcpy(t1, &v1, 16);
+            __builtin_memcpy(t2, &v2, 16);
+            // The max is taken in fp32 behind an empty asm: left to itself, this compiler
+            // turns an f16 max of this shape into v_max3_f16 and then packs two results
+            // with a plain OR, as if the instruction cleared the upper 16 bits of its
+            // destination, which it does not (the odd channel of each pair came out wrong).
+            auto wide = [](T v) {
+                float f = to_f32(v);
+                asm volatile("" : "+v"(f));
+                return f;
+            };
 #pragma unroll
-            for (int pp = 0; pp < 2; ++pp) {
-                const u32x4 v0 = *reinterpret_cast<const u32x4 *>(prow_at(r0, j * 2 + pp));
-                const u32x4 v1 = *reinterpret_cast<const u32x4 *>(prow_at(r1, j * 2 + pp));
-                const u32x4 v2 = *reinterpret_cast<const u32x4 *>(prow_at(r2, j * 2 + pp));
-                T t0[8], t1[8], t2[8], m[8];
-                __builtin_memcpy(t0, &v0, 16);
-                __builtin_memcpy(t1, &v1, 16);
-                __builtin_memcpy(t2, &v2, 16);
-                // The max is taken in fp32 behind an empty asm: left to itself, this compiler
-                // turns an f16 max of this shape into v_max3_f16 and then packs two results
-                // with a plain OR, as if the instruction cleared the upper 16 bits of its
-                // destination, which it does not (the odd channel of each pair came out wrong).
-                auto wide = [](T v) {
-                    float f = to_f32(v);
-                    asm volatile("" : "+v"(f));
-                    return f;
-                };
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    m[e] = from_f32<T>(__builtin_fmaxf(wide(t0[e]), __builtin_fmaxf(wide(t1[e]), wide(t2[e]))));
-                // groups 2pp, 2pp+1 (4 channels each) -> 8 consecutive channels per lane half
-                u32x2 qq[2];
-                __builtin_memcpy(&qq[0], &m[0], 8);
-                __builtin_memcpy(&qq[1], &m[4], 8);
-                swap_halves(qq[0], qq[1]);
-                const int co = j * 32 + 16 * pp + 8 * hi;
-                const uint32_t off = (store && co < Cout)
-                                         ? ((uint32_t)((tg.n * pl.PH + py) * pl.PW + px) * (uint32_t)Cout +
-                                            (uint32_t)co) * (uint32_t)sizeof(T)
-                                         : kOOB;
-                __builtin_amdgcn_raw_buffer_store_b128(u32x4{qq[0][0], qq[0][1], qq[1][0], qq[1][1]}, rp, (int)off,
-                                                       0, 0);
-            }
+            for (int e = 0; e < 8; ++e)
+                m[e] = from_f32<T>(__builtin_fmaxf(wide(t0[e]), __builtin_fmaxf(wide(t1[e]), wide(t2[e]))));
+            // groups 2pp, 2pp+1 (4 channels each) -> 8 consecutive channels per lane half
+            u32x2 qq2[2];
+            __builtin_memcpy(&qq2[0], &m[0], 8);
+            __builtin_memcpy(&qq2[1], &m[4], 8);
+            swap_halves(qq2[0], qq2[1]);
+            const int co = j * 32 + 16 * pp + 8 * hi;
+            const uint32_t off = (store && co < Cout)
+                                     ? ((uint32_t)((tg.n * pl.PH + py) * pl.PW + px) * (uint32_t)Cout +
+                                        (uint32_t)co) * (uint32_t)sizeof(T)
+                                     : kOOB;
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4{qq2[0][0], qq2[0][1], qq2[1][0], qq2[1][1]}, rp, (int)off,
+                                                   0, 0);
+        }
     };
 
     float *mine = reinterpret_cast<float *>(xch + wave * XBYTES);
