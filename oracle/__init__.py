@@ -63,6 +63,8 @@ def _bind(lib):
     lib.oracle_maxpool3x3s2_nchw.restype = i
     lib.oracle_avgpool2x2_nchw.argtypes = [fp, fp, i, i, i, i, i]
     lib.oracle_avgpool2x2_nchw.restype = i
+    lib.oracle_conv_transpose4x4s2_nchw.argtypes = [dp, dp, dp, dp, dp] + [i] * 7
+    lib.oracle_conv_transpose4x4s2_nchw.restype = i
     return lib
 
 
@@ -218,3 +220,44 @@ def quantize(v, dtype: str):
         r = np.where(r > max_finite, np.inf, r)
         r = np.where(np.isfinite(a), r, a)
     return np.copysign(r, v)
+
+
+def conv_transpose4x4s2(x, w, bias=None, alpha=None, *, act="none", layout="nhwc", threads=0):
+    """ConvTranspose2d 4x4, stride 2, pad 1 in fp64 (framecast `wgslDeconv`): each
+    input pixel (iy, ix) adds x * w[ci, co, ky, kx] to output (2*iy - 1 + ky,
+    2*ix - 1 + kx); then bias and the activation. ``w`` is [Cin, Cout, 4, 4] in both
+    layouts; x and the result are [N,H,W,C] ("nhwc") or [N,C,H,W] ("nchw"); the
+    output is 2H x 2W."""
+    x = np.asarray(x)
+    xc = _f64(x.transpose(0, 3, 1, 2) if layout == "nhwc" else x)
+    wc = _f64(w)
+    N, Cin, H, W = xc.shape
+    if wc.shape[0] != Cin or wc.shape[2:] != (4, 4):
+        raise ValueError("weight must be [Cin, Cout, 4, 4]")
+    Cout = wc.shape[1]
+    y = np.empty((N, Cout, 2 * H, 2 * W), dtype=np.float64)
+    code = _ACT_NAMES[act] if isinstance(act, str) else int(act)
+    if _load().oracle_conv_transpose4x4s2_nchw(_dptr(xc), _dptr(wc), _dptr(_f64(bias)), _dptr(_f64(alpha)),
+                                                _dptr(y), N, H, W, Cin, Cout, code, threads) != 0:
+        raise ValueError("oracle rejected the arguments")
+    return np.ascontiguousarray(y.transpose(0, 2, 3, 1)) if layout == "nhwc" else y
+
+
+def upsample_nearest2x(x, *, layout="nhwc"):
+    """Nearest-neighbour 2x upsample (inferencelayer `UPSAMPLE_SRC`): output pixel
+    (oy, ox) is input pixel (oy // 2, ox // 2). Exact."""
+    x = np.asarray(x)
+    if layout == "nhwc":
+        N, H, W, C = x.shape
+        oy = np.arange(2 * H) // 2
+        ox = np.arange(2 * W) // 2
+        return x[:, oy][:, :, ox]
+    N, C, H, W = x.shape
+    oy = np.arange(2 * H) // 2
+    ox = np.arange(2 * W) // 2
+    return x[:, :, oy][:, :, :, ox]
+
+
+def concat_channels(a, b, *, layout="nhwc"):
+    """Per-pixel channel concat (inferencelayer `CONCAT_SRC`): a's channels, then b's."""
+    return np.concatenate([np.asarray(a), np.asarray(b)], axis=3 if layout == "nhwc" else 1)

@@ -35,6 +35,9 @@
  *   of the in-range taps; out-of-range taps are skipped, which is the same as
  *   padding with -infinity. Output size floor((H - 1)/2) + 1.
  *
+ *   Transposed convolution 4x4, stride 2, pad 1 (framecast `wgslDeconv`): see
+ *   oracle_conv_transpose4x4s2_nchw at the end of this file.
+ *
  *   Average pool 2x2, stride 2, pad 0 (inferencelayer `AVGPOOL_SRC`): the sum
  *   ((x00 + x01) + x10) + x11 in single precision, in exactly that order, then
  *   times 0.25 in single precision. Output size floor(H/2); an odd last row or
@@ -249,6 +252,49 @@ int oracle_avgpool2x2_nchw(const float *x, float *y, int N, int C, int H, int W,
                 s = s + t[W + 1];
                 yp[(size_t)oh * OW + ow] = s * 0.25f;
             }
+    }
+    return 0;
+}
+
+/*
+ * Transposed convolution, 4x4 kernel, stride 2, pad 1 (framecast `wgslDeconv`,
+ * the ConvTranspose2d that ends an IFNet block): x [N][Cin][H][W], weight
+ * [Cin][Cout][4][4] (the transposed conv's own layout), y [N][Cout][2H][2W].
+ * Input pixel (iy, ix) with tap (ky, kx) lands on output row 2*iy - 1 + ky and
+ * column 2*ix - 1 + kx; written as a gather, output (oy, ox) takes the taps whose
+ * oy + 1 - ky and ox + 1 - kx are even and halve to an in-range input pixel. The
+ * sum runs over ci, then ky, then kx in fp64; then bias and the activation.
+ */
+int oracle_conv_transpose4x4s2_nchw(const double *x, const double *w, const double *bias,
+                                    const double *alpha, double *y, int N, int H, int W,
+                                    int Cin, int Cout, int act, int nthreads) {
+    if (N <= 0 || H <= 0 || W <= 0 || Cin <= 0 || Cout <= 0) return -1;
+    const int OH = 2 * H, OW = 2 * W;
+    long rows = (long)N * Cout * OH;
+#pragma omp parallel for schedule(static) num_threads(threads_to_use(nthreads))
+    for (long r = 0; r < rows; ++r) {
+        const int oy = (int)(r % OH);
+        const int co = (int)((r / OH) % Cout);
+        const int n = (int)(r / ((long)OH * Cout));
+        for (int ox = 0; ox < OW; ++ox) {
+            double acc = 0.0;
+            for (int ci = 0; ci < Cin; ++ci) {
+                const double *xc = x + ((size_t)n * Cin + ci) * (size_t)H * W;
+                const double *wc = w + ((size_t)ci * Cout + co) * 16;
+                for (int ky = 0; ky < 4; ++ky) {
+                    const int ty = oy + 1 - ky;
+                    if (ty < 0 || (ty % 2) != 0 || ty / 2 >= H) continue;
+                    for (int kx = 0; kx < 4; ++kx) {
+                        const int tx = ox + 1 - kx;
+                        if (tx < 0 || (tx % 2) != 0 || tx / 2 >= W) continue;
+                        acc += xc[(size_t)(ty / 2) * W + tx / 2] * wc[ky * 4 + kx];
+                    }
+                }
+            }
+            const double v = acc + (bias ? bias[co] : 0.0);
+            y[(((size_t)n * Cout + co) * OH + oy) * OW + ox] =
+                oracle_activation(act & 0xff, v, alpha ? alpha[co] : 0.0);
+        }
     }
     return 0;
 }

@@ -367,7 +367,111 @@ def pin_quantize(orc):
     assert np.isnan(nan[0])
 
 
+# --- transposed convolution, upsample, concat -------------------------------------------
+
+
+def _deconv_scatter(x, w):
+    """ConvTranspose2d 4x4 s2 p1 written as the scatter the layer is defined by:
+    every input pixel adds x * w[ci, co, ky, kx] to output (2*iy - 1 + ky, 2*ix - 1 + kx)
+    when that output exists. Pure Python loops, NCHW, tiny sizes only."""
+    N, Cin, H, W = x.shape
+    Cout = w.shape[1]
+    y = np.zeros((N, Cout, 2 * H, 2 * W))
+    for n in range(N):
+        for ci in range(Cin):
+            for iy in range(H):
+                for ix in range(W):
+                    for ky in range(4):
+                        for kx in range(4):
+                            oy, ox = 2 * iy - 1 + ky, 2 * ix - 1 + kx
+                            if 0 <= oy < 2 * H and 0 <= ox < 2 * W:
+                                for co in range(Cout):
+                                    y[n, co, oy, ox] += x[n, ci, iy, ix] * w[ci, co, ky, kx]
+    return y
+
+
+def pin_deconv_scatter_bruteforce(orc):
+    """The gather the oracle evaluates equals the scatter definition on small shapes,
+    including 1x1 and odd sizes."""
+    r = _rng(40)
+    for (N, Cin, Cout, H, W) in [(1, 1, 1, 1, 1), (2, 3, 2, 3, 4), (1, 2, 3, 5, 2), (1, 4, 1, 2, 7)]:
+        x = r.standard_normal((N, Cin, H, W))
+        w = r.standard_normal((Cin, Cout, 4, 4))
+        _close(orc.conv_transpose4x4s2(x, w, layout="nchw"), _deconv_scatter(x, w), what=f"scatter {N, Cin, H, W}")
+
+
+def pin_deconv_is_adjoint_of_conv(orc):
+    """A transposed conv is the adjoint of the stride-2 pad-1 4x4 conv with the same
+    weights read as [out = Cin][in = Cout]: <T(x), y> = <x, C(y)> (the conv side is the
+    oracle's own, separately pinned conv)."""
+    r = _rng(41)
+    N, Cin, Cout, H, W = 2, 5, 3, 6, 7
+    x = r.standard_normal((N, Cin, H, W))
+    w = r.standard_normal((Cin, Cout, 4, 4))
+    y = r.standard_normal((N, Cout, 2 * H, 2 * W))
+    lhs = float(np.sum(orc.conv_transpose4x4s2(x, w, layout="nchw") * y))
+    cy = orc.conv2d(y, w, stride=2, pad=1, layout="nchw")
+    assert cy.shape == x.shape
+    rhs = float(np.sum(x * cy))
+    assert abs(lhs - rhs) <= 1e-11 * max(1.0, abs(lhs)), (lhs, rhs)
+
+
+def pin_deconv_single_pixel(orc):
+    """One input pixel of one channel set to 1: the output is that channel's 4x4 kernel
+    placed with its top-left tap at (2*iy - 1, 2*ix - 1), cut at the border; bias is
+    added everywhere and the activation applied (closed form)."""
+    Cin, Cout, H, W = 2, 3, 4, 5
+    w = np.arange(Cin * Cout * 16, dtype=np.float64).reshape(Cin, Cout, 4, 4) / 7.0
+    b = np.array([0.5, -1.0, 2.0])
+    for (ci, iy, ix) in [(0, 0, 0), (1, 2, 3), (1, 3, 4)]:
+        x = np.zeros((1, Cin, H, W))
+        x[0, ci, iy, ix] = 1.0
+        want = np.zeros((1, Cout, 2 * H, 2 * W)) + b[None, :, None, None]
+        for ky in range(4):
+            for kx in range(4):
+                oy, ox = 2 * iy - 1 + ky, 2 * ix - 1 + kx
+                if 0 <= oy < 2 * H and 0 <= ox < 2 * W:
+                    want[0, :, oy, ox] += w[ci, :, ky, kx]
+        _close(orc.conv_transpose4x4s2(x, w, b, layout="nchw"), want, what="single pixel")
+        got = orc.conv_transpose4x4s2(x.transpose(0, 2, 3, 1), w, b, act="relu", layout="nhwc")
+        _close(got, np.maximum(want, 0.0).transpose(0, 2, 3, 1), what="single pixel nhwc relu")
+
+
+def pin_deconv_torch(orc):
+    """torch.nn.functional.conv_transpose2d (fp64, CPU; weight [Cin, Cout, 4, 4],
+    stride 2, padding 1) with bias and PReLU."""
+    r = _rng(42)
+    x = r.standard_normal((2, 6, 5, 4))
+    w = r.standard_normal((6, 4, 4, 4))
+    b = r.uniform(-1, 1, 4)
+    al = r.uniform(0, 0.25, 4)
+    t = torch.nn.functional.conv_transpose2d(torch.from_numpy(x), torch.from_numpy(w), torch.from_numpy(b),
+                                             stride=2, padding=1)
+    t = torch.where(t >= 0, t, torch.from_numpy(al)[None, :, None, None] * t).numpy()
+    _close(orc.conv_transpose4x4s2(x, w, b, al, act="prelu", layout="nchw"), t, what="torch deconv")
+
+
+def pin_upsample_concat(orc):
+    """Nearest 2x upsample of a ramp is the ramp at (oy // 2, ox // 2); concat puts a's
+    channels first (closed forms, both layouts)."""
+    N, H, W, C = 2, 3, 5, 4
+    x = np.arange(N * H * W * C, dtype=np.float64).reshape(N, H, W, C)
+    up = orc.upsample_nearest2x(x)
+    assert up.shape == (N, 2 * H, 2 * W, C)
+    for oy in range(2 * H):
+        for ox in range(2 * W):
+            assert np.array_equal(up[:, oy, ox], x[:, oy // 2, ox // 2])
+    assert np.array_equal(orc.upsample_nearest2x(x.transpose(0, 3, 1, 2), layout="nchw"), up.transpose(0, 3, 1, 2))
+    b = -np.arange(N * H * W * 3, dtype=np.float64).reshape(N, H, W, 3)
+    cat = orc.concat_channels(x, b)
+    assert cat.shape == (N, H, W, C + 3)
+    assert np.array_equal(cat[..., :C], x) and np.array_equal(cat[..., C:], b)
+    catc = orc.concat_channels(x.transpose(0, 3, 1, 2), b.transpose(0, 3, 1, 2), layout="nchw")
+    assert np.array_equal(catc, cat.transpose(0, 3, 1, 2))
+
+
 ALL_PINS = [pin_worked_example, pin_geometry, pin_pointwise_is_matmul, pin_delta_kernel,
             pin_im2col_bruteforce, pin_constant_borders, pin_linearity, pin_layout_equivalence,
             pin_batch_independence, pin_torch_conv2d, pin_activations, pin_residual_order,
-            pin_points_match_full, pin_maxpool, pin_avgpool]
+            pin_points_match_full, pin_maxpool, pin_avgpool, pin_deconv_scatter_bruteforce,
+            pin_deconv_is_adjoint_of_conv, pin_deconv_single_pixel, pin_deconv_torch, pin_upsample_concat]

@@ -42,6 +42,14 @@ MUTANTS = {
                       "                s = s + t[W];"),
     "avgpool_scale": ("s * 0.25f", "s * 0.5f"),
     "avgpool_row_offset": ("s = s + t[W];", "s = s + t[1];"),
+    "deconv_pad_sign": ("const int ty = oy + 1 - ky;", "const int ty = oy - 1 - ky;"),
+    "deconv_flipped_taps": ("acc += xc[(size_t)(ty / 2) * W + tx / 2] * wc[ky * 4 + kx];",
+                            "acc += xc[(size_t)(ty / 2) * W + tx / 2] * wc[(3 - ky) * 4 + (3 - kx)];"),
+    "deconv_weight_transposed": ("const double *wc = w + ((size_t)ci * Cout + co) * 16;",
+                                 "const double *wc = w + ((size_t)co * Cin + ci) * 16;"),
+    "deconv_odd_taps_kept": ("if (tx < 0 || (tx % 2) != 0 || tx / 2 >= W) continue;",
+                             "if (tx < 0 || tx / 2 >= W) continue;"),
+    "deconv_bias_dropped": ("const double v = acc + (bias ? bias[co] : 0.0);", "const double v = acc;"),
 }
 
 
