@@ -16,7 +16,9 @@ import torch
 
 __all__ = ["conv2d_fused", "conv2d_fused_maxpool3x3s2", "maxpool3x3s2", "avgpool2x2", "out_dim",
            "check_args", "plan", "plan_maxpool", "Op", "conv_op", "pool_op", "copy_op", "stack_check",
-           "stack_plan", "stack_run", "StackGraph",
+           "stack_plan", "stack_run", "StackGraph", "conv_transpose4x4s2", "plan_deconv",
+           "upsample_nearest2x", "concat_channels", "upsample2x_concat", "deconv_op", "upsample_op",
+           "concat_op",
            "last_error", "library_path", "Conv2dError", "ACT_NONE", "ACT_RELU", "ACT_SILU",
            "ACT_PRELU", "RES_BEFORE_ACT", "LAYOUT_NHWC", "LAYOUT_NCHW", "DTYPE_F32",
            "DTYPE_BF16", "DTYPE_F16"]
@@ -38,6 +40,7 @@ _LIB_PATH = os.path.join(_HERE, "libconv2d_fused.so")
 # Every exported symbol of the C ABI, with (restype, argtypes).
 _vp, _fp, _i, _cp = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_char_p
 OP_CONV, OP_CONV_MAXPOOL, OP_MAXPOOL, OP_AVGPOOL, OP_COPY = 0, 1, 2, 3, 4
+OP_DECONV, OP_UPSAMPLE, OP_CONCAT, OP_UPSAMPLE_CONCAT = 5, 6, 7, 8
 
 
 class Op(ctypes.Structure):
@@ -65,6 +68,11 @@ SIGNATURES = {
     "conv2d_stack_graph_create": (_i, [_op_p, _i, _i, _i, ctypes.POINTER(ctypes.c_void_p)]),
     "conv2d_stack_graph_launch": (_i, [_vp, _vp]),
     "conv2d_stack_graph_destroy": (_i, [_vp]),
+    "conv_transpose4x4s2": (_i, [_vp, _vp, _fp, _fp, _vp] + [_i] * 9 + [_vp]),
+    "conv_transpose4x4s2_plan": (_i, [_i] * 9 + [_cp, _i]),
+    "upsample_nearest2x": (_i, [_vp, _vp] + [_i] * 6 + [_vp]),
+    "concat_channels": (_i, [_vp, _vp, _vp] + [_i] * 7 + [_vp]),
+    "upsample2x_concat": (_i, [_vp, _vp, _vp] + [_i] * 7 + [_vp]),
     "conv2d_last_error": (_cp, []),
     "conv2d_abi_version": (_i, []),
 }
@@ -365,3 +373,127 @@ class StackGraph:
             self.close()
         except Exception:
             pass
+
+
+def _dtype_code(dtype):
+    dt = _DTYPES.get(dtype)
+    if dt is None:
+        raise ValueError(f"unsupported dtype {dtype}")
+    return dt
+
+
+def conv_transpose4x4s2(x, w, bias=None, alpha=None, *, act="none", layout="nhwc", out_dtype=None,
+                        out=None, stream=None):
+    """ConvTranspose2d 4x4, stride 2, pad 1 (+bias, activation) on the GPU; see
+    include/conv2d_fused.h. w is [Cin, Cout, 4, 4] in x's dtype for both layouts; the
+    output is [N, 2H, 2W, Cout] ("nhwc") or [N, Cout, 2H, 2W] ("nchw") in ``out_dtype``
+    (x's dtype, or torch.float32)."""
+    lib = _load()
+    lay = _LAYOUTS[layout]
+    dt = _dtype_code(x.dtype)
+    out_dtype = x.dtype if out_dtype is None else out_dtype
+    odt = _dtype_code(out_dtype)
+    if x.dim() != 4 or w.dim() != 4 or tuple(w.shape[2:]) != (4, 4):
+        raise ValueError("x must be 4-D and w [Cin, Cout, 4, 4]")
+    if layout == "nhwc":
+        N, H, W, Cin = x.shape
+    else:
+        N, Cin, H, W = x.shape
+    if w.shape[0] != Cin:
+        raise ValueError(f"weight has {w.shape[0]} input channels, x has {Cin}")
+    Cout = w.shape[1]
+    dev = x.device
+    _require(x, "x", x.dtype, dev)
+    _require(w, "w", x.dtype, dev)
+    _require(bias, "bias", torch.float32, dev)
+    _require(alpha, "alpha", torch.float32, dev)
+    for t, name in ((bias, "bias"), (alpha, "alpha")):
+        if t is not None and tuple(t.shape) != (Cout,):
+            raise ValueError(f"{name} must have shape ({Cout},)")
+    yshape = (N, 2 * H, 2 * W, Cout) if layout == "nhwc" else (N, Cout, 2 * H, 2 * W)
+    if out is None:
+        out = torch.empty(yshape, dtype=out_dtype, device=dev)
+    else:
+        _require(out, "out", out_dtype, dev)
+        if tuple(out.shape) != yshape:
+            raise ValueError(f"out must have shape {yshape}")
+    rc = lib.conv_transpose4x4s2(_ptr(x), _ptr(w), _ptr(bias), _ptr(alpha), _ptr(out), N, H, W, Cin, Cout,
+                                 _act_code(act, False), lay, dt, odt, _stream_handle(stream))
+    _check(rc)
+    return out
+
+
+def plan_deconv(N, H, W, Cin, Cout, act, layout, dtype, out_dtype=None) -> str:
+    """Kernel variants conv_transpose4x4s2 picks for a shape (host only)."""
+    buf = ctypes.create_string_buffer(256)
+    n = _load().conv_transpose4x4s2_plan(N, H, W, Cin, Cout, act, layout, dtype,
+                                         dtype if out_dtype is None else out_dtype, buf, 256)
+    _check(n if n < 0 else OK)
+    return buf.value.decode()
+
+
+def _resample(fn_name, a, b, up, layout, out, stream):
+    lib = _load()
+    lay = _LAYOUTS[layout]
+    dt = _dtype_code(a.dtype)
+    if a.dim() != 4 or (b is not None and b.dim() != 4):
+        raise ValueError("inputs must be 4-D")
+    N, H, W, Ca = _nhwc_dims(a, layout)
+    s = 2 if up else 1
+    _require(a, "a", a.dtype, a.device)
+    Cb = 0
+    if b is not None:
+        _require(b, "b", a.dtype, a.device)
+        Nb, Hb, Wb, Cb = _nhwc_dims(b, layout)
+        if (Nb, Hb, Wb) != (N, s * H, s * W):
+            raise ValueError(f"b must be {s * H}x{s * W} with batch {N}")
+    C = Ca + Cb
+    yshape = (N, s * H, s * W, C) if layout == "nhwc" else (N, C, s * H, s * W)
+    if out is None:
+        out = torch.empty(yshape, dtype=a.dtype, device=a.device)
+    else:
+        _require(out, "out", a.dtype, a.device)
+        if tuple(out.shape) != yshape:
+            raise ValueError(f"out must have shape {yshape}")
+    if b is None:
+        rc = getattr(lib, fn_name)(_ptr(a), _ptr(out), N, H, W, Ca, lay, dt, _stream_handle(stream))
+    else:
+        rc = getattr(lib, fn_name)(_ptr(a), _ptr(b), _ptr(out), N, H, W, Ca, Cb, lay, dt, _stream_handle(stream))
+    _check(rc)
+    return out
+
+
+def upsample_nearest2x(x, *, layout="nhwc", out=None, stream=None):
+    """Nearest-neighbour 2x upsample on the GPU (bit-exact copy)."""
+    return _resample("upsample_nearest2x", x, None, True, layout, out, stream)
+
+
+def concat_channels(a, b, *, layout="nhwc", out=None, stream=None):
+    """Channel concat [a, b] of two same-size maps on the GPU (bit-exact copy)."""
+    return _resample("concat_channels", a, b, False, layout, out, stream)
+
+
+def upsample2x_concat(a, b, *, layout="nhwc", out=None, stream=None):
+    """concat_channels(upsample_nearest2x(a), b) in one pass (b is twice a's size)."""
+    return _resample("upsample2x_concat", a, b, True, layout, out, stream)
+
+
+def deconv_op(x, w, y, bias=None, alpha=None, *, act="none", layout="nhwc"):
+    """An Op for conv_transpose4x4s2 (output in the stack's dtype)."""
+    N, H, W, Cin = _nhwc_dims(x, layout)
+    return Op(OP_DECONV, x.data_ptr(), w.data_ptr(), _tensor_ptr(bias), _tensor_ptr(alpha), None, y.data_ptr(),
+              N, H, W, Cin, w.shape[1], 4, 4, 2, 1, _act_code(act, False))
+
+
+def upsample_op(x, y, *, layout="nhwc"):
+    """An Op for upsample_nearest2x."""
+    N, H, W, C = _nhwc_dims(x, layout)
+    return Op(OP_UPSAMPLE, x.data_ptr(), None, None, None, None, y.data_ptr(), N, H, W, C, 0, 0, 0, 0, 0, 0)
+
+
+def concat_op(a, b, y, *, up=False, layout="nhwc"):
+    """An Op for concat_channels, or with up=True upsample2x_concat (a is the small map)."""
+    N, H, W, Ca = _nhwc_dims(a, layout)
+    Cb = _nhwc_dims(b, layout)[3]
+    return Op(OP_UPSAMPLE_CONCAT if up else OP_CONCAT, a.data_ptr(), None, None, None, b.data_ptr(),
+              y.data_ptr(), N, H, W, Ca, Cb, 0, 0, 0, 0, 0)

@@ -484,6 +484,92 @@ int check_conv_pool(const void *x, const void *w, const float *alpha, const void
     return CONV2D_OK;
 }
 
+// Transposed conv 4x4/s2/p1: the matrix-core kernel for 16-bit types with Cin % 8 == 0
+// (weights repacked into the scratch, and a channel-first input copied to channel-last
+// there too), the direct kernel otherwise.
+struct DeconvPlan {
+    bool mfma;
+    bool x_copy;   // channel-first input copied to channel-last in the scratch
+    bool out_f32;  // y in fp32 (16-bit input)
+    size_t x_off;  // byte offset of the input copy in the scratch (after the packed weights)
+};
+
+int check_deconv(const void *x, const void *w, const float *bias, const float *alpha, const void *y, int N, int H,
+                 int W, int Cin, int Cout, int act, int layout, int dtype, int out_dtype, DeconvArgs *a,
+                 DeconvPlan *p) {
+    if (!x || !w || !y) return set_error(CONV2D_EINVAL, "conv_transpose4x4s2: x, w and y must not be null");
+    if (N <= 0 || H <= 0 || W <= 0 || Cin <= 0 || Cout <= 0)
+        return set_error(CONV2D_EINVAL, "conv_transpose4x4s2: sizes must be positive (N=%d H=%d W=%d Cin=%d Cout=%d)",
+                         N, H, W, Cin, Cout);
+    if (layout != CONV2D_LAYOUT_NHWC && layout != CONV2D_LAYOUT_NCHW)
+        return set_error(CONV2D_EINVAL, "conv_transpose4x4s2: unknown layout %d", layout);
+    if (!dtype_bytes(dtype)) return set_error(CONV2D_EINVAL, "conv_transpose4x4s2: unknown dtype %d", dtype);
+    if (out_dtype != dtype && out_dtype != CONV2D_DTYPE_F32)
+        return set_error(CONV2D_EINVAL, "conv_transpose4x4s2: out_dtype must be dtype or CONV2D_DTYPE_F32 (got %d)",
+                         out_dtype);
+    const int code = act & 0xff;
+    if (code > CONV2D_ACT_PRELU || (act & ~0xff))
+        return set_error(CONV2D_EINVAL, "conv_transpose4x4s2: unknown activation flags 0x%x", act);
+    if (code == CONV2D_ACT_PRELU && !alpha) return set_error(CONV2D_EINVAL, "conv_transpose4x4s2: PRELU needs alpha");
+    const long long xe = (long long)N * H * W * Cin, we = 16ll * Cin * Cout, ye = 4ll * N * H * W * Cout;
+    if (xe > kMaxElems || we > kMaxElems || ye > kMaxElems)
+        return set_error(CONV2D_EUNSUPPORTED, "conv_transpose4x4s2: tensors of 2^31 or more elements are not supported");
+    const int eb = dtype_bytes(dtype), ob = dtype_bytes(out_dtype);
+    if (overlap(y, ye * ob, x, xe * eb)) return set_error(CONV2D_EINVAL, "conv_transpose4x4s2: y overlaps x");
+    if (overlap(y, ye * ob, w, we * eb)) return set_error(CONV2D_EINVAL, "conv_transpose4x4s2: y overlaps w");
+    *a = DeconvArgs{};
+    a->x = x;
+    a->w = w;
+    a->bias = bias;
+    a->alpha = code == CONV2D_ACT_PRELU ? alpha : nullptr;
+    a->y = const_cast<void *>(y);
+    a->N = N;
+    a->H = H;
+    a->W = W;
+    a->Cin = Cin;
+    a->Cout = Cout;
+    a->CoP = (Cout + 31) / 32 * 32;
+    a->act = code;
+    *p = DeconvPlan{};
+    p->out_f32 = out_dtype == CONV2D_DTYPE_F32 && dtype != CONV2D_DTYPE_F32;
+    const bool nchw = layout == CONV2D_LAYOUT_NCHW;
+    const size_t wp_bytes = round256((size_t)16 * a->CoP * Cin * eb);
+    const size_t x_bytes = nchw ? round256((size_t)xe * eb) : 0;
+    p->x_off = wp_bytes;
+    p->x_copy = nchw;
+    p->mfma = dtype != CONV2D_DTYPE_F32 && (Cin % 8) == 0 && wp_bytes + x_bytes <= kScratchBytes &&
+              (nchw ? N <= 65535 : aligned16(x));
+    return CONV2D_OK;
+}
+
+// Upsample and concat: y = concat(up ? upsample2x(a) : a, b). H, W: a's size when up,
+// else the common size.
+int check_concat(const void *a, const void *b, const void *y, int N, int H, int W, int Ca, int Cb, bool up,
+                 int layout, int dtype, const char *name) {
+    if (!a || !y || (Cb > 0 && !b)) return set_error(CONV2D_EINVAL, "%s: inputs and y must not be null", name);
+    if (N <= 0 || H <= 0 || W <= 0 || Ca <= 0 || Cb < 0)
+        return set_error(CONV2D_EINVAL, "%s: sizes must be positive", name);
+    if (layout != CONV2D_LAYOUT_NHWC && layout != CONV2D_LAYOUT_NCHW)
+        return set_error(CONV2D_EINVAL, "%s: unknown layout %d", name, layout);
+    if (!dtype_bytes(dtype)) return set_error(CONV2D_EINVAL, "%s: unknown dtype %d", name, dtype);
+    const long long s = up ? 4 : 1;
+    const long long ae = (long long)N * H * W * Ca, be = s * N * H * W * Cb, ye = s * N * H * W * (Ca + (long long)Cb);
+    if (ye > kMaxElems) return set_error(CONV2D_EUNSUPPORTED, "%s: tensors of 2^31 or more elements are not supported",
+                                         name);
+    const int eb = dtype_bytes(dtype);
+    if (overlap(y, ye * eb, a, ae * eb)) return set_error(CONV2D_EINVAL, "%s: y overlaps an input", name);
+    if (Cb > 0 && overlap(y, ye * eb, b, be * eb)) return set_error(CONV2D_EINVAL, "%s: y overlaps an input", name);
+    return CONV2D_OK;
+}
+
+bool concat_vec(const void *a, const void *b, const void *y, int H, int W, int Ca, int Cb, bool up, int layout,
+                int dtype) {
+    const int ve = 16 / dtype_bytes(dtype);
+    const bool al = aligned16(a) && aligned16(y) && (Cb == 0 || aligned16(b));
+    if (layout == CONV2D_LAYOUT_NHWC) return al && (Ca % ve) == 0 && (Cb % ve) == 0;
+    return al && !up && ((long long)H * W) % ve == 0;
+}
+
 // One validated op of a call or a stack: everything its launch needs, decided on
 // the host before anything is launched.
 struct OpPlan {
@@ -495,13 +581,19 @@ struct OpPlan {
     const void *x;  // pools, copy
     void *y;
     int N, H, W, C;
-    bool vec;      // pools: the 16-byte channel-last kernels
+    bool vec;      // pools, upsample/concat: the 16-byte kernels
     size_t bytes;  // copy
+    DeconvArgs da;  // CONV2D_OP_DECONV
+    DeconvPlan dp;
+    const void *b;  // concat: second input
+    int Ca, Cb;     // concat channels (Cb = 0: upsample)
+    bool up;        // upsample the first input
 };
 
 bool needs_scratch(const OpPlan &o) {
     if (o.kind == CONV2D_OP_CONV)
         return o.plan.family == FAM_NCHW_VIA_NHWC || (o.plan.family == FAM_NHWC && o.plan.nh.splits > 1);
+    if (o.kind == CONV2D_OP_DECONV) return o.dp.mfma;
     return o.kind == CONV2D_OP_CONV_MAXPOOL && o.pf.kind == POOL_TWO_KERNELS;
 }
 
@@ -558,6 +650,33 @@ int check_op(const conv2d_op &op, int layout, int dtype, OpPlan *o) {
             return set_error(CONV2D_EINVAL, "copy: y overlaps x");
         o->x = op.x;
         o->y = op.y;
+        return CONV2D_OK;
+    }
+    case CONV2D_OP_DECONV:
+        return check_deconv(op.x, op.w, op.bias, op.alpha, op.y, op.N, op.H, op.W, op.Cin, op.Cout, op.act, layout,
+                            dtype, dtype, &o->da, &o->dp);
+    case CONV2D_OP_UPSAMPLE:
+    case CONV2D_OP_CONCAT:
+    case CONV2D_OP_UPSAMPLE_CONCAT: {
+        const bool up = op.kind != CONV2D_OP_CONCAT;
+        const int Cb = op.kind == CONV2D_OP_UPSAMPLE ? 0 : op.Cout;
+        const char *name = op.kind == CONV2D_OP_UPSAMPLE ? "upsample_nearest2x"
+                           : op.kind == CONV2D_OP_CONCAT ? "concat_channels"
+                                                         : "upsample2x_concat";
+        if (op.kind != CONV2D_OP_UPSAMPLE && Cb <= 0) return set_error(CONV2D_EINVAL, "%s: Cb must be positive", name);
+        const void *b = Cb > 0 ? op.residual : nullptr;
+        int rc = check_concat(op.x, b, op.y, op.N, op.H, op.W, op.Cin, Cb, up, layout, dtype, name);
+        if (rc) return rc;
+        o->x = op.x;
+        o->b = b;
+        o->y = op.y;
+        o->N = op.N;
+        o->H = up ? 2 * op.H : op.H;  // y's size
+        o->W = up ? 2 * op.W : op.W;
+        o->Ca = op.Cin;
+        o->Cb = Cb;
+        o->up = up;
+        o->vec = concat_vec(op.x, b, op.y, o->H, o->W, op.Cin, Cb, up, layout, dtype);
         return CONV2D_OK;
     }
     default:
@@ -633,6 +752,30 @@ int launch_op(const OpPlan &o, hipStream_t st) {
     case CONV2D_OP_COPY:
         e = launch_copy(o.x, o.y, o.bytes, st);
         return e == hipSuccess ? CONV2D_OK : hip_fail(e, "copy launch");
+    case CONV2D_OP_DECONV: {
+        if (!o.dp.mfma) {
+            e = launch_deconv_direct(o.da, o.dtype, o.dp.out_f32, nchw, st);
+            return e == hipSuccess ? CONV2D_OK : hip_fail(e, "conv_transpose4x4s2 launch");
+        }
+        float *scratch = nullptr;
+        int rc = get_scratch(&scratch);
+        if (rc) return rc;
+        DeconvArgs a = o.da;
+        a.wp = scratch;
+        e = launch_deconv_pack(a.w, scratch, a.Cin, a.Cout, a.CoP, o.dtype, st);
+        if (e == hipSuccess && o.dp.x_copy) {
+            void *xs = reinterpret_cast<char *>(scratch) + o.dp.x_off;
+            e = launch_nchw_to_nhwc(a.x, xs, a.N, a.Cin, a.H * a.W, o.dtype, st);
+            a.x = xs;
+        }
+        if (e == hipSuccess) e = launch_deconv_mfma(a, o.dtype, o.dp.out_f32, nchw, st);
+        return e == hipSuccess ? CONV2D_OK : hip_fail(e, "conv_transpose4x4s2 launch");
+    }
+    case CONV2D_OP_UPSAMPLE:
+    case CONV2D_OP_CONCAT:
+    case CONV2D_OP_UPSAMPLE_CONCAT:
+        e = launch_concat(o.x, o.b, o.y, o.N, o.H, o.W, o.Ca, o.Cb, o.up, nchw, o.dtype, o.vec, st);
+        return e == hipSuccess ? CONV2D_OK : hip_fail(e, "upsample/concat launch");
     default:
         return set_error(CONV2D_EINVAL, "unknown op kind %d", o.kind);
     }
@@ -669,6 +812,19 @@ int describe_op(const OpPlan &o, char *buf, int cap) {
     case CONV2D_OP_AVGPOOL:
         snprintf(tmp, sizeof tmp, "avgpool2x2");
         break;
+    case CONV2D_OP_DECONV:
+        if (o.dp.mfma)
+            snprintf(tmp, sizeof tmp, "deconv4x4s2_pack+%sdeconv4x4s2_mfma %s%s", o.dp.x_copy ? "to_nhwc+" : "",
+                     dtype_name(o.dtype), o.dp.out_f32 ? " out f32" : "");
+        else
+            snprintf(tmp, sizeof tmp, "deconv4x4s2_direct %s%s", dtype_name(o.dtype), o.dp.out_f32 ? " out f32" : "");
+        break;
+    case CONV2D_OP_UPSAMPLE:
+    case CONV2D_OP_CONCAT:
+    case CONV2D_OP_UPSAMPLE_CONCAT:
+        snprintf(tmp, sizeof tmp, "%s%s", o.kind == CONV2D_OP_UPSAMPLE ? "upsample2x" : o.up ? "upsample2x_concat" : "concat",
+                 o.vec ? "_vec16" : "_scalar");
+        break;
     default:
         snprintf(tmp, sizeof tmp, "copy");
         break;
@@ -685,7 +841,7 @@ int describe_op(const OpPlan &o, char *buf, int cap) {
 
 extern "C" {
 
-int conv2d_abi_version(void) { return 2; }
+int conv2d_abi_version(void) { return 3; }
 
 const char *conv2d_last_error(void) { return g_err.c_str(); }
 
@@ -756,6 +912,51 @@ int maxpool3x3s2(const void *x, void *y, int N, int H, int W, int C, int layout,
 int avgpool2x2(const void *x, void *y, int N, int H, int W, int C, int layout, int dtype,
                void *stream) {
     const conv2d_op op{CONV2D_OP_AVGPOOL, x, nullptr, nullptr, nullptr, nullptr, y, N, H, W, C, C, 2, 2, 2, 0, 0};
+    return run_one(op, layout, dtype, stream);
+}
+
+int conv_transpose4x4s2(const void *x, const void *w, const float *bias, const float *alpha, void *y, int N, int H,
+                        int W, int Cin, int Cout, int act, int layout, int dtype, int out_dtype, void *stream) {
+    OpPlan o{};
+    o.kind = CONV2D_OP_DECONV;
+    o.layout = layout;
+    o.dtype = dtype;
+    int rc = check_deconv(x, w, bias, alpha, y, N, H, W, Cin, Cout, act, layout, dtype, out_dtype, &o.da, &o.dp);
+    if (rc) return rc;
+    rc = launch_op(o, static_cast<hipStream_t>(stream));
+    return rc ? rc : set_ok();
+}
+
+int conv_transpose4x4s2_plan(int N, int H, int W, int Cin, int Cout, int act, int layout, int dtype, int out_dtype,
+                             char *buf, int cap) {
+    OpPlan o{};
+    o.kind = CONV2D_OP_DECONV;
+    o.layout = layout;
+    o.dtype = dtype;
+    const void *px = (const void *)(uintptr_t)0x100000000ull;
+    const void *pw = (const void *)(uintptr_t)0x900000000ull;
+    const void *py = (const void *)(uintptr_t)0x1100000000ull;
+    const float *pa = (const float *)(uintptr_t)0x1900000000ull;
+    int rc = check_deconv(px, pw, nullptr, pa, py, N, H, W, Cin, Cout, act, layout, dtype, out_dtype, &o.da, &o.dp);
+    if (rc) return rc;
+    set_ok();
+    return describe_op(o, buf, cap);
+}
+
+int upsample_nearest2x(const void *x, void *y, int N, int H, int W, int C, int layout, int dtype, void *stream) {
+    const conv2d_op op{CONV2D_OP_UPSAMPLE, x, nullptr, nullptr, nullptr, nullptr, y, N, H, W, C, 0, 0, 0, 0, 0, 0};
+    return run_one(op, layout, dtype, stream);
+}
+
+int concat_channels(const void *a, const void *b, void *y, int N, int H, int W, int Ca, int Cb, int layout, int dtype,
+                    void *stream) {
+    const conv2d_op op{CONV2D_OP_CONCAT, a, nullptr, nullptr, nullptr, b, y, N, H, W, Ca, Cb, 0, 0, 0, 0, 0};
+    return run_one(op, layout, dtype, stream);
+}
+
+int upsample2x_concat(const void *a, const void *b, void *y, int N, int H, int W, int Ca, int Cb, int layout,
+                      int dtype, void *stream) {
+    const conv2d_op op{CONV2D_OP_UPSAMPLE_CONCAT, a, nullptr, nullptr, nullptr, b, y, N, H, W, Ca, Cb, 0, 0, 0, 0, 0};
     return run_one(op, layout, dtype, stream);
 }
 

@@ -28,7 +28,8 @@
  *    and keeps until the process ends. It holds the fp32 partial sums of split-K
  *    calls, the channel-last copies of x and w of 16-bit channel-first calls and
  *    the unpooled conv output of conv2d_fused_maxpool3x3s2 calls that run as two
- *    kernels.
+ *    kernels, and the repacked weights (plus a channel-last input copy) of
+ *    conv_transpose4x4s2 calls on the matrix cores.
  *    Such calls on one device all use that buffer: callers that run conv2d_fused
  *    on several streams of one device at the same time must serialise those
  *    calls. (Under HIP graph capture, make one call on each device before
@@ -168,6 +169,63 @@ int conv2d_fused_maxpool_plan(int N, int H, int W, int Cin, int Cout, int kh, in
 int avgpool2x2(const void *x, void *y, int N, int H, int W, int C, int layout, int dtype,
                void *stream);
 
+/*
+ * Transposed convolution (ConvTranspose2d), 4x4 kernel, stride 2, padding 1: the layer
+ * that ends an IFNet block (framecast page, `wgslDeconv`, the 4x4 stride-2 deconv from
+ * the stride-16 map to the stride-8 map). Input pixel (iy, ix) with tap (ky, kx) adds
+ * x[ci] * w[ci][co][ky][kx] to output (2*iy - 1 + ky, 2*ix - 1 + kx) when that lies in
+ * the 2H x 2W output; then bias[co] and the activation are applied (no residual).
+ *
+ * x      [N,H,W,Cin] or [N,Cin,H,W] in `dtype` (required)
+ * w      [Cin][Cout][4][4] in `dtype`, the transposed conv's own layout in both
+ *        layouts (required)
+ * bias   fp32 [Cout] or NULL; alpha fp32 [Cout], required when act is PRELU
+ * y      [N,2H,2W,Cout] or [N,Cout,2H,2W] in `out_dtype` (required; may not overlap x
+ *        or w)
+ * act    CONV2D_ACT_* (CONV2D_RES_BEFORE_ACT is rejected)
+ * out_dtype  `dtype`, or CONV2D_DTYPE_F32 for an fp32 output from 16-bit inputs
+ *        (framecast keeps the deconv output in fp32 under f16 storage)
+ *
+ * Accumulation is fp32 in any order, rounded once to out_dtype. 16-bit inputs with
+ * Cin % 8 == 0 run on the matrix cores: the weights are first repacked into the
+ * library's per-device scratch buffer (16 * ceil(Cout/32)*32 * Cin elements) and a
+ * channel-first input is copied to channel-last there too; those buffers must fit the
+ * 64 MiB scratch, else (and for fp32 or other Cin) a direct kernel on the vector ALUs
+ * runs instead. Shares the scratch as conv2d_fused does. Errors as conv2d_fused.
+ */
+int conv_transpose4x4s2(const void *x, const void *w, const float *bias, const float *alpha, void *y, int N, int H,
+                        int W, int Cin, int Cout, int act, int layout, int dtype, int out_dtype, void *stream);
+
+/* Host-only: the kernel variants conv_transpose4x4s2 would launch (as conv2d_plan). */
+int conv_transpose4x4s2_plan(int N, int H, int W, int Cin, int Cout, int act, int layout, int dtype, int out_dtype,
+                             char *buf, int cap);
+
+/*
+ * Nearest-neighbour 2x upsample: y[n, oy, ox, c] = x[n, oy/2, ox/2, c] (floor).
+ * Source: inferencelayer page, `UPSAMPLE_SRC` and the top-down path of the CCFM neck.
+ * x [N,H,W,C] or [N,C,H,W] in `dtype`; y [N,2H,2W,C] or [N,C,2H,2W]. Bit-exact copy.
+ */
+int upsample_nearest2x(const void *x, void *y, int N, int H, int W, int C, int layout, int dtype, void *stream);
+
+/*
+ * Per-pixel channel concat: y holds a's Ca channels, then b's Cb channels.
+ * Source: inferencelayer page, `CONCAT_SRC` and the CCFM neck ([upsampled, backbone]
+ * on the top-down path, [downsampled, top-down] on the bottom-up path).
+ * a [N,H,W,Ca] / [N,Ca,H,W], b [N,H,W,Cb] / [N,Cb,H,W], y [N,H,W,Ca+Cb] /
+ * [N,Ca+Cb,H,W], all in `dtype`; y may not overlap a or b. Bit-exact copy.
+ */
+int concat_channels(const void *a, const void *b, void *y, int N, int H, int W, int Ca, int Cb, int layout, int dtype,
+                    void *stream);
+
+/*
+ * y = concat_channels(upsample_nearest2x(a), b) in one pass, without writing the
+ * upsampled map: the upsample and concat of the CCFM top-down path (inferencelayer
+ * page, `UPSAMPLE_SRC` then `CONCAT_SRC`). a [N,H,W,Ca] / [N,Ca,H,W] (the small map);
+ * b [N,2H,2W,Cb] / [N,Cb,2H,2W]; y [N,2H,2W,Ca+Cb] / [N,Ca+Cb,2H,2W]. Bit-exact copy.
+ */
+int upsample2x_concat(const void *a, const void *b, void *y, int N, int H, int W, int Ca, int Cb, int layout,
+                      int dtype, void *stream);
+
 /* floor((in + 2*pad - k)/stride) + 1, or -1 if in, k, stride <= 0, pad < 0 or the
  * kernel does not fit the padded input (inferencelayer `conv()`). Host only. */
 int conv2d_out_dim(int in, int k, int stride, int pad);
@@ -207,6 +265,13 @@ int conv2d_plan(int N, int H, int W, int Cin, int Cout, int kh, int kw, int stri
  *   CONV2D_OP_MAXPOOL       maxpool3x3s2(x, y, N, H, W, C = Cin)
  *   CONV2D_OP_AVGPOOL       avgpool2x2(x, y, N, H, W, C = Cin)
  *   CONV2D_OP_COPY          y = x, N*H*W*Cin elements of dtype (y may not overlap x)
+ *   CONV2D_OP_DECONV        conv_transpose4x4s2(x, w, bias, alpha, y, N, H, W, Cin, Cout,
+ *                           act) with out_dtype = dtype
+ *   CONV2D_OP_UPSAMPLE      upsample_nearest2x(x, y, N, H, W, C = Cin)
+ *   CONV2D_OP_CONCAT        concat_channels(a = x, b = residual, y, N, H, W, Ca = Cin,
+ *                           Cb = Cout)
+ *   CONV2D_OP_UPSAMPLE_CONCAT upsample2x_concat(a = x, b = residual, y, N, H, W,
+ *                           Ca = Cin, Cb = Cout)
  * Layout and dtype are shared by the whole stack.
  */
 #define CONV2D_OP_CONV 0
@@ -214,6 +279,10 @@ int conv2d_plan(int N, int H, int W, int Cin, int Cout, int kh, int kw, int stri
 #define CONV2D_OP_MAXPOOL 2
 #define CONV2D_OP_AVGPOOL 3
 #define CONV2D_OP_COPY 4
+#define CONV2D_OP_DECONV 5
+#define CONV2D_OP_UPSAMPLE 6
+#define CONV2D_OP_CONCAT 7
+#define CONV2D_OP_UPSAMPLE_CONCAT 8
 
 typedef struct conv2d_op {
     int kind;
@@ -257,7 +326,8 @@ int conv2d_stack_graph_destroy(conv2d_graph *g);
  * valid until the thread's next call into the library. */
 const char *conv2d_last_error(void);
 
-/* ABI version of this header: 2 (1 plus the stack calls and the fused conv + max pool). */
+/* ABI version of this header: 3 (2 plus the transposed conv, upsample and concat calls and
+ * their stack ops; 2 added the stack calls and the fused conv + max pool). */
 int conv2d_abi_version(void);
 
 #ifdef __cplusplus

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     for name in names:
         assert hasattr(lib, name), name
     assert names == set(c2d.SIGNATURES)
-    assert c2d._load().conv2d_abi_version() == 2
+    assert c2d._load().conv2d_abi_version() == 3
 
 
 def test_out_dim():
@@ -156,3 +156,64 @@ def test_stack_check_names_the_bad_op():
     assert c2d.stack_plan([ok, pool, copy], 1) == "maxpool3x3s2"
     assert c2d.stack_plan([ok, pool, copy], 2) == "copy"
     assert c2d.stack_plan([ok, pool, copy], 0) == c2d.plan(1, 16, 16, 32, 32, 3, 3, 1, 1, 1, 0, c2d.DTYPE_BF16)
+
+
+def test_deconv_plan_and_argument_checks():
+    """Host-only: which kernels conv_transpose4x4s2 picks, and what it rejects."""
+    bf16, f16, f32 = c2d.DTYPE_BF16, c2d.DTYPE_F16, c2d.DTYPE_F32
+    nhwc, nchw = c2d.LAYOUT_NHWC, c2d.LAYOUT_NCHW
+    assert c2d.plan_deconv(1, 68, 120, 240, 5, 0, nchw, f16, f32) == \
+        "deconv4x4s2_pack+to_nhwc+deconv4x4s2_mfma f16 out f32"
+    assert c2d.plan_deconv(1, 64, 64, 256, 128, 1, nhwc, bf16) == "deconv4x4s2_pack+deconv4x4s2_mfma bf16"
+    assert c2d.plan_deconv(1, 8, 8, 12, 8, 1, nhwc, bf16) == "deconv4x4s2_direct bf16"  # Cin % 8 != 0
+    assert c2d.plan_deconv(1, 8, 8, 16, 8, 1, nhwc, f32) == "deconv4x4s2_direct f32"
+    # a channel-first input whose channel-last copy does not fit the 64 MiB scratch
+    assert c2d.plan_deconv(8, 256, 256, 64, 8, 0, nchw, bf16).startswith("deconv4x4s2_direct")
+    for args in [(1, 8, 8, 16, 8, 3, nhwc, bf16, bf16),             # PReLU: alpha is given by the plan stand-in
+                 ]:
+        assert c2d.plan_deconv(*args)
+    bad = [(0, 8, 8, 16, 8, 0, nhwc, bf16, bf16),                     # N = 0
+           (1, 8, 8, 16, 8, 0, 2, bf16, bf16),                        # layout
+           (1, 8, 8, 16, 8, 0, nhwc, bf16, f16),                      # out dtype neither x's nor fp32
+           (1, 8, 8, 16, 8, 1 | c2d.RES_BEFORE_ACT, nhwc, bf16, bf16),  # no residual here
+           (1, 8, 8, 16, 8, 9, nhwc, bf16, bf16)]                     # activation code
+    for args in bad:
+        with pytest.raises(c2d.Conv2dError) as e:
+            c2d.plan_deconv(*args)
+        assert e.value.code == c2d.EINVAL, args
+    with pytest.raises(c2d.Conv2dError) as e:
+        c2d.plan_deconv(1, 32768, 32768, 8, 8, 0, nhwc, bf16)
+    assert e.value.code == c2d.EUNSUPPORTED
+    lib = c2d._load()
+    P = ctypes.c_void_p
+    x, w, y = P(0x100000000), P(0x900000000), P(0x1100000000)
+    # PReLU without slopes, and y overlapping x (1x4x4x16 bf16 = 512 bytes)
+    assert lib.conv_transpose4x4s2(x, w, None, None, y, 1, 4, 4, 16, 8, 3, nhwc, bf16, bf16, None) == c2d.EINVAL
+    assert lib.conv_transpose4x4s2(x, w, None, None, P(0x100000000 + 256), 1, 4, 4, 16, 8, 0, nhwc, bf16, bf16,
+                                   None) == c2d.EINVAL
+    assert "overlaps" in c2d.last_error()
+
+
+def test_resample_ops_in_stack_check():
+    """Upsample and concat ops: valid shapes pass the host-only stack check; overlaps,
+    a missing second input and bad sizes are named by index."""
+    up = c2d.Op(c2d.OP_UPSAMPLE, 1 << 32, None, None, None, None, 9 << 32, 2, 10, 12, 32, 0, 0, 0, 0, 0, 0)
+    cat = c2d.Op(c2d.OP_CONCAT, 9 << 32, None, None, None, 17 << 32, 25 << 32, 2, 20, 24, 32, 16, 0, 0, 0, 0, 0)
+    upcat = c2d.Op(c2d.OP_UPSAMPLE_CONCAT, 1 << 32, None, None, None, 17 << 32, 33 << 32, 2, 10, 12, 32, 16,
+                   0, 0, 0, 0, 0)
+    dec = c2d.Op(c2d.OP_DECONV, 1 << 32, 41 << 32, None, None, None, 49 << 32, 2, 10, 12, 32, 16, 4, 4, 2, 1, 1)
+    assert c2d.stack_check([up, cat, upcat, dec]) == (c2d.OK, -1)
+    assert c2d.stack_plan([up, cat, upcat, dec], 0) == "upsample2x_vec16"
+    assert c2d.stack_plan([up, cat, upcat, dec], 1) == "concat_vec16"
+    assert c2d.stack_plan([up, cat, upcat, dec], 2) == "upsample2x_concat_vec16"
+    assert c2d.stack_plan([up, cat, upcat, dec], 3) == "deconv4x4s2_pack+deconv4x4s2_mfma bf16"
+    no_b = c2d.Op(c2d.OP_CONCAT, 9 << 32, None, None, None, None, 25 << 32, 2, 20, 24, 32, 16, 0, 0, 0, 0, 0)
+    assert c2d.stack_check([up, no_b]) == (c2d.EINVAL, 1)
+    zero_cb = c2d.Op(c2d.OP_CONCAT, 9 << 32, None, None, None, 17 << 32, 25 << 32, 2, 20, 24, 32, 0, 0, 0, 0, 0, 0)
+    assert c2d.stack_check([zero_cb]) == (c2d.EINVAL, 0)
+    # the upsampled output (2x20x24x32 bf16 = 61440 bytes) runs into the next buffer
+    clash = c2d.Op(c2d.OP_UPSAMPLE, 1 << 32, None, None, None, None, (1 << 32) + 4096, 2, 10, 12, 32, 0, 0, 0, 0,
+                   0, 0)
+    assert c2d.stack_check([clash]) == (c2d.EINVAL, 0)
+    odd = c2d.Op(c2d.OP_UPSAMPLE, 1 << 32, None, None, None, None, 9 << 32, 2, 10, 12, 5, 0, 0, 0, 0, 0, 0)
+    assert c2d.stack_plan([odd], 0) == "upsample2x_scalar"

@@ -14,6 +14,9 @@ from .inputs import (  # noqa: F401
     conv4_ifnet_block,
     conv5_resnet18d,
     conv_flops,
+    ifnet_deconv,
     random_conv_case,
+    random_deconv_case,
+    random_map,
     to_storage,
 )

@@ -246,3 +246,33 @@ def random_conv_case(seed: int, *, n, h, w, cin, cout, k, stride, pad, act, layo
         rshape = (n, oh, ow, cout) if layout == "nhwc" else (n, cout, oh, ow)
         r = to_storage(_normal(rng, rshape, 1.0), dtype)
     return x, spec, r
+
+
+def random_deconv_case(seed: int, *, n, h, w, cin, cout, act, layout, dtype, x_dist="normal"):
+    """One random 4x4 stride-2 transposed-conv layer: returns (x, w, bias, alpha-or-None).
+
+    x ~ N(0,1) (or U[0,1]) in ``layout``; w [Cin, Cout, 4, 4] He-normal with fan_in =
+    4*Cin (each output pixel takes 2x2 taps of every input channel); bias U[-0.1,0.1];
+    PReLU slope U[0,0.25]. Draw order: x, w, bias, slope.
+    """
+    rng = np.random.default_rng(seed)
+    xshape = (n, h, w, cin) if layout == "nhwc" else (n, cin, h, w)
+    xa = _normal(rng, xshape, 1.0) if x_dist == "normal" else _uniform(rng, xshape, 0.0, 1.0)
+    x = to_storage(xa, dtype)
+    wt = to_storage(_normal(rng, (cin, cout, 4, 4), 2.0 / (4 * cin)), dtype)
+    bias = torch.from_numpy(_uniform(rng, (cout,), -0.1, 0.1))
+    alpha = torch.from_numpy(_uniform(rng, (cout,), 0.0, 0.25)) if act == "prelu" else None
+    return x, wt, bias, alpha
+
+
+def ifnet_deconv(seed: int = 5, c: int = 240, h: int = 68, w: int = 120, cout: int = 5):
+    """The transposed conv that ends IFNet block 0 at a 1920x1088 frame: the stride-16
+    map [1, 240, 68, 120] (NCHW f16, N(0,1)) to the 5-channel stride-8 map (4 flow
+    channels and a mask), no activation; the output is kept in fp32 as framecast does."""
+    return random_deconv_case(seed, n=1, h=h, w=w, cin=c, cout=cout, act="none", layout="nchw", dtype="f16")
+
+
+def random_map(seed: int, shape, dtype: str) -> torch.Tensor:
+    """A map of N(0,1) values in the storage dtype (upsample and concat inputs)."""
+    rng = np.random.default_rng(seed)
+    return to_storage(_normal(rng, shape, 1.0), dtype)
