@@ -63,6 +63,10 @@ def parse():
                    help="run a conv and the max pool after it as two calls")
     p.add_argument("--workload", choices=list(WORKLOADS), default="resnet18d",
                    help="the backbone (default; the headline) or one of the other layer configs")
+    p.add_argument("--ops", action="store_true",
+                   help="instead of the backbone: time the transposed conv, upsample and concat calls "
+                        "at the pages' shapes (one JSON line with a row per call)")
+    p.add_argument("--ops-reps", type=int, default=50)
     return p.parse_args()
 
 
@@ -342,6 +346,80 @@ def write_traffic(src, copy_mib, plan):
     print(json.dumps(rec))
 
 
+def time_call(torch, fn, reps):
+    """Average duration (ms) of `reps` back-to-back calls of fn(stream) between one pair of
+    HIP events on the launch stream, behind a spin that covers the host's queueing."""
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        fn(stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    prefill(torch, ms=5.0)
+    e0.record(stream)
+    for _ in range(reps):
+        fn(stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def bench_ops(torch, dev, reps):
+    """The neck and block-end calls at the pages' shapes. Per call: algorithmic flops (a
+    transposed conv: 2 * output pixels * Cout * Cin * 4, the taps that reach an output; the
+    copies: none) and bytes (each input read once, the output written once), the average
+    launch time, and the fraction of the bounding roofline."""
+    import conv2d_bias_activation_amd as c2d
+    import workloads as wl
+
+    rows = []
+
+    def add(name, plan, fn, flops, nbytes):
+        ms = time_call(torch, fn, reps)
+        tf = flops / (ms * 1e-3) / 1e12 if flops else None
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        bound = "mfma" if flops and flops / nbytes >= PEAK_BF16_TFLOPS / PEAK_HBM_GBS * 1e3 else "hbm"
+        frac = tf / PEAK_BF16_TFLOPS if bound == "mfma" else gbs / PEAK_HBM_GBS
+        rows.append(dict(name=name, plan=plan, us=round(ms * 1e3, 2), gflop=round(flops / 1e9, 4),
+                         mb=round(nbytes / 1e6, 3), tflops=round(tf, 1) if tf else None, gbs=round(gbs, 1),
+                         bound=bound, frac=round(frac, 4)))
+
+    # IFNet block 0's transposed conv at a 1920x1088 frame (fp32 output, as framecast keeps it)
+    x, w, b, _ = wl.ifnet_deconv()
+    x, w, b = x.to(dev), w.to(dev), b.to(dev)
+    y = torch.empty(1, 5, 136, 240, dtype=torch.float32, device=dev)
+    flops = 2 * 136 * 240 * 5 * 240 * 4
+    nbytes = 2 * (x.numel() + w.numel()) + 4 * (b.numel() + y.numel())
+    add("ifnet_deconv_240to5_68x120_nchw_f16_out_f32",
+        c2d.plan_deconv(1, 68, 120, 240, 5, 0, c2d.LAYOUT_NCHW, c2d.DTYPE_F16, c2d.DTYPE_F32),
+        lambda st: c2d.conv_transpose4x4s2(x, w, b, layout="nchw", out_dtype=torch.float32, out=y, stream=st),
+        flops, nbytes)
+    # a decoder-sized transposed conv, channel-last bf16
+    x2, w2, b2, _ = wl.random_deconv_case(21, n=1, h=64, w=64, cin=256, cout=128, act="relu", layout="nhwc",
+                                          dtype="bf16")
+    x2, w2, b2 = x2.to(dev), w2.to(dev), b2.to(dev)
+    y2 = torch.empty(1, 128, 128, 128, dtype=torch.bfloat16, device=dev)
+    flops = 2 * 128 * 128 * 128 * 256 * 4
+    nbytes = 2 * (x2.numel() + w2.numel() + y2.numel()) + 4 * b2.numel()
+    add("deconv_256to128_64x64_nhwc_bf16_relu",
+        c2d.plan_deconv(1, 64, 64, 256, 128, 1, c2d.LAYOUT_NHWC, c2d.DTYPE_BF16),
+        lambda st: c2d.conv_transpose4x4s2(x2, w2, b2, act="relu", out=y2, stream=st), flops, nbytes)
+    # the CCFM top-down joins at a 640x640 image, batch 4: [lateral up 2x, backbone] -> 512 ch
+    for hw in (20, 40):
+        a = wl.random_map(6, (4, hw, hw, 256), "bf16").to(dev)
+        bb = wl.random_map(7, (4, 2 * hw, 2 * hw, 256), "bf16").to(dev)
+        yy = torch.empty(4, 2 * hw, 2 * hw, 512, dtype=torch.bfloat16, device=dev)
+        up = torch.empty(4, 2 * hw, 2 * hw, 256, dtype=torch.bfloat16, device=dev)
+        nb = 2 * (a.numel() + bb.numel() + yy.numel())
+        add(f"upsample2x_concat_4x{hw}x{hw}x256+4x{2 * hw}x{2 * hw}x256_bf16", "upsample2x_concat_vec16",
+            lambda st, a=a, bb=bb, yy=yy: c2d.upsample2x_concat(a, bb, out=yy, stream=st), 0, nb)
+        add(f"upsample2x_4x{hw}x{hw}x256_bf16", "upsample2x_vec16",
+            lambda st, a=a, up=up: c2d.upsample_nearest2x(a, out=up, stream=st), 0, 2 * (a.numel() + up.numel()))
+        add(f"concat_4x{2 * hw}x{2 * hw}x(256+256)_bf16", "concat_vec16",
+            lambda st, up=up, bb=bb, yy=yy: c2d.concat_channels(up, bb, out=yy, stream=st), 0,
+            2 * (up.numel() + bb.numel() + yy.numel()))
+    return rows
+
+
 def main():
     args = parse()
     if args.traffic_from:
@@ -363,6 +441,12 @@ def main():
         for _ in range(10):
             dst.copy_(src)
         torch.cuda.synchronize()
+        return
+    if args.ops:
+        rows = bench_ops(torch, dev, args.ops_reps)
+        print(json.dumps({"ops": rows, "reps": args.ops_reps,
+                          "note": "per-launch averages of back-to-back calls; inputs stay warm in the "
+                                  "256 MB last-level cache between calls"}), flush=True)
         return
     builder, config_name = WORKLOADS[args.workload]
     work = getattr(wl, builder)()

@@ -485,13 +485,11 @@ int check_conv_pool(const void *x, const void *w, const float *alpha, const void
 }
 
 // Transposed conv 4x4/s2/p1: the matrix-core kernel for 16-bit types with Cin % 8 == 0
-// (weights repacked into the scratch, and a channel-first input copied to channel-last
-// there too), the direct kernel otherwise.
+// (weights repacked into the scratch first; a channel-first input is transposed while
+// it is staged), the direct kernel otherwise.
 struct DeconvPlan {
     bool mfma;
-    bool x_copy;   // channel-first input copied to channel-last in the scratch
     bool out_f32;  // y in fp32 (16-bit input)
-    size_t x_off;  // byte offset of the input copy in the scratch (after the packed weights)
 };
 
 int check_deconv(const void *x, const void *w, const float *bias, const float *alpha, const void *y, int N, int H,
@@ -533,12 +531,11 @@ int check_deconv(const void *x, const void *w, const float *bias, const float *a
     *p = DeconvPlan{};
     p->out_f32 = out_dtype == CONV2D_DTYPE_F32 && dtype != CONV2D_DTYPE_F32;
     const bool nchw = layout == CONV2D_LAYOUT_NCHW;
-    const size_t wp_bytes = round256((size_t)16 * a->CoP * Cin * eb);
-    const size_t x_bytes = nchw ? round256((size_t)xe * eb) : 0;
-    p->x_off = wp_bytes;
-    p->x_copy = nchw;
-    p->mfma = dtype != CONV2D_DTYPE_F32 && (Cin % 8) == 0 && wp_bytes + x_bytes <= kScratchBytes &&
-              (nchw ? N <= 65535 : aligned16(x));
+    const size_t wp_bytes = (size_t)16 * a->CoP * ((Cin + 63) / 64 * 64) * eb;
+    p->mfma = dtype != CONV2D_DTYPE_F32 && (Cin % 8) == 0 && wp_bytes <= kScratchBytes && (nchw || aligned16(x)) &&
+              xe * eb < (1ll << 31);
+    a->x_bytes = (uint32_t)(xe * eb < (1ll << 31) ? xe * eb : 0);
+    a->wp_bytes = (uint32_t)wp_bytes;
     return CONV2D_OK;
 }
 
@@ -763,11 +760,6 @@ int launch_op(const OpPlan &o, hipStream_t st) {
         DeconvArgs a = o.da;
         a.wp = scratch;
         e = launch_deconv_pack(a.w, scratch, a.Cin, a.Cout, a.CoP, o.dtype, st);
-        if (e == hipSuccess && o.dp.x_copy) {
-            void *xs = reinterpret_cast<char *>(scratch) + o.dp.x_off;
-            e = launch_nchw_to_nhwc(a.x, xs, a.N, a.Cin, a.H * a.W, o.dtype, st);
-            a.x = xs;
-        }
         if (e == hipSuccess) e = launch_deconv_mfma(a, o.dtype, o.dp.out_f32, nchw, st);
         return e == hipSuccess ? CONV2D_OK : hip_fail(e, "conv_transpose4x4s2 launch");
     }
@@ -814,8 +806,9 @@ int describe_op(const OpPlan &o, char *buf, int cap) {
         break;
     case CONV2D_OP_DECONV:
         if (o.dp.mfma)
-            snprintf(tmp, sizeof tmp, "deconv4x4s2_pack+%sdeconv4x4s2_mfma %s%s", o.dp.x_copy ? "to_nhwc+" : "",
-                     dtype_name(o.dtype), o.dp.out_f32 ? " out f32" : "");
+            snprintf(tmp, sizeof tmp, "deconv4x4s2_pack+deconv4x4s2_mfma_%s %s%s",
+                     o.layout == CONV2D_LAYOUT_NCHW ? "nchw" : "nhwc", dtype_name(o.dtype),
+                     o.dp.out_f32 ? " out f32" : "");
         else
             snprintf(tmp, sizeof tmp, "deconv4x4s2_direct %s%s", dtype_name(o.dtype), o.dp.out_f32 ? " out f32" : "");
         break;

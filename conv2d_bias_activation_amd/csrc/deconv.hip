@@ -8,10 +8,11 @@
 // parity classes (py, px) is a 2x2 stride-1 convolution over the input, tap (ty, tx)
 // reading input pixel (j - 1 + py + ty, i - 1 + px + tx) with weight
 // w[ci][co][3 - py - 2*ty][3 - px - 2*tx]. The matrix-core kernel runs exactly that:
-// the weights are first repacked (once per call, into the library scratch) to
-// wp[class][co][tap][ci] with ci contiguous, so each class is a GEMM with K = 4*Cin
-// whose B operand rows are 16-byte runs; a workgroup stages three input rows of a
-// 34-pixel strip once and its four waves (one per class) read shifted views of it.
+// each class is a GEMM with K = 4*Cin over 64-channel chunks. The weights are first
+// repacked (once per call, into the library scratch) in the order in which the kernel's
+// lanes take them as MFMA B operands, so that each wave-wide weight load reads one
+// contiguous kilobyte; a workgroup stages three input rows of a 34-pixel strip once
+// and its four waves (one per class) read shifted views of it.
 #include "common.hpp"
 #include "igemm_common.hpp"
 #include "kernels.hpp"
@@ -21,44 +22,77 @@ namespace c2d {
 namespace {
 
 constexpr int DC_TW = 32;           // input columns per tile: 64 output columns, 2 output rows
-constexpr int DC_KC = 32;           // input channels per staged chunk
+constexpr int DC_KC = 64;           // input channels per staged chunk
 constexpr int DC_SPX = DC_TW + 2;   // staged columns i0 - 1 .. i0 + 32
-constexpr int DC_PS = 40;           // LDS elements per staged pixel: 80 bytes, an odd number of
+constexpr int DC_PS = DC_KC + 8;    // LDS elements per staged pixel: 144 bytes, an odd number of
                                     // 16-byte slots, so 32 lanes reading 32 pixels hit distinct banks
 constexpr int DC_BUF = 3 * DC_SPX * DC_PS;
-constexpr int DC_VECS = 3 * DC_SPX * (DC_KC / 8);  // 16-byte vectors per staged chunk (408)
-constexpr int DC_OLD = 2 * DC_TW + 2;              // output tile row in LDS: 64 columns + 2 pad
+constexpr int DC_VECS = 3 * DC_SPX * (DC_KC / 8);   // 16-byte vectors per chunk, channel-last (816)
+constexpr int DC_VQ = (DC_VECS + 255) / 256;        // per thread (4)
+constexpr int DC_ELEMS = 3 * DC_SPX * DC_KC;        // elements per chunk, channel-first (6528)
+constexpr int DC_EQ = (DC_ELEMS + 255) / 256;       // per thread (26)
+constexpr int DC_KS = DC_KC / 16;                   // 16-deep MFMA steps per tap and chunk
+// Staging lanes past the chunk's last vector or element store into a pad after the
+// buffer, so every lane stores and no load is sunk into a branch (where its wait would
+// be vmcnt(0)).
+constexpr int DC_PAD = (256 * DC_VQ - DC_VECS) * 8 > 256 * DC_EQ - DC_ELEMS ? (256 * DC_VQ - DC_VECS) * 8
+                                                                             : 256 * DC_EQ - DC_ELEMS;
+constexpr int DC_BUFA = DC_BUF + DC_PAD;  // allocated elements per buffer
+constexpr int DC_OLD = 2 * DC_TW + 2;               // output tile row in LDS: 64 columns + 2 pad
 
 template <typename TO> __device__ __forceinline__ TO out_cast(float v) { return from_f32<TO>(v); }
 
+// Buffer resource over `bytes` bytes: a load at an offset past the end returns zero, so
+// padding taps and channel tails are loads like any other (no branch around them, which
+// would make the compiler wait for every load in flight at the join).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_bytes(const void *p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (int)bytes, 0x00020000);
+}
+constexpr uint32_t kOob = 0xFFFFFFF0u;  // an offset past the end of any buffer under 2^31 bytes
+
 }  // namespace
 
-// w[ci][co][ky][kx] -> wp[cls][co][t][ci], cls = 2*py + px, t = 2*ty + tx, with
-// ky = 3 - py - 2*ty and kx = 3 - px - 2*tx; rows co >= Cout (up to CoP) are zero.
+// w[ci][co][ky][kx] -> wp in MFMA operand order: for class cls = 2*py + px, 32-channel
+// output block cob, 64-channel input chunk c, tap t = 2*ty + tx (ky = 3 - py - 2*ty,
+// kx = 3 - px - 2*tx) and 16-deep step ks, one 1 KiB run of 64 lanes x 8 channels:
+// lane (h << 5) | col holds w[ci][co] for co = 32*cob + col and
+// ci = 64*c + 16*ks + 8*h .. +8. Channels past Cin and outputs past Cout are zero, so
+// the kernel's weight loads need no bounds. One thread per (co, ci) pair of the padded
+// ranges reads that pair's 16 contiguous taps.
 template <typename T>
 __global__ __launch_bounds__(256) void deconv_pack_kernel(const T *__restrict__ w, T *__restrict__ wp, int Cin,
-                                                          int Cout, int CoP) {
-    const long long total = 16ll * CoP * Cin;
-    for (long long i = blockIdx.x * 256ll + threadIdx.x; i < total; i += (long long)gridDim.x * 256) {
-        const int ci = (int)(i % Cin);
-        long long r = i / Cin;
-        const int t = (int)(r & 3);
-        r >>= 2;
-        const int co = (int)(r % CoP);
-        const int cls = (int)(r / CoP);
-        const int py = cls >> 1, px = cls & 1, ty = t >> 1, tx = t & 1;
-        const int ky = 3 - py - 2 * ty, kx = 3 - px - 2 * tx;
-        wp[i] = co < Cout ? w[((size_t)ci * Cout + co) * 16 + ky * 4 + kx] : from_f32<T>(0.0f);
-    }
+                                                          int Cout, int CoP, int CinP) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= CoP * CinP) return;
+    const int ci = i % CinP, co = i / CinP;
+    const bool in = ci < Cin && co < Cout;
+    T tap[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) tap[k] = in ? w[((size_t)ci * Cout + co) * 16 + k] : from_f32<T>(0.0f);
+    const int cob = co >> 5, col = co & 31;
+    const int c = ci >> 6, ks = (ci >> 4) & 3, h = (ci >> 3) & 1, e = ci & 7;
+    const int nch = CinP >> 6, ncob = CoP >> 5;
+#pragma unroll
+    for (int cls = 0; cls < 4; ++cls)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int py = cls >> 1, px = cls & 1, ty = t >> 1, tx = t & 1;
+            const int ky = 3 - py - 2 * ty, kx = 3 - px - 2 * tx;
+            const size_t run = (((size_t)(cls * ncob + cob) * nch + c) * 4 + t) * 4 + ks;
+            wp[run * 512 + ((h << 5) | col) * 8 + e] = tap[ky * 4 + kx];
+        }
 }
 
-// Channel-last 16-bit input (Cin % 8 == 0, 16-byte aligned), packed weights. Block: 4
+// 16-bit input with Cin % 8 == 0 (channel-last: 16-byte aligned; channel-first: read
+// straight from the planes and transposed while staging), packed weights. Block: 4
 // waves, wave = parity class; tile = input row j of image n, input columns i0 .. i0+31,
-// output channels co0 .. co0+31 (blockIdx.y).
-template <typename T, typename TO, bool NCHW_OUT>
+// output channels co0 .. co0+31 (blockIdx.y). The K loop runs over 64-channel chunks
+// with the next chunk's input and weight loads in flight during the current chunk's
+// products.
+template <typename T, typename TO, bool NCHW>
 __global__ __launch_bounds__(256) void deconv_mfma_kernel(DeconvArgs a) {
     typedef typename Mfma32<T>::vec vec;
-    __shared__ __attribute__((aligned(16))) T sx[2][DC_BUF];
+    __shared__ __attribute__((aligned(16))) T sx[2][DC_BUFA];
     __shared__ float so[32][2][DC_OLD];
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -73,69 +107,104 @@ __global__ __launch_bounds__(256) void deconv_mfma_kernel(DeconvArgs a) {
     const int co0 = blockIdx.y * 32;
     const T *__restrict__ x = static_cast<const T *>(a.x);
 
-    // staging of one chunk: 3 rows x 34 pixels x 4 vectors of 8 channels, zero outside
-    // the image and past Cin
-    u32x4 st[2];
+    // staging registers of one chunk: 3 rows x 34 pixels x 64 channels, zero outside the
+    // image and past Cin
+    u32x4 sv[NCHW ? 1 : DC_VQ];
+    T se[NCHW ? DC_EQ : 1];
+    const __amdgpu_buffer_rsrc_t rx = rsrc_bytes(x, a.x_bytes);
     auto load_chunk = [&](int c0) {
+        if constexpr (NCHW) {
+            // element e: pixel fastest (coalesced along the plane row), then row, channel
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int idx = tid + 256 * q;
-            const int r = idx / (DC_SPX * 4), rem = idx - r * (DC_SPX * 4);
-            const int p = rem >> 2, cv = rem & 3;
-            const int iy = j - 1 + r, ix = i0 - 1 + p, ci = c0 + cv * 8;
-            const bool ok = idx < DC_VECS && (unsigned)iy < (unsigned)H && (unsigned)ix < (unsigned)W && ci < Cin;
-            st[q] = ok ? *reinterpret_cast<const u32x4 *>(x + (((size_t)n * H + iy) * W + ix) * Cin + ci)
-                       : u32x4{0u, 0u, 0u, 0u};
+            for (int q = 0; q < DC_EQ; ++q) {
+                const int e = tid + 256 * q;
+                const int p = e % DC_SPX, rc = e / DC_SPX;
+                const int r = rc % 3, cl = rc / 3;
+                const int iy = j - 1 + r, ix = i0 - 1 + p, ci = c0 + cl;
+                const bool ok = e < DC_ELEMS && (unsigned)iy < (unsigned)H && (unsigned)ix < (unsigned)W && ci < Cin;
+                const uint32_t off = ok ? ((((uint32_t)n * Cin + ci) * H + iy) * W + ix) * 2u : kOob;
+                const unsigned short v = __builtin_amdgcn_raw_buffer_load_b16(rx, (int)off, 0, 0);
+                __builtin_memcpy(&se[q], &v, 2);
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < DC_VQ; ++q) {
+                const int idx = tid + 256 * q;
+                const int r = idx / (DC_SPX * 8), rem = idx - r * (DC_SPX * 8);
+                const int p = rem >> 3, cv = rem & 7;
+                const int iy = j - 1 + r, ix = i0 - 1 + p, ci = c0 + cv * 8;
+                const bool ok = idx < DC_VECS && (unsigned)iy < (unsigned)H && (unsigned)ix < (unsigned)W && ci < Cin;
+                const uint32_t off = ok ? ((((uint32_t)n * H + iy) * W + ix) * Cin + ci) * 2u : kOob;
+                sv[q] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)off, 0, 0);
+            }
         }
     };
     auto store_chunk = [&](int buf) {
+        if constexpr (NCHW) {
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int idx = tid + 256 * q;
-            if (idx < DC_VECS) {
-                const int r = idx / (DC_SPX * 4), rem = idx - r * (DC_SPX * 4);
-                const int p = rem >> 2, cv = rem & 3;
-                *reinterpret_cast<u32x4 *>(&sx[buf][(r * DC_SPX + p) * DC_PS + cv * 8]) = st[q];
+            for (int q = 0; q < DC_EQ; ++q) {
+                const int e = tid + 256 * q;
+                const int p = e % DC_SPX, rc = e / DC_SPX;
+                const int r = rc % 3, cl = rc / 3;
+                sx[buf][e < DC_ELEMS ? (r * DC_SPX + p) * DC_PS + cl : DC_BUF + (e - DC_ELEMS)] = se[q];
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < DC_VQ; ++q) {
+                const int idx = tid + 256 * q;
+                const int r = idx / (DC_SPX * 8), rem = idx - r * (DC_SPX * 8);
+                const int p = rem >> 3, cv = rem & 7;
+                const int at = idx < DC_VECS ? (r * DC_SPX + p) * DC_PS + cv * 8 : DC_BUF + (idx - DC_VECS) * 8;
+                *reinterpret_cast<u32x4 *>(&sx[buf][at]) = sv[q];
             }
         }
     };
 
     const int col = lane & 31, kq = (lane >> 5) * 8;
-    const T *__restrict__ wrow =
-        static_cast<const T *>(a.wp) + ((size_t)((2 * py + px) * a.CoP + co0 + col) * 4) * Cin;
+    // B operands of one chunk: tap tp, 16-deep step ks; this lane's 16 bytes of each
+    // 1 KiB run (the past-the-end prefetch after the last chunk reads zero)
+    const __amdgpu_buffer_rsrc_t rw = rsrc_bytes(a.wp, a.wp_bytes);
+    const int nchp = (Cin + DC_KC - 1) / DC_KC;
+    const uint32_t wbase = (uint32_t)(((2 * py + px) * (a.CoP >> 5) + blockIdx.y) * nchp) * (16u * 1024u) + lane * 16u;
+    u32x4 bw[4 * DC_KS];
+    auto load_b = [&](int c) {
+        const uint32_t cb = wbase + (uint32_t)c * (16u * 1024u);
+#pragma unroll
+        for (int i = 0; i < 4 * DC_KS; ++i)
+            bw[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(c < nchp ? cb + i * 1024u : kOob), 0, 0);
+    };
     f32x16 acc;
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
 
     const int nch = (Cin + DC_KC - 1) / DC_KC;
     load_chunk(0);
+    load_b(0);
     store_chunk(0);
     __syncthreads();
     for (int c = 0; c < nch; ++c) {
         const int c0 = c * DC_KC;
-        if (c + 1 < nch) load_chunk(c0 + DC_KC);
-        vec bw[4][2];
+        // this chunk's weights leave the prefetch registers before the next loads land
+        // there; the next chunk's loads are issued unconditionally (past the last chunk
+        // every channel is out of range and reads zero)
+        vec bcur[4 * DC_KS];
 #pragma unroll
-        for (int tp = 0; tp < 4; ++tp)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int ci = c0 + h * 16 + kq;
-                u32x4 v = ci < Cin ? *reinterpret_cast<const u32x4 *>(wrow + tp * Cin + ci) : u32x4{0u, 0u, 0u, 0u};
-                __builtin_memcpy(&bw[tp][h], &v, 16);
-            }
+        for (int i = 0; i < 4 * DC_KS; ++i) __builtin_memcpy(&bcur[i], &bw[i], 16);
+        load_chunk(c0 + DC_KC);
+        load_b(c + 1);
         const T *sb = sx[c & 1];
 #pragma unroll
         for (int tp = 0; tp < 4; ++tp) {
             const int ty = tp >> 1, tx = tp & 1;
             const T *pa = sb + ((py + ty) * DC_SPX + col + px + tx) * DC_PS + kq;
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
+            for (int ks = 0; ks < DC_KS; ++ks) {
                 vec av;
-                __builtin_memcpy(&av, pa + h * 16, 16);
-                acc = Mfma32<T>::run(av, bw[tp][h], acc);
+                __builtin_memcpy(&av, pa + ks * 16, 16);
+                acc = Mfma32<T>::run(av, bcur[tp * DC_KS + ks], acc);
             }
         }
-        if (c + 1 < nch) store_chunk((c + 1) & 1);
+        store_chunk((c + 1) & 1);
         __syncthreads();
     }
 
@@ -154,7 +223,7 @@ __global__ __launch_bounds__(256) void deconv_mfma_kernel(DeconvArgs a) {
     TO *__restrict__ y = static_cast<TO *>(a.y);
     const int OH = 2 * H, OW = 2 * W;
     const int oc0 = 2 * i0;
-    if constexpr (NCHW_OUT) {
+    if constexpr (NCHW) {
 #pragma unroll 4
         for (int it = 0; it < 16; ++it) {
             const int e = tid + 256 * it;
@@ -228,11 +297,10 @@ __global__ __launch_bounds__(256) void deconv_direct_kernel(DeconvArgs a) {
 
 template <typename T>
 static hipError_t pack_t(const void *w, void *wp, int Cin, int Cout, int CoP, hipStream_t st) {
-    const long long total = 16ll * CoP * Cin;
-    long long blocks = (total + 255) / 256;
-    if (blocks > 4096) blocks = 4096;
-    return launch_kernel(deconv_pack_kernel<T>, dim3((unsigned)blocks), dim3(256), 0, st, static_cast<const T *>(w),
-                         static_cast<T *>(wp), Cin, Cout, CoP);
+    const int CinP = (Cin + DC_KC - 1) / DC_KC * DC_KC;
+    const long long total = (long long)CoP * CinP;
+    return launch_kernel(deconv_pack_kernel<T>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
+                         static_cast<const T *>(w), static_cast<T *>(wp), Cin, Cout, CoP, CinP);
 }
 
 hipError_t launch_deconv_pack(const void *w, void *wp, int Cin, int Cout, int CoP, int dtype, hipStream_t st) {
@@ -247,19 +315,19 @@ hipError_t launch_deconv_pack(const void *w, void *wp, int Cin, int Cout, int Co
 }
 
 template <typename T, typename TO>
-static hipError_t mfma_t(const DeconvArgs &a, bool nchw_out, hipStream_t st) {
+static hipError_t mfma_t(const DeconvArgs &a, bool nchw, hipStream_t st) {
     const long long tiles = (long long)a.N * a.H * ((a.W + DC_TW - 1) / DC_TW);
     dim3 grid((unsigned)tiles, (unsigned)(a.CoP / 32));
-    if (nchw_out) return launch_kernel(deconv_mfma_kernel<T, TO, true>, grid, dim3(256), 0, st, a);
+    if (nchw) return launch_kernel(deconv_mfma_kernel<T, TO, true>, grid, dim3(256), 0, st, a);
     return launch_kernel(deconv_mfma_kernel<T, TO, false>, grid, dim3(256), 0, st, a);
 }
 
-hipError_t launch_deconv_mfma(const DeconvArgs &a, int dtype, bool out_f32, bool nchw_out, hipStream_t st) {
+hipError_t launch_deconv_mfma(const DeconvArgs &a, int dtype, bool out_f32, bool nchw, hipStream_t st) {
     switch (dtype) {
     case CONV2D_DTYPE_BF16:
-        return out_f32 ? mfma_t<bf16, float>(a, nchw_out, st) : mfma_t<bf16, bf16>(a, nchw_out, st);
+        return out_f32 ? mfma_t<bf16, float>(a, nchw, st) : mfma_t<bf16, bf16>(a, nchw, st);
     case CONV2D_DTYPE_F16:
-        return out_f32 ? mfma_t<f16, float>(a, nchw_out, st) : mfma_t<f16, f16>(a, nchw_out, st);
+        return out_f32 ? mfma_t<f16, float>(a, nchw, st) : mfma_t<f16, f16>(a, nchw, st);
     default:
         return hipErrorInvalidValue;
     }

@@ -109,29 +109,28 @@ hipError_t launch_avgpool(const void *x, void *y, int N, int H, int W, int C, bo
 struct DeconvArgs {
     const void *x;       // [N,H,W,Cin] (channel-last kernel) or the caller's layout (direct kernel)
     const void *w;       // caller's [Cin][Cout][4][4] (direct kernel)
-    const void *wp;      // packed [4 classes][CoP][4 taps][Cin] (matrix-core kernel)
+    const void *wp;      // packed in MFMA operand order, 16 * CoP * ceil(Cin/64)*64 elements
     const float *bias;   // may be null
     const float *alpha;  // null unless PReLU
     void *y;
     int N, H, W, Cin, Cout;
     int CoP;  // Cout rounded up to 32
     int act;  // CONV2D_ACT_*
+    uint32_t x_bytes, wp_bytes;  // buffer extents (matrix-core kernel; both under 2^31)
 };
 
-// w [Cin][Cout][4][4] -> wp [4][CoP][4][Cin] (16-bit types), per output parity class the
-// two-by-two taps with input channels contiguous; rows past Cout are zero.
+// w [Cin][Cout][4][4] -> wp (16-bit types, 16 * CoP * ceil(Cin/64)*64 elements): per
+// output parity class, 32-channel output block, 64-channel input chunk, tap and 16-deep
+// step, the 64 lanes' MFMA B operands in lane order; padding is zero.
 hipError_t launch_deconv_pack(const void *w, void *wp, int Cin, int Cout, int CoP, int dtype, hipStream_t st);
 
-// Matrix-core kernel: channel-last 16-bit x with Cin % 8 == 0, x and wp 16-byte aligned,
-// x and y under 2^31 elements; y in the channel-last or (nchw_out) channel-first layout,
-// in the input's type or (out_f32) fp32.
-hipError_t launch_deconv_mfma(const DeconvArgs &a, int dtype, bool out_f32, bool nchw_out, hipStream_t st);
+// Matrix-core kernel: 16-bit x with Cin % 8 == 0 (channel-last: 16-byte aligned), wp
+// 16-byte aligned, x and wp under 2^31 bytes, y under 2^31 elements; x and y both channel-last or (nchw) both
+// channel-first; y in the input's type or (out_f32) fp32.
+hipError_t launch_deconv_mfma(const DeconvArgs &a, int dtype, bool out_f32, bool nchw, hipStream_t st);
 
 // Any layout and type, one thread per output (weights in the caller's layout).
 hipError_t launch_deconv_direct(const DeconvArgs &a, int dtype, bool out_f32, bool nchw, hipStream_t st);
-
-// Channel-first 16-bit map to channel-last (N planes of C x HW).
-hipError_t launch_nchw_to_nhwc(const void *x, void *y, int N, int C, int HW, int dtype, hipStream_t st);
 
 // y = concat(up ? upsample2x(a) : a, b) along channels; a alone (Cb = 0, b unused) is
 // the plain upsample. H, W: y's size (even when up). vec: channel-last with Ca and Cb

@@ -28,8 +28,8 @@
  *    and keeps until the process ends. It holds the fp32 partial sums of split-K
  *    calls, the channel-last copies of x and w of 16-bit channel-first calls and
  *    the unpooled conv output of conv2d_fused_maxpool3x3s2 calls that run as two
- *    kernels, and the repacked weights (plus a channel-last input copy) of
- *    conv_transpose4x4s2 calls on the matrix cores.
+ *    kernels, and the repacked weights of conv_transpose4x4s2 calls on the matrix
+ *    cores.
  *    Such calls on one device all use that buffer: callers that run conv2d_fused
  *    on several streams of one device at the same time must serialise those
  *    calls. (Under HIP graph capture, make one call on each device before
@@ -187,11 +187,11 @@ int avgpool2x2(const void *x, void *y, int N, int H, int W, int C, int layout, i
  *        (framecast keeps the deconv output in fp32 under f16 storage)
  *
  * Accumulation is fp32 in any order, rounded once to out_dtype. 16-bit inputs with
- * Cin % 8 == 0 run on the matrix cores: the weights are first repacked into the
- * library's per-device scratch buffer (16 * ceil(Cout/32)*32 * Cin elements) and a
- * channel-first input is copied to channel-last there too; those buffers must fit the
- * 64 MiB scratch, else (and for fp32 or other Cin) a direct kernel on the vector ALUs
- * runs instead. Shares the scratch as conv2d_fused does. Errors as conv2d_fused.
+ * Cin % 8 == 0 (channel-last x 16-byte aligned) run on the matrix cores: the weights
+ * are first repacked into the library's per-device scratch buffer
+ * (16 * ceil(Cout/32)*32 * ceil(Cin/64)*64 elements, which must fit its 64 MiB); otherwise (and
+ * for fp32) a direct kernel on the vector ALUs runs. Shares the scratch as
+ * conv2d_fused does. Errors as conv2d_fused.
  */
 int conv_transpose4x4s2(const void *x, const void *w, const float *bias, const float *alpha, void *y, int N, int H,
                         int W, int Cin, int Cout, int act, int layout, int dtype, int out_dtype, void *stream);

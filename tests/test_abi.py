@@ -163,12 +163,15 @@ def test_deconv_plan_and_argument_checks():
     bf16, f16, f32 = c2d.DTYPE_BF16, c2d.DTYPE_F16, c2d.DTYPE_F32
     nhwc, nchw = c2d.LAYOUT_NHWC, c2d.LAYOUT_NCHW
     assert c2d.plan_deconv(1, 68, 120, 240, 5, 0, nchw, f16, f32) == \
-        "deconv4x4s2_pack+to_nhwc+deconv4x4s2_mfma f16 out f32"
-    assert c2d.plan_deconv(1, 64, 64, 256, 128, 1, nhwc, bf16) == "deconv4x4s2_pack+deconv4x4s2_mfma bf16"
+        "deconv4x4s2_pack+deconv4x4s2_mfma_nchw f16 out f32"
+    assert c2d.plan_deconv(1, 64, 64, 256, 128, 1, nhwc, bf16) == "deconv4x4s2_pack+deconv4x4s2_mfma_nhwc bf16"
     assert c2d.plan_deconv(1, 8, 8, 12, 8, 1, nhwc, bf16) == "deconv4x4s2_direct bf16"  # Cin % 8 != 0
     assert c2d.plan_deconv(1, 8, 8, 16, 8, 1, nhwc, f32) == "deconv4x4s2_direct f32"
-    # a channel-first input whose channel-last copy does not fit the 64 MiB scratch
-    assert c2d.plan_deconv(8, 256, 256, 64, 8, 0, nchw, bf16).startswith("deconv4x4s2_direct")
+    # packed weights over the 64 MiB scratch: 16 * 2048 * 1024 bf16 = 64 MiB fits, one more
+    # output block or input chunk does not
+    assert c2d.plan_deconv(1, 8, 8, 1024, 2048, 0, nhwc, bf16).startswith("deconv4x4s2_pack")
+    assert c2d.plan_deconv(1, 8, 8, 1024, 2049, 0, nhwc, bf16).startswith("deconv4x4s2_direct")
+    assert c2d.plan_deconv(1, 8, 8, 1032, 2048, 0, nhwc, bf16).startswith("deconv4x4s2_direct")
     for args in [(1, 8, 8, 16, 8, 3, nhwc, bf16, bf16),             # PReLU: alpha is given by the plan stand-in
                  ]:
         assert c2d.plan_deconv(*args)
@@ -206,7 +209,7 @@ def test_resample_ops_in_stack_check():
     assert c2d.stack_plan([up, cat, upcat, dec], 0) == "upsample2x_vec16"
     assert c2d.stack_plan([up, cat, upcat, dec], 1) == "concat_vec16"
     assert c2d.stack_plan([up, cat, upcat, dec], 2) == "upsample2x_concat_vec16"
-    assert c2d.stack_plan([up, cat, upcat, dec], 3) == "deconv4x4s2_pack+deconv4x4s2_mfma bf16"
+    assert c2d.stack_plan([up, cat, upcat, dec], 3) == "deconv4x4s2_pack+deconv4x4s2_mfma_nhwc bf16"
     no_b = c2d.Op(c2d.OP_CONCAT, 9 << 32, None, None, None, None, 25 << 32, 2, 20, 24, 32, 16, 0, 0, 0, 0, 0)
     assert c2d.stack_check([up, no_b]) == (c2d.EINVAL, 1)
     zero_cb = c2d.Op(c2d.OP_CONCAT, 9 << 32, None, None, None, 17 << 32, 25 << 32, 2, 20, 24, 32, 0, 0, 0, 0, 0, 0)
