@@ -240,12 +240,29 @@ def time_layers(torch, net, reps):
     return out
 
 
-def kernel_source_hash():
-    h = hashlib.sha256()
+# Source files whose text compiles into each kernel family's device code (matched on the
+# start of the plan name); the declarations-only kernels.hpp is left out. A traffic record
+# is only used while these files are unchanged.
+KERNEL_SOURCES = [
+    ("igemm_nhwc_pipe", ["conv_igemm_nhwc.hip", "igemm_common.hpp", "common.hpp"]),
+    ("halo3x3", ["conv_halo.hip", "igemm_common.hpp", "common.hpp"]),
+    ("stem3x3", ["conv_stem.hip", "igemm_common.hpp", "common.hpp"]),
+    ("igemm_", ["conv_igemm.hip", "igemm_common.hpp", "common.hpp"]),
+    ("maxpool", ["pool.hip", "common.hpp"]),
+    ("avgpool", ["pool.hip", "common.hpp"]),
+]
+
+
+def kernel_source_hash(plan=None):
     csrc = os.path.join(ROOT, "conv2d_bias_activation_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".hpp")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+    files = sorted(f for f in os.listdir(csrc) if f.endswith((".hip", ".hpp")))
+    for prefix, fs in KERNEL_SOURCES:
+        if plan and plan.startswith(prefix):
+            files = fs
+            break
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -259,10 +276,8 @@ def measured_traffic(plan, launches_bytes):
         rec = json.load(open(path))
     except (OSError, ValueError):
         return None
-    if rec.get("source_hash") != kernel_source_hash():
-        return None
     k = rec.get("kernels", {}).get(plan)
-    if not k:
+    if not k or k.get("source_hash") != kernel_source_hash(plan):
         return None
     return k.get("bytes_per_launch")
 
@@ -335,10 +350,10 @@ def write_traffic(src, copy_mib, plan):
     kname, kf = busiest(os.path.join(src, "fetch"), "FETCH_SIZE")
     _, kw = busiest(os.path.join(src, "write"), "WRITE_SIZE")
     sf, sw = known / cf, known / cw
-    rec = dict(source_hash=kernel_source_hash(),
-               copy=dict(mib=copy_mib, fetch_kib=round(cf, 1), write_kib=round(cw, 1),
+    rec = dict(copy=dict(mib=copy_mib, fetch_kib=round(cf, 1), write_kib=round(cw, 1),
                          fetch_scale=round(sf, 4), write_scale=round(sw, 4)),
-               kernels={plan: dict(kernel=kname, fetch_kib=round(kf, 1), write_kib=round(kw, 1),
+               kernels={plan: dict(kernel=kname, source_hash=kernel_source_hash(plan), fetch_kib=round(kf, 1),
+                                   write_kib=round(kw, 1),
                                    bytes_per_launch=int(round((kf * sf + kw * sw) * 1024)))})
     out = os.path.join(ROOT, "profiles", "traffic.json")
     with open(out, "w") as f:
