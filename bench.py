@@ -63,6 +63,11 @@ def parse():
                    help="run a conv and the max pool after it as two calls")
     p.add_argument("--workload", choices=list(WORKLOADS), default="resnet18d",
                    help="the backbone (default; the headline) or one of the other layer configs")
+    p.add_argument("--no-tune", action="store_true",
+                   help="skip the per-shape tuning (conv2d_tune) of the workload's convs before timing")
+    p.add_argument("--tune-out", default=None, help="save the tuned-plan table to this file")
+    p.add_argument("--tune-in", default=None,
+                   help="load a tuned-plan table (written by --tune-out) instead of tuning")
     p.add_argument("--ops", action="store_true",
                    help="instead of the backbone: time the transposed conv, upsample and concat calls "
                         "at the pages' shapes (one JSON line with a row per call)")
@@ -276,6 +281,7 @@ def measured_traffic(plan, launches_bytes):
         rec = json.load(open(path))
     except (OSError, ValueError):
         return None
+    plan = plan[:-len(" tuned")] if plan.endswith(" tuned") else plan  # a tuned choice is the same kernel
     k = rec.get("kernels", {}).get(plan)
     if not k or k.get("source_hash") != kernel_source_hash(plan):
         return None
@@ -359,6 +365,36 @@ def write_traffic(src, copy_mib, plan):
     with open(out, "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec))
+
+
+def tune_workload(work):
+    """Set-up, outside the timed region: time the kernel variants of each distinct conv
+    shape of the workload on this GPU (conv2d_tune) so the stack picks the fastest.
+    Returns the number of shapes tuned."""
+    import conv2d_bias_activation_amd as c2d
+
+    dt = {"f32": c2d.DTYPE_F32, "bf16": c2d.DTYPE_BF16, "f16": c2d.DTYPE_F16}[work.dtype]
+    nchw = work.layout == "nchw"
+    shapes = {"x": tuple(work.x.shape)}
+    seen = set()
+    for spec in work.layers:
+        src = shapes[spec.src]
+        n, c, h, w = src if nchw else (src[0], src[3], src[1], src[2])
+        if hasattr(spec, "cin"):
+            oh = (h + 2 * spec.pad - spec.k) // spec.stride + 1
+            ow = (w + 2 * spec.pad - spec.k) // spec.stride + 1
+            key = (n, h, w, c, spec.cout, spec.k, spec.stride, spec.pad, spec.act, bool(spec.res), spec.res_before_act)
+            if key not in seen:
+                seen.add(key)
+                c2d.tune(n, h, w, c, spec.cout, spec.k, spec.k, spec.stride, spec.pad, spec.act,
+                         residual=bool(spec.res), res_before_act=spec.res_before_act, layout=work.layout, dtype=dt,
+                         reps=10)
+            oshape = (n, spec.cout, oh, ow) if nchw else (n, oh, ow, spec.cout)
+        else:
+            oh, ow = ((h - 1) // 2 + 1, (w - 1) // 2 + 1) if spec.kind == "max" else (h // 2, w // 2)
+            oshape = (n, c, oh, ow) if nchw else (n, oh, ow, c)
+        shapes[spec.out] = oshape
+    return len(seen)
 
 
 def time_call(torch, fn, reps):
@@ -465,10 +501,19 @@ def main():
         return
     builder, config_name = WORKLOADS[args.workload]
     work = getattr(wl, builder)()
+    import conv2d_bias_activation_amd as c2d
+
+    tuned = 0
+    if args.tune_in:
+        tuned = c2d.tune_load(args.tune_in)
+    elif not args.no_tune:
+        tuned = tune_workload(work)
+        if args.tune_out:
+            c2d.tune_save(args.tune_out)
     net = Net(work, dev, fuse_pool=not args.no_fuse_pool)
     if args.launch_plan:
         h = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-        chosen = [L for L in net.layers if L["plan"] == args.launch_plan]
+        chosen = [L for L in net.layers if L["plan"].replace(" tuned", "") == args.launch_plan.replace(" tuned", "")]
         if not chosen:
             raise SystemExit(f"no layer runs plan {args.launch_plan!r}")
         for _ in range(5):
@@ -540,7 +585,8 @@ def main():
         "config": {"workload": config_name, "global_batch": int(work.x.shape[0]),
                    "convs": sum(1 for L in net.layers if L["flops"]),
                    "pools": sum(1 for L in net.layers if not L["flops"]),
-                   "gflop_per_step": round(net.flops / 1e9, 3), "launch": args.mode},
+                   "gflop_per_step": round(net.flops / 1e9, 3), "launch": args.mode,
+                   "tuned_shapes": tuned},
         "roofline": roof,
         "cpu_baseline": cpu,
     }

@@ -18,7 +18,7 @@ __all__ = ["conv2d_fused", "conv2d_fused_maxpool3x3s2", "maxpool3x3s2", "avgpool
            "check_args", "plan", "plan_maxpool", "Op", "conv_op", "pool_op", "copy_op", "stack_check",
            "stack_plan", "stack_run", "StackGraph", "conv_transpose4x4s2", "plan_deconv",
            "upsample_nearest2x", "concat_channels", "upsample2x_concat", "deconv_op", "upsample_op",
-           "concat_op",
+           "concat_op", "tune", "tune_save", "tune_load", "tune_clear",
            "last_error", "library_path", "Conv2dError", "ACT_NONE", "ACT_RELU", "ACT_SILU",
            "ACT_PRELU", "RES_BEFORE_ACT", "LAYOUT_NHWC", "LAYOUT_NCHW", "DTYPE_F32",
            "DTYPE_BF16", "DTYPE_F16"]
@@ -73,6 +73,10 @@ SIGNATURES = {
     "upsample_nearest2x": (_i, [_vp, _vp] + [_i] * 6 + [_vp]),
     "concat_channels": (_i, [_vp, _vp, _vp] + [_i] * 7 + [_vp]),
     "upsample2x_concat": (_i, [_vp, _vp, _vp] + [_i] * 7 + [_vp]),
+    "conv2d_tune": (_i, [_i] * 14 + [ctypes.POINTER(ctypes.c_float), _cp, _i]),
+    "conv2d_tune_save": (_i, [_cp]),
+    "conv2d_tune_load": (_i, [_cp]),
+    "conv2d_tune_clear": (_i, []),
     "conv2d_last_error": (_cp, []),
     "conv2d_abi_version": (_i, []),
 }
@@ -497,3 +501,35 @@ def concat_op(a, b, y, *, up=False, layout="nhwc"):
     Cb = _nhwc_dims(b, layout)[3]
     return Op(OP_UPSAMPLE_CONCAT if up else OP_CONCAT, a.data_ptr(), None, None, None, b.data_ptr(),
               y.data_ptr(), N, H, W, Ca, Cb, 0, 0, 0, 0, 0)
+
+
+def tune(N, H, W, Cin, Cout, kh, kw, stride, pad, act="none", *, residual=False, res_before_act=False,
+         layout="nhwc", dtype=DTYPE_BF16, reps=20):
+    """Time the kernel variants of one conv shape on the current device and keep the
+    fastest for later calls of that shape (include/conv2d_fused.h, conv2d_tune).
+    Returns (variant name, average launch time in microseconds)."""
+    buf = ctypes.create_string_buffer(256)
+    us = ctypes.c_float(0.0)
+    n = _load().conv2d_tune(N, H, W, Cin, Cout, kh, kw, stride, pad, _act_code(act, res_before_act),
+                            1 if residual else 0, _LAYOUTS[layout], dtype, reps, ctypes.byref(us), buf, 256)
+    _check(n if n < 0 else OK)
+    return buf.value.decode(), us.value
+
+
+def tune_save(path) -> int:
+    """Write the tuned-plan table to a text file; returns the number of records."""
+    n = _load().conv2d_tune_save(os.fsencode(path))
+    _check(n if n < 0 else OK)
+    return n
+
+
+def tune_load(path) -> int:
+    """Add the records of a file written by tune_save; returns the number read."""
+    n = _load().conv2d_tune_load(os.fsencode(path))
+    _check(n if n < 0 else OK)
+    return n
+
+
+def tune_clear():
+    """Forget every tuned plan."""
+    _check(_load().conv2d_tune_clear())

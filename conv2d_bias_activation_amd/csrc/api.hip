@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <map>
 #include <mutex>
 #include <new>
 #include <string>
@@ -139,6 +140,7 @@ struct Plan {
     IgemmPlan ig;
     NhwcPlan nh;
     HaloPlan halo;
+    bool tuned;  // chosen by a conv2d_tune measurement rather than the built-in heuristics
 };
 
 // Library scratch, one buffer per device, allocated on the first call that needs it
@@ -319,7 +321,7 @@ Plan igemm_plan(const ConvArgs &a, int layout, int dtype) {
     return p;
 }
 
-Plan make_plan(const ConvArgs &a, int layout, int dtype) {
+Plan make_plan_default(const ConvArgs &a, int layout, int dtype) {
     Plan p{};
     if (stem_fits(a, layout, dtype)) {
         p.family = FAM_STEM;
@@ -357,6 +359,94 @@ Plan make_plan(const ConvArgs &a, int layout, int dtype) {
     return igemm_plan(a, layout, dtype);
 }
 
+// ---- tuned plans (framecast's `tuneConvRB`: time the candidate variants of a shape on
+// this device once, keep the fastest, persist the answer) ----
+//
+// The table maps a shape key (device, sizes, layout, dtype, residual or not) to a kernel
+// variant of the channel-last matrix-core families. make_plan consults it for shapes
+// whose built-in choice is one of those families, and uses an entry only if the variant
+// is valid for the call at hand (alignment, scratch size).
+struct TunedEntry {
+    int family;  // FAM_NHWC or FAM_HALO
+    int tile;    // NhwcTile (FAM_NHWC)
+    int splits;  // K slices (FAM_NHWC)
+    int th;      // tile height (FAM_HALO)
+};
+std::mutex g_tune_mu;
+std::map<std::string, TunedEntry> g_tuned;
+std::atomic<int> g_tuned_n{0};  // entries in g_tuned (the planner skips the lookup at 0)
+std::string g_dev_tag[kMaxDevices];
+std::once_flag g_dev_tag_once[kMaxDevices];
+
+// "<gfx arch>:<compute units>" of the current device, or "" without one.
+std::string device_tag() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return "";
+    std::call_once(g_dev_tag_once[dev], [dev] {
+        hipDeviceProp_t pr;
+        if (hipGetDeviceProperties(&pr, dev) == hipSuccess) {
+            std::string arch = pr.gcnArchName;
+            arch = arch.substr(0, arch.find(':'));
+            g_dev_tag[dev] = arch + ":" + std::to_string(pr.multiProcessorCount);
+        }
+    });
+    return g_dev_tag[dev];
+}
+
+std::string tune_key(const std::string &dev, const ConvArgs &a, int layout, int dtype) {
+    char k[192];
+    snprintf(k, sizeof k, "%s|%d|%d|%d|%d|%d|%d|%d|%d|%d|%d|%d|%d", dev.c_str(), a.N, a.H, a.W, a.Cin, a.Cout,
+             a.kh, a.kw, a.stride, a.pad, layout, dtype, a.res ? 1 : 0);
+    return k;
+}
+
+bool splits_ok(const ConvArgs &a, int splits) {
+    if (splits <= 1) return true;
+    return (a.Cout % 8) == 0 && a.vec_out && (unsigned long long)splits * a.M * a.Cout * 4 <= kScratchBytes &&
+           (a.K + 63) / 64 >= splits;
+}
+
+bool halo_th_ok(const ConvArgs &a, int th) {
+    const int wm = 4;  // waves along the rows: 4-wave workgroups, or 8 with k split over wave pairs
+    const int fn = a.Cout <= 32 ? 1 : 2;
+    return fn == 1 ? (th == wm || th == 2 * wm) : th == wm;
+}
+
+// Applies the table's entry for this call, if any and valid; p is the built-in choice.
+void apply_tuned(const ConvArgs &a, int layout, int dtype, Plan *p) {
+    if (g_tuned_n.load(std::memory_order_acquire) == 0) return;
+    if (p->family != FAM_NHWC && p->family != FAM_HALO) return;
+    const std::string dev = device_tag();
+    if (dev.empty()) return;
+    TunedEntry e;
+    {
+        std::lock_guard<std::mutex> lock(g_tune_mu);
+        auto it = g_tuned.find(tune_key(dev, a, layout, dtype));
+        if (it == g_tuned.end()) return;
+        e = it->second;
+    }
+    if (e.family == FAM_HALO) {
+        if (!halo_fits(a, layout, dtype) || !halo_th_ok(a, e.th)) return;
+        p->family = FAM_HALO;
+        p->halo = plan_halo(a);
+        p->halo.th = e.th;
+        p->tuned = true;
+    } else if (e.family == FAM_NHWC) {
+        if (e.tile < 0 || e.tile >= NHWC_TILE_COUNT || !splits_ok(a, e.splits)) return;
+        p->family = FAM_NHWC;
+        p->nh = plan_nhwc(a);
+        p->nh.tile = e.tile;
+        p->nh.splits = e.splits > 1 ? e.splits : 1;
+        p->tuned = true;
+    }
+}
+
+Plan make_plan(const ConvArgs &a, int layout, int dtype) {
+    Plan p = make_plan_default(a, layout, dtype);
+    apply_tuned(a, layout, dtype, &p);
+    return p;
+}
+
 int describe(const Plan &p, int layout, int dtype, char *buf, int cap) {
     char tmp[160];
     if (p.family == FAM_DIRECT) {
@@ -375,6 +465,7 @@ int describe(const Plan &p, int layout, int dtype, char *buf, int cap) {
         snprintf(tmp, sizeof tmp, "igemm_%s%s %s %s", p.ig.nchw ? "nchw" : "nhwc",
                  p.ig.avec ? "_vec" : "_gather", dtype_name(dtype), tile_name(p.ig.tile));
     }
+    if (p.tuned) strncat(tmp, " tuned", sizeof tmp - strlen(tmp) - 1);
     int n = (int)strlen(tmp);
     if (buf && cap > 0) {
         strncpy(buf, tmp, (size_t)cap - 1);
@@ -830,11 +921,130 @@ int describe_op(const OpPlan &o, char *buf, int cap) {
     return n;
 }
 
+// Device buffers of one tuning run, freed on every path out.
+struct TuneBuffers {
+    void *p[6] = {};
+    ~TuneBuffers() {
+        for (void *q : p)
+            if (q) (void)hipFree(q);
+    }
+};
+
+int tune_run(int N, int H, int W, int Cin, int Cout, int kh, int kw, int stride, int pad, int act, int has_residual,
+             int layout, int dtype, int reps, Plan *best_out, float *best_us) {
+    if (reps < 1 || reps > 10000) return set_error(CONV2D_EINVAL, "conv2d_tune: reps must be in 1..10000");
+    // validate the shape first with stand-in addresses (nothing is allocated for a bad call)
+    {
+        ConvArgs t{};
+        const void *px = (const void *)(uintptr_t)0x100000000ull, *pw = (const void *)(uintptr_t)0x900000000ull;
+        const void *py = (const void *)(uintptr_t)0x1100000000ull, *pr = (const void *)(uintptr_t)0x1900000000ull;
+        const float *pa = (const float *)(uintptr_t)0x2100000000ull;
+        int rc = check_conv(px, pw, pa, has_residual ? pr : nullptr, py, N, H, W, Cin, Cout, kh, kw, stride, pad, act,
+                            layout, dtype, &t);
+        if (rc) return rc;
+    }
+    const int eb = dtype_bytes(dtype);
+    const int OH = out_dim(H, kh, stride, pad), OW = out_dim(W, kw, stride, pad);
+    const size_t sizes[6] = {(size_t)N * H * W * Cin * eb, (size_t)Cout * kh * kw * Cin * eb,
+                             (size_t)N * OH * OW * Cout * eb, has_residual ? (size_t)N * OH * OW * Cout * eb : 0,
+                             (size_t)Cout * 4, (size_t)Cout * 4};
+    TuneBuffers b;
+    for (int i = 0; i < 6; ++i) {
+        if (!sizes[i]) continue;
+        hipError_t e = hipMalloc(&b.p[i], sizes[i]);
+        if (e != hipSuccess) return hip_fail(e, "conv2d_tune buffers");
+        e = hipMemset(b.p[i], 0, sizes[i]);
+        if (e != hipSuccess) return hip_fail(e, "conv2d_tune buffers");
+    }
+    ConvArgs a{};
+    int rc = check_conv(b.p[0], b.p[1], (const float *)b.p[5], b.p[3], b.p[2], N, H, W, Cin, Cout, kh, kw, stride,
+                        pad, act, layout, dtype, &a);
+    if (rc) return rc;
+    a.bias = (const float *)b.p[4];
+    if (a.act != CONV2D_ACT_PRELU) a.alpha = nullptr;
+    const Plan def = make_plan_default(a, layout, dtype);
+    std::vector<Plan> cands;
+    cands.push_back(def);
+    if (def.family == FAM_NHWC || def.family == FAM_HALO) {
+        if (halo_fits(a, layout, dtype)) {
+            for (int th : {4, 8}) {
+                if (!halo_th_ok(a, th)) continue;
+                Plan c{};
+                c.family = FAM_HALO;
+                c.halo = plan_halo(a);
+                c.halo.th = th;
+                cands.push_back(c);
+            }
+        }
+        for (int tile = 0; tile < NHWC_TILE_COUNT; ++tile)
+            for (int sp : {1, 2, 3, 4}) {
+                if (!splits_ok(a, sp)) continue;
+                Plan c{};
+                c.family = FAM_NHWC;
+                c.nh = plan_nhwc(a);
+                c.nh.tile = tile;
+                c.nh.splits = sp;
+                cands.push_back(c);
+            }
+    }
+    // everything the launches need, fetched before timing
+    float *scratch = nullptr;
+    rc = get_scratch(&scratch);
+    if (rc) return rc;
+    int cus = 0;
+    rc = device_cus(&cus);
+    if (rc) return rc;
+    hipStream_t st = nullptr;
+    hipError_t e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking);
+    if (e != hipSuccess) return hip_fail(e, "conv2d_tune stream");
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    e = hipEventCreate(&e0);
+    if (e == hipSuccess) e = hipEventCreate(&e1);
+    int best = -1;
+    float best_ms = 0.0f;
+    for (size_t i = 0; i < cands.size() && e == hipSuccess; ++i) {
+        for (int w = 0; w < 2 && rc == CONV2D_OK; ++w) rc = launch_conv(a, cands[i], layout, dtype, st);
+        if (rc) break;
+        e = hipEventRecord(e0, st);
+        for (int r = 0; r < reps && rc == CONV2D_OK && e == hipSuccess; ++r) rc = launch_conv(a, cands[i], layout, dtype, st);
+        if (rc || e != hipSuccess) break;
+        e = hipEventRecord(e1, st);
+        if (e == hipSuccess) e = hipEventSynchronize(e1);
+        float ms = 0.0f;
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+        if (e == hipSuccess && (best < 0 || ms < best_ms)) {
+            best = (int)i;
+            best_ms = ms;
+        }
+    }
+    if (e0) (void)hipEventDestroy(e0);
+    if (e1) (void)hipEventDestroy(e1);
+    hipError_t es = hipStreamSynchronize(st);
+    (void)hipStreamDestroy(st);
+    if (rc) return rc;
+    if (e != hipSuccess) return hip_fail(e, "conv2d_tune timing");
+    if (es != hipSuccess) return hip_fail(es, "conv2d_tune");
+    *best_out = cands[(size_t)best];
+    *best_us = best_ms * 1e3f / (float)reps;
+    // record the winner (only for the families the planner looks up)
+    if (best_out->family == FAM_NHWC || best_out->family == FAM_HALO) {
+        const std::string dev = device_tag();
+        if (!dev.empty()) {
+            TunedEntry t{best_out->family, best_out->nh.tile, best_out->nh.splits, best_out->halo.th};
+            std::lock_guard<std::mutex> lock(g_tune_mu);
+            g_tuned[tune_key(dev, a, layout, dtype)] = t;
+            g_tuned_n.store((int)g_tuned.size(), std::memory_order_release);
+        }
+        best_out->tuned = true;
+    }
+    return CONV2D_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
-int conv2d_abi_version(void) { return 3; }
+int conv2d_abi_version(void) { return 4; }
 
 const char *conv2d_last_error(void) { return g_err.c_str(); }
 
@@ -951,6 +1161,76 @@ int upsample2x_concat(const void *a, const void *b, void *y, int N, int H, int W
                       int dtype, void *stream) {
     const conv2d_op op{CONV2D_OP_UPSAMPLE_CONCAT, a, nullptr, nullptr, nullptr, b, y, N, H, W, Ca, Cb, 0, 0, 0, 0, 0};
     return run_one(op, layout, dtype, stream);
+}
+
+int conv2d_tune(int N, int H, int W, int Cin, int Cout, int kh, int kw, int stride, int pad, int act, int has_residual,
+                int layout, int dtype, int reps, float *best_us, char *buf, int cap) {
+    Plan best{};
+    float us = 0.0f;
+    int rc = tune_run(N, H, W, Cin, Cout, kh, kw, stride, pad, act, has_residual, layout, dtype, reps, &best, &us);
+    if (rc) return rc;
+    if (best_us) *best_us = us;
+    set_ok();
+    return describe(best, layout, dtype, buf, cap);
+}
+
+int conv2d_tune_save(const char *path) {
+    if (!path) return set_error(CONV2D_EINVAL, "conv2d_tune_save: path must not be null");
+    std::map<std::string, TunedEntry> copy;
+    {
+        std::lock_guard<std::mutex> lock(g_tune_mu);
+        copy = g_tuned;
+    }
+    FILE *f = fopen(path, "w");
+    if (!f) return set_error(CONV2D_EINVAL, "conv2d_tune_save: cannot open %s", path);
+    fprintf(f, "# conv2d tuned plans v1: device|N|H|W|Cin|Cout|kh|kw|stride|pad|layout|dtype|residual family tile splits th\n");
+    for (const auto &kv : copy)
+        fprintf(f, "%s %d %d %d %d\n", kv.first.c_str(), kv.second.family, kv.second.tile, kv.second.splits,
+                kv.second.th);
+    const bool bad = ferror(f) != 0;
+    if (fclose(f) != 0 || bad) return set_error(CONV2D_EINVAL, "conv2d_tune_save: write to %s failed", path);
+    set_ok();
+    return (int)copy.size();
+}
+
+int conv2d_tune_load(const char *path) {
+    if (!path) return set_error(CONV2D_EINVAL, "conv2d_tune_load: path must not be null");
+    FILE *f = fopen(path, "r");
+    if (!f) return set_error(CONV2D_EINVAL, "conv2d_tune_load: cannot open %s", path);
+    std::map<std::string, TunedEntry> add;
+    char line[512];
+    int lineno = 0;
+    while (fgets(line, sizeof line, f)) {
+        ++lineno;
+        if (line[0] == '#' || line[0] == '\n' || line[0] == 0) continue;
+        char key[256];
+        TunedEntry t{};
+        char extra[4];
+        const int got = sscanf(line, "%255s %d %d %d %d %3s", key, &t.family, &t.tile, &t.splits, &t.th, extra);
+        int bars = 0;
+        for (const char *c = key; *c; ++c) bars += *c == '|';
+        const bool ok = got == 5 && bars == 12 && ((t.family == FAM_NHWC && t.tile >= 0 && t.tile < NHWC_TILE_COUNT &&
+                                                    t.splits >= 1 && t.splits <= 4) ||
+                                                   (t.family == FAM_HALO && (t.th == 4 || t.th == 8)));
+        if (!ok) {
+            fclose(f);
+            return set_error(CONV2D_EINVAL, "conv2d_tune_load: %s line %d is not a tuned-plan record", path, lineno);
+        }
+        add[key] = t;
+    }
+    fclose(f);
+    std::lock_guard<std::mutex> lock(g_tune_mu);
+    for (const auto &kv : add) g_tuned[kv.first] = kv.second;
+    g_tuned_n.store((int)g_tuned.size(), std::memory_order_release);
+    set_ok();
+    return (int)add.size();
+}
+
+int conv2d_tune_clear(void) {
+    std::lock_guard<std::mutex> lock(g_tune_mu);
+    g_tuned.clear();
+    g_tuned_n.store(0, std::memory_order_release);
+    return set_ok();
 }
 
 int conv2d_stack_check(const conv2d_op *ops, int n, int layout, int dtype, int *bad_index) {

@@ -21,16 +21,18 @@ namespace c2d {
 
 namespace {
 
-constexpr int DC_TW = 32;           // input columns per tile: 64 output columns, 2 output rows
+constexpr int DC_TW = 32;           // input columns per tile
+constexpr int DC_MR = 2;            // input rows per tile: a wave's 32-pixel blocks that share each weight load
+constexpr int DC_ROWS = DC_MR + 2;  // staged rows j0 - 1 .. j0 + DC_MR
 constexpr int DC_KC = 64;           // input channels per staged chunk
 constexpr int DC_SPX = DC_TW + 2;   // staged columns i0 - 1 .. i0 + 32
 constexpr int DC_PS = DC_KC + 8;    // LDS elements per staged pixel: 144 bytes, an odd number of
                                     // 16-byte slots, so 32 lanes reading 32 pixels hit distinct banks
-constexpr int DC_BUF = 3 * DC_SPX * DC_PS;
-constexpr int DC_VECS = 3 * DC_SPX * (DC_KC / 8);   // 16-byte vectors per chunk, channel-last (816)
-constexpr int DC_VQ = (DC_VECS + 255) / 256;        // per thread (4)
-constexpr int DC_ELEMS = 3 * DC_SPX * DC_KC;        // elements per chunk, channel-first (6528)
-constexpr int DC_EQ = (DC_ELEMS + 255) / 256;       // per thread (26)
+constexpr int DC_BUF = DC_ROWS * DC_SPX * DC_PS;
+constexpr int DC_VECS = DC_ROWS * DC_SPX * (DC_KC / 8);  // 16-byte vectors per chunk, channel-last (1088)
+constexpr int DC_VQ = (DC_VECS + 255) / 256;             // per thread (5)
+constexpr int DC_ELEMS = DC_ROWS * DC_SPX * DC_KC;       // elements per chunk, channel-first (8704)
+constexpr int DC_EQ = (DC_ELEMS + 255) / 256;            // per thread (34)
 constexpr int DC_KS = DC_KC / 16;                   // 16-deep MFMA steps per tap and chunk
 // Staging lanes past the chunk's last vector or element store into a pad after the
 // buffer, so every lane stores and no load is sunk into a branch (where its wait would
@@ -85,15 +87,16 @@ __global__ __launch_bounds__(256) void deconv_pack_kernel(const T *__restrict__ 
 
 // 16-bit input with Cin % 8 == 0 (channel-last: 16-byte aligned; channel-first: read
 // straight from the planes and transposed while staging), packed weights. Block: 4
-// waves, wave = parity class; tile = input row j of image n, input columns i0 .. i0+31,
-// output channels co0 .. co0+31 (blockIdx.y). The K loop runs over 64-channel chunks
-// with the next chunk's input and weight loads in flight during the current chunk's
-// products.
+// waves, wave = parity class; tile = input rows j0, j0 + 1 of image n, input columns
+// i0 .. i0+31, output channels co0 .. co0+31 (blockIdx.y): each wave computes two
+// 32-pixel blocks (one per input row) with every weight operand it loads. The K loop
+// runs over 64-channel chunks with the next chunk's input and weight loads in flight
+// during the current chunk's products.
 template <typename T, typename TO, bool NCHW>
 __global__ __launch_bounds__(256) void deconv_mfma_kernel(DeconvArgs a) {
     typedef typename Mfma32<T>::vec vec;
     __shared__ __attribute__((aligned(16))) T sx[2][DC_BUFA];
-    __shared__ float so[32][2][DC_OLD];
+    __shared__ float so[32][2 * DC_MR][DC_OLD];
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int py = wv >> 1, px = wv & 1;
@@ -102,12 +105,13 @@ __global__ __launch_bounds__(256) void deconv_mfma_kernel(DeconvArgs a) {
     int t = blockIdx.x;
     const int ib = t % tiles_w;
     t /= tiles_w;
-    const int j = t % H, n = t / H;
+    const int tiles_h = (H + DC_MR - 1) / DC_MR;
+    const int j0 = (t % tiles_h) * DC_MR, n = t / tiles_h;
     const int i0 = ib * DC_TW;
     const int co0 = blockIdx.y * 32;
     const T *__restrict__ x = static_cast<const T *>(a.x);
 
-    // staging registers of one chunk: 3 rows x 34 pixels x 64 channels, zero outside the
+    // staging registers of one chunk: 4 rows x 34 pixels x 64 channels, zero outside the
     // image and past Cin
     u32x4 sv[NCHW ? 1 : DC_VQ];
     T se[NCHW ? DC_EQ : 1];
@@ -119,8 +123,8 @@ __global__ __launch_bounds__(256) void deconv_mfma_kernel(DeconvArgs a) {
             for (int q = 0; q < DC_EQ; ++q) {
                 const int e = tid + 256 * q;
                 const int p = e % DC_SPX, rc = e / DC_SPX;
-                const int r = rc % 3, cl = rc / 3;
-                const int iy = j - 1 + r, ix = i0 - 1 + p, ci = c0 + cl;
+                const int r = rc % DC_ROWS, cl = rc / DC_ROWS;
+                const int iy = j0 - 1 + r, ix = i0 - 1 + p, ci = c0 + cl;
                 const bool ok = e < DC_ELEMS && (unsigned)iy < (unsigned)H && (unsigned)ix < (unsigned)W && ci < Cin;
                 const uint32_t off = ok ? ((((uint32_t)n * Cin + ci) * H + iy) * W + ix) * 2u : kOob;
                 const unsigned short v = __builtin_amdgcn_raw_buffer_load_b16(rx, (int)off, 0, 0);
@@ -132,7 +136,7 @@ __global__ __launch_bounds__(256) void deconv_mfma_kernel(DeconvArgs a) {
                 const int idx = tid + 256 * q;
                 const int r = idx / (DC_SPX * 8), rem = idx - r * (DC_SPX * 8);
                 const int p = rem >> 3, cv = rem & 7;
-                const int iy = j - 1 + r, ix = i0 - 1 + p, ci = c0 + cv * 8;
+                const int iy = j0 - 1 + r, ix = i0 - 1 + p, ci = c0 + cv * 8;
                 const bool ok = idx < DC_VECS && (unsigned)iy < (unsigned)H && (unsigned)ix < (unsigned)W && ci < Cin;
                 const uint32_t off = ok ? ((((uint32_t)n * H + iy) * W + ix) * Cin + ci) * 2u : kOob;
                 sv[q] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)off, 0, 0);
@@ -145,7 +149,7 @@ __global__ __launch_bounds__(256) void deconv_mfma_kernel(DeconvArgs a) {
             for (int q = 0; q < DC_EQ; ++q) {
                 const int e = tid + 256 * q;
                 const int p = e % DC_SPX, rc = e / DC_SPX;
-                const int r = rc % 3, cl = rc / 3;
+                const int r = rc % DC_ROWS, cl = rc / DC_ROWS;
                 sx[buf][e < DC_ELEMS ? (r * DC_SPX + p) * DC_PS + cl : DC_BUF + (e - DC_ELEMS)] = se[q];
             }
         } else {
@@ -173,9 +177,11 @@ __global__ __launch_bounds__(256) void deconv_mfma_kernel(DeconvArgs a) {
         for (int i = 0; i < 4 * DC_KS; ++i)
             bw[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(c < nchp ? cb + i * 1024u : kOob), 0, 0);
     };
-    f32x16 acc;
+    f32x16 acc[DC_MR];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+    for (int m = 0; m < DC_MR; ++m)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[m][i] = 0.0f;
 
     const int nch = (Cin + DC_KC - 1) / DC_KC;
     load_chunk(0);
@@ -196,12 +202,15 @@ __global__ __launch_bounds__(256) void deconv_mfma_kernel(DeconvArgs a) {
 #pragma unroll
         for (int tp = 0; tp < 4; ++tp) {
             const int ty = tp >> 1, tx = tp & 1;
-            const T *pa = sb + ((py + ty) * DC_SPX + col + px + tx) * DC_PS + kq;
 #pragma unroll
-            for (int ks = 0; ks < DC_KS; ++ks) {
-                vec av;
-                __builtin_memcpy(&av, pa + ks * 16, 16);
-                acc = Mfma32<T>::run(av, bcur[tp * DC_KS + ks], acc);
+            for (int m = 0; m < DC_MR; ++m) {
+                const T *pa = sb + ((m + py + ty) * DC_SPX + col + px + tx) * DC_PS + kq;
+#pragma unroll
+                for (int ks = 0; ks < DC_KS; ++ks) {
+                    vec av;
+                    __builtin_memcpy(&av, pa + ks * 16, 16);
+                    acc[m] = Mfma32<T>::run(av, bcur[tp * DC_KS + ks], acc[m]);
+                }
             }
         }
         store_chunk((c + 1) & 1);
@@ -215,29 +224,32 @@ __global__ __launch_bounds__(256) void deconv_mfma_kernel(DeconvArgs a) {
     const float bv = (a.bias && co < Cout) ? a.bias[co] : 0.0f;
     const float av = (a.alpha && co < Cout) ? a.alpha[co] : 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int p = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-        so[col][py][2 * p + px] = activate(a.act, acc[i] + bv, av);
-    }
+    for (int m = 0; m < DC_MR; ++m)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int p = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+            so[col][2 * m + py][2 * p + px] = activate(a.act, acc[m][i] + bv, av);
+        }
     __syncthreads();
+    // output rows 2*j0 .. 2*j0 + 2*DC_MR - 1 (local row lr), columns 2*i0 .. +63
     TO *__restrict__ y = static_cast<TO *>(a.y);
     const int OH = 2 * H, OW = 2 * W;
-    const int oc0 = 2 * i0;
+    const int oc0 = 2 * i0, or0 = 2 * j0;
     if constexpr (NCHW) {
 #pragma unroll 4
-        for (int it = 0; it < 16; ++it) {
+        for (int it = 0; it < 16 * DC_MR; ++it) {
             const int e = tid + 256 * it;
-            const int oc = e & 63, r = (e >> 6) & 1, cl = e >> 7;
-            if (co0 + cl < Cout && oc0 + oc < OW)
-                y[(((size_t)n * Cout + co0 + cl) * OH + 2 * j + r) * OW + oc0 + oc] = out_cast<TO>(so[cl][r][oc]);
+            const int oc = e & 63, lr = (e >> 6) & (2 * DC_MR - 1), cl = e / (128 * DC_MR);
+            if (co0 + cl < Cout && oc0 + oc < OW && or0 + lr < OH)
+                y[(((size_t)n * Cout + co0 + cl) * OH + or0 + lr) * OW + oc0 + oc] = out_cast<TO>(so[cl][lr][oc]);
         }
     } else {
 #pragma unroll 4
-        for (int it = 0; it < 16; ++it) {
+        for (int it = 0; it < 16 * DC_MR; ++it) {
             const int e = tid + 256 * it;
-            const int cl = e & 31, oc = (e >> 5) & 63, r = e >> 11;
-            if (co0 + cl < Cout && oc0 + oc < OW)
-                y[(((size_t)n * OH + 2 * j + r) * OW + oc0 + oc) * Cout + co0 + cl] = out_cast<TO>(so[cl][r][oc]);
+            const int cl = e & 31, oc = (e >> 5) & 63, lr = e >> 11;
+            if (co0 + cl < Cout && oc0 + oc < OW && or0 + lr < OH)
+                y[(((size_t)n * OH + or0 + lr) * OW + oc0 + oc) * Cout + co0 + cl] = out_cast<TO>(so[cl][lr][oc]);
         }
     }
 }
@@ -316,7 +328,7 @@ hipError_t launch_deconv_pack(const void *w, void *wp, int Cin, int Cout, int Co
 
 template <typename T, typename TO>
 static hipError_t mfma_t(const DeconvArgs &a, bool nchw, hipStream_t st) {
-    const long long tiles = (long long)a.N * a.H * ((a.W + DC_TW - 1) / DC_TW);
+    const long long tiles = (long long)a.N * ((a.H + DC_MR - 1) / DC_MR) * ((a.W + DC_TW - 1) / DC_TW);
     dim3 grid((unsigned)tiles, (unsigned)(a.CoP / 32));
     if (nchw) return launch_kernel(deconv_mfma_kernel<T, TO, true>, grid, dim3(256), 0, st, a);
     return launch_kernel(deconv_mfma_kernel<T, TO, false>, grid, dim3(256), 0, st, a);

@@ -322,12 +322,54 @@ int conv2d_stack_graph_launch(conv2d_graph *g, void *stream);
 /* Frees the graph (NULL is allowed). The caller makes sure no replay is still running. */
 int conv2d_stack_graph_destroy(conv2d_graph *g);
 
+/*
+ * Tuning: time the candidate kernel variants of one conv shape on the current device
+ * and keep the fastest for later calls of that shape, like framecast's `tuneConvRB`,
+ * which benchmarks its conv variants once per device and resolution and persists the
+ * winner because the best variant flips with the shape; inferencelayer's per-shape
+ * GEMM tile table is the static form of the same choice.
+ *
+ * conv2d_tune allocates its own inputs and output for the shape (zero-filled device
+ * buffers; act, has_residual, layout and dtype as conv2d_fused's arguments would be),
+ * times the built-in choice and, for shapes on the channel-last matrix-core kernels,
+ * every tile shape and split-K depth (1-4) of the implicit-GEMM kernel and the tile
+ * heights of the halo kernel: each variant runs twice, then `reps` times between two
+ * events on a private stream. It synchronises that stream, frees its buffers and
+ * records the fastest variant in a process-wide table keyed by (device arch and
+ * compute units, N, H, W, Cin, Cout, kh, kw, stride, pad, layout, dtype, residual or
+ * not). From then on conv2d_fused, the fused conv + max pool and the stacks (and
+ * conv2d_plan, whose name then ends in " tuned") use it for that shape whenever the
+ * variant is valid for the call (alignment, scratch size); otherwise they fall back
+ * to the built-in choice. Not for use under HIP graph capture (it allocates and
+ * synchronises). Writes the winner's name to buf (as conv2d_plan) and its average
+ * launch time in microseconds to *best_us (if not NULL); returns the name's length or
+ * a negative CONV2D_E* code. Argument errors as conv2d_fused, plus reps outside
+ * 1..10000.
+ */
+int conv2d_tune(int N, int H, int W, int Cin, int Cout, int kh, int kw, int stride, int pad, int act, int has_residual,
+                int layout, int dtype, int reps, float *best_us, char *buf, int cap);
+
+/* Writes the whole table to a text file (a comment line, then one record per line:
+ * the key with '|' separators, then four integers). Returns the number of records or
+ * CONV2D_EINVAL if the file cannot be written. Host only. */
+int conv2d_tune_save(const char *path);
+
+/* Adds the records of a file written by conv2d_tune_save to the table (a record for a
+ * key already present replaces it). Records of other devices are kept but never match
+ * this device's calls. Returns the number of records read, or CONV2D_EINVAL (nothing
+ * added) if the file cannot be read or a line is not a record. Host only. */
+int conv2d_tune_load(const char *path);
+
+/* Empties the table: every shape goes back to the built-in choice. Host only. */
+int conv2d_tune_clear(void);
+
 /* Message of the last error on the calling thread ("" if none). The pointer stays
  * valid until the thread's next call into the library. */
 const char *conv2d_last_error(void);
 
-/* ABI version of this header: 3 (2 plus the transposed conv, upsample and concat calls and
- * their stack ops; 2 added the stack calls and the fused conv + max pool). */
+/* ABI version of this header: 4 (3 plus the tuning calls; 3 added the transposed conv,
+ * upsample and concat calls and their stack ops; 2 the stack calls and the fused conv +
+ * max pool). */
 int conv2d_abi_version(void);
 
 #ifdef __cplusplus

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     for name in names:
         assert hasattr(lib, name), name
     assert names == set(c2d.SIGNATURES)
-    assert c2d._load().conv2d_abi_version() == 3
+    assert c2d._load().conv2d_abi_version() == 4
 
 
 def test_out_dim():
@@ -220,3 +220,33 @@ def test_resample_ops_in_stack_check():
     assert c2d.stack_check([clash]) == (c2d.EINVAL, 0)
     odd = c2d.Op(c2d.OP_UPSAMPLE, 1 << 32, None, None, None, None, 9 << 32, 2, 10, 12, 5, 0, 0, 0, 0, 0, 0)
     assert c2d.stack_plan([odd], 0) == "upsample2x_scalar"
+
+
+def test_tune_table_file_round_trip(tmp_path):
+    """Host only: tuned-plan records load, save and clear without a device; malformed
+    files are rejected whole; a loaded record for another device changes no plan."""
+    c2d.tune_clear()
+    good = tmp_path / "plans.txt"
+    good.write_text("# comment\n"
+                    "gfx000:1|4|40|40|256|256|3|3|1|1|0|1|0 2 5 1 0\n"
+                    "gfx000:1|4|160|160|64|64|3|3|1|1|0|1|1 4 0 1 4\n")
+    before = c2d.plan(4, 40, 40, 256, 256, 3, 3, 1, 1, 1, 0, c2d.DTYPE_BF16)
+    assert c2d.tune_load(str(good)) == 2
+    assert c2d.plan(4, 40, 40, 256, 256, 3, 3, 1, 1, 1, 0, c2d.DTYPE_BF16) == before
+    out = tmp_path / "saved.txt"
+    assert c2d.tune_save(str(out)) == 2
+    lines = [l for l in out.read_text().splitlines() if not l.startswith("#")]
+    assert sorted(lines) == sorted(l for l in good.read_text().splitlines() if not l.startswith("#"))
+    for bad in ["gfx000:1|4|40|40 2 5 1 0\n",                             # short key
+                "gfx000:1|4|40|40|256|256|3|3|1|1|0|1|0 2 99 1 0\n",      # tile out of range
+                "gfx000:1|4|40|40|256|256|3|3|1|1|0|1|0 4 0 1 5\n",       # halo height
+                "gfx000:1|4|40|40|256|256|3|3|1|1|0|1|0 2 5\n"]:          # missing fields
+        f = tmp_path / "bad.txt"
+        f.write_text(bad)
+        with pytest.raises(c2d.Conv2dError):
+            c2d.tune_load(str(f))
+    with pytest.raises(c2d.Conv2dError):
+        c2d.tune_load(str(tmp_path / "missing.txt"))
+    assert c2d.tune_save(str(out)) == 2  # failed loads added nothing
+    c2d.tune_clear()
+    assert c2d.tune_save(str(out)) == 0
