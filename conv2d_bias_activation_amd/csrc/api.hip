@@ -348,7 +348,7 @@ Plan make_plan_default(const ConvArgs &a, int layout, int dtype) {
     }
     // Channel-first 16-bit layers: channel-last copies of x and w in the scratch, the
     // channel-last kernel, and an epilogue that writes the channel-first output.
-    if (layout == CONV2D_LAYOUT_NCHW && dtype != CONV2D_DTYPE_F32 && (a.Cin % 8) == 0 &&
+    if (layout == CONV2D_LAYOUT_NCHW && dtype != CONV2D_DTYPE_F32 && (a.Cin % 8) == 0 && a.N <= 65535 &&
         round256((size_t)xbytes) + round256((size_t)wbytes) <= kScratchBytes && ybytes < (1ll << 31)) {
         p.family = FAM_NCHW_VIA_NHWC;
         p.nh = plan_nhwc(a);
@@ -367,9 +367,9 @@ Plan make_plan_default(const ConvArgs &a, int layout, int dtype) {
 // whose built-in choice is one of those families, and uses an entry only if the variant
 // is valid for the call at hand (alignment, scratch size).
 struct TunedEntry {
-    int family;  // FAM_NHWC or FAM_HALO
-    int tile;    // NhwcTile (FAM_NHWC)
-    int splits;  // K slices (FAM_NHWC)
+    int family;  // FAM_NHWC, FAM_NCHW_VIA_NHWC or FAM_HALO
+    int tile;    // NhwcTile (FAM_NHWC, FAM_NCHW_VIA_NHWC)
+    int splits;  // K slices (FAM_NHWC; 1 for FAM_NCHW_VIA_NHWC)
     int th;      // tile height (FAM_HALO)
 };
 std::mutex g_tune_mu;
@@ -415,7 +415,7 @@ bool halo_th_ok(const ConvArgs &a, int th) {
 // Applies the table's entry for this call, if any and valid; p is the built-in choice.
 void apply_tuned(const ConvArgs &a, int layout, int dtype, Plan *p) {
     if (g_tuned_n.load(std::memory_order_acquire) == 0) return;
-    if (p->family != FAM_NHWC && p->family != FAM_HALO) return;
+    if (p->family != FAM_NHWC && p->family != FAM_HALO && p->family != FAM_NCHW_VIA_NHWC) return;
     const std::string dev = device_tag();
     if (dev.empty()) return;
     TunedEntry e;
@@ -425,7 +425,14 @@ void apply_tuned(const ConvArgs &a, int layout, int dtype, Plan *p) {
         if (it == g_tuned.end()) return;
         e = it->second;
     }
-    if (e.family == FAM_HALO) {
+    if (p->family == FAM_NCHW_VIA_NHWC || e.family == FAM_NCHW_VIA_NHWC) {
+        // channel-first layers: only the tile of the channel-last kernel is chosen
+        if (p->family != FAM_NCHW_VIA_NHWC || e.family != FAM_NCHW_VIA_NHWC || e.tile < 0 ||
+            e.tile >= NHWC_TILE_COUNT)
+            return;
+        p->nh.tile = e.tile;
+        p->tuned = true;
+    } else if (e.family == FAM_HALO) {
         if (!halo_fits(a, layout, dtype) || !halo_th_ok(a, e.th)) return;
         p->family = FAM_HALO;
         p->halo = plan_halo(a);
@@ -965,7 +972,13 @@ int tune_run(int N, int H, int W, int Cin, int Cout, int kh, int kw, int stride,
     const Plan def = make_plan_default(a, layout, dtype);
     std::vector<Plan> cands;
     cands.push_back(def);
-    if (def.family == FAM_NHWC || def.family == FAM_HALO) {
+    if (def.family == FAM_NCHW_VIA_NHWC) {
+        for (int tile = 0; tile < NHWC_TILE_COUNT; ++tile) {
+            Plan c = def;
+            c.nh.tile = tile;
+            cands.push_back(c);
+        }
+    } else if (def.family == FAM_NHWC || def.family == FAM_HALO) {
         if (halo_fits(a, layout, dtype)) {
             for (int th : {4, 8}) {
                 if (!halo_th_ok(a, th)) continue;
@@ -1027,7 +1040,7 @@ int tune_run(int N, int H, int W, int Cin, int Cout, int kh, int kw, int stride,
     *best_out = cands[(size_t)best];
     *best_us = best_ms * 1e3f / (float)reps;
     // record the winner (only for the families the planner looks up)
-    if (best_out->family == FAM_NHWC || best_out->family == FAM_HALO) {
+    if (best_out->family == FAM_NHWC || best_out->family == FAM_HALO || best_out->family == FAM_NCHW_VIA_NHWC) {
         const std::string dev = device_tag();
         if (!dev.empty()) {
             TunedEntry t{best_out->family, best_out->nh.tile, best_out->nh.splits, best_out->halo.th};
@@ -1211,6 +1224,8 @@ int conv2d_tune_load(const char *path) {
         for (const char *c = key; *c; ++c) bars += *c == '|';
         const bool ok = got == 5 && bars == 12 && ((t.family == FAM_NHWC && t.tile >= 0 && t.tile < NHWC_TILE_COUNT &&
                                                     t.splits >= 1 && t.splits <= 4) ||
+                                                   (t.family == FAM_NCHW_VIA_NHWC && t.tile >= 0 &&
+                                                    t.tile < NHWC_TILE_COUNT && t.splits == 1) ||
                                                    (t.family == FAM_HALO && (t.th == 4 || t.th == 8)));
         if (!ok) {
             fclose(f);

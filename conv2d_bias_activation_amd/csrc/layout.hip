@@ -1,5 +1,5 @@
 // Layout conversion for channel-first layers: the input map NCHW -> NHWC and the
-// weight OIHW -> OHWI, so that a channel-first call can run on the channel-last
+// weight OIHW -> OHWI (weights under 2^31 elements, as the library requires), so that a channel-first call can run on the channel-last
 // matrix-core kernel (whose patch rows and weight rows are then contiguous channel
 // runs). Both are pure data movement.
 #include "common.hpp"
@@ -29,31 +29,74 @@ __global__ __launch_bounds__(256) void nchw_to_nhwc_kernel(const T *__restrict__
     }
 }
 
-// w[co][ci][t] -> w2[co][t][ci], t = ky*kw + kx; one thread per element.
+// The same transposition with 16-byte accesses on both sides, for C % 8 == 0, HW % 8 ==
+// 0 and 16-byte aligned pointers: a thread reads 8 pixels of one channel, the block
+// writes them to LDS as [channel][pixel], and a thread then gathers 8 channels of one
+// pixel into one 16-byte store.
+template <typename T>
+__global__ __launch_bounds__(256) void nchw_to_nhwc_vec_kernel(const T *__restrict__ x, T *__restrict__ y, int C,
+                                                               int HW) {
+    __shared__ T tile[64][64 + 2];
+    const int n = blockIdx.z;
+    const int c0 = blockIdx.y * 64, p0 = blockIdx.x * 64;
+    const T *xn = x + (size_t)n * C * HW;
+    T *yn = y + (size_t)n * HW * C;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int v = tid + 256 * q;        // 512 vectors: 64 channels x 8 pixel runs
+        const int c = v >> 3, pv = v & 7;   // channel, run of 8 pixels
+        const int cc = c0 + c, pp = p0 + pv * 8;
+        u32x4 d = {0u, 0u, 0u, 0u};
+        if (cc < C && pp < HW) d = *reinterpret_cast<const u32x4 *>(xn + (size_t)cc * HW + pp);
+        T e[8];
+        __builtin_memcpy(e, &d, 16);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) tile[c][pv * 8 + k] = e[k];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int v = tid + 256 * q;        // 512 vectors: 64 pixels x 8 channel runs
+        const int p = v >> 3, cv = v & 7;
+        const int pp = p0 + p, cc = c0 + cv * 8;
+        if (pp < HW && cc < C) {
+            T e[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) e[k] = tile[cv * 8 + k][p];
+            u32x4 d;
+            __builtin_memcpy(&d, e, 16);
+            *reinterpret_cast<u32x4 *>(yn + (size_t)pp * C + cc) = d;
+        }
+    }
+}
+
+// w[co][ci][t] -> w2[co][t][ci], t = ky*kw + kx: one thread per (co, ci) reads that
+// pair's `taps` contiguous values and writes them at stride Cin (neighbouring threads
+// write neighbouring elements). The host keeps Cout * Cin * taps under 2^31.
 template <typename T>
 __global__ __launch_bounds__(256) void oihw_to_ohwi_kernel(const T *__restrict__ w, T *__restrict__ w2,
                                                            int Cout, int Cin, int taps) {
-    const long long total = (long long)Cout * Cin * taps;
-    for (long long i = blockIdx.x * 256ll + threadIdx.x; i < total; i += (long long)gridDim.x * 256) {
-        const int ci = (int)(i % Cin);
-        const long long r = i / Cin;
-        const int t = (int)(r % taps);
-        const int co = (int)(r / taps);
-        w2[i] = w[((size_t)co * Cin + ci) * taps + t];
-    }
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= Cout * Cin) return;
+    const int co = i / Cin, ci = i - co * Cin;
+    const T *src = w + (size_t)i * taps;
+    T *dst = w2 + (size_t)co * taps * Cin + ci;
+    for (int t = 0; t < taps; ++t) dst[(size_t)t * Cin] = src[t];
 }
 
 template <typename T>
 static hipError_t to_nhwc_t(const void *x, void *y, int N, int C, int HW, const void *w, void *w2,
                             int Cout, int taps, hipStream_t st) {
     dim3 grid((HW + 63) / 64, (C + 63) / 64, N);
-    hipError_t e = launch_kernel(nchw_to_nhwc_kernel<T>, grid, dim3(256), 0, st, static_cast<const T *>(x),
-                                 static_cast<T *>(y), C, HW);
+    const bool vec = (C % 8) == 0 && (HW % 8) == 0 && (((uintptr_t)x | (uintptr_t)y) & 15) == 0;
+    hipError_t e = vec ? launch_kernel(nchw_to_nhwc_vec_kernel<T>, grid, dim3(256), 0, st,
+                                       static_cast<const T *>(x), static_cast<T *>(y), C, HW)
+                       : launch_kernel(nchw_to_nhwc_kernel<T>, grid, dim3(256), 0, st, static_cast<const T *>(x),
+                                       static_cast<T *>(y), C, HW);
     if (e != hipSuccess) return e;
-    long long total = (long long)Cout * C * taps;
-    long long blocks = (total + 255) / 256;
-    if (blocks > 8192) blocks = 8192;
-    return launch_kernel(oihw_to_ohwi_kernel<T>, dim3((unsigned)blocks), dim3(256), 0, st,
+    const long long pairs = (long long)Cout * C;
+    return launch_kernel(oihw_to_ohwi_kernel<T>, dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0, st,
                          static_cast<const T *>(w), static_cast<T *>(w2), Cout, C, taps);
 }
 

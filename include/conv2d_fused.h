@@ -333,7 +333,8 @@ int conv2d_stack_graph_destroy(conv2d_graph *g);
  * buffers; act, has_residual, layout and dtype as conv2d_fused's arguments would be),
  * times the built-in choice and, for shapes on the channel-last matrix-core kernels,
  * every tile shape and split-K depth (1-4) of the implicit-GEMM kernel and the tile
- * heights of the halo kernel: each variant runs twice, then `reps` times between two
+ * heights of the halo kernel (for channel-first 16-bit layers, which run on that
+ * kernel after a layout copy, every tile shape): each variant runs twice, then `reps` times between two
  * events on a private stream. It synchronises that stream, frees its buffers and
  * records the fastest variant in a process-wide table keyed by (device arch and
  * compute units, N, H, W, Cin, Cout, kh, kw, stride, pad, layout, dtype, residual or
