@@ -1,0 +1,43 @@
+"""The launch configuration bench.py times, checked against the oracle: the workload's
+shapes tuned on this GPU, the stem conv fused with the max pool, every layer recorded
+once into the library's stack graph and replayed. The replays must agree bit for bit
+with each other, and the last map with the oracle chain end to end."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from parity import gate, to64
+from test_gpu_conv import oracle_chain
+
+pytestmark = pytest.mark.gpu
+
+c2d = pytest.importorskip("conv2d_bias_activation_amd")
+bench = pytest.importorskip("bench")
+DEV = torch.device("cuda")
+
+
+@pytest.mark.parametrize("key,builder", [("resnet", wl.conv5_resnet18d), ("ifnet", wl.conv4_ifnet_block)])
+def test_tuned_stack_graph_end_to_end(key, builder):
+    work = builder()
+    c2d.tune_clear()
+    try:
+        tuned = bench.tune_workload(work)
+        assert tuned >= 1
+        net = bench.Net(work, DEV, fuse_pool=True)
+        assert any(L["plan"].endswith(" tuned") for L in net.layers)
+        g = c2d.StackGraph([L["op"] for L in net.layers], layout=work.layout,
+                           dtype={"bf16": c2d.DTYPE_BF16, "f16": c2d.DTYPE_F16}[work.dtype])
+        out = net.t[net.out_name]
+        outs = []
+        for _ in range(3):
+            out.zero_()
+            g.launch()
+            torch.cuda.synchronize()
+            outs.append(out.clone())
+        g.close()
+    finally:
+        c2d.tune_clear()
+    assert all(torch.equal(outs[0], o) for o in outs[1:]), "graph replays differ"
+    _, ref = oracle_chain(key, work)
+    gate(to64(outs[0]), ref[work.layers[-1].out], work.dtype, what=f"{key} tuned stack graph", elementwise=False)
