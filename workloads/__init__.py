@@ -15,6 +15,7 @@ from .inputs import (  # noqa: F401
     conv5_resnet18d,
     conv_flops,
     ifnet_deconv,
+    large_map,
     random_conv_case,
     random_deconv_case,
     random_map,

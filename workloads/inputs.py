@@ -276,3 +276,22 @@ def random_map(seed: int, shape, dtype: str) -> torch.Tensor:
     """A map of N(0,1) values in the storage dtype (upsample and concat inputs)."""
     rng = np.random.default_rng(seed)
     return to_storage(_normal(rng, shape, 1.0), dtype)
+
+
+def large_map(seed: int, n: int, h: int, w: int, c: int, dtype: str = "bf16") -> torch.Tensor:
+    """A channel-last map of n*h*w*c elements for tests at the size limits, built row by
+    row so that no full-size fp32 or fp64 temporary is needed: a seeded N(0,1) block of
+    61 x 67 pixels repeated over the map, plus a second seeded [29, c] table indexed by
+    (row + 2*column) % 29, so that a read displaced by a whole block period still sees
+    different values. Rounded to the storage dtype per row."""
+    rng = np.random.default_rng(seed)
+    base = _normal(rng, (61, 67, c), 1.0)
+    tab = _normal(rng, (29, c), 0.25)
+    cols = np.arange(w)
+    base_w = base[:, cols % 67, :]                     # [61, w, c]
+    out = torch.empty((n, h, w, c), dtype=TORCH_DTYPES[dtype])
+    for b in range(n):
+        for r in range(h):
+            row = base_w[r % 61] + tab[(r + 2 * cols) % 29]
+            out[b, r] = torch.from_numpy(row).to(TORCH_DTYPES[dtype])
+    return out
