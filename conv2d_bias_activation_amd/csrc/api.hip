@@ -587,6 +587,9 @@ int check_conv_pool(const void *x, const void *w, const float *alpha, const void
 // it is staged), the direct kernel otherwise.
 struct DeconvPlan {
     bool mfma;
+    bool all;      // Cin <= 256: the kernel that stages the whole input strip at once
+    bool x_copy;   // channel-first input copied to channel-last in the scratch first (all)
+    size_t x_off;  // byte offset of that copy in the scratch (after the packed weights)
     bool out_f32;  // y in fp32 (16-bit input)
 };
 
@@ -632,6 +635,15 @@ int check_deconv(const void *x, const void *w, const float *bias, const float *a
     const size_t wp_bytes = (size_t)16 * a->CoP * ((Cin + 63) / 64 * 64) * eb;
     p->mfma = dtype != CONV2D_DTYPE_F32 && (Cin % 8) == 0 && wp_bytes <= kScratchBytes && (nchw || aligned16(x)) &&
               xe * eb < (1ll << 31);
+    // channel-first inputs with up to 256 channels: copied to channel-last in the scratch
+    // (when that fits beside the weights) by a 16-byte transpose, then the kernel that
+    // stages the whole input strip at once (measured faster than staging element by
+    // element from the planes for the IFNet deconv; for channel-last inputs the chunked
+    // kernel measured faster)
+    p->x_off = round256(wp_bytes);
+    p->x_copy = nchw;
+    p->all = p->mfma && nchw && Cin <= 256 && N <= 65535 &&
+             p->x_off + round256((size_t)(xe * eb)) <= kScratchBytes;
     a->x_bytes = (uint32_t)(xe * eb < (1ll << 31) ? xe * eb : 0);
     a->wp_bytes = (uint32_t)wp_bytes;
     return CONV2D_OK;
@@ -858,7 +870,16 @@ int launch_op(const OpPlan &o, hipStream_t st) {
         DeconvArgs a = o.da;
         a.wp = scratch;
         e = launch_deconv_pack(a.w, scratch, a.Cin, a.Cout, a.CoP, o.dtype, st);
-        if (e == hipSuccess) e = launch_deconv_mfma(a, o.dtype, o.dp.out_f32, nchw, st);
+        if (e == hipSuccess && o.dp.all) {
+            if (o.dp.x_copy) {
+                void *xs = reinterpret_cast<char *>(scratch) + o.dp.x_off;
+                e = launch_nchw_to_nhwc(a.x, xs, a.N, a.Cin, a.H * a.W, o.dtype, st);
+                a.x = xs;
+            }
+            if (e == hipSuccess) e = launch_deconv_mfma_all(a, o.dtype, o.dp.out_f32, nchw, st);
+        } else if (e == hipSuccess) {
+            e = launch_deconv_mfma(a, o.dtype, o.dp.out_f32, nchw, st);
+        }
         return e == hipSuccess ? CONV2D_OK : hip_fail(e, "conv_transpose4x4s2 launch");
     }
     case CONV2D_OP_UPSAMPLE:
@@ -904,7 +925,8 @@ int describe_op(const OpPlan &o, char *buf, int cap) {
         break;
     case CONV2D_OP_DECONV:
         if (o.dp.mfma)
-            snprintf(tmp, sizeof tmp, "deconv4x4s2_pack+deconv4x4s2_mfma_%s %s%s",
+            snprintf(tmp, sizeof tmp, "deconv4x4s2_pack+%sdeconv4x4s2_mfma%s_%s %s%s",
+                     o.dp.all && o.dp.x_copy ? "to_nhwc+" : "", o.dp.all ? "_all" : "",
                      o.layout == CONV2D_LAYOUT_NCHW ? "nchw" : "nhwc", dtype_name(o.dtype),
                      o.dp.out_f32 ? " out f32" : "");
         else

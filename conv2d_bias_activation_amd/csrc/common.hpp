@@ -69,6 +69,15 @@ __device__ __forceinline__ float activate(int act, float v, float alpha) {
     }
 }
 
+// The same activation with the code fixed at compile time, for epilogues that select it
+// once (a switch outside the loop over their values) rather than per value.
+template <int ACT> __device__ __forceinline__ float activate_c(float v, float alpha) {
+    if constexpr (ACT == CONV2D_ACT_RELU) return v > 0.0f ? v : 0.0f;
+    if constexpr (ACT == CONV2D_ACT_SILU) return v * __builtin_amdgcn_rcpf(1.0f + __expf(-v));
+    if constexpr (ACT == CONV2D_ACT_PRELU) return v >= 0.0f ? v : alpha * v;
+    return v;
+}
+
 // bias, residual (before or after the activation) and activation of one output.
 __device__ __forceinline__ float epilogue(float acc, float bias, float alpha, float r,
                                           bool has_res, int act, bool res_before) {

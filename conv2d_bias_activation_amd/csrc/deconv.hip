@@ -13,6 +13,8 @@
 // lanes take them as MFMA B operands, so that each wave-wide weight load reads one
 // contiguous kilobyte; a workgroup stages three input rows of a 34-pixel strip once
 // and its four waves (one per class) read shifted views of it.
+#include <type_traits>
+
 #include "common.hpp"
 #include "igemm_common.hpp"
 #include "kernels.hpp"
@@ -199,19 +201,19 @@ __global__ __launch_bounds__(256) void deconv_mfma_kernel(DeconvArgs a) {
         load_chunk(c0 + DC_KC);
         load_b(c + 1);
         const T *sb = sx[c & 1];
+        // consecutive products alternate between the two pixel blocks' accumulators, so
+        // each waits on the one two instructions back rather than the one just issued
 #pragma unroll
         for (int tp = 0; tp < 4; ++tp) {
             const int ty = tp >> 1, tx = tp & 1;
 #pragma unroll
-            for (int m = 0; m < DC_MR; ++m) {
-                const T *pa = sb + ((m + py + ty) * DC_SPX + col + px + tx) * DC_PS + kq;
+            for (int ks = 0; ks < DC_KS; ++ks)
 #pragma unroll
-                for (int ks = 0; ks < DC_KS; ++ks) {
+                for (int m = 0; m < DC_MR; ++m) {
                     vec av;
-                    __builtin_memcpy(&av, pa + ks * 16, 16);
+                    __builtin_memcpy(&av, sb + ((m + py + ty) * DC_SPX + col + px + tx) * DC_PS + kq + ks * 16, 16);
                     acc[m] = Mfma32<T>::run(av, bcur[tp * DC_KS + ks], acc[m]);
                 }
-            }
         }
         store_chunk((c + 1) & 1);
         __syncthreads();
@@ -223,19 +225,164 @@ __global__ __launch_bounds__(256) void deconv_mfma_kernel(DeconvArgs a) {
     const int co = co0 + col;
     const float bv = (a.bias && co < Cout) ? a.bias[co] : 0.0f;
     const float av = (a.alpha && co < Cout) ? a.alpha[co] : 0.0f;
+    // the activation is chosen once, outside the loop over the 32 values
+    auto epi = [&](auto actc) {
+        constexpr int ACT = decltype(actc)::value;
 #pragma unroll
-    for (int m = 0; m < DC_MR; ++m)
+        for (int m = 0; m < DC_MR; ++m)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int p = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-            so[col][2 * m + py][2 * p + px] = activate(a.act, acc[m][i] + bv, av);
-        }
+            for (int i = 0; i < 16; ++i) {
+                const int p = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+                so[col][2 * m + py][2 * p + px] = activate_c<ACT>(acc[m][i] + bv, av);
+            }
+    };
+    switch (a.act) {
+    case CONV2D_ACT_RELU: epi(std::integral_constant<int, CONV2D_ACT_RELU>{}); break;
+    case CONV2D_ACT_SILU: epi(std::integral_constant<int, CONV2D_ACT_SILU>{}); break;
+    case CONV2D_ACT_PRELU: epi(std::integral_constant<int, CONV2D_ACT_PRELU>{}); break;
+    default: epi(std::integral_constant<int, CONV2D_ACT_NONE>{}); break;
+    }
     __syncthreads();
     // output rows 2*j0 .. 2*j0 + 2*DC_MR - 1 (local row lr), columns 2*i0 .. +63
     TO *__restrict__ y = static_cast<TO *>(a.y);
     const int OH = 2 * H, OW = 2 * W;
     const int oc0 = 2 * i0, or0 = 2 * j0;
     if constexpr (NCHW) {
+#pragma unroll 4
+        for (int it = 0; it < 16 * DC_MR; ++it) {
+            const int e = tid + 256 * it;
+            const int oc = e & 63, lr = (e >> 6) & (2 * DC_MR - 1), cl = e / (128 * DC_MR);
+            if (co0 + cl < Cout && oc0 + oc < OW && or0 + lr < OH)
+                y[(((size_t)n * Cout + co0 + cl) * OH + or0 + lr) * OW + oc0 + oc] = out_cast<TO>(so[cl][lr][oc]);
+        }
+    } else {
+#pragma unroll 4
+        for (int it = 0; it < 16 * DC_MR; ++it) {
+            const int e = tid + 256 * it;
+            const int cl = e & 31, oc = (e >> 5) & 63, lr = e >> 11;
+            if (co0 + cl < Cout && oc0 + oc < OW && or0 + lr < OH)
+                y[(((size_t)n * OH + or0 + lr) * OW + oc0 + oc) * Cout + co0 + cl] = out_cast<TO>(so[cl][lr][oc]);
+        }
+    }
+}
+
+// Channel-last 16-bit input with Cin % 8 == 0 and Cin <= 256 (16-byte aligned; for a
+// channel-first layer, its channel-last copy), packed weights: the same tiles and
+// products as deconv_mfma_kernel, but the whole strip (4 rows x 34 pixels x every input
+// channel) is staged in LDS at once with 16-byte loads, so a workgroup waits for one
+// round of input loads instead of one per 64-channel chunk. y channel-first (NCHW_OUT)
+// or channel-last.
+constexpr int DA_CMAX = 256;                                  // input channels staged at most
+constexpr int DA_PSMAX = DA_CMAX + 8;                         // LDS elements per pixel at most
+constexpr int DA_VQ = (DC_ROWS * DC_SPX * (DA_CMAX / 8) + 255) / 256;  // vectors per thread (17)
+
+template <typename T, typename TO, bool NCHW_OUT>
+__global__ __launch_bounds__(256) void deconv_mfma_all_kernel(DeconvArgs a) {
+    typedef typename Mfma32<T>::vec vec;
+    // the staged strip; its tail also receives the stores of lanes past the last vector
+    __shared__ __attribute__((aligned(16))) T sx[DC_ROWS * DC_SPX * DA_PSMAX + 256 * 8];
+    __shared__ float so[32][2 * DC_MR][DC_OLD];
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int py = wv >> 1, px = wv & 1;
+    const int H = a.H, W = a.W, Cin = a.Cin, Cout = a.Cout;
+    const int tiles_w = (W + DC_TW - 1) / DC_TW;
+    int t = blockIdx.x;
+    const int ib = t % tiles_w;
+    t /= tiles_w;
+    const int tiles_h = (H + DC_MR - 1) / DC_MR;
+    const int j0 = (t % tiles_h) * DC_MR, n = t / tiles_h;
+    const int i0 = ib * DC_TW;
+    const int co0 = blockIdx.y * 32;
+    const int nchp = (Cin + DC_KC - 1) / DC_KC;
+    const int CinP = nchp * DC_KC;        // staged channels: zero past Cin
+    const int PS = CinP + 8;              // LDS elements per pixel (an odd number of 16-byte slots)
+    const int CV = CinP / 8;              // 16-byte vectors per pixel
+    const int nvec = DC_ROWS * DC_SPX * CV;
+
+    // every input load of the strip in flight at once (out-of-range offsets read zero)
+    const __amdgpu_buffer_rsrc_t rx = rsrc_bytes(a.x, a.x_bytes);
+    u32x4 sv[DA_VQ];
+#pragma unroll
+    for (int q = 0; q < DA_VQ; ++q) {
+        const int idx = tid + 256 * q;
+        const int pr = idx / CV, cv = idx - pr * CV;     // pixel of the strip, channel vector
+        const int r = pr / DC_SPX, p = pr - r * DC_SPX;
+        const int iy = j0 - 1 + r, ix = i0 - 1 + p, ci = cv * 8;
+        const bool ok = idx < nvec && (unsigned)iy < (unsigned)H && (unsigned)ix < (unsigned)W && ci < Cin;
+        const uint32_t off = ok ? ((((uint32_t)n * H + iy) * W + ix) * Cin + ci) * 2u : kOob;
+        sv[q] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)off, 0, 0);
+    }
+    // weight operands of chunk 0
+    const __amdgpu_buffer_rsrc_t rw = rsrc_bytes(a.wp, a.wp_bytes);
+    const int col = lane & 31, kq = (lane >> 5) * 8;
+    const uint32_t wbase = (uint32_t)(((2 * py + px) * (a.CoP >> 5) + blockIdx.y) * nchp) * (16u * 1024u) + lane * 16u;
+    u32x4 bw[4 * DC_KS];
+    auto load_b = [&](int c) {
+        const uint32_t cb = wbase + (uint32_t)c * (16u * 1024u);
+#pragma unroll
+        for (int i = 0; i < 4 * DC_KS; ++i)
+            bw[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(c < nchp ? cb + i * 1024u : kOob), 0, 0);
+    };
+    load_b(0);
+#pragma unroll
+    for (int q = 0; q < DA_VQ; ++q) {
+        const int idx = tid + 256 * q;
+        const int pr = idx / CV, cv = idx - pr * CV;
+        const int at = idx < nvec ? pr * PS + cv * 8 : DC_ROWS * DC_SPX * DA_PSMAX + tid * 8;
+        *reinterpret_cast<u32x4 *>(&sx[at]) = sv[q];
+    }
+    __syncthreads();
+
+    f32x16 acc[DC_MR];
+#pragma unroll
+    for (int m = 0; m < DC_MR; ++m)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[m][i] = 0.0f;
+    for (int c = 0; c < nchp; ++c) {
+        vec bcur[4 * DC_KS];
+#pragma unroll
+        for (int i = 0; i < 4 * DC_KS; ++i) __builtin_memcpy(&bcur[i], &bw[i], 16);
+        load_b(c + 1);
+        const int c0 = c * DC_KC;
+#pragma unroll
+        for (int tp = 0; tp < 4; ++tp) {
+            const int ty = tp >> 1, tx = tp & 1;
+#pragma unroll
+            for (int ks = 0; ks < DC_KS; ++ks)
+#pragma unroll
+                for (int m = 0; m < DC_MR; ++m) {
+                    vec av;
+                    __builtin_memcpy(&av, &sx[((m + py + ty) * DC_SPX + col + px + tx) * PS + c0 + kq + ks * 16], 16);
+                    acc[m] = Mfma32<T>::run(av, bcur[tp * DC_KS + ks], acc[m]);
+                }
+        }
+    }
+
+    const int co = co0 + col;
+    const float bv = (a.bias && co < Cout) ? a.bias[co] : 0.0f;
+    const float av = (a.alpha && co < Cout) ? a.alpha[co] : 0.0f;
+    auto epi = [&](auto actc) {
+        constexpr int ACT = decltype(actc)::value;
+#pragma unroll
+        for (int m = 0; m < DC_MR; ++m)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int p = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+                so[col][2 * m + py][2 * p + px] = activate_c<ACT>(acc[m][i] + bv, av);
+            }
+    };
+    switch (a.act) {
+    case CONV2D_ACT_RELU: epi(std::integral_constant<int, CONV2D_ACT_RELU>{}); break;
+    case CONV2D_ACT_SILU: epi(std::integral_constant<int, CONV2D_ACT_SILU>{}); break;
+    case CONV2D_ACT_PRELU: epi(std::integral_constant<int, CONV2D_ACT_PRELU>{}); break;
+    default: epi(std::integral_constant<int, CONV2D_ACT_NONE>{}); break;
+    }
+    __syncthreads();
+    TO *__restrict__ y = static_cast<TO *>(a.y);
+    const int OH = 2 * H, OW = 2 * W;
+    const int oc0 = 2 * i0, or0 = 2 * j0;
+    if constexpr (NCHW_OUT) {
 #pragma unroll 4
         for (int it = 0; it < 16 * DC_MR; ++it) {
             const int e = tid + 256 * it;
@@ -340,6 +487,26 @@ hipError_t launch_deconv_mfma(const DeconvArgs &a, int dtype, bool out_f32, bool
         return out_f32 ? mfma_t<bf16, float>(a, nchw, st) : mfma_t<bf16, bf16>(a, nchw, st);
     case CONV2D_DTYPE_F16:
         return out_f32 ? mfma_t<f16, float>(a, nchw, st) : mfma_t<f16, f16>(a, nchw, st);
+    default:
+        return hipErrorInvalidValue;
+    }
+}
+
+template <typename T, typename TO>
+static hipError_t mfma_all_t(const DeconvArgs &a, bool nchw_out, hipStream_t st) {
+    const long long tiles = (long long)a.N * ((a.H + DC_MR - 1) / DC_MR) * ((a.W + DC_TW - 1) / DC_TW);
+    dim3 grid((unsigned)tiles, (unsigned)(a.CoP / 32));
+    (void)nchw_out;
+    return launch_kernel(deconv_mfma_all_kernel<T, TO, true>, grid, dim3(256), 0, st, a);
+}
+
+hipError_t launch_deconv_mfma_all(const DeconvArgs &a, int dtype, bool out_f32, bool nchw_out, hipStream_t st) {
+    if (a.Cin > DA_CMAX || (a.Cin % 8) != 0 || !nchw_out) return hipErrorInvalidValue;  // channel-first layers only
+    switch (dtype) {
+    case CONV2D_DTYPE_BF16:
+        return out_f32 ? mfma_all_t<bf16, float>(a, nchw_out, st) : mfma_all_t<bf16, bf16>(a, nchw_out, st);
+    case CONV2D_DTYPE_F16:
+        return out_f32 ? mfma_all_t<f16, float>(a, nchw_out, st) : mfma_all_t<f16, f16>(a, nchw_out, st);
     default:
         return hipErrorInvalidValue;
     }

@@ -129,6 +129,15 @@ hipError_t launch_deconv_pack(const void *w, void *wp, int Cin, int Cout, int Co
 // channel-first; y in the input's type or (out_f32) fp32.
 hipError_t launch_deconv_mfma(const DeconvArgs &a, int dtype, bool out_f32, bool nchw, hipStream_t st);
 
+// The same products with the whole input strip staged at once: channel-last x (the
+// channel-last copy of a channel-first layer's input) with Cin % 8 == 0 and Cin <= 256;
+// y channel-first (nchw_out must be true).
+hipError_t launch_deconv_mfma_all(const DeconvArgs &a, int dtype, bool out_f32, bool nchw_out, hipStream_t st);
+
+// Channel-first 16-bit map to channel-last (N planes of C x HW; 16-byte accesses when C
+// and HW are multiples of 8 and both pointers are 16-byte aligned).
+hipError_t launch_nchw_to_nhwc(const void *x, void *y, int N, int C, int HW, int dtype, hipStream_t st);
+
 // Any layout and type, one thread per output (weights in the caller's layout).
 hipError_t launch_deconv_direct(const DeconvArgs &a, int dtype, bool out_f32, bool nchw, hipStream_t st);
 

@@ -100,6 +100,25 @@ static hipError_t to_nhwc_t(const void *x, void *y, int N, int C, int HW, const 
                          static_cast<const T *>(w), static_cast<T *>(w2), Cout, C, taps);
 }
 
+hipError_t launch_nchw_to_nhwc(const void *x, void *y, int N, int C, int HW, int dtype, hipStream_t st) {
+    dim3 grid((HW + 63) / 64, (C + 63) / 64, N);
+    const bool vec = (C % 8) == 0 && (HW % 8) == 0 && (((uintptr_t)x | (uintptr_t)y) & 15) == 0;
+    switch (dtype) {
+    case CONV2D_DTYPE_BF16:
+        return vec ? launch_kernel(nchw_to_nhwc_vec_kernel<bf16>, grid, dim3(256), 0, st, static_cast<const bf16 *>(x),
+                                   static_cast<bf16 *>(y), C, HW)
+                   : launch_kernel(nchw_to_nhwc_kernel<bf16>, grid, dim3(256), 0, st, static_cast<const bf16 *>(x),
+                                   static_cast<bf16 *>(y), C, HW);
+    case CONV2D_DTYPE_F16:
+        return vec ? launch_kernel(nchw_to_nhwc_vec_kernel<f16>, grid, dim3(256), 0, st, static_cast<const f16 *>(x),
+                                   static_cast<f16 *>(y), C, HW)
+                   : launch_kernel(nchw_to_nhwc_kernel<f16>, grid, dim3(256), 0, st, static_cast<const f16 *>(x),
+                                   static_cast<f16 *>(y), C, HW);
+    default:
+        return hipErrorInvalidValue;
+    }
+}
+
 hipError_t launch_to_channel_last(const void *x, void *x_nhwc, int N, int C, int HW, const void *w,
                                   void *w_ohwi, int Cout, int taps, int dtype, hipStream_t st) {
     switch (dtype) {

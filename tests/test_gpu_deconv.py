@@ -40,6 +40,9 @@ CASES = [
     (3, 3, 33, 24, 40, "relu", "nchw", "f16", "f16", "mfma"),
     (1, 1, 1, 8, 4, "relu", "nhwc", "bf16", "bf16", "mfma"),         # 1x1 input
     (1, 2, 65, 8, 1, "silu", "nhwc", "f16", "f16", "mfma"),          # one output channel
+    (1, 7, 40, 264, 40, "prelu", "nhwc", "bf16", "bf16", "mfma"),    # Cin > 256: chunked ring, K tail
+    (1, 9, 35, 320, 33, "relu", "nchw", "f16", "f32", "mfma"),       # chunked, channel-first staging
+    (3, 5, 21, 256, 8, "silu", "nchw", "bf16", "bf16", "mfma"),      # whole strip, channel-first copy
     (1, 6, 9, 12, 7, "relu", "nhwc", "bf16", "bf16", "direct"),      # Cin % 8 != 0
     (1, 6, 9, 16, 7, "prelu", "nhwc", "f32", "f32", "direct"),
     (2, 5, 6, 10, 3, "silu", "nchw", "f32", "f32", "direct"),
