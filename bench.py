@@ -5,7 +5,9 @@ One step is one forward pass of the ResNet-18-D-style backbone (N=4, 640x640x3,
 NHWC bf16: 22 fused convs, 1 max pool, 3 average pools; 134.09 GFLOP), which
 runs every part of the path: the low-Cin stem kernel, the matrix-core implicit
 GEMM for 3x3 (stride 1 and 2) and 1x1 convs with bias, ReLU and the residual
-fused in the epilogue, and both pools. All inputs, weights and output buffers
+fused in the epilogue, and both pools. The stem's last conv and the max pool run
+as one call; the 25 calls are recorded once into the library's stack graph and
+replayed. All inputs, weights and output buffers
 are resident in device memory before timing starts. The metric is conv TFLOP/s
 = sum over convs of 2*N*OH*OW*Cout*Cin*kh*kw, divided by the step time.
 
@@ -61,6 +63,9 @@ def parse():
                         "rocprofv3 --pmc outputs (FETCH_SIZE, WRITE_SIZE), then exit")
     p.add_argument("--no-fuse-pool", action="store_true",
                    help="run a conv and the max pool after it as two calls")
+    p.add_argument("--fuse-shortcut", action="store_true",
+                   help="run each average pool + 1x1 shortcut conv as one conv2d_avgpool2x2_conv1x1 call (measured "
+                        "slower than the two calls on MI355X: the per-call weight expansion and the 4x deeper GEMM)")
     p.add_argument("--workload", choices=list(WORKLOADS), default="resnet18d",
                    help="the backbone (default; the headline) or one of the other layer configs")
     p.add_argument("--no-tune", action="store_true",
@@ -78,7 +83,7 @@ def parse():
 class Net:
     """The backbone's layers with preallocated device buffers and prebuilt C-ABI arguments."""
 
-    def __init__(self, work, dev, fuse_pool=True):
+    def __init__(self, work, dev, fuse_pool=True, fuse_shortcut=False):
         import torch
 
         import conv2d_bias_activation_amd as c2d
@@ -152,6 +157,35 @@ class Net:
                 self.layers.append(dict(name=spec.name, fn=self.lib.conv2d_fused, args=args,
                                         flops=flops, bytes=nbytes, plan=plan, keep=keep, op=op))
             else:
+                nxt = work.layers[i + 1] if i + 1 < len(work.layers) else None
+                if (fuse_shortcut and spec.kind == "avg" and nxt is not None and hasattr(nxt, "cin") and nxt.k == 1
+                        and nxt.stride == 1 and nxt.pad == 0 and nxt.src == spec.out and not nxt.res
+                        and readers.get(spec.out) == 1):
+                    # the ResNet-D shortcut in one call: average pool + 1x1 conv, the pooled map
+                    # never written
+                    oh, ow = h // 2, w // 2
+                    out = torch.empty((n, nxt.cout, oh, ow) if nchw else (n, oh, ow, nxt.cout), dtype=src.dtype,
+                                      device=dev)
+                    wdev, bdev = nxt.w.to(dev), nxt.bias.to(dev)
+                    adev = nxt.alpha.to(dev) if nxt.alpha is not None else None
+                    act = {"none": 0, "relu": 1, "silu": 2, "prelu": 3}[nxt.act]
+                    args = [ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(wdev.data_ptr()),
+                            ctypes.c_void_p(bdev.data_ptr()),
+                            ctypes.c_void_p(adev.data_ptr()) if adev is not None else None,
+                            ctypes.c_void_p(out.data_ptr()), n, h, w, c, nxt.cout, act, lay, dt]
+                    op = c2d.Op(c2d.OP_AVGPOOL_CONV1X1, src.data_ptr(), wdev.data_ptr(), bdev.data_ptr(),
+                                adev.data_ptr() if adev is not None else None, None, out.data_ptr(), n, h, w, c,
+                                nxt.cout, 1, 1, 1, 0, act)
+                    flops = 2 * n * oh * ow * nxt.cout * c  # the 1x1 conv's own flops
+                    nbytes = esz * (src.numel() + nxt.w.numel() + out.numel()) + 4 * nxt.cout * (
+                        2 if adev is not None else 1)
+                    plan = c2d.stack_plan([op], 0, layout=["nhwc", "nchw"][lay], dtype=dt)
+                    self.layers.append(dict(name=spec.name + "+" + nxt.name, fn=self.lib.conv2d_avgpool2x2_conv1x1,
+                                            args=args, flops=flops, bytes=nbytes, plan=plan,
+                                            keep=(wdev, bdev, adev), op=op))
+                    self.t[nxt.out] = out
+                    skip.add(i + 1)
+                    continue
                 if spec.kind == "max":
                     oh, ow, fn = (h - 1) // 2 + 1, (w - 1) // 2 + 1, self.lib.maxpool3x3s2
                     plan = "maxpool3x3s2"
@@ -367,7 +401,7 @@ def write_traffic(src, copy_mib, plan):
     print(json.dumps(rec))
 
 
-def tune_workload(work):
+def tune_workload(work, fuse_shortcut=False):
     """Set-up, outside the timed region: time the kernel variants of each distinct conv
     shape of the workload on this GPU (conv2d_tune) so the stack picks the fastest.
     Returns the number of shapes tuned."""
@@ -376,6 +410,7 @@ def tune_workload(work):
     dt = {"f32": c2d.DTYPE_F32, "bf16": c2d.DTYPE_BF16, "f16": c2d.DTYPE_F16}[work.dtype]
     nchw = work.layout == "nchw"
     shapes = {"x": tuple(work.x.shape)}
+    pooled_from = {}  # average-pool output -> the pool's input size (n, h, w, c)
     seen = set()
     for spec in work.layers:
         src = shapes[spec.src]
@@ -393,7 +428,18 @@ def tune_workload(work):
         else:
             oh, ow = ((h - 1) // 2 + 1, (w - 1) // 2 + 1) if spec.kind == "max" else (h // 2, w // 2)
             oshape = (n, c, oh, ow) if nchw else (n, oh, ow, c)
+            if spec.kind == "avg":
+                pooled_from[spec.out] = (n, h, w, c)
         shapes[spec.out] = oshape
+    # with fused shortcuts an average pool feeding a 1x1 conv runs as one 2x2 stride-2
+    # conv: tune that shape too
+    for spec in (work.layers if fuse_shortcut else []):
+        if hasattr(spec, "cin") and spec.k == 1 and spec.stride == 1 and spec.pad == 0 and spec.src in pooled_from:
+            n, h, w, c = pooled_from[spec.src]
+            key = (n, h, w, c, spec.cout, 2, 2, 0, spec.act, False, False)
+            if key not in seen:
+                seen.add(key)
+                c2d.tune(n, h, w, c, spec.cout, 2, 2, 2, 0, spec.act, layout=work.layout, dtype=dt, reps=10)
     return len(seen)
 
 
@@ -507,10 +553,10 @@ def main():
     if args.tune_in:
         tuned = c2d.tune_load(args.tune_in)
     elif not args.no_tune:
-        tuned = tune_workload(work)
+        tuned = tune_workload(work, fuse_shortcut=args.fuse_shortcut)
         if args.tune_out:
             c2d.tune_save(args.tune_out)
-    net = Net(work, dev, fuse_pool=not args.no_fuse_pool)
+    net = Net(work, dev, fuse_pool=not args.no_fuse_pool, fuse_shortcut=args.fuse_shortcut)
     if args.launch_plan:
         h = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
         chosen = [L for L in net.layers if L["plan"].replace(" tuned", "") == args.launch_plan.replace(" tuned", "")]
@@ -583,8 +629,9 @@ def main():
         "dtype": work.dtype,
         "data": "synthetic: seeded PCG64 tensors with the shapes and value ranges of the pages' layers (workloads/inputs.py)",
         "config": {"workload": config_name, "global_batch": int(work.x.shape[0]),
-                   "convs": sum(1 for L in net.layers if L["flops"]),
-                   "pools": sum(1 for L in net.layers if not L["flops"]),
+                   "convs": sum(1 for spec in work.layers if hasattr(spec, "cin")),
+                   "pools": sum(1 for spec in work.layers if not hasattr(spec, "cin")),
+                   "calls_per_step": len(net.layers),
                    "gflop_per_step": round(net.flops / 1e9, 3), "launch": args.mode,
                    "tuned_shapes": tuned},
         "roofline": roof,

@@ -18,7 +18,8 @@ __all__ = ["conv2d_fused", "conv2d_fused_maxpool3x3s2", "maxpool3x3s2", "avgpool
            "check_args", "plan", "plan_maxpool", "Op", "conv_op", "pool_op", "copy_op", "stack_check",
            "stack_plan", "stack_run", "StackGraph", "conv_transpose4x4s2", "plan_deconv",
            "upsample_nearest2x", "concat_channels", "upsample2x_concat", "deconv_op", "upsample_op",
-           "concat_op", "tune", "tune_save", "tune_load", "tune_clear",
+           "concat_op", "tune", "tune_save", "tune_load", "tune_clear", "avgpool2x2_conv1x1",
+           "pool_conv_op",
            "last_error", "library_path", "Conv2dError", "ACT_NONE", "ACT_RELU", "ACT_SILU",
            "ACT_PRELU", "RES_BEFORE_ACT", "LAYOUT_NHWC", "LAYOUT_NCHW", "DTYPE_F32",
            "DTYPE_BF16", "DTYPE_F16"]
@@ -40,7 +41,7 @@ _LIB_PATH = os.path.join(_HERE, "libconv2d_fused.so")
 # Every exported symbol of the C ABI, with (restype, argtypes).
 _vp, _fp, _i, _cp = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_char_p
 OP_CONV, OP_CONV_MAXPOOL, OP_MAXPOOL, OP_AVGPOOL, OP_COPY = 0, 1, 2, 3, 4
-OP_DECONV, OP_UPSAMPLE, OP_CONCAT, OP_UPSAMPLE_CONCAT = 5, 6, 7, 8
+OP_DECONV, OP_UPSAMPLE, OP_CONCAT, OP_UPSAMPLE_CONCAT, OP_AVGPOOL_CONV1X1 = 5, 6, 7, 8, 9
 
 
 class Op(ctypes.Structure):
@@ -77,6 +78,7 @@ SIGNATURES = {
     "conv2d_tune_save": (_i, [_cp]),
     "conv2d_tune_load": (_i, [_cp]),
     "conv2d_tune_clear": (_i, []),
+    "conv2d_avgpool2x2_conv1x1": (_i, [_vp, _vp, _fp, _fp, _vp] + [_i] * 8 + [_vp]),
     "conv2d_last_error": (_cp, []),
     "conv2d_abi_version": (_i, []),
 }
@@ -533,3 +535,26 @@ def tune_load(path) -> int:
 def tune_clear():
     """Forget every tuned plan."""
     _check(_load().conv2d_tune_clear())
+
+
+def avgpool2x2_conv1x1(x, w, bias=None, alpha=None, *, act="none", layout="nhwc", out=None, stream=None):
+    """act(conv1x1(avgpool2x2(x), w) + bias) in one call (the ResNet-D shortcut); w is the
+    1x1 conv's weight ([Cout, 1, 1, Cin] for "nhwc", [Cout, Cin, 1, 1] for "nchw"). See
+    include/conv2d_fused.h, conv2d_avgpool2x2_conv1x1."""
+    lib = _load()
+    lay, dt, (N, H, W, Cin, Cout, kh, kw), _ = _conv_args(x, w, bias, alpha, 1, 0, layout)
+    if (kh, kw) != (1, 1):
+        raise ValueError("w must be a 1x1 conv weight")
+    yshape = (N, H // 2, W // 2, Cout) if layout == "nhwc" else (N, Cout, H // 2, W // 2)
+    out = _out(out, yshape, x)
+    rc = lib.conv2d_avgpool2x2_conv1x1(_ptr(x), _ptr(w), _ptr(bias), _ptr(alpha), _ptr(out), N, H, W, Cin, Cout,
+                                       _act_code(act, False), lay, dt, _stream_handle(stream))
+    _check(rc)
+    return out
+
+
+def pool_conv_op(x, w, y, bias=None, alpha=None, *, act="none", layout="nhwc"):
+    """An Op for conv2d_avgpool2x2_conv1x1 (w: the 1x1 conv weight)."""
+    N, H, W, Cin, Cout, kh, kw = _dims(x, w, layout)
+    return Op(OP_AVGPOOL_CONV1X1, x.data_ptr(), w.data_ptr(), _tensor_ptr(bias), _tensor_ptr(alpha), None,
+              y.data_ptr(), N, H, W, Cin, Cout, 1, 1, 1, 0, _act_code(act, False))

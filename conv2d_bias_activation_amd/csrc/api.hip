@@ -695,12 +695,15 @@ struct OpPlan {
     const void *b;  // concat: second input
     int Ca, Cb;     // concat channels (Cb = 0: upsample)
     bool up;        // upsample the first input
+    const void *w1;  // average pool + 1x1 conv: the caller's [Cout][Cin] weights
+    size_t w_off;    // byte offset of their 2x2 expansion in the scratch (at its end)
 };
 
 bool needs_scratch(const OpPlan &o) {
     if (o.kind == CONV2D_OP_CONV)
         return o.plan.family == FAM_NCHW_VIA_NHWC || (o.plan.family == FAM_NHWC && o.plan.nh.splits > 1);
     if (o.kind == CONV2D_OP_DECONV) return o.dp.mfma;
+    if (o.kind == CONV2D_OP_AVGPOOL_CONV1X1) return true;
     return o.kind == CONV2D_OP_CONV_MAXPOOL && o.pf.kind == POOL_TWO_KERNELS;
 }
 
@@ -762,6 +765,35 @@ int check_op(const conv2d_op &op, int layout, int dtype, OpPlan *o) {
     case CONV2D_OP_DECONV:
         return check_deconv(op.x, op.w, op.bias, op.alpha, op.y, op.N, op.H, op.W, op.Cin, op.Cout, op.act, layout,
                             dtype, dtype, &o->da, &o->dp);
+    case CONV2D_OP_AVGPOOL_CONV1X1: {
+        // the 2x2 stride-2 conv with weights w/4 on every tap (built in the scratch)
+        if (op.residual || (op.act & CONV2D_RES_BEFORE_ACT))
+            return set_error(CONV2D_EINVAL, "avgpool2x2_conv1x1 takes no residual");
+        if (!op.w) return set_error(CONV2D_EINVAL, "avgpool2x2_conv1x1: w must not be null");
+        int rc = check_conv(op.x, op.w, op.alpha, nullptr, op.y, op.N, op.H, op.W, op.Cin, op.Cout, 2, 2, 2, 0,
+                            op.act, layout, dtype, &o->a);
+        if (rc) return rc;
+        o->a.bias = op.bias;
+        if ((op.act & 0xff) != CONV2D_ACT_PRELU) o->a.alpha = nullptr;
+        const long long eb = dtype_bytes(dtype);
+        const size_t w2b = round256((size_t)op.Cout * 4 * op.Cin * eb);
+        if (w2b > kScratchBytes)
+            return set_error(CONV2D_EUNSUPPORTED, "avgpool2x2_conv1x1: the 2x2 weights exceed the %zu-byte scratch",
+                             kScratchBytes);
+        o->w1 = op.w;
+        o->w_off = kScratchBytes - w2b;
+        ConvArgs b = o->a;
+        b.w = (const void *)(uintptr_t)0x100000000ull;  // a 256-byte aligned stand-in for the scratch copy
+        Plan pl = make_plan(b, layout, dtype);
+        // the conv may use the scratch below the weights only: no split-K, and channel-first
+        // copies only where they fit
+        if (pl.family == FAM_NHWC) pl.nh.splits = 1;
+        if (pl.family == FAM_NCHW_VIA_NHWC &&
+            round256((size_t)op.N * op.H * op.W * op.Cin * eb) + w2b > o->w_off)
+            pl = igemm_plan(b, layout, dtype);
+        o->plan = pl;
+        return CONV2D_OK;
+    }
     case CONV2D_OP_UPSAMPLE:
     case CONV2D_OP_CONCAT:
     case CONV2D_OP_UPSAMPLE_CONCAT: {
@@ -887,6 +919,17 @@ int launch_op(const OpPlan &o, hipStream_t st) {
     case CONV2D_OP_UPSAMPLE_CONCAT:
         e = launch_concat(o.x, o.b, o.y, o.N, o.H, o.W, o.Ca, o.Cb, o.up, nchw, o.dtype, o.vec, st);
         return e == hipSuccess ? CONV2D_OK : hip_fail(e, "upsample/concat launch");
+    case CONV2D_OP_AVGPOOL_CONV1X1: {
+        float *scratch = nullptr;
+        int rc = get_scratch(&scratch);
+        if (rc) return rc;
+        void *w2 = reinterpret_cast<char *>(scratch) + o.w_off;
+        e = launch_pool_weights(o.w1, w2, o.a.Cout, o.a.Cin, nchw, o.dtype, st);
+        if (e != hipSuccess) return hip_fail(e, "avgpool2x2_conv1x1 launch");
+        ConvArgs a = o.a;
+        a.w = w2;
+        return launch_conv(a, o.plan, o.layout, o.dtype, st);
+    }
     default:
         return set_error(CONV2D_EINVAL, "unknown op kind %d", o.kind);
     }
@@ -932,6 +975,12 @@ int describe_op(const OpPlan &o, char *buf, int cap) {
         else
             snprintf(tmp, sizeof tmp, "deconv4x4s2_direct %s%s", dtype_name(o.dtype), o.dp.out_f32 ? " out f32" : "");
         break;
+    case CONV2D_OP_AVGPOOL_CONV1X1: {
+        char inner[160];
+        describe(o.plan, o.layout, o.dtype, inner, sizeof inner);
+        snprintf(tmp, sizeof tmp, "pool_weights+%s", inner);
+        break;
+    }
     case CONV2D_OP_UPSAMPLE:
     case CONV2D_OP_CONCAT:
     case CONV2D_OP_UPSAMPLE_CONCAT:
@@ -1079,7 +1128,7 @@ int tune_run(int N, int H, int W, int Cin, int Cout, int kh, int kw, int stride,
 
 extern "C" {
 
-int conv2d_abi_version(void) { return 4; }
+int conv2d_abi_version(void) { return 5; }
 
 const char *conv2d_last_error(void) { return g_err.c_str(); }
 
@@ -1268,6 +1317,12 @@ int conv2d_tune_clear(void) {
     g_tuned.clear();
     g_tuned_n.store(0, std::memory_order_release);
     return set_ok();
+}
+
+int conv2d_avgpool2x2_conv1x1(const void *x, const void *w, const float *bias, const float *alpha, void *y, int N,
+                              int H, int W, int Cin, int Cout, int act, int layout, int dtype, void *stream) {
+    const conv2d_op op{CONV2D_OP_AVGPOOL_CONV1X1, x, w, bias, alpha, nullptr, y, N, H, W, Cin, Cout, 1, 1, 1, 0, act};
+    return run_one(op, layout, dtype, stream);
 }
 
 int conv2d_stack_check(const conv2d_op *ops, int n, int layout, int dtype, int *bad_index) {

@@ -226,6 +226,28 @@ int concat_channels(const void *a, const void *b, void *y, int N, int H, int W, 
 int upsample2x_concat(const void *a, const void *b, void *y, int N, int H, int W, int Ca, int Cb, int layout,
                       int dtype, void *stream);
 
+/*
+ * y = act(conv1x1(avgpool2x2(x), w) + bias): the ResNet-D shortcut of a downsampling
+ * block in one call (inferencelayer page, `encoder_maps`: the 2x2 average pool, then
+ * the 1x1 projection conv, run there as `AVGPOOL_SRC` and a GEMM).
+ *
+ * x      [N,H,W,Cin] or [N,Cin,H,W] in `dtype`, H, W >= 2 (required)
+ * w      the 1x1 conv's weights [Cout][Cin] in `dtype` ([Cout,1,1,Cin] or [Cout,Cin,1,1])
+ * bias   fp32 [Cout] or NULL; alpha fp32 [Cout], required when act is PRELU
+ * y      [N,H/2,W/2,Cout] or [N,Cout,H/2,W/2] (floor: an odd last row or column of x
+ *        is dropped, as by avgpool2x2), may not overlap x
+ * act    CONV2D_ACT_* (no residual flag)
+ *
+ * Computed as the 2x2 stride-2 conv whose every tap holds w/4 (written into the end of
+ * the library's per-device scratch, Cout*4*Cin elements, then the conv kernels), so the
+ * pooled map is neither rounded to `dtype` nor written: the result equals
+ * conv2d_fused(avgpool2x2(x)) up to the pooled map's one rounding and fp32
+ * accumulation order. (w/4 is exact, except that in f16 a quarter of a weight below
+ * 2^-12 is subnormal.) Shares the scratch as conv2d_fused does; errors as conv2d_fused.
+ */
+int conv2d_avgpool2x2_conv1x1(const void *x, const void *w, const float *bias, const float *alpha, void *y, int N,
+                              int H, int W, int Cin, int Cout, int act, int layout, int dtype, void *stream);
+
 /* floor((in + 2*pad - k)/stride) + 1, or -1 if in, k, stride <= 0, pad < 0 or the
  * kernel does not fit the padded input (inferencelayer `conv()`). Host only. */
 int conv2d_out_dim(int in, int k, int stride, int pad);
@@ -272,6 +294,8 @@ int conv2d_plan(int N, int H, int W, int Cin, int Cout, int kh, int kw, int stri
  *                           Cb = Cout)
  *   CONV2D_OP_UPSAMPLE_CONCAT upsample2x_concat(a = x, b = residual, y, N, H, W,
  *                           Ca = Cin, Cb = Cout)
+ *   CONV2D_OP_AVGPOOL_CONV1X1 conv2d_avgpool2x2_conv1x1(x, w, bias, alpha, y, N, H, W,
+ *                           Cin, Cout, act); residual must be NULL
  * Layout and dtype are shared by the whole stack.
  */
 #define CONV2D_OP_CONV 0
@@ -283,6 +307,7 @@ int conv2d_plan(int N, int H, int W, int Cin, int Cout, int kh, int kw, int stri
 #define CONV2D_OP_UPSAMPLE 6
 #define CONV2D_OP_CONCAT 7
 #define CONV2D_OP_UPSAMPLE_CONCAT 8
+#define CONV2D_OP_AVGPOOL_CONV1X1 9
 
 typedef struct conv2d_op {
     int kind;
@@ -368,7 +393,7 @@ int conv2d_tune_clear(void);
  * valid until the thread's next call into the library. */
 const char *conv2d_last_error(void);
 
-/* ABI version of this header: 4 (3 plus the tuning calls; 3 added the transposed conv,
+/* ABI version of this header: 5 (4 plus conv2d_avgpool2x2_conv1x1; 4 added the tuning calls; 3 added the transposed conv,
  * upsample and concat calls and their stack ops; 2 the stack calls and the fused conv +
  * max pool). */
 int conv2d_abi_version(void);

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     for name in names:
         assert hasattr(lib, name), name
     assert names == set(c2d.SIGNATURES)
-    assert c2d._load().conv2d_abi_version() == 4
+    assert c2d._load().conv2d_abi_version() == 5
 
 
 def test_out_dim():
@@ -255,3 +255,28 @@ def test_tune_table_file_round_trip(tmp_path):
     assert c2d.tune_save(str(out)) == 2  # failed loads added nothing
     c2d.tune_clear()
     assert c2d.tune_save(str(out)) == 0
+
+
+def test_avgpool_conv1x1_plan_and_checks():
+    """Host only: the fused shortcut call validates like a 2x2 stride-2 conv, names its
+    kernels, never splits K (its weights sit at the end of the scratch) and rejects a
+    residual."""
+    G = 1 << 32
+    op = c2d.Op(c2d.OP_AVGPOOL_CONV1X1, G, 3 * G, None, None, None, 5 * G, 4, 160, 160, 64, 128, 1, 1, 1, 0, 0)
+    assert c2d.stack_check([op]) == (c2d.OK, -1)
+    name = c2d.stack_plan([op], 0)
+    assert name.startswith("pool_weights+igemm_nhwc_pipe") and "splitk=1" in name, name
+    deep = c2d.Op(c2d.OP_AVGPOOL_CONV1X1, G, 3 * G, None, None, None, 5 * G, 1, 8, 8, 2048, 512, 1, 1, 1, 0, 0)
+    assert "splitk=1" in c2d.stack_plan([deep], 0)
+    f32 = c2d.stack_plan([op], 0, dtype=c2d.DTYPE_F32)
+    assert f32.startswith("pool_weights+igemm_nhwc"), f32
+    nchw = c2d.stack_plan([op], 0, layout="nchw", dtype=c2d.DTYPE_F16)
+    assert nchw.startswith("pool_weights+to_nhwc+igemm_nhwc_pipe"), nchw
+    res = c2d.Op(c2d.OP_AVGPOOL_CONV1X1, G, 3 * G, None, None, 7 * G, 5 * G, 4, 160, 160, 64, 128, 1, 1, 1, 0, 0)
+    assert c2d.stack_check([res]) == (c2d.EINVAL, 0)
+    one = c2d.Op(c2d.OP_AVGPOOL_CONV1X1, G, 3 * G, None, None, None, 5 * G, 1, 1, 9, 8, 8, 1, 1, 1, 0, 0)
+    assert c2d.stack_check([one]) == (c2d.EINVAL, 0)   # H = 1: no 2x2 window
+    lib = c2d._load()
+    P = ctypes.c_void_p
+    assert lib.conv2d_avgpool2x2_conv1x1(P(G), P(3 * G), None, None, P(G + 64), 1, 8, 8, 16, 16, 0, 0,
+                                         c2d.DTYPE_BF16, None) == c2d.EINVAL  # y overlaps x

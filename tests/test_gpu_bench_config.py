@@ -17,14 +17,19 @@ bench = pytest.importorskip("bench")
 DEV = torch.device("cuda")
 
 
-@pytest.mark.parametrize("key,builder", [("resnet", wl.conv5_resnet18d), ("ifnet", wl.conv4_ifnet_block)])
-def test_tuned_stack_graph_end_to_end(key, builder):
+@pytest.mark.parametrize("key,builder,shortcut", [("resnet", wl.conv5_resnet18d, False),
+                                                  ("resnet", wl.conv5_resnet18d, True),
+                                                  ("ifnet", wl.conv4_ifnet_block, False)])
+def test_tuned_stack_graph_end_to_end(key, builder, shortcut):
+    """shortcut: the average pool + 1x1 shortcut convs as single fused calls (bench.py
+    --fuse-shortcut)."""
     work = builder()
     c2d.tune_clear()
     try:
-        tuned = bench.tune_workload(work)
+        tuned = bench.tune_workload(work, fuse_shortcut=shortcut)
         assert tuned >= 1
-        net = bench.Net(work, DEV, fuse_pool=True)
+        net = bench.Net(work, DEV, fuse_pool=True, fuse_shortcut=shortcut)
+        assert any("pool_weights" in L["plan"] for L in net.layers) == shortcut
         assert any(L["plan"].endswith(" tuned") for L in net.layers)
         g = c2d.StackGraph([L["op"] for L in net.layers], layout=work.layout,
                            dtype={"bf16": c2d.DTYPE_BF16, "f16": c2d.DTYPE_F16}[work.dtype])
