@@ -500,6 +500,19 @@ def bench_ops(torch, dev, reps):
     add("deconv_256to128_64x64_nhwc_bf16_relu",
         c2d.plan_deconv(1, 64, 64, 256, 128, 1, c2d.LAYOUT_NHWC, c2d.DTYPE_BF16),
         lambda st: c2d.conv_transpose4x4s2(x2, w2, b2, act="relu", out=y2, stream=st), flops, nbytes)
+    # the same two layers with their weights packed once beforehand (weight residency)
+    pk = c2d.deconv_pack(w)
+    add("ifnet_deconv_240to5_68x120_nchw_f16_out_f32 prepacked",
+        c2d.plan_deconv(1, 68, 120, 240, 5, 0, c2d.LAYOUT_NCHW, c2d.DTYPE_F16, c2d.DTYPE_F32).replace(
+            "deconv4x4s2_pack+", ""),
+        lambda st: c2d.conv_transpose4x4s2_prepacked(x, pk, b, layout="nchw", out_dtype=torch.float32, out=y,
+                                                     stream=st),
+        2 * 136 * 240 * 5 * 240 * 4, 2 * (x.numel() + w.numel()) + 4 * (b.numel() + y.numel()))
+    pk2 = c2d.deconv_pack(w2)
+    add("deconv_256to128_64x64_nhwc_bf16_relu prepacked",
+        c2d.plan_deconv(1, 64, 64, 256, 128, 1, c2d.LAYOUT_NHWC, c2d.DTYPE_BF16).replace("deconv4x4s2_pack+", ""),
+        lambda st: c2d.conv_transpose4x4s2_prepacked(x2, pk2, b2, act="relu", out=y2, stream=st),
+        2 * 128 * 128 * 128 * 256 * 4, 2 * (x2.numel() + w2.numel() + y2.numel()) + 4 * b2.numel())
     # the CCFM top-down joins at a 640x640 image, batch 4: [lateral up 2x, backbone] -> 512 ch
     for hw in (20, 40):
         a = wl.random_map(6, (4, hw, hw, 256), "bf16").to(dev)

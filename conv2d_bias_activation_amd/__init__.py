@@ -19,7 +19,7 @@ __all__ = ["conv2d_fused", "conv2d_fused_maxpool3x3s2", "maxpool3x3s2", "avgpool
            "stack_plan", "stack_run", "StackGraph", "conv_transpose4x4s2", "plan_deconv",
            "upsample_nearest2x", "concat_channels", "upsample2x_concat", "deconv_op", "upsample_op",
            "concat_op", "tune", "tune_save", "tune_load", "tune_clear", "avgpool2x2_conv1x1",
-           "pool_conv_op",
+           "pool_conv_op", "deconv_pack", "conv_transpose4x4s2_prepacked",
            "last_error", "library_path", "Conv2dError", "ACT_NONE", "ACT_RELU", "ACT_SILU",
            "ACT_PRELU", "RES_BEFORE_ACT", "LAYOUT_NHWC", "LAYOUT_NCHW", "DTYPE_F32",
            "DTYPE_BF16", "DTYPE_F16"]
@@ -79,6 +79,9 @@ SIGNATURES = {
     "conv2d_tune_load": (_i, [_cp]),
     "conv2d_tune_clear": (_i, []),
     "conv2d_avgpool2x2_conv1x1": (_i, [_vp, _vp, _fp, _fp, _vp] + [_i] * 8 + [_vp]),
+    "conv_transpose4x4s2_packed_bytes": (_i, [_i, _i, _i, ctypes.POINTER(ctypes.c_size_t)]),
+    "conv_transpose4x4s2_pack": (_i, [_vp, _vp, _i, _i, _i, _vp]),
+    "conv_transpose4x4s2_prepacked": (_i, [_vp, _vp, _fp, _fp, _vp] + [_i] * 9 + [_vp]),
     "conv2d_last_error": (_cp, []),
     "conv2d_abi_version": (_i, []),
 }
@@ -558,3 +561,50 @@ def pool_conv_op(x, w, y, bias=None, alpha=None, *, act="none", layout="nhwc"):
     N, H, W, Cin, Cout, kh, kw = _dims(x, w, layout)
     return Op(OP_AVGPOOL_CONV1X1, x.data_ptr(), w.data_ptr(), _tensor_ptr(bias), _tensor_ptr(alpha), None,
               y.data_ptr(), N, H, W, Cin, Cout, 1, 1, 1, 0, _act_code(act, False))
+
+
+def deconv_pack(w, stream=None):
+    """Pack transposed-conv weights w [Cin, Cout, 4, 4] (bf16/f16, Cin % 8 == 0) once;
+    returns (packed tensor, Cout) for conv_transpose4x4s2_prepacked."""
+    lib = _load()
+    dt = _dtype_code(w.dtype)
+    if w.dim() != 4 or tuple(w.shape[2:]) != (4, 4):
+        raise ValueError("w must be [Cin, Cout, 4, 4]")
+    _require(w, "w", w.dtype, w.device)
+    Cin, Cout = int(w.shape[0]), int(w.shape[1])
+    nbytes = ctypes.c_size_t(0)
+    _check(lib.conv_transpose4x4s2_packed_bytes(Cin, Cout, dt, ctypes.byref(nbytes)))
+    wp = torch.empty(nbytes.value // w.element_size(), dtype=w.dtype, device=w.device)
+    _check(lib.conv_transpose4x4s2_pack(_ptr(w), _ptr(wp), Cin, Cout, dt, _stream_handle(stream)))
+    return wp, Cout
+
+
+def conv_transpose4x4s2_prepacked(x, packed, bias=None, alpha=None, *, act="none", layout="nhwc", out_dtype=None,
+                                  out=None, stream=None):
+    """conv_transpose4x4s2 with weights packed by deconv_pack (``packed`` = its result)."""
+    lib = _load()
+    wp, Cout = packed
+    lay = _LAYOUTS[layout]
+    dt = _dtype_code(x.dtype)
+    out_dtype = x.dtype if out_dtype is None else out_dtype
+    odt = _dtype_code(out_dtype)
+    if layout == "nhwc":
+        N, H, W, Cin = x.shape
+    else:
+        N, Cin, H, W = x.shape
+    dev = x.device
+    _require(x, "x", x.dtype, dev)
+    _require(wp, "wp", x.dtype, dev)
+    _require(bias, "bias", torch.float32, dev)
+    _require(alpha, "alpha", torch.float32, dev)
+    yshape = (N, 2 * H, 2 * W, Cout) if layout == "nhwc" else (N, Cout, 2 * H, 2 * W)
+    if out is None:
+        out = torch.empty(yshape, dtype=out_dtype, device=dev)
+    else:
+        _require(out, "out", out_dtype, dev)
+        if tuple(out.shape) != yshape:
+            raise ValueError(f"out must have shape {yshape}")
+    rc = lib.conv_transpose4x4s2_prepacked(_ptr(x), _ptr(wp), _ptr(bias), _ptr(alpha), _ptr(out), N, H, W, Cin, Cout,
+                                           _act_code(act, False), lay, dt, odt, _stream_handle(stream))
+    _check(rc)
+    return out

@@ -587,15 +587,21 @@ int check_conv_pool(const void *x, const void *w, const float *alpha, const void
 // it is staged), the direct kernel otherwise.
 struct DeconvPlan {
     bool mfma;
+    bool prepacked;  // the weights come packed by conv_transpose4x4s2_pack (da.wp)
     bool all;      // Cin <= 256: the kernel that stages the whole input strip at once
     bool x_copy;   // channel-first input copied to channel-last in the scratch first (all)
     size_t x_off;  // byte offset of that copy in the scratch (after the packed weights)
     bool out_f32;  // y in fp32 (16-bit input)
 };
 
+size_t deconv_packed_bytes(int Cin, int Cout, int eb) {
+    return (size_t)16 * ((Cout + 31) / 32 * 32) * ((Cin + 63) / 64 * 64) * eb;
+}
+
+// packed: w is the caller's copy of the packed weights (conv_transpose4x4s2_pack).
 int check_deconv(const void *x, const void *w, const float *bias, const float *alpha, const void *y, int N, int H,
                  int W, int Cin, int Cout, int act, int layout, int dtype, int out_dtype, DeconvArgs *a,
-                 DeconvPlan *p) {
+                 DeconvPlan *p, bool packed = false) {
     if (!x || !w || !y) return set_error(CONV2D_EINVAL, "conv_transpose4x4s2: x, w and y must not be null");
     if (N <= 0 || H <= 0 || W <= 0 || Cin <= 0 || Cout <= 0)
         return set_error(CONV2D_EINVAL, "conv_transpose4x4s2: sizes must be positive (N=%d H=%d W=%d Cin=%d Cout=%d)",
@@ -615,7 +621,8 @@ int check_deconv(const void *x, const void *w, const float *bias, const float *a
         return set_error(CONV2D_EUNSUPPORTED, "conv_transpose4x4s2: tensors of 2^31 or more elements are not supported");
     const int eb = dtype_bytes(dtype), ob = dtype_bytes(out_dtype);
     if (overlap(y, ye * ob, x, xe * eb)) return set_error(CONV2D_EINVAL, "conv_transpose4x4s2: y overlaps x");
-    if (overlap(y, ye * ob, w, we * eb)) return set_error(CONV2D_EINVAL, "conv_transpose4x4s2: y overlaps w");
+    const long long wbytes = packed ? (long long)deconv_packed_bytes(Cin, Cout, eb) : we * eb;
+    if (overlap(y, ye * ob, w, wbytes)) return set_error(CONV2D_EINVAL, "conv_transpose4x4s2: y overlaps w");
     *a = DeconvArgs{};
     a->x = x;
     a->w = w;
@@ -640,7 +647,20 @@ int check_deconv(const void *x, const void *w, const float *bias, const float *a
     // stages the whole input strip at once (measured faster than staging element by
     // element from the planes for the IFNet deconv; for channel-last inputs the chunked
     // kernel measured faster)
-    p->x_off = round256(wp_bytes);
+    if (packed) {
+        // caller-owned packed weights: the matrix-core path only, the scratch only for the
+        // channel-last copy of a channel-first input
+        if (!(dtype != CONV2D_DTYPE_F32 && (Cin % 8) == 0 && wp_bytes < (1ull << 31) && (nchw || aligned16(x)) &&
+              xe * eb < (1ll << 31)))
+            return set_error(CONV2D_EUNSUPPORTED,
+                             "conv_transpose4x4s2_prepacked: needs 16-bit x with Cin %% 8 == 0 (16-byte aligned "
+                             "when channel-last) under 2 GiB");
+        if (!aligned16(w)) return set_error(CONV2D_EINVAL, "conv_transpose4x4s2_prepacked: wp must be 16-byte aligned");
+        p->mfma = true;
+        p->prepacked = true;
+        a->wp = w;
+    }
+    p->x_off = packed ? 0 : round256(wp_bytes);
     p->x_copy = nchw;
     p->all = p->mfma && nchw && Cin <= 256 && N <= 65535 &&
              p->x_off + round256((size_t)(xe * eb)) <= kScratchBytes;
@@ -897,11 +917,15 @@ int launch_op(const OpPlan &o, hipStream_t st) {
             return e == hipSuccess ? CONV2D_OK : hip_fail(e, "conv_transpose4x4s2 launch");
         }
         float *scratch = nullptr;
-        int rc = get_scratch(&scratch);
-        if (rc) return rc;
         DeconvArgs a = o.da;
-        a.wp = scratch;
-        e = launch_deconv_pack(a.w, scratch, a.Cin, a.Cout, a.CoP, o.dtype, st);
+        if (!o.dp.prepacked || o.dp.all) {
+            int rc = get_scratch(&scratch);
+            if (rc) return rc;
+        }
+        if (!o.dp.prepacked) {
+            a.wp = scratch;
+            e = launch_deconv_pack(a.w, scratch, a.Cin, a.Cout, a.CoP, o.dtype, st);
+        }
         if (e == hipSuccess && o.dp.all) {
             if (o.dp.x_copy) {
                 void *xs = reinterpret_cast<char *>(scratch) + o.dp.x_off;
@@ -968,7 +992,7 @@ int describe_op(const OpPlan &o, char *buf, int cap) {
         break;
     case CONV2D_OP_DECONV:
         if (o.dp.mfma)
-            snprintf(tmp, sizeof tmp, "deconv4x4s2_pack+%sdeconv4x4s2_mfma%s_%s %s%s",
+            snprintf(tmp, sizeof tmp, "%s%sdeconv4x4s2_mfma%s_%s %s%s", o.dp.prepacked ? "" : "deconv4x4s2_pack+",
                      o.dp.all && o.dp.x_copy ? "to_nhwc+" : "", o.dp.all ? "_all" : "",
                      o.layout == CONV2D_LAYOUT_NCHW ? "nchw" : "nhwc", dtype_name(o.dtype),
                      o.dp.out_f32 ? " out f32" : "");
@@ -1128,7 +1152,7 @@ int tune_run(int N, int H, int W, int Cin, int Cout, int kh, int kw, int stride,
 
 extern "C" {
 
-int conv2d_abi_version(void) { return 5; }
+int conv2d_abi_version(void) { return 6; }
 
 const char *conv2d_last_error(void) { return g_err.c_str(); }
 
@@ -1209,6 +1233,45 @@ int conv_transpose4x4s2(const void *x, const void *w, const float *bias, const f
     o.layout = layout;
     o.dtype = dtype;
     int rc = check_deconv(x, w, bias, alpha, y, N, H, W, Cin, Cout, act, layout, dtype, out_dtype, &o.da, &o.dp);
+    if (rc) return rc;
+    rc = launch_op(o, static_cast<hipStream_t>(stream));
+    return rc ? rc : set_ok();
+}
+
+int conv_transpose4x4s2_packed_bytes(int Cin, int Cout, int dtype, size_t *bytes) {
+    if (!bytes) return set_error(CONV2D_EINVAL, "conv_transpose4x4s2_packed_bytes: bytes must not be null");
+    if (Cin <= 0 || Cout <= 0) return set_error(CONV2D_EINVAL, "conv_transpose4x4s2_packed_bytes: sizes must be positive");
+    if (dtype != CONV2D_DTYPE_BF16 && dtype != CONV2D_DTYPE_F16)
+        return set_error(CONV2D_EUNSUPPORTED, "conv_transpose4x4s2_packed_bytes: packing is for 16-bit weights");
+    *bytes = deconv_packed_bytes(Cin, Cout, 2);
+    return set_ok();
+}
+
+int conv_transpose4x4s2_pack(const void *w, void *wp, int Cin, int Cout, int dtype, void *stream) {
+    if (!w || !wp) return set_error(CONV2D_EINVAL, "conv_transpose4x4s2_pack: w and wp must not be null");
+    if (Cin <= 0 || Cout <= 0) return set_error(CONV2D_EINVAL, "conv_transpose4x4s2_pack: sizes must be positive");
+    if (dtype != CONV2D_DTYPE_BF16 && dtype != CONV2D_DTYPE_F16)
+        return set_error(CONV2D_EUNSUPPORTED, "conv_transpose4x4s2_pack: packing is for 16-bit weights");
+    if ((Cin % 8) != 0) return set_error(CONV2D_EUNSUPPORTED, "conv_transpose4x4s2_pack: Cin must be a multiple of 8");
+    const size_t wb = deconv_packed_bytes(Cin, Cout, 2);
+    if (wb >= (1ull << 31) || 16ll * Cin * Cout > kMaxElems)
+        return set_error(CONV2D_EUNSUPPORTED, "conv_transpose4x4s2_pack: packed weights of 2 GiB or more");
+    if (!aligned16(wp)) return set_error(CONV2D_EINVAL, "conv_transpose4x4s2_pack: wp must be 16-byte aligned");
+    if (overlap(wp, (long long)wb, w, 32ll * Cin * Cout))
+        return set_error(CONV2D_EINVAL, "conv_transpose4x4s2_pack: wp overlaps w");
+    hipError_t e = launch_deconv_pack(w, wp, Cin, Cout, (Cout + 31) / 32 * 32, dtype, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "conv_transpose4x4s2_pack launch");
+    return set_ok();
+}
+
+int conv_transpose4x4s2_prepacked(const void *x, const void *wp, const float *bias, const float *alpha, void *y, int N,
+                                  int H, int W, int Cin, int Cout, int act, int layout, int dtype, int out_dtype,
+                                  void *stream) {
+    OpPlan o{};
+    o.kind = CONV2D_OP_DECONV;
+    o.layout = layout;
+    o.dtype = dtype;
+    int rc = check_deconv(x, wp, bias, alpha, y, N, H, W, Cin, Cout, act, layout, dtype, out_dtype, &o.da, &o.dp, true);
     if (rc) return rc;
     rc = launch_op(o, static_cast<hipStream_t>(stream));
     return rc ? rc : set_ok();

@@ -196,6 +196,27 @@ int avgpool2x2(const void *x, void *y, int N, int H, int W, int C, int layout, i
 int conv_transpose4x4s2(const void *x, const void *w, const float *bias, const float *alpha, void *y, int N, int H,
                         int W, int Cin, int Cout, int act, int layout, int dtype, int out_dtype, void *stream);
 
+/*
+ * Weight residency for the transposed conv: pack a layer's weights once (for example at
+ * model load) into a caller-owned buffer, then run calls without the per-call repack.
+ *
+ * conv_transpose4x4s2_packed_bytes: *bytes = the packed size for (Cin, Cout) in a 16-bit
+ *   dtype (16 * ceil(Cout/32)*32 * ceil(Cin/64)*64 elements); CONV2D_EUNSUPPORTED for
+ *   fp32. Host only.
+ * conv_transpose4x4s2_pack: w [Cin][Cout][4][4] (bf16/f16, Cin % 8 == 0) -> wp, a device
+ *   buffer of that size, 16-byte aligned, not overlapping w (enqueued on `stream`).
+ * conv_transpose4x4s2_prepacked: conv_transpose4x4s2 with the packed weights wp in place
+ *   of w; needs 16-bit x with Cin % 8 == 0 (16-byte aligned when channel-last), x and wp
+ *   under 2 GiB (CONV2D_EUNSUPPORTED otherwise). Results are bit-identical to
+ *   conv_transpose4x4s2 on the unpacked weights. A channel-first input still uses the
+ *   library scratch for its channel-last copy; nothing else is written but y.
+ */
+int conv_transpose4x4s2_packed_bytes(int Cin, int Cout, int dtype, size_t *bytes);
+int conv_transpose4x4s2_pack(const void *w, void *wp, int Cin, int Cout, int dtype, void *stream);
+int conv_transpose4x4s2_prepacked(const void *x, const void *wp, const float *bias, const float *alpha, void *y, int N,
+                                  int H, int W, int Cin, int Cout, int act, int layout, int dtype, int out_dtype,
+                                  void *stream);
+
 /* Host-only: the kernel variants conv_transpose4x4s2 would launch (as conv2d_plan). */
 int conv_transpose4x4s2_plan(int N, int H, int W, int Cin, int Cout, int act, int layout, int dtype, int out_dtype,
                              char *buf, int cap);
@@ -393,7 +414,8 @@ int conv2d_tune_clear(void);
  * valid until the thread's next call into the library. */
 const char *conv2d_last_error(void);
 
-/* ABI version of this header: 5 (4 plus conv2d_avgpool2x2_conv1x1; 4 added the tuning calls; 3 added the transposed conv,
+/* ABI version of this header: 6 (5 plus the transposed conv's weight packing calls; 5
+ * added conv2d_avgpool2x2_conv1x1; 4 added the tuning calls; 3 added the transposed conv,
  * upsample and concat calls and their stack ops; 2 the stack calls and the fused conv +
  * max pool). */
 int conv2d_abi_version(void);

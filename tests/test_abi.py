@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     for name in names:
         assert hasattr(lib, name), name
     assert names == set(c2d.SIGNATURES)
-    assert c2d._load().conv2d_abi_version() == 5
+    assert c2d._load().conv2d_abi_version() == 6
 
 
 def test_out_dim():
@@ -280,3 +280,25 @@ def test_avgpool_conv1x1_plan_and_checks():
     P = ctypes.c_void_p
     assert lib.conv2d_avgpool2x2_conv1x1(P(G), P(3 * G), None, None, P(G + 64), 1, 8, 8, 16, 16, 0, 0,
                                          c2d.DTYPE_BF16, None) == c2d.EINVAL  # y overlaps x
+
+
+def test_deconv_pack_sizes_and_checks():
+    """Host only: packed sizes, and what the pack and pre-packed calls reject before launching."""
+    lib = c2d._load()
+    nb = ctypes.c_size_t(0)
+    assert lib.conv_transpose4x4s2_packed_bytes(240, 5, c2d.DTYPE_F16, ctypes.byref(nb)) == c2d.OK
+    assert nb.value == 16 * 32 * 256 * 2
+    assert lib.conv_transpose4x4s2_packed_bytes(256, 128, c2d.DTYPE_BF16, ctypes.byref(nb)) == c2d.OK
+    assert nb.value == 16 * 128 * 256 * 2
+    assert lib.conv_transpose4x4s2_packed_bytes(16, 16, c2d.DTYPE_F32, ctypes.byref(nb)) == c2d.EUNSUPPORTED
+    P = ctypes.c_void_p
+    w, wp, x, y = P(1 << 32), P(9 << 32), P(17 << 32), P(25 << 32)
+    assert lib.conv_transpose4x4s2_pack(w, wp, 12, 8, c2d.DTYPE_BF16, None) == c2d.EUNSUPPORTED   # Cin % 8
+    assert lib.conv_transpose4x4s2_pack(w, P((9 << 32) + 2), 16, 8, c2d.DTYPE_BF16, None) == c2d.EINVAL  # alignment
+    assert lib.conv_transpose4x4s2_pack(w, P((1 << 32) + 64), 16, 8, c2d.DTYPE_BF16, None) == c2d.EINVAL  # overlap
+    assert lib.conv_transpose4x4s2_prepacked(x, wp, None, None, y, 1, 8, 8, 12, 8, 0, 0, c2d.DTYPE_BF16,
+                                             c2d.DTYPE_BF16, None) == c2d.EUNSUPPORTED            # Cin % 8
+    assert lib.conv_transpose4x4s2_prepacked(x, wp, None, None, y, 1, 8, 8, 16, 8, 0, 0, c2d.DTYPE_F32,
+                                             c2d.DTYPE_F32, None) == c2d.EUNSUPPORTED             # fp32
+    assert lib.conv_transpose4x4s2_prepacked(x, P((9 << 32) + 8), None, None, y, 1, 8, 8, 16, 8, 0, 0,
+                                             c2d.DTYPE_BF16, c2d.DTYPE_BF16, None) == c2d.EINVAL  # wp alignment

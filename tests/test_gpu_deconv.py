@@ -109,3 +109,22 @@ def test_deconv_rejects_bad_arguments():
         c2d.conv_transpose4x4s2(x, w, act="prelu")  # PReLU without slopes
     with pytest.raises(c2d.Conv2dError):
         c2d.conv_transpose4x4s2(x, w, out_dtype=torch.float16)  # neither x's dtype nor fp32
+
+
+@pytest.mark.parametrize("layout,dt,odt,n,h,w,cin,cout", [
+    ("nhwc", "bf16", "bf16", 1, 16, 40, 256, 128),
+    ("nhwc", "f16", "f32", 2, 9, 37, 40, 33),
+    ("nchw", "f16", "f32", 1, 17, 30, 240, 5),
+    ("nchw", "bf16", "bf16", 1, 7, 40, 264, 40),
+])
+def test_prepacked_weights_give_identical_results(layout, dt, odt, n, h, w, cin, cout):
+    """Packing once and calling the pre-packed entry point gives the bit-identical output
+    of the per-call-pack entry point (same kernels, same packed operands)."""
+    x, wt, b, _ = wl.random_deconv_case(91 + cin, n=n, h=h, w=w, cin=cin, cout=cout, act="relu", layout=layout,
+                                        dtype=dt)
+    xd, wd, bd = x.to(DEV), wt.to(DEV), b.to(DEV)
+    packed = c2d.deconv_pack(wd)
+    y1 = c2d.conv_transpose4x4s2(xd, wd, bd, act="relu", layout=layout, out_dtype=TD[odt])
+    y2 = c2d.conv_transpose4x4s2_prepacked(xd, packed, bd, act="relu", layout=layout, out_dtype=TD[odt])
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
