@@ -63,6 +63,9 @@ def parse():
                         "rocprofv3 --pmc outputs (FETCH_SIZE, WRITE_SIZE), then exit")
     p.add_argument("--no-fuse-pool", action="store_true",
                    help="run a conv and the max pool after it as two calls")
+    p.add_argument("--oihw", action="store_true",
+                   help="give channel-first layers their weights in OIHW order (converted per call) instead of "
+                        "converting them to OHWI once during set-up")
     p.add_argument("--fuse-shortcut", action="store_true",
                    help="run each average pool + 1x1 shortcut conv as one conv2d_avgpool2x2_conv1x1 call (measured "
                         "slower than the two calls on MI355X: the per-call weight expansion and the 4x deeper GEMM)")
@@ -83,7 +86,7 @@ def parse():
 class Net:
     """The backbone's layers with preallocated device buffers and prebuilt C-ABI arguments."""
 
-    def __init__(self, work, dev, fuse_pool=True, fuse_shortcut=False):
+    def __init__(self, work, dev, fuse_pool=True, fuse_shortcut=False, weights_ohwi=True):
         import torch
 
         import conv2d_bias_activation_amd as c2d
@@ -122,6 +125,17 @@ class Net:
                 res = self.t[spec.res] if spec.res else None
                 act = {"none": 0, "relu": 1, "silu": 2, "prelu": 3}[spec.act]
                 act |= c2d.RES_BEFORE_ACT if spec.res_before_act else 0
+                nxt = work.layers[i + 1] if i + 1 < len(work.layers) else None
+                pooled = (fuse_pool and res is None and nxt is not None and getattr(nxt, "kind", "") == "max"
+                          and nxt.src == spec.out and readers.get(spec.out) == 1)
+                if weights_ohwi and nchw and dt != c2d.DTYPE_F32 and c % 8 == 0 and not pooled:
+                    # weight residency: converted to channel-last once here, so a call copies
+                    # only its input
+                    trial = c2d.plan(n, h, w, c, spec.cout, spec.k, spec.k, spec.stride, spec.pad,
+                                     act | c2d.WEIGHTS_OHWI, lay, dt)
+                    if trial.startswith("x_to_nhwc"):
+                        wdev = c2d.weights_to_ohwi(wdev)
+                        act |= c2d.WEIGHTS_OHWI
                 keep = (wdev, bdev, adev)
                 args = [ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(wdev.data_ptr()),
                         ctypes.c_void_p(bdev.data_ptr()),
@@ -134,9 +148,7 @@ class Net:
                                 (res.numel() if res is not None else 0)) + 4 * spec.cout * (2 if adev is not None else 1)
                 plan = c2d.plan(n, h, w, c, spec.cout, spec.k, spec.k, spec.stride, spec.pad, act,
                                 lay, dt)
-                nxt = work.layers[i + 1] if i + 1 < len(work.layers) else None
-                if (fuse_pool and res is None and nxt is not None and getattr(nxt, "kind", "") == "max"
-                        and nxt.src == spec.out and readers.get(spec.out) == 1):
+                if pooled:
                     # conv + max pool in one call: only the pooled map is written
                     ph, pw = (oh - 1) // 2 + 1, (ow - 1) // 2 + 1
                     out = torch.empty((n, spec.cout, ph, pw) if nchw else (n, ph, pw, spec.cout),
@@ -569,7 +581,8 @@ def main():
         tuned = tune_workload(work, fuse_shortcut=args.fuse_shortcut)
         if args.tune_out:
             c2d.tune_save(args.tune_out)
-    net = Net(work, dev, fuse_pool=not args.no_fuse_pool, fuse_shortcut=args.fuse_shortcut)
+    net = Net(work, dev, fuse_pool=not args.no_fuse_pool, fuse_shortcut=args.fuse_shortcut,
+              weights_ohwi=not args.oihw)
     if args.launch_plan:
         h = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
         chosen = [L for L in net.layers if L["plan"].replace(" tuned", "") == args.launch_plan.replace(" tuned", "")]

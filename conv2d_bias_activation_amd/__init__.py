@@ -19,7 +19,7 @@ __all__ = ["conv2d_fused", "conv2d_fused_maxpool3x3s2", "maxpool3x3s2", "avgpool
            "stack_plan", "stack_run", "StackGraph", "conv_transpose4x4s2", "plan_deconv",
            "upsample_nearest2x", "concat_channels", "upsample2x_concat", "deconv_op", "upsample_op",
            "concat_op", "tune", "tune_save", "tune_load", "tune_clear", "avgpool2x2_conv1x1",
-           "pool_conv_op", "deconv_pack", "conv_transpose4x4s2_prepacked",
+           "pool_conv_op", "deconv_pack", "conv_transpose4x4s2_prepacked", "weights_to_ohwi", "WEIGHTS_OHWI",
            "last_error", "library_path", "Conv2dError", "ACT_NONE", "ACT_RELU", "ACT_SILU",
            "ACT_PRELU", "RES_BEFORE_ACT", "LAYOUT_NHWC", "LAYOUT_NCHW", "DTYPE_F32",
            "DTYPE_BF16", "DTYPE_F16"]
@@ -29,6 +29,7 @@ LAYOUT_NHWC, LAYOUT_NCHW = 0, 1
 DTYPE_F32, DTYPE_BF16, DTYPE_F16 = 0, 1, 2
 ACT_NONE, ACT_RELU, ACT_SILU, ACT_PRELU = 0, 1, 2, 3
 RES_BEFORE_ACT = 0x100
+WEIGHTS_OHWI = 0x200
 OK, EINVAL, EUNSUPPORTED, EHIP = 0, -1, -2, -3
 
 _ACTS = {"none": ACT_NONE, "relu": ACT_RELU, "silu": ACT_SILU, "prelu": ACT_PRELU}
@@ -82,6 +83,7 @@ SIGNATURES = {
     "conv_transpose4x4s2_packed_bytes": (_i, [_i, _i, _i, ctypes.POINTER(ctypes.c_size_t)]),
     "conv_transpose4x4s2_pack": (_i, [_vp, _vp, _i, _i, _i, _vp]),
     "conv_transpose4x4s2_prepacked": (_i, [_vp, _vp, _fp, _fp, _vp] + [_i] * 9 + [_vp]),
+    "conv2d_weights_to_ohwi": (_i, [_vp, _vp] + [_i] * 5 + [_vp]),
     "conv2d_last_error": (_cp, []),
     "conv2d_abi_version": (_i, []),
 }
@@ -144,10 +146,13 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _dims(x, w, layout):
+def _dims(x, w, layout, weights_ohwi=False):
     if x.dim() != 4 or w.dim() != 4:
         raise ValueError("x and w must be 4-D")
-    if layout == "nhwc":
+    if weights_ohwi:
+        N, Cin, H, W = x.shape
+        Cout, kh, kw, wc = w.shape
+    elif layout == "nhwc":
         N, H, W, Cin = x.shape
         Cout, kh, kw, wc = w.shape
     else:
@@ -169,12 +174,12 @@ def _require(t, name, dtype, device):
         raise ValueError(f"{name} must be contiguous")
 
 
-def _conv_args(x, w, bias, alpha, stride, pad, layout):
+def _conv_args(x, w, bias, alpha, stride, pad, layout, weights_ohwi=False):
     lay = _LAYOUTS[layout]
     dt = _DTYPES.get(x.dtype)
     if dt is None:
         raise ValueError(f"unsupported dtype {x.dtype}")
-    dims = _dims(x, w, layout)
+    dims = _dims(x, w, layout, weights_ohwi)
     N, H, W, Cin, Cout, kh, kw = dims
     OH, OW = out_dim(H, kh, stride, pad), out_dim(W, kw, stride, pad)
     if OH < 1 or OW < 1:
@@ -200,15 +205,17 @@ def _out(out, shape, x):
 
 
 def conv2d_fused(x, w, bias=None, alpha=None, residual=None, *, stride=1, pad=0, act="none",
-                 res_before_act=False, layout="nhwc", out=None, stream=None):
+                 res_before_act=False, layout="nhwc", weights_ohwi=False, out=None, stream=None):
     """y = epilogue(conv(x, w)) on the GPU; see include/conv2d_fused.h.
 
     x, w, residual, out: CUDA tensors of one storage dtype (float32, bfloat16 or
     float16), contiguous, in ``layout`` ("nhwc" with OHWI weights or "nchw" with
-    OIHW weights). bias, alpha: float32 [Cout] or None. Returns y.
+    OIHW weights; with ``weights_ohwi`` a channel-first layer takes OHWI weights, see
+    weights_to_ohwi). bias, alpha: float32 [Cout] or None. Returns y.
     """
     lib = _load()
-    lay, dt, (N, H, W, Cin, Cout, kh, kw), (OH, OW) = _conv_args(x, w, bias, alpha, stride, pad, layout)
+    lay, dt, (N, H, W, Cin, Cout, kh, kw), (OH, OW) = _conv_args(x, w, bias, alpha, stride, pad, layout,
+                                                                  weights_ohwi)
     yshape = (N, OH, OW, Cout) if layout == "nhwc" else (N, Cout, OH, OW)
     _require(residual, "residual", x.dtype, x.device)
     if residual is not None and tuple(residual.shape) != yshape:
@@ -216,7 +223,8 @@ def conv2d_fused(x, w, bias=None, alpha=None, residual=None, *, stride=1, pad=0,
     out = _out(out, yshape, x)
     rc = lib.conv2d_fused(_ptr(x), _ptr(w), _ptr(bias), _ptr(alpha), _ptr(residual), _ptr(out),
                           N, H, W, Cin, Cout, kh, kw, stride, pad,
-                          _act_code(act, res_before_act), lay, dt, _stream_handle(stream))
+                          _act_code(act, res_before_act) | (WEIGHTS_OHWI if weights_ohwi else 0), lay, dt,
+                          _stream_handle(stream))
     _check(rc)
     return out
 
@@ -303,13 +311,13 @@ def _tensor_ptr(t):
 
 
 def conv_op(x, w, y, bias=None, alpha=None, residual=None, *, stride=1, pad=0, act="none",
-            res_before_act=False, layout="nhwc", pool=False):
+            res_before_act=False, layout="nhwc", pool=False, weights_ohwi=False):
     """An Op for conv2d_fused (or, with pool=True, conv2d_fused_maxpool3x3s2) on these
     tensors. The tensors must stay alive while the stack (or its graph) is in use."""
-    N, H, W, Cin, Cout, kh, kw = _dims(x, w, layout)
+    N, H, W, Cin, Cout, kh, kw = _dims(x, w, layout, weights_ohwi)
     return Op(OP_CONV_MAXPOOL if pool else OP_CONV, _tensor_ptr(x), _tensor_ptr(w), _tensor_ptr(bias),
               _tensor_ptr(alpha), _tensor_ptr(residual), _tensor_ptr(y), N, H, W, Cin, Cout, kh, kw, stride, pad,
-              _act_code(act, res_before_act))
+              _act_code(act, res_before_act) | (WEIGHTS_OHWI if weights_ohwi else 0))
 
 
 def _nhwc_dims(x, layout):
@@ -608,3 +616,17 @@ def conv_transpose4x4s2_prepacked(x, packed, bias=None, alpha=None, *, act="none
                                            _act_code(act, False), lay, dt, odt, _stream_handle(stream))
     _check(rc)
     return out
+
+
+def weights_to_ohwi(w, stream=None):
+    """OIHW conv weights [Cout, Cin, kh, kw] (bf16/f16) -> a new OHWI tensor [Cout, kh, kw, Cin],
+    for channel-first convs called with weights_ohwi=True (convert once, reuse)."""
+    lib = _load()
+    dt = _dtype_code(w.dtype)
+    if w.dim() != 4:
+        raise ValueError("w must be 4-D")
+    _require(w, "w", w.dtype, w.device)
+    Cout, Cin, kh, kw = (int(v) for v in w.shape)
+    w2 = torch.empty((Cout, kh, kw, Cin), dtype=w.dtype, device=w.device)
+    _check(lib.conv2d_weights_to_ohwi(_ptr(w), _ptr(w2), Cout, Cin, kh, kw, dt, _stream_handle(stream)))
+    return w2

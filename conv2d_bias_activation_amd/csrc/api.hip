@@ -93,8 +93,10 @@ int check_conv(const void *x, const void *w, const float *alpha, const void *res
         return set_error(CONV2D_EINVAL, "unknown layout %d", layout);
     if (!dtype_bytes(dtype)) return set_error(CONV2D_EINVAL, "unknown dtype %d", dtype);
     int code = act & 0xff;
-    if (code > CONV2D_ACT_PRELU || (act & ~(0xff | CONV2D_RES_BEFORE_ACT)))
+    if (code > CONV2D_ACT_PRELU || (act & ~(0xff | CONV2D_RES_BEFORE_ACT | CONV2D_WEIGHTS_OHWI)))
         return set_error(CONV2D_EINVAL, "unknown activation flags 0x%x", act);
+    if ((act & CONV2D_WEIGHTS_OHWI) && layout != CONV2D_LAYOUT_NCHW)
+        return set_error(CONV2D_EINVAL, "CONV2D_WEIGHTS_OHWI is for channel-first layers");
     if (code == CONV2D_ACT_PRELU && !alpha) return set_error(CONV2D_EINVAL, "PRELU needs alpha");
     int OH = out_dim(H, kh, stride, pad), OW = out_dim(W, kw, stride, pad);
     if (OH < 1 || OW < 1)
@@ -129,6 +131,7 @@ int check_conv(const void *x, const void *w, const float *alpha, const void *res
     a->K = (int)we / Cout;
     a->act = code;
     a->res_before_act = (act & CONV2D_RES_BEFORE_ACT) ? 1 : 0;
+    a->w_ohwi = (act & CONV2D_WEIGHTS_OHWI) ? 1 : 0;
     a->vec_out = aligned16(y) && (!residual || aligned16(residual));
     return CONV2D_OK;
 }
@@ -141,6 +144,7 @@ struct Plan {
     NhwcPlan nh;
     HaloPlan halo;
     bool tuned;  // chosen by a conv2d_tune measurement rather than the built-in heuristics
+    bool w_ohwi; // channel-first layer with channel-last weights: only the input is copied
 };
 
 // Library scratch, one buffer per device, allocated on the first call that needs it
@@ -451,7 +455,18 @@ void apply_tuned(const ConvArgs &a, int layout, int dtype, Plan *p) {
 Plan make_plan(const ConvArgs &a, int layout, int dtype) {
     Plan p = make_plan_default(a, layout, dtype);
     apply_tuned(a, layout, dtype, &p);
+    p.w_ohwi = a.w_ohwi != 0;
     return p;
+}
+
+// Channel-first layers with channel-last weights run only on the channel-last kernel
+// (after the input's layout copy): 16-bit, Cin % 8 == 0, the copy within the scratch.
+int check_w_ohwi(const ConvArgs &a, const Plan &p) {
+    if (a.w_ohwi && p.family != FAM_NCHW_VIA_NHWC)
+        return set_error(CONV2D_EUNSUPPORTED,
+                         "CONV2D_WEIGHTS_OHWI needs a 16-bit layer with Cin %% 8 == 0 whose channel-last input copy "
+                         "fits the library scratch");
+    return CONV2D_OK;
 }
 
 int describe(const Plan &p, int layout, int dtype, char *buf, int cap) {
@@ -466,7 +481,8 @@ int describe(const Plan &p, int layout, int dtype, char *buf, int cap) {
                  p.halo.waves);
     } else if (p.family == FAM_NHWC || p.family == FAM_NCHW_VIA_NHWC) {
         snprintf(tmp, sizeof tmp, "%sigemm_nhwc_pipe%s %s %s splitk=%d",
-                 p.family == FAM_NCHW_VIA_NHWC ? "to_nhwc+" : "", p.nh.tap_inner ? "_tapinner" : "",
+                 p.family == FAM_NCHW_VIA_NHWC ? (p.w_ohwi ? "x_to_nhwc+" : "to_nhwc+") : "",
+                 p.nh.tap_inner ? "_tapinner" : "",
                  dtype_name(dtype), nhwc_tile_name(p.nh.tile), p.nh.splits);
     } else {
         snprintf(tmp, sizeof tmp, "igemm_%s%s %s %s", p.ig.nchw ? "nchw" : "nhwc",
@@ -530,11 +546,13 @@ int launch_conv(const ConvArgs &a, const Plan &p, int layout, int dtype, hipStre
         const int eb = dtype_bytes(dtype);
         char *xs = reinterpret_cast<char *>(scratch);
         char *ws = xs + round256((size_t)a.N * a.H * a.W * a.Cin * eb);
-        e = launch_to_channel_last(a.x, xs, a.N, a.Cin, a.H * a.W, a.w, ws, a.Cout, a.kh * a.kw, dtype, st);
+        // weights given channel-last (converted once by the caller) need no copy
+        e = a.w_ohwi ? launch_nchw_to_nhwc(a.x, xs, a.N, a.Cin, a.H * a.W, dtype, st)
+                     : launch_to_channel_last(a.x, xs, a.N, a.Cin, a.H * a.W, a.w, ws, a.Cout, a.kh * a.kw, dtype, st);
         if (e == hipSuccess) {
             ConvArgs b = a;
             b.x = xs;
-            b.w = ws;
+            b.w = a.w_ohwi ? a.w : ws;
             e = launch_igemm_nhwc(b, dtype, p.nh, nullptr, st);
         }
     } else {
@@ -558,6 +576,8 @@ int check_conv_pool(const void *x, const void *w, const float *alpha, const void
                     ConvArgs *a, PoolFusion *f) {
     if (act & CONV2D_RES_BEFORE_ACT)
         return set_error(CONV2D_EINVAL, "conv2d_fused_maxpool3x3s2 takes no residual");
+    if (act & CONV2D_WEIGHTS_OHWI)
+        return set_error(CONV2D_EINVAL, "conv2d_fused_maxpool3x3s2 takes the weights in the layout's own order");
     int rc = check_conv(x, w, alpha, nullptr, y, N, H, W, Cin, Cout, kh, kw, stride, pad, act, layout, dtype, a,
                         true);
     if (rc) return rc;
@@ -740,7 +760,7 @@ int check_op(const conv2d_op &op, int layout, int dtype, OpPlan *o) {
         o->a.bias = op.bias;
         if ((op.act & 0xff) != CONV2D_ACT_PRELU) o->a.alpha = nullptr;
         o->plan = make_plan(o->a, layout, dtype);
-        return CONV2D_OK;
+        return check_w_ohwi(o->a, o->plan);
     }
     case CONV2D_OP_CONV_MAXPOOL: {
         if (op.residual) return set_error(CONV2D_EINVAL, "conv2d_fused_maxpool3x3s2 takes no residual");
@@ -789,6 +809,8 @@ int check_op(const conv2d_op &op, int layout, int dtype, OpPlan *o) {
         // the 2x2 stride-2 conv with weights w/4 on every tap (built in the scratch)
         if (op.residual || (op.act & CONV2D_RES_BEFORE_ACT))
             return set_error(CONV2D_EINVAL, "avgpool2x2_conv1x1 takes no residual");
+        if (op.act & CONV2D_WEIGHTS_OHWI)
+            return set_error(CONV2D_EINVAL, "avgpool2x2_conv1x1 takes [Cout][Cin] weights");
         if (!op.w) return set_error(CONV2D_EINVAL, "avgpool2x2_conv1x1: w must not be null");
         int rc = check_conv(op.x, op.w, op.alpha, nullptr, op.y, op.N, op.H, op.W, op.Cin, op.Cout, 2, 2, 2, 0,
                             op.act, layout, dtype, &o->a);
@@ -1152,7 +1174,7 @@ int tune_run(int N, int H, int W, int Cin, int Cout, int kh, int kw, int stride,
 
 extern "C" {
 
-int conv2d_abi_version(void) { return 6; }
+int conv2d_abi_version(void) { return 7; }
 
 const char *conv2d_last_error(void) { return g_err.c_str(); }
 
@@ -1166,6 +1188,7 @@ int conv2d_check_args(const void *x, const void *w, const float *bias, const flo
     ConvArgs a{};
     int rc = check_conv(x, w, alpha, residual, y, N, H, W, Cin, Cout, kh, kw, stride, pad, act,
                         layout, dtype, &a);
+    if (!rc && a.w_ohwi) rc = check_w_ohwi(a, make_plan(a, layout, dtype));
     return rc ? rc : set_ok();
 }
 
@@ -1180,8 +1203,11 @@ int conv2d_plan(int N, int H, int W, int Cin, int Cout, int kh, int kw, int stri
     int rc = check_conv(px, pw, pa, nullptr, py, N, H, W, Cin, Cout, kh, kw, stride, pad, act,
                         layout, dtype, &a);
     if (rc) return rc;
+    const Plan pl = make_plan(a, layout, dtype);
+    rc = check_w_ohwi(a, pl);
+    if (rc) return rc;
     set_ok();
-    return describe(make_plan(a, layout, dtype), layout, dtype, buf, cap);
+    return describe(pl, layout, dtype, buf, cap);
 }
 
 int conv2d_fused(const void *x, const void *w, const float *bias, const float *alpha,
@@ -1386,6 +1412,20 @@ int conv2d_avgpool2x2_conv1x1(const void *x, const void *w, const float *bias, c
                               int H, int W, int Cin, int Cout, int act, int layout, int dtype, void *stream) {
     const conv2d_op op{CONV2D_OP_AVGPOOL_CONV1X1, x, w, bias, alpha, nullptr, y, N, H, W, Cin, Cout, 1, 1, 1, 0, act};
     return run_one(op, layout, dtype, stream);
+}
+
+int conv2d_weights_to_ohwi(const void *w, void *w2, int Cout, int Cin, int kh, int kw, int dtype, void *stream) {
+    if (!w || !w2) return set_error(CONV2D_EINVAL, "conv2d_weights_to_ohwi: w and w2 must not be null");
+    if (Cout <= 0 || Cin <= 0 || kh <= 0 || kw <= 0)
+        return set_error(CONV2D_EINVAL, "conv2d_weights_to_ohwi: sizes must be positive");
+    if (dtype != CONV2D_DTYPE_BF16 && dtype != CONV2D_DTYPE_F16)
+        return set_error(CONV2D_EUNSUPPORTED, "conv2d_weights_to_ohwi: for the 16-bit types");
+    const long long e = (long long)Cout * Cin * kh * kw;
+    if (e > kMaxElems) return set_error(CONV2D_EUNSUPPORTED, "conv2d_weights_to_ohwi: too large");
+    if (overlap(w2, e * 2, w, e * 2)) return set_error(CONV2D_EINVAL, "conv2d_weights_to_ohwi: w2 overlaps w");
+    hipError_t er = launch_oihw_to_ohwi(w, w2, Cout, Cin, kh * kw, dtype, static_cast<hipStream_t>(stream));
+    if (er != hipSuccess) return hip_fail(er, "conv2d_weights_to_ohwi launch");
+    return set_ok();
 }
 
 int conv2d_stack_check(const conv2d_op *ops, int n, int layout, int dtype, int *bad_index) {

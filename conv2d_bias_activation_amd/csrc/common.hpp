@@ -39,6 +39,7 @@ struct ConvArgs {
     int K;    // Cin*kh*kw (GEMM depth)
     int act;  // CONV2D_ACT_* (low byte only)
     int res_before_act;
+    int w_ohwi;  // channel-first layer whose weights are given channel-last (OHWI)
     int vec_out;  // y and residual are 16-byte aligned
 };
 

@@ -134,6 +134,9 @@ hipError_t launch_deconv_mfma(const DeconvArgs &a, int dtype, bool out_f32, bool
 // y channel-first (nchw_out must be true).
 hipError_t launch_deconv_mfma_all(const DeconvArgs &a, int dtype, bool out_f32, bool nchw_out, hipStream_t st);
 
+// OIHW -> OHWI weights alone (16-bit types).
+hipError_t launch_oihw_to_ohwi(const void *w, void *w2, int Cout, int Cin, int taps, int dtype, hipStream_t st);
+
 // Channel-first 16-bit map to channel-last (N planes of C x HW; 16-byte accesses when C
 // and HW are multiples of 8 and both pointers are 16-byte aligned).
 hipError_t launch_nchw_to_nhwc(const void *x, void *y, int N, int C, int HW, int dtype, hipStream_t st);

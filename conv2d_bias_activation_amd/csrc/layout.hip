@@ -156,6 +156,20 @@ hipError_t launch_nchw_to_nhwc(const void *x, void *y, int N, int C, int HW, int
     }
 }
 
+hipError_t launch_oihw_to_ohwi(const void *w, void *w2, int Cout, int Cin, int taps, int dtype, hipStream_t st) {
+    const dim3 grid((unsigned)(((long long)Cout * Cin + 255) / 256));
+    switch (dtype) {
+    case CONV2D_DTYPE_BF16:
+        return launch_kernel(oihw_to_ohwi_kernel<bf16>, grid, dim3(256), 0, st, static_cast<const bf16 *>(w),
+                             static_cast<bf16 *>(w2), Cout, Cin, taps);
+    case CONV2D_DTYPE_F16:
+        return launch_kernel(oihw_to_ohwi_kernel<f16>, grid, dim3(256), 0, st, static_cast<const f16 *>(w),
+                             static_cast<f16 *>(w2), Cout, Cin, taps);
+    default:
+        return hipErrorInvalidValue;
+    }
+}
+
 hipError_t launch_to_channel_last(const void *x, void *x_nhwc, int N, int C, int HW, const void *w,
                                   void *w_ohwi, int Cout, int taps, int dtype, hipStream_t st) {
     switch (dtype) {

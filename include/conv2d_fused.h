@@ -74,6 +74,14 @@ extern "C" {
 #define CONV2D_ACT_PRELU 3
 #define CONV2D_RES_BEFORE_ACT 0x100
 
+/* OR-ed into `act` of a channel-first (CONV2D_LAYOUT_NCHW) conv: the weights are given
+ * in OHWI order [Cout][kh][kw][Cin] instead of OIHW, e.g. converted once at model load by
+ * conv2d_weights_to_ohwi (weight residency: such a layer then copies only its input to
+ * channel-last form per call). Only for 16-bit layers with Cin % 8 == 0 whose input copy
+ * fits the library scratch (CONV2D_EUNSUPPORTED otherwise); not accepted by
+ * conv2d_fused_maxpool3x3s2 or conv2d_avgpool2x2_conv1x1 (CONV2D_EINVAL). */
+#define CONV2D_WEIGHTS_OHWI 0x200
+
 /* Status codes. */
 #define CONV2D_OK 0
 #define CONV2D_EINVAL (-1)      /* bad argument: null required pointer, size <= 0, stride
@@ -269,6 +277,11 @@ int upsample2x_concat(const void *a, const void *b, void *y, int N, int H, int W
 int conv2d_avgpool2x2_conv1x1(const void *x, const void *w, const float *bias, const float *alpha, void *y, int N,
                               int H, int W, int Cin, int Cout, int act, int layout, int dtype, void *stream);
 
+/* w [Cout][Cin][kh][kw] (OIHW) -> w2 [Cout][kh][kw][Cin] (OHWI), 16-bit types, for
+ * channel-first convs called with CONV2D_WEIGHTS_OHWI. w2 is a caller-owned device
+ * buffer of the same size that may not overlap w; enqueued on `stream`. */
+int conv2d_weights_to_ohwi(const void *w, void *w2, int Cout, int Cin, int kh, int kw, int dtype, void *stream);
+
 /* floor((in + 2*pad - k)/stride) + 1, or -1 if in, k, stride <= 0, pad < 0 or the
  * kernel does not fit the padded input (inferencelayer `conv()`). Host only. */
 int conv2d_out_dim(int in, int k, int stride, int pad);
@@ -414,7 +427,8 @@ int conv2d_tune_clear(void);
  * valid until the thread's next call into the library. */
 const char *conv2d_last_error(void);
 
-/* ABI version of this header: 6 (5 plus the transposed conv's weight packing calls; 5
+/* ABI version of this header: 7 (6 plus CONV2D_WEIGHTS_OHWI and conv2d_weights_to_ohwi; 6
+ * added the transposed conv's weight packing calls; 5
  * added conv2d_avgpool2x2_conv1x1; 4 added the tuning calls; 3 added the transposed conv,
  * upsample and concat calls and their stack ops; 2 the stack calls and the fused conv +
  * max pool). */

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     for name in names:
         assert hasattr(lib, name), name
     assert names == set(c2d.SIGNATURES)
-    assert c2d._load().conv2d_abi_version() == 6
+    assert c2d._load().conv2d_abi_version() == 7
 
 
 def test_out_dim():
@@ -302,3 +302,22 @@ def test_deconv_pack_sizes_and_checks():
                                              c2d.DTYPE_F32, None) == c2d.EUNSUPPORTED             # fp32
     assert lib.conv_transpose4x4s2_prepacked(x, P((9 << 32) + 8), None, None, y, 1, 8, 8, 16, 8, 0, 0,
                                              c2d.DTYPE_BF16, c2d.DTYPE_BF16, None) == c2d.EINVAL  # wp alignment
+
+
+def test_weights_ohwi_flag_checks():
+    """Host only: channel-first convs may take OHWI weights (16-bit, Cin % 8 == 0); elsewhere
+    the flag is rejected before anything is launched."""
+    f16, f32 = c2d.DTYPE_F16, c2d.DTYPE_F32
+    nchw, nhwc = c2d.LAYOUT_NCHW, c2d.LAYOUT_NHWC
+    act = c2d.ACT_PRELU | c2d.WEIGHTS_OHWI
+    assert c2d.plan(1, 68, 120, 240, 240, 3, 3, 1, 1, act, nchw, f16).startswith("x_to_nhwc+igemm_nhwc_pipe")
+    assert _check(layout=nchw, dtype=f16, Cin=16, act=c2d.ACT_RELU | c2d.WEIGHTS_OHWI) == c2d.OK
+    assert _check(layout=nhwc, act=c2d.ACT_RELU | c2d.WEIGHTS_OHWI) == c2d.EINVAL            # channel-last layer
+    assert _check(layout=nchw, dtype=f32, act=c2d.ACT_RELU | c2d.WEIGHTS_OHWI) == c2d.EUNSUPPORTED
+    assert _check(layout=nchw, dtype=f16, Cin=12, act=c2d.ACT_RELU | c2d.WEIGHTS_OHWI) == c2d.EUNSUPPORTED
+    with pytest.raises(c2d.Conv2dError):
+        c2d.plan_maxpool(1, 64, 64, 16, 16, 3, 3, 1, 1, c2d.ACT_RELU | c2d.WEIGHTS_OHWI, nchw, f16)
+    lib = c2d._load()
+    P = ctypes.c_void_p
+    assert lib.conv2d_weights_to_ohwi(P(1 << 32), P((1 << 32) + 64), 8, 8, 3, 3, f16, None) == c2d.EINVAL
+    assert lib.conv2d_weights_to_ohwi(P(1 << 32), P(9 << 32), 8, 8, 3, 3, f32, None) == c2d.EUNSUPPORTED

@@ -375,3 +375,24 @@ def test_invalid_arguments_raise_without_writing():
     assert e.value.code == c2d.EINVAL
     torch.cuda.synchronize()
     assert torch.all(y == 3.0) and torch.all(y3 == 3.0)
+
+
+@pytest.mark.parametrize("n,h,w,cin,cout,k,stride,act,dt", [
+    (1, 17, 30, 240, 240, 3, 1, "prelu", "f16"),
+    (2, 9, 7, 64, 40, 3, 2, "relu", "bf16"),
+    (3, 12, 12, 72, 200, 1, 1, "silu", "f16"),
+])
+def test_channel_first_with_ohwi_weights(n, h, w, cin, cout, k, stride, act, dt):
+    """Weights converted once to OHWI (weights_to_ohwi) and passed with weights_ohwi give the
+    bit-identical output of the OIHW call, which is checked against the oracle."""
+    x, spec, r = wl.random_conv_case(101 + cin, n=n, h=h, w=w, cin=cin, cout=cout, k=k, stride=stride, pad=k // 2,
+                                     act=act, layout="nchw", dtype=dt, residual=True)
+    xd, wd, bd, rd = x.to(DEV), spec.w.to(DEV), spec.bias.to(DEV), r.to(DEV)
+    ad = spec.alpha.to(DEV) if spec.alpha is not None else None
+    y1 = c2d.conv2d_fused(xd, wd, bd, ad, rd, stride=stride, pad=k // 2, act=act, layout="nchw")
+    w2 = c2d.weights_to_ohwi(wd)
+    y2 = c2d.conv2d_fused(xd, w2, bd, ad, rd, stride=stride, pad=k // 2, act=act, layout="nchw", weights_ohwi=True)
+    torch.cuda.synchronize()
+    assert torch.equal(w2.cpu(), spec.w.permute(0, 2, 3, 1).contiguous())
+    assert torch.equal(y1, y2)
+    gate(to64(y2), _oracle_conv(x, spec, r, "nchw"), dt, what="ohwi weights")
