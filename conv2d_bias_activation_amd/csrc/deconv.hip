@@ -43,6 +43,10 @@ constexpr int DC_PAD = (256 * DC_VQ - DC_VECS) * 8 > 256 * DC_EQ - DC_ELEMS ? (2
                                                                              : 256 * DC_EQ - DC_ELEMS;
 constexpr int DC_BUFA = DC_BUF + DC_PAD;  // allocated elements per buffer
 constexpr int DC_OLD = 2 * DC_TW + 2;               // output tile row in LDS: 64 columns + 2 pad
+// output tile in LDS: per channel 2*DC_MR rows of DC_OLD floats plus one word, so the
+// channel stride (265 words) is odd and the 32 lanes that hold 32 channels of one pixel
+// write and read 32 different banks
+constexpr int DC_OCS = 2 * DC_MR * DC_OLD + 1;
 
 template <typename TO> __device__ __forceinline__ TO out_cast(float v) { return from_f32<TO>(v); }
 
@@ -98,7 +102,7 @@ template <typename T, typename TO, bool NCHW>
 __global__ __launch_bounds__(256) void deconv_mfma_kernel(DeconvArgs a) {
     typedef typename Mfma32<T>::vec vec;
     __shared__ __attribute__((aligned(16))) T sx[2][DC_BUFA];
-    __shared__ float so[32][2 * DC_MR][DC_OLD];
+    __shared__ float so[32 * DC_OCS];
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int py = wv >> 1, px = wv & 1;
@@ -233,7 +237,7 @@ __global__ __launch_bounds__(256) void deconv_mfma_kernel(DeconvArgs a) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int p = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-                so[col][2 * m + py][2 * p + px] = activate_c<ACT>(acc[m][i] + bv, av);
+                so[col * DC_OCS + (2 * m + py) * DC_OLD + 2 * p + px] = activate_c<ACT>(acc[m][i] + bv, av);
             }
     };
     switch (a.act) {
@@ -253,7 +257,7 @@ __global__ __launch_bounds__(256) void deconv_mfma_kernel(DeconvArgs a) {
             const int e = tid + 256 * it;
             const int oc = e & 63, lr = (e >> 6) & (2 * DC_MR - 1), cl = e / (128 * DC_MR);
             if (co0 + cl < Cout && oc0 + oc < OW && or0 + lr < OH)
-                y[(((size_t)n * Cout + co0 + cl) * OH + or0 + lr) * OW + oc0 + oc] = out_cast<TO>(so[cl][lr][oc]);
+                y[(((size_t)n * Cout + co0 + cl) * OH + or0 + lr) * OW + oc0 + oc] = out_cast<TO>(so[cl * DC_OCS + lr * DC_OLD + oc]);
         }
     } else {
 #pragma unroll 4
@@ -261,7 +265,7 @@ __global__ __launch_bounds__(256) void deconv_mfma_kernel(DeconvArgs a) {
             const int e = tid + 256 * it;
             const int cl = e & 31, oc = (e >> 5) & 63, lr = e >> 11;
             if (co0 + cl < Cout && oc0 + oc < OW && or0 + lr < OH)
-                y[(((size_t)n * OH + or0 + lr) * OW + oc0 + oc) * Cout + co0 + cl] = out_cast<TO>(so[cl][lr][oc]);
+                y[(((size_t)n * OH + or0 + lr) * OW + oc0 + oc) * Cout + co0 + cl] = out_cast<TO>(so[cl * DC_OCS + lr * DC_OLD + oc]);
         }
     }
 }
@@ -281,7 +285,7 @@ __global__ __launch_bounds__(256) void deconv_mfma_all_kernel(DeconvArgs a) {
     typedef typename Mfma32<T>::vec vec;
     // the staged strip; its tail also receives the stores of lanes past the last vector
     __shared__ __attribute__((aligned(16))) T sx[DC_ROWS * DC_SPX * DA_PSMAX + 256 * 8];
-    __shared__ float so[32][2 * DC_MR][DC_OLD];
+    __shared__ float so[32 * DC_OCS];
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int py = wv >> 1, px = wv & 1;
@@ -369,7 +373,7 @@ __global__ __launch_bounds__(256) void deconv_mfma_all_kernel(DeconvArgs a) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int p = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-                so[col][2 * m + py][2 * p + px] = activate_c<ACT>(acc[m][i] + bv, av);
+                so[col * DC_OCS + (2 * m + py) * DC_OLD + 2 * p + px] = activate_c<ACT>(acc[m][i] + bv, av);
             }
     };
     switch (a.act) {
@@ -388,7 +392,7 @@ __global__ __launch_bounds__(256) void deconv_mfma_all_kernel(DeconvArgs a) {
             const int e = tid + 256 * it;
             const int oc = e & 63, lr = (e >> 6) & (2 * DC_MR - 1), cl = e / (128 * DC_MR);
             if (co0 + cl < Cout && oc0 + oc < OW && or0 + lr < OH)
-                y[(((size_t)n * Cout + co0 + cl) * OH + or0 + lr) * OW + oc0 + oc] = out_cast<TO>(so[cl][lr][oc]);
+                y[(((size_t)n * Cout + co0 + cl) * OH + or0 + lr) * OW + oc0 + oc] = out_cast<TO>(so[cl * DC_OCS + lr * DC_OLD + oc]);
         }
     } else {
 #pragma unroll 4
@@ -396,7 +400,7 @@ __global__ __launch_bounds__(256) void deconv_mfma_all_kernel(DeconvArgs a) {
             const int e = tid + 256 * it;
             const int cl = e & 31, oc = (e >> 5) & 63, lr = e >> 11;
             if (co0 + cl < Cout && oc0 + oc < OW && or0 + lr < OH)
-                y[(((size_t)n * OH + or0 + lr) * OW + oc0 + oc) * Cout + co0 + cl] = out_cast<TO>(so[cl][lr][oc]);
+                y[(((size_t)n * OH + or0 + lr) * OW + oc0 + oc) * Cout + co0 + cl] = out_cast<TO>(so[cl * DC_OCS + lr * DC_OLD + oc]);
         }
     }
 }
