@@ -321,3 +321,36 @@ def test_weights_ohwi_flag_checks():
     P = ctypes.c_void_p
     assert lib.conv2d_weights_to_ohwi(P(1 << 32), P((1 << 32) + 64), 8, 8, 3, 3, f16, None) == c2d.EINVAL
     assert lib.conv2d_weights_to_ohwi(P(1 << 32), P(9 << 32), 8, 8, 3, 3, f32, None) == c2d.EUNSUPPORTED
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0,
+                    reason="needs a machine without a GPU: the stand-in pointers would be launched on a real device")
+def test_no_device_returns_ehip_not_a_crash():
+    """Without a GPU, every launching entry point validates, then reports CONV2D_EHIP with a
+    message (the library loads and fails cleanly)."""
+    lib = c2d._load()
+    P = ctypes.c_void_p
+    G = 1 << 32
+    bf16 = c2d.DTYPE_BF16
+    calls = {
+        "conv2d_fused": lambda: lib.conv2d_fused(P(G), P(9 * G), None, None, None, P(17 * G), 1, 8, 8, 16, 16, 3, 3,
+                                                 1, 1, 1, 0, bf16, None),
+        "maxpool3x3s2": lambda: lib.maxpool3x3s2(P(G), P(17 * G), 1, 8, 8, 16, 0, bf16, None),
+        "avgpool2x2": lambda: lib.avgpool2x2(P(G), P(17 * G), 1, 8, 8, 16, 0, bf16, None),
+        "conv_transpose4x4s2": lambda: lib.conv_transpose4x4s2(P(G), P(9 * G), None, None, P(17 * G), 1, 8, 8, 16, 8,
+                                                               0, 0, bf16, bf16, None),
+        "upsample2x_concat": lambda: lib.upsample2x_concat(P(G), P(9 * G), P(17 * G), 1, 4, 4, 8, 8, 0, bf16, None),
+        "conv2d_avgpool2x2_conv1x1": lambda: lib.conv2d_avgpool2x2_conv1x1(P(G), P(9 * G), None, None, P(17 * G), 1,
+                                                                           8, 8, 16, 16, 0, 0, bf16, None),
+    }
+    for name, call in calls.items():
+        assert call() == c2d.EHIP, name
+        assert "device" in c2d.last_error(), name
+    op = c2d.Op(c2d.OP_CONV, G, 9 * G, None, None, None, 17 * G, 1, 8, 8, 16, 16, 3, 3, 1, 1, 1)
+    arr = (c2d.Op * 1)(op)
+    h = ctypes.c_void_p()
+    assert lib.conv2d_stack_graph_create(arr, 1, 0, bf16, ctypes.byref(h)) == c2d.EHIP and not h.value
+    assert lib.conv2d_stack_run(arr, 1, 0, bf16, None) == c2d.EHIP
+    with pytest.raises(c2d.Conv2dError) as e:
+        c2d.tune(1, 8, 8, 16, 16, 3, 3, 1, 1, "relu", reps=3)
+    assert e.value.code == c2d.EHIP
