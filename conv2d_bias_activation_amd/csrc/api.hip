@@ -233,7 +233,8 @@ int choose_tile(const ConvArgs &a) {
 const char *nhwc_tile_name(int t) {
     static const char *names[NHWC_TILE_COUNT] = {
         "256x128w8", "128x128",  "128x64",   "256x64w8",    "256x32",   "64x64",   "128x128w8",
-        "128x256w8", "64x64d6",  "128x64d5", "128x128w8d4", "64x128d5", "64x64d4", "256x128w8d3"};
+        "128x256w8", "64x64d6",  "128x64d5", "128x128w8d4", "64x128d5", "64x64d4", "256x128w8d3",
+        "64x64k2",   "64x64k2d4", "64x64k2d2"};
     return (t >= 0 && t < NHWC_TILE_COUNT) ? names[t] : "?";
 }
 

@@ -18,6 +18,10 @@
 //  * When Cin is a multiple of 64 the K loop takes the taps innermost, so the patch
 //    rows of consecutive steps are the same pixels shifted by one tap and mostly
 //    hit in the vector L1 cache.
+//  * KG = 2 runs two wave groups per workgroup on alternate K steps (each with its own
+//    half of every LDS stage) and adds the two fp32 accumulators through LDS at the
+//    end: two waves per SIMD for layers with too few output tiles to put one
+//    workgroup on every CU twice (ResNet stages 3-4), without a second pass.
 #include <utility>
 
 #include "igemm_common.hpp"
@@ -42,12 +46,12 @@ __device__ __forceinline__ void barrier_nofence() {
     asm volatile("" ::: "memory");
 }
 
-template <typename T, int BM, int BN, int WGM, int WGN, int NS, bool TAP_INNER, bool SPLIT,
+template <typename T, int BM, int BN, int WGM, int WGN, int NS, int KG, bool TAP_INNER, bool SPLIT,
           bool NCHW_OUT>
-__global__ __launch_bounds__(64 * WGM * WGN, 8 / (WGM * WGN)) void igemm_nhwc_kernel(ConvArgs a, int tiles_n,
-                                                                   int steps_per_split,
-                                                                   float *partials) {
-    constexpr int NW = WGM * WGN;        // waves per workgroup (4 or 8)
+__global__ __launch_bounds__(64 * WGM * WGN * KG, 8 / (WGM * WGN * KG)) void igemm_nhwc_kernel(
+    ConvArgs a, int tiles_n, int steps_per_split, float *partials) {
+    constexpr int NW = WGM * WGN;        // waves per K group (4 or 8)
+    static_assert(KG == 1 || (KG == 2 && NW == 4), "two K groups of four waves");
     constexpr int BK = 64;               // k per step (elements)
     constexpr int ROWB = 128;            // bytes per LDS row (BK 16-bit values)
     constexpr int FM = BM / (32 * WGM);  // 32x32 blocks per wave along M
@@ -59,21 +63,24 @@ __global__ __launch_bounds__(64 * WGM * WGN, 8 / (WGM * WGN)) void igemm_nhwc_ke
     constexpr int LA = BM / RR;          // 16-byte A loads per thread per step
     constexpr int LB = BN / RR;
     constexpr int L = LA + LB;
-    constexpr int STAGE = (BM + BN) * ROWB;
+    constexpr int STAGE = (BM + BN) * ROWB;  // one K group's half of a stage
+    constexpr int STAGE_ALL = KG * STAGE;
     constexpr int WN = FN * 32;          // columns per wave
     constexpr int WLD = WN + 4;          // row stride of a wave's epilogue slice (floats)
     constexpr int SLICE = 16 * WLD * 4;  // bytes
-    constexpr int SPS = STAGE / SLICE;   // slices per stage array
+    constexpr int SPS = STAGE_ALL / SLICE;  // slices per stage array
     static_assert(SPS * 2 >= NW, "epilogue slices fit in two stages");
+    // KG = 2: group 1's accumulators pass through stage 1 while group 0's slices are in stage 0
+    static_assert(KG == 1 || (SPS >= NW && NW * FM * FN * 16 * 64 * 4 <= STAGE_ALL), "K-group reduction fits");
     // One array per stage: distinct objects let the compiler see that the direct-to-LDS
     // loads into one stage never alias the operand reads from another, so it keeps the
     // explicit vmcnt waits instead of draining every load before each read.
-    __shared__ __attribute__((aligned(1024))) char st0[STAGE];
-    __shared__ __attribute__((aligned(1024))) char st1[STAGE];
-    __shared__ __attribute__((aligned(1024))) char st2[NS > 2 ? STAGE : 16];
-    __shared__ __attribute__((aligned(1024))) char st3[NS > 3 ? STAGE : 16];
-    __shared__ __attribute__((aligned(1024))) char st4[NS > 4 ? STAGE : 16];
-    __shared__ __attribute__((aligned(1024))) char st5[NS > 5 ? STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) char st0[STAGE_ALL];
+    __shared__ __attribute__((aligned(1024))) char st1[STAGE_ALL];
+    __shared__ __attribute__((aligned(1024))) char st2[NS > 2 ? STAGE_ALL : 16];
+    __shared__ __attribute__((aligned(1024))) char st3[NS > 3 ? STAGE_ALL : 16];
+    __shared__ __attribute__((aligned(1024))) char st4[NS > 4 ? STAGE_ALL : 16];
+    __shared__ __attribute__((aligned(1024))) char st5[NS > 5 ? STAGE_ALL : 16];
     auto stage_ptr = [&](auto idx) -> char * {
         constexpr int I = decltype(idx)::value;
         if constexpr (I == 0) return st0;
@@ -86,8 +93,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, 8 / (WGM * WGN)) void igemm_nhwc_ke
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave_all / NW;           // K group: takes the steps s with s % KG == grp
+    const int wave = wave_all - grp * NW;    // wave within its group
     const int wm = wave % WGM, wn = wave / WGM;
+    const int gofs = grp * STAGE;            // the group's half of each stage
 
     const int tile = xcd_remap(blockIdx.x, gridDim.x);
     const int m0 = (tile / tiles_n) * BM;
@@ -99,6 +109,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 8 / (WGM * WGN)) void igemm_nhwc_ke
     const int nsteps_all = (K + BK - 1) / BK;
     const int s_begin = blockIdx.y * steps_per_split;
     const int nsteps = max(0, min(nsteps_all, s_begin + steps_per_split) - s_begin);
+    const int nsup = (nsteps + KG - 1) / KG;  // ring steps: KG K steps each, one per group
+    const int s_first = s_begin + grp;        // this group's first K step
 
     const i32x4 rx = rsrc_words(a.x, (uint32_t)((size_t)a.N * H * W * Cin * sizeof(T)));
     const i32x4 rw = rsrc_words(a.w, (uint32_t)((size_t)a.Cout * K * sizeof(T)));
@@ -145,8 +157,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 8 / (WGM * WGN)) void igemm_nhwc_ke
     uint32_t a_mask[LA];
     if constexpr (TAP_INNER) {
         const int taps = kh * kw;
-        cb = s_begin / taps;
-        const int tap = s_begin - cb * taps;
+        cb = s_first / taps;
+        const int tap = s_first - cb * taps;
         ky = tap / kw;
         kx = tap - ky * kw;
         ci = 0;
@@ -165,7 +177,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 8 / (WGM * WGN)) void igemm_nhwc_ke
 #pragma unroll
         for (int j = 0; j < LB; ++j) b_base[j] = b_ok[j] ? (b_off[j] + c * 8) * (int)sizeof(T) : (int)0x80000000u;
     } else {
-        const int k = s_begin * BK + c * 8;
+        const int k = s_first * BK + c * 8;
         const int tap = k / Cin;
         ci = k - tap * Cin;
         ky = tap / kw;
@@ -175,8 +187,28 @@ __global__ __launch_bounds__(64 * WGM * WGN, 8 / (WGM * WGN)) void igemm_nhwc_ke
     // Issues one step's loads into LDS stage `stage`. A step past this slice (live
     // false) still issues them, with out-of-range offsets (no memory traffic), so every
     // step adds exactly L to the vector-memory counter and the waits below are exact.
+    auto advance = [&]() {
+        if constexpr (TAP_INNER) {
+            if (++kx == kw) {
+                kx = 0;
+                if (++ky == kh) {
+                    ky = 0;
+                    ++cb;
+                }
+            }
+        } else {
+            ci += BK;
+            while (ci >= Cin) {
+                ci -= Cin;
+                if (++kx == kw) {
+                    kx = 0;
+                    ++ky;
+                }
+            }
+        }
+    };
     auto issue = [&](char *stage, bool live) {
-        char *sA = stage;
+        char *sA = stage + gofs;
         char *sB = sA + BM * ROWB;
         if constexpr (TAP_INNER) {
             const int tap = ky * kw + kx;
@@ -191,13 +223,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 8 / (WGM * WGN)) void igemm_nhwc_ke
 #pragma unroll
             for (int j = 0; j < LB; ++j)
                 dma_b128(rw, kin ? (uint32_t)(b_base[j] + koff) : kOOB, lds_addr(sB + (j * NW + wave) * 1024));
-            if (++kx == kw) {
-                kx = 0;
-                if (++ky == kh) {
-                    ky = 0;
-                    ++cb;
-                }
-            }
+#pragma unroll
+            for (int r = 0; r < KG; ++r) advance();
             return;
         }
         const bool kin = live && ky < kh;
@@ -214,14 +241,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 8 / (WGM * WGN)) void igemm_nhwc_ke
             uint32_t off = (uint32_t)(b_off[j] + kk) * (uint32_t)sizeof(T);
             dma_b128(rw, (b_ok[j] && kin) ? off : kOOB, lds_addr(sB + (j * NW + wave) * 1024));
         }
-        ci += BK;
-        while (ci >= Cin) {
-            ci -= Cin;
-            if (++kx == kw) {
-                kx = 0;
-                ++ky;
-            }
-        }
+#pragma unroll
+        for (int r = 0; r < KG; ++r) advance();
     };
 
     f32x16 acc[FM][FN];
@@ -237,7 +258,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 8 / (WGM * WGN)) void igemm_nhwc_ke
     // One step's matrix-core work. The operand reads of sub-step ks+1 are issued
     // before the products of sub-step ks, so LDS latency overlaps the matrix cores.
     auto compute = [&](const char *stage) {
-        const char *sA = stage;
+        const char *sA = stage + gofs;
         const char *sB = sA + BM * ROWB;
         vec fa[2][FM], fb[2][FN];
         auto read = [&](int ks, vec(&xa)[FM], vec(&xb)[FN]) {
@@ -268,24 +289,48 @@ __global__ __launch_bounds__(64 * WGM * WGN, 8 / (WGM * WGN)) void igemm_nhwc_ke
     // flight), barrier (every wave's have landed and every wave is done with the
     // previous step's stage), matrix cores on this step, then refill the previous
     // step's stage with step s+NS-1 (so the matrix cores start right after the barrier).
+    // With KG = 2 a ring step holds two K steps, one per group; a group whose K step is
+    // past the slice loads zeros (live false) and adds zero products.
     auto step = [&](auto idx, int s) {
         constexpr int I = decltype(idx)::value;
         wait_vmcnt<(NS - 2) * L>();
         barrier_nofence();
         compute(stage_ptr(std::integral_constant<int, I>{}));
-        issue(stage_ptr(std::integral_constant<int, (I + NS - 1) % NS>{}), s + NS - 1 < nsteps);
+        issue(stage_ptr(std::integral_constant<int, (I + NS - 1) % NS>{}), KG * (s + NS - 1) + grp < nsteps);
     };
     [&]<int... I>(std::integer_sequence<int, I...>) {
-        (issue(stage_ptr(std::integral_constant<int, I>{}), I < nsteps), ...);
+        (issue(stage_ptr(std::integral_constant<int, I>{}), KG * I + grp < nsteps), ...);
     }(std::make_integer_sequence<int, NS - 1>{});
-    for (int s0 = 0; s0 < nsteps; s0 += NS) {
+    for (int s0 = 0; s0 < nsup; s0 += NS) {
         bool done = false;
         [&]<int... I>(std::integer_sequence<int, I...>) {
-            ((done = done || s0 + I >= nsteps, done ? void() : step(std::integral_constant<int, I>{}, s0 + I)), ...);
+            ((done = done || s0 + I >= nsup, done ? void() : step(std::integral_constant<int, I>{}, s0 + I)), ...);
         }(std::make_integer_sequence<int, NS>{});
     }
     wait_vmcnt<0>();
     __syncthreads();
+
+    if constexpr (KG == 2) {
+        // group 1 hands its accumulators to the wave of group 0 with the same output
+        // block (lane-major floats: conflict-free), then leaves
+        float *red = reinterpret_cast<float *>(st1) + wave * (FM * FN * 16 * 64) + lane;
+        if (grp == 1) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) red[((i * FN + j) * 16 + e) * 64] = acc[i][j][e];
+        }
+        __syncthreads();
+        if (grp == 1) return;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[i][j][e] += red[((i * FN + j) * 16 + e) * 64];
+    }
 
     // Epilogue, each wave over its own rows through its slice of stage 0 (LDS phase,
     // then global phase; see wave_epilogue_nhwc32).
@@ -371,23 +416,26 @@ namespace {
 
 // Tile shapes: (BM, BN) per workgroup, waves WGM x WGN, LDS stages.
 struct TileCfg {
-    int bm, bn, wgm, wgn, ns;
+    int bm, bn, wgm, wgn, ns, kg;
 };
 constexpr TileCfg kTiles[NHWC_TILE_COUNT] = {
-    {256, 128, 4, 2, 2},  // NHWC_TILE_256x128_W8
-    {128, 128, 2, 2, 3},  // NHWC_TILE_128x128
-    {128, 64, 2, 2, 3},   // NHWC_TILE_128x64
-    {256, 64, 4, 2, 3},   // NHWC_TILE_256x64_W8
-    {256, 32, 4, 1, 3},   // NHWC_TILE_256x32
-    {64, 64, 2, 2, 3},    // NHWC_TILE_64x64
-    {128, 128, 2, 4, 3},  // NHWC_TILE_128x128_W8
-    {128, 256, 2, 4, 2},  // NHWC_TILE_128x256_W8
-    {64, 64, 2, 2, 6},    // NHWC_TILE_64x64_D6
-    {128, 64, 2, 2, 5},   // NHWC_TILE_128x64_D5
-    {128, 128, 2, 4, 4},  // NHWC_TILE_128x128_W8_D4
-    {64, 128, 2, 2, 5},   // NHWC_TILE_64x128_D5
-    {64, 64, 2, 2, 4},    // NHWC_TILE_64x64_D4
-    {256, 128, 4, 2, 3},  // NHWC_TILE_256x128_W8_D3
+    {256, 128, 4, 2, 2, 1},  // NHWC_TILE_256x128_W8
+    {128, 128, 2, 2, 3, 1},  // NHWC_TILE_128x128
+    {128, 64, 2, 2, 3, 1},   // NHWC_TILE_128x64
+    {256, 64, 4, 2, 3, 1},   // NHWC_TILE_256x64_W8
+    {256, 32, 4, 1, 3, 1},   // NHWC_TILE_256x32
+    {64, 64, 2, 2, 3, 1},    // NHWC_TILE_64x64
+    {128, 128, 2, 4, 3, 1},  // NHWC_TILE_128x128_W8
+    {128, 256, 2, 4, 2, 1},  // NHWC_TILE_128x256_W8
+    {64, 64, 2, 2, 6, 1},    // NHWC_TILE_64x64_D6
+    {128, 64, 2, 2, 5, 1},   // NHWC_TILE_128x64_D5
+    {128, 128, 2, 4, 4, 1},  // NHWC_TILE_128x128_W8_D4
+    {64, 128, 2, 2, 5, 1},   // NHWC_TILE_64x128_D5
+    {64, 64, 2, 2, 4, 1},    // NHWC_TILE_64x64_D4
+    {256, 128, 4, 2, 3, 1},  // NHWC_TILE_256x128_W8_D3
+    {64, 64, 2, 2, 3, 2},    // NHWC_TILE_64x64_K2
+    {64, 64, 2, 2, 4, 2},    // NHWC_TILE_64x64_K2_D4
+    {64, 64, 2, 2, 2, 2},    // NHWC_TILE_64x64_K2_D2 (64 KiB of LDS: two workgroups per CU)
 };
 
 template <typename T, int TILE>
@@ -400,29 +448,29 @@ hipError_t launch_t(const ConvArgs &a, const NhwcPlan &p, float *partials, hipSt
     const int nsteps = (a.K + 63) / 64;
     const int per = (nsteps + splits - 1) / splits;
     dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)splits);
-    dim3 block(64 * c.wgm * c.wgn);
+    dim3 block(64 * c.wgm * c.wgn * c.kg);
     hipError_t e;
     if (p.nchw_out) {
         if (splits > 1) return hipErrorInvalidValue;  // split-K writes channel-last only
         if (p.tap_inner)
-            e = launch_kernel(igemm_nhwc_kernel<T, c.bm, c.bn, c.wgm, c.wgn, c.ns, true, false, true>, grid, block, 0,
+            e = launch_kernel(igemm_nhwc_kernel<T, c.bm, c.bn, c.wgm, c.wgn, c.ns, c.kg, true, false, true>, grid, block, 0,
                               st, a, tiles_n, per, partials);
         else
-            e = launch_kernel(igemm_nhwc_kernel<T, c.bm, c.bn, c.wgm, c.wgn, c.ns, false, false, true>, grid, block,
+            e = launch_kernel(igemm_nhwc_kernel<T, c.bm, c.bn, c.wgm, c.wgn, c.ns, c.kg, false, false, true>, grid, block,
                               0, st, a, tiles_n, per, partials);
     } else if (p.tap_inner) {
         if (splits > 1)
-            e = launch_kernel(igemm_nhwc_kernel<T, c.bm, c.bn, c.wgm, c.wgn, c.ns, true, true, false>, grid, block, 0,
+            e = launch_kernel(igemm_nhwc_kernel<T, c.bm, c.bn, c.wgm, c.wgn, c.ns, c.kg, true, true, false>, grid, block, 0,
                               st, a, tiles_n, per, partials);
         else
-            e = launch_kernel(igemm_nhwc_kernel<T, c.bm, c.bn, c.wgm, c.wgn, c.ns, true, false, false>, grid, block,
+            e = launch_kernel(igemm_nhwc_kernel<T, c.bm, c.bn, c.wgm, c.wgn, c.ns, c.kg, true, false, false>, grid, block,
                               0, st, a, tiles_n, per, partials);
     } else {
         if (splits > 1)
-            e = launch_kernel(igemm_nhwc_kernel<T, c.bm, c.bn, c.wgm, c.wgn, c.ns, false, true, false>, grid, block,
+            e = launch_kernel(igemm_nhwc_kernel<T, c.bm, c.bn, c.wgm, c.wgn, c.ns, c.kg, false, true, false>, grid, block,
                               0, st, a, tiles_n, per, partials);
         else
-            e = launch_kernel(igemm_nhwc_kernel<T, c.bm, c.bn, c.wgm, c.wgn, c.ns, false, false, false>, grid, block,
+            e = launch_kernel(igemm_nhwc_kernel<T, c.bm, c.bn, c.wgm, c.wgn, c.ns, c.kg, false, false, false>, grid, block,
                               0, st, a, tiles_n, per, partials);
     }
     if (e != hipSuccess || splits == 1) return e;
@@ -451,6 +499,9 @@ hipError_t launch_dtype(const ConvArgs &a, const NhwcPlan &p, float *partials, h
     case 11: return launch_t<T, 11>(a, p, partials, st);
     case 12: return launch_t<T, 12>(a, p, partials, st);
     case 13: return launch_t<T, 13>(a, p, partials, st);
+    case 14: return launch_t<T, 14>(a, p, partials, st);
+    case 15: return launch_t<T, 15>(a, p, partials, st);
+    case 16: return launch_t<T, 16>(a, p, partials, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -460,7 +511,7 @@ hipError_t launch_dtype(const ConvArgs &a, const NhwcPlan &p, float *partials, h
 int nhwc_tile_bm(int tile) { return (tile >= 0 && tile < NHWC_TILE_COUNT) ? kTiles[tile].bm : 0; }
 int nhwc_tile_bn(int tile) { return (tile >= 0 && tile < NHWC_TILE_COUNT) ? kTiles[tile].bn : 0; }
 int nhwc_tile_waves(int tile) {
-    return (tile >= 0 && tile < NHWC_TILE_COUNT) ? kTiles[tile].wgm * kTiles[tile].wgn : 0;
+    return (tile >= 0 && tile < NHWC_TILE_COUNT) ? kTiles[tile].wgm * kTiles[tile].wgn * kTiles[tile].kg : 0;
 }
 
 hipError_t launch_igemm_nhwc(const ConvArgs &a, int dtype, const NhwcPlan &p, float *partials,

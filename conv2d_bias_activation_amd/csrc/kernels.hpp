@@ -37,7 +37,10 @@ enum NhwcTile {
     NHWC_TILE_64x128_D5 = 11,
     NHWC_TILE_64x64_D4 = 12,
     NHWC_TILE_256x128_W8_D3 = 13,
-    NHWC_TILE_COUNT = 14,
+    NHWC_TILE_64x64_K2 = 14,
+    NHWC_TILE_64x64_K2_D4 = 15,
+    NHWC_TILE_64x64_K2_D2 = 16,
+    NHWC_TILE_COUNT = 17,
 };
 
 struct NhwcPlan {
