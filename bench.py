@@ -304,6 +304,17 @@ KERNEL_SOURCES = [
 ]
 
 
+# plan-name prefix -> part of the kernel's symbol (the library's kernels live in namespace c2d)
+KERNEL_SYMBOLS = [
+    ("igemm_nhwc_pipe", "3c2d17igemm_nhwc_kernel"),
+    ("halo3x3", "3c2d14halo3x3_kernel"),
+    ("stem3x3", "3c2d"),
+    ("igemm_", "3c2d"),
+    ("maxpool", "3c2d"),
+    ("avgpool", "3c2d"),
+]
+
+
 def kernel_source_hash(plan=None):
     csrc = os.path.join(ROOT, "conv2d_bias_activation_amd", "csrc")
     files = sorted(f for f in os.listdir(csrc) if f.endswith((".hip", ".hpp")))
@@ -391,23 +402,35 @@ def pmc_per_dispatch(path, counter):
 
 def write_traffic(src, copy_mib, plan):
     """HBM bytes per launch of `plan`'s kernel: FETCH_SIZE and WRITE_SIZE (KiB per dispatch),
-    each scaled by bytes / counter of a plain copy of copy_mib MiB read and written."""
+    each scaled by bytes / counter of a plain copy of copy_mib MiB read and written. The
+    record joins those of other plans already in the file (each valid while its own
+    kernel sources hash the same)."""
     known = copy_mib * 1024.0  # KiB
-    def busiest(path, counter):
+    def busiest(path, counter, symbol=""):
         d = pmc_per_dispatch(path, counter)
-        name = max(d, key=lambda k: d[k][0])  # the kernel launched most often in that run
+        names = [k for k in d if symbol in k]
+        if not names:
+            raise SystemExit(f"no kernel named like {symbol!r} in {path}")
+        name = max(names, key=lambda k: d[k][0])  # the one launched most often in that run
         return name, d[name][1]
+    family = plan.split("+")[-1]  # a channel-first plan's kernel is the channel-last one after the copy
+    symbol = next((s for prefix, s in KERNEL_SYMBOLS if family.startswith(prefix)), "")
     _, cf = busiest(os.path.join(src, "copy_fetch"), "FETCH_SIZE")
     _, cw = busiest(os.path.join(src, "copy_write"), "WRITE_SIZE")
-    kname, kf = busiest(os.path.join(src, "fetch"), "FETCH_SIZE")
-    _, kw = busiest(os.path.join(src, "write"), "WRITE_SIZE")
+    kname, kf = busiest(os.path.join(src, "fetch"), "FETCH_SIZE", symbol)
+    _, kw = busiest(os.path.join(src, "write"), "WRITE_SIZE", symbol)
     sf, sw = known / cf, known / cw
+    out = os.path.join(ROOT, "profiles", "traffic.json")
+    kernels = {}
+    if os.path.exists(out):
+        with open(out) as f:
+            kernels = json.load(f).get("kernels", {})
+    kernels[plan.replace(" tuned", "")] = dict(kernel=kname, source_hash=kernel_source_hash(plan),
+                                               fetch_kib=round(kf, 1), write_kib=round(kw, 1),
+                                               bytes_per_launch=int(round((kf * sf + kw * sw) * 1024)))
     rec = dict(copy=dict(mib=copy_mib, fetch_kib=round(cf, 1), write_kib=round(cw, 1),
                          fetch_scale=round(sf, 4), write_scale=round(sw, 4)),
-               kernels={plan: dict(kernel=kname, source_hash=kernel_source_hash(plan), fetch_kib=round(kf, 1),
-                                   write_kib=round(kw, 1),
-                                   bytes_per_launch=int(round((kf * sf + kw * sw) * 1024)))})
-    out = os.path.join(ROOT, "profiles", "traffic.json")
+               kernels=kernels)
     with open(out, "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec))

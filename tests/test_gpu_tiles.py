@@ -8,6 +8,9 @@ is a multiple of 64, channel runs across taps otherwise), an odd number of K ste
 (the second K group of the two-group tiles then idles on the last one), split-K
 and the channel-first output path.
 """
+import os
+import tempfile
+
 import pytest
 import torch
 
@@ -50,7 +53,6 @@ def _device_key(n, h, w, cin, cout, k, stride, pad, layout, dt, res):
     """Table key of a shape on this device: the tuner writes it for one small shape, the
     device part (architecture and CU count) is reused."""
     c2d.tune(1, 8, 8, 64, 64, 3, 3, 1, 1, "relu", dtype=c2d.DTYPE_BF16, reps=1)
-    import tempfile, os
     with tempfile.TemporaryDirectory() as d:
         p = os.path.join(d, "t.txt")
         c2d.tune_save(p)
