@@ -308,10 +308,10 @@ KERNEL_SOURCES = [
 KERNEL_SYMBOLS = [
     ("igemm_nhwc_pipe", "3c2d17igemm_nhwc_kernel"),
     ("halo3x3", "3c2d14halo3x3_kernel"),
-    ("stem3x3", "3c2d"),
-    ("igemm_", "3c2d"),
-    ("maxpool", "3c2d"),
-    ("avgpool", "3c2d"),
+    ("stem3x3", "stem3_"),  # stem3_kernel, stem3_pool_kernel
+    ("igemm_", "3c2d12igemm_kernel"),
+    ("maxpool", "maxpool_"),
+    ("avgpool", "avgpool_"),
 ]
 
 
@@ -571,8 +571,8 @@ def main():
         write_traffic(args.traffic_from, args.copy_probe or 256, args.launch_plan)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU only; multi-GPU runs are not "
-                                   "part of this build", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "this benchmark runs on one GPU only: the library has no multi-GPU "
+                                   "path (each GPU would run its own share of the batch)", "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
 
