@@ -610,7 +610,8 @@ struct DeconvPlan {
     bool mfma;
     bool prepacked;  // the weights come packed by conv_transpose4x4s2_pack (da.wp)
     bool all;      // Cin <= 256: the kernel that stages the whole input strip at once
-    bool x_copy;   // channel-first input copied to channel-last in the scratch first (all)
+    bool x_copy;   // channel-first input copied to channel-last in the scratch first (all); else
+                   // the kernel reads the planes (W % 8 == 0, x 16-byte aligned)
     size_t x_off;  // byte offset of that copy in the scratch (after the packed weights)
     bool out_f32;  // y in fp32 (16-bit input)
 };
@@ -663,11 +664,12 @@ int check_deconv(const void *x, const void *w, const float *bias, const float *a
     const size_t wp_bytes = (size_t)16 * a->CoP * ((Cin + 63) / 64 * 64) * eb;
     p->mfma = dtype != CONV2D_DTYPE_F32 && (Cin % 8) == 0 && wp_bytes <= kScratchBytes && (nchw || aligned16(x)) &&
               xe * eb < (1ll << 31);
-    // channel-first inputs with up to 256 channels: copied to channel-last in the scratch
-    // (when that fits beside the weights) by a 16-byte transpose, then the kernel that
-    // stages the whole input strip at once (measured faster than staging element by
-    // element from the planes for the IFNet deconv; for channel-last inputs the chunked
-    // kernel measured faster)
+    // channel-first inputs with up to 256 channels: the kernel that stages the whole input
+    // strip at once, reading the planes with 16-byte loads of 8-pixel segments when W % 8
+    // == 0 and x is 16-byte aligned, else from a channel-last copy in the scratch (when
+    // that fits beside the weights) made by a 16-byte transpose (element-by-element
+    // staging from the planes measured slower than that copy; for channel-last inputs the
+    // chunked kernel measured faster)
     if (packed) {
         // caller-owned packed weights: the matrix-core path only, the scratch only for the
         // channel-last copy of a channel-first input
@@ -682,9 +684,9 @@ int check_deconv(const void *x, const void *w, const float *bias, const float *a
         a->wp = w;
     }
     p->x_off = packed ? 0 : round256(wp_bytes);
-    p->x_copy = nchw;
+    p->x_copy = nchw && !((W % 8) == 0 && aligned16(x));
     p->all = p->mfma && nchw && Cin <= 256 && N <= 65535 &&
-             p->x_off + round256((size_t)(xe * eb)) <= kScratchBytes;
+             p->x_off + (p->x_copy ? round256((size_t)(xe * eb)) : 0) <= kScratchBytes;
     a->x_bytes = (uint32_t)(xe * eb < (1ll << 31) ? xe * eb : 0);
     a->wp_bytes = (uint32_t)wp_bytes;
     return CONV2D_OK;
@@ -743,7 +745,7 @@ struct OpPlan {
 bool needs_scratch(const OpPlan &o) {
     if (o.kind == CONV2D_OP_CONV)
         return o.plan.family == FAM_NCHW_VIA_NHWC || (o.plan.family == FAM_NHWC && o.plan.nh.splits > 1);
-    if (o.kind == CONV2D_OP_DECONV) return o.dp.mfma;
+    if (o.kind == CONV2D_OP_DECONV) return o.dp.mfma && (!o.dp.prepacked || (o.dp.all && o.dp.x_copy));
     if (o.kind == CONV2D_OP_AVGPOOL_CONV1X1) return true;
     return o.kind == CONV2D_OP_CONV_MAXPOOL && o.pf.kind == POOL_TWO_KERNELS;
 }
@@ -941,7 +943,7 @@ int launch_op(const OpPlan &o, hipStream_t st) {
         }
         float *scratch = nullptr;
         DeconvArgs a = o.da;
-        if (!o.dp.prepacked || o.dp.all) {
+        if (!o.dp.prepacked || (o.dp.all && o.dp.x_copy)) {
             int rc = get_scratch(&scratch);
             if (rc) return rc;
         }
@@ -955,7 +957,7 @@ int launch_op(const OpPlan &o, hipStream_t st) {
                 e = launch_nchw_to_nhwc(a.x, xs, a.N, a.Cin, a.H * a.W, o.dtype, st);
                 a.x = xs;
             }
-            if (e == hipSuccess) e = launch_deconv_mfma_all(a, o.dtype, o.dp.out_f32, nchw, st);
+            if (e == hipSuccess) e = launch_deconv_mfma_all(a, o.dtype, o.dp.out_f32, nchw, !o.dp.x_copy, st);
         } else if (e == hipSuccess) {
             e = launch_deconv_mfma(a, o.dtype, o.dp.out_f32, nchw, st);
         }

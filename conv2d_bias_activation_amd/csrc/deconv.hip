@@ -270,17 +270,21 @@ __global__ __launch_bounds__(256) void deconv_mfma_kernel(DeconvArgs a) {
     }
 }
 
-// Channel-last 16-bit input with Cin % 8 == 0 and Cin <= 256 (16-byte aligned; for a
-// channel-first layer, its channel-last copy), packed weights: the same tiles and
+// 16-bit input with Cin % 8 == 0 and Cin <= 256, packed weights: the same tiles and
 // products as deconv_mfma_kernel, but the whole strip (4 rows x 34 pixels x every input
 // channel) is staged in LDS at once with 16-byte loads, so a workgroup waits for one
-// round of input loads instead of one per 64-channel chunk. y channel-first (NCHW_OUT)
-// or channel-last.
+// round of input loads instead of one per 64-channel chunk. The input is channel-last
+// (16-byte aligned; for a channel-first layer, its channel-last copy) or, with NCHW_IN,
+// the caller's channel-first planes (W % 8 == 0, 16-byte aligned), transposed while they
+// are staged. y channel-first (NCHW_OUT) or channel-last.
 constexpr int DA_CMAX = 256;                                  // input channels staged at most
 constexpr int DA_PSMAX = DA_CMAX + 8;                         // LDS elements per pixel at most
 constexpr int DA_VQ = (DC_ROWS * DC_SPX * (DA_CMAX / 8) + 255) / 256;  // vectors per thread (17)
+// channel-first staging: 8-pixel segments i0-8+8s (s < 6) cover the strip's pixels i0-1 .. i0+32
+constexpr int DA_NSEG = 6;
+constexpr int DA_PQ = (DA_CMAX / 2 * DC_ROWS * DA_NSEG + 255) / 256;  // work items per thread (12)
 
-template <typename T, typename TO, bool NCHW_OUT>
+template <typename T, typename TO, bool NCHW_OUT, bool NCHW_IN>
 __global__ __launch_bounds__(256) void deconv_mfma_all_kernel(DeconvArgs a) {
     typedef typename Mfma32<T>::vec vec;
     // the staged strip; its tail also receives the stores of lanes past the last vector
@@ -306,16 +310,33 @@ __global__ __launch_bounds__(256) void deconv_mfma_all_kernel(DeconvArgs a) {
 
     // every input load of the strip in flight at once (out-of-range offsets read zero)
     const __amdgpu_buffer_rsrc_t rx = rsrc_bytes(a.x, a.x_bytes);
-    u32x4 sv[DA_VQ];
+    u32x4 sv[NCHW_IN ? 1 : DA_VQ];
+    // channel-first: work item (channel pair cp, strip row r, segment sg) loads 8 pixels
+    // of both planes of the pair; a segment lies wholly inside or outside the image row
+    u32x4 pv0[NCHW_IN ? DA_PQ : 1], pv1[NCHW_IN ? DA_PQ : 1];
+    const int nitems = CinP / 2 * DC_ROWS * DA_NSEG;
+    if constexpr (NCHW_IN) {
 #pragma unroll
-    for (int q = 0; q < DA_VQ; ++q) {
-        const int idx = tid + 256 * q;
-        const int pr = idx / CV, cv = idx - pr * CV;     // pixel of the strip, channel vector
-        const int r = pr / DC_SPX, p = pr - r * DC_SPX;
-        const int iy = j0 - 1 + r, ix = i0 - 1 + p, ci = cv * 8;
-        const bool ok = idx < nvec && (unsigned)iy < (unsigned)H && (unsigned)ix < (unsigned)W && ci < Cin;
-        const uint32_t off = ok ? ((((uint32_t)n * H + iy) * W + ix) * Cin + ci) * 2u : kOob;
-        sv[q] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)off, 0, 0);
+        for (int q = 0; q < DA_PQ; ++q) {
+            const int idx = tid + 256 * q;
+            const int sg = idx % DA_NSEG, r = (idx / DA_NSEG) % DC_ROWS, ci = 2 * (idx / (DA_NSEG * DC_ROWS));
+            const int iy = j0 - 1 + r, ix = i0 - 8 + 8 * sg;
+            const bool ok = idx < nitems && (unsigned)iy < (unsigned)H && (unsigned)ix < (unsigned)W && ci < Cin;
+            const uint32_t off = ok ? ((((uint32_t)n * Cin + ci) * H + iy) * W + ix) * 2u : kOob;
+            pv0[q] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)off, 0, 0);
+            pv1[q] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(ok ? off + (uint32_t)H * W * 2u : kOob), 0, 0);
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < DA_VQ; ++q) {
+            const int idx = tid + 256 * q;
+            const int pr = idx / CV, cv = idx - pr * CV;     // pixel of the strip, channel vector
+            const int r = pr / DC_SPX, p = pr - r * DC_SPX;
+            const int iy = j0 - 1 + r, ix = i0 - 1 + p, ci = cv * 8;
+            const bool ok = idx < nvec && (unsigned)iy < (unsigned)H && (unsigned)ix < (unsigned)W && ci < Cin;
+            const uint32_t off = ok ? ((((uint32_t)n * H + iy) * W + ix) * Cin + ci) * 2u : kOob;
+            sv[q] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)off, 0, 0);
+        }
     }
     // weight operands of chunk 0
     const __amdgpu_buffer_rsrc_t rw = rsrc_bytes(a.wp, a.wp_bytes);
@@ -329,12 +350,31 @@ __global__ __launch_bounds__(256) void deconv_mfma_all_kernel(DeconvArgs a) {
             bw[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(c < nchp ? cb + i * 1024u : kOob), 0, 0);
     };
     load_b(0);
+    if constexpr (NCHW_IN) {
+        // pixel k of segment sg is strip pixel p = 8 sg + k - 7; the pair's two values go
+        // to LDS as one 4-byte word (ci even, PS even)
 #pragma unroll
-    for (int q = 0; q < DA_VQ; ++q) {
-        const int idx = tid + 256 * q;
-        const int pr = idx / CV, cv = idx - pr * CV;
-        const int at = idx < nvec ? pr * PS + cv * 8 : DC_ROWS * DC_SPX * DA_PSMAX + tid * 8;
-        *reinterpret_cast<u32x4 *>(&sx[at]) = sv[q];
+        for (int q = 0; q < DA_PQ; ++q) {
+            const int idx = tid + 256 * q;
+            if (idx >= nitems) continue;
+            const int sg = idx % DA_NSEG, r = (idx / DA_NSEG) % DC_ROWS, ci = 2 * (idx / (DA_NSEG * DC_ROWS));
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int p = 8 * sg + k - 7;
+                if (p < 0 || p >= DC_SPX) continue;
+                const uint32_t lo = (pv0[q][k >> 1] >> (16 * (k & 1))) & 0xffffu;
+                const uint32_t hi = (pv1[q][k >> 1] >> (16 * (k & 1))) & 0xffffu;
+                *reinterpret_cast<uint32_t *>(&sx[(r * DC_SPX + p) * PS + ci]) = lo | (hi << 16);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < DA_VQ; ++q) {
+            const int idx = tid + 256 * q;
+            const int pr = idx / CV, cv = idx - pr * CV;
+            const int at = idx < nvec ? pr * PS + cv * 8 : DC_ROWS * DC_SPX * DA_PSMAX + tid * 8;
+            *reinterpret_cast<u32x4 *>(&sx[at]) = sv[q];
+        }
     }
     __syncthreads();
 
@@ -497,20 +537,22 @@ hipError_t launch_deconv_mfma(const DeconvArgs &a, int dtype, bool out_f32, bool
 }
 
 template <typename T, typename TO>
-static hipError_t mfma_all_t(const DeconvArgs &a, bool nchw_out, hipStream_t st) {
+static hipError_t mfma_all_t(const DeconvArgs &a, bool nchw_in, hipStream_t st) {
     const long long tiles = (long long)a.N * ((a.H + DC_MR - 1) / DC_MR) * ((a.W + DC_TW - 1) / DC_TW);
     dim3 grid((unsigned)tiles, (unsigned)(a.CoP / 32));
-    (void)nchw_out;
-    return launch_kernel(deconv_mfma_all_kernel<T, TO, true>, grid, dim3(256), 0, st, a);
+    if (nchw_in) return launch_kernel(deconv_mfma_all_kernel<T, TO, true, true>, grid, dim3(256), 0, st, a);
+    return launch_kernel(deconv_mfma_all_kernel<T, TO, true, false>, grid, dim3(256), 0, st, a);
 }
 
-hipError_t launch_deconv_mfma_all(const DeconvArgs &a, int dtype, bool out_f32, bool nchw_out, hipStream_t st) {
-    if (a.Cin > DA_CMAX || (a.Cin % 8) != 0 || !nchw_out) return hipErrorInvalidValue;  // channel-first layers only
+hipError_t launch_deconv_mfma_all(const DeconvArgs &a, int dtype, bool out_f32, bool nchw_out, bool nchw_in,
+                                  hipStream_t st) {
+    // channel-first layers only; the planes are read directly only when 8-pixel segments are aligned
+    if (a.Cin > DA_CMAX || (a.Cin % 8) != 0 || !nchw_out || (nchw_in && (a.W % 8) != 0)) return hipErrorInvalidValue;
     switch (dtype) {
     case CONV2D_DTYPE_BF16:
-        return out_f32 ? mfma_all_t<bf16, float>(a, nchw_out, st) : mfma_all_t<bf16, bf16>(a, nchw_out, st);
+        return out_f32 ? mfma_all_t<bf16, float>(a, nchw_in, st) : mfma_all_t<bf16, bf16>(a, nchw_in, st);
     case CONV2D_DTYPE_F16:
-        return out_f32 ? mfma_all_t<f16, float>(a, nchw_out, st) : mfma_all_t<f16, f16>(a, nchw_out, st);
+        return out_f32 ? mfma_all_t<f16, float>(a, nchw_in, st) : mfma_all_t<f16, f16>(a, nchw_in, st);
     default:
         return hipErrorInvalidValue;
     }

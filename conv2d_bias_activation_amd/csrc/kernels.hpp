@@ -132,10 +132,12 @@ hipError_t launch_deconv_pack(const void *w, void *wp, int Cin, int Cout, int Co
 // channel-first; y in the input's type or (out_f32) fp32.
 hipError_t launch_deconv_mfma(const DeconvArgs &a, int dtype, bool out_f32, bool nchw, hipStream_t st);
 
-// The same products with the whole input strip staged at once: channel-last x (the
-// channel-last copy of a channel-first layer's input) with Cin % 8 == 0 and Cin <= 256;
+// The same products with the whole input strip staged at once, Cin % 8 == 0 and
+// Cin <= 256: channel-last x (the channel-last copy of a channel-first layer's input)
+// or, with nchw_in, the channel-first x itself (W % 8 == 0, 16-byte aligned);
 // y channel-first (nchw_out must be true).
-hipError_t launch_deconv_mfma_all(const DeconvArgs &a, int dtype, bool out_f32, bool nchw_out, hipStream_t st);
+hipError_t launch_deconv_mfma_all(const DeconvArgs &a, int dtype, bool out_f32, bool nchw_out, bool nchw_in,
+                                  hipStream_t st);
 
 // OIHW -> OHWI weights alone (16-bit types).
 hipError_t launch_oihw_to_ohwi(const void *w, void *w2, int Cout, int Cin, int taps, int dtype, hipStream_t st);

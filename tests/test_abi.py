@@ -162,14 +162,20 @@ def test_deconv_plan_and_argument_checks():
     """Host-only: which kernels conv_transpose4x4s2 picks, and what it rejects."""
     bf16, f16, f32 = c2d.DTYPE_BF16, c2d.DTYPE_F16, c2d.DTYPE_F32
     nhwc, nchw = c2d.LAYOUT_NHWC, c2d.LAYOUT_NCHW
+    # channel-first, W % 8 == 0: the whole-strip kernel reads the planes itself
     assert c2d.plan_deconv(1, 68, 120, 240, 5, 0, nchw, f16, f32) == \
+        "deconv4x4s2_pack+deconv4x4s2_mfma_all_nchw f16 out f32"
+    # W % 8 != 0: a channel-last copy first
+    assert c2d.plan_deconv(1, 17, 30, 240, 5, 0, nchw, f16, f32) == \
         "deconv4x4s2_pack+to_nhwc+deconv4x4s2_mfma_all_nchw f16 out f32"
     assert c2d.plan_deconv(1, 64, 64, 256, 128, 1, nhwc, bf16) == "deconv4x4s2_pack+deconv4x4s2_mfma_nhwc bf16"
     # past 256 input channels: 64-channel chunks through a double-buffered LDS ring
     assert c2d.plan_deconv(1, 16, 16, 264, 64, 1, nhwc, bf16) == "deconv4x4s2_pack+deconv4x4s2_mfma_nhwc bf16"
     assert c2d.plan_deconv(1, 16, 16, 512, 64, 1, nchw, bf16) == "deconv4x4s2_pack+deconv4x4s2_mfma_nchw bf16"
     # a channel-first input whose channel-last copy does not fit the scratch beside the weights
-    assert c2d.plan_deconv(4, 512, 512, 64, 8, 0, nchw, bf16) == "deconv4x4s2_pack+deconv4x4s2_mfma_nchw bf16"
+    assert c2d.plan_deconv(4, 512, 516, 64, 8, 0, nchw, bf16) == "deconv4x4s2_pack+deconv4x4s2_mfma_nchw bf16"
+    # the same map with W % 8 == 0 needs no copy
+    assert c2d.plan_deconv(4, 512, 512, 64, 8, 0, nchw, bf16) == "deconv4x4s2_pack+deconv4x4s2_mfma_all_nchw bf16"
     assert c2d.plan_deconv(1, 8, 8, 12, 8, 1, nhwc, bf16) == "deconv4x4s2_direct bf16"  # Cin % 8 != 0
     assert c2d.plan_deconv(1, 8, 8, 16, 8, 1, nhwc, f32) == "deconv4x4s2_direct f32"
     # packed weights over the 64 MiB scratch: 16 * 2048 * 1024 bf16 = 64 MiB fits, one more

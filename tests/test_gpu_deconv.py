@@ -43,6 +43,12 @@ CASES = [
     (1, 7, 40, 264, 40, "prelu", "nhwc", "bf16", "bf16", "mfma"),    # Cin > 256: chunked ring, K tail
     (1, 9, 35, 320, 33, "relu", "nchw", "f16", "f32", "mfma"),       # chunked, channel-first staging
     (3, 5, 21, 256, 8, "silu", "nchw", "bf16", "bf16", "mfma"),      # whole strip, channel-first copy
+    # whole strip read from the planes (W % 8 == 0): ragged last tile column, partial
+    # 64-channel chunk, two Cout blocks, several images, odd heights
+    (2, 5, 40, 40, 33, "relu", "nchw", "bf16", "bf16", "mfma"),
+    (1, 7, 16, 200, 5, "prelu", "nchw", "f16", "f32", "mfma"),
+    (3, 4, 64, 8, 16, "silu", "nchw", "f16", "f16", "mfma"),
+    (1, 3, 8, 256, 40, "none", "nchw", "bf16", "f32", "mfma"),
     (1, 6, 9, 12, 7, "relu", "nhwc", "bf16", "bf16", "direct"),      # Cin % 8 != 0
     (1, 6, 9, 16, 7, "prelu", "nhwc", "f32", "f32", "direct"),
     (2, 5, 6, 10, 3, "silu", "nchw", "f32", "f32", "direct"),
