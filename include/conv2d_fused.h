@@ -28,8 +28,9 @@
  *    and keeps until the process ends. It holds the fp32 partial sums of split-K
  *    calls, the channel-last copies of x and w of 16-bit channel-first calls and
  *    the unpooled conv output of conv2d_fused_maxpool3x3s2 calls that run as two
- *    kernels, and the repacked weights of conv_transpose4x4s2 calls on the matrix
- *    cores.
+ *    kernels, and the repacked weights (and, for channel-first inputs whose width is
+ *    not a multiple of 8, the channel-last copy of x) of conv_transpose4x4s2 calls on
+ *    the matrix cores.
  *    Such calls on one device all use that buffer: callers that run conv2d_fused
  *    on several streams of one device at the same time must serialise those
  *    calls. (Under HIP graph capture, make one call on each device before
@@ -216,8 +217,9 @@ int conv_transpose4x4s2(const void *x, const void *w, const float *bias, const f
  * conv_transpose4x4s2_prepacked: conv_transpose4x4s2 with the packed weights wp in place
  *   of w; needs 16-bit x with Cin % 8 == 0 (16-byte aligned when channel-last), x and wp
  *   under 2 GiB (CONV2D_EUNSUPPORTED otherwise). Results are bit-identical to
- *   conv_transpose4x4s2 on the unpacked weights. A channel-first input still uses the
- *   library scratch for its channel-last copy; nothing else is written but y.
+ *   conv_transpose4x4s2 on the unpacked weights. A channel-first input whose width is
+ *   not a multiple of 8 (or that is not 16-byte aligned) still uses the library scratch
+ *   for its channel-last copy; other calls write nothing but y.
  */
 int conv_transpose4x4s2_packed_bytes(int Cin, int Cout, int dtype, size_t *bytes);
 int conv_transpose4x4s2_pack(const void *w, void *wp, int Cin, int Cout, int dtype, void *stream);
