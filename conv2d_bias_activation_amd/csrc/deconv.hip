@@ -279,17 +279,20 @@ __global__ __launch_bounds__(256) void deconv_mfma_kernel(DeconvArgs a) {
 // are staged. y channel-first (NCHW_OUT) or channel-last.
 constexpr int DA_CMAX = 256;                                  // input channels staged at most
 constexpr int DA_PSMAX = DA_CMAX + 8;                         // LDS elements per pixel at most
-constexpr int DA_VQ = (DC_ROWS * DC_SPX * (DA_CMAX / 8) + 255) / 256;  // vectors per thread (17)
 // channel-first staging: 8-pixel segments i0-8+8s (s < 6) cover the strip's pixels i0-1 .. i0+32
 constexpr int DA_NSEG = 6;
-constexpr int DA_PQ = (DA_CMAX / 2 * DC_ROWS * DA_NSEG + 255) / 256;  // work items per thread (12)
 
-template <typename T, typename TO, bool NCHW_OUT, bool NCHW_IN>
+template <typename T, typename TO, bool NCHW_OUT, bool NCHW_IN, int MR>
 __global__ __launch_bounds__(256) void deconv_mfma_all_kernel(DeconvArgs a) {
+    // MR input rows per tile (2, or 1 when the 2-row tiles leave CUs idle); ROWS staged rows
+    constexpr int ROWS = MR + 2;
+    constexpr int OCS = 2 * MR * DC_OLD + 1;  // epilogue tile channel stride (odd)
+    constexpr int VQ = (ROWS * DC_SPX * (DA_CMAX / 8) + 255) / 256;  // 16-byte vectors per thread (17 at MR 2)
+    constexpr int PQ = (DA_CMAX / 2 * ROWS * DA_NSEG + 255) / 256;   // plane work items per thread (12 at MR 2)
     typedef typename Mfma32<T>::vec vec;
     // the staged strip; its tail also receives the stores of lanes past the last vector
-    __shared__ __attribute__((aligned(16))) T sx[DC_ROWS * DC_SPX * DA_PSMAX + 256 * 8];
-    __shared__ float so[32 * DC_OCS];
+    __shared__ __attribute__((aligned(16))) T sx[ROWS * DC_SPX * DA_PSMAX + 256 * 8];
+    __shared__ float so[32 * OCS];
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int py = wv >> 1, px = wv & 1;
@@ -298,28 +301,28 @@ __global__ __launch_bounds__(256) void deconv_mfma_all_kernel(DeconvArgs a) {
     int t = blockIdx.x;
     const int ib = t % tiles_w;
     t /= tiles_w;
-    const int tiles_h = (H + DC_MR - 1) / DC_MR;
-    const int j0 = (t % tiles_h) * DC_MR, n = t / tiles_h;
+    const int tiles_h = (H + MR - 1) / MR;
+    const int j0 = (t % tiles_h) * MR, n = t / tiles_h;
     const int i0 = ib * DC_TW;
     const int co0 = blockIdx.y * 32;
     const int nchp = (Cin + DC_KC - 1) / DC_KC;
     const int CinP = nchp * DC_KC;        // staged channels: zero past Cin
     const int PS = CinP + 8;              // LDS elements per pixel (an odd number of 16-byte slots)
     const int CV = CinP / 8;              // 16-byte vectors per pixel
-    const int nvec = DC_ROWS * DC_SPX * CV;
+    const int nvec = ROWS * DC_SPX * CV;
 
     // every input load of the strip in flight at once (out-of-range offsets read zero)
     const __amdgpu_buffer_rsrc_t rx = rsrc_bytes(a.x, a.x_bytes);
-    u32x4 sv[NCHW_IN ? 1 : DA_VQ];
+    u32x4 sv[NCHW_IN ? 1 : VQ];
     // channel-first: work item (channel pair cp, strip row r, segment sg) loads 8 pixels
     // of both planes of the pair; a segment lies wholly inside or outside the image row
-    u32x4 pv0[NCHW_IN ? DA_PQ : 1], pv1[NCHW_IN ? DA_PQ : 1];
-    const int nitems = CinP / 2 * DC_ROWS * DA_NSEG;
+    u32x4 pv0[NCHW_IN ? PQ : 1], pv1[NCHW_IN ? PQ : 1];
+    const int nitems = CinP / 2 * ROWS * DA_NSEG;
     if constexpr (NCHW_IN) {
 #pragma unroll
-        for (int q = 0; q < DA_PQ; ++q) {
+        for (int q = 0; q < PQ; ++q) {
             const int idx = tid + 256 * q;
-            const int sg = idx % DA_NSEG, r = (idx / DA_NSEG) % DC_ROWS, ci = 2 * (idx / (DA_NSEG * DC_ROWS));
+            const int sg = idx % DA_NSEG, r = (idx / DA_NSEG) % ROWS, ci = 2 * (idx / (DA_NSEG * ROWS));
             const int iy = j0 - 1 + r, ix = i0 - 8 + 8 * sg;
             const bool ok = idx < nitems && (unsigned)iy < (unsigned)H && (unsigned)ix < (unsigned)W && ci < Cin;
             const uint32_t off = ok ? ((((uint32_t)n * Cin + ci) * H + iy) * W + ix) * 2u : kOob;
@@ -328,7 +331,7 @@ __global__ __launch_bounds__(256) void deconv_mfma_all_kernel(DeconvArgs a) {
         }
     } else {
 #pragma unroll
-        for (int q = 0; q < DA_VQ; ++q) {
+        for (int q = 0; q < VQ; ++q) {
             const int idx = tid + 256 * q;
             const int pr = idx / CV, cv = idx - pr * CV;     // pixel of the strip, channel vector
             const int r = pr / DC_SPX, p = pr - r * DC_SPX;
@@ -354,10 +357,10 @@ __global__ __launch_bounds__(256) void deconv_mfma_all_kernel(DeconvArgs a) {
         // pixel k of segment sg is strip pixel p = 8 sg + k - 7; the pair's two values go
         // to LDS as one 4-byte word (ci even, PS even)
 #pragma unroll
-        for (int q = 0; q < DA_PQ; ++q) {
+        for (int q = 0; q < PQ; ++q) {
             const int idx = tid + 256 * q;
             if (idx >= nitems) continue;
-            const int sg = idx % DA_NSEG, r = (idx / DA_NSEG) % DC_ROWS, ci = 2 * (idx / (DA_NSEG * DC_ROWS));
+            const int sg = idx % DA_NSEG, r = (idx / DA_NSEG) % ROWS, ci = 2 * (idx / (DA_NSEG * ROWS));
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 const int p = 8 * sg + k - 7;
@@ -369,18 +372,18 @@ __global__ __launch_bounds__(256) void deconv_mfma_all_kernel(DeconvArgs a) {
         }
     } else {
 #pragma unroll
-        for (int q = 0; q < DA_VQ; ++q) {
+        for (int q = 0; q < VQ; ++q) {
             const int idx = tid + 256 * q;
             const int pr = idx / CV, cv = idx - pr * CV;
-            const int at = idx < nvec ? pr * PS + cv * 8 : DC_ROWS * DC_SPX * DA_PSMAX + tid * 8;
+            const int at = idx < nvec ? pr * PS + cv * 8 : ROWS * DC_SPX * DA_PSMAX + tid * 8;
             *reinterpret_cast<u32x4 *>(&sx[at]) = sv[q];
         }
     }
     __syncthreads();
 
-    f32x16 acc[DC_MR];
+    f32x16 acc[MR];
 #pragma unroll
-    for (int m = 0; m < DC_MR; ++m)
+    for (int m = 0; m < MR; ++m)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[m][i] = 0.0f;
     for (int c = 0; c < nchp; ++c) {
@@ -395,7 +398,7 @@ __global__ __launch_bounds__(256) void deconv_mfma_all_kernel(DeconvArgs a) {
 #pragma unroll
             for (int ks = 0; ks < DC_KS; ++ks)
 #pragma unroll
-                for (int m = 0; m < DC_MR; ++m) {
+                for (int m = 0; m < MR; ++m) {
                     vec av;
                     __builtin_memcpy(&av, &sx[((m + py + ty) * DC_SPX + col + px + tx) * PS + c0 + kq + ks * 16], 16);
                     acc[m] = Mfma32<T>::run(av, bcur[tp * DC_KS + ks], acc[m]);
@@ -409,11 +412,11 @@ __global__ __launch_bounds__(256) void deconv_mfma_all_kernel(DeconvArgs a) {
     auto epi = [&](auto actc) {
         constexpr int ACT = decltype(actc)::value;
 #pragma unroll
-        for (int m = 0; m < DC_MR; ++m)
+        for (int m = 0; m < MR; ++m)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int p = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-                so[col * DC_OCS + (2 * m + py) * DC_OLD + 2 * p + px] = activate_c<ACT>(acc[m][i] + bv, av);
+                so[col * OCS + (2 * m + py) * DC_OLD + 2 * p + px] = activate_c<ACT>(acc[m][i] + bv, av);
             }
     };
     switch (a.act) {
@@ -428,19 +431,19 @@ __global__ __launch_bounds__(256) void deconv_mfma_all_kernel(DeconvArgs a) {
     const int oc0 = 2 * i0, or0 = 2 * j0;
     if constexpr (NCHW_OUT) {
 #pragma unroll 4
-        for (int it = 0; it < 16 * DC_MR; ++it) {
+        for (int it = 0; it < 16 * MR; ++it) {
             const int e = tid + 256 * it;
-            const int oc = e & 63, lr = (e >> 6) & (2 * DC_MR - 1), cl = e / (128 * DC_MR);
+            const int oc = e & 63, lr = (e >> 6) & (2 * MR - 1), cl = e / (128 * MR);
             if (co0 + cl < Cout && oc0 + oc < OW && or0 + lr < OH)
-                y[(((size_t)n * Cout + co0 + cl) * OH + or0 + lr) * OW + oc0 + oc] = out_cast<TO>(so[cl * DC_OCS + lr * DC_OLD + oc]);
+                y[(((size_t)n * Cout + co0 + cl) * OH + or0 + lr) * OW + oc0 + oc] = out_cast<TO>(so[cl * OCS + lr * DC_OLD + oc]);
         }
     } else {
 #pragma unroll 4
-        for (int it = 0; it < 16 * DC_MR; ++it) {
+        for (int it = 0; it < 16 * MR; ++it) {
             const int e = tid + 256 * it;
             const int cl = e & 31, oc = (e >> 5) & 63, lr = e >> 11;
             if (co0 + cl < Cout && oc0 + oc < OW && or0 + lr < OH)
-                y[(((size_t)n * OH + or0 + lr) * OW + oc0 + oc) * Cout + co0 + cl] = out_cast<TO>(so[cl * DC_OCS + lr * DC_OLD + oc]);
+                y[(((size_t)n * OH + or0 + lr) * OW + oc0 + oc) * Cout + co0 + cl] = out_cast<TO>(so[cl * OCS + lr * DC_OLD + oc]);
         }
     }
 }
@@ -536,12 +539,21 @@ hipError_t launch_deconv_mfma(const DeconvArgs &a, int dtype, bool out_f32, bool
     }
 }
 
+template <typename T, typename TO, int MR>
+static hipError_t mfma_all_mr(const DeconvArgs &a, bool nchw_in, hipStream_t st) {
+    const long long tiles = (long long)a.N * ((a.H + MR - 1) / MR) * ((a.W + DC_TW - 1) / DC_TW);
+    dim3 grid((unsigned)tiles, (unsigned)(a.CoP / 32));
+    if (nchw_in) return launch_kernel(deconv_mfma_all_kernel<T, TO, true, true, MR>, grid, dim3(256), 0, st, a);
+    return launch_kernel(deconv_mfma_all_kernel<T, TO, true, false, MR>, grid, dim3(256), 0, st, a);
+}
+
+// One-row tiles when two-row tiles would leave CUs idle (the IFNet deconv: 136 two-row
+// tiles for 256 CUs); those workgroups fit two to a CU (smaller strip and epilogue tile).
 template <typename T, typename TO>
 static hipError_t mfma_all_t(const DeconvArgs &a, bool nchw_in, hipStream_t st) {
-    const long long tiles = (long long)a.N * ((a.H + DC_MR - 1) / DC_MR) * ((a.W + DC_TW - 1) / DC_TW);
-    dim3 grid((unsigned)tiles, (unsigned)(a.CoP / 32));
-    if (nchw_in) return launch_kernel(deconv_mfma_all_kernel<T, TO, true, true>, grid, dim3(256), 0, st, a);
-    return launch_kernel(deconv_mfma_all_kernel<T, TO, true, false>, grid, dim3(256), 0, st, a);
+    const long long tiles2 = (long long)a.N * ((a.H + 1) / 2) * ((a.W + DC_TW - 1) / DC_TW) * (a.CoP / 32);
+    if (tiles2 < 256) return mfma_all_mr<T, TO, 1>(a, nchw_in, st);
+    return mfma_all_mr<T, TO, 2>(a, nchw_in, st);
 }
 
 hipError_t launch_deconv_mfma_all(const DeconvArgs &a, int dtype, bool out_f32, bool nchw_out, bool nchw_in,

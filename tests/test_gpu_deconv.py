@@ -49,6 +49,9 @@ CASES = [
     (1, 7, 16, 200, 5, "prelu", "nchw", "f16", "f32", "mfma"),
     (3, 4, 64, 8, 16, "silu", "nchw", "f16", "f16", "mfma"),
     (1, 3, 8, 256, 40, "none", "nchw", "bf16", "f32", "mfma"),
+    # enough tiles for the two-row whole-strip tiles (the small cases above run one-row tiles)
+    (2, 41, 256, 64, 24, "relu", "nchw", "f16", "f16", "mfma"),
+    (1, 33, 200, 40, 40, "prelu", "nchw", "bf16", "f32", "mfma"),
     (1, 6, 9, 12, 7, "relu", "nhwc", "bf16", "bf16", "direct"),      # Cin % 8 != 0
     (1, 6, 9, 16, 7, "prelu", "nhwc", "f32", "f32", "direct"),
     (2, 5, 6, 10, 3, "silu", "nchw", "f32", "f32", "direct"),
