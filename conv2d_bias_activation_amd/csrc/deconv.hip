@@ -11,8 +11,9 @@
 // each class is a GEMM with K = 4*Cin over 64-channel chunks. The weights are first
 // repacked (once per call, into the library scratch) in the order in which the kernel's
 // lanes take them as MFMA B operands, so that each wave-wide weight load reads one
-// contiguous kilobyte; a workgroup stages three input rows of a 34-pixel strip once
-// and its four waves (one per class) read shifted views of it.
+// contiguous kilobyte; a workgroup stages the input rows its tile's taps reach (the
+// tile's one or two rows and one above and below) over a 34-pixel strip once, and its
+// four waves (one per class) read shifted views of it.
 #include <type_traits>
 
 #include "common.hpp"
