@@ -133,6 +133,7 @@ int check_conv(const void *x, const void *w, const float *alpha, const void *res
     a->res_before_act = (act & CONV2D_RES_BEFORE_ACT) ? 1 : 0;
     a->w_ohwi = (act & CONV2D_WEIGHTS_OHWI) ? 1 : 0;
     a->vec_out = aligned16(y) && (!residual || aligned16(residual));
+    a->y2 = nullptr;  // set per launch for chained channel-first layers
     return CONV2D_OK;
 }
 
@@ -145,6 +146,11 @@ struct Plan {
     HaloPlan halo;
     bool tuned;  // chosen by a conv2d_tune measurement rather than the built-in heuristics
     bool w_ohwi; // channel-first layer with channel-last weights: only the input is copied
+    // chained channel-first layers of a stack (FAM_NCHW_VIA_NHWC, set by link_chains)
+    bool chain_in;   // the input's channel-last copy is already in the scratch at x_at
+    size_t x_at;
+    bool chain_out;  // also write the output channel-last into the scratch at y2_at
+    size_t y2_at;
 };
 
 // Library scratch, one buffer per device, allocated on the first call that needs it
@@ -481,10 +487,10 @@ int describe(const Plan &p, int layout, int dtype, char *buf, int cap) {
         snprintf(tmp, sizeof tmp, "halo3x3_nhwc %s th%d co%d w%d", dtype_name(dtype), p.halo.th, 32 * p.halo.fn,
                  p.halo.waves);
     } else if (p.family == FAM_NHWC || p.family == FAM_NCHW_VIA_NHWC) {
-        snprintf(tmp, sizeof tmp, "%sigemm_nhwc_pipe%s %s %s splitk=%d",
-                 p.family == FAM_NCHW_VIA_NHWC ? (p.w_ohwi ? "x_to_nhwc+" : "to_nhwc+") : "",
+        snprintf(tmp, sizeof tmp, "%sigemm_nhwc_pipe%s %s %s splitk=%d%s",
+                 p.family == FAM_NCHW_VIA_NHWC ? (p.chain_in ? "chained+" : p.w_ohwi ? "x_to_nhwc+" : "to_nhwc+") : "",
                  p.nh.tap_inner ? "_tapinner" : "",
-                 dtype_name(dtype), nhwc_tile_name(p.nh.tile), p.nh.splits);
+                 dtype_name(dtype), nhwc_tile_name(p.nh.tile), p.nh.splits, p.chain_out ? " +y_nhwc" : "");
     } else {
         snprintf(tmp, sizeof tmp, "igemm_%s%s %s %s", p.ig.nchw ? "nchw" : "nhwc",
                  p.ig.avec ? "_vec" : "_gather", dtype_name(dtype), tile_name(p.ig.tile));
@@ -545,15 +551,22 @@ int launch_conv(const ConvArgs &a, const Plan &p, int layout, int dtype, hipStre
         rc = get_scratch(&scratch);
         if (rc) return rc;
         const int eb = dtype_bytes(dtype);
-        char *xs = reinterpret_cast<char *>(scratch);
+        char *base = reinterpret_cast<char *>(scratch);
+        char *xs = base + (p.chain_in ? p.x_at : 0);
         char *ws = xs + round256((size_t)a.N * a.H * a.W * a.Cin * eb);
-        // weights given channel-last (converted once by the caller) need no copy
-        e = a.w_ohwi ? launch_nchw_to_nhwc(a.x, xs, a.N, a.Cin, a.H * a.W, dtype, st)
-                     : launch_to_channel_last(a.x, xs, a.N, a.Cin, a.H * a.W, a.w, ws, a.Cout, a.kh * a.kw, dtype, st);
+        // weights given channel-last (converted once by the caller) need no copy; a
+        // chained layer's input copy was written by the layer before it
+        if (p.chain_in)
+            e = hipSuccess;
+        else
+            e = a.w_ohwi ? launch_nchw_to_nhwc(a.x, xs, a.N, a.Cin, a.H * a.W, dtype, st)
+                         : launch_to_channel_last(a.x, xs, a.N, a.Cin, a.H * a.W, a.w, ws, a.Cout, a.kh * a.kw, dtype,
+                                                  st);
         if (e == hipSuccess) {
             ConvArgs b = a;
             b.x = xs;
             b.w = a.w_ohwi ? a.w : ws;
+            b.y2 = p.chain_out ? base + p.y2_at : nullptr;
             e = launch_igemm_nhwc(b, dtype, p.nh, nullptr, st);
         }
     } else {
@@ -868,6 +881,31 @@ int check_op(const conv2d_op &op, int layout, int dtype, OpPlan *o) {
     }
 }
 
+// Chained channel-first convs of a stack: when a conv's output is the next op's input
+// and both run on the channel-last kernel with channel-last weights (the IFNet block's
+// chain), the producer (without a residual) also writes its output channel-last into
+// one half of the scratch and the consumer reads that instead of copying its input;
+// the halves alternate along the chain, so a layer never writes the half it reads.
+void link_chains(std::vector<OpPlan> &plans) {
+    const size_t half = kScratchBytes / 2;
+    for (size_t i = 0; i + 1 < plans.size(); ++i) {
+        OpPlan &p = plans[i], &q = plans[i + 1];
+        if (p.kind != CONV2D_OP_CONV || q.kind != CONV2D_OP_CONV) continue;
+        if (p.plan.family != FAM_NCHW_VIA_NHWC || q.plan.family != FAM_NCHW_VIA_NHWC) continue;
+        if (!p.plan.w_ohwi || !q.plan.w_ohwi || p.a.res || p.dtype != q.dtype) continue;
+        if (q.a.x != p.a.y || q.a.N != p.a.N || q.a.H != p.a.OH || q.a.W != p.a.OW || q.a.Cin != p.a.Cout) continue;
+        const int eb = dtype_bytes(p.dtype);
+        const size_t in_bytes = round256((size_t)p.a.N * p.a.H * p.a.W * p.a.Cin * eb);
+        const size_t out_bytes = round256((size_t)p.a.M * p.a.Cout * eb);
+        const size_t at_in = p.plan.chain_in ? p.plan.x_at : 0;
+        if (in_bytes > half || out_bytes > half) continue;
+        p.plan.chain_out = true;
+        p.plan.y2_at = at_in == 0 ? half : 0;
+        q.plan.chain_in = true;
+        q.plan.x_at = p.plan.y2_at;
+    }
+}
+
 int check_stack(const conv2d_op *ops, int n, int layout, int dtype, std::vector<OpPlan> *plans, int *bad) {
     if (n < 0 || (n > 0 && !ops)) return set_error(CONV2D_EINVAL, "ops must hold n >= 0 entries");
     plans->resize((size_t)n);
@@ -878,6 +916,7 @@ int check_stack(const conv2d_op *ops, int n, int layout, int dtype, std::vector<
             return set_error(rc, "op %d: %s", i, g_err.c_str());
         }
     }
+    link_chains(*plans);
     return CONV2D_OK;
 }
 

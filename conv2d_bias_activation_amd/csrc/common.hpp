@@ -41,6 +41,7 @@ struct ConvArgs {
     int res_before_act;
     int w_ohwi;  // channel-first layer whose weights are given channel-last (OHWI)
     int vec_out;  // y and residual are 16-byte aligned
+    void *y2;     // channel-first output: also written channel-last here (no residual), or null
 };
 
 __device__ __forceinline__ float to_f32(float v) { return v; }

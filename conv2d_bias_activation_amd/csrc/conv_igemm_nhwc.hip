@@ -338,6 +338,15 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG, 8 / (WGM * WGN * KG)) void ige
     const uint32_t out_bytes = (uint32_t)((size_t)a.M * a.Cout * sizeof(T));
     if constexpr (NCHW_OUT) {
         wave_epilogue_nchw32<T, FM, FN, WLD>(acc, slice, a, m0 + wm * FM * 32, n0 + wn * WN, lane, out_bytes);
+        if (a.y2) {
+            // the same values again, channel-last, for the next channel-first conv of a
+            // stack (same epilogue arithmetic, so the copy equals y element for element)
+            ConvArgs b = a;
+            b.y = a.y2;
+            b.res = nullptr;
+            b.vec_out = 1;
+            wave_epilogue_nhwc32<T, FM, FN, WLD>(acc, slice, b, m0 + wm * FM * 32, n0 + wn * WN, lane, out_bytes);
+        }
     } else {
         float *part = SPLIT ? partials + (size_t)blockIdx.y * a.M * a.Cout : nullptr;
         wave_epilogue_nhwc32<T, FM, FN, WLD>(acc, slice, a, m0 + wm * FM * 32, n0 + wn * WN, lane, out_bytes,

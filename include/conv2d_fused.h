@@ -366,7 +366,12 @@ int conv2d_stack_check(const conv2d_op *ops, int n, int layout, int dtype, int *
 int conv2d_stack_plan(const conv2d_op *ops, int n, int layout, int dtype, int index, char *buf, int cap);
 
 /* Validates the whole stack, then enqueues its ops in order on `stream`. Same memory
- * and scratch rules as the single calls. */
+ * and scratch rules as the single calls. Consecutive channel-first 16-bit convs given
+ * channel-last weights (CONV2D_WEIGHTS_OHWI), where one conv's y is the next one's x
+ * with matching sizes and the first has no residual, are chained: the first also writes
+ * its output channel-last into one half of the scratch and the next reads its input
+ * from there instead of copying it (conv2d_stack_plan names show "+y_nhwc" and
+ * "chained+"). The results are bit-identical to running the ops one call at a time. */
 int conv2d_stack_run(const conv2d_op *ops, int n, int layout, int dtype, void *stream);
 
 /* Validates the stack and records it once into a HIP graph (stream capture on a

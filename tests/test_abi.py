@@ -360,3 +360,35 @@ def test_no_device_returns_ehip_not_a_crash():
     with pytest.raises(c2d.Conv2dError) as e:
         c2d.tune(1, 8, 8, 16, 16, 3, 3, 1, 1, "relu", reps=3)
     assert e.value.code == c2d.EHIP
+
+
+def test_channel_first_chain_links():
+    """Host only: consecutive channel-first convs with channel-last weights, each reading
+    the previous one's output, are linked (the producer also writes a channel-last copy
+    that the consumer reads); a producer with a residual, channel-first weights or a
+    consumer reading another buffer breaks the link."""
+    G = 1 << 32
+    f16 = c2d.DTYPE_F16
+    act = c2d._ACTS["prelu"] | c2d.WEIGHTS_OHWI
+    x, y0, y1, y2, w, al, b = G, 3 * G, 5 * G, 7 * G, 9 * G, 10 * G, 11 * G
+
+    def conv(src, dst, res=None, a=act):
+        return c2d.Op(c2d.OP_CONV, src, w, b, al, res, dst, 1, 68, 120, 240, 240, 3, 3, 1, 1, a)
+
+    def names(ops):
+        return [c2d.stack_plan(ops, i, layout="nchw", dtype=f16) for i in range(len(ops))]
+
+    n = names([conv(x, y0), conv(y0, y1), conv(y1, y2, res=x)])
+    assert n[0].startswith("x_to_nhwc+") and n[0].endswith(" +y_nhwc"), n
+    assert n[1].startswith("chained+") and n[1].endswith(" +y_nhwc"), n
+    assert n[2].startswith("chained+") and not n[2].endswith(" +y_nhwc"), n
+    # the producer adds a residual: its channel-last copy would differ from y
+    n = names([conv(x, y0, res=y2), conv(y0, y1)])
+    assert n[0].startswith("x_to_nhwc+") and not n[0].endswith(" +y_nhwc") and n[1].startswith("x_to_nhwc+"), n
+    # channel-first weights: no link
+    plain = c2d._ACTS["prelu"]
+    n = names([conv(x, y0, a=plain), conv(y0, y1, a=plain)])
+    assert all(k.startswith("to_nhwc+") and not k.endswith(" +y_nhwc") for k in n), n
+    # the next conv reads another buffer
+    n = names([conv(x, y0), conv(y1, y2)])
+    assert not n[0].endswith(" +y_nhwc") and n[1].startswith("x_to_nhwc+"), n

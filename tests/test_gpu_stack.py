@@ -22,10 +22,10 @@ def _layer(seed, cin, cout, k, stride, pad, act, layout, dtype):
     return spec.w.to(DEV), spec.bias.to(DEV), spec.alpha.to(DEV) if spec.alpha is not None else None
 
 
-def _ifnet_chain(layout="nchw", dtype="f16", c=240, h=17, w=30):
+def _ifnet_chain(layout="nchw", dtype="f16", c=240, h=17, w=30, ohwi=False):
     """The IFNet block: eight 3x3 convs with PReLU, the block input added to the last
     one's output; the input buffer is reused as a ping-pong buffer, so the block first
-    copies it aside."""
+    copies it aside. ohwi: the ops take the weights converted to channel-last once."""
     rng = np.random.default_rng(7)
     x = wl.to_storage(rng.standard_normal((1, c, h, w) if layout == "nchw" else (1, h, w, c)).astype(np.float32),
                       dtype).to(DEV)
@@ -34,15 +34,18 @@ def _ifnet_chain(layout="nchw", dtype="f16", c=240, h=17, w=30):
     a, b, snap, out = (torch.empty_like(x) for _ in range(4))
     bufs = [x, a, b]
     ops = [c2d.copy_op(x, snap)]
+    keep = []
     src = x
     for i, (wt, bs, al) in enumerate(layers):
         last = i == 7
         dst = out if last else bufs[(i + 1) % 3]
-        ops.append(c2d.conv_op(src, wt, dst, bs, al, residual=snap if last else None, stride=1, pad=1,
-                               act="prelu", layout=layout))
+        wo = c2d.weights_to_ohwi(wt) if ohwi else wt
+        keep.append(wo)
+        ops.append(c2d.conv_op(src, wo, dst, bs, al, residual=snap if last else None, stride=1, pad=1,
+                               act="prelu", layout=layout, weights_ohwi=ohwi))
         src = dst
     # the ops hold raw pointers: the buffers must outlive them
-    return x, x0, layers, ops, out, (a, b, snap)
+    return x, x0, layers, ops, out, (a, b, snap, keep)
 
 
 def _ifnet_oracle(x0, layers, layout, dtype):
@@ -80,6 +83,35 @@ def test_ifnet_block_graph_replays():
     try:
         for rep in range(3):
             # eager work between replays: restore the block input, poison the output
+            x.copy_(x0)
+            out.fill_(float("nan"))
+            torch.cuda.synchronize()
+            g.launch()
+            torch.cuda.synchronize()
+            assert bits_equal(out, want), f"replay {rep}"
+    finally:
+        g.close()
+
+
+def test_ifnet_chain_with_channel_last_weights():
+    """With channel-last weights the chained channel-first convs hand each other their
+    input's channel-last copy (written by the producing conv's epilogue into alternating
+    scratch halves) instead of copying it again: the same bits as one call per op, in a
+    stack run and in every replay of its graph."""
+    x, x0, layers, ops, out, _keep = _ifnet_chain(ohwi=True)
+    names = [c2d.stack_plan(ops, i, layout="nchw", dtype=c2d.DTYPE_F16) for i in range(1, 9)]
+    assert names[0].startswith("x_to_nhwc+") and names[0].endswith(" +y_nhwc"), names[0]
+    assert all(n.startswith("chained+") and n.endswith(" +y_nhwc") for n in names[1:7]), names
+    assert names[7].startswith("chained+") and not names[7].endswith(" +y_nhwc"), names[7]
+    want = _ifnet_calls(x0, layers, "nchw")
+    torch.cuda.synchronize()
+    c2d.stack_run(ops, layout="nchw", dtype=c2d.DTYPE_F16)
+    torch.cuda.synchronize()
+    assert bits_equal(out, want)
+    gate(to64(out), _ifnet_oracle(x0, layers, "nchw", "f16"), "f16", what="ifnet chain", elementwise=False)
+    g = c2d.StackGraph(ops, layout="nchw", dtype=c2d.DTYPE_F16)
+    try:
+        for rep in range(3):
             x.copy_(x0)
             out.fill_(float("nan"))
             torch.cuda.synchronize()
