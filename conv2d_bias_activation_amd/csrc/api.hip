@@ -4,6 +4,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 #include <map>
 #include <mutex>
@@ -1177,6 +1178,10 @@ int tune_run(int N, int H, int W, int Cin, int Cout, int kh, int kw, int stride,
     for (size_t i = 0; i < cands.size() && e == hipSuccess; ++i) {
         for (int w = 0; w < 2 && rc == CONV2D_OK; ++w) rc = launch_conv(a, cands[i], layout, dtype, st);
         if (rc) break;
+        // the GPU idles while the host queues the timed launches (about 30 us of host
+        // time each, more under a profiler), so host-side cost stays out of the timing
+        e = launch_idle(std::min(4096, 8 + reps * 12), st);
+        if (e != hipSuccess) break;
         e = hipEventRecord(e0, st);
         for (int r = 0; r < reps && rc == CONV2D_OK && e == hipSuccess; ++r) rc = launch_conv(a, cands[i], layout, dtype, st);
         if (rc || e != hipSuccess) break;

@@ -101,6 +101,9 @@ hipError_t launch_direct(const ConvArgs &a, int dtype, bool nchw, hipStream_t st
 // y = x, `bytes` bytes (a snapshot inside a stream of layers).
 hipError_t launch_copy(const void *x, void *y, size_t bytes, hipStream_t st);
 
+// One wave that idles for rounds x s_sleep 127 (about 3.4 us each at 2.4 GHz), 0..4096.
+hipError_t launch_idle(int rounds, hipStream_t st);
+
 // Pools (layout: CONV2D_LAYOUT_*). vec: C a multiple of the 16-byte vector and
 // both pointers aligned (channel-last only).
 hipError_t launch_maxpool(const void *x, void *y, int N, int H, int W, int C, bool nchw,

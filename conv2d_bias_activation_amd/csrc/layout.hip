@@ -196,6 +196,18 @@ __global__ __launch_bounds__(256) void copy1_kernel(const uint8_t *__restrict__ 
     for (size_t i = blockIdx.x * 256ull + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) y[i] = x[i];
 }
 
+// One wave that idles for `rounds` x s_sleep 127 (about 64 x 127 clocks each) and then
+// ends: queued ahead of a timed region so the host has enqueued the whole region
+// before the GPU reaches it. No memory access; the loop count is fixed.
+__global__ __launch_bounds__(64) void idle_kernel(int rounds) {
+    for (int i = 0; i < rounds; ++i) __builtin_amdgcn_s_sleep(127);
+}
+
+hipError_t launch_idle(int rounds, hipStream_t st) {
+    if (rounds < 0 || rounds > 4096) return hipErrorInvalidValue;
+    return launch_kernel(idle_kernel, dim3(1), dim3(64), 0, st, rounds);
+}
+
 hipError_t launch_copy(const void *x, void *y, size_t bytes, hipStream_t st) {
     if (bytes == 0) return hipSuccess;
     const bool v16 = (((uintptr_t)x | (uintptr_t)y | bytes) & 15) == 0;
