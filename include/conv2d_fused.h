@@ -401,7 +401,8 @@ int conv2d_stack_graph_destroy(conv2d_graph *g);
  * every tile shape and split-K depth (1-4) of the implicit-GEMM kernel and the tile
  * heights of the halo kernel (for channel-first 16-bit layers, which run on that
  * kernel after a layout copy, every tile shape): each variant runs twice, then `reps` times between two
- * events on a private stream. It synchronises that stream, frees its buffers and
+ * events on a private stream, queued behind a short idle kernel so that the host's launch cost does
+ * not enter the timing. It synchronises that stream, frees its buffers and
  * records the fastest variant in a process-wide table keyed by (device arch and
  * compute units, N, H, W, Cin, Cout, kh, kw, stride, pad, layout, dtype, residual or
  * not). From then on conv2d_fused, the fused conv + max pool and the stacks (and
