@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import workloads as wl
-from parity import gate, to64
+from parity import bits_equal, gate, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -137,3 +137,21 @@ def test_prepacked_weights_give_identical_results(layout, dt, odt, n, h, w, cin,
     y2 = c2d.conv_transpose4x4s2_prepacked(xd, packed, bd, act="relu", layout=layout, out_dtype=TD[odt])
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
+
+
+def test_channel_first_input_not_16_byte_aligned():
+    """A channel-first input whose width allows reading the planes directly but whose
+    pointer is not 16-byte aligned takes the channel-last copy instead; both give the
+    oracle's result."""
+    n, h, w, cin, cout = 1, 6, 16, 40, 24
+    x, wt, b, al = wl.random_deconv_case(77, n=n, h=h, w=w, cin=cin, cout=cout, act="relu", layout="nchw",
+                                         dtype="f16")
+    big = torch.empty(x.numel() + 1, dtype=x.dtype, device=DEV)
+    xs = big[1:].view(x.shape)  # 2 bytes past a 16-byte boundary
+    xs.copy_(x.to(DEV))
+    assert xs.data_ptr() % 16 != 0
+    y = c2d.conv_transpose4x4s2(xs, wt.to(DEV), b.to(DEV), act="relu", layout="nchw")
+    ya = _run(x, wt, b, al, "relu", "nchw", "f16")
+    torch.cuda.synchronize()
+    assert bits_equal(y, ya)
+    gate(to64(y), _ref(x, wt, b, al, "relu", "nchw"), "f16", what="unaligned channel-first input")
