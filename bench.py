@@ -66,9 +66,6 @@ def parse():
     p.add_argument("--oihw", action="store_true",
                    help="give channel-first layers their weights in OIHW order (converted per call) instead of "
                         "converting them to OHWI once during set-up")
-    p.add_argument("--fuse-shortcut", action="store_true",
-                   help="run each average pool + 1x1 shortcut conv as one conv2d_avgpool2x2_conv1x1 call (measured "
-                        "slower than the two calls on MI355X: the per-call weight expansion and the 4x deeper GEMM)")
     p.add_argument("--workload", choices=list(WORKLOADS), default="resnet18d",
                    help="the backbone (default; the headline) or one of the other layer configs")
     p.add_argument("--no-tune", action="store_true",
@@ -86,7 +83,7 @@ def parse():
 class Net:
     """The backbone's layers with preallocated device buffers and prebuilt C-ABI arguments."""
 
-    def __init__(self, work, dev, fuse_pool=True, fuse_shortcut=False, weights_ohwi=True):
+    def __init__(self, work, dev, fuse_pool=True, weights_ohwi=True, workspace=True):
         import torch
 
         import conv2d_bias_activation_amd as c2d
@@ -169,35 +166,6 @@ class Net:
                 self.layers.append(dict(name=spec.name, fn=self.lib.conv2d_fused, args=args,
                                         flops=flops, bytes=nbytes, plan=plan, keep=keep, op=op))
             else:
-                nxt = work.layers[i + 1] if i + 1 < len(work.layers) else None
-                if (fuse_shortcut and spec.kind == "avg" and nxt is not None and hasattr(nxt, "cin") and nxt.k == 1
-                        and nxt.stride == 1 and nxt.pad == 0 and nxt.src == spec.out and not nxt.res
-                        and readers.get(spec.out) == 1):
-                    # the ResNet-D shortcut in one call: average pool + 1x1 conv, the pooled map
-                    # never written
-                    oh, ow = h // 2, w // 2
-                    out = torch.empty((n, nxt.cout, oh, ow) if nchw else (n, oh, ow, nxt.cout), dtype=src.dtype,
-                                      device=dev)
-                    wdev, bdev = nxt.w.to(dev), nxt.bias.to(dev)
-                    adev = nxt.alpha.to(dev) if nxt.alpha is not None else None
-                    act = {"none": 0, "relu": 1, "silu": 2, "prelu": 3}[nxt.act]
-                    args = [ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(wdev.data_ptr()),
-                            ctypes.c_void_p(bdev.data_ptr()),
-                            ctypes.c_void_p(adev.data_ptr()) if adev is not None else None,
-                            ctypes.c_void_p(out.data_ptr()), n, h, w, c, nxt.cout, act, lay, dt]
-                    op = c2d.Op(c2d.OP_AVGPOOL_CONV1X1, src.data_ptr(), wdev.data_ptr(), bdev.data_ptr(),
-                                adev.data_ptr() if adev is not None else None, None, out.data_ptr(), n, h, w, c,
-                                nxt.cout, 1, 1, 1, 0, act)
-                    flops = 2 * n * oh * ow * nxt.cout * c  # the 1x1 conv's own flops
-                    nbytes = esz * (src.numel() + nxt.w.numel() + out.numel()) + 4 * nxt.cout * (
-                        2 if adev is not None else 1)
-                    plan = c2d.stack_plan([op], 0, layout=["nhwc", "nchw"][lay], dtype=dt)
-                    self.layers.append(dict(name=spec.name + "+" + nxt.name, fn=self.lib.conv2d_avgpool2x2_conv1x1,
-                                            args=args, flops=flops, bytes=nbytes, plan=plan,
-                                            keep=(wdev, bdev, adev), op=op))
-                    self.t[nxt.out] = out
-                    skip.add(i + 1)
-                    continue
                 if spec.kind == "max":
                     oh, ow, fn = (h - 1) // 2 + 1, (w - 1) // 2 + 1, self.lib.maxpool3x3s2
                     plan = "maxpool3x3s2"
@@ -216,6 +184,23 @@ class Net:
         self.flops = sum(L["flops"] for L in self.layers)
         self.layout, self.dtype = lay, dt
         self.out_name = work.layers[-1].out
+        # the caller-owned workspace of every call (plans above assume the default size;
+        # the stack's own need is below it for these workloads)
+        self.ws = None
+        if workspace:
+            need = c2d.stack_workspace_size([L["op"] for L in self.layers], layout=["nhwc", "nchw"][lay], dtype=dt)
+            self.ws = torch.empty(max(need, c2d.DEFAULT_WORKSPACE_BYTES), dtype=torch.uint8, device=dev)
+        # kernel variants of each layer run on its own with this workspace
+        wsb = self.ws.numel() if self.ws is not None else 0
+        for L in self.layers:
+            o = L["op"]
+            if o.kind in (c2d.OP_CONV, c2d.OP_CONV_MAXPOOL):
+                fn = c2d.plan if o.kind == c2d.OP_CONV else c2d.plan_maxpool
+                L["plan"] = fn(o.N, o.H, o.W, o.Cin, o.Cout, o.kh, o.kw, o.stride, o.pad, o.act, lay, dt,
+                               workspace_bytes=wsb)
+
+    def use_workspace(self):
+        self.c2d.set_workspace(self.ws)
 
     def run_layer(self, L, stream_handle):
         rc = L["fn"](*L["args"], stream_handle)
@@ -223,6 +208,7 @@ class Net:
             raise RuntimeError(f"{L['name']}: {self.c2d.last_error()}")
 
     def step(self, stream):
+        self.use_workspace()
         h = ctypes.c_void_p(stream.cuda_stream)
         for L in self.layers:
             self.run_layer(L, h)
@@ -241,7 +227,7 @@ def time_steps(torch, net, steps, warmup, mode):
         net.step(stream)
         torch.cuda.synchronize()
         graph = net.c2d.StackGraph([L["op"] for L in net.layers], layout=["nhwc", "nchw"][net.layout],
-                                   dtype=net.dtype)
+                                   dtype=net.dtype, workspace=net.ws if net.ws is not None else False)
         run = lambda: graph.launch(stream)
     elif mode == "graph":
         side = torch.cuda.Stream()
@@ -278,6 +264,7 @@ def time_layers(torch, net, reps):
     the GPU busy until the host has queued them, so no launch or event gap is counted."""
     stream = torch.cuda.current_stream()
     h = ctypes.c_void_p(stream.cuda_stream)
+    net.use_workspace()
     out = []
     for L in net.layers:
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -436,7 +423,7 @@ def write_traffic(src, copy_mib, plan):
     print(json.dumps(rec))
 
 
-def tune_workload(work, fuse_shortcut=False):
+def tune_workload(work):
     """Set-up, outside the timed region: time the kernel variants of each distinct conv
     shape of the workload on this GPU (conv2d_tune) so the stack picks the fastest.
     Returns the number of shapes tuned."""
@@ -445,7 +432,6 @@ def tune_workload(work, fuse_shortcut=False):
     dt = {"f32": c2d.DTYPE_F32, "bf16": c2d.DTYPE_BF16, "f16": c2d.DTYPE_F16}[work.dtype]
     nchw = work.layout == "nchw"
     shapes = {"x": tuple(work.x.shape)}
-    pooled_from = {}  # average-pool output -> the pool's input size (n, h, w, c)
     seen = set()
     for spec in work.layers:
         src = shapes[spec.src]
@@ -463,18 +449,7 @@ def tune_workload(work, fuse_shortcut=False):
         else:
             oh, ow = ((h - 1) // 2 + 1, (w - 1) // 2 + 1) if spec.kind == "max" else (h // 2, w // 2)
             oshape = (n, c, oh, ow) if nchw else (n, oh, ow, c)
-            if spec.kind == "avg":
-                pooled_from[spec.out] = (n, h, w, c)
         shapes[spec.out] = oshape
-    # with fused shortcuts an average pool feeding a 1x1 conv runs as one 2x2 stride-2
-    # conv: tune that shape too
-    for spec in (work.layers if fuse_shortcut else []):
-        if hasattr(spec, "cin") and spec.k == 1 and spec.stride == 1 and spec.pad == 0 and spec.src in pooled_from:
-            n, h, w, c = pooled_from[spec.src]
-            key = (n, h, w, c, spec.cout, 2, 2, 0, spec.act, False, False)
-            if key not in seen:
-                seen.add(key)
-                c2d.tune(n, h, w, c, spec.cout, 2, 2, 2, 0, spec.act, layout=work.layout, dtype=dt, reps=10)
     return len(seen)
 
 
@@ -601,12 +576,12 @@ def main():
     if args.tune_in:
         tuned = c2d.tune_load(args.tune_in)
     elif not args.no_tune:
-        tuned = tune_workload(work, fuse_shortcut=args.fuse_shortcut)
+        tuned = tune_workload(work)
         if args.tune_out:
             c2d.tune_save(args.tune_out)
-    net = Net(work, dev, fuse_pool=not args.no_fuse_pool, fuse_shortcut=args.fuse_shortcut,
-              weights_ohwi=not args.oihw)
+    net = Net(work, dev, fuse_pool=not args.no_fuse_pool, weights_ohwi=not args.oihw)
     if args.launch_plan:
+        net.use_workspace()
         h = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
         chosen = [L for L in net.layers if L["plan"].replace(" tuned", "") == args.launch_plan.replace(" tuned", "")]
         if not chosen:

@@ -4,8 +4,17 @@ A thin ctypes binding over the C ABI of ``libconv2d_fused.so``
 (include/conv2d_fused.h). PyTorch supplies device memory and the current HIP
 stream; every step of the computation runs in the library's HIP kernels. The
 binding only checks tensor shapes, dtypes and devices, derives the sizes the C
-ABI takes, allocates outputs when none are given and raises on an error code.
-There is no fallback: if the library is not built, importing the ops raises.
+ABI takes, allocates outputs and workspaces when none are given and raises on an
+error code. There is no fallback: if the library is not built, importing the ops
+raises.
+
+Workspace: the library allocates no device memory; kernel variants that need
+scratch use a caller-owned workspace registered per thread and device. Every call
+here takes ``workspace=``: ``None`` (default) uses a buffer this module keeps per
+(device, stream), allocated with torch.empty and grown to what the call's preferred
+variant needs (so calls on different streams never share one); ``False`` runs the
+call without a workspace (variants that need none); a uint8 CUDA tensor is used as
+given.
 """
 from __future__ import annotations
 
@@ -18,9 +27,9 @@ __all__ = ["conv2d_fused", "conv2d_fused_maxpool3x3s2", "maxpool3x3s2", "avgpool
            "check_args", "plan", "plan_maxpool", "Op", "conv_op", "pool_op", "copy_op", "stack_check",
            "stack_plan", "stack_run", "StackGraph", "conv_transpose4x4s2", "plan_deconv",
            "upsample_nearest2x", "concat_channels", "upsample2x_concat", "deconv_op", "upsample_op",
-           "concat_op", "tune", "tune_save", "tune_load", "tune_clear", "avgpool2x2_conv1x1",
-           "pool_conv_op", "deconv_pack", "conv_transpose4x4s2_prepacked", "weights_to_ohwi", "WEIGHTS_OHWI",
+           "concat_op", "tune", "tune_save", "tune_load", "tune_clear", "deconv_pack", "conv_transpose4x4s2_prepacked", "weights_to_ohwi", "WEIGHTS_OHWI",
            "last_error", "library_path", "Conv2dError", "ACT_NONE", "ACT_RELU", "ACT_SILU",
+           "workspace_size", "stack_workspace_size", "set_workspace", "DEFAULT_WORKSPACE_BYTES",
            "ACT_PRELU", "RES_BEFORE_ACT", "LAYOUT_NHWC", "LAYOUT_NCHW", "DTYPE_F32",
            "DTYPE_BF16", "DTYPE_F16"]
 
@@ -42,7 +51,7 @@ _LIB_PATH = os.path.join(_HERE, "libconv2d_fused.so")
 # Every exported symbol of the C ABI, with (restype, argtypes).
 _vp, _fp, _i, _cp = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_char_p
 OP_CONV, OP_CONV_MAXPOOL, OP_MAXPOOL, OP_AVGPOOL, OP_COPY = 0, 1, 2, 3, 4
-OP_DECONV, OP_UPSAMPLE, OP_CONCAT, OP_UPSAMPLE_CONCAT, OP_AVGPOOL_CONV1X1 = 5, 6, 7, 8, 9
+OP_DECONV, OP_UPSAMPLE, OP_CONCAT, OP_UPSAMPLE_CONCAT = 5, 6, 7, 8
 
 
 class Op(ctypes.Structure):
@@ -79,11 +88,13 @@ SIGNATURES = {
     "conv2d_tune_save": (_i, [_cp]),
     "conv2d_tune_load": (_i, [_cp]),
     "conv2d_tune_clear": (_i, []),
-    "conv2d_avgpool2x2_conv1x1": (_i, [_vp, _vp, _fp, _fp, _vp] + [_i] * 8 + [_vp]),
     "conv_transpose4x4s2_packed_bytes": (_i, [_i, _i, _i, ctypes.POINTER(ctypes.c_size_t)]),
     "conv_transpose4x4s2_pack": (_i, [_vp, _vp, _i, _i, _i, _vp]),
     "conv_transpose4x4s2_prepacked": (_i, [_vp, _vp, _fp, _fp, _vp] + [_i] * 9 + [_vp]),
     "conv2d_weights_to_ohwi": (_i, [_vp, _vp] + [_i] * 5 + [_vp]),
+    "conv2d_set_workspace": (_i, [_vp, ctypes.c_size_t]),
+    "conv2d_workspace_size": (_i, [_i] * 12 + [ctypes.POINTER(ctypes.c_size_t)]),
+    "conv2d_stack_workspace_size": (_i, [_op_p, _i, _i, _i, ctypes.POINTER(ctypes.c_size_t)]),
     "conv2d_last_error": (_cp, []),
     "conv2d_abi_version": (_i, []),
 }
@@ -146,6 +157,62 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+DEFAULT_WORKSPACE_BYTES = 64 << 20
+_ws_cache = {}  # (device index, stream handle) -> uint8 tensor
+
+
+def set_workspace(ws, device=None):
+    """Register ``ws`` (a uint8 CUDA tensor, or None for none) as the workspace of this
+    thread's later calls on its device (conv2d_set_workspace). Returns nothing."""
+    lib = _load()
+    if ws is None:
+        _check(lib.conv2d_set_workspace(None, 0))
+        return
+    if ws.dtype != torch.uint8 or not ws.is_cuda or not ws.is_contiguous():
+        raise ValueError("a workspace is a contiguous uint8 CUDA tensor")
+    if ws.data_ptr() % 256:
+        raise ValueError("a workspace must be 256-byte aligned")
+    with torch.cuda.device(ws.device):
+        _check(lib.conv2d_set_workspace(ctypes.c_void_p(ws.data_ptr()), ws.numel()))
+
+
+def _stream_of(device, stream):
+    return torch.cuda.current_stream(device) if stream is None else stream
+
+
+def _default_workspace(device, stream, need):
+    key = (device.index if device.index is not None else torch.cuda.current_device(), stream.cuda_stream)
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < need:
+        # torch's allocator is stream-ordered: the old buffer is reused only by work
+        # queued after the calls that still use it on this stream
+        ws = torch.empty(max(need, DEFAULT_WORKSPACE_BYTES), dtype=torch.uint8, device=device)
+        _ws_cache[key] = ws
+    return ws
+
+
+def _use_workspace(device, stream, workspace, need=0):
+    """Registers the workspace for a call on `stream` (see the module doc); returns it."""
+    lib = _load()
+    with torch.cuda.device(device):
+        if workspace is False:
+            _check(lib.conv2d_set_workspace(None, 0))
+            return None
+        ws = _default_workspace(device, stream, need) if workspace is None else workspace
+        if ws.dtype != torch.uint8 or ws.device != device or not ws.is_contiguous() or ws.data_ptr() % 256:
+            raise ValueError("a workspace is a contiguous, 256-byte aligned uint8 tensor on the call's device")
+        _check(lib.conv2d_set_workspace(ctypes.c_void_p(ws.data_ptr()), ws.numel()))
+        return ws
+
+
+def workspace_size(N, H, W, Cin, Cout, kh, kw, stride, pad, act, layout, dtype) -> int:
+    """Bytes of workspace conv2d_fused's preferred variant for a shape writes (host only)."""
+    n = ctypes.c_size_t(0)
+    _check(_load().conv2d_workspace_size(N, H, W, Cin, Cout, kh, kw, stride, pad, act, layout, dtype,
+                                         ctypes.byref(n)))
+    return n.value
+
+
 def _dims(x, w, layout, weights_ohwi=False):
     if x.dim() != 4 or w.dim() != 4:
         raise ValueError("x and w must be 4-D")
@@ -205,7 +272,8 @@ def _out(out, shape, x):
 
 
 def conv2d_fused(x, w, bias=None, alpha=None, residual=None, *, stride=1, pad=0, act="none",
-                 res_before_act=False, layout="nhwc", weights_ohwi=False, out=None, stream=None):
+                 res_before_act=False, layout="nhwc", weights_ohwi=False, out=None, stream=None,
+                 workspace=None):
     """y = epilogue(conv(x, w)) on the GPU; see include/conv2d_fused.h.
 
     x, w, residual, out: CUDA tensors of one storage dtype (float32, bfloat16 or
@@ -221,25 +289,33 @@ def conv2d_fused(x, w, bias=None, alpha=None, residual=None, *, stride=1, pad=0,
     if residual is not None and tuple(residual.shape) != yshape:
         raise ValueError(f"residual must have shape {yshape}")
     out = _out(out, yshape, x)
-    rc = lib.conv2d_fused(_ptr(x), _ptr(w), _ptr(bias), _ptr(alpha), _ptr(residual), _ptr(out),
-                          N, H, W, Cin, Cout, kh, kw, stride, pad,
-                          _act_code(act, res_before_act) | (WEIGHTS_OHWI if weights_ohwi else 0), lay, dt,
-                          _stream_handle(stream))
+    code = _act_code(act, res_before_act) | (WEIGHTS_OHWI if weights_ohwi else 0)
+    st = _stream_of(x.device, stream)
+    need = 0 if workspace is not None else workspace_size(N, H, W, Cin, Cout, kh, kw, stride, pad, code, lay, dt)
+    with torch.cuda.device(x.device):
+        _use_workspace(x.device, st, workspace, need)
+        rc = lib.conv2d_fused(_ptr(x), _ptr(w), _ptr(bias), _ptr(alpha), _ptr(residual), _ptr(out),
+                              N, H, W, Cin, Cout, kh, kw, stride, pad, code, lay, dt, _stream_handle(st))
     _check(rc)
     return out
 
 
 def conv2d_fused_maxpool3x3s2(x, w, bias=None, alpha=None, *, stride=1, pad=0, act="none",
-                              layout="nhwc", out=None, stream=None):
+                              layout="nhwc", out=None, stream=None, workspace=None):
     """maxpool3x3s2(conv2d_fused(x, w, bias, alpha)) with only the pooled map written;
     see include/conv2d_fused.h. Returns the pooled y."""
     lib = _load()
     lay, dt, (N, H, W, Cin, Cout, kh, kw), (OH, OW) = _conv_args(x, w, bias, alpha, stride, pad, layout)
     PH, PW = (OH - 1) // 2 + 1, (OW - 1) // 2 + 1
     out = _out(out, (N, PH, PW, Cout) if layout == "nhwc" else (N, Cout, PH, PW), x)
-    rc = lib.conv2d_fused_maxpool3x3s2(_ptr(x), _ptr(w), _ptr(bias), _ptr(alpha), _ptr(out),
-                                       N, H, W, Cin, Cout, kh, kw, stride, pad,
-                                       _act_code(act, False), lay, dt, _stream_handle(stream))
+    st = _stream_of(x.device, stream)
+    # the two-kernel form holds the unpooled conv output in the workspace
+    need = -(-N * OH * OW * Cout * x.element_size() // 256) * 256
+    with torch.cuda.device(x.device):
+        _use_workspace(x.device, st, workspace, need)
+        rc = lib.conv2d_fused_maxpool3x3s2(_ptr(x), _ptr(w), _ptr(bias), _ptr(alpha), _ptr(out),
+                                           N, H, W, Cin, Cout, kh, kw, stride, pad,
+                                           _act_code(act, False), lay, dt, _stream_handle(st))
     _check(rc)
     return out
 
@@ -289,19 +365,43 @@ def check_args(x_ptr, w_ptr, bias_ptr, alpha_ptr, res_ptr, y_ptr, N, H, W, Cin, 
                                      Cin, Cout, kh, kw, stride, pad, act, layout, dtype)
 
 
-def plan(N, H, W, Cin, Cout, kh, kw, stride, pad, act, layout, dtype) -> str:
-    """Name of the kernel variant conv2d_fused picks for a shape (host only)."""
+_WS_STANDIN = 0x4000000000  # 256-byte aligned; host-only planning never dereferences it
+
+
+class _planning_workspace:
+    """Registers a stand-in workspace of `nbytes` (0: none) for host-only planning calls,
+    and no workspace again afterwards."""
+
+    def __init__(self, nbytes):
+        self.nbytes = int(nbytes)
+
+    def __enter__(self):
+        lib = _load()
+        _check(lib.conv2d_set_workspace(ctypes.c_void_p(_WS_STANDIN) if self.nbytes else None, self.nbytes))
+        return self
+
+    def __exit__(self, *exc):
+        _load().conv2d_set_workspace(None, 0)
+        return False
+
+
+def plan(N, H, W, Cin, Cout, kh, kw, stride, pad, act, layout, dtype, workspace_bytes=DEFAULT_WORKSPACE_BYTES) -> str:
+    """Name of the kernel variant conv2d_fused picks for a shape with a workspace of
+    ``workspace_bytes`` (0: none; host only)."""
     buf = ctypes.create_string_buffer(256)
-    n = _load().conv2d_plan(N, H, W, Cin, Cout, kh, kw, stride, pad, act, layout, dtype, buf, 256)
+    with _planning_workspace(workspace_bytes):
+        n = _load().conv2d_plan(N, H, W, Cin, Cout, kh, kw, stride, pad, act, layout, dtype, buf, 256)
     _check(n if n < 0 else OK)
     return buf.value.decode()
 
 
-def plan_maxpool(N, H, W, Cin, Cout, kh, kw, stride, pad, act, layout, dtype) -> str:
+def plan_maxpool(N, H, W, Cin, Cout, kh, kw, stride, pad, act, layout, dtype,
+                 workspace_bytes=DEFAULT_WORKSPACE_BYTES) -> str:
     """Kernel variants conv2d_fused_maxpool3x3s2 picks for a shape (host only)."""
     buf = ctypes.create_string_buffer(256)
-    n = _load().conv2d_fused_maxpool_plan(N, H, W, Cin, Cout, kh, kw, stride, pad, act, layout, dtype,
-                                          buf, 256)
+    with _planning_workspace(workspace_bytes):
+        n = _load().conv2d_fused_maxpool_plan(N, H, W, Cin, Cout, kh, kw, stride, pad, act, layout, dtype,
+                                              buf, 256)
     _check(n if n < 0 else OK)
     return buf.value.decode()
 
@@ -354,27 +454,63 @@ def stack_check(ops, layout="nhwc", dtype=DTYPE_BF16):
     return rc, bad.value
 
 
-def stack_plan(ops, index, layout="nhwc", dtype=DTYPE_BF16) -> str:
+def stack_workspace_size(ops, layout="nhwc", dtype=DTYPE_BF16) -> int:
+    """Bytes of workspace the stack's preferred variants write (host only)."""
     arr, n = _op_array(ops)
+    nb = ctypes.c_size_t(0)
+    _check(_load().conv2d_stack_workspace_size(arr, n, _LAYOUTS[layout], dtype, ctypes.byref(nb)))
+    return nb.value
+
+
+def stack_plan(ops, index, layout="nhwc", dtype=DTYPE_BF16, workspace_bytes=None) -> str:
+    """Kernel variants of op `index` with a workspace of ``workspace_bytes`` (None: what the
+    stack wants, as stack_run and StackGraph give it; 0: none). Host only."""
+    arr, n = _op_array(ops)
+    if workspace_bytes is None:
+        workspace_bytes = stack_workspace_size(ops, layout, dtype)
     buf = ctypes.create_string_buffer(256)
-    rc = _load().conv2d_stack_plan(arr, n, _LAYOUTS[layout], dtype, index, buf, 256)
+    with _planning_workspace(workspace_bytes):
+        rc = _load().conv2d_stack_plan(arr, n, _LAYOUTS[layout], dtype, index, buf, 256)
     _check(rc if rc < 0 else OK)
     return buf.value.decode()
 
 
-def stack_run(ops, layout="nhwc", dtype=DTYPE_BF16, stream=None):
+def _stack_device(ops):
+    # every op's tensors live on the current device (the stack calls take raw pointers)
+    return torch.device("cuda", torch.cuda.current_device())
+
+
+def stack_run(ops, layout="nhwc", dtype=DTYPE_BF16, stream=None, workspace=None):
     """Validate the whole stack, then enqueue its ops in order on the stream."""
     arr, n = _op_array(ops)
-    _check(_load().conv2d_stack_run(arr, n, _LAYOUTS[layout], dtype, _stream_handle(stream)))
+    dev = _stack_device(ops)
+    st = _stream_of(dev, stream)
+    need = 0 if workspace is not None else stack_workspace_size(ops, layout, dtype)
+    _use_workspace(dev, st, workspace, need)
+    _check(_load().conv2d_stack_run(arr, n, _LAYOUTS[layout], dtype, _stream_handle(st)))
 
 
 class StackGraph:
-    """A stack recorded once into a HIP graph; launch() replays it on a stream."""
+    """A stack recorded once into a HIP graph; launch() replays it on a stream.
 
-    def __init__(self, ops, layout="nhwc", dtype=DTYPE_BF16):
+    The graph keeps the workspace it was made with: by default one of its own (sized by
+    stack_workspace_size, held by this object), so replays never share it with other
+    calls; ``workspace=False`` records the variants that need none."""
+
+    def __init__(self, ops, layout="nhwc", dtype=DTYPE_BF16, workspace=None):
         arr, n = _op_array(ops)
+        dev = _stack_device(ops)
+        lib = _load()
+        if workspace is None:
+            need = stack_workspace_size(ops, layout, dtype)
+            workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev) if need else False
+        self.workspace = workspace if workspace is not False else None
+        if self.workspace is None:
+            _check(lib.conv2d_set_workspace(None, 0))
+        else:
+            set_workspace(self.workspace)
         h = ctypes.c_void_p()
-        _check(_load().conv2d_stack_graph_create(arr, n, _LAYOUTS[layout], dtype, ctypes.byref(h)))
+        _check(lib.conv2d_stack_graph_create(arr, n, _LAYOUTS[layout], dtype, ctypes.byref(h)))
         self._h = h
 
     def launch(self, stream=None):
@@ -399,8 +535,15 @@ def _dtype_code(dtype):
     return dt
 
 
+def _deconv_ws_need(Cin, Cout, x):
+    # the packed weights, then (channel-first, width not a multiple of 8) a copy of x
+    e = x.element_size()
+    return (16 * (-(-Cout // 32) * 32) * (-(-Cin // 64) * 64) * e + 255) // 256 * 256 + \
+        (x.numel() * e + 255) // 256 * 256
+
+
 def conv_transpose4x4s2(x, w, bias=None, alpha=None, *, act="none", layout="nhwc", out_dtype=None,
-                        out=None, stream=None):
+                        out=None, stream=None, workspace=None):
     """ConvTranspose2d 4x4, stride 2, pad 1 (+bias, activation) on the GPU; see
     include/conv2d_fused.h. w is [Cin, Cout, 4, 4] in x's dtype for both layouts; the
     output is [N, 2H, 2W, Cout] ("nhwc") or [N, Cout, 2H, 2W] ("nchw") in ``out_dtype``
@@ -434,17 +577,21 @@ def conv_transpose4x4s2(x, w, bias=None, alpha=None, *, act="none", layout="nhwc
         _require(out, "out", out_dtype, dev)
         if tuple(out.shape) != yshape:
             raise ValueError(f"out must have shape {yshape}")
-    rc = lib.conv_transpose4x4s2(_ptr(x), _ptr(w), _ptr(bias), _ptr(alpha), _ptr(out), N, H, W, Cin, Cout,
-                                 _act_code(act, False), lay, dt, odt, _stream_handle(stream))
+    st = _stream_of(dev, stream)
+    with torch.cuda.device(dev):
+        _use_workspace(dev, st, workspace, _deconv_ws_need(Cin, Cout, x))
+        rc = lib.conv_transpose4x4s2(_ptr(x), _ptr(w), _ptr(bias), _ptr(alpha), _ptr(out), N, H, W, Cin, Cout,
+                                     _act_code(act, False), lay, dt, odt, _stream_handle(st))
     _check(rc)
     return out
 
 
-def plan_deconv(N, H, W, Cin, Cout, act, layout, dtype, out_dtype=None) -> str:
+def plan_deconv(N, H, W, Cin, Cout, act, layout, dtype, out_dtype=None, workspace_bytes=DEFAULT_WORKSPACE_BYTES) -> str:
     """Kernel variants conv_transpose4x4s2 picks for a shape (host only)."""
     buf = ctypes.create_string_buffer(256)
-    n = _load().conv_transpose4x4s2_plan(N, H, W, Cin, Cout, act, layout, dtype,
-                                         dtype if out_dtype is None else out_dtype, buf, 256)
+    with _planning_workspace(workspace_bytes):
+        n = _load().conv_transpose4x4s2_plan(N, H, W, Cin, Cout, act, layout, dtype,
+                                             dtype if out_dtype is None else out_dtype, buf, 256)
     _check(n if n < 0 else OK)
     return buf.value.decode()
 
@@ -517,12 +664,19 @@ def concat_op(a, b, y, *, up=False, layout="nhwc"):
 
 
 def tune(N, H, W, Cin, Cout, kh, kw, stride, pad, act="none", *, residual=False, res_before_act=False,
-         layout="nhwc", dtype=DTYPE_BF16, reps=20):
+         layout="nhwc", dtype=DTYPE_BF16, reps=20, workspace=None):
     """Time the kernel variants of one conv shape on the current device and keep the
     fastest for later calls of that shape (include/conv2d_fused.h, conv2d_tune).
-    Returns (variant name, average launch time in microseconds)."""
+    The candidates are those the workspace allows (default: the current stream's, grown
+    to hold split-K in four); later calls use an entry only where their workspace allows
+    it. Returns (variant name, average launch time in microseconds)."""
     buf = ctypes.create_string_buffer(256)
     us = ctypes.c_float(0.0)
+    if torch.cuda.is_available():  # (without a device the call itself reports CONV2D_EHIP)
+        dev = torch.device("cuda", torch.cuda.current_device())
+        OH, OW = out_dim(H, kh, stride, pad), out_dim(W, kw, stride, pad)
+        need = 4 * N * max(OH, 0) * max(OW, 0) * Cout * 4
+        _use_workspace(dev, _stream_of(dev, None), workspace, need)
     n = _load().conv2d_tune(N, H, W, Cin, Cout, kh, kw, stride, pad, _act_code(act, res_before_act),
                             1 if residual else 0, _LAYOUTS[layout], dtype, reps, ctypes.byref(us), buf, 256)
     _check(n if n < 0 else OK)
@@ -548,29 +702,6 @@ def tune_clear():
     _check(_load().conv2d_tune_clear())
 
 
-def avgpool2x2_conv1x1(x, w, bias=None, alpha=None, *, act="none", layout="nhwc", out=None, stream=None):
-    """act(conv1x1(avgpool2x2(x), w) + bias) in one call (the ResNet-D shortcut); w is the
-    1x1 conv's weight ([Cout, 1, 1, Cin] for "nhwc", [Cout, Cin, 1, 1] for "nchw"). See
-    include/conv2d_fused.h, conv2d_avgpool2x2_conv1x1."""
-    lib = _load()
-    lay, dt, (N, H, W, Cin, Cout, kh, kw), _ = _conv_args(x, w, bias, alpha, 1, 0, layout)
-    if (kh, kw) != (1, 1):
-        raise ValueError("w must be a 1x1 conv weight")
-    yshape = (N, H // 2, W // 2, Cout) if layout == "nhwc" else (N, Cout, H // 2, W // 2)
-    out = _out(out, yshape, x)
-    rc = lib.conv2d_avgpool2x2_conv1x1(_ptr(x), _ptr(w), _ptr(bias), _ptr(alpha), _ptr(out), N, H, W, Cin, Cout,
-                                       _act_code(act, False), lay, dt, _stream_handle(stream))
-    _check(rc)
-    return out
-
-
-def pool_conv_op(x, w, y, bias=None, alpha=None, *, act="none", layout="nhwc"):
-    """An Op for conv2d_avgpool2x2_conv1x1 (w: the 1x1 conv weight)."""
-    N, H, W, Cin, Cout, kh, kw = _dims(x, w, layout)
-    return Op(OP_AVGPOOL_CONV1X1, x.data_ptr(), w.data_ptr(), _tensor_ptr(bias), _tensor_ptr(alpha), None,
-              y.data_ptr(), N, H, W, Cin, Cout, 1, 1, 1, 0, _act_code(act, False))
-
-
 def deconv_pack(w, stream=None):
     """Pack transposed-conv weights w [Cin, Cout, 4, 4] (bf16/f16, Cin % 8 == 0) once;
     returns (packed tensor, Cout) for conv_transpose4x4s2_prepacked."""
@@ -588,7 +719,7 @@ def deconv_pack(w, stream=None):
 
 
 def conv_transpose4x4s2_prepacked(x, packed, bias=None, alpha=None, *, act="none", layout="nhwc", out_dtype=None,
-                                  out=None, stream=None):
+                                  out=None, stream=None, workspace=None):
     """conv_transpose4x4s2 with weights packed by deconv_pack (``packed`` = its result)."""
     lib = _load()
     wp, Cout = packed
@@ -612,8 +743,11 @@ def conv_transpose4x4s2_prepacked(x, packed, bias=None, alpha=None, *, act="none
         _require(out, "out", out_dtype, dev)
         if tuple(out.shape) != yshape:
             raise ValueError(f"out must have shape {yshape}")
-    rc = lib.conv_transpose4x4s2_prepacked(_ptr(x), _ptr(wp), _ptr(bias), _ptr(alpha), _ptr(out), N, H, W, Cin, Cout,
-                                           _act_code(act, False), lay, dt, odt, _stream_handle(stream))
+    st = _stream_of(dev, stream)
+    with torch.cuda.device(dev):
+        _use_workspace(dev, st, workspace, (x.numel() * x.element_size() + 255) // 256 * 256)
+        rc = lib.conv_transpose4x4s2_prepacked(_ptr(x), _ptr(wp), _ptr(bias), _ptr(alpha), _ptr(out), N, H, W, Cin,
+                                               Cout, _act_code(act, False), lay, dt, odt, _stream_handle(st))
     _check(rc)
     return out
 

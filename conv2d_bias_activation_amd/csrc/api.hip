@@ -81,7 +81,7 @@ constexpr long long kMaxElems = 0x7fffffffll;
 
 // Validates conv2d_fused's arguments; fills the derived geometry into `a`. With
 // pooled_y, y holds the 3x3 stride-2 max pool of the conv output instead.
-int check_conv(const void *x, const void *w, const float *alpha, const void *residual,
+int check_conv(const void *x, const void *w, const float *bias, const float *alpha, const void *residual,
                const void *y, int N, int H, int W, int Cin, int Cout, int kh, int kw,
                int stride, int pad, int act, int layout, int dtype, ConvArgs *a, bool pooled_y = false) {
     if (!x || !w || !y) return set_error(CONV2D_EINVAL, "x, w and y must not be null");
@@ -112,6 +112,11 @@ int check_conv(const void *x, const void *w, const float *alpha, const void *res
     const long long yb = pooled_y ? (long long)N * out_dim(OH, 3, 2, 1) * out_dim(OW, 3, 2, 1) * Cout * eb : ye * eb;
     if (overlap(y, yb, x, xe * eb)) return set_error(CONV2D_EINVAL, "y overlaps x");
     if (overlap(y, yb, residual, ye * eb)) return set_error(CONV2D_EINVAL, "y overlaps the residual");
+    // other workgroups still read the weights, bias and slopes while one stores y
+    if (overlap(y, yb, w, we * eb)) return set_error(CONV2D_EINVAL, "y overlaps w");
+    if (overlap(y, yb, bias, (long long)Cout * 4)) return set_error(CONV2D_EINVAL, "y overlaps bias");
+    if (code == CONV2D_ACT_PRELU && overlap(y, yb, alpha, (long long)Cout * 4))
+        return set_error(CONV2D_EINVAL, "y overlaps alpha");
     a->x = x;
     a->w = w;
     a->alpha = alpha;
@@ -148,35 +153,38 @@ struct Plan {
     bool tuned;  // chosen by a conv2d_tune measurement rather than the built-in heuristics
     bool w_ohwi; // channel-first layer with channel-last weights: only the input is copied
     // chained channel-first layers of a stack (FAM_NCHW_VIA_NHWC, set by link_chains)
-    bool chain_in;   // the input's channel-last copy is already in the scratch at x_at
+    bool chain_in;   // the input's channel-last copy is already in the workspace at x_at
     size_t x_at;
-    bool chain_out;  // also write the output channel-last into the scratch at y2_at
+    bool chain_out;  // also write the output channel-last into the workspace at y2_at
     size_t y2_at;
 };
 
-// Library scratch, one buffer per device, allocated on the first call that needs it
-// and kept until the process ends: split-K fp32 partial sums, or the channel-last
-// copies of a channel-first layer's input and weight.
-constexpr size_t kScratchBytes = 64ull << 20;
+// Caller-owned workspace (device scratch) of the calls made from this thread on one
+// device, registered by conv2d_set_workspace. It holds split-K fp32 partial sums, the
+// channel-last copies of a channel-first layer's input and weight, the unpooled output
+// of a conv + max pool that runs as two kernels, and a transposed conv's packed
+// weights. Without one (or when it is too small) every call takes a variant that
+// needs no scratch, or returns CONV2D_EUNSUPPORTED where none exists.
+struct Workspace {
+    char *p;
+    size_t bytes;
+};
 constexpr int kMaxDevices = 64;
-float *g_scratch[kMaxDevices];
-std::mutex g_scratch_mu;
+thread_local Workspace g_ws[kMaxDevices];
+// a planning-only stand-in for "as much workspace as the preferred variants want"
+constexpr size_t kUnlimitedWs = (size_t)1 << 50;
 
-int get_scratch(float **out) {
+// The registry slot of the current device: device 0's when no device can be queried, so
+// that host-only planning calls see a registered size on a machine without a GPU.
+int ws_slot() {
     int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return set_error(CONV2D_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
-    if (dev < 0 || dev >= kMaxDevices) return set_error(CONV2D_EHIP, "device index %d out of range", dev);
-    std::lock_guard<std::mutex> lock(g_scratch_mu);
-    if (!g_scratch[dev]) {
-        void *p = nullptr;
-        e = hipMalloc(&p, kScratchBytes);
-        if (e != hipSuccess)
-            return set_error(CONV2D_EHIP, "split-K scratch allocation: %s", hipGetErrorString(e));
-        g_scratch[dev] = static_cast<float *>(p);
-    }
-    *out = g_scratch[dev];
-    return CONV2D_OK;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    return dev;
+}
+
+Workspace current_ws() {
+    const int dev = ws_slot();
+    return dev >= 0 && dev < kMaxDevices ? g_ws[dev] : Workspace{nullptr, 0};
 }
 
 // Compute units of the current device (queried once per device).
@@ -251,7 +259,7 @@ const char *nhwc_tile_name(int t) {
 // bigger tiles there), 128x256 for wide pointwise layers, 128x64 for narrow outputs.
 size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 
-NhwcPlan plan_nhwc(const ConvArgs &a) {
+NhwcPlan plan_nhwc(const ConvArgs &a, size_t ws) {
     NhwcPlan p{};
     auto tiles = [&](int bm, int bn) {
         return (long long)((a.M + bm - 1) / bm) * ((a.Cout + bn - 1) / bn);
@@ -271,7 +279,7 @@ NhwcPlan plan_nhwc(const ConvArgs &a) {
     const int nsteps = (a.K + 63) / 64;
     p.splits = 1;
     if (waves < 1200 && nsteps >= 48 && (a.Cout % 8) == 0 && a.vec_out &&
-        3ull * a.M * a.Cout * 4 <= kScratchBytes)
+        3ull * a.M * a.Cout * 4 <= ws)
         p.splits = 3;
     p.tap_inner = (a.Cin % 64) == 0 && a.kh * a.kw <= 32;  // tap masks are 32-bit
     return p;
@@ -321,7 +329,7 @@ bool stem_fits(const ConvArgs &a, int layout, int dtype) {
            (long long)a.M * a.Cout * 2 < (1ll << 31);
 }
 
-// The general MFMA implicit GEMM: any shape, layout and dtype, no scratch.
+// The general MFMA implicit GEMM: any shape, layout and dtype, no workspace.
 Plan igemm_plan(const ConvArgs &a, int layout, int dtype) {
     Plan p{};
     const int ve = 16 / dtype_bytes(dtype);
@@ -333,7 +341,7 @@ Plan igemm_plan(const ConvArgs &a, int layout, int dtype) {
     return p;
 }
 
-Plan make_plan_default(const ConvArgs &a, int layout, int dtype) {
+Plan make_plan_default(const ConvArgs &a, int layout, int dtype, size_t ws) {
     Plan p{};
     if (stem_fits(a, layout, dtype)) {
         p.family = FAM_STEM;
@@ -355,15 +363,16 @@ Plan make_plan_default(const ConvArgs &a, int layout, int dtype) {
         aligned16(a.x) && aligned16(a.w) && xbytes < (1ll << 31) && wbytes < (1ll << 31) &&
         ybytes < (1ll << 31)) {
         p.family = FAM_NHWC;
-        p.nh = plan_nhwc(a);
+        p.nh = plan_nhwc(a, ws);
         return p;
     }
-    // Channel-first 16-bit layers: channel-last copies of x and w in the scratch, the
-    // channel-last kernel, and an epilogue that writes the channel-first output.
+    // Channel-first 16-bit layers: channel-last copies of x (and of w, unless given
+    // channel-last) in the workspace, the channel-last kernel, and an epilogue that
+    // writes the channel-first output.
     if (layout == CONV2D_LAYOUT_NCHW && dtype != CONV2D_DTYPE_F32 && (a.Cin % 8) == 0 && a.N <= 65535 &&
-        round256((size_t)xbytes) + round256((size_t)wbytes) <= kScratchBytes && ybytes < (1ll << 31)) {
+        round256((size_t)xbytes) + (a.w_ohwi ? 0 : round256((size_t)wbytes)) <= ws && ybytes < (1ll << 31)) {
         p.family = FAM_NCHW_VIA_NHWC;
-        p.nh = plan_nhwc(a);
+        p.nh = plan_nhwc(a, ws);
         p.nh.splits = 1;
         p.nh.nchw_out = true;
         return p;
@@ -377,7 +386,7 @@ Plan make_plan_default(const ConvArgs &a, int layout, int dtype) {
 // The table maps a shape key (device, sizes, layout, dtype, residual or not) to a kernel
 // variant of the channel-last matrix-core families. make_plan consults it for shapes
 // whose built-in choice is one of those families, and uses an entry only if the variant
-// is valid for the call at hand (alignment, scratch size).
+// is valid for the call at hand (alignment, workspace size).
 struct TunedEntry {
     int family;  // FAM_NHWC, FAM_NCHW_VIA_NHWC or FAM_HALO
     int tile;    // NhwcTile (FAM_NHWC, FAM_NCHW_VIA_NHWC)
@@ -412,9 +421,9 @@ std::string tune_key(const std::string &dev, const ConvArgs &a, int layout, int 
     return k;
 }
 
-bool splits_ok(const ConvArgs &a, int splits) {
+bool splits_ok(const ConvArgs &a, int splits, size_t ws) {
     if (splits <= 1) return true;
-    return (a.Cout % 8) == 0 && a.vec_out && (unsigned long long)splits * a.M * a.Cout * 4 <= kScratchBytes &&
+    return (a.Cout % 8) == 0 && a.vec_out && (unsigned long long)splits * a.M * a.Cout * 4 <= ws &&
            (a.K + 63) / 64 >= splits;
 }
 
@@ -425,7 +434,7 @@ bool halo_th_ok(const ConvArgs &a, int th) {
 }
 
 // Applies the table's entry for this call, if any and valid; p is the built-in choice.
-void apply_tuned(const ConvArgs &a, int layout, int dtype, Plan *p) {
+void apply_tuned(const ConvArgs &a, int layout, int dtype, size_t ws, Plan *p) {
     if (g_tuned_n.load(std::memory_order_acquire) == 0) return;
     if (p->family != FAM_NHWC && p->family != FAM_HALO && p->family != FAM_NCHW_VIA_NHWC) return;
     const std::string dev = device_tag();
@@ -451,29 +460,30 @@ void apply_tuned(const ConvArgs &a, int layout, int dtype, Plan *p) {
         p->halo.th = e.th;
         p->tuned = true;
     } else if (e.family == FAM_NHWC) {
-        if (e.tile < 0 || e.tile >= NHWC_TILE_COUNT || !splits_ok(a, e.splits)) return;
+        if (e.tile < 0 || e.tile >= NHWC_TILE_COUNT || !splits_ok(a, e.splits, ws)) return;
         p->family = FAM_NHWC;
-        p->nh = plan_nhwc(a);
+        p->nh = plan_nhwc(a, ws);
         p->nh.tile = e.tile;
         p->nh.splits = e.splits > 1 ? e.splits : 1;
         p->tuned = true;
     }
 }
 
-Plan make_plan(const ConvArgs &a, int layout, int dtype) {
-    Plan p = make_plan_default(a, layout, dtype);
-    apply_tuned(a, layout, dtype, &p);
+Plan make_plan(const ConvArgs &a, int layout, int dtype, size_t ws) {
+    Plan p = make_plan_default(a, layout, dtype, ws);
+    apply_tuned(a, layout, dtype, ws, &p);
     p.w_ohwi = a.w_ohwi != 0;
     return p;
 }
 
 // Channel-first layers with channel-last weights run only on the channel-last kernel
-// (after the input's layout copy): 16-bit, Cin % 8 == 0, the copy within the scratch.
+// (after the input's layout copy): 16-bit, Cin % 8 == 0, the copy within the workspace.
 int check_w_ohwi(const ConvArgs &a, const Plan &p) {
     if (a.w_ohwi && p.family != FAM_NCHW_VIA_NHWC)
         return set_error(CONV2D_EUNSUPPORTED,
                          "CONV2D_WEIGHTS_OHWI needs a 16-bit layer with Cin %% 8 == 0 whose channel-last input copy "
-                         "fits the library scratch");
+                         "(%lld bytes) fits the workspace set by conv2d_set_workspace",
+                         (long long)round256((size_t)a.N * a.H * a.W * a.Cin * 2));
     return CONV2D_OK;
 }
 
@@ -525,8 +535,9 @@ int check_pool(const void *x, const void *y, int N, int H, int W, int C, int lay
     return CONV2D_OK;
 }
 
-// Launches the kernels of plan p for a validated conv (y = a.y). Returns a status code.
-int launch_conv(const ConvArgs &a, const Plan &p, int layout, int dtype, hipStream_t st) {
+// Launches the kernels of plan p for a validated conv (y = a.y); ws is the workspace the
+// plan was made for. Returns a status code.
+int launch_conv(const ConvArgs &a, const Plan &p, int layout, int dtype, const Workspace &ws, hipStream_t st) {
     hipError_t e;
     int rc;
     if (p.family == FAM_DIRECT) {
@@ -541,18 +552,10 @@ int launch_conv(const ConvArgs &a, const Plan &p, int layout, int dtype, hipStre
         h.grid_cap = cus * (8 / h.waves);
         e = launch_halo3x3(a, dtype, h, st);
     } else if (p.family == FAM_NHWC) {
-        float *scratch = nullptr;
-        if (p.nh.splits > 1) {
-            rc = get_scratch(&scratch);
-            if (rc) return rc;
-        }
-        e = launch_igemm_nhwc(a, dtype, p.nh, scratch, st);
+        e = launch_igemm_nhwc(a, dtype, p.nh, p.nh.splits > 1 ? reinterpret_cast<float *>(ws.p) : nullptr, st);
     } else if (p.family == FAM_NCHW_VIA_NHWC) {
-        float *scratch = nullptr;
-        rc = get_scratch(&scratch);
-        if (rc) return rc;
         const int eb = dtype_bytes(dtype);
-        char *base = reinterpret_cast<char *>(scratch);
+        char *base = ws.p;
         char *xs = base + (p.chain_in ? p.x_at : 0);
         char *ws = xs + round256((size_t)a.N * a.H * a.W * a.Cin * eb);
         // weights given channel-last (converted once by the caller) need no copy; a
@@ -581,19 +584,20 @@ enum PoolKernel { POOL_TWO_KERNELS = 0, POOL_FUSED_STEM = 1, POOL_FUSED_HALO = 2
 
 struct PoolFusion {
     int kind;        // PoolKernel
-    Plan conv_plan;  // POOL_TWO_KERNELS: this conv into the scratch, then the pool kernel
+    Plan conv_plan;  // POOL_TWO_KERNELS: this conv into the workspace, then the pool kernel
 };
 
 // Validates conv2d_fused_maxpool3x3s2's arguments (y is the pooled map) and picks the
 // fused kernel or the two-kernel path.
-int check_conv_pool(const void *x, const void *w, const float *alpha, const void *y, int N, int H, int W,
+int check_conv_pool(const void *x, const void *w, const float *bias, const float *alpha, const void *y, int N, int H,
+                    int W,
                     int Cin, int Cout, int kh, int kw, int stride, int pad, int act, int layout, int dtype,
-                    ConvArgs *a, PoolFusion *f) {
+                    size_t ws, ConvArgs *a, PoolFusion *f) {
     if (act & CONV2D_RES_BEFORE_ACT)
         return set_error(CONV2D_EINVAL, "conv2d_fused_maxpool3x3s2 takes no residual");
     if (act & CONV2D_WEIGHTS_OHWI)
         return set_error(CONV2D_EINVAL, "conv2d_fused_maxpool3x3s2 takes the weights in the layout's own order");
-    int rc = check_conv(x, w, alpha, nullptr, y, N, H, W, Cin, Cout, kh, kw, stride, pad, act, layout, dtype, a,
+    int rc = check_conv(x, w, bias, alpha, nullptr, y, N, H, W, Cin, Cout, kh, kw, stride, pad, act, layout, dtype, a,
                         true);
     if (rc) return rc;
     const long long xbytes = (long long)N * H * W * Cin * dtype_bytes(dtype);
@@ -601,32 +605,32 @@ int check_conv_pool(const void *x, const void *w, const float *alpha, const void
               : (halo_fits(*a, layout, dtype) && Cin <= 32 && xbytes < (1ll << 31)) ? POOL_FUSED_HALO
                                                                                      : POOL_TWO_KERNELS;
     if (f->kind == POOL_TWO_KERNELS) {
-        // the conv output goes to the library scratch, which the conv kernels then must
-        // not use themselves: no split-K, and channel-first layers on the general kernel
-        if ((long long)a->M * Cout * dtype_bytes(dtype) > (long long)kScratchBytes)
+        // the conv output goes to the workspace, which the conv kernels then must not
+        // use themselves (planned without a workspace: no split-K, channel-first layers
+        // on the general kernel)
+        if ((unsigned long long)a->M * Cout * dtype_bytes(dtype) > ws)
             return set_error(CONV2D_EUNSUPPORTED,
-                             "conv2d_fused_maxpool3x3s2: the unpooled conv output (%lld bytes) exceeds the %zu-byte "
-                             "scratch; call conv2d_fused and maxpool3x3s2",
-                             (long long)a->M * Cout * dtype_bytes(dtype), kScratchBytes);
+                             "conv2d_fused_maxpool3x3s2: this shape runs as a conv and a pool kernel, whose unpooled "
+                             "conv output (%lld bytes) needs a workspace of that size (conv2d_set_workspace; set: "
+                             "%zu bytes); or call conv2d_fused and maxpool3x3s2",
+                             (long long)a->M * Cout * dtype_bytes(dtype), ws);
         ConvArgs b = *a;
-        b.vec_out = true;  // the scratch is 256-byte aligned
-        f->conv_plan = make_plan(b, layout, dtype);
-        if (f->conv_plan.family == FAM_NCHW_VIA_NHWC) f->conv_plan = igemm_plan(b, layout, dtype);
-        if (f->conv_plan.family == FAM_NHWC) f->conv_plan.nh.splits = 1;
+        b.vec_out = true;  // the workspace is 256-byte aligned
+        f->conv_plan = make_plan(b, layout, dtype, 0);
     }
     return CONV2D_OK;
 }
 
 // Transposed conv 4x4/s2/p1: the matrix-core kernel for 16-bit types with Cin % 8 == 0
-// (weights repacked into the scratch first; a channel-first input is transposed while
+// (weights repacked into the workspace first; a channel-first input is transposed while
 // it is staged), the direct kernel otherwise.
 struct DeconvPlan {
     bool mfma;
     bool prepacked;  // the weights come packed by conv_transpose4x4s2_pack (da.wp)
     bool all;      // Cin <= 256: the kernel that stages the whole input strip at once
-    bool x_copy;   // channel-first input copied to channel-last in the scratch first (all); else
-                   // the kernel reads the planes (W % 8 == 0, x 16-byte aligned)
-    size_t x_off;  // byte offset of that copy in the scratch (after the packed weights)
+    bool x_copy;   // channel-first input copied to channel-last in the workspace first (all);
+                   // else the kernel reads the planes (W % 8 == 0, x 16-byte aligned)
+    size_t x_off;  // byte offset of that copy in the workspace (after the packed weights)
     bool out_f32;  // y in fp32 (16-bit input)
 };
 
@@ -636,8 +640,8 @@ size_t deconv_packed_bytes(int Cin, int Cout, int eb) {
 
 // packed: w is the caller's copy of the packed weights (conv_transpose4x4s2_pack).
 int check_deconv(const void *x, const void *w, const float *bias, const float *alpha, const void *y, int N, int H,
-                 int W, int Cin, int Cout, int act, int layout, int dtype, int out_dtype, DeconvArgs *a,
-                 DeconvPlan *p, bool packed = false) {
+                 int W, int Cin, int Cout, int act, int layout, int dtype, int out_dtype, size_t ws,
+                 DeconvArgs *a, DeconvPlan *p, bool packed = false) {
     if (!x || !w || !y) return set_error(CONV2D_EINVAL, "conv_transpose4x4s2: x, w and y must not be null");
     if (N <= 0 || H <= 0 || W <= 0 || Cin <= 0 || Cout <= 0)
         return set_error(CONV2D_EINVAL, "conv_transpose4x4s2: sizes must be positive (N=%d H=%d W=%d Cin=%d Cout=%d)",
@@ -676,16 +680,18 @@ int check_deconv(const void *x, const void *w, const float *bias, const float *a
     p->out_f32 = out_dtype == CONV2D_DTYPE_F32 && dtype != CONV2D_DTYPE_F32;
     const bool nchw = layout == CONV2D_LAYOUT_NCHW;
     const size_t wp_bytes = (size_t)16 * a->CoP * ((Cin + 63) / 64 * 64) * eb;
-    p->mfma = dtype != CONV2D_DTYPE_F32 && (Cin % 8) == 0 && wp_bytes <= kScratchBytes && (nchw || aligned16(x)) &&
+    // the matrix cores need the weights packed into the workspace first (or packed once
+    // by the caller); without room for them the direct kernel runs
+    p->mfma = dtype != CONV2D_DTYPE_F32 && (Cin % 8) == 0 && wp_bytes <= ws && (nchw || aligned16(x)) &&
               xe * eb < (1ll << 31);
     // channel-first inputs with up to 256 channels: the kernel that stages the whole input
     // strip at once, reading the planes with 16-byte loads of 8-pixel segments when W % 8
-    // == 0 and x is 16-byte aligned, else from a channel-last copy in the scratch (when
+    // == 0 and x is 16-byte aligned, else from a channel-last copy in the workspace (when
     // that fits beside the weights) made by a 16-byte transpose (element-by-element
     // staging from the planes measured slower than that copy; for channel-last inputs the
     // chunked kernel measured faster)
     if (packed) {
-        // caller-owned packed weights: the matrix-core path only, the scratch only for the
+        // caller-owned packed weights: the matrix-core path only, the workspace only for the
         // channel-last copy of a channel-first input
         if (!(dtype != CONV2D_DTYPE_F32 && (Cin % 8) == 0 && wp_bytes < (1ull << 31) && (nchw || aligned16(x)) &&
               xe * eb < (1ll << 31)))
@@ -700,7 +706,7 @@ int check_deconv(const void *x, const void *w, const float *bias, const float *a
     p->x_off = packed ? 0 : round256(wp_bytes);
     p->x_copy = nchw && !((W % 8) == 0 && aligned16(x));
     p->all = p->mfma && nchw && Cin <= 256 && N <= 65535 &&
-             p->x_off + (p->x_copy ? round256((size_t)(xe * eb)) : 0) <= kScratchBytes;
+             p->x_off + (p->x_copy ? round256((size_t)(xe * eb)) : 0) <= ws;
     a->x_bytes = (uint32_t)(xe * eb < (1ll << 31) ? xe * eb : 0);
     a->wp_bytes = (uint32_t)wp_bytes;
     return CONV2D_OK;
@@ -752,37 +758,51 @@ struct OpPlan {
     const void *b;  // concat: second input
     int Ca, Cb;     // concat channels (Cb = 0: upsample)
     bool up;        // upsample the first input
-    const void *w1;  // average pool + 1x1 conv: the caller's [Cout][Cin] weights
-    size_t w_off;    // byte offset of their 2x2 expansion in the scratch (at its end)
 };
 
-bool needs_scratch(const OpPlan &o) {
-    if (o.kind == CONV2D_OP_CONV)
-        return o.plan.family == FAM_NCHW_VIA_NHWC || (o.plan.family == FAM_NHWC && o.plan.nh.splits > 1);
-    if (o.kind == CONV2D_OP_DECONV) return o.dp.mfma && (!o.dp.prepacked || (o.dp.all && o.dp.x_copy));
-    if (o.kind == CONV2D_OP_AVGPOOL_CONV1X1) return true;
-    return o.kind == CONV2D_OP_CONV_MAXPOOL && o.pf.kind == POOL_TWO_KERNELS;
+// Bytes of workspace the launch of a planned op writes (0 for none).
+size_t ws_need(const OpPlan &o) {
+    const int eb = dtype_bytes(o.dtype);
+    if (o.kind == CONV2D_OP_CONV) {
+        const ConvArgs &a = o.a;
+        if (o.plan.family == FAM_NHWC && o.plan.nh.splits > 1) return (size_t)o.plan.nh.splits * a.M * a.Cout * 4;
+        if (o.plan.family == FAM_NCHW_VIA_NHWC) {
+            const size_t xb = round256((size_t)a.N * a.H * a.W * a.Cin * eb);
+            const size_t wb = a.w_ohwi ? 0 : round256((size_t)a.Cout * a.K * eb);
+            size_t need = (o.plan.chain_in ? o.plan.x_at : 0) + xb + wb;
+            if (o.plan.chain_out) need = std::max(need, o.plan.y2_at + round256((size_t)a.M * a.Cout * eb));
+            return need;
+        }
+        return 0;
+    }
+    if (o.kind == CONV2D_OP_CONV_MAXPOOL)
+        return o.pf.kind == POOL_TWO_KERNELS ? round256((size_t)o.a.M * o.a.Cout * eb) : 0;
+    if (o.kind == CONV2D_OP_DECONV && o.dp.mfma) {
+        const size_t wp = o.dp.prepacked ? 0 : round256(o.da.wp_bytes);
+        return wp + (o.dp.all && o.dp.x_copy ? round256((size_t)o.da.N * o.da.H * o.da.W * o.da.Cin * eb) : 0);
+    }
+    return 0;
 }
 
-int check_op(const conv2d_op &op, int layout, int dtype, OpPlan *o) {
+int check_op(const conv2d_op &op, int layout, int dtype, size_t ws, OpPlan *o) {
     *o = OpPlan{};
     o->kind = op.kind;
     o->layout = layout;
     o->dtype = dtype;
     switch (op.kind) {
     case CONV2D_OP_CONV: {
-        int rc = check_conv(op.x, op.w, op.alpha, op.residual, op.y, op.N, op.H, op.W, op.Cin, op.Cout, op.kh,
+        int rc = check_conv(op.x, op.w, op.bias, op.alpha, op.residual, op.y, op.N, op.H, op.W, op.Cin, op.Cout, op.kh,
                             op.kw, op.stride, op.pad, op.act, layout, dtype, &o->a);
         if (rc) return rc;
         o->a.bias = op.bias;
         if ((op.act & 0xff) != CONV2D_ACT_PRELU) o->a.alpha = nullptr;
-        o->plan = make_plan(o->a, layout, dtype);
+        o->plan = make_plan(o->a, layout, dtype, ws);
         return check_w_ohwi(o->a, o->plan);
     }
     case CONV2D_OP_CONV_MAXPOOL: {
         if (op.residual) return set_error(CONV2D_EINVAL, "conv2d_fused_maxpool3x3s2 takes no residual");
-        int rc = check_conv_pool(op.x, op.w, op.alpha, op.y, op.N, op.H, op.W, op.Cin, op.Cout, op.kh, op.kw,
-                                 op.stride, op.pad, op.act, layout, dtype, &o->a, &o->pf);
+        int rc = check_conv_pool(op.x, op.w, op.bias, op.alpha, op.y, op.N, op.H, op.W, op.Cin, op.Cout, op.kh, op.kw,
+                                 op.stride, op.pad, op.act, layout, dtype, ws, &o->a, &o->pf);
         if (rc) return rc;
         o->a.bias = op.bias;
         if ((op.act & 0xff) != CONV2D_ACT_PRELU) o->a.alpha = nullptr;
@@ -821,38 +841,7 @@ int check_op(const conv2d_op &op, int layout, int dtype, OpPlan *o) {
     }
     case CONV2D_OP_DECONV:
         return check_deconv(op.x, op.w, op.bias, op.alpha, op.y, op.N, op.H, op.W, op.Cin, op.Cout, op.act, layout,
-                            dtype, dtype, &o->da, &o->dp);
-    case CONV2D_OP_AVGPOOL_CONV1X1: {
-        // the 2x2 stride-2 conv with weights w/4 on every tap (built in the scratch)
-        if (op.residual || (op.act & CONV2D_RES_BEFORE_ACT))
-            return set_error(CONV2D_EINVAL, "avgpool2x2_conv1x1 takes no residual");
-        if (op.act & CONV2D_WEIGHTS_OHWI)
-            return set_error(CONV2D_EINVAL, "avgpool2x2_conv1x1 takes [Cout][Cin] weights");
-        if (!op.w) return set_error(CONV2D_EINVAL, "avgpool2x2_conv1x1: w must not be null");
-        int rc = check_conv(op.x, op.w, op.alpha, nullptr, op.y, op.N, op.H, op.W, op.Cin, op.Cout, 2, 2, 2, 0,
-                            op.act, layout, dtype, &o->a);
-        if (rc) return rc;
-        o->a.bias = op.bias;
-        if ((op.act & 0xff) != CONV2D_ACT_PRELU) o->a.alpha = nullptr;
-        const long long eb = dtype_bytes(dtype);
-        const size_t w2b = round256((size_t)op.Cout * 4 * op.Cin * eb);
-        if (w2b > kScratchBytes)
-            return set_error(CONV2D_EUNSUPPORTED, "avgpool2x2_conv1x1: the 2x2 weights exceed the %zu-byte scratch",
-                             kScratchBytes);
-        o->w1 = op.w;
-        o->w_off = kScratchBytes - w2b;
-        ConvArgs b = o->a;
-        b.w = (const void *)(uintptr_t)0x100000000ull;  // a 256-byte aligned stand-in for the scratch copy
-        Plan pl = make_plan(b, layout, dtype);
-        // the conv may use the scratch below the weights only: no split-K, and channel-first
-        // copies only where they fit
-        if (pl.family == FAM_NHWC) pl.nh.splits = 1;
-        if (pl.family == FAM_NCHW_VIA_NHWC &&
-            round256((size_t)op.N * op.H * op.W * op.Cin * eb) + w2b > o->w_off)
-            pl = igemm_plan(b, layout, dtype);
-        o->plan = pl;
-        return CONV2D_OK;
-    }
+                            dtype, dtype, ws, &o->da, &o->dp);
     case CONV2D_OP_UPSAMPLE:
     case CONV2D_OP_CONCAT:
     case CONV2D_OP_UPSAMPLE_CONCAT: {
@@ -885,10 +874,10 @@ int check_op(const conv2d_op &op, int layout, int dtype, OpPlan *o) {
 // Chained channel-first convs of a stack: when a conv's output is the next op's input
 // and both run on the channel-last kernel with channel-last weights (the IFNet block's
 // chain), the producer (without a residual) also writes its output channel-last into
-// one half of the scratch and the consumer reads that instead of copying its input;
+// one half of the workspace and the consumer reads that instead of copying its input;
 // the halves alternate along the chain, so a layer never writes the half it reads.
-void link_chains(std::vector<OpPlan> &plans) {
-    const size_t half = kScratchBytes / 2;
+void link_chains(std::vector<OpPlan> &plans, size_t ws) {
+    const size_t half = ws / 2 & ~(size_t)255;
     for (size_t i = 0; i + 1 < plans.size(); ++i) {
         OpPlan &p = plans[i], &q = plans[i + 1];
         if (p.kind != CONV2D_OP_CONV || q.kind != CONV2D_OP_CONV) continue;
@@ -907,40 +896,34 @@ void link_chains(std::vector<OpPlan> &plans) {
     }
 }
 
-int check_stack(const conv2d_op *ops, int n, int layout, int dtype, std::vector<OpPlan> *plans, int *bad) {
+int check_stack(const conv2d_op *ops, int n, int layout, int dtype, size_t ws, std::vector<OpPlan> *plans,
+                int *bad) {
     if (n < 0 || (n > 0 && !ops)) return set_error(CONV2D_EINVAL, "ops must hold n >= 0 entries");
     plans->resize((size_t)n);
     for (int i = 0; i < n; ++i) {
-        int rc = check_op(ops[i], layout, dtype, &(*plans)[(size_t)i]);
+        int rc = check_op(ops[i], layout, dtype, ws, &(*plans)[(size_t)i]);
         if (rc) {
             if (bad) *bad = i;
             return set_error(rc, "op %d: %s", i, g_err.c_str());
         }
     }
-    link_chains(*plans);
+    link_chains(*plans, ws);
     return CONV2D_OK;
 }
 
-// Host-side state the launches need (the scratch buffer, the CU count), fetched before
-// any launch so that a captured stack makes no allocation inside the capture.
+// Host-side state the launches need (the CU count), fetched before any launch so that a
+// captured stack makes no device query inside the capture.
 int prepare_stack(const std::vector<OpPlan> &plans) {
-    bool scratch = false;
-    for (const OpPlan &o : plans) scratch = scratch || needs_scratch(o);
-    if (scratch) {
-        float *p = nullptr;
-        int rc = get_scratch(&p);
-        if (rc) return rc;
-    }
     int cus = 0;
     return plans.empty() ? CONV2D_OK : device_cus(&cus);
 }
 
-int launch_op(const OpPlan &o, hipStream_t st) {
+int launch_op(const OpPlan &o, const Workspace &ws, hipStream_t st) {
     hipError_t e = hipSuccess;
     const bool nchw = o.layout == CONV2D_LAYOUT_NCHW;
     switch (o.kind) {
     case CONV2D_OP_CONV:
-        return launch_conv(o.a, o.plan, o.layout, o.dtype, st);
+        return launch_conv(o.a, o.plan, o.layout, o.dtype, ws, st);
     case CONV2D_OP_CONV_MAXPOOL: {
         const ConvArgs &a = o.a;
         if (o.pf.kind == POOL_FUSED_STEM) {
@@ -951,18 +934,15 @@ int launch_op(const OpPlan &o, hipStream_t st) {
             if (rc) return rc;
             e = launch_halo3x3_maxpool(a, a.y, o.dtype, 2 * cus, st);
         } else {
-            // the conv into the scratch buffer, then the pool kernel
-            float *scratch = nullptr;
-            int rc = get_scratch(&scratch);
-            if (rc) return rc;
+            // the conv into the workspace, then the pool kernel
             ConvArgs b = a;
-            b.y = scratch;
+            b.y = ws.p;
             b.vec_out = true;
-            rc = launch_conv(b, o.pf.conv_plan, o.layout, o.dtype, st);
+            int rc = launch_conv(b, o.pf.conv_plan, o.layout, o.dtype, Workspace{nullptr, 0}, st);
             if (rc) return rc;
             const int ve = 16 / dtype_bytes(o.dtype);
             const bool vec = !nchw && (a.Cout % ve) == 0 && aligned16(a.y);
-            e = launch_maxpool(scratch, a.y, a.N, a.OH, a.OW, a.Cout, nchw, o.dtype, vec, st);
+            e = launch_maxpool(ws.p, a.y, a.N, a.OH, a.OW, a.Cout, nchw, o.dtype, vec, st);
         }
         if (e != hipSuccess) return hip_fail(e, "conv2d_fused_maxpool3x3s2 launch");
         return CONV2D_OK;
@@ -981,19 +961,14 @@ int launch_op(const OpPlan &o, hipStream_t st) {
             e = launch_deconv_direct(o.da, o.dtype, o.dp.out_f32, nchw, st);
             return e == hipSuccess ? CONV2D_OK : hip_fail(e, "conv_transpose4x4s2 launch");
         }
-        float *scratch = nullptr;
         DeconvArgs a = o.da;
-        if (!o.dp.prepacked || (o.dp.all && o.dp.x_copy)) {
-            int rc = get_scratch(&scratch);
-            if (rc) return rc;
-        }
         if (!o.dp.prepacked) {
-            a.wp = scratch;
-            e = launch_deconv_pack(a.w, scratch, a.Cin, a.Cout, a.CoP, o.dtype, st);
+            a.wp = ws.p;
+            e = launch_deconv_pack(a.w, ws.p, a.Cin, a.Cout, a.CoP, o.dtype, st);
         }
         if (e == hipSuccess && o.dp.all) {
             if (o.dp.x_copy) {
-                void *xs = reinterpret_cast<char *>(scratch) + o.dp.x_off;
+                void *xs = ws.p + o.dp.x_off;
                 e = launch_nchw_to_nhwc(a.x, xs, a.N, a.Cin, a.H * a.W, o.dtype, st);
                 a.x = xs;
             }
@@ -1008,27 +983,16 @@ int launch_op(const OpPlan &o, hipStream_t st) {
     case CONV2D_OP_UPSAMPLE_CONCAT:
         e = launch_concat(o.x, o.b, o.y, o.N, o.H, o.W, o.Ca, o.Cb, o.up, nchw, o.dtype, o.vec, st);
         return e == hipSuccess ? CONV2D_OK : hip_fail(e, "upsample/concat launch");
-    case CONV2D_OP_AVGPOOL_CONV1X1: {
-        float *scratch = nullptr;
-        int rc = get_scratch(&scratch);
-        if (rc) return rc;
-        void *w2 = reinterpret_cast<char *>(scratch) + o.w_off;
-        e = launch_pool_weights(o.w1, w2, o.a.Cout, o.a.Cin, nchw, o.dtype, st);
-        if (e != hipSuccess) return hip_fail(e, "avgpool2x2_conv1x1 launch");
-        ConvArgs a = o.a;
-        a.w = w2;
-        return launch_conv(a, o.plan, o.layout, o.dtype, st);
-    }
     default:
         return set_error(CONV2D_EINVAL, "unknown op kind %d", o.kind);
     }
 }
 
-int run_one(const conv2d_op &op, int layout, int dtype, void *stream) {
+int run_one(const conv2d_op &op, int layout, int dtype, void *stream, const Workspace &ws) {
     OpPlan o{};
-    int rc = check_op(op, layout, dtype, &o);
+    int rc = check_op(op, layout, dtype, ws.bytes, &o);
     if (rc) return rc;
-    rc = launch_op(o, static_cast<hipStream_t>(stream));
+    rc = launch_op(o, ws, static_cast<hipStream_t>(stream));
     return rc ? rc : set_ok();
 }
 
@@ -1064,12 +1028,6 @@ int describe_op(const OpPlan &o, char *buf, int cap) {
         else
             snprintf(tmp, sizeof tmp, "deconv4x4s2_direct %s%s", dtype_name(o.dtype), o.dp.out_f32 ? " out f32" : "");
         break;
-    case CONV2D_OP_AVGPOOL_CONV1X1: {
-        char inner[160];
-        describe(o.plan, o.layout, o.dtype, inner, sizeof inner);
-        snprintf(tmp, sizeof tmp, "pool_weights+%s", inner);
-        break;
-    }
     case CONV2D_OP_UPSAMPLE:
     case CONV2D_OP_CONCAT:
     case CONV2D_OP_UPSAMPLE_CONCAT:
@@ -1106,7 +1064,7 @@ int tune_run(int N, int H, int W, int Cin, int Cout, int kh, int kw, int stride,
         const void *px = (const void *)(uintptr_t)0x100000000ull, *pw = (const void *)(uintptr_t)0x900000000ull;
         const void *py = (const void *)(uintptr_t)0x1100000000ull, *pr = (const void *)(uintptr_t)0x1900000000ull;
         const float *pa = (const float *)(uintptr_t)0x2100000000ull;
-        int rc = check_conv(px, pw, pa, has_residual ? pr : nullptr, py, N, H, W, Cin, Cout, kh, kw, stride, pad, act,
+        int rc = check_conv(px, pw, nullptr, pa, has_residual ? pr : nullptr, py, N, H, W, Cin, Cout, kh, kw, stride, pad, act,
                             layout, dtype, &t);
         if (rc) return rc;
     }
@@ -1124,12 +1082,15 @@ int tune_run(int N, int H, int W, int Cin, int Cout, int kh, int kw, int stride,
         if (e != hipSuccess) return hip_fail(e, "conv2d_tune buffers");
     }
     ConvArgs a{};
-    int rc = check_conv(b.p[0], b.p[1], (const float *)b.p[5], b.p[3], b.p[2], N, H, W, Cin, Cout, kh, kw, stride,
+    int rc = check_conv(b.p[0], b.p[1], (const float *)b.p[4], (const float *)b.p[5], b.p[3], b.p[2], N, H, W, Cin, Cout, kh, kw, stride,
                         pad, act, layout, dtype, &a);
     if (rc) return rc;
     a.bias = (const float *)b.p[4];
     if (a.act != CONV2D_ACT_PRELU) a.alpha = nullptr;
-    const Plan def = make_plan_default(a, layout, dtype);
+    // the candidates are the variants this thread's workspace allows (the same the
+    // planner may later pick from for calls with that workspace)
+    const Workspace ws = current_ws();
+    const Plan def = make_plan_default(a, layout, dtype, ws.bytes);
     std::vector<Plan> cands;
     cands.push_back(def);
     if (def.family == FAM_NCHW_VIA_NHWC) {
@@ -1151,19 +1112,16 @@ int tune_run(int N, int H, int W, int Cin, int Cout, int kh, int kw, int stride,
         }
         for (int tile = 0; tile < NHWC_TILE_COUNT; ++tile)
             for (int sp : {1, 2, 3, 4}) {
-                if (!splits_ok(a, sp)) continue;
+                if (!splits_ok(a, sp, ws.bytes)) continue;
                 Plan c{};
                 c.family = FAM_NHWC;
-                c.nh = plan_nhwc(a);
+                c.nh = plan_nhwc(a, ws.bytes);
                 c.nh.tile = tile;
                 c.nh.splits = sp;
                 cands.push_back(c);
             }
     }
     // everything the launches need, fetched before timing
-    float *scratch = nullptr;
-    rc = get_scratch(&scratch);
-    if (rc) return rc;
     int cus = 0;
     rc = device_cus(&cus);
     if (rc) return rc;
@@ -1176,14 +1134,15 @@ int tune_run(int N, int H, int W, int Cin, int Cout, int kh, int kw, int stride,
     int best = -1;
     float best_ms = 0.0f;
     for (size_t i = 0; i < cands.size() && e == hipSuccess; ++i) {
-        for (int w = 0; w < 2 && rc == CONV2D_OK; ++w) rc = launch_conv(a, cands[i], layout, dtype, st);
+        for (int w = 0; w < 2 && rc == CONV2D_OK; ++w) rc = launch_conv(a, cands[i], layout, dtype, ws, st);
         if (rc) break;
         // the GPU idles while the host queues the timed launches (about 30 us of host
         // time each, more under a profiler), so host-side cost stays out of the timing
         e = launch_idle(std::min(4096, 8 + reps * 12), st);
         if (e != hipSuccess) break;
         e = hipEventRecord(e0, st);
-        for (int r = 0; r < reps && rc == CONV2D_OK && e == hipSuccess; ++r) rc = launch_conv(a, cands[i], layout, dtype, st);
+        for (int r = 0; r < reps && rc == CONV2D_OK && e == hipSuccess; ++r)
+            rc = launch_conv(a, cands[i], layout, dtype, ws, st);
         if (rc || e != hipSuccess) break;
         e = hipEventRecord(e1, st);
         if (e == hipSuccess) e = hipEventSynchronize(e1);
@@ -1221,7 +1180,7 @@ int tune_run(int N, int H, int W, int Cin, int Cout, int kh, int kw, int stride,
 
 extern "C" {
 
-int conv2d_abi_version(void) { return 7; }
+int conv2d_abi_version(void) { return 8; }
 
 const char *conv2d_last_error(void) { return g_err.c_str(); }
 
@@ -1231,11 +1190,10 @@ int conv2d_check_args(const void *x, const void *w, const float *bias, const flo
                       const void *residual, const void *y, int N, int H, int W, int Cin,
                       int Cout, int kh, int kw, int stride, int pad, int act, int layout,
                       int dtype) {
-    (void)bias;
     ConvArgs a{};
-    int rc = check_conv(x, w, alpha, residual, y, N, H, W, Cin, Cout, kh, kw, stride, pad, act,
+    int rc = check_conv(x, w, bias, alpha, residual, y, N, H, W, Cin, Cout, kh, kw, stride, pad, act,
                         layout, dtype, &a);
-    if (!rc && a.w_ohwi) rc = check_w_ohwi(a, make_plan(a, layout, dtype));
+    if (!rc && a.w_ohwi) rc = check_w_ohwi(a, make_plan(a, layout, dtype, current_ws().bytes));
     return rc ? rc : set_ok();
 }
 
@@ -1247,10 +1205,10 @@ int conv2d_plan(int N, int H, int W, int Cin, int Cout, int kh, int kw, int stri
     const void *py = (const void *)(uintptr_t)0x1100000000ull;
     const float *pa = (const float *)(uintptr_t)0x1900000000ull;
     ConvArgs a{};
-    int rc = check_conv(px, pw, pa, nullptr, py, N, H, W, Cin, Cout, kh, kw, stride, pad, act,
+    int rc = check_conv(px, pw, nullptr, pa, nullptr, py, N, H, W, Cin, Cout, kh, kw, stride, pad, act,
                         layout, dtype, &a);
     if (rc) return rc;
-    const Plan pl = make_plan(a, layout, dtype);
+    const Plan pl = make_plan(a, layout, dtype, current_ws().bytes);
     rc = check_w_ohwi(a, pl);
     if (rc) return rc;
     set_ok();
@@ -1261,7 +1219,7 @@ int conv2d_fused(const void *x, const void *w, const float *bias, const float *a
                  const void *residual, void *y, int N, int H, int W, int Cin, int Cout, int kh,
                  int kw, int stride, int pad, int act, int layout, int dtype, void *stream) {
     const conv2d_op op{CONV2D_OP_CONV, x, w, bias, alpha, residual, y, N, H, W, Cin, Cout, kh, kw, stride, pad, act};
-    return run_one(op, layout, dtype, stream);
+    return run_one(op, layout, dtype, stream, current_ws());
 }
 
 int conv2d_fused_maxpool3x3s2(const void *x, const void *w, const float *bias, const float *alpha, void *y,
@@ -1269,7 +1227,7 @@ int conv2d_fused_maxpool3x3s2(const void *x, const void *w, const float *bias, c
                               int act, int layout, int dtype, void *stream) {
     const conv2d_op op{CONV2D_OP_CONV_MAXPOOL, x, w, bias, alpha, nullptr, y, N, H, W, Cin, Cout, kh, kw,
                        stride, pad, act};
-    return run_one(op, layout, dtype, stream);
+    return run_one(op, layout, dtype, stream, current_ws());
 }
 
 int conv2d_fused_maxpool_plan(int N, int H, int W, int Cin, int Cout, int kh, int kw, int stride, int pad,
@@ -1281,7 +1239,7 @@ int conv2d_fused_maxpool_plan(int N, int H, int W, int Cin, int Cout, int kh, in
     const conv2d_op op{CONV2D_OP_CONV_MAXPOOL, px, pw, nullptr, pa, nullptr, py, N, H, W, Cin, Cout, kh, kw,
                        stride, pad, act};
     OpPlan o{};
-    int rc = check_op(op, layout, dtype, &o);
+    int rc = check_op(op, layout, dtype, current_ws().bytes, &o);
     if (rc) return rc;
     set_ok();
     return describe_op(o, buf, cap);
@@ -1290,13 +1248,13 @@ int conv2d_fused_maxpool_plan(int N, int H, int W, int Cin, int Cout, int kh, in
 int maxpool3x3s2(const void *x, void *y, int N, int H, int W, int C, int layout, int dtype,
                  void *stream) {
     const conv2d_op op{CONV2D_OP_MAXPOOL, x, nullptr, nullptr, nullptr, nullptr, y, N, H, W, C, C, 3, 3, 2, 1, 0};
-    return run_one(op, layout, dtype, stream);
+    return run_one(op, layout, dtype, stream, current_ws());
 }
 
 int avgpool2x2(const void *x, void *y, int N, int H, int W, int C, int layout, int dtype,
                void *stream) {
     const conv2d_op op{CONV2D_OP_AVGPOOL, x, nullptr, nullptr, nullptr, nullptr, y, N, H, W, C, C, 2, 2, 2, 0, 0};
-    return run_one(op, layout, dtype, stream);
+    return run_one(op, layout, dtype, stream, current_ws());
 }
 
 int conv_transpose4x4s2(const void *x, const void *w, const float *bias, const float *alpha, void *y, int N, int H,
@@ -1305,9 +1263,11 @@ int conv_transpose4x4s2(const void *x, const void *w, const float *bias, const f
     o.kind = CONV2D_OP_DECONV;
     o.layout = layout;
     o.dtype = dtype;
-    int rc = check_deconv(x, w, bias, alpha, y, N, H, W, Cin, Cout, act, layout, dtype, out_dtype, &o.da, &o.dp);
+    const Workspace ws = current_ws();
+    int rc = check_deconv(x, w, bias, alpha, y, N, H, W, Cin, Cout, act, layout, dtype, out_dtype, ws.bytes, &o.da,
+                          &o.dp);
     if (rc) return rc;
-    rc = launch_op(o, static_cast<hipStream_t>(stream));
+    rc = launch_op(o, ws, static_cast<hipStream_t>(stream));
     return rc ? rc : set_ok();
 }
 
@@ -1344,9 +1304,11 @@ int conv_transpose4x4s2_prepacked(const void *x, const void *wp, const float *bi
     o.kind = CONV2D_OP_DECONV;
     o.layout = layout;
     o.dtype = dtype;
-    int rc = check_deconv(x, wp, bias, alpha, y, N, H, W, Cin, Cout, act, layout, dtype, out_dtype, &o.da, &o.dp, true);
+    const Workspace ws = current_ws();
+    int rc = check_deconv(x, wp, bias, alpha, y, N, H, W, Cin, Cout, act, layout, dtype, out_dtype, ws.bytes, &o.da,
+                          &o.dp, true);
     if (rc) return rc;
-    rc = launch_op(o, static_cast<hipStream_t>(stream));
+    rc = launch_op(o, ws, static_cast<hipStream_t>(stream));
     return rc ? rc : set_ok();
 }
 
@@ -1360,7 +1322,8 @@ int conv_transpose4x4s2_plan(int N, int H, int W, int Cin, int Cout, int act, in
     const void *pw = (const void *)(uintptr_t)0x900000000ull;
     const void *py = (const void *)(uintptr_t)0x1100000000ull;
     const float *pa = (const float *)(uintptr_t)0x1900000000ull;
-    int rc = check_deconv(px, pw, nullptr, pa, py, N, H, W, Cin, Cout, act, layout, dtype, out_dtype, &o.da, &o.dp);
+    int rc = check_deconv(px, pw, nullptr, pa, py, N, H, W, Cin, Cout, act, layout, dtype, out_dtype,
+                          current_ws().bytes, &o.da, &o.dp);
     if (rc) return rc;
     set_ok();
     return describe_op(o, buf, cap);
@@ -1368,19 +1331,19 @@ int conv_transpose4x4s2_plan(int N, int H, int W, int Cin, int Cout, int act, in
 
 int upsample_nearest2x(const void *x, void *y, int N, int H, int W, int C, int layout, int dtype, void *stream) {
     const conv2d_op op{CONV2D_OP_UPSAMPLE, x, nullptr, nullptr, nullptr, nullptr, y, N, H, W, C, 0, 0, 0, 0, 0, 0};
-    return run_one(op, layout, dtype, stream);
+    return run_one(op, layout, dtype, stream, current_ws());
 }
 
 int concat_channels(const void *a, const void *b, void *y, int N, int H, int W, int Ca, int Cb, int layout, int dtype,
                     void *stream) {
     const conv2d_op op{CONV2D_OP_CONCAT, a, nullptr, nullptr, nullptr, b, y, N, H, W, Ca, Cb, 0, 0, 0, 0, 0};
-    return run_one(op, layout, dtype, stream);
+    return run_one(op, layout, dtype, stream, current_ws());
 }
 
 int upsample2x_concat(const void *a, const void *b, void *y, int N, int H, int W, int Ca, int Cb, int layout,
                       int dtype, void *stream) {
     const conv2d_op op{CONV2D_OP_UPSAMPLE_CONCAT, a, nullptr, nullptr, nullptr, b, y, N, H, W, Ca, Cb, 0, 0, 0, 0, 0};
-    return run_one(op, layout, dtype, stream);
+    return run_one(op, layout, dtype, stream, current_ws());
 }
 
 int conv2d_tune(int N, int H, int W, int Cin, int Cout, int kh, int kw, int stride, int pad, int act, int has_residual,
@@ -1455,12 +1418,6 @@ int conv2d_tune_clear(void) {
     return set_ok();
 }
 
-int conv2d_avgpool2x2_conv1x1(const void *x, const void *w, const float *bias, const float *alpha, void *y, int N,
-                              int H, int W, int Cin, int Cout, int act, int layout, int dtype, void *stream) {
-    const conv2d_op op{CONV2D_OP_AVGPOOL_CONV1X1, x, w, bias, alpha, nullptr, y, N, H, W, Cin, Cout, 1, 1, 1, 0, act};
-    return run_one(op, layout, dtype, stream);
-}
-
 int conv2d_weights_to_ohwi(const void *w, void *w2, int Cout, int Cin, int kh, int kw, int dtype, void *stream) {
     if (!w || !w2) return set_error(CONV2D_EINVAL, "conv2d_weights_to_ohwi: w and w2 must not be null");
     if (Cout <= 0 || Cin <= 0 || kh <= 0 || kw <= 0)
@@ -1478,14 +1435,14 @@ int conv2d_weights_to_ohwi(const void *w, void *w2, int Cout, int Cin, int kh, i
 int conv2d_stack_check(const conv2d_op *ops, int n, int layout, int dtype, int *bad_index) {
     if (bad_index) *bad_index = -1;
     std::vector<OpPlan> plans;
-    int rc = check_stack(ops, n, layout, dtype, &plans, bad_index);
+    int rc = check_stack(ops, n, layout, dtype, current_ws().bytes, &plans, bad_index);
     return rc ? rc : set_ok();
 }
 
 int conv2d_stack_plan(const conv2d_op *ops, int n, int layout, int dtype, int index, char *buf, int cap) {
     std::vector<OpPlan> plans;
     int bad = -1;
-    int rc = check_stack(ops, n, layout, dtype, &plans, &bad);
+    int rc = check_stack(ops, n, layout, dtype, current_ws().bytes, &plans, &bad);
     if (rc) return rc;
     if (index < 0 || index >= n) return set_error(CONV2D_EINVAL, "op index %d outside the stack of %d", index, n);
     set_ok();
@@ -1495,13 +1452,14 @@ int conv2d_stack_plan(const conv2d_op *ops, int n, int layout, int dtype, int in
 int conv2d_stack_run(const conv2d_op *ops, int n, int layout, int dtype, void *stream) {
     std::vector<OpPlan> plans;
     int bad = -1;
-    int rc = check_stack(ops, n, layout, dtype, &plans, &bad);
+    const Workspace ws = current_ws();
+    int rc = check_stack(ops, n, layout, dtype, ws.bytes, &plans, &bad);
     if (rc) return rc;
     rc = prepare_stack(plans);
     if (rc) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
     for (int i = 0; i < n; ++i) {
-        rc = launch_op(plans[(size_t)i], st);
+        rc = launch_op(plans[(size_t)i], ws, st);
         if (rc) return set_error(rc, "op %d: %s", i, g_err.c_str());
     }
     return set_ok();
@@ -1518,9 +1476,11 @@ int conv2d_stack_graph_create(const conv2d_op *ops, int n, int layout, int dtype
     *out = nullptr;
     std::vector<OpPlan> plans;
     int bad = -1;
-    int rc = check_stack(ops, n, layout, dtype, &plans, &bad);
+    // the graph keeps the workspace set now: its replays use that memory
+    const Workspace ws = current_ws();
+    int rc = check_stack(ops, n, layout, dtype, ws.bytes, &plans, &bad);
     if (rc) return rc;
-    // everything that may allocate or query the device happens before the capture
+    // everything that queries the device happens before the capture
     rc = prepare_stack(plans);
     if (rc) return rc;
     hipStream_t cs = nullptr;
@@ -1534,7 +1494,7 @@ int conv2d_stack_graph_create(const conv2d_op *ops, int n, int layout, int dtype
     int lrc = CONV2D_OK;
     std::string lerr;
     for (int i = 0; i < n && lrc == CONV2D_OK; ++i) {
-        lrc = launch_op(plans[(size_t)i], cs);
+        lrc = launch_op(plans[(size_t)i], ws, cs);
         if (lrc) lerr = "op " + std::to_string(i) + ": " + g_err;
     }
     hipGraph_t g = nullptr;
@@ -1575,6 +1535,52 @@ int conv2d_stack_graph_destroy(conv2d_graph *g) {
     delete g;
     if (e1 != hipSuccess) return hip_fail(e1, "hipGraphExecDestroy");
     if (e2 != hipSuccess) return hip_fail(e2, "hipGraphDestroy");
+    return set_ok();
+}
+
+int conv2d_set_workspace(void *p, size_t bytes) {
+    if (!p && bytes) return set_error(CONV2D_EINVAL, "conv2d_set_workspace: a null workspace must have 0 bytes");
+    if (((uintptr_t)p & 255u) != 0) return set_error(CONV2D_EINVAL, "conv2d_set_workspace: p must be 256-byte aligned");
+    const int dev = ws_slot();
+    if (dev < 0 || dev >= kMaxDevices) return set_error(CONV2D_EHIP, "device index %d out of range", dev);
+    g_ws[dev] = Workspace{static_cast<char *>(p), p ? bytes : 0};
+    return CONV2D_OK;  // a setter: the thread's last error stays as it was
+}
+
+int conv2d_workspace_size(int N, int H, int W, int Cin, int Cout, int kh, int kw, int stride, int pad, int act,
+                          int layout, int dtype, size_t *bytes) {
+    if (!bytes) return set_error(CONV2D_EINVAL, "conv2d_workspace_size: bytes must not be null");
+    const void *px = (const void *)(uintptr_t)0x100000000ull;
+    const void *pw = (const void *)(uintptr_t)0x900000000ull;
+    void *py = (void *)(uintptr_t)0x1100000000ull;
+    const float *pa = (const float *)(uintptr_t)0x1900000000ull;
+    const conv2d_op op{CONV2D_OP_CONV, px, pw, nullptr, pa, nullptr, py, N, H, W, Cin, Cout, kh, kw, stride, pad, act};
+    OpPlan o{};
+    int rc = check_op(op, layout, dtype, kUnlimitedWs, &o);
+    if (rc) return rc;
+    *bytes = ws_need(o);
+    return set_ok();
+}
+
+int conv2d_stack_workspace_size(const conv2d_op *ops, int n, int layout, int dtype, size_t *bytes) {
+    if (!bytes) return set_error(CONV2D_EINVAL, "conv2d_stack_workspace_size: bytes must not be null");
+    std::vector<OpPlan> plans;
+    int bad = -1;
+    int rc = check_stack(ops, n, layout, dtype, kUnlimitedWs, &plans, &bad);
+    if (rc) return rc;
+    // chained convs use two halves, each holding an input or output copy; the other ops
+    // use the workspace from its start
+    size_t need = 0, half = 0;
+    for (const OpPlan &o : plans) {
+        if (o.kind == CONV2D_OP_CONV && (o.plan.chain_in || o.plan.chain_out)) {
+            const int eb = dtype_bytes(o.dtype);
+            half = std::max(half, round256((size_t)o.a.N * o.a.H * o.a.W * o.a.Cin * eb));
+            half = std::max(half, round256((size_t)o.a.M * o.a.Cout * eb));
+        } else {
+            need = std::max(need, ws_need(o));
+        }
+    }
+    *bytes = std::max(need, 2 * half);
     return set_ok();
 }
 

@@ -149,10 +149,6 @@ hipError_t launch_oihw_to_ohwi(const void *w, void *w2, int Cout, int Cin, int t
 // and HW are multiples of 8 and both pointers are 16-byte aligned).
 hipError_t launch_nchw_to_nhwc(const void *x, void *y, int N, int C, int HW, int dtype, hipStream_t st);
 
-// w [Cout][Cin] (a 1x1 conv) -> the 2x2 stride-2 weights w/4 on every tap, OHWI
-// (channel-last) or OIHW (nchw): an average pool 2x2 then this 1x1 conv is that conv.
-hipError_t launch_pool_weights(const void *w, void *w2, int Cout, int Cin, bool nchw, int dtype, hipStream_t st);
-
 // Any layout and type, one thread per output (weights in the caller's layout).
 hipError_t launch_deconv_direct(const DeconvArgs &a, int dtype, bool out_f32, bool nchw, hipStream_t st);
 

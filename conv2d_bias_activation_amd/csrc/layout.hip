@@ -100,43 +100,6 @@ static hipError_t to_nhwc_t(const void *x, void *y, int N, int C, int HW, const 
                          static_cast<const T *>(w), static_cast<T *>(w2), Cout, C, taps);
 }
 
-// The 2x2 stride-2 weights of an average pool followed by a 1x1 conv: every tap of
-// w2[co] is w[co] / 4 (exact scaling; in f16 a quarter of a weight under 2^-12 lands in
-// the subnormal range and keeps fewer bits). w [Cout][Cin] -> w2 [Cout][2][2][Cin]
-// (channel-last, OHWI) or [Cout][Cin][2][2] (channel-first, OIHW). One thread per weight.
-template <typename T>
-__global__ __launch_bounds__(256) void pool_weights_kernel(const T *__restrict__ w, T *__restrict__ w2, int Cout,
-                                                           int Cin, int nchw) {
-    const int i = blockIdx.x * 256 + threadIdx.x;
-    if (i >= Cout * Cin) return;
-    const int co = i / Cin, ci = i - co * Cin;
-    const T v = from_f32<T>(to_f32(w[i]) * 0.25f);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        if (nchw)
-            w2[(size_t)i * 4 + t] = v;
-        else
-            w2[((size_t)co * 4 + t) * Cin + ci] = v;
-    }
-}
-
-hipError_t launch_pool_weights(const void *w, void *w2, int Cout, int Cin, bool nchw, int dtype, hipStream_t st) {
-    const dim3 grid((unsigned)(((long long)Cout * Cin + 255) / 256));
-    switch (dtype) {
-    case CONV2D_DTYPE_F32:
-        return launch_kernel(pool_weights_kernel<float>, grid, dim3(256), 0, st, static_cast<const float *>(w),
-                             static_cast<float *>(w2), Cout, Cin, nchw ? 1 : 0);
-    case CONV2D_DTYPE_BF16:
-        return launch_kernel(pool_weights_kernel<bf16>, grid, dim3(256), 0, st, static_cast<const bf16 *>(w),
-                             static_cast<bf16 *>(w2), Cout, Cin, nchw ? 1 : 0);
-    case CONV2D_DTYPE_F16:
-        return launch_kernel(pool_weights_kernel<f16>, grid, dim3(256), 0, st, static_cast<const f16 *>(w),
-                             static_cast<f16 *>(w2), Cout, Cin, nchw ? 1 : 0);
-    default:
-        return hipErrorInvalidValue;
-    }
-}
-
 hipError_t launch_nchw_to_nhwc(const void *x, void *y, int N, int C, int HW, int dtype, hipStream_t st) {
     dim3 grid((HW + 63) / 64, (C + 63) / 64, N);
     const bool vec = (C % 8) == 0 && (HW % 8) == 0 && (((uintptr_t)x | (uintptr_t)y) & 15) == 0;

@@ -21,20 +21,27 @@
  *    the last error on the calling thread is returned by conv2d_last_error().
  *  - Tensors are dense and contiguous. Every tensor must hold fewer than 2^31
  *    elements (CONV2D_EUNSUPPORTED otherwise).
- *  - The output may not overlap the input or the residual (CONV2D_EINVAL).
- *  - State kept between calls: the last-error message (per thread), the compute
- *    unit count of each device (queried once), and, per device, one 64 MiB
- *    scratch buffer that the library allocates on the first call that needs it
- *    and keeps until the process ends. It holds the fp32 partial sums of split-K
- *    calls, the channel-last copies of x and w of 16-bit channel-first calls and
- *    the unpooled conv output of conv2d_fused_maxpool3x3s2 calls that run as two
- *    kernels, and the repacked weights (and, for channel-first inputs whose width is
- *    not a multiple of 8, the channel-last copy of x) of conv_transpose4x4s2 calls on
- *    the matrix cores.
- *    Such calls on one device all use that buffer: callers that run conv2d_fused
- *    on several streams of one device at the same time must serialise those
- *    calls. (Under HIP graph capture, make one call on each device before
- *    capturing, so the allocation does not happen inside the capture.)
+ *  - The output may not overlap any input: x, w, bias, alpha or the residual
+ *    (CONV2D_EINVAL).
+ *  - The library allocates no device memory (conv2d_tune aside, which allocates and
+ *    frees its own timing buffers). Some kernel variants need device scratch memory
+ *    (split-K fp32 partial sums, channel-last copies of a channel-first layer's input
+ *    and weights, the unpooled output of a conv + max pool that runs as two kernels,
+ *    the repacked weights of a transposed conv). It comes from a caller-owned
+ *    WORKSPACE registered with conv2d_set_workspace for the calling thread and the
+ *    current device; it replaces the library-reserved scratch arena that the
+ *    rlx-wgpu page sizes with `compute_scratch_bytes`. Calls plan their kernels for
+ *    the workspace registered when they are made: without one, or with one too small,
+ *    they take a variant that needs none (no split-K; channel-first layers on the
+ *    general kernel; the transposed conv on the vector ALUs) and return
+ *    CONV2D_EUNSUPPORTED only where no such variant exists (said per call below).
+ *    conv2d_workspace_size and conv2d_stack_workspace_size report how much the
+ *    preferred variants use. Two calls that may run at the same time (on two streams)
+ *    must not share a workspace; a call reads and writes its workspace only on its own
+ *    stream, in its own launches, so calls queued on one stream may share one.
+ *  - Other state kept between calls: the last-error message (per thread), the
+ *    compute-unit count and arch name of each device (queried once), the registered
+ *    workspaces (per thread and device) and the tuned-plan table (conv2d_tune).
  */
 #ifndef CONV2D_FUSED_H
 #define CONV2D_FUSED_H
@@ -79,8 +86,8 @@ extern "C" {
  * in OHWI order [Cout][kh][kw][Cin] instead of OIHW, e.g. converted once at model load by
  * conv2d_weights_to_ohwi (weight residency: such a layer then copies only its input to
  * channel-last form per call). Only for 16-bit layers with Cin % 8 == 0 whose input copy
- * fits the library scratch (CONV2D_EUNSUPPORTED otherwise); not accepted by
- * conv2d_fused_maxpool3x3s2 or conv2d_avgpool2x2_conv1x1 (CONV2D_EINVAL). */
+ * fits the workspace (CONV2D_EUNSUPPORTED otherwise); not accepted by
+ * conv2d_fused_maxpool3x3s2 (CONV2D_EINVAL). */
 #define CONV2D_WEIGHTS_OHWI 0x200
 
 /* Status codes. */
@@ -90,8 +97,7 @@ extern "C" {
                                    PRELU without alpha, output overlapping an input */
 #define CONV2D_EUNSUPPORTED (-2) /* valid but not handled (a tensor of 2^31 or more
                                    elements) */
-#define CONV2D_EHIP (-3)        /* the HIP runtime failed (no device, launch failure,
-                                   scratch allocation failure) */
+#define CONV2D_EHIP (-3)        /* the HIP runtime failed (no device, launch failure) */
 
 /*
  * y = epilogue(conv(x, w)) for one layer.
@@ -114,11 +120,12 @@ extern "C" {
  * stream   hipStream_t or NULL
  *
  * Accumulation is fp32 in any order; the result is rounded once to `dtype`.
- * Layers with a deep K and few output tiles run as split-K: fp32 partial sums of
- * K slices go to the library's per-device scratch buffer and a second kernel adds
- * them in slice order and applies the epilogue. 16-bit channel-first layers with
- * Cin % 8 == 0 are first copied to channel-last form in that buffer. (Either
- * returns CONV2D_EHIP if the one-time scratch allocation fails.)
+ * With a workspace (conv2d_set_workspace) of the size conv2d_workspace_size reports,
+ * layers with a deep K and few output tiles may run as split-K (fp32 partial sums of
+ * K slices in the workspace, added in slice order by a second kernel that applies the
+ * epilogue), and 16-bit channel-first layers with Cin % 8 == 0 are first copied to
+ * channel-last form there. Without it they run as one kernel on the caller's tensors;
+ * the result differs only by fp32 accumulation order.
  */
 int conv2d_fused(const void *x, const void *w, const float *bias, const float *alpha,
                  const void *residual, void *y, int N, int H, int W, int Cin, int Cout, int kh,
@@ -147,14 +154,15 @@ int maxpool3x3s2(const void *x, void *y, int N, int H, int W, int C, int layout,
  * except y: [N,PH,PW,Cout] or [N,Cout,PH,PW] in `dtype` with PH = (OH - 1)/2 + 1,
  * PW = (OW - 1)/2 + 1 and OH, OW the conv's output size. y may not overlap x.
  *
- * The max is taken on the activated fp32 values and then rounded; rounding is
- * monotone, so this equals rounding first and pooling after. Channel-last 16-bit
- * 3-channel 3x3 pad-1 convs (Cout <= 64, Cout % 8 == 0, W % 8 == 0, W <= 3000, x and
- * y 16-byte aligned) run as one kernel that keeps the conv output on chip. Any
- * other shape runs the conv into the library's per-device scratch buffer and then
- * the pool kernel; that needs N*OH*OW*Cout elements of `dtype` to fit the 64 MiB
- * buffer (CONV2D_EUNSUPPORTED otherwise), and it shares the buffer as conv2d_fused
- * does.
+ * The max is taken on rounded values (rounding is monotone, so rounding first and
+ * pooling after gives the same bits), skipping NaN as maxpool3x3s2 does, so the result
+ * equals maxpool3x3s2(conv2d_fused(...)) bit for bit. Channel-last 16-bit 3-channel
+ * 3x3 pad-1 convs (Cout <= 64, Cout % 8 == 0, W % 8 == 0, W <= 3000, x and y 16-byte
+ * aligned) and channel-last 16-bit 3x3 stride-1 pad-1 convs with Cin 16 or 32 and
+ * Cout <= 64 run as one kernel that keeps the conv output on chip. Any other shape
+ * runs the conv into the workspace and then the pool kernel; that needs a workspace
+ * of N*OH*OW*Cout elements of `dtype` (rounded up to 256 bytes;
+ * CONV2D_EUNSUPPORTED otherwise).
  */
 int conv2d_fused_maxpool3x3s2(const void *x, const void *w, const float *bias, const float *alpha,
                               void *y, int N, int H, int W, int Cin, int Cout, int kh, int kw,
@@ -196,11 +204,10 @@ int avgpool2x2(const void *x, void *y, int N, int H, int W, int C, int layout, i
  *        (framecast keeps the deconv output in fp32 under f16 storage)
  *
  * Accumulation is fp32 in any order, rounded once to out_dtype. 16-bit inputs with
- * Cin % 8 == 0 (channel-last x 16-byte aligned) run on the matrix cores: the weights
- * are first repacked into the library's per-device scratch buffer
- * (16 * ceil(Cout/32)*32 * ceil(Cin/64)*64 elements, which must fit its 64 MiB); otherwise (and
- * for fp32) a direct kernel on the vector ALUs runs. Shares the scratch as
- * conv2d_fused does. Errors as conv2d_fused.
+ * Cin % 8 == 0 (channel-last x 16-byte aligned) run on the matrix cores when the
+ * workspace holds the repacked weights (16 * ceil(Cout/32)*32 * ceil(Cin/64)*64
+ * elements; conv_transpose4x4s2_pack does this once instead); otherwise (and for fp32)
+ * a direct kernel on the vector ALUs runs. Errors as conv2d_fused.
  */
 int conv_transpose4x4s2(const void *x, const void *w, const float *bias, const float *alpha, void *y, int N, int H,
                         int W, int Cin, int Cout, int act, int layout, int dtype, int out_dtype, void *stream);
@@ -218,8 +225,8 @@ int conv_transpose4x4s2(const void *x, const void *w, const float *bias, const f
  *   of w; needs 16-bit x with Cin % 8 == 0 (16-byte aligned when channel-last), x and wp
  *   under 2 GiB (CONV2D_EUNSUPPORTED otherwise). Results are bit-identical to
  *   conv_transpose4x4s2 on the unpacked weights. A channel-first input whose width is
- *   not a multiple of 8 (or that is not 16-byte aligned) still uses the library scratch
- *   for its channel-last copy; other calls write nothing but y.
+ *   not a multiple of 8 (or that is not 16-byte aligned) uses the workspace, when it
+ *   has room, for a channel-last copy of x; other calls write nothing but y.
  */
 int conv_transpose4x4s2_packed_bytes(int Cin, int Cout, int dtype, size_t *bytes);
 int conv_transpose4x4s2_pack(const void *w, void *wp, int Cin, int Cout, int dtype, void *stream);
@@ -257,28 +264,6 @@ int concat_channels(const void *a, const void *b, void *y, int N, int H, int W, 
 int upsample2x_concat(const void *a, const void *b, void *y, int N, int H, int W, int Ca, int Cb, int layout,
                       int dtype, void *stream);
 
-/*
- * y = act(conv1x1(avgpool2x2(x), w) + bias): the ResNet-D shortcut of a downsampling
- * block in one call (inferencelayer page, `encoder_maps`: the 2x2 average pool, then
- * the 1x1 projection conv, run there as `AVGPOOL_SRC` and a GEMM).
- *
- * x      [N,H,W,Cin] or [N,Cin,H,W] in `dtype`, H, W >= 2 (required)
- * w      the 1x1 conv's weights [Cout][Cin] in `dtype` ([Cout,1,1,Cin] or [Cout,Cin,1,1])
- * bias   fp32 [Cout] or NULL; alpha fp32 [Cout], required when act is PRELU
- * y      [N,H/2,W/2,Cout] or [N,Cout,H/2,W/2] (floor: an odd last row or column of x
- *        is dropped, as by avgpool2x2), may not overlap x
- * act    CONV2D_ACT_* (no residual flag)
- *
- * Computed as the 2x2 stride-2 conv whose every tap holds w/4 (written into the end of
- * the library's per-device scratch, Cout*4*Cin elements, then the conv kernels), so the
- * pooled map is neither rounded to `dtype` nor written: the result equals
- * conv2d_fused(avgpool2x2(x)) up to the pooled map's one rounding and fp32
- * accumulation order. (w/4 is exact, except that in f16 a quarter of a weight below
- * 2^-12 is subnormal.) Shares the scratch as conv2d_fused does; errors as conv2d_fused.
- */
-int conv2d_avgpool2x2_conv1x1(const void *x, const void *w, const float *bias, const float *alpha, void *y, int N,
-                              int H, int W, int Cin, int Cout, int act, int layout, int dtype, void *stream);
-
 /* w [Cout][Cin][kh][kw] (OIHW) -> w2 [Cout][kh][kw][Cin] (OHWI), 16-bit types, for
  * channel-first convs called with CONV2D_WEIGHTS_OHWI. w2 is a caller-owned device
  * buffer of the same size that may not overlap w; enqueued on `stream`. */
@@ -303,6 +288,33 @@ int conv2d_check_args(const void *x, const void *w, const float *bias, const flo
  * negative CONV2D_E* code for invalid arguments. */
 int conv2d_plan(int N, int H, int W, int Cin, int Cout, int kh, int kw, int stride, int pad,
                 int act, int layout, int dtype, char *buf, int cap);
+
+/*
+ * Registers the caller-owned workspace of the calling thread on the current device
+ * (hipSetDevice's device; device 0's entry on a host where no device can be queried,
+ * for the host-only planning calls): p, a device buffer of `bytes` bytes, 256-byte
+ * aligned, or
+ * NULL with bytes 0 to have none (the initial state). Replaces the library-reserved
+ * scratch of the rlx-wgpu page (`compute_scratch_bytes` sizes one arena for a whole
+ * network) with memory the caller allocates, e.g. torch.empty on the device.
+ *
+ * The library keeps only the pointer: it never frees the buffer, and the buffer must
+ * stay allocated until every call (and every stack graph) planned with it has finished
+ * on the GPU. Each later call from this thread on this device plans its kernels for
+ * this workspace (a call's variant may change with it; see conv2d_plan) and enqueues
+ * kernels that read and write it on the call's own stream. Calls that may run at the
+ * same time need distinct workspaces: register the one for a stream before each call
+ * on that stream (registering is a host-side store, cheap enough for every call).
+ * Host only. CONV2D_EINVAL for a misaligned p or a NULL p with bytes > 0; success
+ * leaves conv2d_last_error() as it was.
+ */
+int conv2d_set_workspace(void *p, size_t bytes);
+
+/* Host-only: *bytes = the workspace that conv2d_fused's preferred variant for this shape
+ * writes (0 when it needs none), with the tuned-plan table applied as for a call.
+ * Argument errors as conv2d_plan. */
+int conv2d_workspace_size(int N, int H, int W, int Cin, int Cout, int kh, int kw, int stride, int pad, int act,
+                          int layout, int dtype, size_t *bytes);
 
 /*
  * Stacks of layers: a list of ops run in order on one stream, like one call per op,
@@ -330,8 +342,6 @@ int conv2d_plan(int N, int H, int W, int Cin, int Cout, int kh, int kw, int stri
  *                           Cb = Cout)
  *   CONV2D_OP_UPSAMPLE_CONCAT upsample2x_concat(a = x, b = residual, y, N, H, W,
  *                           Ca = Cin, Cb = Cout)
- *   CONV2D_OP_AVGPOOL_CONV1X1 conv2d_avgpool2x2_conv1x1(x, w, bias, alpha, y, N, H, W,
- *                           Cin, Cout, act); residual must be NULL
  * Layout and dtype are shared by the whole stack.
  */
 #define CONV2D_OP_CONV 0
@@ -343,7 +353,6 @@ int conv2d_plan(int N, int H, int W, int Cin, int Cout, int kh, int kw, int stri
 #define CONV2D_OP_UPSAMPLE 6
 #define CONV2D_OP_CONCAT 7
 #define CONV2D_OP_UPSAMPLE_CONCAT 8
-#define CONV2D_OP_AVGPOOL_CONV1X1 9
 
 typedef struct conv2d_op {
     int kind;
@@ -365,20 +374,28 @@ int conv2d_stack_check(const conv2d_op *ops, int n, int layout, int dtype, int *
 /* Host-only: the kernel variants of op `index` of a stack, as conv2d_plan. */
 int conv2d_stack_plan(const conv2d_op *ops, int n, int layout, int dtype, int index, char *buf, int cap);
 
+/* Host-only: *bytes = the workspace the stack's preferred variants write (the largest op,
+ * or twice the largest copy of a chain of channel-first convs), as
+ * conv2d_workspace_size. Argument errors as conv2d_stack_check. */
+int conv2d_stack_workspace_size(const conv2d_op *ops, int n, int layout, int dtype, size_t *bytes);
+
 /* Validates the whole stack, then enqueues its ops in order on `stream`. Same memory
- * and scratch rules as the single calls. Consecutive channel-first 16-bit convs given
- * channel-last weights (CONV2D_WEIGHTS_OHWI), where one conv's y is the next one's x
- * with matching sizes and the first has no residual, are chained: the first also writes
- * its output channel-last into one half of the scratch and the next reads its input
- * from there instead of copying it (conv2d_stack_plan names show "+y_nhwc" and
- * "chained+"). The results are bit-identical to running the ops one call at a time. */
+ * and workspace rules as the single calls (the workspace registered now is used by
+ * every op). Consecutive channel-first 16-bit convs given channel-last weights
+ * (CONV2D_WEIGHTS_OHWI), where one conv's y is the next one's x with matching sizes
+ * and the first has no residual, are chained when each half of the workspace holds
+ * their input and output copies: the first also writes its output channel-last into
+ * one half of the workspace and the next reads its input from there instead of copying
+ * it (conv2d_stack_plan names show "+y_nhwc" and "chained+"). The results are
+ * bit-identical to running the ops one call at a time. */
 int conv2d_stack_run(const conv2d_op *ops, int n, int layout, int dtype, void *stream);
 
 /* Validates the stack and records it once into a HIP graph (stream capture on a
- * private stream; the scratch buffer, if an op needs it, is allocated before the
- * capture). The graph holds the ops' pointers and sizes as given: every replay runs
- * the same ops on the same buffers, which must stay allocated until the graph is
- * destroyed. *out receives an opaque handle (NULL on error). */
+ * private stream; nothing is allocated). The graph holds the ops' pointers and sizes as
+ * given and the workspace registered at creation: every replay runs the same ops on the
+ * same buffers and workspace, which must stay allocated until the graph is destroyed;
+ * replays that may overlap (on two streams) need two graphs made with two workspaces.
+ * *out receives an opaque handle (NULL on error). */
 typedef struct conv2d_graph conv2d_graph;
 int conv2d_stack_graph_create(const conv2d_op *ops, int n, int layout, int dtype, conv2d_graph **out);
 
@@ -396,8 +413,11 @@ int conv2d_stack_graph_destroy(conv2d_graph *g);
  * GEMM tile table is the static form of the same choice.
  *
  * conv2d_tune allocates its own inputs and output for the shape (zero-filled device
- * buffers; act, has_residual, layout and dtype as conv2d_fused's arguments would be),
- * times the built-in choice and, for shapes on the channel-last matrix-core kernels,
+ * buffers; act, has_residual, layout and dtype as conv2d_fused's arguments would be;
+ * this is the library's only device allocation), uses the calling thread's registered
+ * workspace for the variants that need one (only those it has room for are timed, so
+ * nothing else may use that workspace meanwhile), times the built-in choice and, for
+ * shapes on the channel-last matrix-core kernels,
  * every tile shape and split-K depth (1-4) of the implicit-GEMM kernel and the tile
  * heights of the halo kernel (for channel-first 16-bit layers, which run on that
  * kernel after a layout copy, every tile shape): each variant runs twice, then `reps` times between two
@@ -407,7 +427,7 @@ int conv2d_stack_graph_destroy(conv2d_graph *g);
  * compute units, N, H, W, Cin, Cout, kh, kw, stride, pad, layout, dtype, residual or
  * not). From then on conv2d_fused, the fused conv + max pool and the stacks (and
  * conv2d_plan, whose name then ends in " tuned") use it for that shape whenever the
- * variant is valid for the call (alignment, scratch size); otherwise they fall back
+ * variant is valid for the call (alignment, workspace size); otherwise they fall back
  * to the built-in choice. Not for use under HIP graph capture (it allocates and
  * synchronises). Writes the winner's name to buf (as conv2d_plan) and its average
  * launch time in microseconds to *best_us (if not NULL); returns the name's length or
@@ -435,7 +455,9 @@ int conv2d_tune_clear(void);
  * valid until the thread's next call into the library. */
 const char *conv2d_last_error(void);
 
-/* ABI version of this header: 7 (6 plus CONV2D_WEIGHTS_OHWI and conv2d_weights_to_ohwi; 6
+/* ABI version of this header: 8 (caller-owned workspace: conv2d_set_workspace and the
+ * size queries replace the library's own scratch; conv2d_avgpool2x2_conv1x1 and its op
+ * kind are gone; 7 added CONV2D_WEIGHTS_OHWI and conv2d_weights_to_ohwi; 6
  * added the transposed conv's weight packing calls; 5
  * added conv2d_avgpool2x2_conv1x1; 4 added the tuning calls; 3 added the transposed conv,
  * upsample and concat calls and their stack ops; 2 the stack calls and the fused conv +

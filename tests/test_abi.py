@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     for name in names:
         assert hasattr(lib, name), name
     assert names == set(c2d.SIGNATURES)
-    assert c2d._load().conv2d_abi_version() == 7
+    assert c2d._load().conv2d_abi_version() == 8
 
 
 def test_out_dim():
@@ -99,11 +99,11 @@ def test_conv_pool_plan_and_argument_checks():
     assert c2d.plan_maxpool(4, 160, 160, 64, 64, 3, 3, 1, 1, 1, 0, bf16).endswith("then maxpool3x3s2")
     assert c2d.plan_maxpool(1, 640, 640, 3, 32, 3, 3, 2, 1, 2, 0, f32).startswith("direct_nhwc")
     assert c2d.plan_maxpool(1, 640, 640, 3, 32, 3, 3, 2, 1, 2, 0, f32).endswith("then maxpool3x3s2")
-    # channel-first 16-bit layers keep the scratch for the conv output: the general kernel
+    # channel-first 16-bit layers leave the workspace to the conv output: the general kernel
     assert c2d.plan_maxpool(1, 17, 23, 40, 72, 3, 3, 2, 1, 1, 1, bf16).startswith("igemm_nchw")
     # split-K is turned off for the same reason
     assert "splitk=1" in c2d.plan_maxpool(1, 10, 10, 512, 512, 3, 3, 1, 1, 1, 0, bf16)
-    # an unpooled conv output over the 64 MiB scratch
+    # an unpooled conv output over the 64 MiB workspace
     with pytest.raises(c2d.Conv2dError) as e:
         c2d.plan_maxpool(4, 640, 640, 64, 64, 3, 3, 1, 1, 1, 0, bf16)
     assert e.value.code == c2d.EUNSUPPORTED
@@ -172,13 +172,13 @@ def test_deconv_plan_and_argument_checks():
     # past 256 input channels: 64-channel chunks through a double-buffered LDS ring
     assert c2d.plan_deconv(1, 16, 16, 264, 64, 1, nhwc, bf16) == "deconv4x4s2_pack+deconv4x4s2_mfma_nhwc bf16"
     assert c2d.plan_deconv(1, 16, 16, 512, 64, 1, nchw, bf16) == "deconv4x4s2_pack+deconv4x4s2_mfma_nchw bf16"
-    # a channel-first input whose channel-last copy does not fit the scratch beside the weights
+    # a channel-first input whose channel-last copy does not fit the workspace beside the weights
     assert c2d.plan_deconv(4, 512, 516, 64, 8, 0, nchw, bf16) == "deconv4x4s2_pack+deconv4x4s2_mfma_nchw bf16"
     # the same map with W % 8 == 0 needs no copy
     assert c2d.plan_deconv(4, 512, 512, 64, 8, 0, nchw, bf16) == "deconv4x4s2_pack+deconv4x4s2_mfma_all_nchw bf16"
     assert c2d.plan_deconv(1, 8, 8, 12, 8, 1, nhwc, bf16) == "deconv4x4s2_direct bf16"  # Cin % 8 != 0
     assert c2d.plan_deconv(1, 8, 8, 16, 8, 1, nhwc, f32) == "deconv4x4s2_direct f32"
-    # packed weights over the 64 MiB scratch: 16 * 2048 * 1024 bf16 = 64 MiB fits, one more
+    # packed weights over a 64 MiB workspace: 16 * 2048 * 1024 bf16 = 64 MiB fits, one more
     # output block or input chunk does not
     assert c2d.plan_deconv(1, 8, 8, 1024, 2048, 0, nhwc, bf16).startswith("deconv4x4s2_pack")
     assert c2d.plan_deconv(1, 8, 8, 1024, 2049, 0, nhwc, bf16).startswith("deconv4x4s2_direct")
@@ -263,31 +263,6 @@ def test_tune_table_file_round_trip(tmp_path):
     assert c2d.tune_save(str(out)) == 0
 
 
-def test_avgpool_conv1x1_plan_and_checks():
-    """Host only: the fused shortcut call validates like a 2x2 stride-2 conv, names its
-    kernels, never splits K (its weights sit at the end of the scratch) and rejects a
-    residual."""
-    G = 1 << 32
-    op = c2d.Op(c2d.OP_AVGPOOL_CONV1X1, G, 3 * G, None, None, None, 5 * G, 4, 160, 160, 64, 128, 1, 1, 1, 0, 0)
-    assert c2d.stack_check([op]) == (c2d.OK, -1)
-    name = c2d.stack_plan([op], 0)
-    assert name.startswith("pool_weights+igemm_nhwc_pipe") and "splitk=1" in name, name
-    deep = c2d.Op(c2d.OP_AVGPOOL_CONV1X1, G, 3 * G, None, None, None, 5 * G, 1, 8, 8, 2048, 512, 1, 1, 1, 0, 0)
-    assert "splitk=1" in c2d.stack_plan([deep], 0)
-    f32 = c2d.stack_plan([op], 0, dtype=c2d.DTYPE_F32)
-    assert f32.startswith("pool_weights+igemm_nhwc"), f32
-    nchw = c2d.stack_plan([op], 0, layout="nchw", dtype=c2d.DTYPE_F16)
-    assert nchw.startswith("pool_weights+to_nhwc+igemm_nhwc_pipe"), nchw
-    res = c2d.Op(c2d.OP_AVGPOOL_CONV1X1, G, 3 * G, None, None, 7 * G, 5 * G, 4, 160, 160, 64, 128, 1, 1, 1, 0, 0)
-    assert c2d.stack_check([res]) == (c2d.EINVAL, 0)
-    one = c2d.Op(c2d.OP_AVGPOOL_CONV1X1, G, 3 * G, None, None, None, 5 * G, 1, 1, 9, 8, 8, 1, 1, 1, 0, 0)
-    assert c2d.stack_check([one]) == (c2d.EINVAL, 0)   # H = 1: no 2x2 window
-    lib = c2d._load()
-    P = ctypes.c_void_p
-    assert lib.conv2d_avgpool2x2_conv1x1(P(G), P(3 * G), None, None, P(G + 64), 1, 8, 8, 16, 16, 0, 0,
-                                         c2d.DTYPE_BF16, None) == c2d.EINVAL  # y overlaps x
-
-
 def test_deconv_pack_sizes_and_checks():
     """Host only: packed sizes, and what the pack and pre-packed calls reject before launching."""
     lib = c2d._load()
@@ -317,7 +292,10 @@ def test_weights_ohwi_flag_checks():
     nchw, nhwc = c2d.LAYOUT_NCHW, c2d.LAYOUT_NHWC
     act = c2d.ACT_PRELU | c2d.WEIGHTS_OHWI
     assert c2d.plan(1, 68, 120, 240, 240, 3, 3, 1, 1, act, nchw, f16).startswith("x_to_nhwc+igemm_nhwc_pipe")
-    assert _check(layout=nchw, dtype=f16, Cin=16, act=c2d.ACT_RELU | c2d.WEIGHTS_OHWI) == c2d.OK
+    # the input's channel-last copy goes to the workspace: needed for this flag
+    assert _check(layout=nchw, dtype=f16, Cin=16, act=c2d.ACT_RELU | c2d.WEIGHTS_OHWI) == c2d.EUNSUPPORTED
+    with c2d._planning_workspace(1 << 20):
+        assert _check(layout=nchw, dtype=f16, Cin=16, act=c2d.ACT_RELU | c2d.WEIGHTS_OHWI) == c2d.OK
     assert _check(layout=nhwc, act=c2d.ACT_RELU | c2d.WEIGHTS_OHWI) == c2d.EINVAL            # channel-last layer
     assert _check(layout=nchw, dtype=f32, act=c2d.ACT_RELU | c2d.WEIGHTS_OHWI) == c2d.EUNSUPPORTED
     assert _check(layout=nchw, dtype=f16, Cin=12, act=c2d.ACT_RELU | c2d.WEIGHTS_OHWI) == c2d.EUNSUPPORTED
@@ -346,8 +324,6 @@ def test_no_device_returns_ehip_not_a_crash():
         "conv_transpose4x4s2": lambda: lib.conv_transpose4x4s2(P(G), P(9 * G), None, None, P(17 * G), 1, 8, 8, 16, 8,
                                                                0, 0, bf16, bf16, None),
         "upsample2x_concat": lambda: lib.upsample2x_concat(P(G), P(9 * G), P(17 * G), 1, 4, 4, 8, 8, 0, bf16, None),
-        "conv2d_avgpool2x2_conv1x1": lambda: lib.conv2d_avgpool2x2_conv1x1(P(G), P(9 * G), None, None, P(17 * G), 1,
-                                                                           8, 8, 16, 16, 0, 0, bf16, None),
     }
     for name, call in calls.items():
         assert call() == c2d.EHIP, name
@@ -392,3 +368,74 @@ def test_channel_first_chain_links():
     # the next conv reads another buffer
     n = names([conv(x, y0), conv(y1, y2)])
     assert not n[0].endswith(" +y_nhwc") and n[1].startswith("x_to_nhwc+"), n
+
+
+def test_workspace_registration_and_sizes():
+    """Host only: the caller-owned workspace. Registration checks its arguments; the size
+    queries report what the preferred variants write; planning without a workspace (or
+    with one too small) picks variants that need none, and rejects only what has none."""
+    lib = c2d._load()
+    P = ctypes.c_void_p
+    bf16, f16 = c2d.DTYPE_BF16, c2d.DTYPE_F16
+    nhwc, nchw = c2d.LAYOUT_NHWC, c2d.LAYOUT_NCHW
+    assert lib.conv2d_set_workspace(P(0x4000000010), 1 << 20) == c2d.EINVAL   # not 256-byte aligned
+    assert lib.conv2d_set_workspace(None, 4096) == c2d.EINVAL                 # null with a size
+    assert lib.conv2d_set_workspace(None, 0) == c2d.OK
+    c2d.tune_clear()
+    # a deep-K layer with few tiles: split-K in three, 3 * M * Cout fp32 partial sums
+    deep = (4, 20, 20, 512, 512, 3, 3, 1, 1, 1, nhwc, bf16)
+    assert "splitk=3" in c2d.plan(*deep)
+    assert c2d.workspace_size(*deep) == 3 * 1600 * 512 * 4
+    assert "splitk=1" in c2d.plan(*deep, workspace_bytes=0)
+    assert "splitk=1" in c2d.plan(*deep, workspace_bytes=3 * 1600 * 512 * 4 - 1)
+    # a channel-first 16-bit layer: channel-last copies of x and w (each rounded to 256 bytes)
+    ifn = (1, 68, 120, 240, 240, 3, 3, 1, 1, 3, nchw, f16)
+    xb, wb = 68 * 120 * 240 * 2, 240 * 9 * 240 * 2
+    assert c2d.workspace_size(*ifn) == (xb + 255) // 256 * 256 + (wb + 255) // 256 * 256
+    assert c2d.plan(*ifn).startswith("to_nhwc+")
+    assert c2d.plan(*ifn, workspace_bytes=0).startswith("igemm_nchw")
+    ohwi = ifn[:9] + (3 | c2d.WEIGHTS_OHWI,) + ifn[10:]
+    assert c2d.workspace_size(*ohwi) == (xb + 255) // 256 * 256
+    with pytest.raises(c2d.Conv2dError) as e:
+        c2d.plan(*ohwi, workspace_bytes=0)
+    assert e.value.code == c2d.EUNSUPPORTED and "workspace" in str(e.value)
+    # layers on kernels without scratch
+    assert c2d.workspace_size(4, 160, 160, 64, 64, 3, 3, 1, 1, 1, nhwc, bf16) == 0
+    assert c2d.workspace_size(1, 640, 640, 3, 32, 3, 3, 2, 1, 2, nhwc, bf16) == 0
+    # conv + max pool: the fused kernels need none, the two-kernel form needs the
+    # unpooled output and has no other variant
+    assert c2d.plan_maxpool(4, 320, 320, 32, 64, 3, 3, 1, 1, 1, 0, bf16, workspace_bytes=0).endswith(
+        "fused with maxpool3x3s2")
+    with pytest.raises(c2d.Conv2dError) as e:
+        c2d.plan_maxpool(1, 64, 64, 64, 64, 3, 3, 1, 1, 1, 0, bf16, workspace_bytes=64 * 64 * 64 * 2 - 256)
+    assert e.value.code == c2d.EUNSUPPORTED
+    assert c2d.plan_maxpool(1, 64, 64, 64, 64, 3, 3, 1, 1, 1, 0, bf16,
+                            workspace_bytes=64 * 64 * 64 * 2).endswith("then maxpool3x3s2")
+    # transposed conv: the matrix cores need the packed weights in the workspace
+    assert c2d.plan_deconv(1, 64, 64, 256, 128, 1, nhwc, bf16, workspace_bytes=0) == "deconv4x4s2_direct bf16"
+    assert c2d.plan_deconv(1, 64, 64, 256, 128, 1, nhwc, bf16,
+                           workspace_bytes=16 * 128 * 256 * 2).startswith("deconv4x4s2_pack+")
+    # a stack: the largest op's need, or both halves of a chain of channel-first convs
+    G = 1 << 32
+    act = c2d._ACTS["prelu"] | c2d.WEIGHTS_OHWI
+    chain = [c2d.Op(c2d.OP_CONV, s, 9 * G, 11 * G, 10 * G, None, d, 1, 68, 120, 240, 240, 3, 3, 1, 1, act)
+             for s, d in ((G, 3 * G), (3 * G, 5 * G))]
+    need = c2d.stack_workspace_size(chain, layout="nchw", dtype=f16)
+    assert need == 2 * ((xb + 255) // 256 * 256)
+    assert c2d.stack_plan(chain, 1, layout="nchw", dtype=f16).startswith("chained+")
+    assert c2d.stack_plan(chain, 1, layout="nchw", dtype=f16, workspace_bytes=need - 512).startswith("x_to_nhwc+")
+    with pytest.raises(c2d.Conv2dError):
+        c2d.stack_plan(chain, 1, layout="nchw", dtype=f16, workspace_bytes=0)
+    assert lib.conv2d_set_workspace(None, 0) == c2d.OK
+
+
+@pytest.mark.parametrize("what", ["w", "bias", "alpha"])
+def test_output_may_not_overlap_weights_bias_or_slopes(what):
+    """y overlapping w, bias or alpha is rejected before launch (other workgroups still read
+    them while one stores y)."""
+    inside = ctypes.c_void_p((17 << 32) + 64)
+    kw = dict(act=c2d.ACT_PRELU, alpha=A, bias=ctypes.c_void_p(41 << 32))
+    kw[what] = inside
+    assert _check(**kw) == c2d.EINVAL
+    assert "overlaps " + what in c2d.last_error()
+    assert _check(act=c2d.ACT_PRELU, alpha=A, bias=ctypes.c_void_p(41 << 32)) == c2d.OK

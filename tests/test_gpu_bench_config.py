@@ -17,22 +17,30 @@ bench = pytest.importorskip("bench")
 DEV = torch.device("cuda")
 
 
-@pytest.mark.parametrize("key,builder,shortcut", [("resnet", wl.conv5_resnet18d, False),
-                                                  ("resnet", wl.conv5_resnet18d, True),
-                                                  ("ifnet", wl.conv4_ifnet_block, False)])
-def test_tuned_stack_graph_end_to_end(key, builder, shortcut):
-    """shortcut: the average pool + 1x1 shortcut convs as single fused calls (bench.py
-    --fuse-shortcut)."""
+@pytest.mark.parametrize("key,builder,workspace", [("resnet", wl.conv5_resnet18d, True),
+                                                   ("resnet", wl.conv5_resnet18d, False),
+                                                   ("ifnet", wl.conv4_ifnet_block, True),
+                                                   ("ifnet", wl.conv4_ifnet_block, False)])
+def test_tuned_stack_graph_end_to_end(key, builder, workspace):
+    """workspace False: the stack recorded without a workspace, so every op takes a variant
+    that needs none (channel-first convs on the general kernel, no split-K)."""
     work = builder()
     c2d.tune_clear()
     try:
-        tuned = bench.tune_workload(work, fuse_shortcut=shortcut)
+        tuned = bench.tune_workload(work)
         assert tuned >= 1
-        net = bench.Net(work, DEV, fuse_pool=True, fuse_shortcut=shortcut)
-        assert any("pool_weights" in L["plan"] for L in net.layers) == shortcut
-        assert any(L["plan"].endswith(" tuned") for L in net.layers)
+        net = bench.Net(work, DEV, fuse_pool=True, weights_ohwi=workspace, workspace=workspace)
+        names = [L["plan"] for L in net.layers]
+        if key == "ifnet":
+            # channel-first convs: channel-last copies in the workspace, else the general kernel
+            assert all(n.startswith("x_to_nhwc+" if workspace else "igemm_nchw") for n in names), names
+        if not workspace:
+            assert all("splitk=" not in n or "splitk=1" in n for n in names), names
         g = c2d.StackGraph([L["op"] for L in net.layers], layout=work.layout,
-                           dtype={"bf16": c2d.DTYPE_BF16, "f16": c2d.DTYPE_F16}[work.dtype])
+                           dtype={"bf16": c2d.DTYPE_BF16, "f16": c2d.DTYPE_F16}[work.dtype],
+                           workspace=None if workspace else False)
+        if key == "ifnet" and workspace:
+            assert g.workspace is not None and g.workspace.numel() >= 2 * 68 * 120 * 240 * 2
         out = net.t[net.out_name]
         outs = []
         for _ in range(3):
