@@ -309,6 +309,13 @@ def pin_maxpool(orc):
     # all-negative input: the -inf padding never wins
     x = -np.abs(r.standard_normal((1, 2, 5, 5))) - 1.0
     assert np.all(orc.maxpool3x3s2(x, layout="nchw") <= -1.0)
+    # NaN taps are skipped, an all-NaN window gives -inf, and of equal zeros the first in
+    # row-major tap order is kept (hand-worked, tests/golden/pools_worked_example.txt)
+    for xk, yk, shape in [("maxpool_nan_x", "maxpool_nan_y", (4, 4)), ("maxpool_zeros_x", "maxpool_zeros_y", (3, 3))]:
+        y = orc.maxpool3x3s2(g[xk].reshape(1, 1, *shape), layout="nchw")[0, 0]
+        assert np.array_equal(y, g[yk]) and np.array_equal(np.signbit(y), np.signbit(g[yk])), (xk, y)
+    y = orc.maxpool3x3s2(np.full((1, 1, 3, 3), np.nan), layout="nchw")[0, 0]
+    assert np.array_equal(y, g["maxpool_allnan_y"]), y
 
 
 def pin_avgpool(orc):

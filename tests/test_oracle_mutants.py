@@ -36,6 +36,8 @@ MUTANTS = {
     "maxpool_no_pad": ("int iy = 2 * oh + dy - 1;", "int iy = 2 * oh + dy;"),
     "maxpool_zero_init": ("double best = -INFINITY;", "double best = 0.0;"),
     "maxpool_skips_last_col": ("for (int dx = 0; dx < 3; ++dx) {", "for (int dx = 0; dx < 2; ++dx) {"),
+    "maxpool_nan_wins": ("if (v > best) best = v;", "if (!(v <= best)) best = v;"),
+    "maxpool_last_of_equal": ("if (v > best) best = v;", "if (v >= best) best = v;"),
     "avgpool_order": ("float s = t[0] + t[1];\n                s = s + t[W];\n"
                       "                s = s + t[W + 1];",
                       "float s = t[0] + t[W + 1];\n                s = s + t[1];\n"
