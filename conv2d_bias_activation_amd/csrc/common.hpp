@@ -55,6 +55,17 @@ template <> __device__ __forceinline__ float from_f32<float>(float v) { return v
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return (bf16)v; }
 template <> __device__ __forceinline__ f16 from_f32<f16>(float v) { return (f16)v; }
 
+// x, the fp32 result of an epilogue, rounded once to T. The empty asm makes x an fp32
+// value first: otherwise this compiler may fold a multiply that produced x into the
+// conversion (v_fma_mix*), rounding the exact product to T instead of the fp32 product,
+// which can differ in the last place from another kernel's epilogue of the same sums.
+// Epilogues whose outputs must match bit for bit (a fused conv + pool and the two-call
+// path) all round through here.
+template <typename T> __device__ __forceinline__ T round_fp32(float x) {
+    asm volatile("" : "+v"(x));
+    return from_f32<T>(x);
+}
+
 // Activation of the epilogue: ReLU, SiLU v/(1+exp(-v)) or per-channel PReLU.
 __device__ __forceinline__ float activate(int act, float v, float alpha) {
     switch (act) {
@@ -88,6 +99,18 @@ __device__ __forceinline__ float epilogue(float acc, float bias, float alpha, fl
     v = activate(act, v, alpha);
     if (has_res && !res_before) v += r;
     return v;
+}
+
+// The max pool's comparison (inferencelayer page, `MAXPOOL_SRC`: `v > best` from the
+// padding value): of a, b, c taken in that order, starting from -inf, a later value
+// replaces the running one only when strictly greater, so NaN is skipped, three NaN give
+// -inf, and of equal values (-0 and +0) the first stays.
+__device__ __forceinline__ float first_max3(float a, float b, float c) {
+    float m = -__builtin_inff();
+    m = a > m ? a : m;
+    m = b > m ? b : m;
+    m = c > m ? c : m;
+    return m;
 }
 
 // Maps a hardware workgroup id to a logical tile id so that each of the 8 XCDs

@@ -99,7 +99,7 @@ __global__ __launch_bounds__(256) void direct_kernel(ConvArgs a, int cic) {
                 float b = a.bias ? a.bias[co] : 0.0f;
                 float al = a.alpha ? a.alpha[co] : 0.0f;
                 float r = has_res ? to_f32(rv[e]) : 0.0f;
-                out[e] = from_f32<T>(epilogue(acc[j], b, al, r, has_res, a.act, pre));
+                out[e] = round_fp32<T>(epilogue(acc[j], b, al, r, has_res, a.act, pre));
             }
             u32x4 t;
             __builtin_memcpy(&t, out, 16);
@@ -115,7 +115,7 @@ __global__ __launch_bounds__(256) void direct_kernel(ConvArgs a, int cic) {
         float b = a.bias ? a.bias[co] : 0.0f;
         float al = a.alpha ? a.alpha[co] : 0.0f;
         float r = has_res ? to_f32(res[o]) : 0.0f;
-        y[o] = from_f32<T>(epilogue(acc[j], b, al, r, has_res, a.act, pre));
+        y[o] = round_fp32<T>(epilogue(acc[j], b, al, r, has_res, a.act, pre));
     }
 }
 

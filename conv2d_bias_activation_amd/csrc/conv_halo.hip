@@ -66,8 +66,10 @@ __device__ __forceinline__ void halo_barrier() {
 // Each workgroup walks one run of tiles down the image (ty = seg*L .. seg*L + L - 1),
 // carrying the activated, column-maxed last row of a tile in LDS into the next; a run
 // that does not start at the top first computes the last row of the tile above
-// (one wave's products). The max is taken on rounded values: rounding is monotone,
-// so this equals pooling the rounded conv output.
+// (one wave's products). The max is taken on the rounded values, columns left to right
+// within a row, then the rows top to bottom, each step keeping the running value unless
+// the next is strictly greater: the taps in row-major order, as the pool kernel takes
+// them, so the result equals pooling the stored conv output bit for bit (NaN included).
 struct HaloPool {
     void *y;
     int PH, PW;
@@ -332,13 +334,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void halo3x3_kernel(ConvArgs a, in
             T q[16];
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                // through a scalar: this compiler lowers a bit cast applied directly to a
-                // vector element as a read of element 0
-                const float c = acc[0][j][e];
+                // rounded first, as the pool of the stored conv output sees it; then the
+                // first largest of (left, centre, right) from -inf, as `v > best` over the
+                // taps in row-major order (NaN never wins; of equal zeros the first stays).
+                // Through a scalar: this compiler lowers a bit cast applied directly to a
+                // vector element as a read of element 0.
+                const float c = to_f32(round_fp32<T>(acc[0][j][e]));
                 const int v = __builtin_bit_cast(int, c);
                 const float l = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(left, v));
                 const float rgt = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(right, v));
-                q[e] = from_f32<T>(__builtin_fmaxf(c, __builtin_fmaxf(l, rgt)));
+                q[e] = from_f32<T>(first_max3(l, c, rgt));
             }
 #pragma unroll
             for (int pp = 0; pp < 2; ++pp) {
@@ -365,18 +370,17 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void halo3x3_kernel(ConvArgs a, in
             __builtin_memcpy(t0, &v0, 16);
             __builtin_memcpy(t1, &v1, 16);
             __builtin_memcpy(t2, &v2, 16);
-            // The max is taken in fp32 behind an empty asm: left to itself, this compiler
-            // turns an f16 max of this shape into v_max3_f16 and then packs two results
-            // with a plain OR, as if the instruction cleared the upper 16 bits of its
-            // destination, which it does not (the odd channel of each pair came out wrong).
+            // The rows top to bottom, first largest as above. Compared in fp32 behind an
+            // empty asm: left to itself, this compiler turned an f16 max of this shape into
+            // v_max3_f16 and then packed two results with a plain OR, as if the instruction
+            // cleared the upper 16 bits of its destination, which it does not.
             auto wide = [](T v) {
                 float f = to_f32(v);
                 asm volatile("" : "+v"(f));
                 return f;
             };
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                m[e] = from_f32<T>(__builtin_fmaxf(wide(t0[e]), __builtin_fmaxf(wide(t1[e]), wide(t2[e]))));
+            for (int e = 0; e < 8; ++e) m[e] = from_f32<T>(first_max3(wide(t0[e]), wide(t1[e]), wide(t2[e])));
             // groups 2pp, 2pp+1 (4 channels each) -> 8 consecutive channels per lane half
             u32x2 qq2[2];
             __builtin_memcpy(&qq2[0], &m[0], 8);
@@ -478,7 +482,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void halo3x3_kernel(ConvArgs a, in
                                 if constexpr (ACT == CONV2D_ACT_SILU) x = x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
                                 if constexpr (ACT == CONV2D_ACT_PRELU) x = x >= 0.0f ? x : al[e] * x;
                                 if constexpr (RES == 2) x += to_f32(rt[e]);
-                                out[e] = from_f32<T>(x);
+                                out[e] = round_fp32<T>(x);
                             }
                             __builtin_memcpy(&q[h], out, 8);
                         }

@@ -196,7 +196,7 @@ __global__ __launch_bounds__(256) void stem3_kernel(ConvArgs a, int rstr) {
                             if constexpr (ACT == CONV2D_ACT_SILU) x = x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
                             if constexpr (ACT == CONV2D_ACT_PRELU) x = x >= 0.0f ? x : al[e] * x;
                             if constexpr (RES == 2) x += to_f32(rt[e]);
-                            out[e] = from_f32<T>(x);
+                            out[e] = round_fp32<T>(x);
                         }
                         __builtin_memcpy(&q[h], out, 8);
                     }
@@ -227,10 +227,12 @@ __global__ __launch_bounds__(256) void stem3_kernel(ConvArgs a, int rstr) {
 // and 4 column groups (one per wave). A group covers 32 conv columns c0 = 30g - 1 ..
 // c0 + 31 of the three conv rows 2py-1 .. 2py+1 (six products per 32 channels); lane
 // rl = 2k+1 (k < 15) is the centre of pooled column 15g + k, so every pool window lies
-// inside one group (groups overlap by two columns). Max over the three rows in
-// registers, over the columns from lanes rl-1 and rl+1 (ds_bpermute), taken in fp32
-// on the activated sums: rounding is monotone, so rounding the maximum equals the
-// maximum of the rounded conv outputs. Taps outside the conv map count as -inf.
+// inside one group (groups overlap by two columns). Each conv row is activated and
+// rounded to T; its columns rl-1, rl, rl+1 (ds_bpermute) are maxed left to right, then
+// the rows top to bottom, each step keeping the running value unless the next is
+// strictly greater: the taps in row-major order with the pool kernel's comparison, so
+// the result equals pooling the stored conv output bit for bit (NaN skipped, an all-NaN
+// window -inf, the first of equal zeros kept). Taps outside the conv map count as -inf.
 template <typename T, int FN, int S>
 __global__ __launch_bounds__(256) void stem3_pool_kernel(ConvArgs a, int PH, int PW, int groups, int rstr,
                                                          int ixs_step) {
@@ -304,6 +306,7 @@ __global__ __launch_bounds__(256) void stem3_pool_kernel(ConvArgs a, int PH, int
     for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) best[j][e] = -__builtin_inff();
+    const int left = (lane - 1 < 0 ? 0 : lane - 1) * 4, right = (lane + 1 < 64 ? lane + 1 : lane) * 4;
     auto act_max = [&](auto act_tag, const f32x16 (&acc)[FN], bool ok) {
         constexpr int ACT = decltype(act_tag)::value;
 #pragma unroll
@@ -317,7 +320,14 @@ __global__ __launch_bounds__(256) void stem3_pool_kernel(ConvArgs a, int PH, int
                     const float al = bal[1][j * 32 + 8 * (e / 4) + 4 * hi + (e % 4)];
                     x = x >= 0.0f ? x : al * x;
                 }
-                best[j][e] = ok ? __builtin_fmaxf(best[j][e], x) : best[j][e];
+                // through a scalar: this compiler lowers a bit cast applied directly to a
+                // vector element as a read of element 0
+                const float c = ok ? to_f32(round_fp32<T>(x)) : -__builtin_inff();
+                const int v = __builtin_bit_cast(int, c);
+                const float l = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(left, v));
+                const float r = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(right, v));
+                const float m = first_max3(l, c, r);
+                best[j][e] = m > best[j][e] ? m : best[j][e];
             }
     };
 #pragma unroll
@@ -347,17 +357,6 @@ __global__ __launch_bounds__(256) void stem3_pool_kernel(ConvArgs a, int PH, int
         default: act_max(std::integral_constant<int, CONV2D_ACT_NONE>{}, acc, ok); break;
         }
     }
-    // column max with the neighbouring conv columns (same half of the wave)
-    const int left = (lane - 1) * 4, right = (lane + 1 < 64 ? lane + 1 : lane) * 4;
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int v = __builtin_bit_cast(int, best[j][e]);
-            const float l = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(left < 0 ? 0 : left, v));
-            const float r = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(right, v));
-            best[j][e] = __builtin_fmaxf(best[j][e], __builtin_fmaxf(l, r));
-        }
     // pooled column of this lane (odd lanes below 30 are window centres)
     const int px = 15 * g + (rl - 1) / 2;
     const bool store = (rl & 1) && rl < 30 && px < PW;

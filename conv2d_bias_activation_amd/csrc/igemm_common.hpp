@@ -104,7 +104,7 @@ __device__ __forceinline__ void store_tile(const float *sC, const ConvArgs &a, i
 #pragma unroll
                     for (int e = 0; e < VE; ++e) {
                         float r = has_res ? to_f32(rv[e]) : 0.0f;
-                        out[e] = from_f32<T>(epilogue(sC[row * LDC + cv * VE + e], bv[e], av[e], r, has_res, act, pre));
+                        out[e] = round_fp32<T>(epilogue(sC[row * LDC + cv * VE + e], bv[e], av[e], r, has_res, act, pre));
                     }
                     u32x4 t;
                     __builtin_memcpy(&t, out, 16);
@@ -120,7 +120,7 @@ __device__ __forceinline__ void store_tile(const float *sC, const ConvArgs &a, i
                 float b = a.bias ? a.bias[co] : 0.0f;
                 float al = a.alpha ? a.alpha[co] : 0.0f;
                 float r = has_res ? to_f32(res[o]) : 0.0f;
-                y[o] = from_f32<T>(epilogue(sC[row * LDC + col], b, al, r, has_res, act, pre));
+                y[o] = round_fp32<T>(epilogue(sC[row * LDC + col], b, al, r, has_res, act, pre));
             }
         }
     } else {
@@ -145,7 +145,7 @@ __device__ __forceinline__ void store_tile(const float *sC, const ConvArgs &a, i
 #pragma unroll
                 for (int e = 0; e < VE; ++e) {
                     float r = has_res ? to_f32(rvv[e]) : 0.0f;
-                    out[e] = from_f32<T>(epilogue(sC[(rv * VE + e) * LDC + col], b, al, r, has_res, act, pre));
+                    out[e] = round_fp32<T>(epilogue(sC[(rv * VE + e) * LDC + col], b, al, r, has_res, act, pre));
                 }
                 u32x4 t;
                 __builtin_memcpy(&t, out, 16);
@@ -157,7 +157,7 @@ __device__ __forceinline__ void store_tile(const float *sC, const ConvArgs &a, i
                     int n2 = m / OHW, pix2 = m - n2 * OHW;
                     size_t o2 = ((size_t)n2 * Cout + co) * OHW + pix2;
                     float r = has_res ? to_f32(res[o2]) : 0.0f;
-                    y[o2] = from_f32<T>(epilogue(sC[(rv * VE + e) * LDC + col], b, al, r, has_res, act, pre));
+                    y[o2] = round_fp32<T>(epilogue(sC[(rv * VE + e) * LDC + col], b, al, r, has_res, act, pre));
                 }
             }
         }
@@ -219,7 +219,7 @@ __device__ __forceinline__ void wave_epilogue_nhwc(const f32x4 (&acc)[FM][FN], f
 #pragma unroll
                 for (int e = 0; e < VE; ++e) {
                     float r = has_res ? to_f32(rv[e]) : 0.0f;
-                    out[e] = from_f32<T>(epilogue(src[e], bv[e], av[e], r, has_res, act, pre));
+                    out[e] = round_fp32<T>(epilogue(src[e], bv[e], av[e], r, has_res, act, pre));
                 }
                 u32x4 t;
                 __builtin_memcpy(&t, out, 16);
@@ -229,7 +229,7 @@ __device__ __forceinline__ void wave_epilogue_nhwc(const f32x4 (&acc)[FM][FN], f
                 for (int e = 0; e < VE; ++e) {
                     if (co + e >= Cout) break;
                     float r = has_res ? to_f32(res[o + e]) : 0.0f;
-                    y[o + e] = from_f32<T>(epilogue(src[e], bv[e], av[e], r, has_res, act, pre));
+                    y[o + e] = round_fp32<T>(epilogue(src[e], bv[e], av[e], r, has_res, act, pre));
                 }
             }
         }
@@ -252,7 +252,7 @@ __device__ __forceinline__ void epilogue_vec(const float *v, const float *bv, co
         if (ACT == CONV2D_ACT_SILU) x = x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
         if (ACT == CONV2D_ACT_PRELU) x = x >= 0.0f ? x : av[e] * x;
         x += pre ? 0.0f : r;
-        out[e] = from_f32<T>(x);
+        out[e] = round_fp32<T>(x);
     }
 }
 

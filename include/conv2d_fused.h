@@ -138,8 +138,9 @@ int conv2d_fused(const void *x, const void *w, const float *bias, const float *a
  *
  * x [N,H,W,C] or [N,C,H,W] in `dtype`; y [N,OH,OW,C] or [N,C,OH,OW] with
  * OH = (H - 1)/2 + 1 (floor), OW likewise. The result is bit-exactly one of the
- * input values (the first largest in row-major tap order; NaN inputs are
- * skipped unless every tap is NaN, in which case -infinity is written).
+ * input values: the page's `v > best` from -infinity over the taps in row-major order,
+ * so the first largest is kept (of -0 and +0, the first), NaN inputs are skipped, and a
+ * window of NaN alone gives -infinity.
  */
 int maxpool3x3s2(const void *x, void *y, int N, int H, int W, int C, int layout, int dtype,
                  void *stream);

@@ -159,3 +159,40 @@ def test_fused_writes_only_the_pooled_map():
     assert bits_equal(first, out)
     assert torch.all(buf[:4096] == 7.0) and torch.all(buf[4096 + numel:] == 7.0)
     gate(to64(out), _oracle(x, spec, "nhwc"), "bf16", what="guarded")
+
+
+# NaN in the input (a NaN pixel makes every conv output whose window holds it NaN): the
+# fused kernels skip NaN and give -inf for an all-NaN window, bit for bit as the two-call
+# path, and agree with the oracle chain (finite outputs within the gate, -inf exactly
+# where the oracle has it). (kind, n, h, w, cin, cout, stride, act, NaN block rows, cols)
+NAN_CASES = [
+    ("stem", 1, 40, 48, 3, 32, 2, "silu", (4, 13), (12, 21)),
+    ("halo", 1, 30, 40, 32, 64, 1, "none", (8, 14), (10, 16)),
+    ("halo", 2, 17, 33, 16, 24, 1, "silu", (0, 6), (26, 33)),
+]
+
+
+@pytest.mark.parametrize("case", NAN_CASES, ids=lambda c: "-".join(map(str, c[:8])))
+def test_fused_maxpool_with_nan_inputs(case):
+    kind, n, h, w, cin, cout, s, act, (r0, r1), (c0, c1) = case
+    x, spec, _ = wl.random_conv_case(zlib.crc32(repr(case).encode()), n=n, h=h, w=w, cin=cin, cout=cout, k=3,
+                                     stride=s, pad=1, act=act, layout="nhwc", dtype="bf16",
+                                     x_dist="uniform" if kind == "stem" else "normal")
+    x = x.clone()
+    rng = np.random.default_rng(5)
+    pts = rng.integers(0, [n, h, w], size=(6, 3))
+    for b, i, j in pts:
+        x[b, i, j, rng.integers(0, cin)] = float("nan")
+    x[0, r0:r1, c0:c1, :] = float("nan")
+    args = (n, h, w, cin, cout, 3, 3, s, 1, c2d._ACTS[act], 0, c2d.DTYPE_BF16)
+    assert c2d.plan_maxpool(*args).startswith("stem3x3_mfma" if kind == "stem" else "halo3x3_nhwc")
+    y = _fused(x, spec, "nhwc")
+    y2 = _two_calls(x, spec, "nhwc")
+    torch.cuda.synchronize()
+    assert bits_equal(y, y2), "fused and two-call results differ"
+    got, ref = to64(y), _oracle(x, spec, "nhwc")
+    assert not np.isnan(got).any()
+    assert np.isneginf(ref).any(), "the case should hold an all-NaN window"
+    assert np.array_equal(np.isneginf(got), np.isneginf(ref))
+    fin = np.isfinite(ref)
+    gate(got[fin], ref[fin], "bf16", what=str(case))
