@@ -92,6 +92,7 @@ SIGNATURES = {
     "conv_transpose4x4s2_pack": (_i, [_vp, _vp, _i, _i, _i, _vp]),
     "conv_transpose4x4s2_prepacked": (_i, [_vp, _vp, _fp, _fp, _vp] + [_i] * 9 + [_vp]),
     "conv2d_weights_to_ohwi": (_i, [_vp, _vp] + [_i] * 5 + [_vp]),
+    "conv2d_fused_noalloc": (_i, [_vp, _vp, _fp, _fp, _vp, _vp] + [_i] * 12 + [_vp]),
     "conv2d_set_workspace": (_i, [_vp, ctypes.c_size_t]),
     "conv2d_workspace_size": (_i, [_i] * 12 + [ctypes.POINTER(ctypes.c_size_t)]),
     "conv2d_stack_workspace_size": (_i, [_op_p, _i, _i, _i, ctypes.POINTER(ctypes.c_size_t)]),

@@ -1180,7 +1180,7 @@ int tune_run(int N, int H, int W, int Cin, int Cout, int kh, int kw, int stride,
 
 extern "C" {
 
-int conv2d_abi_version(void) { return 8; }
+int conv2d_abi_version(void) { return 9; }
 
 const char *conv2d_last_error(void) { return g_err.c_str(); }
 
@@ -1536,6 +1536,61 @@ int conv2d_stack_graph_destroy(conv2d_graph *g) {
     if (e1 != hipSuccess) return hip_fail(e1, "hipGraphExecDestroy");
     if (e2 != hipSuccess) return hip_fail(e2, "hipGraphDestroy");
     return set_ok();
+}
+
+}  // extern "C"
+
+namespace {
+
+// Scratch of conv2d_fused_noalloc, for callers that cannot allocate device memory: one
+// copy of this array per GPU, held until the process ends. In host code its name is
+// only a stand-in; the device address comes from hipGetSymbolAddress, looked up once
+// per device with that device current, and is the only form passed to kernels.
+constexpr size_t kNoAllocScratchBytes = 16ull << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+char *g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int noalloc_scratch(Workspace *ws) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "conv2d_fused_noalloc: hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return set_error(CONV2D_EHIP, "device index %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr) return hip_fail(e, "conv2d_fused_noalloc: hipGetSymbolAddress(scratch)");
+        g_scratch_ptr[dev] = static_cast<char *>(ptr);
+    }
+    *ws = Workspace{g_scratch_ptr[dev], kNoAllocScratchBytes};
+    return CONV2D_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int conv2d_fused_noalloc(const void *x, const void *w, const float *bias, const float *alpha,
+                         const void *residual, void *y, int N, int H, int W, int Cin, int Cout, int kh,
+                         int kw, int stride, int pad, int act, int layout, int dtype, void *stream) {
+    const conv2d_op op{CONV2D_OP_CONV, x, w, bias, alpha, residual, y, N, H, W, Cin, Cout, kh, kw, stride, pad, act};
+    // the variant conv2d_fused takes with all the workspace it wants; its scratch must
+    // fit the static array (nothing is launched otherwise)
+    OpPlan o{};
+    int rc = check_op(op, layout, dtype, kUnlimitedWs, &o);
+    if (rc) return rc;
+    const size_t need = ws_need(o);
+    if (need > kNoAllocScratchBytes)
+        return set_error(CONV2D_EUNSUPPORTED,
+                         "conv2d_fused_noalloc: this layer's kernels need %zu bytes of scratch, more than the %zu "
+                         "bytes of the library's static scratch; use conv2d_fused with a workspace",
+                         need, kNoAllocScratchBytes);
+    Workspace ws{};
+    rc = noalloc_scratch(&ws);
+    if (rc) return rc;
+    return run_one(op, layout, dtype, stream, ws);
 }
 
 int conv2d_set_workspace(void *p, size_t bytes) {

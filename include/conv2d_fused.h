@@ -132,6 +132,28 @@ int conv2d_fused(const void *x, const void *w, const float *bias, const float *a
                  int kw, int stride, int pad, int act, int layout, int dtype, void *stream);
 
 /*
+ * conv2d_fused for callers that cannot allocate device memory or register a workspace
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same arguments, layouts and results, with the scratch of the
+ * kernel variant conv2d_fused takes when given all the workspace it wants (split-K
+ * partial sums, channel-last copies of a channel-first layer) taken from a static
+ * device array inside the library: 16 MiB, one copy per GPU the library runs on, held
+ * until the process ends. Its device address is looked up once per device on the first
+ * call there; nothing is allocated, by this call or later ones.
+ *
+ * The output is the same as conv2d_fused's with a workspace of at least
+ * conv2d_workspace_size bytes (the same kernels). A layer whose variant needs more than
+ * 16 MiB of scratch returns CONV2D_EUNSUPPORTED with a message and launches nothing.
+ * Every call on one GPU shares that GPU's array and leaves it holding its own data
+ * (each call writes all the scratch it reads; none needs it zeroed), so calls that may
+ * run at the same time on one GPU (two streams, two threads) race: serialise them, or
+ * use conv2d_fused with a workspace per stream. Errors as conv2d_fused.
+ */
+int conv2d_fused_noalloc(const void *x, const void *w, const float *bias, const float *alpha,
+                         const void *residual, void *y, int N, int H, int W, int Cin, int Cout, int kh,
+                         int kw, int stride, int pad, int act, int layout, int dtype, void *stream);
+
+/*
  * 3x3 max pool, stride 2, padding 1 with -infinity (out-of-range taps never win).
  * Source: inferencelayer page, `MAXPOOL_SRC` and the max-pool step of
  * `encoder_maps` (output (h + 2 - 3)/2 + 1).
@@ -456,7 +478,7 @@ int conv2d_tune_clear(void);
  * valid until the thread's next call into the library. */
 const char *conv2d_last_error(void);
 
-/* ABI version of this header: 8 (caller-owned workspace: conv2d_set_workspace and the
+/* ABI version of this header: 9 (conv2d_fused_noalloc; 8: caller-owned workspace: conv2d_set_workspace and the
  * size queries replace the library's own scratch; conv2d_avgpool2x2_conv1x1 and its op
  * kind are gone; 7 added CONV2D_WEIGHTS_OHWI and conv2d_weights_to_ohwi; 6
  * added the transposed conv's weight packing calls; 5

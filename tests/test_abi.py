@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     for name in names:
         assert hasattr(lib, name), name
     assert names == set(c2d.SIGNATURES)
-    assert c2d._load().conv2d_abi_version() == 8
+    assert c2d._load().conv2d_abi_version() == 9
 
 
 def test_out_dim():
@@ -439,3 +439,20 @@ def test_output_may_not_overlap_weights_bias_or_slopes(what):
     assert _check(**kw) == c2d.EINVAL
     assert "overlaps " + what in c2d.last_error()
     assert _check(act=c2d.ACT_PRELU, alpha=A, bias=ctypes.c_void_p(41 << 32)) == c2d.OK
+
+
+def test_noalloc_rejects_layers_over_its_static_scratch():
+    """Host only: conv2d_fused_noalloc refuses, before touching any device, a layer whose
+    kernels need more scratch than its 16 MiB static array (here the channel-last copies
+    of a channel-first 128-channel 256x256 f16 input and its weights)."""
+    lib = c2d._load()
+    P = ctypes.c_void_p
+    G = 1 << 32
+    assert c2d.workspace_size(1, 256, 256, 128, 64, 3, 3, 1, 1, 1, c2d.LAYOUT_NCHW, c2d.DTYPE_F16) > 16 << 20
+    rc = lib.conv2d_fused_noalloc(P(G), P(9 * G), None, None, None, P(17 * G), 1, 256, 256, 128, 64, 3, 3, 1, 1, 1,
+                                  c2d.LAYOUT_NCHW, c2d.DTYPE_F16, None)
+    assert rc == c2d.EUNSUPPORTED and "static scratch" in c2d.last_error()
+    # argument errors come first, as for conv2d_fused
+    rc = lib.conv2d_fused_noalloc(P(G), P(9 * G), None, None, None, P(17 * G), 1, 8, 8, 16, 16, 3, 3, 3, 1, 1,
+                                  c2d.LAYOUT_NHWC, c2d.DTYPE_BF16, None)
+    assert rc == c2d.EINVAL
