@@ -143,7 +143,15 @@ int check_conv(const void *x, const void *w, const float *bias, const float *alp
     return CONV2D_OK;
 }
 
-enum Family { FAM_DIRECT = 0, FAM_IGEMM = 1, FAM_NHWC = 2, FAM_NCHW_VIA_NHWC = 3, FAM_HALO = 4, FAM_STEM = 5 };
+enum Family {
+    FAM_DIRECT = 0,
+    FAM_IGEMM = 1,
+    FAM_NHWC = 2,
+    FAM_NCHW_VIA_NHWC = 3,
+    FAM_HALO = 4,
+    FAM_STEM = 5,
+    FAM_HALO_WS = 6
+};
 
 struct Plan {
     int family;
@@ -355,7 +363,9 @@ Plan make_plan_default(const ConvArgs &a, int layout, int dtype, size_t ws) {
     const long long wbytes = (long long)a.Cout * a.K * dtype_bytes(dtype);
     const long long ybytes = (long long)a.M * a.Cout * dtype_bytes(dtype);
     if (halo_fits(a, layout, dtype) && xbytes < (1ll << 31) && ybytes < (1ll << 31)) {
-        p.family = FAM_HALO;
+        // 64 input channels: the kernel with specialised compute and loader waves
+        // (measured on MI355X, ResNet-D stage 1: 21 -> see the design notes)
+        p.family = a.Cin == 64 ? FAM_HALO_WS : FAM_HALO;
         p.halo = plan_halo(a);
         return p;
     }
@@ -388,7 +398,7 @@ Plan make_plan_default(const ConvArgs &a, int layout, int dtype, size_t ws) {
 // whose built-in choice is one of those families, and uses an entry only if the variant
 // is valid for the call at hand (alignment, workspace size).
 struct TunedEntry {
-    int family;  // FAM_NHWC, FAM_NCHW_VIA_NHWC or FAM_HALO
+    int family;  // FAM_NHWC, FAM_NCHW_VIA_NHWC, FAM_HALO or FAM_HALO_WS
     int tile;    // NhwcTile (FAM_NHWC, FAM_NCHW_VIA_NHWC)
     int splits;  // K slices (FAM_NHWC; 1 for FAM_NCHW_VIA_NHWC)
     int th;      // tile height (FAM_HALO)
@@ -436,7 +446,8 @@ bool halo_th_ok(const ConvArgs &a, int th) {
 // Applies the table's entry for this call, if any and valid; p is the built-in choice.
 void apply_tuned(const ConvArgs &a, int layout, int dtype, size_t ws, Plan *p) {
     if (g_tuned_n.load(std::memory_order_acquire) == 0) return;
-    if (p->family != FAM_NHWC && p->family != FAM_HALO && p->family != FAM_NCHW_VIA_NHWC) return;
+    if (p->family != FAM_NHWC && p->family != FAM_HALO && p->family != FAM_HALO_WS && p->family != FAM_NCHW_VIA_NHWC)
+        return;
     const std::string dev = device_tag();
     if (dev.empty()) return;
     TunedEntry e;
@@ -458,6 +469,11 @@ void apply_tuned(const ConvArgs &a, int layout, int dtype, size_t ws, Plan *p) {
         p->family = FAM_HALO;
         p->halo = plan_halo(a);
         p->halo.th = e.th;
+        p->tuned = true;
+    } else if (e.family == FAM_HALO_WS) {
+        if (!halo_fits(a, layout, dtype) || a.Cin != 64) return;
+        p->family = FAM_HALO_WS;
+        p->halo = plan_halo(a);
         p->tuned = true;
     } else if (e.family == FAM_NHWC) {
         if (e.tile < 0 || e.tile >= NHWC_TILE_COUNT || !splits_ok(a, e.splits, ws)) return;
@@ -497,6 +513,8 @@ int describe(const Plan &p, int layout, int dtype, char *buf, int cap) {
     } else if (p.family == FAM_HALO) {
         snprintf(tmp, sizeof tmp, "halo3x3_nhwc %s th%d co%d w%d", dtype_name(dtype), p.halo.th, 32 * p.halo.fn,
                  p.halo.waves);
+    } else if (p.family == FAM_HALO_WS) {
+        snprintf(tmp, sizeof tmp, "halo3x3ws_nhwc %s th4 w4+4", dtype_name(dtype));
     } else if (p.family == FAM_NHWC || p.family == FAM_NCHW_VIA_NHWC) {
         snprintf(tmp, sizeof tmp, "%sigemm_nhwc_pipe%s %s %s splitk=%d%s",
                  p.family == FAM_NCHW_VIA_NHWC ? (p.chain_in ? "chained+" : p.w_ohwi ? "x_to_nhwc+" : "to_nhwc+") : "",
@@ -551,6 +569,11 @@ int launch_conv(const ConvArgs &a, const Plan &p, int layout, int dtype, const W
         HaloPlan h = p.halo;
         h.grid_cap = cus * (8 / h.waves);
         e = launch_halo3x3(a, dtype, h, st);
+    } else if (p.family == FAM_HALO_WS) {
+        int cus = 0;
+        rc = device_cus(&cus);
+        if (rc) return rc;
+        e = launch_halo3x3_ws(a, dtype, cus, st);
     } else if (p.family == FAM_NHWC) {
         e = launch_igemm_nhwc(a, dtype, p.nh, p.nh.splits > 1 ? reinterpret_cast<float *>(ws.p) : nullptr, st);
     } else if (p.family == FAM_NCHW_VIA_NHWC) {
@@ -1099,7 +1122,13 @@ int tune_run(int N, int H, int W, int Cin, int Cout, int kh, int kw, int stride,
             c.nh.tile = tile;
             cands.push_back(c);
         }
-    } else if (def.family == FAM_NHWC || def.family == FAM_HALO) {
+    } else if (def.family == FAM_NHWC || def.family == FAM_HALO || def.family == FAM_HALO_WS) {
+        if (halo_fits(a, layout, dtype) && a.Cin == 64 && def.family != FAM_HALO_WS) {
+            Plan c{};
+            c.family = FAM_HALO_WS;
+            c.halo = plan_halo(a);
+            cands.push_back(c);
+        }
         if (halo_fits(a, layout, dtype)) {
             for (int th : {4, 8}) {
                 if (!halo_th_ok(a, th)) continue;
@@ -1163,7 +1192,8 @@ int tune_run(int N, int H, int W, int Cin, int Cout, int kh, int kw, int stride,
     *best_out = cands[(size_t)best];
     *best_us = best_ms * 1e3f / (float)reps;
     // record the winner (only for the families the planner looks up)
-    if (best_out->family == FAM_NHWC || best_out->family == FAM_HALO || best_out->family == FAM_NCHW_VIA_NHWC) {
+    if (best_out->family == FAM_NHWC || best_out->family == FAM_HALO || best_out->family == FAM_HALO_WS ||
+        best_out->family == FAM_NCHW_VIA_NHWC) {
         const std::string dev = device_tag();
         if (!dev.empty()) {
             TunedEntry t{best_out->family, best_out->nh.tile, best_out->nh.splits, best_out->halo.th};
@@ -1396,7 +1426,8 @@ int conv2d_tune_load(const char *path) {
                                                     t.splits >= 1 && t.splits <= 4) ||
                                                    (t.family == FAM_NCHW_VIA_NHWC && t.tile >= 0 &&
                                                     t.tile < NHWC_TILE_COUNT && t.splits == 1) ||
-                                                   (t.family == FAM_HALO && (t.th == 4 || t.th == 8)));
+                                                   (t.family == FAM_HALO && (t.th == 4 || t.th == 8)) ||
+                                                   (t.family == FAM_HALO_WS && t.th == 4));
         if (!ok) {
             fclose(f);
             return set_error(CONV2D_EINVAL, "conv2d_tune_load: %s line %d is not a tuned-plan record", path, lineno);

@@ -1,0 +1,367 @@
+// 3x3 stride-1 pad-1 channel-last convolution with 64 input channels and up to 64 output
+// channels (the ResNet-D stage-1 convs) on CDNA4 matrix cores: halo tiles with
+// specialised waves.
+//
+// The GEMM is the implicit-GEMM one of the other kernels (m = output pixel, k = (tap,
+// input channel), n = output channel; inferencelayer page, `conv()`: im2col + GEMM with
+// bias and activation in the epilogue); as in the halo kernel, a 4 x 32-pixel output
+// tile reads its patches from one copy of its (4+2) x 34-pixel input halo in LDS (the
+// halo tiles of the framecast page's convolution shader). What differs is who does
+// what: a workgroup of 8 waves has
+//
+//  * four compute waves (one per SIMD) that hold their weights in registers for the
+//    whole launch (32 output channels x all 576 k: 36 operand fragments, taken once from
+//    a coalesced copy of the weights in LDS) and run only matrix-core products: each
+//    takes two tile rows (64 pixels) x 32 channels, and hands its fp32 sums of tile s-1
+//    to a tile in LDS while the products of tile s run;
+//  * four loader/epilogue waves that keep the input halos coming (direct-to-LDS loads,
+//    two tiles ahead into a ring of three halo buffers, with the tile-invariant address
+//    arithmetic hoisted out of the loop), load the residual three tiles ahead into
+//    registers, and run the epilogue of tile s-2 from the hand-off tile (bias, residual
+//    before or after the activation, activation, one rounding, 16-byte stores of 8
+//    channels).
+//
+// The two groups meet at one workgroup barrier per tile, so the matrix cores work on
+// tile s while the hand-off of s-1, the epilogue of s-2 and the loads of tiles s+1, s+2
+// proceed. The workgroups are persistent (one per CU) and walk tiles t = s*G + r.
+#include "igemm_common.hpp"
+#include "kernels.hpp"
+
+namespace c2d {
+
+namespace {
+
+template <int N> __device__ __forceinline__ void ws_wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier after this wave's LDS accesses have completed (s_barrier does not
+// wait for them); direct-to-LDS loads are published by the loaders' vmcnt waits.
+__device__ __forceinline__ void ws_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+constexpr int kWsTH = 4, kWsTW = 32, kWsHR = kWsTH + 2, kWsHW = kWsTW + 2;
+
+}  // namespace
+
+template <typename T, int CIN>
+__global__ __launch_bounds__(512, 1) void halo3x3_ws_kernel(ConvArgs a, int tiles_w, int tiles_h, int ntiles) {
+    constexpr int CPX = CIN / 8;                 // 16-byte chunks of channels per pixel
+    constexpr int SPX = CPX + 1;                 // 16-byte slots per pixel in LDS (odd)
+    constexpr int PSTR = SPX * 16;               // pixel stride in a halo buffer
+    constexpr int NQ = kWsHR * kWsHW;            // halo pixels
+    constexpr int NCHUNK = (NQ * SPX + 63) / 64;  // 1 KiB load chunks per halo
+    constexpr int HBUF = NCHUNK * 1024;
+    constexpr int NLD = (NCHUNK + 3) / 4;        // loads per loader lane per halo
+    constexpr int KC = CIN / 16;                 // 16-wide k steps per tap
+    constexpr int KS = 9 * KC;                   // k steps
+    constexpr int XPIX = 64 * 4 + 16;            // hand-off tile: 64 fp32 channels per pixel, padded
+    constexpr int XBUF = kWsTH * kWsTW * XPIX;
+    constexpr int NRES = 4;                      // 16-byte units per epilogue lane per tile
+    // One LDS array: halo buffers 0..2, the two hand-off tiles, then a sink for the load
+    // chunks past a halo. At the start the 64-channel weights (Cout x 576 elements) pass
+    // through the space from halo buffer 2 on, which nothing else uses before step 0
+    // (the first two halos and their sink chunks go elsewhere).
+    constexpr int XOFF = 3 * HBUF, SINK = XOFF + 2 * XBUF, WOFF = 2 * HBUF;
+    constexpr int LDS_BYTES = SINK + 1024;
+    constexpr int WBYTES = 64 * 9 * CIN * (int)sizeof(T);
+    static_assert(LDS_BYTES <= 160 * 1024 && WOFF + WBYTES <= SINK, "LDS");
+    __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
+    typedef typename Mfma32<T>::vec vec;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const bool compute_wave = wave < 4;
+    const int rl = lane & 31, hi = lane >> 5;
+    const int H = a.H, W = a.W, Cout = a.Cout;
+
+    // tiles of this workgroup: t = s*G + r, the workgroups of one XCD (blockIdx % 8) taking
+    // a contiguous run of each round's tiles (neighbouring halos share rows in one L2)
+    const int G = gridDim.x;
+    const int r = (G % 8) == 0 ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
+    const int nsteps = r < ntiles ? (ntiles - r + G - 1) / G : 0;  // tiles of this workgroup
+    struct Geo {
+        int n, oy0, ox0;
+        bool live;
+    };
+    auto geo = [&](int s) -> Geo {
+        const int t = s * G + r;
+        const bool live = s < nsteps;
+        const int tt = live ? t : 0;
+        const int tx = tt % tiles_w, rr = tt / tiles_w;
+        return Geo{rr / tiles_h, (rr % tiles_h) * kWsTH, tx * kWsTW, live};
+    };
+
+    // Weights: every wave copies 1/8 of the [64][9*CIN] block (rows past Cout read as
+    // zeros) into LDS with 16-byte direct-to-LDS loads; the compute waves then take their
+    // operand fragments from there into registers.
+    {
+        const i32x4 rw = rsrc_words(a.w, (uint32_t)((size_t)Cout * 9 * CIN * sizeof(T)));
+        constexpr int WCH = WBYTES / 1024;
+        static_assert(WBYTES % 1024 == 0 && WCH % 8 == 0, "whole chunks per wave");
+#pragma unroll
+        for (int d = 0; d < WCH / 8; ++d) {
+            const int chunk = d * 8 + wave;
+            dma_b128(rw, (uint32_t)(chunk * 1024 + lane * 16), lds_addr(lds + WOFF + chunk * 1024));
+        }
+    }
+    const uint32_t out_bytes = (uint32_t)((size_t)a.M * Cout * sizeof(T));
+
+    if (compute_wave) {
+        // ---- compute waves: wave (wn, wm) = channels 32*wn.., tile rows 2*wm, 2*wm + 1 ----
+        const int wn = wave & 1, wm = wave >> 1;
+        ws_wait_vmcnt<0>();
+        ws_barrier();  // weights in LDS
+        vec bw[KS];
+        {
+            const char *wrow = lds + WOFF + ((32 * wn + rl) * 9 * CIN + 8 * hi) * (int)sizeof(T);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) bw[ks] = *reinterpret_cast<const vec *>(wrow + ks * 16 * (int)sizeof(T));
+        }
+        ws_barrier();  // weights in registers, the first halo landed
+        f32x16 acc[2][2];  // two tiles' sums: one accumulating, the previous one handed off
+        auto compute = [&](auto cur, int s) {
+            constexpr int C = decltype(cur)::value;
+            const char *buf = lds + (s % 3) * HBUF;
+            // B operand of tile row 2*wm + i at k step ks: halo pixel (row + ky, rl + kx),
+            // channels 16*kc + 8*hi ..
+            const char *base = buf + ((2 * wm) * kWsHW + rl) * PSTR + hi * 16;
+            auto read = [&](int ks, vec(&f)[2]) {
+                const int tap = ks / KC, kc = ks % KC, ky = tap / 3, kx = tap % 3;
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+                    f[i] = *reinterpret_cast<const vec *>(base + ((i + ky) * kWsHW + kx) * PSTR + kc * 32);
+            };
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[C][i][e] = 0.0f;
+            constexpr int PF = 2;  // operand reads run PF k steps ahead of the products
+            vec f[PF + 1][2];
+#pragma unroll
+            for (int ks = 0; ks < PF; ++ks) read(ks, f[ks]);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                if (ks + PF < KS) read(ks + PF, f[(ks + PF) % (PF + 1)]);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i = 0; i < 2; ++i) acc[C][i] = Mfma32<T>::run(bw[ks], f[ks % (PF + 1)][i], acc[C][i]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        // hand-off of tile s: lane (rl, hi) holds channels 32*wn + 8*g + 4*hi + 0..3 of pixel rl
+        auto handoff = [&](auto prev, int s) {
+            constexpr int C = decltype(prev)::value;
+            char *x = lds + XOFF + (s & 1) * XBUF;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int p = (2 * wm + i) * kWsTW + rl;
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    *reinterpret_cast<f32x4 *>(x + p * XPIX + (32 * wn + 8 * g + 4 * hi) * 4) =
+                        f32x4{acc[C][i][4 * g], acc[C][i][4 * g + 1], acc[C][i][4 * g + 2], acc[C][i][4 * g + 3]};
+            }
+        };
+        // Step s: the sums of tile s-1 go to the hand-off tile while the products of tile s
+        // run (the LDS writes and the matrix cores overlap), then the barrier.
+        auto step = [&](auto cur, int s) {
+            constexpr int C = decltype(cur)::value;
+            if (s >= 1 && s <= nsteps) handoff(std::integral_constant<int, 1 - C>{}, s - 1);
+            if (s < nsteps) compute(cur, s);
+            ws_barrier();
+        };
+        for (int s = 0; s <= nsteps; s += 2) {
+            step(std::integral_constant<int, 0>{}, s);
+            if (s + 1 > nsteps) break;
+            step(std::integral_constant<int, 1>{}, s + 1);
+        }
+        ws_barrier();  // the epilogue of the last tile
+        return;
+    }
+
+    // ---- loader / epilogue waves ----
+    const int we = wave - 4;
+    const int te = we * 64 + lane;   // 0..255
+    const int c8 = te & 7;           // this lane's 8-channel group, the same in every unit
+    const i32x4 rx = rsrc_words(a.x, (uint32_t)((size_t)a.N * H * W * CIN * sizeof(T)));
+    const bool has_res = a.res != nullptr;
+    const __amdgpu_buffer_rsrc_t rres = make_rsrc(a.res, has_res ? out_bytes : 0u);
+    const __amdgpu_buffer_rsrc_t ry = make_rsrc(a.y, out_bytes);
+    float bv[8], av[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int co = 8 * c8 + e;
+        bv[e] = a.bias && co < Cout ? a.bias[co] : 0.0f;
+        av[e] = a.alpha && co < Cout ? a.alpha[co] : 0.0f;
+    }
+    // Tile-invariant parts of this lane's halo slots: pixel (hy, hx) of the halo and
+    // channel chunk c, as an element offset from the tile's corner pixel (row oy0 - 1,
+    // column ox0 - 1); kNoPix marks a padding slot (nothing to load).
+    constexpr uint32_t kNoPix = 0xffffffffu;
+    int h_rel[NLD];
+    uint32_t h_yx[NLD];  // hy << 8 | hx
+#pragma unroll
+    for (int d = 0; d < NLD; ++d) {
+        const int slot = (d * 4 + we) * 64 + lane;
+        const int q = slot / SPX, c = slot - q * SPX;
+        const int hy = q / kWsHW, hx = q - hy * kWsHW;
+        const bool real = c < CPX && q < NQ;
+        h_rel[d] = (hy * W + hx) * CIN + c * 8;
+        h_yx[d] = real ? (uint32_t)(hy << 8 | hx) : kNoPix;
+    }
+    // the same for this lane's output units: pixel (py, px) of the tile (kNoPix for a
+    // channel group past Cout)
+    int u_rel[NRES];
+    uint32_t u_yx[NRES];
+    const bool c_ok = 8 * c8 < Cout;
+#pragma unroll
+    for (int j = 0; j < NRES; ++j) {
+        const int p = (te + 256 * j) >> 3, py = p / kWsTW, px = p % kWsTW;
+        u_rel[j] = (py * W + px) * Cout + 8 * c8;
+        u_yx[j] = c_ok ? (uint32_t)(py << 8 | px) : kNoPix;
+    }
+
+    // the input halo of tile s into buffer s % 3; a step past the last tile still issues
+    // its loads, with out-of-range offsets (no traffic), so every step's count is the same
+    auto issue_halo = [&](int s) {
+        const Geo g = geo(s);
+        char *buf = lds + (s % 3) * HBUF;
+        const int corner = ((g.n * H + g.oy0 - 1) * W + g.ox0 - 1) * CIN;
+#pragma unroll
+        for (int d = 0; d < NLD; ++d) {
+            const int chunk = d * 4 + we;
+            const int iy = g.oy0 - 1 + (int)(h_yx[d] >> 8), ix = g.ox0 - 1 + (int)(h_yx[d] & 0xff);
+            const bool ok =
+                g.live && h_yx[d] != kNoPix && (unsigned)iy < (unsigned)H && (unsigned)ix < (unsigned)W;
+            char *dst = chunk < NCHUNK ? buf + chunk * 1024 : lds + SINK;
+            dma_b128(rx, ok ? (uint32_t)(corner + h_rel[d]) * (uint32_t)sizeof(T) : kOOB, lds_addr(dst));
+        }
+    };
+    // byte offset in y (and the residual) of this lane's unit j of tile s, or kOOB
+    auto unit_off = [&](const Geo &g, int j) -> uint32_t {
+        const int oy = g.oy0 + (int)(u_yx[j] >> 8), ox = g.ox0 + (int)(u_yx[j] & 0xff);
+        return (g.live && u_yx[j] != kNoPix && oy < H && ox < W)
+                   ? (uint32_t)(((g.n * H + g.oy0) * W + g.ox0) * Cout + u_rel[j]) * (uint32_t)sizeof(T)
+                   : kOOB;
+    };
+    u32x4 res[3][NRES];
+    auto issue_res = [&](auto slot, int s) {
+        constexpr int I = decltype(slot)::value;
+        const Geo g = geo(s);
+#pragma unroll
+        for (int j = 0; j < NRES; ++j)
+            res[I][j] = __builtin_amdgcn_raw_buffer_load_b128(rres, (int)(has_res ? unit_off(g, j) : kOOB), 0, 0);
+    };
+    auto epilogue = [&](auto slot, int s) {
+        constexpr int I = decltype(slot)::value;
+        const Geo g = geo(s);
+        const char *x = lds + XOFF + (s & 1) * XBUF;
+        const int mode = has_res ? (a.res_before_act ? 1 : 2) : 0;
+        auto finish = [&](auto act_tag, auto res_tag) {
+            constexpr int ACT = decltype(act_tag)::value;
+            constexpr int RES = decltype(res_tag)::value;
+#pragma unroll
+            for (int j = 0; j < NRES; ++j) {
+                const int p = (te + 256 * j) >> 3;
+                const f32x4 v0 = *reinterpret_cast<const f32x4 *>(x + p * XPIX + c8 * 32);
+                const f32x4 v1 = *reinterpret_cast<const f32x4 *>(x + p * XPIX + c8 * 32 + 16);
+                T rt[8], out[8];
+                __builtin_memcpy(rt, &res[I][j], 16);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    float v = (e < 4 ? v0[e] : v1[e - 4]) + bv[e];
+                    if constexpr (RES == 1) v += to_f32(rt[e]);
+                    if constexpr (ACT == CONV2D_ACT_RELU) v = v > 0.0f ? v : 0.0f;
+                    if constexpr (ACT == CONV2D_ACT_SILU) v = v * __builtin_amdgcn_rcpf(1.0f + __expf(-v));
+                    if constexpr (ACT == CONV2D_ACT_PRELU) v = v >= 0.0f ? v : av[e] * v;
+                    if constexpr (RES == 2) v += to_f32(rt[e]);
+                    out[e] = round_fp32<T>(v);
+                }
+                u32x4 o;
+                __builtin_memcpy(&o, out, 16);
+                __builtin_amdgcn_raw_buffer_store_b128(o, ry, (int)unit_off(g, j), 0, 0);
+            }
+        };
+        auto with_res = [&](auto act_tag) {
+            switch (mode) {
+            case 1: finish(act_tag, std::integral_constant<int, 1>{}); break;
+            case 2: finish(act_tag, std::integral_constant<int, 2>{}); break;
+            default: finish(act_tag, std::integral_constant<int, 0>{}); break;
+            }
+        };
+        switch (a.act) {
+        case CONV2D_ACT_RELU: with_res(std::integral_constant<int, CONV2D_ACT_RELU>{}); break;
+        case CONV2D_ACT_SILU: with_res(std::integral_constant<int, CONV2D_ACT_SILU>{}); break;
+        case CONV2D_ACT_PRELU: with_res(std::integral_constant<int, CONV2D_ACT_PRELU>{}); break;
+        default: with_res(std::integral_constant<int, CONV2D_ACT_NONE>{}); break;
+        }
+    };
+
+    // Start: the halos of tiles 0 and 1 and the residual of tile 0 go out behind this
+    // wave's weight chunks; the weights land (barrier), then the first halo (barrier).
+    constexpr int WLD = WBYTES / 1024 / 8;
+    issue_halo(0);
+    issue_halo(1);
+    issue_res(std::integral_constant<int, 0>{}, 0);
+    ws_wait_vmcnt<2 * NLD + NRES>();  // this wave's weight chunks
+    ws_barrier();
+    ws_wait_vmcnt<NLD + NRES>();  // the halo of tile 0
+    ws_barrier();
+    // Step s: the halo of tile s+2 issued; the epilogue of tile s-2, whose sums the
+    // compute waves handed off during step s-1 (its residual went out three steps
+    // before); the residual of tile s+1 issued into the register slot that epilogue just
+    // freed; then a wait that leaves only this step's loads and stores in flight, so the
+    // halo of tile s+1 is in LDS before the barrier that starts its products.
+    // Halo buffer s+2 = s-1 (mod 3): its products ended at the barrier that began step s.
+    constexpr int STEP_OPS = NLD + NRES + NRES;
+    auto step = [&](auto slot, int s) {
+        constexpr int I = decltype(slot)::value;  // s % 3
+        issue_halo(s + 2);
+        if (s >= 2) {
+            epilogue(std::integral_constant<int, (I + 1) % 3>{}, s - 2);
+        } else {
+#pragma unroll
+            for (int j = 0; j < NRES; ++j)  // the same count of stores, none of them live
+                __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, ry, (int)kOOB, 0, 0);
+        }
+        issue_res(std::integral_constant<int, (I + 1) % 3>{}, s + 1);
+        ws_wait_vmcnt<STEP_OPS>();
+        ws_barrier();
+    };
+    for (int s = 0; s <= nsteps + 1; s += 3) {
+        step(std::integral_constant<int, 0>{}, s);
+        if (s + 1 > nsteps + 1) break;
+        step(std::integral_constant<int, 1>{}, s + 1);
+        if (s + 2 > nsteps + 1) break;
+        step(std::integral_constant<int, 2>{}, s + 2);
+    }
+    ws_wait_vmcnt<0>();  // no direct-to-LDS load outlives the workgroup
+}
+
+template <typename T>
+static hipError_t launch_ws_t(const ConvArgs &a, int grid_cap, hipStream_t st) {
+    const int tiles_w = (a.W + kWsTW - 1) / kWsTW, tiles_h = (a.H + kWsTH - 1) / kWsTH;
+    const long long nt = (long long)a.N * tiles_w * tiles_h;
+    if (nt > 0x7fffffffll) return hipErrorInvalidValue;
+    const int ntiles = (int)nt;
+    int grid = ntiles < grid_cap ? ntiles : grid_cap;
+    if (grid > 8) grid -= grid % 8;
+    return launch_kernel(halo3x3_ws_kernel<T, 64>, dim3(grid), dim3(512), 0, st, a, tiles_w, tiles_h, ntiles);
+}
+
+hipError_t launch_halo3x3_ws(const ConvArgs &a, int dtype, int grid_cap, hipStream_t st) {
+    if (a.Cin != 64 || a.Cout > 64 || a.kh != 3 || a.kw != 3 || a.stride != 1 || a.pad != 1)
+        return hipErrorInvalidValue;
+    switch (dtype) {
+    case CONV2D_DTYPE_BF16: return launch_ws_t<bf16>(a, grid_cap, st);
+    case CONV2D_DTYPE_F16: return launch_ws_t<f16>(a, grid_cap, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace c2d

@@ -79,6 +79,12 @@ struct HaloPlan {
 // for p.fn = 1, p.th = WM for p.fn = 2.
 hipError_t launch_halo3x3(const ConvArgs &a, int dtype, const HaloPlan &p, hipStream_t st);
 
+// The same convolution for Cin 64 (Cout <= 64) with specialised waves: four compute
+// waves with their weights in registers run only the matrix-core products, four
+// loader/epilogue waves prefetch the halos and run the previous tile's epilogue; one
+// persistent workgroup of 8 waves per CU (grid_cap workgroups). Limits as launch_halo3x3.
+hipError_t launch_halo3x3_ws(const ConvArgs &a, int dtype, int grid_cap, hipStream_t st);
+
 // The same convolution for Cin 16 or 32 followed by the 3x3 stride-2 pad-1 max pool in
 // one kernel: only the pooled map is written, to y ([N, PH, PW, Cout], PH = (H-1)/2 + 1,
 // 16-byte aligned); no residual. About grid_cap workgroups of 4 waves (two per CU).

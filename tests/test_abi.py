@@ -81,7 +81,7 @@ def test_plan_names_a_kernel_for_every_workload_shape():
              ((1, 68, 120, 240, 240, 3, 3, 1, 1, 3, 1, f16), "to_nhwc+igemm_nhwc_pipe"),
              ((4, 40, 40, 256, 256, 3, 3, 1, 1, 1, 0, bf16), "igemm_nhwc_pipe"),
              ((4, 320, 320, 32, 64, 3, 3, 1, 1, 1, 0, bf16), "halo3x3_nhwc"),
-             ((4, 160, 160, 64, 64, 3, 3, 1, 1, 1, 0, bf16), "halo3x3_nhwc"),
+             ((4, 160, 160, 64, 64, 3, 3, 1, 1, 1, 0, bf16), "halo3x3ws_nhwc"),
              ((4, 160, 160, 64, 128, 3, 3, 2, 1, 1, 0, bf16), "igemm_nhwc_pipe")]
     for s, family in cases:
         name = c2d.plan(*s)

@@ -110,6 +110,13 @@ HALO = [
     (2, 160, 160, 32, 48, "silu", "post", "bf16"),
     (4, 256, 256, 64, 32, "relu", "pre", "bf16"),
     (2, 64, 100, 16, 64, "silu", None, "f16"),
+    # 64 input channels (the kernel with specialised waves): one pixel, two tiles (fewer
+    # workgroups than CUs), a wide short map, channel groups past Cout, every epilogue
+    (1, 1, 1, 64, 64, "relu", "post", "bf16"),
+    (1, 8, 40, 64, 64, "silu", "pre", "bf16"),
+    (1, 5, 300, 64, 56, "silu", "post", "f16"),
+    (3, 17, 31, 64, 8, "none", None, "bf16"),
+    (2, 41, 77, 64, 40, "prelu", None, "bf16"),
 ]
 
 
