@@ -283,6 +283,8 @@ def time_layers(torch, net, reps):
 # is only used while these files are unchanged.
 KERNEL_SOURCES = [
     ("igemm_nhwc_pipe", ["conv_igemm_nhwc.hip", "igemm_common.hpp", "common.hpp"]),
+    ("hgemm3x3", ["conv_hgemm.hip", "igemm_common.hpp", "common.hpp"]),
+    ("halo3x3ws", ["conv_halo_ws.hip", "igemm_common.hpp", "common.hpp"]),
     ("halo3x3", ["conv_halo.hip", "igemm_common.hpp", "common.hpp"]),
     ("stem3x3", ["conv_stem.hip", "igemm_common.hpp", "common.hpp"]),
     ("igemm_", ["conv_igemm.hip", "igemm_common.hpp", "common.hpp"]),
@@ -294,6 +296,8 @@ KERNEL_SOURCES = [
 # plan-name prefix -> part of the kernel's symbol (the library's kernels live in namespace c2d)
 KERNEL_SYMBOLS = [
     ("igemm_nhwc_pipe", "3c2d17igemm_nhwc_kernel"),
+    ("hgemm3x3", "3c2d15hgemm3x3_kernel"),
+    ("halo3x3ws", "3c2d17halo3x3_ws_kernel"),
     ("halo3x3", "3c2d14halo3x3_kernel"),
     ("stem3x3", "stem3_"),  # stem3_kernel, stem3_pool_kernel
     ("igemm_", "3c2d12igemm_kernel"),

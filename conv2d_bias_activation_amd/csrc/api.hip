@@ -150,7 +150,8 @@ enum Family {
     FAM_NCHW_VIA_NHWC = 3,
     FAM_HALO = 4,
     FAM_STEM = 5,
-    FAM_HALO_WS = 6
+    FAM_HALO_WS = 6,
+    FAM_HGEMM = 7
 };
 
 struct Plan {
@@ -158,6 +159,7 @@ struct Plan {
     IgemmPlan ig;
     NhwcPlan nh;
     HaloPlan halo;
+    HgemmPlan hg;
     bool tuned;  // chosen by a conv2d_tune measurement rather than the built-in heuristics
     bool w_ohwi; // channel-first layer with channel-last weights: only the input is copied
     // chained channel-first layers of a stack (FAM_NCHW_VIA_NHWC, set by link_chains)
@@ -337,6 +339,40 @@ bool stem_fits(const ConvArgs &a, int layout, int dtype) {
            (long long)a.M * a.Cout * 2 < (1ll << 31);
 }
 
+// Halo-tile GEMM kernel for wide 3x3 stride-1 layers (channel-last, 16-bit, Cin a
+// multiple of 32; variants with 64-channel K chunks need Cin % 64 == 0).
+bool hgemm_fits(const ConvArgs &a, int layout, int dtype) {
+    const int eb = dtype_bytes(dtype);
+    return layout == CONV2D_LAYOUT_NHWC && dtype != CONV2D_DTYPE_F32 && a.kh == 3 && a.kw == 3 && a.stride == 1 &&
+           a.pad == 1 && (a.Cin % 32) == 0 && (a.Cout % 8) == 0 && a.vec_out && aligned16(a.x) && aligned16(a.w) &&
+           (long long)a.N * a.H * a.W * a.Cin * eb < (1ll << 31) && (long long)a.Cout * a.K * eb < (1ll << 31) &&
+           (long long)a.M * a.Cout * eb < (1ll << 31);
+}
+
+bool hgemm_cfg_ok(const ConvArgs &a, int cfg) {
+    HgemmInfo in{};
+    return hgemm_cfg_info(cfg, a, &in) && (a.Cin % in.ck) == 0 && in.tiles > 0 && in.tiles < (1ll << 31);
+}
+
+// Tile order: each XCD (one L2) gets a contiguous run of tile ids; with the channel
+// tile fastest an XCD reads about 1/8 of the input and all the weights, with the pixel
+// tile fastest all the input and 1/8 of the weights. The smaller total wins.
+bool hgemm_cfast(const ConvArgs &a) {
+    const double xb = (double)a.N * a.H * a.W * a.Cin, wb = (double)a.Cout * a.K;
+    return xb / 8 + wb <= xb + wb / 8;
+}
+
+// Variant: the specialised-wave kernel (1) where its tiles fit one round of workgroups
+// over `cus` CUs (a deep K on few pixels, e.g. ResNet stage 4), else the two-workgroups-
+// per-CU kernel (0); from MI355X timings (256 CUs) of the ResNet stage 3 and 4 layers.
+HgemmPlan plan_hgemm(const ConvArgs &a, int cus) {
+    HgemmPlan p{};
+    p.cfast = hgemm_cfast(a);
+    HgemmInfo in{};
+    p.cfg = (hgemm_cfg_ok(a, 1) && hgemm_cfg_info(1, a, &in) && in.tiles <= cus) ? 1 : hgemm_cfg_ok(a, 0) ? 0 : -1;
+    return p;
+}
+
 // The general MFMA implicit GEMM: any shape, layout and dtype, no workspace.
 Plan igemm_plan(const ConvArgs &a, int layout, int dtype) {
     Plan p{};
@@ -369,6 +405,15 @@ Plan make_plan_default(const ConvArgs &a, int layout, int dtype, size_t ws) {
         p.halo = plan_halo(a);
         return p;
     }
+    // wide 3x3 layers with at least 256 input channels (narrower ones, e.g. ResNet stage
+    // 2, are faster on the tiled GEMM below)
+    if (hgemm_fits(a, layout, dtype) && a.Cin >= 256) {
+        p.hg = plan_hgemm(a, 256);
+        if (p.hg.cfg >= 0) {
+            p.family = FAM_HGEMM;
+            return p;
+        }
+    }
     if (layout == CONV2D_LAYOUT_NHWC && dtype != CONV2D_DTYPE_F32 && (a.Cin % 8) == 0 &&
         aligned16(a.x) && aligned16(a.w) && xbytes < (1ll << 31) && wbytes < (1ll << 31) &&
         ybytes < (1ll << 31)) {
@@ -398,10 +443,10 @@ Plan make_plan_default(const ConvArgs &a, int layout, int dtype, size_t ws) {
 // whose built-in choice is one of those families, and uses an entry only if the variant
 // is valid for the call at hand (alignment, workspace size).
 struct TunedEntry {
-    int family;  // FAM_NHWC, FAM_NCHW_VIA_NHWC, FAM_HALO or FAM_HALO_WS
-    int tile;    // NhwcTile (FAM_NHWC, FAM_NCHW_VIA_NHWC)
-    int splits;  // K slices (FAM_NHWC; 1 for FAM_NCHW_VIA_NHWC)
-    int th;      // tile height (FAM_HALO)
+    int family;  // FAM_NHWC, FAM_NCHW_VIA_NHWC, FAM_HALO, FAM_HALO_WS or FAM_HGEMM
+    int tile;    // NhwcTile (FAM_NHWC, FAM_NCHW_VIA_NHWC) or kernel variant (FAM_HGEMM)
+    int splits;  // K slices (FAM_NHWC; 1 for FAM_NCHW_VIA_NHWC and FAM_HGEMM)
+    int th;      // tile height (FAM_HALO); tile order, channel tiles fastest or not (FAM_HGEMM)
 };
 std::mutex g_tune_mu;
 std::map<std::string, TunedEntry> g_tuned;
@@ -446,7 +491,8 @@ bool halo_th_ok(const ConvArgs &a, int th) {
 // Applies the table's entry for this call, if any and valid; p is the built-in choice.
 void apply_tuned(const ConvArgs &a, int layout, int dtype, size_t ws, Plan *p) {
     if (g_tuned_n.load(std::memory_order_acquire) == 0) return;
-    if (p->family != FAM_NHWC && p->family != FAM_HALO && p->family != FAM_HALO_WS && p->family != FAM_NCHW_VIA_NHWC)
+    if (p->family != FAM_NHWC && p->family != FAM_HALO && p->family != FAM_HALO_WS && p->family != FAM_NCHW_VIA_NHWC &&
+        p->family != FAM_HGEMM)
         return;
     const std::string dev = device_tag();
     if (dev.empty()) return;
@@ -474,6 +520,12 @@ void apply_tuned(const ConvArgs &a, int layout, int dtype, size_t ws, Plan *p) {
         if (!halo_fits(a, layout, dtype) || a.Cin != 64) return;
         p->family = FAM_HALO_WS;
         p->halo = plan_halo(a);
+        p->tuned = true;
+    } else if (e.family == FAM_HGEMM) {
+        if (!hgemm_fits(a, layout, dtype) || !hgemm_cfg_ok(a, e.tile) || (e.th != 0 && e.th != 1)) return;
+        p->family = FAM_HGEMM;
+        p->hg.cfg = e.tile;
+        p->hg.cfast = e.th == 1;
         p->tuned = true;
     } else if (e.family == FAM_NHWC) {
         if (e.tile < 0 || e.tile >= NHWC_TILE_COUNT || !splits_ok(a, e.splits, ws)) return;
@@ -515,6 +567,12 @@ int describe(const Plan &p, int layout, int dtype, char *buf, int cap) {
                  p.halo.waves);
     } else if (p.family == FAM_HALO_WS) {
         snprintf(tmp, sizeof tmp, "halo3x3ws_nhwc %s th4 w4+4", dtype_name(dtype));
+    } else if (p.family == FAM_HGEMM) {
+        ConvArgs z{};
+        HgemmInfo in{};
+        (void)hgemm_cfg_info(p.hg.cfg, z, &in);
+        snprintf(tmp, sizeof tmp, "hgemm3x3_nhwc %s v%d %dx%dx%d ck%d w%d %s", dtype_name(dtype), p.hg.cfg, in.th, in.tw,
+                 in.cb, in.ck, in.waves, p.hg.cfast ? "cfast" : "pfast");
     } else if (p.family == FAM_NHWC || p.family == FAM_NCHW_VIA_NHWC) {
         snprintf(tmp, sizeof tmp, "%sigemm_nhwc_pipe%s %s %s splitk=%d%s",
                  p.family == FAM_NCHW_VIA_NHWC ? (p.chain_in ? "chained+" : p.w_ohwi ? "x_to_nhwc+" : "to_nhwc+") : "",
@@ -574,6 +632,8 @@ int launch_conv(const ConvArgs &a, const Plan &p, int layout, int dtype, const W
         rc = device_cus(&cus);
         if (rc) return rc;
         e = launch_halo3x3_ws(a, dtype, cus, st);
+    } else if (p.family == FAM_HGEMM) {
+        e = launch_hgemm3x3(a, dtype, p.hg, st);
     } else if (p.family == FAM_NHWC) {
         e = launch_igemm_nhwc(a, dtype, p.nh, p.nh.splits > 1 ? reinterpret_cast<float *>(ws.p) : nullptr, st);
     } else if (p.family == FAM_NCHW_VIA_NHWC) {
@@ -1122,7 +1182,19 @@ int tune_run(int N, int H, int W, int Cin, int Cout, int kh, int kw, int stride,
             c.nh.tile = tile;
             cands.push_back(c);
         }
-    } else if (def.family == FAM_NHWC || def.family == FAM_HALO || def.family == FAM_HALO_WS) {
+    } else if (def.family == FAM_NHWC || def.family == FAM_HALO || def.family == FAM_HALO_WS ||
+               def.family == FAM_HGEMM) {
+        if (hgemm_fits(a, layout, dtype)) {
+            for (int cfg = 0; cfg < hgemm_cfg_count(); ++cfg)
+                for (bool cf : {false, true}) {
+                    if (!hgemm_cfg_ok(a, cfg)) continue;
+                    Plan c{};
+                    c.family = FAM_HGEMM;
+                    c.hg.cfg = cfg;
+                    c.hg.cfast = cf;
+                    cands.push_back(c);
+                }
+        }
         if (halo_fits(a, layout, dtype) && a.Cin == 64 && def.family != FAM_HALO_WS) {
             Plan c{};
             c.family = FAM_HALO_WS;
@@ -1193,10 +1265,11 @@ int tune_run(int N, int H, int W, int Cin, int Cout, int kh, int kw, int stride,
     *best_us = best_ms * 1e3f / (float)reps;
     // record the winner (only for the families the planner looks up)
     if (best_out->family == FAM_NHWC || best_out->family == FAM_HALO || best_out->family == FAM_HALO_WS ||
-        best_out->family == FAM_NCHW_VIA_NHWC) {
+        best_out->family == FAM_NCHW_VIA_NHWC || best_out->family == FAM_HGEMM) {
         const std::string dev = device_tag();
         if (!dev.empty()) {
             TunedEntry t{best_out->family, best_out->nh.tile, best_out->nh.splits, best_out->halo.th};
+            if (best_out->family == FAM_HGEMM) t = TunedEntry{FAM_HGEMM, best_out->hg.cfg, 1, best_out->hg.cfast ? 1 : 0};
             std::lock_guard<std::mutex> lock(g_tune_mu);
             g_tuned[tune_key(dev, a, layout, dtype)] = t;
             g_tuned_n.store((int)g_tuned.size(), std::memory_order_release);
@@ -1427,7 +1500,9 @@ int conv2d_tune_load(const char *path) {
                                                    (t.family == FAM_NCHW_VIA_NHWC && t.tile >= 0 &&
                                                     t.tile < NHWC_TILE_COUNT && t.splits == 1) ||
                                                    (t.family == FAM_HALO && (t.th == 4 || t.th == 8)) ||
-                                                   (t.family == FAM_HALO_WS && t.th == 4));
+                                                   (t.family == FAM_HALO_WS && t.th == 4) ||
+                                                   (t.family == FAM_HGEMM && t.tile >= 0 && t.tile < hgemm_cfg_count() &&
+                                                    t.splits == 1 && (t.th == 0 || t.th == 1)));
         if (!ok) {
             fclose(f);
             return set_error(CONV2D_EINVAL, "conv2d_tune_load: %s line %d is not a tuned-plan record", path, lineno);

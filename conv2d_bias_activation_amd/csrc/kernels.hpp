@@ -85,6 +85,32 @@ hipError_t launch_halo3x3(const ConvArgs &a, int dtype, const HaloPlan &p, hipSt
 // persistent workgroup of 8 waves per CU (grid_cap workgroups). Limits as launch_halo3x3.
 hipError_t launch_halo3x3_ws(const ConvArgs &a, int dtype, int grid_cap, hipStream_t st);
 
+// Geometry of one hgemm launch (host-computed).
+struct HgemmGeo {
+    int tiles_x, tiles_y, tiles_c;  // output tiles along W, H and the output channels
+    int ntiles_p;                   // pixel tiles (N * tiles_y * tiles_x)
+    int cfast;                      // consecutive tile ids vary the channel tile fastest
+};
+
+struct HgemmPlan {
+    int cfg;     // kernel variant (tile shape, wave grid, ring depth, K chunk)
+    bool cfast;  // tile order: channel tiles fastest (true) or pixel tiles fastest
+};
+
+struct HgemmInfo {
+    int ck;           // input channels per K chunk
+    int th, tw, cb;   // tile: output rows, columns, channels
+    int waves, lds;   // waves and LDS bytes per workgroup
+    long long tiles;  // workgroups of the launch
+};
+
+// 3x3 stride-1 pad-1 channel-last 16-bit convolution of wide layers with halo tiles
+// and weights staged per K chunk: Cin a multiple of the variant's K chunk (32 or 64),
+// Cout % 8 == 0, y and the residual 16-byte aligned (a.vec_out), x, w and y under 2 GiB.
+hipError_t launch_hgemm3x3(const ConvArgs &a, int dtype, const HgemmPlan &p, hipStream_t st);
+int hgemm_cfg_count();
+bool hgemm_cfg_info(int cfg, const ConvArgs &a, HgemmInfo *out);
+
 // The same convolution for Cin 16 or 32 followed by the 3x3 stride-2 pad-1 max pool in
 // one kernel: only the pooled map is written, to y ([N, PH, PW, Cout], PH = (H-1)/2 + 1,
 // 16-byte aligned); no residual. About grid_cap workgroups of 4 waves (two per CU).

@@ -79,7 +79,7 @@ def test_plan_names_a_kernel_for_every_workload_shape():
              ((2, 23, 19, 3, 32, 3, 3, 2, 1, 2, 0, bf16), "direct_nhwc"),  # W % 8 != 0
              ((4, 80, 80, 512, 256, 1, 1, 1, 0, 1, 0, bf16), "igemm_nhwc_pipe"),
              ((1, 68, 120, 240, 240, 3, 3, 1, 1, 3, 1, f16), "to_nhwc+igemm_nhwc_pipe"),
-             ((4, 40, 40, 256, 256, 3, 3, 1, 1, 1, 0, bf16), "igemm_nhwc_pipe"),
+             ((4, 40, 40, 256, 256, 3, 3, 1, 1, 1, 0, bf16), "hgemm3x3_nhwc"),
              ((4, 320, 320, 32, 64, 3, 3, 1, 1, 1, 0, bf16), "halo3x3_nhwc"),
              ((4, 160, 160, 64, 64, 3, 3, 1, 1, 1, 0, bf16), "halo3x3ws_nhwc"),
              ((4, 160, 160, 64, 128, 3, 3, 2, 1, 1, 0, bf16), "igemm_nhwc_pipe")]
@@ -102,7 +102,7 @@ def test_conv_pool_plan_and_argument_checks():
     # channel-first 16-bit layers leave the workspace to the conv output: the general kernel
     assert c2d.plan_maxpool(1, 17, 23, 40, 72, 3, 3, 2, 1, 1, 1, bf16).startswith("igemm_nchw")
     # split-K is turned off for the same reason
-    assert "splitk=1" in c2d.plan_maxpool(1, 10, 10, 512, 512, 3, 3, 1, 1, 1, 0, bf16)
+    assert "splitk=1" in c2d.plan_maxpool(1, 10, 10, 512, 512, 3, 3, 2, 1, 1, 0, bf16)
     # an unpooled conv output over the 64 MiB workspace
     with pytest.raises(c2d.Conv2dError) as e:
         c2d.plan_maxpool(4, 640, 640, 64, 64, 3, 3, 1, 1, 1, 0, bf16)
@@ -382,12 +382,15 @@ def test_workspace_registration_and_sizes():
     assert lib.conv2d_set_workspace(None, 4096) == c2d.EINVAL                 # null with a size
     assert lib.conv2d_set_workspace(None, 0) == c2d.OK
     c2d.tune_clear()
-    # a deep-K layer with few tiles: split-K in three, 3 * M * Cout fp32 partial sums
-    deep = (4, 20, 20, 512, 512, 3, 3, 1, 1, 1, nhwc, bf16)
+    # a deep-K strided layer with few tiles: split-K in three, 3 * M * Cout fp32 partial sums
+    deep = (4, 20, 20, 512, 512, 3, 3, 2, 1, 1, nhwc, bf16)
     assert "splitk=3" in c2d.plan(*deep)
-    assert c2d.workspace_size(*deep) == 3 * 1600 * 512 * 4
+    assert c2d.workspace_size(*deep) == 3 * 400 * 512 * 4
     assert "splitk=1" in c2d.plan(*deep, workspace_bytes=0)
-    assert "splitk=1" in c2d.plan(*deep, workspace_bytes=3 * 1600 * 512 * 4 - 1)
+    assert "splitk=1" in c2d.plan(*deep, workspace_bytes=3 * 400 * 512 * 4 - 1)
+    # the same layer at stride 1: the halo-tile GEMM kernel, which needs no workspace
+    assert c2d.plan(4, 20, 20, 512, 512, 3, 3, 1, 1, 1, nhwc, bf16).startswith("hgemm3x3_nhwc")
+    assert c2d.workspace_size(4, 20, 20, 512, 512, 3, 3, 1, 1, 1, nhwc, bf16) == 0
     # a channel-first 16-bit layer: channel-last copies of x and w (each rounded to 256 bytes)
     ifn = (1, 68, 120, 240, 240, 3, 3, 1, 1, 3, nchw, f16)
     xb, wb = 68 * 120 * 240 * 2, 240 * 9 * 240 * 2
