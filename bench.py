@@ -29,7 +29,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16/f16 matrix peak
+PEAK_F32_TFLOPS = 157.3     # MI355X dense fp32 matrix peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+COLD_BYTES = 512 << 20      # a cold launch rotates over buffer copies totalling at least this
+
+
+def matrix_peak(dtype):
+    """Dense matrix-core peak (TFLOP/s) for layers stored in `dtype`."""
+    return PEAK_F32_TFLOPS if dtype == "f32" else PEAK_BF16_TFLOPS
 
 # name -> (builder, config description)
 WORKLOADS = {
@@ -50,6 +57,8 @@ def parse():
                    help="replay the library's stack graph (conv2d_stack_graph_*) per step, a torch-captured "
                         "HIP graph of the same calls, or launch eagerly")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cold-sets", type=int, default=8,
+                   help="copies of the network the cold step timing rotates over (0: no cold timing)")
     p.add_argument("--layer-reps", type=int, default=20)
     p.add_argument("--layers-out", default=None, help="write per-layer timings (JSON) here")
     # counter runs (rocprofv3 --pmc): launch one kernel group, or a plain copy of known size,
@@ -158,13 +167,15 @@ class Net:
                     op = c2d.Op(c2d.OP_CONV_MAXPOOL, *[a.value if isinstance(a, ctypes.c_void_p) else a
                                                        for a in args[:4] + [None] + args[4:5] + args[5:15]])
                     self.layers.append(dict(name=spec.name + "+" + nxt.name, fn=self.lib.conv2d_fused_maxpool3x3s2,
-                                            args=args, flops=flops, bytes=nbytes, plan=plan, keep=keep, op=op))
+                                            args=args, flops=flops, bytes=nbytes, plan=plan, keep=keep, op=op,
+                                            tens={0: src, 1: wdev, 2: bdev, 3: adev, 4: out}, outs=(4,)))
                     self.t[nxt.out] = out
                     skip.add(i + 1)
                     continue
                 op = c2d.Op(c2d.OP_CONV, *[a.value if isinstance(a, ctypes.c_void_p) else a for a in args[:16]])
                 self.layers.append(dict(name=spec.name, fn=self.lib.conv2d_fused, args=args,
-                                        flops=flops, bytes=nbytes, plan=plan, keep=keep, op=op))
+                                        flops=flops, bytes=nbytes, plan=plan, keep=keep, op=op,
+                                        tens={0: src, 1: wdev, 2: bdev, 3: adev, 4: res, 5: out}, outs=(5,)))
             else:
                 if spec.kind == "max":
                     oh, ow, fn = (h - 1) // 2 + 1, (w - 1) // 2 + 1, self.lib.maxpool3x3s2
@@ -179,7 +190,8 @@ class Net:
                 op = c2d.Op(c2d.OP_MAXPOOL if spec.kind == "max" else c2d.OP_AVGPOOL, src.data_ptr(), None, None,
                             None, None, out.data_ptr(), n, h, w, c, c, 0, 0, 0, 0, 0)
                 self.layers.append(dict(name=spec.name, fn=fn, args=args, flops=0,
-                                        bytes=esz * (src.numel() + out.numel()), plan=plan, keep=(), op=op))
+                                        bytes=esz * (src.numel() + out.numel()), plan=plan, keep=(), op=op,
+                                        tens={0: src, 1: out}, outs=(1,)))
             self.t[spec.out] = out
         self.flops = sum(L["flops"] for L in self.layers)
         self.layout, self.dtype = lay, dt
@@ -278,12 +290,78 @@ def time_layers(torch, net, reps):
     return out
 
 
+def time_layers_cold(torch, net, reps):
+    """Per-layer average launch durations (ms) with cold caches: each layer's inputs,
+    weights and output are copied into S sets (S >= 8, together at least COLD_BYTES, so
+    that neither the L2s nor the 256 MB last-level cache can hold them), and max(reps, S)
+    back-to-back launches rotate over the sets between one pair of HIP events."""
+    stream = torch.cuda.current_stream()
+    h = ctypes.c_void_p(stream.cuda_stream)
+    net.use_workspace()
+    out = []
+    for L in net.layers:
+        tens = {k: t for k, t in L["tens"].items() if t is not None}
+        nbytes = sum(t.numel() * t.element_size() for t in tens.values())
+        sets = max(8, -(-COLD_BYTES // nbytes))
+        copies = []
+        for _ in range(sets):
+            args = list(L["args"])
+            keep = []
+            for k, t in tens.items():
+                c = torch.empty_like(t) if k in L["outs"] else t.clone()
+                keep.append(c)
+                args[k] = ctypes.c_void_p(c.data_ptr())
+            copies.append((args, keep))
+        n = max(reps, sets)
+        for args, _ in copies[:2]:
+            rc = L["fn"](*args, h)
+            if rc != 0:
+                raise RuntimeError(f"{L['name']}: {net.c2d.last_error()}")
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        prefill(torch, ms=2.0 + 0.03 * n)
+        e0.record(stream)
+        for r in range(n):
+            L["fn"](*copies[r % sets][0], h)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) / n)
+        del copies
+    torch.cuda.empty_cache()
+    return out
+
+
+def time_steps_cold(torch, nets, steps):
+    """Step time (ms) with cold caches: the steps rotate over independent copies of the
+    whole network (inputs, weights, activations, workspace), one library stack graph
+    each, so a step's data was last touched len(nets) - 1 steps earlier."""
+    stream = torch.cuda.current_stream()
+    graphs = []
+    for net in nets:
+        net.step(stream)
+        graphs.append(net.c2d.StackGraph([L["op"] for L in net.layers], layout=["nhwc", "nchw"][net.layout],
+                                         dtype=net.dtype, workspace=net.ws if net.ws is not None else False))
+    for g in graphs:
+        g.launch(stream)
+    torch.cuda.synchronize()
+    n = max(steps, len(nets))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    prefill(torch, ms=min(200.0, 2.0 * n))
+    e0.record(stream)
+    for i in range(n):
+        graphs[i % len(graphs)].launch(stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
 # Source files whose text compiles into each kernel family's device code (matched on the
 # start of the plan name); the declarations-only kernels.hpp is left out. A traffic record
 # is only used while these files are unchanged.
 KERNEL_SOURCES = [
     ("igemm_nhwc_pipe", ["conv_igemm_nhwc.hip", "igemm_common.hpp", "common.hpp"]),
     ("hgemm3x3", ["conv_hgemm.hip", "igemm_common.hpp", "common.hpp"]),
+    ("hgemmws3x3", ["conv_hgemm.hip", "igemm_common.hpp", "common.hpp"]),
     ("halo3x3ws", ["conv_halo_ws.hip", "igemm_common.hpp", "common.hpp"]),
     ("halo3x3", ["conv_halo.hip", "igemm_common.hpp", "common.hpp"]),
     ("stem3x3", ["conv_stem.hip", "igemm_common.hpp", "common.hpp"]),
@@ -297,6 +375,7 @@ KERNEL_SOURCES = [
 KERNEL_SYMBOLS = [
     ("igemm_nhwc_pipe", "3c2d17igemm_nhwc_kernel"),
     ("hgemm3x3", "3c2d15hgemm3x3_kernel"),
+    ("hgemmws3x3", "3c2d17hgemmws3x3_kernel"),
     ("halo3x3ws", "3c2d17halo3x3_ws_kernel"),
     ("halo3x3", "3c2d14halo3x3_kernel"),
     ("stem3x3", "stem3_"),  # stem3_kernel, stem3_pool_kernel
@@ -404,7 +483,9 @@ def write_traffic(src, copy_mib, plan):
             raise SystemExit(f"no kernel named like {symbol!r} in {path}")
         name = max(names, key=lambda k: d[k][0])  # the one launched most often in that run
         return name, d[name][1]
-    family = plan.split("+")[-1]  # a channel-first plan's kernel is the channel-last one after the copy
+    # a channel-first plan's kernel is the channel-last one after the copy ("to_nhwc+...")
+    head, _, rest = plan.partition(" ")
+    family = head.split("+")[-1] + (" " + rest if rest else "")
     symbol = next((s for prefix, s in KERNEL_SYMBOLS if family.startswith(prefix)), "")
     _, cf = busiest(os.path.join(src, "copy_fetch"), "FETCH_SIZE")
     _, cw = busiest(os.path.join(src, "copy_write"), "WRITE_SIZE")
@@ -600,6 +681,23 @@ def main():
     value = net.flops / (ms * 1e-3) / 1e12
 
     layer_ms = time_layers(torch, net, args.layer_reps)
+    cold = None
+    cold_layer_ms = [None] * len(net.layers)
+    if args.cold_sets > 0:
+        cold_layer_ms = time_layers_cold(torch, net, args.layer_reps)
+        nets = [net] + [Net(work, dev, fuse_pool=not args.no_fuse_pool, weights_ohwi=not args.oihw)
+                        for _ in range(args.cold_sets - 1)]
+        set_mb = sum(t.numel() * t.element_size() for t in list(net.t.values()) +
+                     [w for L in net.layers for w in L["keep"] if w is not None] +
+                     ([net.ws] if net.ws is not None else [])) / 1e6
+        cold_ms = time_steps_cold(torch, nets, args.steps)
+        del nets
+        torch.cuda.empty_cache()
+        cold = dict(ms_per_step=round(cold_ms, 4), value=round(net.flops / (cold_ms * 1e-3) / 1e12, 3),
+                    sets=args.cold_sets, mb_per_set=round(set_mb, 1),
+                    note="steps rotate over independent copies of the whole network (inputs, weights, "
+                         "activations, workspace), so no step finds its data in the L2s or the 256 MB "
+                         "last-level cache")
     groups = {}
     for L, t in zip(net.layers, layer_ms):
         g = groups.setdefault(L["plan"], dict(ms=0.0, flops=0, bytes=0, launches=0))
@@ -610,34 +708,47 @@ def main():
     # The dominant kernel: the single-kernel launch group with the most time per step
     # (a split-K layer runs two kernels per call, a channel-first layer three, so
     # neither group is one kernel).
-    single = [k for k in groups if ("splitk=1" in k or "splitk" not in k) and "+" not in k and " then " not in k]
+    single = [k for k in groups
+              if ("splitk=1" in k or "splitk" not in k) and "+" not in k.split()[0] and " then " not in k]
     if not single:
         single = list(groups)
     dom_plan = max(single, key=lambda k: groups[k]["ms"])
     g = groups[dom_plan]
     avg_ms = g["ms"] / g["launches"]
-    if g["flops"] > 0 and g["flops"] / g["bytes"] >= PEAK_BF16_TFLOPS / PEAK_HBM_GBS * 1e3:
-        achieved = g["flops"] / g["launches"] / (avg_ms * 1e-3) / 1e12
-        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=PEAK_BF16_TFLOPS,
-                    unit="TFLOP/s", frac=round(achieved / PEAK_BF16_TFLOPS, 4))
+    peak = matrix_peak(work.dtype)
+    mfma_bound = g["flops"] > 0 and g["flops"] / g["bytes"] >= peak / PEAK_HBM_GBS * 1e3
+    def rate(ms_):
+        return (g["flops"] / g["launches"] / (ms_ * 1e-3) / 1e12 if mfma_bound
+                else g["bytes"] / g["launches"] / (ms_ * 1e-3) / 1e9)
+    achieved = rate(avg_ms)
+    if mfma_bound:
+        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=peak,
+                    unit="TFLOP/s", frac=round(achieved / peak, 4))
     else:
-        achieved = g["bytes"] / g["launches"] / (avg_ms * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
                     frac=round(achieved / PEAK_HBM_GBS, 4))
     roof["traffic"] = measured_traffic(dom_plan, None)
     roof["kernel"] = dom_plan
     roof["avg_launch_us"] = round(avg_ms * 1e3, 2)
     roof["launches_per_step"] = g["launches"]
+    if cold is not None:
+        cold_dom = sum(t for L, t in zip(net.layers, cold_layer_ms) if L["plan"] == dom_plan) / g["launches"]
+        roof["cold_avg_launch_us"] = round(cold_dom * 1e3, 2)
+        roof["cold_achieved"] = round(rate(cold_dom), 2 if mfma_bound else 1)
+        roof["cold_frac"] = round(rate(cold_dom) / (peak if mfma_bound else PEAK_HBM_GBS), 4)
 
     if args.layers_out:
         rows = []
-        for L, t in zip(net.layers, layer_ms):
+        for L, t, tc in zip(net.layers, layer_ms, cold_layer_ms):
             rows.append(dict(name=L["name"], plan=L["plan"], us=round(t * 1e3, 2),
                              tflops=round(L["flops"] / (t * 1e-3) / 1e12, 1) if L["flops"] else None,
                              gbs=round(L["bytes"] / (t * 1e-3) / 1e9, 1),
-                             mfma_frac=round(L["flops"] / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+                             mfma_frac=round(L["flops"] / (t * 1e-3) / 1e12 / peak, 4)
                              if L["flops"] else None,
-                             hbm_frac=round(L["bytes"] / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)))
+                             hbm_frac=round(L["bytes"] / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                             cold_us=round(tc * 1e3, 2) if tc is not None else None,
+                             cold_hbm_frac=round(L["bytes"] / (tc * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+                             if tc is not None else None))
         os.makedirs(os.path.dirname(os.path.abspath(args.layers_out)), exist_ok=True)
         with open(args.layers_out, "w") as f:
             json.dump(dict(step_ms=ms, sum_layer_ms=sum(layer_ms), layers=rows), f, indent=1)
@@ -663,6 +774,7 @@ def main():
                    "gflop_per_step": round(net.flops / 1e9, 3), "launch": args.mode,
                    "tuned_shapes": tuned},
         "roofline": roof,
+        "cold": cold,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

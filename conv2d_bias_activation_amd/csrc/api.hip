@@ -571,8 +571,8 @@ int describe(const Plan &p, int layout, int dtype, char *buf, int cap) {
         ConvArgs z{};
         HgemmInfo in{};
         (void)hgemm_cfg_info(p.hg.cfg, z, &in);
-        snprintf(tmp, sizeof tmp, "hgemm3x3_nhwc %s v%d %dx%dx%d ck%d w%d %s", dtype_name(dtype), p.hg.cfg, in.th, in.tw,
-                 in.cb, in.ck, in.waves, p.hg.cfast ? "cfast" : "pfast");
+        snprintf(tmp, sizeof tmp, "%s %s v%d %dx%dx%d ck%d w%d %s", in.ws ? "hgemmws3x3_nhwc" : "hgemm3x3_nhwc",
+                 dtype_name(dtype), p.hg.cfg, in.th, in.tw, in.cb, in.ck, in.waves, p.hg.cfast ? "cfast" : "pfast");
     } else if (p.family == FAM_NHWC || p.family == FAM_NCHW_VIA_NHWC) {
         snprintf(tmp, sizeof tmp, "%sigemm_nhwc_pipe%s %s %s splitk=%d%s",
                  p.family == FAM_NCHW_VIA_NHWC ? (p.chain_in ? "chained+" : p.w_ohwi ? "x_to_nhwc+" : "to_nhwc+") : "",

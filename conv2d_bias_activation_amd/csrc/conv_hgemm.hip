@@ -740,10 +740,13 @@ bool hgemm_cfg_info(int cfg, const ConvArgs &a, HgemmInfo *o) {
         o->th = C::TH;
         o->tw = C::TW;
         o->cb = C::CB;
-        if constexpr (requires { C::NWV; })
+        if constexpr (requires { C::NWV; }) {
             o->waves = C::NWV;
-        else
+            o->ws = true;
+        } else {
             o->waves = C::NW;
+            o->ws = false;
+        }
         o->lds = C::LDS;
         o->tiles = hg_tiles<C>(a);
         return true;

@@ -101,6 +101,7 @@ struct HgemmInfo {
     int ck;           // input channels per K chunk
     int th, tw, cb;   // tile: output rows, columns, channels
     int waves, lds;   // waves and LDS bytes per workgroup
+    bool ws;          // the specialised-wave kernel (loader and compute waves)
     long long tiles;  // workgroups of the launch
 };
 

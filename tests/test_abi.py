@@ -389,7 +389,7 @@ def test_workspace_registration_and_sizes():
     assert "splitk=1" in c2d.plan(*deep, workspace_bytes=0)
     assert "splitk=1" in c2d.plan(*deep, workspace_bytes=3 * 400 * 512 * 4 - 1)
     # the same layer at stride 1: the halo-tile GEMM kernel, which needs no workspace
-    assert c2d.plan(4, 20, 20, 512, 512, 3, 3, 1, 1, 1, nhwc, bf16).startswith("hgemm3x3_nhwc")
+    assert c2d.plan(4, 20, 20, 512, 512, 3, 3, 1, 1, 1, nhwc, bf16).startswith("hgemmws3x3_nhwc")
     assert c2d.workspace_size(4, 20, 20, 512, 512, 3, 3, 1, 1, 1, nhwc, bf16) == 0
     # a channel-first 16-bit layer: channel-last copies of x and w (each rounded to 256 bytes)
     ifn = (1, 68, 120, 240, 240, 3, 3, 1, 1, 3, nchw, f16)

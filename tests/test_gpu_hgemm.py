@@ -82,7 +82,8 @@ def test_every_variant_meets_the_gate(case, tmp_path):
             c2d.tune_clear()
             assert c2d.tune_load(str(table)) == 2
             name = c2d.plan(n, h, w, cin, cout, 3, 3, 1, 1, actc, c2d.LAYOUT_NHWC, dt)
-            assert name.startswith(f"hgemm3x3_nhwc {dtype} v{v} ") and name.endswith(" tuned"), name
+            kernel = "hgemmws3x3_nhwc" if v in (1, 2) else "hgemm3x3_nhwc"
+            assert name.startswith(f"{kernel} {dtype} v{v} ") and name.endswith(" tuned"), name
             assert ("cfast" if order else "pfast") in name and f" ck{CK[v]} " in name, name
             print(f"variant {v} order {order}: {name}", flush=True)
             y = c2d.conv2d_fused(xd, wd, bd, ad, rd, stride=1, pad=1, act=act, layout="nhwc", res_before_act=pre)
@@ -96,7 +97,7 @@ def test_default_plan_of_wide_layers():
     bf = c2d.DTYPE_BF16
     plan = lambda n, h, w, c: c2d.plan(n, h, w, c, c, 3, 3, 1, 1, c2d.ACT_RELU, c2d.LAYOUT_NHWC, bf)
     assert plan(4, 40, 40, 256).startswith("hgemm3x3_nhwc bf16 v0 ")
-    assert plan(4, 20, 20, 512).startswith("hgemm3x3_nhwc bf16 v1 ")
+    assert plan(4, 20, 20, 512).startswith("hgemmws3x3_nhwc bf16 v1 ")
     assert plan(4, 80, 80, 128).startswith("igemm_nhwc_pipe")
 
 
