@@ -331,12 +331,15 @@ bool halo_fits(const ConvArgs &a, int layout, int dtype) {
            (a.Cout % 8) == 0 && a.vec_out && aligned16(a.x) && aligned16(a.w);
 }
 
-// Matrix-core stem kernel: 3-channel channel-last 16-bit image, 3x3, pad 1.
+// Matrix-core stem kernels: 3-channel channel-last image, 3x3, pad 1; 16-bit storage
+// (32x32x16 products) or fp32 (32x32x2 fp32 products).
 bool stem_fits(const ConvArgs &a, int layout, int dtype) {
-    return layout == CONV2D_LAYOUT_NHWC && dtype != CONV2D_DTYPE_F32 && a.Cin == 3 && a.kh == 3 && a.kw == 3 &&
-           a.pad == 1 && (a.stride == 1 || a.stride == 2) && a.Cout <= 64 && (a.Cout % 8) == 0 && a.vec_out &&
-           aligned16(a.x) && (a.W % 8) == 0 && a.W <= 3000 && (long long)a.N * a.H * a.W * 6 < (1ll << 31) &&
-           (long long)a.M * a.Cout * 2 < (1ll << 31);
+    const bool f32 = dtype == CONV2D_DTYPE_F32;
+    const int eb = dtype_bytes(dtype);
+    return layout == CONV2D_LAYOUT_NHWC && a.Cin == 3 && a.kh == 3 && a.kw == 3 && a.pad == 1 &&
+           (a.stride == 1 || a.stride == 2) && a.Cout <= 64 && (a.Cout % (f32 ? 4 : 8)) == 0 && a.vec_out &&
+           aligned16(a.x) && (a.W % (f32 ? 4 : 8)) == 0 && a.W <= (f32 ? 1700 : 3000) &&
+           (long long)a.N * a.H * a.W * 3 * eb < (1ll << 31) && (long long)a.M * a.Cout * eb < (1ll << 31);
 }
 
 // Halo-tile GEMM kernel for wide 3x3 stride-1 layers (channel-last, 16-bit, Cin a

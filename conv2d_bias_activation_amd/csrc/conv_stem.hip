@@ -419,6 +419,7 @@ hipError_t launch_stem3_maxpool(const ConvArgs &a, void *y, int dtype, hipStream
     switch (dtype) {
     case CONV2D_DTYPE_BF16: return launch_stem_pool_d<bf16>(a, y, st);
     case CONV2D_DTYPE_F16: return launch_stem_pool_d<f16>(a, y, st);
+    case CONV2D_DTYPE_F32: return launch_stem3_f32_maxpool(a, y, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -447,6 +448,7 @@ hipError_t launch_stem3(const ConvArgs &a, int dtype, hipStream_t st) {
     switch (dtype) {
     case CONV2D_DTYPE_BF16: return launch_stem_d<bf16>(a, st);
     case CONV2D_DTYPE_F16: return launch_stem_d<f16>(a, st);
+    case CONV2D_DTYPE_F32: return launch_stem3_f32(a, st);
     default: return hipErrorInvalidValue;
     }
 }

@@ -120,7 +120,14 @@ hipError_t launch_halo3x3_maxpool(const ConvArgs &a, void *y, int dtype, int gri
 // 3x3 convolution of a 3-channel channel-last 16-bit image on the matrix cores:
 // stride 1 or 2, pad 1, Cout <= 64 with Cout % 8 == 0, W % 8 == 0 and W <= 3000, x
 // 16-byte aligned, y and the residual 16-byte aligned (a.vec_out), tensors under 2 GiB.
+// fp32 storage (dtype CONV2D_DTYPE_F32) goes to launch_stem3_f32.
 hipError_t launch_stem3(const ConvArgs &a, int dtype, hipStream_t st);
+
+// The same for fp32 storage (32x32x2 fp32 products): Cout <= 64 with Cout % 4 == 0,
+// W % 4 == 0 and W <= 1700, same alignment and size limits.
+hipError_t launch_stem3_f32(const ConvArgs &a, hipStream_t st);
+// ... followed by the 3x3 stride-2 pad-1 max pool, only the pooled map written to y.
+hipError_t launch_stem3_f32_maxpool(const ConvArgs &a, void *y, hipStream_t st);
 
 // The same convolution followed by the 3x3 stride-2 pad-1 max pool in one kernel: only
 // the pooled map is written, to y ([N, PH, PW, Cout] with PH = (OH - 1) / 2 + 1, 16-byte

@@ -74,7 +74,8 @@ def test_plan_names_a_kernel_for_every_workload_shape():
     bf16, f16, f32 = c2d.DTYPE_BF16, c2d.DTYPE_F16, c2d.DTYPE_F32
     # (shape, expected kernel family): the workload layers and the narrow/stem special cases
     cases = [((1, 32, 32, 16, 32, 3, 3, 1, 1, 1, 0, f32), "igemm_nhwc_vec"),
-             ((1, 640, 640, 3, 32, 3, 3, 2, 1, 2, 0, f32), "direct_nhwc"),
+             ((1, 640, 640, 3, 32, 3, 3, 2, 1, 2, 0, f32), "stem3x3_mfma f32"),
+             ((1, 640, 642, 3, 32, 3, 3, 2, 1, 2, 0, f32), "direct_nhwc"),  # W % 4 != 0
              ((1, 640, 640, 3, 32, 3, 3, 2, 1, 2, 0, bf16), "stem3x3_mfma"),
              ((2, 23, 19, 3, 32, 3, 3, 2, 1, 2, 0, bf16), "direct_nhwc"),  # W % 8 != 0
              ((4, 80, 80, 512, 256, 1, 1, 1, 0, 1, 0, bf16), "igemm_nhwc_pipe"),
@@ -97,8 +98,9 @@ def test_conv_pool_plan_and_argument_checks():
     assert c2d.plan_maxpool(1, 640, 640, 3, 32, 3, 3, 2, 1, 2, 0, bf16) == "stem3x3_mfma bf16 fused with maxpool3x3s2"
     assert c2d.plan_maxpool(4, 320, 320, 32, 64, 3, 3, 1, 1, 1, 0, bf16).endswith("fused with maxpool3x3s2")
     assert c2d.plan_maxpool(4, 160, 160, 64, 64, 3, 3, 1, 1, 1, 0, bf16).endswith("then maxpool3x3s2")
-    assert c2d.plan_maxpool(1, 640, 640, 3, 32, 3, 3, 2, 1, 2, 0, f32).startswith("direct_nhwc")
-    assert c2d.plan_maxpool(1, 640, 640, 3, 32, 3, 3, 2, 1, 2, 0, f32).endswith("then maxpool3x3s2")
+    assert c2d.plan_maxpool(1, 640, 640, 3, 32, 3, 3, 2, 1, 2, 0, f32) == "stem3x3_mfma f32 fused with maxpool3x3s2"
+    assert c2d.plan_maxpool(1, 640, 642, 3, 32, 3, 3, 2, 1, 2, 0, f32).startswith("direct_nhwc")
+    assert c2d.plan_maxpool(1, 640, 642, 3, 32, 3, 3, 2, 1, 2, 0, f32).endswith("then maxpool3x3s2")
     # channel-first 16-bit layers leave the workspace to the conv output: the general kernel
     assert c2d.plan_maxpool(1, 17, 23, 40, 72, 3, 3, 2, 1, 1, 1, bf16).startswith("igemm_nchw")
     # split-K is turned off for the same reason

@@ -147,6 +147,12 @@ STEM = [
     (1, 1, 8, 32, 2, "relu", None, "bf16"),
     (2, 130, 136, 64, 2, "relu", "pre", "bf16"),
     (1, 40, 72, 24, 1, "silu", None, "f16"),
+    # fp32 storage: the 32x32x2 fp32 kernel (Cout % 4 == 0, W % 4 == 0)
+    (1, 17, 24, 32, 2, "silu", None, "f32"),
+    (2, 21, 20, 64, 1, "relu", "pre", "f32"),
+    (1, 9, 36, 12, 2, "prelu", "post", "f32"),
+    (1, 1, 4, 32, 2, "relu", None, "f32"),
+    (3, 33, 132, 40, 1, "none", None, "f32"),
 ]
 
 
@@ -157,7 +163,7 @@ def test_stem(case):
     x, spec, r = wl.random_conv_case(seed, n=n, h=h, w=w, cin=3, cout=cout, k=3, stride=s, pad=1,
                                      act=act, layout="nhwc", dtype=dtype, residual=res is not None,
                                      res_before_act=res == "pre", x_dist="uniform")
-    plan = c2d.plan(n, h, w, 3, cout, 3, 3, s, 1, 0, 0, {"bf16": 1, "f16": 2}[dtype])
+    plan = c2d.plan(n, h, w, 3, cout, 3, 3, s, 1, 0, 0, {"f32": 0, "bf16": 1, "f16": 2}[dtype])
     print(f"case {case} plan {plan}", flush=True)
     assert plan.startswith("stem3x3"), plan
     y = _gpu_conv(x, spec, r, "nhwc")

@@ -74,6 +74,12 @@ FUSED = [
     (1, 40, 488, 24, 1, "silu", "f16"),
     (1, 61, 960, 32, 2, "prelu", "bf16"),
     (2, 33, 1208, 8, 1, "relu", "bf16"),
+    # fp32 storage: the 32x32x2 fp32 kernel
+    (1, 17, 24, 32, 2, "silu", "f32"),
+    (2, 21, 20, 64, 1, "relu", "f32"),
+    (1, 9, 36, 12, 2, "prelu", "f32"),
+    (1, 1, 4, 32, 2, "relu", "f32"),
+    (1, 61, 964, 32, 2, "none", "f32"),
 ]
 
 
@@ -85,7 +91,7 @@ def test_fused_stem_maxpool(case):
     _check(x, spec, "nhwc", dtype, str(case), want_fused=True)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_fused_stem_maxpool_full_image(dtype):
     """The 640x640 stem conv (3 -> 32, stride 2, SiLU) and its max pool: 1x160x160x32."""
     wk = wl.conv2_stem(dtype)
@@ -123,13 +129,13 @@ def test_fused_halo_maxpool(case):
 # Shapes outside the fused kernel: the conv into the library scratch, then the pool.
 # (n, h, w, cin, cout, k, stride, pad, act, layout, dtype, same kernels as two calls)
 UNFUSED = [
-    (1, 23, 19, 3, 32, 3, 2, 1, "silu", "nhwc", "f32", True),     # fp32 stem: direct kernel
+    (1, 23, 19, 3, 32, 3, 2, 1, "silu", "nhwc", "f32", True),     # fp32 stem, W % 4 != 0: direct kernel
     (1, 20, 22, 3, 32, 3, 2, 1, "relu", "nhwc", "bf16", True),    # W % 8 != 0
     (2, 18, 16, 3, 72, 3, 2, 1, "relu", "nhwc", "bf16", True),    # Cout > 64
     (1, 30, 26, 64, 64, 3, 1, 1, "prelu", "nhwc", "f16", True),   # halo kernel, Cin 64
     (2, 17, 23, 40, 72, 3, 2, 1, "relu", "nchw", "f16", False),   # channel-first: general kernel
     (1, 16, 18, 3, 16, 3, 2, 1, "silu", "nchw", "f32", True),
-    (1, 10, 10, 512, 512, 3, 1, 1, "relu", "nhwc", "bf16", False),  # split-K turned off
+    (1, 10, 10, 512, 512, 3, 1, 1, "relu", "nhwc", "bf16", False),  # wide layer: halo-tile GEMM
     (1, 12, 14, 16, 24, 5, 2, 2, "none", "nhwc", "bf16", True),
 ]
 
