@@ -41,6 +41,7 @@ def matrix_peak(dtype):
 # name -> (builder, config description)
 WORKLOADS = {
     "resnet18d": ("conv5_resnet18d", "resnet18d_backbone_4x640x640_nhwc_bf16"),
+    "conv1": ("conv1_single", "conv3x3_16to32_relu_1x32x32_nhwc_f32"),
     "ifnet": ("conv4_ifnet_block", "ifnet_convblock_8x_conv3x3_240ch_68x120_nchw_f16"),
     "pointwise": ("conv3_pointwise", "conv1x1_512to256_relu_4x80x80_nhwc_bf16"),
     "stem_bf16": ("conv2_stem_bf16", "stem_conv3x3s2_3to32_silu_maxpool_1x640x640_nhwc_bf16"),
@@ -57,6 +58,9 @@ def parse():
                    help="replay the library's stack graph (conv2d_stack_graph_*) per step, a torch-captured "
                         "HIP graph of the same calls, or launch eagerly")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--oracle-times", default=None, metavar="JSON",
+                   help="time the CPU oracle on every config (all host threads; one thread for the "
+                        "single-conv configs), check that 1 and all threads give the same bits, write JSON, exit")
     p.add_argument("--cold-sets", type=int, default=8,
                    help="copies of the network the cold step timing rotates over (0: no cold timing)")
     p.add_argument("--layer-reps", type=int, default=20)
@@ -415,6 +419,83 @@ def measured_traffic(plan, launches_bytes):
     return k.get("bytes_per_launch")
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def oracle_forward(work, threads=0):
+    """The oracle on a whole workload (fp64 layers, each output rounded to the storage
+    dtype before the next layer reads it). Returns (flops, seconds, final output)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import workloads as wl
+
+    t = {"x": work.x.to(torch.float64).numpy()}
+    flops = 0
+    t0 = time.perf_counter()
+    for spec in work.layers:
+        src = t[spec.src]
+        if isinstance(spec, wl.ConvSpec):
+            r = t[spec.res] if spec.res else None
+            a = spec.alpha.double().numpy() if spec.alpha is not None else None
+            y = oracle.conv2d(src, spec.w.double().numpy(), spec.bias.double().numpy(), a, r, stride=spec.stride,
+                              pad=spec.pad, act=spec.act, res_before_act=spec.res_before_act, layout=work.layout,
+                              threads=threads)
+            n, c, h, w = src.shape if work.layout == "nchw" else (src.shape[0], src.shape[3], src.shape[1],
+                                                                  src.shape[2])
+            oh, ow = (y.shape[2], y.shape[3]) if work.layout == "nchw" else (y.shape[1], y.shape[2])
+            flops += 2 * n * oh * ow * spec.cout * c * spec.k * spec.k
+            t[spec.out] = oracle.quantize(y, work.dtype)
+        elif spec.kind == "max":
+            t[spec.out] = oracle.maxpool3x3s2(src, layout=work.layout, threads=threads)
+        else:
+            t[spec.out] = oracle.quantize(oracle.avgpool2x2(src, layout=work.layout, threads=threads).astype(np.float64),
+                                          work.dtype)
+    return flops, time.perf_counter() - t0, t[work.layers[-1].out]
+
+
+def oracle_times(path):
+    """Oracle wall time per config on this host: C1-C4 whole, C5 as one-image forwards
+    (the full N=4 step takes minutes); single-thread runs of C1 and C3; and the check
+    that one thread and all threads give the same bits."""
+    import os as _os
+
+    import numpy as np
+
+    import oracle
+    import workloads as wl
+
+    cores = oracle.threads()
+    configs = [("C1", wl.conv1_single(), True), ("C2 f32", wl.conv2_stem("f32"), False),
+               ("C2 bf16", wl.conv2_stem("bf16"), False), ("C3", wl.conv3_pointwise(), True),
+               ("C4", wl.conv4_ifnet_block(), False), ("C5 (one image)", wl.conv5_resnet18d(n=1), False)]
+    rows = []
+    for name, work, single in configs:
+        flops, dt, out = oracle_forward(work, threads=0)
+        row = dict(config=name, workload=work.name, gflop=round(flops / 1e9, 3), seconds=round(dt, 3),
+                   gflops=round(flops / dt / 1e9, 2), threads=cores)
+        if single:
+            f1, dt1, out1 = oracle_forward(work, threads=1)
+            row.update(seconds_1thread=round(dt1, 3), gflops_1thread=round(f1 / dt1 / 1e9, 2),
+                       same_bits_1_vs_all=bool(np.array_equal(out1.view(np.int64), out.view(np.int64))))
+        rows.append(row)
+        print(json.dumps(row), flush=True)
+    rec = dict(cpu_model=cpu_model(), host_threads=len(_os.sched_getaffinity(0)), oracle_threads=cores, configs=rows)
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec), flush=True)
+
+
 def cpu_baseline(min_seconds=10.0):
     """The oracle (fp64 direct loops, all host threads) on a bounded sample of the same
     backbone: one-image forwards (the full 22-conv chain at 640x640, pools included),
@@ -448,7 +529,7 @@ def cpu_baseline(min_seconds=10.0):
         runs += 1
     dt = time.perf_counter() - t0
     return dict(value=round(flops / dt / 1e12, 6), unit="TFLOP/s", cores=oracle.threads(),
-                kind="oracle",
+                kind="oracle", cpu_model=cpu_model(),
                 sample=f"{runs} one-image forwards of the backbone (640x640, 22 convs + 4 pools) "
                        f"in fp64: {flops / 1e9:.1f} GFLOP in {dt:.1f} s")
 
@@ -629,6 +710,9 @@ def main():
     args = parse()
     if args.traffic_from:
         write_traffic(args.traffic_from, args.copy_probe or 256, args.launch_plan)
+        return
+    if args.oracle_times:
+        oracle_times(args.oracle_times)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only: the library has no multi-GPU "
