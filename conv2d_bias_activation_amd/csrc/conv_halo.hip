@@ -302,6 +302,68 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void halo3x3_kernel(ConvArgs a, in
     const __amdgpu_buffer_rsrc_t rp =
         make_rsrc(pl.y, POOL ? (uint32_t)((size_t)a.N * pl.PH * pl.PW * Cout * sizeof(T)) : 0u);
     auto prow_at = [&](int row, int q) -> char * { return prow + row * PROW + (q * 64 + lane) * 16; };
+    // ReLU: every activated value is +0 or positive and never NaN (x > 0 ? x : 0), so
+    // the first largest of a window equals the plain maximum and the bit patterns of
+    // these T values order like 16-bit unsigned integers: two channels at a time with
+    // v_pk_max_u16, and 0 in place of -inf outside the conv output (every pooled window
+    // holds a valid value, which is at least +0). The same bits as the general path.
+    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+    auto pmax = [](uint32_t x, uint32_t y) {
+        return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, x),
+                                                                      __builtin_bit_cast(u16x2, y)));
+    };
+    typedef T t2 __attribute__((ext_vector_type(2)));
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    auto pool_rows_relu = [&](const Geo &tg, int k) {
+        const int oy = tg.oy0 + wm, ox = tg.ox0 + rl;
+        const bool valid = (unsigned)oy < (unsigned)H && (unsigned)ox < (unsigned)W;
+        // ReLU and the conv-output mask in one compare: x > thr ? x : 0
+        const float thr = valid ? 0.0f : __builtin_inff();
+        const int row = wm == WM - 1 ? 4 + ((k + 1) & 1) : wm;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            uint32_t pk[8];
+#pragma unroll
+            for (int e2 = 0; e2 < 8; ++e2) {
+                const float x0 = acc[0][j][2 * e2], x1 = acc[0][j][2 * e2 + 1];
+                // one rounding of each fp32 value to T (a pair conversion, round to nearest even)
+                const t2 t = __builtin_convertvector(f32x2{x0 > thr ? x0 : 0.0f, x1 > thr ? x1 : 0.0f}, t2);
+                const uint32_t c = __builtin_bit_cast(uint32_t, t);
+                // neighbour columns by whole-wave DPP shifts (lanes 0 and 63, never the centre
+                // of a pooled column, read 0)
+                const uint32_t l = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)c, 0x138, 0xf, 0xf, true);
+                const uint32_t r = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)c, 0x130, 0xf, 0xf, true);
+                pk[e2] = pmax(pmax(l, c), r);
+            }
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp)
+                *reinterpret_cast<u32x4 *>(prow_at(row, j * 2 + pp)) =
+                    u32x4{pk[4 * pp], pk[4 * pp + 1], pk[4 * pp + 2], pk[4 * pp + 3]};
+        }
+        halo_barrier();
+        if (!tg.pool) return;
+        const int odd = wave & 1, qh = wave >> 1;
+        const int r0 = odd ? 1 : 4 + (k & 1), r1 = odd ? 2 : 0, r2 = odd ? 4 + ((k + 1) & 1) : 1;
+        const int py = tg.oy0 / 2 + odd, px = (tg.ox0 + 1) / 2 + (rl - 1) / 2;
+        const bool store = (rl & 1) && rl < 30 && px < pl.PW && py < pl.PH;
+#pragma unroll
+        for (int qq = 0; qq < FN; ++qq) {
+            const int q = qh * FN + qq, j = q >> 1, pp = q & 1;
+            const u32x4 v0 = *reinterpret_cast<const u32x4 *>(prow_at(r0, q));
+            const u32x4 v1 = *reinterpret_cast<const u32x4 *>(prow_at(r1, q));
+            const u32x4 v2 = *reinterpret_cast<const u32x4 *>(prow_at(r2, q));
+            u32x2 qq2[2] = {u32x2{pmax(pmax(v0[0], v1[0]), v2[0]), pmax(pmax(v0[1], v1[1]), v2[1])},
+                            u32x2{pmax(pmax(v0[2], v1[2]), v2[2]), pmax(pmax(v0[3], v1[3]), v2[3])}};
+            swap_halves(qq2[0], qq2[1]);
+            const int co = j * 32 + 16 * pp + 8 * hi;
+            const uint32_t off = (store && co < Cout)
+                                     ? ((uint32_t)((tg.n * pl.PH + py) * pl.PW + px) * (uint32_t)Cout +
+                                        (uint32_t)co) * (uint32_t)sizeof(T)
+                                     : kOOB;
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4{qq2[0][0], qq2[0][1], qq2[1][0], qq2[1][1]}, rp, (int)off,
+                                                   0, 0);
+        }
+    };
     auto pool_rows = [&](const Geo &tg, int k) {
         const int oy = tg.oy0 + wm, ox = tg.ox0 + rl;
         const bool valid = (unsigned)oy < (unsigned)H && (unsigned)ox < (unsigned)W;
@@ -312,7 +374,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void halo3x3_kernel(ConvArgs a, in
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     float x = acc[0][j][e];
-                    if constexpr (ACT == CONV2D_ACT_RELU) x = __builtin_fmaxf(x, 0.0f);
+                    if constexpr (ACT == CONV2D_ACT_RELU) x = x > 0.0f ? x : 0.0f;
                     if constexpr (ACT == CONV2D_ACT_SILU) x = x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
                     if constexpr (ACT == CONV2D_ACT_PRELU) {
                         const float al = bal[1][j * 32 + 8 * (e / 4) + 4 * hi + (e % 4)];
@@ -327,7 +389,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void halo3x3_kernel(ConvArgs a, in
         case CONV2D_ACT_PRELU: act_all(std::integral_constant<int, CONV2D_ACT_PRELU>{}); break;
         default: act_all(std::integral_constant<int, CONV2D_ACT_NONE>{}); break;
         }
-        const int left = (lane == 0 ? 0 : lane - 1) * 4, right = (lane == 63 ? 63 : lane + 1) * 4;
         const int row = wm == WM - 1 ? 4 + ((k + 1) & 1) : wm;
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
@@ -339,10 +400,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void halo3x3_kernel(ConvArgs a, in
                 // taps in row-major order (NaN never wins; of equal zeros the first stays).
                 // Through a scalar: this compiler lowers a bit cast applied directly to a
                 // vector element as a read of element 0.
+                // The neighbours come from whole-wave DPP shifts (lane i reads lane i-1, resp.
+                // i+1; lanes 0 and 63 keep their own value), VALU moves with no LDS round trip.
                 const float c = to_f32(round_fp32<T>(acc[0][j][e]));
                 const int v = __builtin_bit_cast(int, c);
-                const float l = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(left, v));
-                const float rgt = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(right, v));
+                const float l = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(v, v, 0x138, 0xf, 0xf, false));
+                const float rgt = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(v, v, 0x130, 0xf, 0xf, false));
                 q[e] = from_f32<T>(first_max3(l, c, rgt));
             }
 #pragma unroll
@@ -451,7 +514,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void halo3x3_kernel(ConvArgs a, in
         halo_wait_vmcnt<0>();
         issue(buf, k + 2);
         if constexpr (POOL) {
-            pool_rows(tg, k);
+            if (a.act == CONV2D_ACT_RELU)
+                pool_rows_relu(tg, k);
+            else
+                pool_rows(tg, k);
             return;
         }
         auto finish = [&](auto act_tag, auto res_tag) {
@@ -478,7 +544,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void halo3x3_kernel(ConvArgs a, in
                             for (int e = 0; e < 4; ++e) {
                                 float x = acc[i][j][4 * (g0 + g) + e];
                                 if constexpr (RES == 1) x += to_f32(rt[e]);
-                                if constexpr (ACT == CONV2D_ACT_RELU) x = __builtin_fmaxf(x, 0.0f);
+                                if constexpr (ACT == CONV2D_ACT_RELU) x = x > 0.0f ? x : 0.0f;
                                 if constexpr (ACT == CONV2D_ACT_SILU) x = x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
                                 if constexpr (ACT == CONV2D_ACT_PRELU) x = x >= 0.0f ? x : al[e] * x;
                                 if constexpr (RES == 2) x += to_f32(rt[e]);
@@ -506,11 +572,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void halo3x3_kernel(ConvArgs a, in
         }
     };
     if constexpr (POOL) {
-        // the carry into a run's first tile: the row above the image
+        // the carry into a run's first tile: the row above the image, a value no pooled
+        // value loses to: -inf, or +0 for the ReLU path (its 16-bit integer order puts
+        // -inf above every positive value)
         if (wm == 0) {
+            const float none = a.act == CONV2D_ACT_RELU ? 0.0f : -__builtin_inff();
             T ninf[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) ninf[e] = from_f32<T>(-__builtin_inff());
+            for (int e = 0; e < 8; ++e) ninf[e] = from_f32<T>(none);
             u32x4 w4;
             __builtin_memcpy(&w4, ninf, 16);
 #pragma unroll

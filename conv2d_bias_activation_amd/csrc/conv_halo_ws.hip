@@ -64,13 +64,17 @@ __global__ __launch_bounds__(512, 1) void halo3x3_ws_kernel(ConvArgs a, int tile
     constexpr int XBUF = kWsTH * kWsTW * XPIX;
     constexpr int NRES = 4;                      // 16-byte units per epilogue lane per tile
     // One LDS array: halo buffers 0..2, the two hand-off tiles, then a sink for the load
-    // chunks past a halo. At the start the 64-channel weights (Cout x 576 elements) pass
-    // through the space from halo buffer 2 on, which nothing else uses before step 0
-    // (the first two halos and their sink chunks go elsewhere).
+    // chunks past a halo. Until the end of step 0 the 64-channel weights (Cout x 9*CIN
+    // elements) sit in the space from halo buffer 2 on, which nothing else uses before
+    // step 1 (halo 2 is issued in step 1, the first hand-off happens in step 1); their
+    // rows are padded to an odd number of 16-byte pieces (RPC), so the 32 rows that one
+    // operand fragment reads start in 16 distinct bank groups per 16 lanes.
     constexpr int XOFF = 3 * HBUF, SINK = XOFF + 2 * XBUF, WOFF = 2 * HBUF;
     constexpr int LDS_BYTES = SINK + 1024;
-    constexpr int WBYTES = 64 * 9 * CIN * (int)sizeof(T);
-    static_assert(LDS_BYTES <= 160 * 1024 && WOFF + WBYTES <= SINK, "LDS");
+    constexpr int RPC = 9 * CIN / 8 + 1;             // 16-byte pieces per padded weight row
+    constexpr int WCHP = (64 * RPC + 63) / 64;       // 1 KiB load chunks of the padded weights
+    constexpr int WLD = (WCHP + 7) / 8;              // of them per wave
+    static_assert(LDS_BYTES <= 160 * 1024 && WOFF + WCHP * 1024 <= SINK, "LDS");
     __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
     typedef typename Mfma32<T>::vec vec;
 
@@ -97,17 +101,19 @@ __global__ __launch_bounds__(512, 1) void halo3x3_ws_kernel(ConvArgs a, int tile
         return Geo{rr / tiles_h, (rr % tiles_h) * kWsTH, tx * kWsTW, live};
     };
 
-    // Weights: every wave copies 1/8 of the [64][9*CIN] block (rows past Cout read as
-    // zeros) into LDS with 16-byte direct-to-LDS loads; the compute waves then take their
-    // operand fragments from there into registers.
+    // Weights: every wave copies its share of the [64][9*CIN] block (rows past Cout read
+    // as zeros) into LDS with 16-byte direct-to-LDS loads, in padded rows; the compute
+    // waves take their operand fragments from there into registers while they compute
+    // tile 0, so no separate copy stands between the loads and the first products.
     {
         const i32x4 rw = rsrc_words(a.w, (uint32_t)((size_t)Cout * 9 * CIN * sizeof(T)));
-        constexpr int WCH = WBYTES / 1024;
-        static_assert(WBYTES % 1024 == 0 && WCH % 8 == 0, "whole chunks per wave");
 #pragma unroll
-        for (int d = 0; d < WCH / 8; ++d) {
+        for (int d = 0; d < WLD; ++d) {
             const int chunk = d * 8 + wave;
-            dma_b128(rw, (uint32_t)(chunk * 1024 + lane * 16), lds_addr(lds + WOFF + chunk * 1024));
+            const int q = chunk * 64 + lane, row = q / RPC, pc = q % RPC;
+            const bool ok = chunk < WCHP && pc < RPC - 1 && row < Cout;
+            dma_b128(rw, ok ? (uint32_t)((row * 9 * CIN + pc * 8) * (int)sizeof(T)) : kOOB,
+                     lds_addr(lds + (chunk < WCHP ? WOFF + chunk * 1024 : SINK)));
         }
     }
     const uint32_t out_bytes = (uint32_t)((size_t)a.M * Cout * sizeof(T));
@@ -116,23 +122,21 @@ __global__ __launch_bounds__(512, 1) void halo3x3_ws_kernel(ConvArgs a, int tile
         // ---- compute waves: wave (wn, wm) = channels 32*wn.., tile rows 2*wm, 2*wm + 1 ----
         const int wn = wave & 1, wm = wave >> 1;
         ws_wait_vmcnt<0>();
-        ws_barrier();  // weights in LDS
+        ws_barrier();  // weights and the first halo in LDS
         vec bw[KS];
-        {
-            const char *wrow = lds + WOFF + ((32 * wn + rl) * 9 * CIN + 8 * hi) * (int)sizeof(T);
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) bw[ks] = *reinterpret_cast<const vec *>(wrow + ks * 16 * (int)sizeof(T));
-        }
-        ws_barrier();  // weights in registers, the first halo landed
+        // this lane's weight row (channel 32*wn + rl), piece 2*ks + hi for k step ks
+        const char *wrow = lds + WOFF + (32 * wn + rl) * RPC * 16 + hi * 16;
         f32x16 acc[2][2];  // two tiles' sums: one accumulating, the previous one handed off
-        auto compute = [&](auto cur, int s) {
+        auto compute = [&](auto cur, auto first, int s) {
             constexpr int C = decltype(cur)::value;
+            constexpr bool FIRST = decltype(first)::value;  // tile 0: the weights come from LDS
             const char *buf = lds + (s % 3) * HBUF;
             // B operand of tile row 2*wm + i at k step ks: halo pixel (row + ky, rl + kx),
             // channels 16*kc + 8*hi ..
             const char *base = buf + ((2 * wm) * kWsHW + rl) * PSTR + hi * 16;
             auto read = [&](int ks, vec(&f)[2]) {
                 const int tap = ks / KC, kc = ks % KC, ky = tap / 3, kx = tap % 3;
+                if constexpr (FIRST) bw[ks] = *reinterpret_cast<const vec *>(wrow + ks * 32);
 #pragma unroll
                 for (int i = 0; i < 2; ++i)
                     f[i] = *reinterpret_cast<const vec *>(base + ((i + ky) * kWsHW + kx) * PSTR + kc * 32);
@@ -172,13 +176,16 @@ __global__ __launch_bounds__(512, 1) void halo3x3_ws_kernel(ConvArgs a, int tile
         auto step = [&](auto cur, int s) {
             constexpr int C = decltype(cur)::value;
             if (s >= 1 && s <= nsteps) handoff(std::integral_constant<int, 1 - C>{}, s - 1);
-            if (s < nsteps) compute(cur, s);
+            if (s < nsteps) compute(cur, std::false_type{}, s);
             ws_barrier();
         };
-        for (int s = 0; s <= nsteps; s += 2) {
-            step(std::integral_constant<int, 0>{}, s);
+        // step 0: tile 0 (every workgroup has one), taking the weights into registers
+        compute(std::integral_constant<int, 0>{}, std::true_type{}, 0);
+        ws_barrier();
+        for (int s = 1; s <= nsteps; s += 2) {
+            step(std::integral_constant<int, 1>{}, s);
             if (s + 1 > nsteps) break;
-            step(std::integral_constant<int, 1>{}, s + 1);
+            step(std::integral_constant<int, 0>{}, s + 1);
         }
         ws_barrier();  // the epilogue of the last tile
         return;
@@ -226,12 +233,35 @@ __global__ __launch_bounds__(512, 1) void halo3x3_ws_kernel(ConvArgs a, int tile
         u_yx[j] = c_ok ? (uint32_t)(py << 8 | px) : kNoPix;
     }
 
+    // Fast paths for tiles away from the image border (wave-uniform tests): a halo wholly
+    // inside the image needs no test per slot and an output tile wholly inside none per
+    // unit, only a base offset plus the lane's offset. For a slot or unit with nothing to
+    // load or store that lane offset is 2^31: x and y hold fewer than 2^31 bytes, so
+    // base + 2^31 lies past the buffer without wrapping (an out-of-range access).
+    constexpr uint32_t kFar = 0x80000000u;
+    uint32_t h_relb[NLD], u_relb[NRES];
+#pragma unroll
+    for (int d = 0; d < NLD; ++d) h_relb[d] = h_yx[d] == kNoPix ? kFar : (uint32_t)h_rel[d] * (uint32_t)sizeof(T);
+#pragma unroll
+    for (int j = 0; j < NRES; ++j) u_relb[j] = u_yx[j] == kNoPix ? kFar : (uint32_t)u_rel[j] * (uint32_t)sizeof(T);
+
     // the input halo of tile s into buffer s % 3; a step past the last tile still issues
     // its loads, with out-of-range offsets (no traffic), so every step's count is the same
     auto issue_halo = [&](int s) {
         const Geo g = geo(s);
         char *buf = lds + (s % 3) * HBUF;
         const int corner = ((g.n * H + g.oy0 - 1) * W + g.ox0 - 1) * CIN;
+        const bool inside = g.live && g.oy0 >= 1 && g.oy0 + kWsTH + 1 <= H && g.ox0 >= 1 && g.ox0 + kWsTW + 1 <= W;
+        if (inside) {
+            const uint32_t cb = (uint32_t)corner * (uint32_t)sizeof(T);
+#pragma unroll
+            for (int d = 0; d < NLD; ++d) {
+                const int chunk = d * 4 + we;
+                char *dst = chunk < NCHUNK ? buf + chunk * 1024 : lds + SINK;
+                dma_b128(rx, cb + h_relb[d], lds_addr(dst));
+            }
+            return;
+        }
 #pragma unroll
         for (int d = 0; d < NLD; ++d) {
             const int chunk = d * 4 + we;
@@ -242,26 +272,46 @@ __global__ __launch_bounds__(512, 1) void halo3x3_ws_kernel(ConvArgs a, int tile
             dma_b128(rx, ok ? (uint32_t)(corner + h_rel[d]) * (uint32_t)sizeof(T) : kOOB, lds_addr(dst));
         }
     };
-    // byte offset in y (and the residual) of this lane's unit j of tile s, or kOOB
+    // byte offset in y (and the residual) of this lane's unit j of tile s, or an
+    // out-of-range offset
+    auto tile_inside = [&](const Geo &g) { return g.live && g.oy0 + kWsTH <= H && g.ox0 + kWsTW <= W; };
+    auto tile_base = [&](const Geo &g) {
+        return (uint32_t)(((g.n * H + g.oy0) * W + g.ox0) * Cout) * (uint32_t)sizeof(T);
+    };
     auto unit_off = [&](const Geo &g, int j) -> uint32_t {
         const int oy = g.oy0 + (int)(u_yx[j] >> 8), ox = g.ox0 + (int)(u_yx[j] & 0xff);
         return (g.live && u_yx[j] != kNoPix && oy < H && ox < W)
                    ? (uint32_t)(((g.n * H + g.oy0) * W + g.ox0) * Cout + u_rel[j]) * (uint32_t)sizeof(T)
                    : kOOB;
     };
+    // the offsets of all this lane's units of tile g
+    auto unit_offs = [&](const Geo &g, uint32_t (&off)[NRES]) {
+        if (tile_inside(g)) {
+            const uint32_t tb = tile_base(g);
+#pragma unroll
+            for (int j = 0; j < NRES; ++j) off[j] = tb + u_relb[j];
+        } else {
+#pragma unroll
+            for (int j = 0; j < NRES; ++j) off[j] = unit_off(g, j);
+        }
+    };
     u32x4 res[3][NRES];
     auto issue_res = [&](auto slot, int s) {
         constexpr int I = decltype(slot)::value;
         const Geo g = geo(s);
+        uint32_t off[NRES];
+        unit_offs(g, off);
 #pragma unroll
         for (int j = 0; j < NRES; ++j)
-            res[I][j] = __builtin_amdgcn_raw_buffer_load_b128(rres, (int)(has_res ? unit_off(g, j) : kOOB), 0, 0);
+            res[I][j] = __builtin_amdgcn_raw_buffer_load_b128(rres, (int)(has_res ? off[j] : kOOB), 0, 0);
     };
     auto epilogue = [&](auto slot, int s) {
         constexpr int I = decltype(slot)::value;
         const Geo g = geo(s);
         const char *x = lds + XOFF + (s & 1) * XBUF;
         const int mode = has_res ? (a.res_before_act ? 1 : 2) : 0;
+        uint32_t off[NRES];
+        unit_offs(g, off);
         auto finish = [&](auto act_tag, auto res_tag) {
             constexpr int ACT = decltype(act_tag)::value;
             constexpr int RES = decltype(res_tag)::value;
@@ -284,7 +334,7 @@ __global__ __launch_bounds__(512, 1) void halo3x3_ws_kernel(ConvArgs a, int tile
                 }
                 u32x4 o;
                 __builtin_memcpy(&o, out, 16);
-                __builtin_amdgcn_raw_buffer_store_b128(o, ry, (int)unit_off(g, j), 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(o, ry, (int)off[j], 0, 0);
             }
         };
         auto with_res = [&](auto act_tag) {
@@ -302,43 +352,55 @@ __global__ __launch_bounds__(512, 1) void halo3x3_ws_kernel(ConvArgs a, int tile
         }
     };
 
-    // Start: the halos of tiles 0 and 1 and the residual of tile 0 go out behind this
-    // wave's weight chunks; the weights land (barrier), then the first halo (barrier).
-    constexpr int WLD = WBYTES / 1024 / 8;
+    // Start: the halo and residual of tile 0 go out behind this wave's weight chunks;
+    // the weights and the halo land (barrier). Only what tile 0 needs is in flight, so
+    // the start-up burst of every CU carries no more than that.
     issue_halo(0);
-    issue_halo(1);
     issue_res(std::integral_constant<int, 0>{}, 0);
-    ws_wait_vmcnt<2 * NLD + NRES>();  // this wave's weight chunks
+    ws_wait_vmcnt<NRES>();  // the weights and the halo of tile 0
     ws_barrier();
-    ws_wait_vmcnt<NLD + NRES>();  // the halo of tile 0
-    ws_barrier();
-    // Step s: the halo of tile s+2 issued; the epilogue of tile s-2, whose sums the
-    // compute waves handed off during step s-1 (its residual went out three steps
-    // before); the residual of tile s+1 issued into the register slot that epilogue just
-    // freed; then a wait that leaves only this step's loads and stores in flight, so the
-    // halo of tile s+1 is in LDS before the barrier that starts its products.
+    // Step s: the epilogue of tile s-2, whose sums the compute waves handed off during
+    // step s-1 (its residual went out three steps before); the halo of tile s+2 issued;
+    // the residual of tile s+1 issued into the register slot that epilogue just freed;
+    // then a wait that leaves only this step's loads and stores in flight, so the halo
+    // of tile s+1 is in LDS before the barrier that starts its products.
     // Halo buffer s+2 = s-1 (mod 3): its products ended at the barrier that began step s.
+    // The epilogue comes before the halo loads: the compiler, which cannot see those
+    // direct-to-LDS loads, counts fewer loads younger than the residual than there are,
+    // and its wait for the residual would otherwise also wait for this step's halo.
+    // Steps 0 and 1 differ: buffer 2 holds the weights until the end of step 0, so step
+    // 0 issues the halo of tile 1 and waits for it, and step 1 those of tiles 2 and 3.
     constexpr int STEP_OPS = NLD + NRES + NRES;
+    auto no_stores = [&]() {
+#pragma unroll
+        for (int j = 0; j < NRES; ++j)  // the same count of stores, none of them live
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, ry, (int)kOOB, 0, 0);
+    };
+    no_stores();
+    issue_halo(1);
+    issue_res(std::integral_constant<int, 1>{}, 1);
+    ws_wait_vmcnt<NRES>();  // the halo of tile 1
+    ws_barrier();
+    no_stores();
+    issue_halo(2);
+    issue_halo(3);
+    issue_res(std::integral_constant<int, 2>{}, 2);
+    ws_wait_vmcnt<NLD + NRES>();  // the halo of tile 2
+    ws_barrier();
     auto step = [&](auto slot, int s) {
         constexpr int I = decltype(slot)::value;  // s % 3
+        epilogue(std::integral_constant<int, (I + 1) % 3>{}, s - 2);
         issue_halo(s + 2);
-        if (s >= 2) {
-            epilogue(std::integral_constant<int, (I + 1) % 3>{}, s - 2);
-        } else {
-#pragma unroll
-            for (int j = 0; j < NRES; ++j)  // the same count of stores, none of them live
-                __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, ry, (int)kOOB, 0, 0);
-        }
         issue_res(std::integral_constant<int, (I + 1) % 3>{}, s + 1);
         ws_wait_vmcnt<STEP_OPS>();
         ws_barrier();
     };
-    for (int s = 0; s <= nsteps + 1; s += 3) {
-        step(std::integral_constant<int, 0>{}, s);
+    for (int s = 2; s <= nsteps + 1; s += 3) {
+        step(std::integral_constant<int, 2>{}, s);
         if (s + 1 > nsteps + 1) break;
-        step(std::integral_constant<int, 1>{}, s + 1);
+        step(std::integral_constant<int, 0>{}, s + 1);
         if (s + 2 > nsteps + 1) break;
-        step(std::integral_constant<int, 2>{}, s + 2);
+        step(std::integral_constant<int, 1>{}, s + 2);
     }
     ws_wait_vmcnt<0>();  // no direct-to-LDS load outlives the workgroup
 }

@@ -228,7 +228,7 @@ __global__ __launch_bounds__(256) void stem3_kernel(ConvArgs a, int rstr) {
 // c0 + 31 of the three conv rows 2py-1 .. 2py+1 (six products per 32 channels); lane
 // rl = 2k+1 (k < 15) is the centre of pooled column 15g + k, so every pool window lies
 // inside one group (groups overlap by two columns). Each conv row is activated and
-// rounded to T; its columns rl-1, rl, rl+1 (ds_bpermute) are maxed left to right, then
+// rounded to T; its columns rl-1, rl, rl+1 (DPP wave shifts) are maxed left to right, then
 // the rows top to bottom, each step keeping the running value unless the next is
 // strictly greater: the taps in row-major order with the pool kernel's comparison, so
 // the result equals pooling the stored conv output bit for bit (NaN skipped, an all-NaN
@@ -306,7 +306,6 @@ __global__ __launch_bounds__(256) void stem3_pool_kernel(ConvArgs a, int PH, int
     for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) best[j][e] = -__builtin_inff();
-    const int left = (lane - 1 < 0 ? 0 : lane - 1) * 4, right = (lane + 1 < 64 ? lane + 1 : lane) * 4;
     auto act_max = [&](auto act_tag, const f32x16 (&acc)[FN], bool ok) {
         constexpr int ACT = decltype(act_tag)::value;
 #pragma unroll
@@ -324,8 +323,10 @@ __global__ __launch_bounds__(256) void stem3_pool_kernel(ConvArgs a, int PH, int
                 // vector element as a read of element 0
                 const float c = ok ? to_f32(round_fp32<T>(x)) : -__builtin_inff();
                 const int v = __builtin_bit_cast(int, c);
-                const float l = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(left, v));
-                const float r = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(right, v));
+                // neighbours by whole-wave DPP shifts: lane i reads lane i-1, resp. i+1
+                // (lanes 0 and 63 keep their own value)
+                const float l = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(v, v, 0x138, 0xf, 0xf, false));
+                const float r = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(v, v, 0x130, 0xf, 0xf, false));
                 const float m = first_max3(l, c, r);
                 best[j][e] = m > best[j][e] ? m : best[j][e];
             }

@@ -180,7 +180,7 @@ __global__ __launch_bounds__(256) void stem3_f32_kernel(ConvArgs a, int rf) {
 // column groups, one per wave. Group g covers conv columns 30g - 1 .. 30g + 30 of the
 // conv rows 2py - 1 .. 2py + 1; lane rl = 2k + 1 (k < 15) is the centre of pooled
 // column 15g + k, so every window lies inside one group. Each conv row is activated,
-// its columns rl - 1, rl, rl + 1 (ds_bpermute) maxed left to right, then the rows top to
+// its columns rl - 1, rl, rl + 1 (DPP wave shifts) maxed left to right, then the rows top to
 // bottom, each step keeping the running value unless the next is strictly greater: the
 // pool kernel's comparison in row-major tap order (NaN skipped, an all-NaN window gives
 // -inf, the first of equal zeros kept); taps outside the conv map count as -inf.
@@ -215,7 +215,6 @@ __global__ __launch_bounds__(256) void stem3_f32_pool_kernel(ConvArgs a, int PH,
     for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) best[j][e] = -__builtin_inff();
-    const int left = (lane - 1 < 0 ? 0 : lane - 1) * 4, right = (lane + 1 < 64 ? lane + 1 : lane) * 4;
     auto act_max = [&](auto act_tag, const f32x16 (&acc)[FN], bool ok) {
         constexpr int ACT = decltype(act_tag)::value;
 #pragma unroll
@@ -224,8 +223,10 @@ __global__ __launch_bounds__(256) void stem3_f32_pool_kernel(ConvArgs a, int PH,
             for (int e = 0; e < 16; ++e) {
                 const float c = ok ? stem_f32_act<ACT>(acc[j][e], aq[j][e]) : -__builtin_inff();
                 const int v = __builtin_bit_cast(int, c);
-                const float l = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(left, v));
-                const float r = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(right, v));
+                // neighbours by whole-wave DPP shifts: lane i reads lane i-1, resp. i+1
+                // (lanes 0 and 63 keep their own value)
+                const float l = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(v, v, 0x138, 0xf, 0xf, false));
+                const float r = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(v, v, 0x130, 0xf, 0xf, false));
                 const float m = first_max3(l, c, r);
                 best[j][e] = m > best[j][e] ? m : best[j][e];
             }

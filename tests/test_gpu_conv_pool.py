@@ -115,6 +115,9 @@ HALO_FUSED = [
     (2, 4, 4, 32, 8, "prelu", "bf16"),
     (4, 160, 160, 32, 64, "relu", "bf16"),
     (4, 320, 320, 32, 64, "relu", "bf16"),
+    # ReLU in f16 (the packed-maximum pool path converts pairs with the f16 instruction)
+    (2, 37, 45, 32, 64, "relu", "f16"),
+    (1, 64, 100, 16, 32, "relu", "f16"),
 ]
 
 
@@ -202,3 +205,33 @@ def test_fused_maxpool_with_nan_inputs(case):
     assert np.array_equal(np.isneginf(got), np.isneginf(ref))
     fin = np.isfinite(ref)
     gate(got[fin], ref[fin], "bf16", what=str(case))
+
+
+# ReLU on the halo kernel pools in 16-bit integer order: NaN inputs (ReLU maps NaN to 0,
+# as the oracle does) and exact zeros (all-negative windows) must give the bits of the
+# two-call path. (n, h, w, cin, cout, dtype)
+RELU_SPECIAL = [
+    (1, 30, 40, 32, 64, "bf16"),
+    (2, 17, 33, 16, 24, "f16"),
+]
+
+
+@pytest.mark.parametrize("case", RELU_SPECIAL, ids=lambda c: "-".join(map(str, c)))
+def test_fused_relu_maxpool_nan_and_zero_windows(case):
+    n, h, w, cin, cout, dtype = case
+    x, spec, _ = wl.random_conv_case(zlib.crc32(repr(case).encode()), n=n, h=h, w=w, cin=cin, cout=cout, k=3,
+                                     stride=1, pad=1, act="relu", layout="nhwc", dtype=dtype)
+    x = x.clone()
+    x[0, 2:9, 3:12, :] = float("nan")
+    x[-1, h - 8:, : w // 2, :] = 0.0  # zero input: conv = bias there; bias < 0 -> a window of zeros
+    spec.bias[: cout // 2] = -torch.abs(spec.bias[: cout // 2]) - 0.25
+    args = (n, h, w, cin, cout, 3, 3, 1, 1, c2d.ACT_RELU, 0, DT[dtype])
+    assert c2d.plan_maxpool(*args).startswith("halo3x3_nhwc")
+    y = _fused(x, spec, "nhwc")
+    y2 = _two_calls(x, spec, "nhwc")
+    torch.cuda.synchronize()
+    assert bits_equal(y, y2), "fused and two-call results differ"
+    got, ref = to64(y), _oracle(x, spec, "nhwc")
+    assert not np.isnan(got).any() and not np.isnan(ref).any()
+    assert (ref == 0).any(), "the case should hold windows of zeros"
+    gate(got, ref, dtype, what=str(case))
