@@ -109,12 +109,21 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void halo3x3_kernel(ConvArgs a, in
     // POOL: six rows of [64 lanes][FN * 32 values] in T: the tile's rows 0..2 and two
     // carry rows (the last row of the tile before and of this one), by tile parity
     constexpr int PROW = FN * 2 * 1024;
-    __shared__ __attribute__((aligned(1024))) char ring[RING];
+    constexpr int PROWB = POOL ? 6 * PROW : 0;
+    // One array holds the two halo buffers and the pooled rows. When the weights fit in
+    // it above halo buffer 0 (ONE_PASS), they are staged there in one go while the first
+    // halo loads; otherwise they pass through the halo buffers in chunks first.
+    constexpr int WTOP = RING + PROWB;
+    constexpr int NDW1 = (WUNITS + NW - 1) / NW;     // weight loads per lane in one pass
+    constexpr int WBASE = WTOP - NDW1 * NW * 1024;  // the one-pass weights (loads past WUNITS
+                                                    // land at the top and are not read)
+    constexpr bool ONE_PASS = WBASE >= HBUF;
+    __shared__ __attribute__((aligned(1024))) char ring[WTOP];
     __shared__ __attribute__((aligned(1024))) char xch[XCH];
-    __shared__ __attribute__((aligned(16))) char prow[POOL ? 6 * PROW : 16];
     __shared__ __attribute__((aligned(16))) float bal[2][32 * FN];  // bias, slopes (0 past Cout)
     char *const hb0 = ring;
     char *const hb1 = ring + HBUF;
+    char *const prow = ring + RING;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -152,22 +161,29 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void halo3x3_kernel(ConvArgs a, in
         bal[1][co] = a.alpha && co < Cout ? a.alpha[co] : 0.0f;
     }
     vec bw[KSW][FN];
+    // all weights in one pass into [WBASE, WTOP)
+    auto stage_all = [&]() {
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-        stage_chunk(c);
-        halo_wait_vmcnt<0>();
-        halo_barrier();
+        for (int d = 0; d < NDW1; ++d) {
+            const int u = d * NW + wave;
+            const int j = u % FN, sw = (u / FN) % KSW, wkk = u / (FN * KSW);
+            const int co = j * 32 + rl, tap = sw / KCW, ci = (wkk * KCW + sw % KCW) * 16 + hi * 8;
+            const bool ok = u < WUNITS && co < Cout;
+            dma_b128(rwt, ok ? (uint32_t)((co * 9 + tap) * CIN + ci) * (uint32_t)sizeof(T) : kOOB,
+                     lds_addr(ring + WBASE + u * 1024));
+        }
+    };
+    auto take_weights = [&](const char *from, int c) {
 #pragma unroll
         for (int sw = 0; sw < KSW; ++sw)
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
                 const int u = (wk * KSW + sw) * FN + j - c * CUNITS;
-                if (NCH == 1 || (u >= 0 && u < CUNITS))
-                    bw[sw][j] = *reinterpret_cast<const vec *>(ring + (u * 64 + lane) * 16);
+                if (ONE_PASS || NCH == 1 || (u >= 0 && u < CUNITS))
+                    bw[sw][j] = *reinterpret_cast<const vec *>(from + (u * 64 + lane) * 16);
             }
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): fragments in registers before the ring is reused
-        halo_barrier();
-    }
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): fragments in registers before the space is reused
+    };
 
     // Tile order: G workgroups, the ones on one XCD (blockIdx % 8) take a contiguous
     // run of each round's G tiles, so neighbouring tiles share halo rows in one L2.
@@ -571,6 +587,25 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void halo3x3_kernel(ConvArgs a, in
         default: with_res(std::integral_constant<int, CONV2D_ACT_NONE>{}); break;
         }
     };
+    if constexpr (ONE_PASS) {
+        // the first halo beside the weights; the weights land (barrier), go into
+        // registers (barrier); then the second halo
+        issue(hb0, 0);
+        stage_all();
+        halo_wait_vmcnt<0>();
+        halo_barrier();
+        take_weights(ring + WBASE, 0);
+        halo_barrier();
+    } else {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            stage_chunk(c);
+            halo_wait_vmcnt<0>();
+            halo_barrier();
+            take_weights(ring, c);
+            halo_barrier();
+        }
+    }
     if constexpr (POOL) {
         // the carry into a run's first tile: the row above the image, a value no pooled
         // value loses to: -inf, or +0 for the ReLU path (its 16-bit integer order puts
@@ -586,9 +621,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void halo3x3_kernel(ConvArgs a, in
             for (int q = 0; q < 2 * FN; ++q) *reinterpret_cast<u32x4 *>(prow_at(4, q)) = w4;
         }
     }
-    issue(hb0, 0);
+    if constexpr (!ONE_PASS) issue(hb0, 0);
     issue(hb1, 1);
-    halo_wait_vmcnt<0>();
+    if constexpr (!ONE_PASS) halo_wait_vmcnt<0>();
     for (int k = 0; geo(k).live; k += 2) {
         tile(hb0, k);
         if (!geo(k + 1).live) break;
