@@ -366,13 +366,20 @@ bool hgemm_cfast(const ConvArgs &a) {
 }
 
 // Variant: the specialised-wave kernel (1) where its tiles fit one round of workgroups
-// over `cus` CUs (a deep K on few pixels, e.g. ResNet stage 4), else the two-workgroups-
-// per-CU kernel (0); from MI355X timings (256 CUs) of the ResNet stage 3 and 4 layers.
+// over `cus` CUs (a deep K on few pixels, e.g. ResNet stage 4); the 10 x 20-pixel tiles
+// (4) where they give at least two workgroups per CU (e.g. ResNet stage 2, 80 x 80 x 128
+// at batch 4); else the 10 x 10-pixel tiles (0). From MI355X timings (256 CUs) of the
+// ResNet stage 2, 3 and 4 layers.
 HgemmPlan plan_hgemm(const ConvArgs &a, int cus) {
     HgemmPlan p{};
     p.cfast = hgemm_cfast(a);
     HgemmInfo in{};
-    p.cfg = (hgemm_cfg_ok(a, 1) && hgemm_cfg_info(1, a, &in) && in.tiles <= cus) ? 1 : hgemm_cfg_ok(a, 0) ? 0 : -1;
+    if (hgemm_cfg_ok(a, 1) && hgemm_cfg_info(1, a, &in) && in.tiles <= cus)
+        p.cfg = 1;
+    else if (hgemm_cfg_ok(a, 4) && hgemm_cfg_info(4, a, &in) && in.tiles >= 2ll * cus)
+        p.cfg = 4;
+    else
+        p.cfg = hgemm_cfg_ok(a, 0) ? 0 : -1;
     return p;
 }
 
@@ -408,11 +415,12 @@ Plan make_plan_default(const ConvArgs &a, int layout, int dtype, size_t ws) {
         p.halo = plan_halo(a);
         return p;
     }
-    // wide 3x3 layers with at least 256 input channels (narrower ones, e.g. ResNet stage
-    // 2, are faster on the tiled GEMM below)
-    if (hgemm_fits(a, layout, dtype) && a.Cin >= 256) {
+    // wide 3x3 layers with at least 256 input channels, or 128 where the 10 x 20-pixel
+    // tiles fill two workgroups per CU (narrower or smaller ones are faster on the
+    // tiled GEMM below)
+    if (hgemm_fits(a, layout, dtype) && a.Cin >= 128) {
         p.hg = plan_hgemm(a, 256);
-        if (p.hg.cfg >= 0) {
+        if (p.hg.cfg >= 0 && (a.Cin >= 256 || p.hg.cfg == 4)) {
             p.family = FAM_HGEMM;
             return p;
         }

@@ -147,15 +147,16 @@ __global__ __launch_bounds__(64 * C::NW, 1) void hgemm3x3_kernel(ConvArgs a, Hge
     // Issues input-channel chunk c into stage st. A chunk past the last one issues the
     // same loads at out-of-range offsets, so that every chunk adds exactly NLD to this
     // wave's count of outstanding vector-memory operations.
-    auto issue = [&](int c, int st) {
+    auto issue_one = [&](int c, int st, int d) {
         const uint32_t cadd = c < nchunks ? (uint32_t)(c * C::CK * (int)sizeof(T)) : kHgBad;
+        const int ch = d * C::NW + wave;
+        const uint32_t dst = ch < C::NCH ? lds0 + st * C::STAGE + ch * 1024 : lds0 + C::SINK;
+        const uint32_t off = base[d] == kHgBad ? kHgBad : base[d] + cadd;
+        dma_b128(ch < C::HCH ? rx : rw, off, dst);
+    };
+    auto issue = [&](int c, int st) {
 #pragma unroll
-        for (int d = 0; d < NLD; ++d) {
-            const int ch = d * C::NW + wave;
-            const uint32_t dst = ch < C::NCH ? lds0 + st * C::STAGE + ch * 1024 : lds0 + C::SINK;
-            const uint32_t off = base[d] == kHgBad ? kHgBad : base[d] + cadd;
-            dma_b128(ch < C::HCH ? rx : rw, off, dst);
-        }
+        for (int d = 0; d < NLD; ++d) issue_one(c, st, d);
     };
 
     // Operand offsets within a stage. B (pixels): lane rl of block b = wp + WP*i is tile
@@ -199,6 +200,7 @@ __global__ __launch_bounds__(64 * C::NW, 1) void hgemm3x3_kernel(ConvArgs a, Hge
     // with the operand fragments of step s + PD read from LDS while step s multiplies
     // (PD + 1 fragment buffers; the scheduling barriers keep that order).
     constexpr int NSTEP = 9 * KS, PD = C::PD, NBF = PD + 1;
+    static_assert(NLD <= NSTEP, "one copy per k step at most");
     auto load = [&](uint32_t sb, int s, vec (&fa)[FN], vec (&fb)[NBW]) {
         const char *L = lds;
         const int tap = s / KS, ks = s % KS;
@@ -209,7 +211,11 @@ __global__ __launch_bounds__(64 * C::NW, 1) void hgemm3x3_kernel(ConvArgs a, Hge
         for (int i = 0; i < NBW; ++i)
             if (i < nb) fb[i] = *reinterpret_cast<const vec *>(L + sb + boff[i][tap][ks]);
     };
-    auto compute = [&](uint32_t sb) {
+    // The products of a chunk also issue the copies of chunk nc into stage nst, spread
+    // over the k steps (copy d after the products of step d*NSTEP/NLD), so the memory
+    // pipe fills the stage while the matrix cores run instead of the wave stalling on a
+    // burst of copies before its products.
+    auto compute = [&](uint32_t sb, int nc, int nst) {
         vec fa[NBF][FN], fb[NBF][NBW];
 #pragma unroll
         for (int s = 0; s < PD; ++s) load(sb, s, fa[s], fb[s]);
@@ -223,21 +229,24 @@ __global__ __launch_bounds__(64 * C::NW, 1) void hgemm3x3_kernel(ConvArgs a, Hge
 #pragma unroll
                     for (int j = 0; j < FN; ++j) acc[i][j] = Mfma32<T>::run(fa[s % NBF][j], fb[s % NBF][i], acc[i][j]);
             __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int d = 0; d < NLD; ++d)
+                if (d * NSTEP / NLD == s) issue_one(nc, nst, d);
         }
     };
 
     // Ring of NS stages: chunk c lives in stage c % NS and is issued NS-1 chunks ahead.
     // Per chunk: wait for this wave's loads of chunk c, barrier (every wave's loads of
     // it have landed, and every wave is done with chunk c-1, whose stage is refilled
-    // next), issue chunk c+NS-1 into that stage, then the products of chunk c.
+    // next), then the products of chunk c, which issue chunk c+NS-1 into that stage as
+    // they go.
     [&]<int... I>(std::integer_sequence<int, I...>) { (issue(I, I), ...); }(std::make_integer_sequence<int, C::NS - 1>{});
     int st = 0;
     for (int c = 0; c < nchunks; ++c) {
         hg_wait_vmcnt<(C::NS - 2) * NLD>();
         hg_barrier();
         const int nst = st == 0 ? C::NS - 1 : st - 1;  // (c + NS - 1) % NS
-        issue(c + C::NS - 1, nst);
-        compute((uint32_t)(st * C::STAGE));
+        compute((uint32_t)(st * C::STAGE), c + C::NS - 1, nst);
         st = st + 1 == C::NS ? 0 : st + 1;
     }
     hg_wait_vmcnt<0>();
@@ -686,7 +695,9 @@ typedef HgCfg<10, 10, 4, 1, 1, 2, 32, 2> HgV0;  // 100 px x 32 ch, two workgroup
 typedef HgwCfg<10, 10, 1, 1, 1> HgV1;           // specialised waves: 100 px x 32 ch
 typedef HgwCfg<10, 10, 1, 1, 2> HgV2;           // the same, taps split over two waves
 typedef HgCfg<16, 16, 4, 1, 2, 2, 32, 2> HgV3;  // 256 px x 64 ch
-constexpr int kHgVariants = 4;
+typedef HgCfg<10, 20, 4, 1, 1, 2, 32, 2> HgV4;  // 200 px x 32 ch (7 pixel blocks, 2 per wave)
+typedef HgCfg<10, 20, 4, 1, 2, 2, 32, 2> HgV5;  // 200 px x 64 ch
+constexpr int kHgVariants = 6;
 
 template <typename C> long long hg_tiles(const ConvArgs &a) {
     return (long long)a.N * ((a.W + C::TW - 1) / C::TW) * ((a.H + C::TH - 1) / C::TH) *
@@ -725,6 +736,8 @@ template <typename T> hipError_t launch_hg_d(const ConvArgs &a, const HgemmPlan 
     case 1: return launch_hgw_c<T, HgV1>(a, p.cfast, st);
     case 2: return launch_hgw_c<T, HgV2>(a, p.cfast, st);
     case 3: return launch_hg_c<T, HgV3>(a, p.cfast, st);
+    case 4: return launch_hg_c<T, HgV4>(a, p.cfast, st);
+    case 5: return launch_hg_c<T, HgV5>(a, p.cfast, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -756,6 +769,8 @@ bool hgemm_cfg_info(int cfg, const ConvArgs &a, HgemmInfo *o) {
     case 1: return fill(HgV1{});
     case 2: return fill(HgV2{});
     case 3: return fill(HgV3{});
+    case 4: return fill(HgV4{});
+    case 5: return fill(HgV5{});
     default: return false;
     }
 }

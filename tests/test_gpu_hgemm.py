@@ -23,7 +23,7 @@ c2d = pytest.importorskip("conv2d_bias_activation_amd")
 DEV = torch.device("cuda")
 
 FAM_HGEMM = 7
-CK = [32, 64, 64, 32]  # input channels per K chunk of each variant
+CK = [32, 64, 64, 32, 32, 32]  # input channels per K chunk of each variant
 NVARIANTS = len(CK)
 
 
@@ -98,7 +98,8 @@ def test_default_plan_of_wide_layers():
     plan = lambda n, h, w, c: c2d.plan(n, h, w, c, c, 3, 3, 1, 1, c2d.ACT_RELU, c2d.LAYOUT_NHWC, bf)
     assert plan(4, 40, 40, 256).startswith("hgemm3x3_nhwc bf16 v0 ")
     assert plan(4, 20, 20, 512).startswith("hgemmws3x3_nhwc bf16 v1 ")
-    assert plan(4, 80, 80, 128).startswith("igemm_nhwc_pipe")
+    assert plan(4, 80, 80, 128).startswith("hgemm3x3_nhwc bf16 v4 ")
+    assert plan(4, 40, 40, 128).startswith("igemm_nhwc_pipe")
 
 
 def test_delta_kernel_is_identity_bit_exact():
