@@ -346,15 +346,16 @@ bool stem_fits(const ConvArgs &a, int layout, int dtype) {
 // multiple of 32; variants with 64-channel K chunks need Cin % 64 == 0).
 bool hgemm_fits(const ConvArgs &a, int layout, int dtype) {
     const int eb = dtype_bytes(dtype);
-    return layout == CONV2D_LAYOUT_NHWC && dtype != CONV2D_DTYPE_F32 && a.kh == 3 && a.kw == 3 && a.stride == 1 &&
-           a.pad == 1 && (a.Cin % 32) == 0 && (a.Cout % 8) == 0 && a.vec_out && aligned16(a.x) && aligned16(a.w) &&
+    return layout == CONV2D_LAYOUT_NHWC && dtype != CONV2D_DTYPE_F32 && a.kh == 3 && a.kw == 3 &&
+           (a.stride == 1 || a.stride == 2) && a.pad == 1 && (a.Cin % 32) == 0 && (a.Cout % 8) == 0 && a.vec_out && aligned16(a.x) && aligned16(a.w) &&
            (long long)a.N * a.H * a.W * a.Cin * eb < (1ll << 31) && (long long)a.Cout * a.K * eb < (1ll << 31) &&
            (long long)a.M * a.Cout * eb < (1ll << 31);
 }
 
 bool hgemm_cfg_ok(const ConvArgs &a, int cfg) {
     HgemmInfo in{};
-    return hgemm_cfg_info(cfg, a, &in) && (a.Cin % in.ck) == 0 && in.tiles > 0 && in.tiles < (1ll << 31);
+    return hgemm_cfg_info(cfg, a, &in) && in.stride == a.stride && (a.Cin % in.ck) == 0 && in.tiles > 0 &&
+           in.tiles < (1ll << 31);
 }
 
 // Tile order: each XCD (one L2) gets a contiguous run of tile ids; with the channel

@@ -1,4 +1,4 @@
-// 3x3 stride-1 pad-1 channel-last convolution for wide layers (Cin a multiple of the K
+// 3x3 stride-1 or stride-2 pad-1 channel-last convolution for wide layers (Cin a multiple of the K
 // chunk, Cout a multiple of 8) on CDNA4 matrix cores: the implicit GEMM of the
 // inferencelayer page's `conv()` (m = output pixel, k = (tap, input channel), n = output
 // channel, fused bias + activation epilogue) with halo tiles in place of a per-tap
@@ -55,17 +55,18 @@ constexpr uint32_t kHgBad = 0x80000000u;  // offset of a load with nothing to fe
 }  // namespace
 
 // Compile-time geometry of one kernel variant.
-template <int TH_, int TW_, int WP_, int WC_, int FN_, int NS_, int CK_, int PD_>
+template <int TH_, int TW_, int WP_, int WC_, int FN_, int NS_, int CK_, int PD_, int S_ = 1>
 struct HgCfg {
     static constexpr int TH = TH_, TW = TW_, WP = WP_, WC = WC_, FN = FN_, NS = NS_, CK = CK_;
     static constexpr int PD = PD_;                     // k steps of operand reads ahead
+    static constexpr int S = S_;                       // stride (1 or 2; pad 1)
     static constexpr int NW = WP * WC;                 // waves per workgroup
     static constexpr int P = TH * TW;                  // tile pixels
     static constexpr int NBLK = (P + 31) / 32;         // 32-pixel blocks of the tile
     static constexpr int NBW = (NBLK + WP - 1) / WP;   // blocks per wave (at most)
     static constexpr int CB = 32 * FN * WC;            // output channels per workgroup
-    static constexpr int HW2 = TW + 2;
-    static constexpr int HR = (TH + 2) * HW2;          // halo rows
+    static constexpr int HW2 = S * (TW - 1) + 3;      // halo columns
+    static constexpr int HR = (S * (TH - 1) + 3) * HW2;  // halo rows (pixels)
     static constexpr int WR = 9 * CB;                  // weight rows
     static constexpr int RS = CK / 8;                  // 16-byte pieces per row
     static constexpr int RB = 2 * CK;                  // bytes per row
@@ -84,6 +85,7 @@ struct HgCfg {
     static_assert(PD >= 1 && PD < 9 * KS, "operand read-ahead within one chunk");
     static_assert(NBW * WP >= NBLK, "every pixel block has a wave");
     static_assert(LDS <= 160 * 1024, "LDS of one CU");
+    static_assert(S == 1 || S == 2, "stride 1 or 2");
 };
 
 template <typename T, typename C>
@@ -96,6 +98,7 @@ __global__ __launch_bounds__(64 * C::NW, 1) void hgemm3x3_kernel(ConvArgs a, Hge
     const int wp = wave % C::WP, wc = wave / C::WP;
     const int rl = lane & 31, hi = lane >> 5;
     const int H = a.H, W = a.W, Cin = a.Cin, Cout = a.Cout;
+    const int OH = a.OH, OW = a.OW;
 
     // Tile of this workgroup. Workgroups go to the 8 XCDs round-robin (blockIdx % 8);
     // each XCD gets a contiguous run of tile ids, and consecutive ids vary the pixel
@@ -126,7 +129,7 @@ __global__ __launch_bounds__(64 * C::NW, 1) void hgemm3x3_kernel(ConvArgs a, Hge
             const int qv = pos ^ ((r / C::SWZ) % RS);
             if (r < C::HR) {
                 const int hy = r / C::HW2, hx = r % C::HW2;
-                const int iy = oy0 - 1 + hy, ix = ox0 - 1 + hx;
+                const int iy = C::S * oy0 - 1 + hy, ix = C::S * ox0 - 1 + hx;
                 if ((unsigned)iy < (unsigned)H && (unsigned)ix < (unsigned)W)
                     b = (uint32_t)((((n * H + iy) * W + ix) * Cin + qv * 8) * (int)sizeof(T));
             }
@@ -174,7 +177,7 @@ __global__ __launch_bounds__(64 * C::NW, 1) void hgemm3x3_kernel(ConvArgs a, Hge
         nb += b < C::NBLK ? 1 : 0;
 #pragma unroll
         for (int tap = 0; tap < 9; ++tap) {
-            const int r = (py + tap / 3) * C::HW2 + px + tap % 3;
+            const int r = (C::S * py + tap / 3) * C::HW2 + C::S * px + tap % 3;
             const int sw = (r / C::SWZ) % RS;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) boff[i][tap][ks] = (uint32_t)(r * RB + (((2 * ks + hi) ^ sw) << 4));
@@ -277,14 +280,14 @@ __global__ __launch_bounds__(64 * C::NW, 1) void hgemm3x3_kernel(ConvArgs a, Hge
         const int p = 32 * b + rl;
         const int py = p / C::TW, px = p % C::TW;
         const int oy = oy0 + py, ox = ox0 + px;
-        const bool pin = b < C::NBLK && p < C::P && oy < H && ox < W;
+        const bool pin = b < C::NBLK && p < C::P && oy < OH && ox < OW;
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
             for (int pp = 0; pp < 2; ++pp) {
                 const int co = co0 + 32 * (wc * FN + j) + 16 * pp + 8 * hi;
                 off[i][j][pp] = (pin && co < Cout)
-                                    ? ((uint32_t)((n * H + oy) * W + ox) * (uint32_t)Cout + (uint32_t)co) *
+                                    ? ((uint32_t)((n * OH + oy) * OW + ox) * (uint32_t)Cout + (uint32_t)co) *
                                           (uint32_t)sizeof(T)
                                     : kOOB;
                 rv[i][j][pp] = has_res ? __builtin_amdgcn_raw_buffer_load_b128(rres, (int)off[i][j][pp], 0, 0)
@@ -697,20 +700,31 @@ typedef HgwCfg<10, 10, 1, 1, 2> HgV2;           // the same, taps split over two
 typedef HgCfg<16, 16, 4, 1, 2, 2, 32, 2> HgV3;  // 256 px x 64 ch
 typedef HgCfg<10, 20, 4, 1, 1, 2, 32, 2> HgV4;  // 200 px x 32 ch (7 pixel blocks, 2 per wave)
 typedef HgCfg<10, 20, 4, 1, 2, 2, 32, 2> HgV5;  // 200 px x 64 ch
-constexpr int kHgVariants = 6;
+// stride 2
+typedef HgCfg<10, 10, 4, 1, 2, 2, 32, 2, 2> HgV6;  // 100 px x 64 ch
+typedef HgCfg<10, 10, 4, 1, 1, 2, 32, 2, 2> HgV7;  // 100 px x 32 ch
+typedef HgCfg<8, 16, 4, 1, 2, 2, 32, 2, 2> HgV8;   // 128 px x 64 ch
+constexpr int kHgVariants = 9;
 
 template <typename C> long long hg_tiles(const ConvArgs &a) {
-    return (long long)a.N * ((a.W + C::TW - 1) / C::TW) * ((a.H + C::TH - 1) / C::TH) *
+    return (long long)a.N * ((a.OW + C::TW - 1) / C::TW) * ((a.OH + C::TH - 1) / C::TH) *
            ((a.Cout + C::CB - 1) / C::CB);
 }
 
+template <typename C> constexpr int hg_stride() {
+    if constexpr (requires { C::S; })
+        return C::S;
+    else
+        return 1;
+}
+
 template <typename T, typename C> hipError_t launch_hgw_c(const ConvArgs &a, bool cfast, hipStream_t st) {
-    if ((a.Cin % C::CK) != 0) return hipErrorInvalidValue;
+    if ((a.Cin % C::CK) != 0 || a.stride != 1 || a.OH != a.H || a.OW != a.W) return hipErrorInvalidValue;
     const long long tiles = hg_tiles<C>(a);
     if (tiles <= 0 || tiles > 0x7fffffffll) return hipErrorInvalidValue;
     HgemmGeo g{};
-    g.tiles_x = (a.W + C::TW - 1) / C::TW;
-    g.tiles_y = (a.H + C::TH - 1) / C::TH;
+    g.tiles_x = (a.OW + C::TW - 1) / C::TW;
+    g.tiles_y = (a.OH + C::TH - 1) / C::TH;
     g.tiles_c = (a.Cout + C::CB - 1) / C::CB;
     g.ntiles_p = a.N * g.tiles_x * g.tiles_y;
     g.cfast = cfast ? 1 : 0;
@@ -718,12 +732,13 @@ template <typename T, typename C> hipError_t launch_hgw_c(const ConvArgs &a, boo
 }
 
 template <typename T, typename C> hipError_t launch_hg_c(const ConvArgs &a, bool cfast, hipStream_t st) {
-    if ((a.Cin % C::CK) != 0) return hipErrorInvalidValue;
+    if ((a.Cin % C::CK) != 0 || a.stride != C::S || a.OH != (a.H - 1) / C::S + 1 || a.OW != (a.W - 1) / C::S + 1)
+        return hipErrorInvalidValue;
     const long long tiles = hg_tiles<C>(a);
     if (tiles <= 0 || tiles > 0x7fffffffll) return hipErrorInvalidValue;
     HgemmGeo g{};
-    g.tiles_x = (a.W + C::TW - 1) / C::TW;
-    g.tiles_y = (a.H + C::TH - 1) / C::TH;
+    g.tiles_x = (a.OW + C::TW - 1) / C::TW;
+    g.tiles_y = (a.OH + C::TH - 1) / C::TH;
     g.tiles_c = (a.Cout + C::CB - 1) / C::CB;
     g.ntiles_p = a.N * g.tiles_x * g.tiles_y;
     g.cfast = cfast ? 1 : 0;
@@ -738,6 +753,9 @@ template <typename T> hipError_t launch_hg_d(const ConvArgs &a, const HgemmPlan 
     case 3: return launch_hg_c<T, HgV3>(a, p.cfast, st);
     case 4: return launch_hg_c<T, HgV4>(a, p.cfast, st);
     case 5: return launch_hg_c<T, HgV5>(a, p.cfast, st);
+    case 6: return launch_hg_c<T, HgV6>(a, p.cfast, st);
+    case 7: return launch_hg_c<T, HgV7>(a, p.cfast, st);
+    case 8: return launch_hg_c<T, HgV8>(a, p.cfast, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -761,6 +779,7 @@ bool hgemm_cfg_info(int cfg, const ConvArgs &a, HgemmInfo *o) {
             o->ws = false;
         }
         o->lds = C::LDS;
+        o->stride = hg_stride<C>();
         o->tiles = hg_tiles<C>(a);
         return true;
     };
@@ -771,12 +790,15 @@ bool hgemm_cfg_info(int cfg, const ConvArgs &a, HgemmInfo *o) {
     case 3: return fill(HgV3{});
     case 4: return fill(HgV4{});
     case 5: return fill(HgV5{});
+    case 6: return fill(HgV6{});
+    case 7: return fill(HgV7{});
+    case 8: return fill(HgV8{});
     default: return false;
     }
 }
 
 hipError_t launch_hgemm3x3(const ConvArgs &a, int dtype, const HgemmPlan &p, hipStream_t st) {
-    if (a.kh != 3 || a.kw != 3 || a.stride != 1 || a.pad != 1 || (a.Cout % 8) != 0 || !a.vec_out)
+    if (a.kh != 3 || a.kw != 3 || (a.stride != 1 && a.stride != 2) || a.pad != 1 || (a.Cout % 8) != 0 || !a.vec_out)
         return hipErrorInvalidValue;
     switch (dtype) {
     case CONV2D_DTYPE_BF16: return launch_hg_d<bf16>(a, p, st);

@@ -282,8 +282,14 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 // compiler, which cannot tell which LDS bytes such a load writes, does not drain every
 // outstanding load before each later LDS read: the caller owns the vmcnt waits and
 // barriers that order these loads before the reads of their data.
+// The compiler also does not see that this is a vector-memory instruction reading the
+// descriptor SGPRs and M0, so it inserts none of the wait states that such a read needs
+// after a VALU write of those SGPRs (5 on gfx9: an SGPR spill reloaded by v_readlane
+// just before made the load use a stale descriptor) or after an SALU write of M0 (1):
+// the s_nop 4 in front provides them.
 __device__ __forceinline__ void dma_b128(i32x4 rsrc, uint32_t voff, uint32_t lds) {
-    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds) : "memory");
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds)
+                 : "memory");
 }
 
 // Fused epilogue of one wave's (FM*32) x (FN*32) block of 32x32 matrix-core

@@ -102,10 +102,11 @@ struct HgemmInfo {
     int th, tw, cb;   // tile: output rows, columns, channels
     int waves, lds;   // waves and LDS bytes per workgroup
     bool ws;          // the specialised-wave kernel (loader and compute waves)
+    int stride;       // the convolution stride the variant computes (1 or 2)
     long long tiles;  // workgroups of the launch
 };
 
-// 3x3 stride-1 pad-1 channel-last 16-bit convolution of wide layers with halo tiles
+// 3x3 stride-1 or stride-2 pad-1 channel-last 16-bit convolution of wide layers with halo tiles
 // and weights staged per K chunk: Cin a multiple of the variant's K chunk (32 or 64),
 // Cout % 8 == 0, y and the residual 16-byte aligned (a.vec_out), x, w and y under 2 GiB.
 hipError_t launch_hgemm3x3(const ConvArgs &a, int dtype, const HgemmPlan &p, hipStream_t st);

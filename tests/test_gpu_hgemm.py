@@ -23,7 +23,8 @@ c2d = pytest.importorskip("conv2d_bias_activation_amd")
 DEV = torch.device("cuda")
 
 FAM_HGEMM = 7
-CK = [32, 64, 64, 32, 32, 32]  # input channels per K chunk of each variant
+CK = [32, 64, 64, 32, 32, 32, 32, 32, 32]  # input channels per K chunk of each variant
+STRIDE = [1, 1, 1, 1, 1, 1, 2, 2, 2]       # the stride each variant computes
 NVARIANTS = len(CK)
 
 
@@ -34,9 +35,9 @@ def _clean_table():
     c2d.tune_clear()
 
 
-def _device_key(n, h, w, cin, cout, dt, res):
-    """Table key of a 3x3 stride-1 pad-1 channel-last shape on this device: the tuner
-    writes one for a small shape, whose device part is reused."""
+def _device_key(n, h, w, cin, cout, dt, res, stride=1):
+    """Table key of a 3x3 pad-1 channel-last shape on this device: the tuner writes one
+    for a small shape, whose device part is reused."""
     c2d.tune(1, 8, 8, 64, 64, 3, 3, 1, 1, "relu", dtype=c2d.DTYPE_BF16, reps=1)
     with tempfile.TemporaryDirectory() as d:
         p = os.path.join(d, "t.txt")
@@ -44,7 +45,7 @@ def _device_key(n, h, w, cin, cout, dt, res):
         line = [ln for ln in open(p) if not ln.startswith("#")][0]
     c2d.tune_clear()
     dev = line.split("|")[0]
-    return f"{dev}|{n}|{h}|{w}|{cin}|{cout}|3|3|1|1|0|{dt}|{res}"
+    return f"{dev}|{n}|{h}|{w}|{cin}|{cout}|3|3|{stride}|1|0|{dt}|{res}"
 
 
 # (n, h, w, cin, cout, act, residual, res_before_act, dtype)
@@ -74,7 +75,7 @@ def test_every_variant_meets_the_gate(case, tmp_path):
     rd = r.to(DEV) if r is not None else None
     ran = 0
     for v in range(NVARIANTS):
-        if cin % CK[v]:
+        if cin % CK[v] or STRIDE[v] != 1:
             continue
         for order in (0, 1):
             table = tmp_path / f"v{v}_{order}.txt"
@@ -111,6 +112,8 @@ def test_delta_kernel_is_identity_bit_exact():
     wt = torch.zeros(c, 3, 3, c, dtype=torch.bfloat16)
     wt[torch.arange(c), 1, 1, torch.arange(c)] = 1.0
     for v in range(NVARIANTS):
+        if STRIDE[v] != 1:
+            continue
         key = _device_key(n, h, w, c, c, c2d.DTYPE_BF16, 0)
         with tempfile.TemporaryDirectory() as d:
             p = os.path.join(d, "t.txt")
@@ -120,3 +123,49 @@ def test_delta_kernel_is_identity_bit_exact():
         y = c2d.conv2d_fused(x.to(DEV), wt.to(DEV), None, None, None, stride=1, pad=1, act="none", layout="nhwc")
         torch.cuda.synchronize()
         assert torch.equal(y.cpu().view(torch.int16), x.view(torch.int16)), f"variant {v}"
+
+
+# Stride 2 (the downsampling convs): odd and even input sizes (the last output row and
+# column read one padding pixel or not), ragged tiles, images smaller than one tile,
+# partial channel blocks, every epilogue.
+# (n, h, w, cin, cout, act, residual, res_before_act, dtype)
+CASES_S2 = [
+    (1, 23, 19, 64, 128, "relu", True, True, "bf16"),
+    (2, 16, 26, 32, 72, "silu", False, False, "f16"),
+    (1, 9, 7, 128, 64, "prelu", True, False, "bf16"),
+    (1, 41, 40, 96, 40, "none", False, False, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", CASES_S2, ids=lambda c: "-".join(map(str, c)))
+def test_stride2_variants_meet_the_gate(case, tmp_path):
+    n, h, w, cin, cout, act, residual, pre, dtype = case
+    dt = {"bf16": c2d.DTYPE_BF16, "f16": c2d.DTYPE_F16}[dtype]
+    actc = c2d._ACTS[act] | (c2d.RES_BEFORE_ACT if pre else 0)
+    key0 = _device_key(n, h, w, cin, cout, dt, 0, stride=2)
+    key1 = key0[:-1] + "1"
+    x, spec, r = wl.random_conv_case(171 + cin + h, n=n, h=h, w=w, cin=cin, cout=cout, k=3, stride=2, pad=1,
+                                     act=act, layout="nhwc", dtype=dtype, residual=residual, res_before_act=pre)
+    ref = oracle.conv2d(to64(x), to64(spec.w), to64(spec.bias), to64(spec.alpha) if spec.alpha is not None else None,
+                        to64(r) if r is not None else None, stride=2, pad=1, act=act, layout="nhwc",
+                        res_before_act=pre)
+    xd, wd, bd = x.to(DEV), spec.w.to(DEV), spec.bias.to(DEV)
+    ad = spec.alpha.to(DEV) if spec.alpha is not None else None
+    rd = r.to(DEV) if r is not None else None
+    ran = 0
+    for v in range(NVARIANTS):
+        if cin % CK[v] or STRIDE[v] != 2:
+            continue
+        for order in (0, 1):
+            table = tmp_path / f"v{v}_{order}.txt"
+            table.write_text(f"{key0} {FAM_HGEMM} {v} 1 {order}\n{key1} {FAM_HGEMM} {v} 1 {order}\n")
+            c2d.tune_clear()
+            assert c2d.tune_load(str(table)) == 2
+            name = c2d.plan(n, h, w, cin, cout, 3, 3, 2, 1, actc, c2d.LAYOUT_NHWC, dt)
+            assert name.startswith(f"hgemm3x3_nhwc {dtype} v{v} ") and name.endswith(" tuned"), name
+            print(f"variant {v} order {order}: {name}", flush=True)
+            y = c2d.conv2d_fused(xd, wd, bd, ad, rd, stride=2, pad=1, act=act, layout="nhwc", res_before_act=pre)
+            torch.cuda.synchronize()
+            gate(to64(y), ref, dtype, what=f"variant {v} order {order} ({name})")
+            ran += 1
+    assert ran >= 4
