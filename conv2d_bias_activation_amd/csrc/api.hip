@@ -853,6 +853,11 @@ struct OpPlan {
     const void *b;  // concat: second input
     int Ca, Cb;     // concat channels (Cb = 0: upsample)
     bool up;        // upsample the first input
+    // stack fusion of a 2x2 average pool with the 1x1 conv that reads its output:
+    // the pool op launches nothing (pool_by_next), the conv op runs both (pool_pw)
+    bool pool_by_next;
+    bool pool_pw;
+    PoolPwArgs pp;
 };
 
 // Bytes of workspace the launch of a planned op writes (0 for none).
@@ -991,6 +996,47 @@ void link_chains(std::vector<OpPlan> &plans, size_t ws) {
     }
 }
 
+// A 2x2 average pool followed by a 1x1 stride-1 conv of its output (the ResNet-D
+// shortcut) runs as one kernel: the conv op computes the pool while it stages its input
+// and still writes the pooled map. Only where that kernel reproduces the two launches
+// bit for bit: channel-last 16-bit, the conv on the general channel-last GEMM without a
+// K split (products over k in increasing order from zero, bias in the epilogue), no
+// residual, and no overlap between the conv output and the pool's tensors.
+void link_pool_pw(std::vector<OpPlan> &plans) {
+    for (size_t i = 0; i + 1 < plans.size(); ++i) {
+        OpPlan &p = plans[i], &q = plans[i + 1];
+        if (p.kind != CONV2D_OP_AVGPOOL || q.kind != CONV2D_OP_CONV || p.pool_by_next || q.pool_pw) continue;
+        if (p.layout != CONV2D_LAYOUT_NHWC || p.dtype != q.dtype || !p.vec) continue;
+        const ConvArgs &a = q.a;
+        if (a.kh != 1 || a.kw != 1 || a.stride != 1 || a.pad != 0 || a.res || a.w_ohwi) continue;
+        if (a.x != p.y || a.N != p.N || a.H != p.H / 2 || a.W != p.W / 2 || a.Cin != p.C) continue;
+        if (q.plan.family != FAM_NHWC || q.plan.nh.splits != 1 || !poolpw_fits(a.Cin, a.Cout, q.dtype)) continue;
+        const long long eb = dtype_bytes(q.dtype);
+        const long long xb = (long long)p.N * p.H * p.W * p.C * eb, pb = (long long)a.M * a.Cin * eb;
+        const long long yb = (long long)a.M * a.Cout * eb;
+        if (xb >= (1ll << 31) || yb >= (1ll << 31) || !aligned16(a.y) || !aligned16(a.w)) continue;
+        if (overlap(a.y, yb, p.x, xb) || overlap(a.y, yb, p.y, pb)) continue;
+        PoolPwArgs pp{};
+        pp.x = p.x;
+        pp.w = a.w;
+        pp.bias = a.bias;
+        pp.alpha = a.alpha;
+        pp.y = a.y;
+        pp.p = p.y;
+        pp.N = p.N;
+        pp.H = p.H;
+        pp.W = p.W;
+        pp.OH = a.H;
+        pp.OW = a.W;
+        pp.Cin = a.Cin;
+        pp.Cout = a.Cout;
+        pp.act = a.act;
+        p.pool_by_next = true;
+        q.pool_pw = true;
+        q.pp = pp;
+    }
+}
+
 int check_stack(const conv2d_op *ops, int n, int layout, int dtype, size_t ws, std::vector<OpPlan> *plans,
                 int *bad) {
     if (n < 0 || (n > 0 && !ops)) return set_error(CONV2D_EINVAL, "ops must hold n >= 0 entries");
@@ -1003,6 +1049,7 @@ int check_stack(const conv2d_op *ops, int n, int layout, int dtype, size_t ws, s
         }
     }
     link_chains(*plans, ws);
+    link_pool_pw(*plans);
     return CONV2D_OK;
 }
 
@@ -1018,6 +1065,10 @@ int launch_op(const OpPlan &o, const Workspace &ws, hipStream_t st) {
     const bool nchw = o.layout == CONV2D_LAYOUT_NCHW;
     switch (o.kind) {
     case CONV2D_OP_CONV:
+        if (o.pool_pw) {
+            e = launch_poolpw(o.pp, o.dtype, st);
+            return e == hipSuccess ? CONV2D_OK : hip_fail(e, "avgpool2x2 + conv1x1 launch");
+        }
         return launch_conv(o.a, o.plan, o.layout, o.dtype, ws, st);
     case CONV2D_OP_CONV_MAXPOOL: {
         const ConvArgs &a = o.a;
@@ -1046,6 +1097,7 @@ int launch_op(const OpPlan &o, const Workspace &ws, hipStream_t st) {
         e = launch_maxpool(o.x, o.y, o.N, o.H, o.W, o.C, nchw, o.dtype, o.vec, st);
         return e == hipSuccess ? CONV2D_OK : hip_fail(e, "maxpool3x3s2 launch");
     case CONV2D_OP_AVGPOOL:
+        if (o.pool_by_next) return CONV2D_OK;  // computed by the next op's kernel
         e = launch_avgpool(o.x, o.y, o.N, o.H, o.W, o.C, nchw, o.dtype, o.vec, st);
         return e == hipSuccess ? CONV2D_OK : hip_fail(e, "avgpool2x2 launch");
     case CONV2D_OP_COPY:
@@ -1095,6 +1147,11 @@ int describe_op(const OpPlan &o, char *buf, int cap) {
     char tmp[200];
     switch (o.kind) {
     case CONV2D_OP_CONV:
+        if (o.pool_pw) {
+            snprintf(tmp, sizeof tmp, "avgpool2x2+conv1x1_nhwc %s %dx128 (with the previous op)",
+                     dtype_name(o.dtype), o.a.Cin == 64 ? 64 : 32);
+            break;
+        }
         return describe(o.plan, o.layout, o.dtype, buf, cap);
     case CONV2D_OP_CONV_MAXPOOL:
         if (o.pf.kind == POOL_FUSED_STEM) {
@@ -1112,7 +1169,7 @@ int describe_op(const OpPlan &o, char *buf, int cap) {
         snprintf(tmp, sizeof tmp, "maxpool3x3s2");
         break;
     case CONV2D_OP_AVGPOOL:
-        snprintf(tmp, sizeof tmp, "avgpool2x2");
+        snprintf(tmp, sizeof tmp, o.pool_by_next ? "avgpool2x2 (in the next op's kernel)" : "avgpool2x2");
         break;
     case CONV2D_OP_DECONV:
         if (o.dp.mfma)

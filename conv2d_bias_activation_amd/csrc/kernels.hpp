@@ -106,6 +106,22 @@ struct HgemmInfo {
     long long tiles;  // workgroups of the launch
 };
 
+// The 2x2 average pool of x followed by a 1x1 convolution of the pooled map, one kernel
+// (channel-last, 16-bit, Cin 64/128/256, Cout % 8 == 0, OH = H/2, OW = W/2): y is the
+// conv output, p (if not null) receives the pooled map as well.
+struct PoolPwArgs {
+    const void *x;      // [N, H, W, Cin]
+    const void *w;      // [Cout, Cin] (1x1 weights)
+    const float *bias;  // may be null
+    const float *alpha; // may be null unless PReLU
+    void *y;            // [N, OH, OW, Cout]
+    void *p;            // [N, OH, OW, Cin] or null
+    int N, H, W, OH, OW, Cin, Cout, act;
+    int tiles_n;        // set by the launcher
+};
+bool poolpw_fits(int Cin, int Cout, int dtype);
+hipError_t launch_poolpw(const PoolPwArgs &a, int dtype, hipStream_t st);
+
 // 3x3 stride-1 or stride-2 pad-1 channel-last 16-bit convolution of wide layers with halo tiles
 // and weights staged per K chunk: Cin a multiple of the variant's K chunk (32 or 64),
 // Cout % 8 == 0, y and the residual 16-byte aligned (a.vec_out), x, w and y under 2 GiB.
