@@ -99,18 +99,29 @@ __global__ __launch_bounds__(256) void stem3_kernel(ConvArgs a, int rstr) {
 
     // Stage input rows iy = oy0*S - 1 + r, r < RS: LDS row r = [16 zero bytes][W x 6
     // bytes][zeros up to rstr]; the pixel at column ix starts at byte 16 + 6*ix.
+    // Eight loads per thread go out before their LDS writes (unconditional, with an
+    // out-of-range offset for padding), so a workgroup waits for one load latency per
+    // round instead of one per load.
     {
         const int row_bytes = W * 6;
-        const int chunks = rstr / 16;
+        const int chunks = rstr / 16, total = RS * chunks;
         const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint32_t)((size_t)a.N * H * row_bytes));
-        for (int i = threadIdx.x; i < RS * chunks; i += 256) {
-            const int r = i / chunks, c = i - r * chunks;
-            const int iy = oy0 * S - 1 + r;
-            const int b = c * 16 - 16;  // byte within the image row
-            u32x4 v = u32x4{0u, 0u, 0u, 0u};
-            if (b >= 0 && b < row_bytes && (unsigned)iy < (unsigned)H)
-                v = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)((size_t)(n * H + iy) * row_bytes + b), 0, 0);
-            *reinterpret_cast<u32x4 *>(srow + r * rstr + c * 16) = v;
+        for (int i0 = threadIdx.x; i0 < total; i0 += 8 * 256) {
+            u32x4 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int i = i0 + 256 * u, r = i / chunks, c = i - r * chunks;
+                const int iy = oy0 * S - 1 + r;
+                const int b = c * 16 - 16;  // byte within the image row
+                const bool ok = i < total && b >= 0 && b < row_bytes && (unsigned)iy < (unsigned)H;
+                v[u] = __builtin_amdgcn_raw_buffer_load_b128(
+                    rx, ok ? (int)((size_t)(n * H + iy) * row_bytes + b) : (int)kOOB, 0, 0);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int i = i0 + 256 * u, r = i / chunks, c = i - r * chunks;
+                if (i < total) *reinterpret_cast<u32x4 *>(srow + r * rstr + c * 16) = v[u];
+            }
         }
     }
     __syncthreads();
@@ -280,16 +291,24 @@ __global__ __launch_bounds__(256) void stem3_pool_kernel(ConvArgs a, int PH, int
     const int ixs = seg * ixs_step - 8;
     {
         const int row_bytes = W * 6;
-        const int chunks = rstr / 16;
+        const int chunks = rstr / 16, total = RS * chunks;
         const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint32_t)((size_t)a.N * H * row_bytes));
-        for (int i = threadIdx.x; i < RS * chunks; i += 256) {
-            const int r = i / chunks, c = i - r * chunks;
-            const int iy = (2 * py - 1) * S - 1 + r;
-            const int b = ixs * 6 + c * 16;  // byte within the image row
-            u32x4 v = u32x4{0u, 0u, 0u, 0u};
-            if (b >= 0 && b < row_bytes && (unsigned)iy < (unsigned)H)
-                v = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)((size_t)(n * H + iy) * row_bytes + b), 0, 0);
-            *reinterpret_cast<u32x4 *>(srow + r * rstr + c * 16) = v;
+        for (int i0 = threadIdx.x; i0 < total; i0 += 8 * 256) {
+            u32x4 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int i = i0 + 256 * u, r = i / chunks, c = i - r * chunks;
+                const int iy = (2 * py - 1) * S - 1 + r;
+                const int b = ixs * 6 + c * 16;  // byte within the image row
+                const bool ok = i < total && b >= 0 && b < row_bytes && (unsigned)iy < (unsigned)H;
+                v[u] = __builtin_amdgcn_raw_buffer_load_b128(
+                    rx, ok ? (int)((size_t)(n * H + iy) * row_bytes + b) : (int)kOOB, 0, 0);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int i = i0 + 256 * u, r = i / chunks, c = i - r * chunks;
+                if (i < total) *reinterpret_cast<u32x4 *>(srow + r * rstr + c * 16) = v[u];
+            }
         }
     }
     __syncthreads();

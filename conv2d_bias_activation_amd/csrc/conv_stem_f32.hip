@@ -90,14 +90,25 @@ __device__ __forceinline__ void stem_f32_stage(const ConvArgs &a, int n, int iy0
     const int H = a.H, W = a.W;
     const int chunks = ncols * 3 / 4;  // 16-byte chunks per staged row
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint32_t)((size_t)a.N * H * W * 12));
-    for (int i = threadIdx.x; i < nrows * chunks; i += blockDim.x) {
-        const int r = i / chunks, c = i - r * chunks;
-        const int iy = iy0 + r;
-        const int fl = ix0 * 3 + c * 4;  // float within the image row (may be negative)
-        u32x4 v = u32x4{0u, 0u, 0u, 0u};
-        if ((unsigned)iy < (unsigned)H && fl >= 0 && fl < W * 3)
-            v = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(((size_t)(n * H + iy) * W * 3 + fl) * 4), 0, 0);
-        *reinterpret_cast<u32x4 *>(sx + r * rf + c * 4) = v;
+    // eight loads per thread in flight before their LDS writes (unconditional, with an
+    // out-of-range offset for padding): one load latency per round
+    const int total = nrows * chunks, step = (int)blockDim.x;
+    for (int i0 = threadIdx.x; i0 < total; i0 += 8 * step) {
+        u32x4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int i = i0 + step * u, r = i / chunks, c = i - r * chunks;
+            const int iy = iy0 + r;
+            const int fl = ix0 * 3 + c * 4;  // float within the image row (may be negative)
+            const bool ok = i < total && (unsigned)iy < (unsigned)H && fl >= 0 && fl < W * 3;
+            v[u] = __builtin_amdgcn_raw_buffer_load_b128(
+                rx, ok ? (int)(((size_t)(n * H + iy) * W * 3 + fl) * 4) : (int)kOOB, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int i = i0 + step * u, r = i / chunks, c = i - r * chunks;
+            if (i < total) *reinterpret_cast<u32x4 *>(sx + r * rf + c * 4) = v[u];
+        }
     }
 }
 
