@@ -160,6 +160,7 @@ struct Plan {
     NhwcPlan nh;
     HaloPlan halo;
     HgemmPlan hg;
+    bool nchw_hg;  // FAM_NCHW_VIA_NHWC: the halo-tile GEMM (hg) instead of the pipelined kernel (nh)
     bool tuned;  // chosen by a conv2d_tune measurement rather than the built-in heuristics
     bool w_ohwi; // channel-first layer with channel-last weights: only the input is copied
     // chained channel-first layers of a stack (FAM_NCHW_VIA_NHWC, set by link_chains)
@@ -344,18 +345,31 @@ bool stem_fits(const ConvArgs &a, int layout, int dtype) {
 
 // Halo-tile GEMM kernel for wide 3x3 stride-1 layers (channel-last, 16-bit, Cin a
 // multiple of 32; variants with 64-channel K chunks need Cin % 64 == 0).
-bool hgemm_fits(const ConvArgs &a, int layout, int dtype) {
+bool hgemm_shape_ok(const ConvArgs &a, int dtype) {
     const int eb = dtype_bytes(dtype);
-    return layout == CONV2D_LAYOUT_NHWC && dtype != CONV2D_DTYPE_F32 && a.kh == 3 && a.kw == 3 &&
-           (a.stride == 1 || a.stride == 2) && a.pad == 1 && (a.Cin % 32) == 0 && (a.Cout % 8) == 0 && a.vec_out && aligned16(a.x) && aligned16(a.w) &&
-           (long long)a.N * a.H * a.W * a.Cin * eb < (1ll << 31) && (long long)a.Cout * a.K * eb < (1ll << 31) &&
-           (long long)a.M * a.Cout * eb < (1ll << 31);
+    return dtype != CONV2D_DTYPE_F32 && a.kh == 3 && a.kw == 3 && (a.stride == 1 || a.stride == 2) && a.pad == 1 &&
+           a.Cin >= 32 && (a.Cin % 8) == 0 && (a.Cout % 8) == 0 && (long long)a.N * a.H * a.W * a.Cin * eb < (1ll << 31) &&
+           (long long)a.Cout * a.K * eb < (1ll << 31) && (long long)a.M * a.Cout * eb < (1ll << 31);
 }
 
-bool hgemm_cfg_ok(const ConvArgs &a, int cfg) {
+bool hgemm_fits(const ConvArgs &a, int layout, int dtype) {
+    return layout == CONV2D_LAYOUT_NHWC && hgemm_shape_ok(a, dtype) && (a.Cin % 32) == 0 && a.vec_out &&
+           aligned16(a.x) && aligned16(a.w);
+}
+
+// A channel-first layer on the halo-tile GEMM: its input copied channel-last into the
+// workspace (or handed over by the previous conv of a stack), weights channel-last,
+// output (and residual) written channel-first by the GEMM's epilogue.
+bool hgemm_nchw_fits(const ConvArgs &a, int layout, int dtype) {
+    return layout == CONV2D_LAYOUT_NCHW && hgemm_shape_ok(a, dtype) && (!a.w_ohwi || aligned16(a.w));
+}
+
+// Channel-last outputs need Cin a multiple of the variant's K chunk; channel-first ones
+// (not on the specialised-wave variants) take a partial last chunk.
+bool hgemm_cfg_ok(const ConvArgs &a, int cfg, bool nchw = false) {
     HgemmInfo in{};
-    return hgemm_cfg_info(cfg, a, &in) && in.stride == a.stride && (a.Cin % in.ck) == 0 && in.tiles > 0 &&
-           in.tiles < (1ll << 31);
+    return hgemm_cfg_info(cfg, a, &in) && in.stride == a.stride && (nchw ? !in.ws : (a.Cin % in.ck) == 0) &&
+           in.tiles > 0 && in.tiles < (1ll << 31);
 }
 
 // Tile order: each XCD (one L2) gets a contiguous run of tile ids; with the channel
@@ -442,6 +456,15 @@ Plan make_plan_default(const ConvArgs &a, int layout, int dtype, size_t ws) {
         p.nh = plan_nhwc(a, ws);
         p.nh.splits = 1;
         p.nh.nchw_out = true;
+        // wide layers on the halo-tile GEMM: the 17 x 15-pixel tiles where one round of
+        // workgroups covers the layer (the IFNet block: 256 tiles), else the 10 x 10 ones
+        if (hgemm_nchw_fits(a, layout, dtype) && a.Cin >= 128) {
+            HgemmInfo in{};
+            p.nchw_hg = true;
+            p.hg.cfg = hgemm_cfg_ok(a, 9, true) && hgemm_cfg_info(9, a, &in) && in.tiles <= 256 ? 9 : 0;
+            p.hg.cfast = false;
+            if (!hgemm_cfg_ok(a, p.hg.cfg, true)) p.nchw_hg = false;
+        }
         return p;
     }
     return igemm_plan(a, layout, dtype);
@@ -454,9 +477,12 @@ Plan make_plan_default(const ConvArgs &a, int layout, int dtype, size_t ws) {
 // variant of the channel-last matrix-core families. make_plan consults it for shapes
 // whose built-in choice is one of those families, and uses an entry only if the variant
 // is valid for the call at hand (alignment, workspace size).
+constexpr int kNchwHgTile = 100;  // FAM_NCHW_VIA_NHWC entries at or above: halo-tile GEMM variants
+
 struct TunedEntry {
     int family;  // FAM_NHWC, FAM_NCHW_VIA_NHWC, FAM_HALO, FAM_HALO_WS or FAM_HGEMM
-    int tile;    // NhwcTile (FAM_NHWC, FAM_NCHW_VIA_NHWC) or kernel variant (FAM_HGEMM)
+    int tile;    // NhwcTile (FAM_NHWC, FAM_NCHW_VIA_NHWC), kernel variant (FAM_HGEMM), or
+                 // kNchwHgTile + kernel variant (FAM_NCHW_VIA_NHWC on the halo-tile GEMM)
     int splits;  // K slices (FAM_NHWC; 1 for FAM_NCHW_VIA_NHWC and FAM_HGEMM)
     int th;      // tile height (FAM_HALO); tile order, channel tiles fastest or not (FAM_HGEMM)
 };
@@ -516,11 +542,19 @@ void apply_tuned(const ConvArgs &a, int layout, int dtype, size_t ws, Plan *p) {
         e = it->second;
     }
     if (p->family == FAM_NCHW_VIA_NHWC || e.family == FAM_NCHW_VIA_NHWC) {
-        // channel-first layers: only the tile of the channel-last kernel is chosen
-        if (p->family != FAM_NCHW_VIA_NHWC || e.family != FAM_NCHW_VIA_NHWC || e.tile < 0 ||
-            e.tile >= NHWC_TILE_COUNT)
-            return;
-        p->nh.tile = e.tile;
+        // channel-first layers: the tile of the channel-last kernel (tile < NHWC_TILE_COUNT),
+        // or halo-tile GEMM variant tile - kNchwHgTile with th the tile order
+        if (p->family != FAM_NCHW_VIA_NHWC || e.family != FAM_NCHW_VIA_NHWC || e.tile < 0) return;
+        if (e.tile < NHWC_TILE_COUNT) {
+            p->nh.tile = e.tile;
+            p->nchw_hg = false;
+        } else {
+            const int cfg = e.tile - kNchwHgTile;
+            if (!hgemm_nchw_fits(a, layout, dtype) || !hgemm_cfg_ok(a, cfg, true) || (e.th != 0 && e.th != 1)) return;
+            p->nchw_hg = true;
+            p->hg.cfg = cfg;
+            p->hg.cfast = e.th == 1;
+        }
         p->tuned = true;
     } else if (e.family == FAM_HALO) {
         if (!halo_fits(a, layout, dtype) || !halo_th_ok(a, e.th)) return;
@@ -585,6 +619,13 @@ int describe(const Plan &p, int layout, int dtype, char *buf, int cap) {
         (void)hgemm_cfg_info(p.hg.cfg, z, &in);
         snprintf(tmp, sizeof tmp, "%s %s v%d %dx%dx%d ck%d w%d %s", in.ws ? "hgemmws3x3_nhwc" : "hgemm3x3_nhwc",
                  dtype_name(dtype), p.hg.cfg, in.th, in.tw, in.cb, in.ck, in.waves, p.hg.cfast ? "cfast" : "pfast");
+    } else if (p.family == FAM_NCHW_VIA_NHWC && p.nchw_hg) {
+        ConvArgs z{};
+        HgemmInfo in{};
+        (void)hgemm_cfg_info(p.hg.cfg, z, &in);
+        snprintf(tmp, sizeof tmp, "%shgemm3x3_nchw_out %s v%d %dx%dx%d ck%d w%d %s%s",
+                 p.chain_in ? "chained+" : p.w_ohwi ? "x_to_nhwc+" : "to_nhwc+", dtype_name(dtype), p.hg.cfg, in.th,
+                 in.tw, in.cb, in.ck, in.waves, p.hg.cfast ? "cfast" : "pfast", p.chain_out ? " +y_nhwc" : "");
     } else if (p.family == FAM_NHWC || p.family == FAM_NCHW_VIA_NHWC) {
         snprintf(tmp, sizeof tmp, "%sigemm_nhwc_pipe%s %s %s splitk=%d%s",
                  p.family == FAM_NCHW_VIA_NHWC ? (p.chain_in ? "chained+" : p.w_ohwi ? "x_to_nhwc+" : "to_nhwc+") : "",
@@ -645,7 +686,7 @@ int launch_conv(const ConvArgs &a, const Plan &p, int layout, int dtype, const W
         if (rc) return rc;
         e = launch_halo3x3_ws(a, dtype, cus, st);
     } else if (p.family == FAM_HGEMM) {
-        e = launch_hgemm3x3(a, dtype, p.hg, st);
+        e = launch_hgemm3x3(a, dtype, p.hg, false, st);
     } else if (p.family == FAM_NHWC) {
         e = launch_igemm_nhwc(a, dtype, p.nh, p.nh.splits > 1 ? reinterpret_cast<float *>(ws.p) : nullptr, st);
     } else if (p.family == FAM_NCHW_VIA_NHWC) {
@@ -666,7 +707,7 @@ int launch_conv(const ConvArgs &a, const Plan &p, int layout, int dtype, const W
             b.x = xs;
             b.w = a.w_ohwi ? a.w : ws;
             b.y2 = p.chain_out ? base + p.y2_at : nullptr;
-            e = launch_igemm_nhwc(b, dtype, p.nh, nullptr, st);
+            e = p.nchw_hg ? launch_hgemm3x3(b, dtype, p.hg, true, st) : launch_igemm_nhwc(b, dtype, p.nh, nullptr, st);
         }
     } else {
         e = launch_igemm(a, dtype, p.ig, st);
@@ -1248,8 +1289,20 @@ int tune_run(int N, int H, int W, int Cin, int Cout, int kh, int kw, int stride,
     if (def.family == FAM_NCHW_VIA_NHWC) {
         for (int tile = 0; tile < NHWC_TILE_COUNT; ++tile) {
             Plan c = def;
+            c.nchw_hg = false;
             c.nh.tile = tile;
             cands.push_back(c);
+        }
+        if (hgemm_nchw_fits(a, layout, dtype)) {
+            for (int cfg = 0; cfg < hgemm_cfg_count(); ++cfg)
+                for (bool cf : {false, true}) {
+                    if (!hgemm_cfg_ok(a, cfg, true)) continue;
+                    Plan c = def;
+                    c.nchw_hg = true;
+                    c.hg.cfg = cfg;
+                    c.hg.cfast = cf;
+                    cands.push_back(c);
+                }
         }
     } else if (def.family == FAM_NHWC || def.family == FAM_HALO || def.family == FAM_HALO_WS ||
                def.family == FAM_HGEMM) {
@@ -1339,6 +1392,8 @@ int tune_run(int N, int H, int W, int Cin, int Cout, int kh, int kw, int stride,
         if (!dev.empty()) {
             TunedEntry t{best_out->family, best_out->nh.tile, best_out->nh.splits, best_out->halo.th};
             if (best_out->family == FAM_HGEMM) t = TunedEntry{FAM_HGEMM, best_out->hg.cfg, 1, best_out->hg.cfast ? 1 : 0};
+            if (best_out->family == FAM_NCHW_VIA_NHWC && best_out->nchw_hg)
+                t = TunedEntry{FAM_NCHW_VIA_NHWC, kNchwHgTile + best_out->hg.cfg, 1, best_out->hg.cfast ? 1 : 0};
             std::lock_guard<std::mutex> lock(g_tune_mu);
             g_tuned[tune_key(dev, a, layout, dtype)] = t;
             g_tuned_n.store((int)g_tuned.size(), std::memory_order_release);
@@ -1568,6 +1623,9 @@ int conv2d_tune_load(const char *path) {
                                                     t.splits >= 1 && t.splits <= 4) ||
                                                    (t.family == FAM_NCHW_VIA_NHWC && t.tile >= 0 &&
                                                     t.tile < NHWC_TILE_COUNT && t.splits == 1) ||
+                                                   (t.family == FAM_NCHW_VIA_NHWC && t.tile >= kNchwHgTile &&
+                                                    t.tile < kNchwHgTile + hgemm_cfg_count() && t.splits == 1 &&
+                                                    (t.th == 0 || t.th == 1)) ||
                                                    (t.family == FAM_HALO && (t.th == 4 || t.th == 8)) ||
                                                    (t.family == FAM_HALO_WS && t.th == 4) ||
                                                    (t.family == FAM_HGEMM && t.tile >= 0 && t.tile < hgemm_cfg_count() &&

@@ -1,5 +1,5 @@
 // 3x3 stride-1 or stride-2 pad-1 channel-last convolution for wide layers (Cin a multiple of the K
-// chunk, Cout a multiple of 8) on CDNA4 matrix cores: the implicit GEMM of the
+// chunk, or of 8 for channel-first outputs; Cout a multiple of 8) on CDNA4 matrix cores: the implicit GEMM of the
 // inferencelayer page's `conv()` (m = output pixel, k = (tap, input channel), n = output
 // channel, fused bias + activation epilogue) with halo tiles in place of a per-tap
 // patch gather, as in the framecast page's tiled convolution shader.
@@ -88,7 +88,7 @@ struct HgCfg {
     static_assert(S == 1 || S == 2, "stride 1 or 2");
 };
 
-template <typename T, typename C>
+template <typename T, typename C, bool NCHW>
 __global__ __launch_bounds__(64 * C::NW, 1) void hgemm3x3_kernel(ConvArgs a, HgemmGeo g) {
     __shared__ __attribute__((aligned(1024))) char lds[C::LDS];
     typedef typename Mfma32<T>::vec vec;
@@ -118,15 +118,24 @@ __global__ __launch_bounds__(64 * C::NW, 1) void hgemm3x3_kernel(ConvArgs a, Hge
     // lane l its 16-byte slot l. base[d] is the byte offset of the slot's data for
     // input-channel chunk 0 (chunk c adds c*CK elements), or kHgBad where there is
     // nothing to load (a halo pixel outside the image or past the halo, a weight row
-    // past Cout or past the weights): such loads write zeros.
+    // past Cout or past the weights): such loads write zeros. The channel-first
+    // instantiation also takes a Cin that is not a multiple of CK: its last chunk is
+    // partial, and bit d of lastok says whether slot d's 8 channels lie inside it (the
+    // others load zeros there, for the pixels and the weights alike, so the k steps past
+    // Cin add zero products). The channel-last one needs whole chunks, which keeps its
+    // copy path free of that test.
+    constexpr bool PARTIAL = NCHW;
     uint32_t base[NLD];
+    uint32_t lastok = 0;
+    const int nfull = Cin / C::CK, crem = PARTIAL ? Cin - nfull * C::CK : 0;
 #pragma unroll
     for (int d = 0; d < NLD; ++d) {
         const int ch = d * C::NW + wave;
         uint32_t b = kHgBad;
+        int qv = 0;
         if (ch < C::HCH) {
             const int s = ch * 64 + lane, r = s / RS, pos = s % RS;
-            const int qv = pos ^ ((r / C::SWZ) % RS);
+            qv = pos ^ ((r / C::SWZ) % RS);
             if (r < C::HR) {
                 const int hy = r / C::HW2, hx = r % C::HW2;
                 const int iy = C::S * oy0 - 1 + hy, ix = C::S * ox0 - 1 + hx;
@@ -135,26 +144,33 @@ __global__ __launch_bounds__(64 * C::NW, 1) void hgemm3x3_kernel(ConvArgs a, Hge
             }
         } else if (ch < C::NCH) {
             const int s = (ch - C::HCH) * 64 + lane, r = s / RS, pos = s % RS;
-            const int qv = pos ^ ((r / C::SWZ) % RS);
+            qv = pos ^ ((r / C::SWZ) % RS);
             if (r < C::WR) {
                 const int tap = r / C::CB, co = co0 + r % C::CB;
                 if (co < Cout) b = (uint32_t)((((co * 9 + tap) * Cin) + qv * 8) * (int)sizeof(T));
             }
         }
         base[d] = b;
+        if (PARTIAL && qv * 8 < crem) lastok |= 1u << d;
     }
     const i32x4 rx = rsrc_words(a.x, (uint32_t)((size_t)a.N * H * W * Cin * sizeof(T)));
     const i32x4 rw = rsrc_words(a.w, (uint32_t)((size_t)Cout * 9 * Cin * sizeof(T)));
-    const int nchunks = Cin / C::CK;
+    const int nchunks = nfull + (crem != 0 ? 1 : 0);
     const uint32_t lds0 = lds_addr(lds);
     // Issues input-channel chunk c into stage st. A chunk past the last one issues the
     // same loads at out-of-range offsets, so that every chunk adds exactly NLD to this
     // wave's count of outstanding vector-memory operations.
     auto issue_one = [&](int c, int st, int d) {
-        const uint32_t cadd = c < nchunks ? (uint32_t)(c * C::CK * (int)sizeof(T)) : kHgBad;
         const int ch = d * C::NW + wave;
         const uint32_t dst = ch < C::NCH ? lds0 + st * C::STAGE + ch * 1024 : lds0 + C::SINK;
-        const uint32_t off = base[d] == kHgBad ? kHgBad : base[d] + cadd;
+        uint32_t off;
+        if constexpr (PARTIAL) {
+            const bool live = c < nfull || (c < nchunks && ((lastok >> d) & 1u) != 0);
+            off = (base[d] == kHgBad || !live) ? kHgBad : base[d] + (uint32_t)(c * C::CK * (int)sizeof(T));
+        } else {
+            const uint32_t cadd = c < nchunks ? (uint32_t)(c * C::CK * (int)sizeof(T)) : kHgBad;
+            off = base[d] == kHgBad ? kHgBad : base[d] + cadd;
+        }
         dma_b128(ch < C::HCH ? rx : rw, off, dst);
     };
     auto issue = [&](int c, int st) {
@@ -257,13 +273,20 @@ __global__ __launch_bounds__(64 * C::NW, 1) void hgemm3x3_kernel(ConvArgs a, Hge
     // Epilogue from registers. Block (i, j): lane (rl, hi) holds channels 8*q + 4*hi +
     // 0..3 (q < 4) of the block's 32, for pixel rl; one lane-half swap per pair of groups
     // (2*pp, 2*pp + 1) leaves lane (rl, hi) with 8 consecutive channels 16*pp + 8*hi..
-    // (lanes 32..63 of the first group trade with lanes 0..31 of the second).
+    // (lanes 32..63 of the first group trade with lanes 0..31 of the second), stored as
+    // one 16-byte run. With NCHW, y and the residual are channel-first instead: each
+    // value is read and stored as one 16-bit element of its channel plane (before the
+    // swap), and the same rounded values also go channel-last to y2 when it is set (the
+    // input copy of the next channel-first conv of a stack).
     const uint32_t out_bytes = (uint32_t)((size_t)a.M * Cout * sizeof(T));
     const bool has_res = a.res != nullptr;
     const __amdgpu_buffer_rsrc_t rres = make_rsrc(a.res, has_res ? out_bytes : 0u);
     const __amdgpu_buffer_rsrc_t ry = make_rsrc(a.y, out_bytes);
+    const bool store_cl = !NCHW || a.y2 != nullptr;  // channel-last runs are stored
+    const __amdgpu_buffer_rsrc_t rcl = NCHW ? make_rsrc(a.y2, a.y2 ? out_bytes : 0u) : ry;
     const __amdgpu_buffer_rsrc_t rbias = make_rsrc(a.bias, a.bias ? (uint32_t)Cout * 4u : 0u);
     const __amdgpu_buffer_rsrc_t ralpha = make_rsrc(a.alpha, a.alpha ? (uint32_t)Cout * 4u : 0u);
+    const uint32_t plane = (uint32_t)OH * (uint32_t)OW;
     auto swap_halves = [](u32x2 &lo, u32x2 &hi2) {
 #pragma unroll
         for (int d = 0; d < 2; ++d) {
@@ -272,7 +295,8 @@ __global__ __launch_bounds__(64 * C::NW, 1) void hgemm3x3_kernel(ConvArgs a, Hge
             hi2[d] = r2[1];
         }
     };
-    uint32_t off[NBW][FN][2];
+    uint32_t off[NBW][FN][2];  // channel-last byte offsets of this lane's two 8-channel runs
+    uint32_t opx[NBW];         // channel-first: the pixel's index within its plane, or kOOB
     u32x4 rv[NBW][FN][2];
 #pragma unroll
     for (int i = 0; i < NBW; ++i) {
@@ -281,6 +305,7 @@ __global__ __launch_bounds__(64 * C::NW, 1) void hgemm3x3_kernel(ConvArgs a, Hge
         const int py = p / C::TW, px = p % C::TW;
         const int oy = oy0 + py, ox = ox0 + px;
         const bool pin = b < C::NBLK && p < C::P && oy < OH && ox < OW;
+        opx[i] = pin ? (uint32_t)(oy * OW + ox) : kOOB;
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
@@ -290,8 +315,8 @@ __global__ __launch_bounds__(64 * C::NW, 1) void hgemm3x3_kernel(ConvArgs a, Hge
                                     ? ((uint32_t)((n * OH + oy) * OW + ox) * (uint32_t)Cout + (uint32_t)co) *
                                           (uint32_t)sizeof(T)
                                     : kOOB;
-                rv[i][j][pp] = has_res ? __builtin_amdgcn_raw_buffer_load_b128(rres, (int)off[i][j][pp], 0, 0)
-                                       : u32x4{0u, 0u, 0u, 0u};
+                rv[i][j][pp] = (has_res && !NCHW) ? __builtin_amdgcn_raw_buffer_load_b128(rres, (int)off[i][j][pp], 0, 0)
+                                                  : u32x4{0u, 0u, 0u, 0u};
             }
     }
     const int mode = has_res ? (a.res_before_act ? 1 : 2) : 0;
@@ -321,16 +346,38 @@ __global__ __launch_bounds__(64 * C::NW, 1) void hgemm3x3_kernel(ConvArgs a, Hge
 #pragma unroll
             for (int i = 0; i < NBW; ++i) {
                 if (i >= nb) continue;
+                // channel-first element offsets of group q (channel co0 + 32*(wc*FN+j) + 8*q + 4*hi + e
+                // at offset oq[q] + e * plane elements), and the residual read from there
+                uint32_t oq[4] = {kOOB, kOOB, kOOB, kOOB};
+                T rn[16];
+                if constexpr (NCHW) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int co = co0 + 32 * (wc * FN + j) + 8 * q + 4 * hi;  // co + 3 < Cout iff co < Cout
+                        oq[q] = (opx[i] != kOOB && co < Cout) ? ((uint32_t)(n * Cout + co) * plane + opx[i]) : kOOB;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            uint16_t u = 0;
+                            if constexpr (RES != 0)
+                                u = __builtin_amdgcn_raw_buffer_load_b16(
+                                    rres, (int)(oq[q] == kOOB ? kOOB : (oq[q] + (uint32_t)e * plane) * 2u), 0, 0);
+                            __builtin_memcpy(&rn[4 * q + e], &u, 2);
+                        }
+                    }
+                }
 #pragma unroll
                 for (int pp = 0; pp < 2; ++pp) {
                     u32x2 q2[2];
                     u32x2 rq[2] = {u32x2{rv[i][j][pp][0], rv[i][j][pp][1]}, u32x2{rv[i][j][pp][2], rv[i][j][pp][3]}};
-                    if constexpr (RES != 0) swap_halves(rq[0], rq[1]);
+                    if constexpr (RES != 0 && !NCHW) swap_halves(rq[0], rq[1]);
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
                         const int q = 2 * pp + h;
                         T rt[4], out[4];
-                        __builtin_memcpy(rt, &rq[h], 8);
+                        if constexpr (NCHW)
+                            __builtin_memcpy(rt, &rn[4 * q], 8);
+                        else
+                            __builtin_memcpy(rt, &rq[h], 8);
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             float v = acc[i][j][4 * q + e] + bq[4 * q + e];
@@ -340,12 +387,20 @@ __global__ __launch_bounds__(64 * C::NW, 1) void hgemm3x3_kernel(ConvArgs a, Hge
                             if constexpr (ACT == CONV2D_ACT_PRELU) v = v >= 0.0f ? v : aq[4 * q + e] * v;
                             if constexpr (RES == 2) v += to_f32(rt[e]);
                             out[e] = round_fp32<T>(v);
+                            if constexpr (NCHW) {
+                                uint16_t u;
+                                __builtin_memcpy(&u, &out[e], 2);
+                                __builtin_amdgcn_raw_buffer_store_b16(
+                                    u, ry, (int)(oq[q] == kOOB ? kOOB : (oq[q] + (uint32_t)e * plane) * 2u), 0, 0);
+                            }
                         }
                         __builtin_memcpy(&q2[h], out, 8);
                     }
-                    swap_halves(q2[0], q2[1]);
-                    __builtin_amdgcn_raw_buffer_store_b128(u32x4{q2[0][0], q2[0][1], q2[1][0], q2[1][1]}, ry,
-                                                           (int)off[i][j][pp], 0, 0);
+                    if (store_cl) {
+                        swap_halves(q2[0], q2[1]);
+                        __builtin_amdgcn_raw_buffer_store_b128(u32x4{q2[0][0], q2[0][1], q2[1][0], q2[1][1]}, rcl,
+                                                               (int)off[i][j][pp], 0, 0);
+                    }
                 }
             }
         }
@@ -704,7 +759,12 @@ typedef HgCfg<10, 20, 4, 1, 2, 2, 32, 2> HgV5;  // 200 px x 64 ch
 typedef HgCfg<10, 10, 4, 1, 2, 2, 32, 2, 2> HgV6;  // 100 px x 64 ch
 typedef HgCfg<10, 10, 4, 1, 1, 2, 32, 2, 2> HgV7;  // 100 px x 32 ch
 typedef HgCfg<8, 16, 4, 1, 2, 2, 32, 2, 2> HgV8;   // 128 px x 64 ch
-constexpr int kHgVariants = 9;
+// 255 px (17 x 15: 8 pixel blocks, one of them one pixel short) x 32 ch: a 68 x 120 map
+// of 240 channels (the IFNet block) in exactly 256 workgroups
+typedef HgCfg<17, 15, 8, 1, 1, 2, 32, 2> HgV9;   // eight waves, one pixel block each
+typedef HgCfg<17, 15, 4, 1, 1, 2, 32, 2> HgV10;  // four waves, two pixel blocks each
+typedef HgCfg<17, 15, 8, 1, 1, 3, 32, 2> HgV11;  // the same in a three-stage ring
+constexpr int kHgVariants = 12;
 
 template <typename C> long long hg_tiles(const ConvArgs &a) {
     return (long long)a.N * ((a.OW + C::TW - 1) / C::TW) * ((a.OH + C::TH - 1) / C::TH) *
@@ -718,8 +778,8 @@ template <typename C> constexpr int hg_stride() {
         return 1;
 }
 
-template <typename T, typename C> hipError_t launch_hgw_c(const ConvArgs &a, bool cfast, hipStream_t st) {
-    if ((a.Cin % C::CK) != 0 || a.stride != 1 || a.OH != a.H || a.OW != a.W) return hipErrorInvalidValue;
+template <typename T, typename C> hipError_t launch_hgw_c(const ConvArgs &a, bool cfast, bool nchw, hipStream_t st) {
+    if (nchw || (a.Cin % C::CK) != 0 || a.stride != 1 || a.OH != a.H || a.OW != a.W) return hipErrorInvalidValue;
     const long long tiles = hg_tiles<C>(a);
     if (tiles <= 0 || tiles > 0x7fffffffll) return hipErrorInvalidValue;
     HgemmGeo g{};
@@ -731,8 +791,9 @@ template <typename T, typename C> hipError_t launch_hgw_c(const ConvArgs &a, boo
     return launch_kernel(hgemmws3x3_kernel<T, C>, dim3((unsigned)tiles), dim3(64 * C::NWV), 0, st, a, g);
 }
 
-template <typename T, typename C> hipError_t launch_hg_c(const ConvArgs &a, bool cfast, hipStream_t st) {
-    if ((a.Cin % C::CK) != 0 || a.stride != C::S || a.OH != (a.H - 1) / C::S + 1 || a.OW != (a.W - 1) / C::S + 1)
+template <typename T, typename C> hipError_t launch_hg_c(const ConvArgs &a, bool cfast, bool nchw, hipStream_t st) {
+    if ((a.Cin % (nchw ? 8 : C::CK)) != 0 || a.stride != C::S || a.OH != (a.H - 1) / C::S + 1 ||
+        a.OW != (a.W - 1) / C::S + 1)
         return hipErrorInvalidValue;
     const long long tiles = hg_tiles<C>(a);
     if (tiles <= 0 || tiles > 0x7fffffffll) return hipErrorInvalidValue;
@@ -742,20 +803,24 @@ template <typename T, typename C> hipError_t launch_hg_c(const ConvArgs &a, bool
     g.tiles_c = (a.Cout + C::CB - 1) / C::CB;
     g.ntiles_p = a.N * g.tiles_x * g.tiles_y;
     g.cfast = cfast ? 1 : 0;
-    return launch_kernel(hgemm3x3_kernel<T, C>, dim3((unsigned)tiles), dim3(64 * C::NW), 0, st, a, g);
+    if (nchw) return launch_kernel(hgemm3x3_kernel<T, C, true>, dim3((unsigned)tiles), dim3(64 * C::NW), 0, st, a, g);
+    return launch_kernel(hgemm3x3_kernel<T, C, false>, dim3((unsigned)tiles), dim3(64 * C::NW), 0, st, a, g);
 }
 
-template <typename T> hipError_t launch_hg_d(const ConvArgs &a, const HgemmPlan &p, hipStream_t st) {
+template <typename T> hipError_t launch_hg_d(const ConvArgs &a, const HgemmPlan &p, bool nchw, hipStream_t st) {
     switch (p.cfg) {
-    case 0: return launch_hg_c<T, HgV0>(a, p.cfast, st);
-    case 1: return launch_hgw_c<T, HgV1>(a, p.cfast, st);
-    case 2: return launch_hgw_c<T, HgV2>(a, p.cfast, st);
-    case 3: return launch_hg_c<T, HgV3>(a, p.cfast, st);
-    case 4: return launch_hg_c<T, HgV4>(a, p.cfast, st);
-    case 5: return launch_hg_c<T, HgV5>(a, p.cfast, st);
-    case 6: return launch_hg_c<T, HgV6>(a, p.cfast, st);
-    case 7: return launch_hg_c<T, HgV7>(a, p.cfast, st);
-    case 8: return launch_hg_c<T, HgV8>(a, p.cfast, st);
+    case 0: return launch_hg_c<T, HgV0>(a, p.cfast, nchw, st);
+    case 1: return launch_hgw_c<T, HgV1>(a, p.cfast, nchw, st);
+    case 2: return launch_hgw_c<T, HgV2>(a, p.cfast, nchw, st);
+    case 3: return launch_hg_c<T, HgV3>(a, p.cfast, nchw, st);
+    case 4: return launch_hg_c<T, HgV4>(a, p.cfast, nchw, st);
+    case 5: return launch_hg_c<T, HgV5>(a, p.cfast, nchw, st);
+    case 6: return launch_hg_c<T, HgV6>(a, p.cfast, nchw, st);
+    case 7: return launch_hg_c<T, HgV7>(a, p.cfast, nchw, st);
+    case 8: return launch_hg_c<T, HgV8>(a, p.cfast, nchw, st);
+    case 9: return launch_hg_c<T, HgV9>(a, p.cfast, nchw, st);
+    case 10: return launch_hg_c<T, HgV10>(a, p.cfast, nchw, st);
+    case 11: return launch_hg_c<T, HgV11>(a, p.cfast, nchw, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -793,16 +858,20 @@ bool hgemm_cfg_info(int cfg, const ConvArgs &a, HgemmInfo *o) {
     case 6: return fill(HgV6{});
     case 7: return fill(HgV7{});
     case 8: return fill(HgV8{});
+    case 9: return fill(HgV9{});
+    case 10: return fill(HgV10{});
+    case 11: return fill(HgV11{});
     default: return false;
     }
 }
 
-hipError_t launch_hgemm3x3(const ConvArgs &a, int dtype, const HgemmPlan &p, hipStream_t st) {
-    if (a.kh != 3 || a.kw != 3 || (a.stride != 1 && a.stride != 2) || a.pad != 1 || (a.Cout % 8) != 0 || !a.vec_out)
+hipError_t launch_hgemm3x3(const ConvArgs &a, int dtype, const HgemmPlan &p, bool nchw_out, hipStream_t st) {
+    if (a.kh != 3 || a.kw != 3 || (a.stride != 1 && a.stride != 2) || a.pad != 1 || (a.Cout % 8) != 0 ||
+        (!nchw_out && !a.vec_out) || (nchw_out && a.y2 && (reinterpret_cast<uintptr_t>(a.y2) & 15) != 0))
         return hipErrorInvalidValue;
     switch (dtype) {
-    case CONV2D_DTYPE_BF16: return launch_hg_d<bf16>(a, p, st);
-    case CONV2D_DTYPE_F16: return launch_hg_d<f16>(a, p, st);
+    case CONV2D_DTYPE_BF16: return launch_hg_d<bf16>(a, p, nchw_out, st);
+    case CONV2D_DTYPE_F16: return launch_hg_d<f16>(a, p, nchw_out, st);
     default: return hipErrorInvalidValue;
     }
 }

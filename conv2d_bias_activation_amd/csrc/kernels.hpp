@@ -125,7 +125,10 @@ hipError_t launch_poolpw(const PoolPwArgs &a, int dtype, hipStream_t st);
 // 3x3 stride-1 or stride-2 pad-1 channel-last 16-bit convolution of wide layers with halo tiles
 // and weights staged per K chunk: Cin a multiple of the variant's K chunk (32 or 64),
 // Cout % 8 == 0, y and the residual 16-byte aligned (a.vec_out), x, w and y under 2 GiB.
-hipError_t launch_hgemm3x3(const ConvArgs &a, int dtype, const HgemmPlan &p, hipStream_t st);
+// With nchw_out, y and the residual are channel-first (no alignment needed), Cin need
+// only be a multiple of 8, and a.y2, if set and 16-byte aligned, receives the same output
+// channel-last; the specialised-wave variants do not take it.
+hipError_t launch_hgemm3x3(const ConvArgs &a, int dtype, const HgemmPlan &p, bool nchw_out, hipStream_t st);
 int hgemm_cfg_count();
 bool hgemm_cfg_info(int cfg, const ConvArgs &a, HgemmInfo *out);
 

@@ -79,7 +79,7 @@ def test_plan_names_a_kernel_for_every_workload_shape():
              ((1, 640, 640, 3, 32, 3, 3, 2, 1, 2, 0, bf16), "stem3x3_mfma"),
              ((2, 23, 19, 3, 32, 3, 3, 2, 1, 2, 0, bf16), "direct_nhwc"),  # W % 8 != 0
              ((4, 80, 80, 512, 256, 1, 1, 1, 0, 1, 0, bf16), "igemm_nhwc_pipe"),
-             ((1, 68, 120, 240, 240, 3, 3, 1, 1, 3, 1, f16), "to_nhwc+igemm_nhwc_pipe"),
+             ((1, 68, 120, 240, 240, 3, 3, 1, 1, 3, 1, f16), "to_nhwc+hgemm3x3_nchw_out"),
              ((4, 40, 40, 256, 256, 3, 3, 1, 1, 1, 0, bf16), "hgemm3x3_nhwc"),
              ((4, 320, 320, 32, 64, 3, 3, 1, 1, 1, 0, bf16), "halo3x3_nhwc"),
              ((4, 160, 160, 64, 64, 3, 3, 1, 1, 1, 0, bf16), "halo3x3ws_nhwc"),
@@ -293,7 +293,8 @@ def test_weights_ohwi_flag_checks():
     f16, f32 = c2d.DTYPE_F16, c2d.DTYPE_F32
     nchw, nhwc = c2d.LAYOUT_NCHW, c2d.LAYOUT_NHWC
     act = c2d.ACT_PRELU | c2d.WEIGHTS_OHWI
-    assert c2d.plan(1, 68, 120, 240, 240, 3, 3, 1, 1, act, nchw, f16).startswith("x_to_nhwc+igemm_nhwc_pipe")
+    assert c2d.plan(1, 68, 120, 240, 240, 3, 3, 1, 1, act, nchw, f16).startswith("x_to_nhwc+hgemm3x3_nchw_out")
+    assert c2d.plan(1, 68, 120, 64, 64, 3, 3, 1, 1, act, nchw, f16).startswith("x_to_nhwc+igemm_nhwc_pipe")
     # the input's channel-last copy goes to the workspace: needed for this flag
     assert _check(layout=nchw, dtype=f16, Cin=16, act=c2d.ACT_RELU | c2d.WEIGHTS_OHWI) == c2d.EUNSUPPORTED
     with c2d._planning_workspace(1 << 20):
