@@ -368,7 +368,7 @@ KERNEL_SOURCES = [
     ("hgemmws3x3", ["conv_hgemm.hip", "igemm_common.hpp", "common.hpp"]),
     ("halo3x3ws", ["conv_halo_ws.hip", "igemm_common.hpp", "common.hpp"]),
     ("halo3x3", ["conv_halo.hip", "igemm_common.hpp", "common.hpp"]),
-    ("stem3x3", ["conv_stem.hip", "igemm_common.hpp", "common.hpp"]),
+    ("stem3x3", ["conv_stem.hip", "conv_stem_f32.hip", "igemm_common.hpp", "common.hpp"]),
     ("igemm_", ["conv_igemm.hip", "igemm_common.hpp", "common.hpp"]),
     ("maxpool", ["pool.hip", "common.hpp"]),
     ("avgpool", ["pool.hip", "common.hpp"]),
@@ -392,6 +392,11 @@ KERNEL_SYMBOLS = [
 def kernel_source_hash(plan=None):
     csrc = os.path.join(ROOT, "conv2d_bias_activation_amd", "csrc")
     files = sorted(f for f in os.listdir(csrc) if f.endswith((".hip", ".hpp")))
+    if plan:
+        # a channel-first plan runs the channel-last kernel after (or without) the layout
+        # copy: "x_to_nhwc+<kernel> ...", "chained+<kernel> ..."
+        head, _, rest = plan.partition(" ")
+        plan = head.split("+")[-1] + (" " + rest if rest else "")
     for prefix, fs in KERNEL_SOURCES:
         if plan and plan.startswith(prefix):
             files = fs
