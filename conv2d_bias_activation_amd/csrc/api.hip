@@ -383,12 +383,20 @@ bool hgemm_cfast(const ConvArgs &a) {
 // Variant: the specialised-wave kernel (1) where its tiles fit one round of workgroups
 // over `cus` CUs (a deep K on few pixels, e.g. ResNet stage 4); the 10 x 20-pixel tiles
 // (4) where they give at least two workgroups per CU (e.g. ResNet stage 2, 80 x 80 x 128
-// at batch 4); else the 10 x 10-pixel tiles (0). From MI355X timings (256 CUs) of the
-// ResNet stage 2, 3 and 4 layers.
+// at batch 4); else the 10 x 10-pixel tiles (0). Stride 2: the three-stage ring (12)
+// where its tiles fit one round, else the 10 x 10 x 64 tiles (6). From MI355X timings
+// (256 CUs) of the ResNet stage 2, 3 and 4 layers.
 HgemmPlan plan_hgemm(const ConvArgs &a, int cus) {
     HgemmPlan p{};
     p.cfast = hgemm_cfast(a);
     HgemmInfo in{};
+    if (a.stride == 2) {
+        if (hgemm_cfg_ok(a, 12) && hgemm_cfg_info(12, a, &in) && in.tiles <= cus)
+            p.cfg = 12;
+        else
+            p.cfg = hgemm_cfg_ok(a, 6) ? 6 : -1;
+        return p;
+    }
     if (hgemm_cfg_ok(a, 1) && hgemm_cfg_info(1, a, &in) && in.tiles <= cus)
         p.cfg = 1;
     else if (hgemm_cfg_ok(a, 4) && hgemm_cfg_info(4, a, &in) && in.tiles >= 2ll * cus)
@@ -431,11 +439,11 @@ Plan make_plan_default(const ConvArgs &a, int layout, int dtype, size_t ws) {
         return p;
     }
     // wide 3x3 layers with at least 256 input channels, or 128 where the 10 x 20-pixel
-    // tiles fill two workgroups per CU (narrower or smaller ones are faster on the
-    // tiled GEMM below)
+    // tiles fill two workgroups per CU or the stride is 2 (narrower or smaller ones are
+    // faster on the tiled GEMM below)
     if (hgemm_fits(a, layout, dtype) && a.Cin >= 128) {
         p.hg = plan_hgemm(a, 256);
-        if (p.hg.cfg >= 0 && (a.Cin >= 256 || p.hg.cfg == 4)) {
+        if (p.hg.cfg >= 0 && (a.Cin >= 256 || p.hg.cfg == 4 || a.stride == 2)) {
             p.family = FAM_HGEMM;
             return p;
         }

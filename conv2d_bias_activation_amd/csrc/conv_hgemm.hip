@@ -764,7 +764,10 @@ typedef HgCfg<8, 16, 4, 1, 2, 2, 32, 2, 2> HgV8;   // 128 px x 64 ch
 typedef HgCfg<17, 15, 8, 1, 1, 2, 32, 2> HgV9;   // eight waves, one pixel block each
 typedef HgCfg<17, 15, 4, 1, 1, 2, 32, 2> HgV10;  // four waves, two pixel blocks each
 typedef HgCfg<17, 15, 8, 1, 1, 3, 32, 2> HgV11;  // the same in a three-stage ring
-constexpr int kHgVariants = 12;
+// stride 2, 100 px x 32 ch in a three-stage ring (copies issued two chunks ahead of
+// their use; one workgroup per CU): leads on the first stage-4 conv (40x40x256 -> 512)
+typedef HgCfg<10, 10, 4, 1, 1, 3, 32, 2, 2> HgV12;
+constexpr int kHgVariants = 13;
 
 template <typename C> long long hg_tiles(const ConvArgs &a) {
     return (long long)a.N * ((a.OW + C::TW - 1) / C::TW) * ((a.OH + C::TH - 1) / C::TH) *
@@ -821,6 +824,7 @@ template <typename T> hipError_t launch_hg_d(const ConvArgs &a, const HgemmPlan 
     case 9: return launch_hg_c<T, HgV9>(a, p.cfast, nchw, st);
     case 10: return launch_hg_c<T, HgV10>(a, p.cfast, nchw, st);
     case 11: return launch_hg_c<T, HgV11>(a, p.cfast, nchw, st);
+    case 12: return launch_hg_c<T, HgV12>(a, p.cfast, nchw, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -861,6 +865,7 @@ bool hgemm_cfg_info(int cfg, const ConvArgs &a, HgemmInfo *o) {
     case 9: return fill(HgV9{});
     case 10: return fill(HgV10{});
     case 11: return fill(HgV11{});
+    case 12: return fill(HgV12{});
     default: return false;
     }
 }

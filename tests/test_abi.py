@@ -83,7 +83,9 @@ def test_plan_names_a_kernel_for_every_workload_shape():
              ((4, 40, 40, 256, 256, 3, 3, 1, 1, 1, 0, bf16), "hgemm3x3_nhwc"),
              ((4, 320, 320, 32, 64, 3, 3, 1, 1, 1, 0, bf16), "halo3x3_nhwc"),
              ((4, 160, 160, 64, 64, 3, 3, 1, 1, 1, 0, bf16), "halo3x3ws_nhwc"),
-             ((4, 160, 160, 64, 128, 3, 3, 2, 1, 1, 0, bf16), "igemm_nhwc_pipe")]
+             ((4, 160, 160, 64, 128, 3, 3, 2, 1, 1, 0, bf16), "igemm_nhwc_pipe"),
+             ((4, 80, 80, 128, 256, 3, 3, 2, 1, 1, 0, bf16), "hgemm3x3_nhwc bf16 v6"),
+             ((4, 40, 40, 256, 512, 3, 3, 2, 1, 1, 0, bf16), "hgemm3x3_nhwc bf16 v12")]
     for s, family in cases:
         name = c2d.plan(*s)
         assert name.startswith(family), (s, name)
@@ -104,7 +106,7 @@ def test_conv_pool_plan_and_argument_checks():
     # channel-first 16-bit layers leave the workspace to the conv output: the general kernel
     assert c2d.plan_maxpool(1, 17, 23, 40, 72, 3, 3, 2, 1, 1, 1, bf16).startswith("igemm_nchw")
     # split-K is turned off for the same reason
-    assert "splitk=1" in c2d.plan_maxpool(1, 10, 10, 512, 512, 3, 3, 2, 1, 1, 0, bf16)
+    assert "splitk=1" in c2d.plan_maxpool(1, 10, 10, 520, 512, 3, 3, 2, 1, 1, 0, bf16)
     # an unpooled conv output over the 64 MiB workspace
     with pytest.raises(c2d.Conv2dError) as e:
         c2d.plan_maxpool(4, 640, 640, 64, 64, 3, 3, 1, 1, 1, 0, bf16)
@@ -385,8 +387,9 @@ def test_workspace_registration_and_sizes():
     assert lib.conv2d_set_workspace(None, 4096) == c2d.EINVAL                 # null with a size
     assert lib.conv2d_set_workspace(None, 0) == c2d.OK
     c2d.tune_clear()
-    # a deep-K strided layer with few tiles: split-K in three, 3 * M * Cout fp32 partial sums
-    deep = (4, 20, 20, 512, 512, 3, 3, 2, 1, 1, nhwc, bf16)
+    # a deep-K strided layer with few tiles whose Cin (520) the halo-tile GEMM does not
+    # take: split-K in three, 3 * M * Cout fp32 partial sums
+    deep = (4, 20, 20, 520, 512, 3, 3, 2, 1, 1, nhwc, bf16)
     assert "splitk=3" in c2d.plan(*deep)
     assert c2d.workspace_size(*deep) == 3 * 400 * 512 * 4
     assert "splitk=1" in c2d.plan(*deep, workspace_bytes=0)

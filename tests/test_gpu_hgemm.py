@@ -24,8 +24,8 @@ c2d = pytest.importorskip("conv2d_bias_activation_amd")
 DEV = torch.device("cuda")
 
 FAM_HGEMM = 7
-CK = [32, 64, 64, 32, 32, 32, 32, 32, 32, 32, 32, 32]  # input channels per K chunk of each variant
-STRIDE = [1, 1, 1, 1, 1, 1, 2, 2, 2, 1, 1, 1]                   # the stride each variant computes
+CK = [32, 64, 64, 32, 32, 32, 32, 32, 32, 32, 32, 32, 32]  # input channels per K chunk of each variant
+STRIDE = [1, 1, 1, 1, 1, 1, 2, 2, 2, 1, 1, 1, 2]  # the stride each variant computes
 NVARIANTS = len(CK)
 
 

@@ -25,7 +25,7 @@ DEV = torch.device("cuda")
 
 FAM_NCHW = 3
 HG_TILE = 100                                  # tuned-plan tile of halo-tile GEMM variant v: HG_TILE + v
-STRIDE = [1, 1, 1, 1, 1, 1, 2, 2, 2, 1, 1, 1]        # the stride each variant computes
+STRIDE = [1, 1, 1, 1, 1, 1, 2, 2, 2, 1, 1, 1, 2]  # the stride each variant computes
 WAVE_SPECIALISED = (1, 2)                      # variants without channel-first outputs
 
 
