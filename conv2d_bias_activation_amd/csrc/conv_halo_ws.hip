@@ -23,7 +23,11 @@
 //
 // The two groups meet at one workgroup barrier per tile, so the matrix cores work on
 // tile s while the hand-off of s-1, the epilogue of s-2 and the loads of tiles s+1, s+2
-// proceed. The workgroups are persistent (one per CU) and walk tiles t = s*G + r.
+// proceed. The workgroups are persistent (one per CU) and walk tiles t = s*G + r. The
+// last tile of a workgroup is not handed off: its compute waves run its epilogue
+// straight from their registers (its residual loaded during the second half of its
+// products) while the loader waves finish the one before, so the launch ends one
+// epilogue after its last products instead of two hand-offs and two epilogues.
 #include "igemm_common.hpp"
 #include "kernels.hpp"
 
@@ -127,7 +131,7 @@ __global__ __launch_bounds__(512, 1) void halo3x3_ws_kernel(ConvArgs a, int tile
         // this lane's weight row (channel 32*wn + rl), piece 2*ks + hi for k step ks
         const char *wrow = lds + WOFF + (32 * wn + rl) * RPC * 16 + hi * 16;
         f32x16 acc[2][2];  // two tiles' sums: one accumulating, the previous one handed off
-        auto compute = [&](auto cur, auto first, int s) {
+        auto compute = [&](auto cur, auto first, int s, auto hook) {
             constexpr int C = decltype(cur)::value;
             constexpr bool FIRST = decltype(first)::value;  // tile 0: the weights come from LDS
             const char *buf = lds + (s % 3) * HBUF;
@@ -156,8 +160,10 @@ __global__ __launch_bounds__(512, 1) void halo3x3_ws_kernel(ConvArgs a, int tile
 #pragma unroll
                 for (int i = 0; i < 2; ++i) acc[C][i] = Mfma32<T>::run(bw[ks], f[ks % (PF + 1)][i], acc[C][i]);
                 __builtin_amdgcn_sched_barrier(0);
+                hook(ks);
             }
         };
+        auto no_hook = [](int) {};
         // hand-off of tile s: lane (rl, hi) holds channels 32*wn + 8*g + 4*hi + 0..3 of pixel rl
         auto handoff = [&](auto prev, int s) {
             constexpr int C = decltype(prev)::value;
@@ -171,23 +177,128 @@ __global__ __launch_bounds__(512, 1) void halo3x3_ws_kernel(ConvArgs a, int tile
                         f32x4{acc[C][i][4 * g], acc[C][i][4 * g + 1], acc[C][i][4 * g + 2], acc[C][i][4 * g + 3]};
             }
         };
-        // Step s: the sums of tile s-1 go to the hand-off tile while the products of tile s
-        // run (the LDS writes and the matrix cores overlap), then the barrier.
+        // The last tile's epilogue runs here, from the registers: its residual (this lane's
+        // two 8-channel runs of each of its two rows) is loaded during the second half of
+        // its products, when the weight fragments of the first half are no longer needed.
+        const bool has_res = a.res != nullptr;
+        const __amdgpu_buffer_rsrc_t rres = make_rsrc(a.res, has_res ? out_bytes : 0u);
+        const __amdgpu_buffer_rsrc_t ry = make_rsrc(a.y, out_bytes);
+        // byte offset of the run of row i (0, 1), channels 32*wn + 16*pp + 8*hi .. of the last tile
+        auto last_off = [&](int i, int pp) -> uint32_t {
+            const Geo gl = geo(nsteps - 1);
+            const int oy = gl.oy0 + 2 * wm + i, ox = gl.ox0 + rl, co = 32 * wn + 16 * pp + 8 * hi;
+            return (gl.live && oy < H && ox < W && co < Cout)
+                       ? (uint32_t)(((gl.n * H + oy) * W + ox) * Cout + co) * (uint32_t)sizeof(T)
+                       : kOOB;
+        };
+        u32x4 lres[2][2];
+        auto res_hook = [&](int ks) {
+            if (ks == KS / 2) {
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int pp = 0; pp < 2; ++pp)
+                        lres[i][pp] =
+                            __builtin_amdgcn_raw_buffer_load_b128(rres, (int)(has_res ? last_off(i, pp) : kOOB), 0, 0);
+            }
+        };
+        auto swap_halves = [](u32x2 &lo, u32x2 &hi2) {
+#pragma unroll
+            for (int d = 0; d < 2; ++d) {
+                const auto r2 = __builtin_amdgcn_permlane32_swap(lo[d], hi2[d], false, false);
+                lo[d] = r2[0];
+                hi2[d] = r2[1];
+            }
+        };
+        // lane (rl, hi) holds channels 32*wn + 8*q + 4*hi + 0..3 (q < 4) of pixel rl of each
+        // row; one lane-half swap per pair of groups (2*pp, 2*pp + 1) leaves 8 consecutive
+        // channels 32*wn + 16*pp + 8*hi .. per lane, stored as one 16-byte run
+        auto last_epilogue = [&](auto cur) {
+            constexpr int C = decltype(cur)::value;
+            const __amdgpu_buffer_rsrc_t rbias = make_rsrc(a.bias, a.bias ? (uint32_t)Cout * 4u : 0u);
+            const __amdgpu_buffer_rsrc_t ralpha = make_rsrc(a.alpha, a.alpha ? (uint32_t)Cout * 4u : 0u);
+            float bq[16], aq[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int co = 32 * wn + 8 * q + 4 * hi;
+                const uint32_t bo = co < Cout ? (uint32_t)co * 4u : kOOB;
+                const f32x4 bv4 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rbias, (int)bo, 0, 0));
+                const f32x4 av4 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ralpha, (int)bo, 0, 0));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    bq[4 * q + e] = bv4[e];
+                    aq[4 * q + e] = av4[e];
+                }
+            }
+            const int mode = has_res ? (a.res_before_act ? 1 : 2) : 0;
+            auto finish = [&](auto act_tag, auto res_tag) {
+                constexpr int ACT = decltype(act_tag)::value;
+                constexpr int RES = decltype(res_tag)::value;
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int pp = 0; pp < 2; ++pp) {
+                        u32x2 q2[2];
+                        u32x2 rq[2] = {u32x2{lres[i][pp][0], lres[i][pp][1]}, u32x2{lres[i][pp][2], lres[i][pp][3]}};
+                        if constexpr (RES != 0) swap_halves(rq[0], rq[1]);
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) {
+                            const int q = 2 * pp + h;
+                            T rt[4], o4[4];
+                            __builtin_memcpy(rt, &rq[h], 8);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                float v = acc[C][i][4 * q + e] + bq[4 * q + e];
+                                if constexpr (RES == 1) v += to_f32(rt[e]);
+                                if constexpr (ACT == CONV2D_ACT_RELU) v = v > 0.0f ? v : 0.0f;
+                                if constexpr (ACT == CONV2D_ACT_SILU) v = v * __builtin_amdgcn_rcpf(1.0f + __expf(-v));
+                                if constexpr (ACT == CONV2D_ACT_PRELU) v = v >= 0.0f ? v : aq[4 * q + e] * v;
+                                if constexpr (RES == 2) v += to_f32(rt[e]);
+                                o4[e] = round_fp32<T>(v);
+                            }
+                            __builtin_memcpy(&q2[h], o4, 8);
+                        }
+                        swap_halves(q2[0], q2[1]);
+                        __builtin_amdgcn_raw_buffer_store_b128(u32x4{q2[0][0], q2[0][1], q2[1][0], q2[1][1]}, ry,
+                                                               (int)last_off(i, pp), 0, 0);
+                    }
+            };
+            auto with_res = [&](auto act_tag) {
+                switch (mode) {
+                case 1: finish(act_tag, std::integral_constant<int, 1>{}); break;
+                case 2: finish(act_tag, std::integral_constant<int, 2>{}); break;
+                default: finish(act_tag, std::integral_constant<int, 0>{}); break;
+                }
+            };
+            switch (a.act) {
+            case CONV2D_ACT_RELU: with_res(std::integral_constant<int, CONV2D_ACT_RELU>{}); break;
+            case CONV2D_ACT_SILU: with_res(std::integral_constant<int, CONV2D_ACT_SILU>{}); break;
+            case CONV2D_ACT_PRELU: with_res(std::integral_constant<int, CONV2D_ACT_PRELU>{}); break;
+            default: with_res(std::integral_constant<int, CONV2D_ACT_NONE>{}); break;
+            }
+        };
+        // Step s (1 <= s < nsteps): the sums of tile s-1 go to the hand-off tile while the
+        // products of tile s run (the LDS writes and the matrix cores overlap), then the
+        // barrier. The last tile's sums stay in the registers for its epilogue below.
         auto step = [&](auto cur, int s) {
             constexpr int C = decltype(cur)::value;
-            if (s >= 1 && s <= nsteps) handoff(std::integral_constant<int, 1 - C>{}, s - 1);
-            if (s < nsteps) compute(cur, std::false_type{}, s);
-            ws_barrier();
+            if (s >= 1 && s < nsteps) handoff(std::integral_constant<int, 1 - C>{}, s - 1);
+            if (s < nsteps) compute(cur, std::false_type{}, s, no_hook);
+            if (s < nsteps) ws_barrier();
         };
         // step 0: tile 0 (every workgroup has one), taking the weights into registers
-        compute(std::integral_constant<int, 0>{}, std::true_type{}, 0);
+        compute(std::integral_constant<int, 0>{}, std::true_type{}, 0, no_hook);
         ws_barrier();
         for (int s = 1; s <= nsteps; s += 2) {
             step(std::integral_constant<int, 1>{}, s);
             if (s + 1 > nsteps) break;
             step(std::integral_constant<int, 0>{}, s + 1);
         }
-        ws_barrier();  // the epilogue of the last tile
+        res_hook(KS / 2);
+        if ((nsteps - 1) & 1)
+            last_epilogue(std::integral_constant<int, 1>{});
+        else
+            last_epilogue(std::integral_constant<int, 0>{});
         return;
     }
 
@@ -386,20 +497,29 @@ __global__ __launch_bounds__(512, 1) void halo3x3_ws_kernel(ConvArgs a, int tile
     issue_halo(3);
     issue_res(std::integral_constant<int, 2>{}, 2);
     ws_wait_vmcnt<NLD + NRES>();  // the halo of tile 2
-    ws_barrier();
+    if (nsteps > 1) ws_barrier();
+    // The loaders run the epilogues of tiles 0 .. nsteps-2 (the compute waves that of the
+    // last tile), so step s issues the halo of tile s+2 and the residual of tile s+1 only
+    // while those are still to come (s + 3 <= nsteps); after that its wait leaves only its
+    // stores in flight (the halo of tile s+1, where it is a tile, came before them). The
+    // last step, nsteps, has no barrier: the compute waves have reached their last one.
     auto step = [&](auto slot, int s) {
         constexpr int I = decltype(slot)::value;  // s % 3
         epilogue(std::integral_constant<int, (I + 1) % 3>{}, s - 2);
-        issue_halo(s + 2);
-        issue_res(std::integral_constant<int, (I + 1) % 3>{}, s + 1);
-        ws_wait_vmcnt<STEP_OPS>();
-        ws_barrier();
+        if (s + 3 <= nsteps) {
+            issue_halo(s + 2);
+            issue_res(std::integral_constant<int, (I + 1) % 3>{}, s + 1);
+            ws_wait_vmcnt<STEP_OPS>();
+        } else {
+            ws_wait_vmcnt<NRES>();
+        }
+        if (s < nsteps) ws_barrier();
     };
-    for (int s = 2; s <= nsteps + 1; s += 3) {
+    for (int s = 2; s <= nsteps; s += 3) {
         step(std::integral_constant<int, 2>{}, s);
-        if (s + 1 > nsteps + 1) break;
+        if (s + 1 > nsteps) break;
         step(std::integral_constant<int, 0>{}, s + 1);
-        if (s + 2 > nsteps + 1) break;
+        if (s + 2 > nsteps) break;
         step(std::integral_constant<int, 1>{}, s + 2);
     }
     ws_wait_vmcnt<0>();  // no direct-to-LDS load outlives the workgroup
