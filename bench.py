@@ -96,7 +96,7 @@ def parse():
 class Net:
     """The backbone's layers with preallocated device buffers and prebuilt C-ABI arguments."""
 
-    def __init__(self, work, dev, fuse_pool=True, weights_ohwi=True, workspace=True):
+    def __init__(self, work, dev, fuse_pool=True, weights_ohwi=True, workspace=True, stem_pair=True):
         import torch
 
         import conv2d_bias_activation_amd as c2d
@@ -138,6 +138,15 @@ class Net:
                 nxt = work.layers[i + 1] if i + 1 < len(work.layers) else None
                 pooled = (fuse_pool and res is None and nxt is not None and getattr(nxt, "kind", "") == "max"
                           and nxt.src == spec.out and readers.get(spec.out) == 1)
+                if (stem_pair and not nchw and dt != c2d.DTYPE_F32 and res is None and c == 3 and spec.k == 3 and
+                        spec.stride == 2 and spec.cout == 32 and nxt is not None and hasattr(nxt, "cin") and
+                        nxt.src == spec.out and readers.get(spec.out) == 1 and not nxt.res and nxt.k == 3 and
+                        nxt.stride == 1 and nxt.cout <= 32):
+                    # the stem conv and the stride-1 conv after it as one stack pair: the first
+                    # output is marked transient and never stored
+                    self._add_pair(spec, nxt, src, out, wdev, bdev, adev, act, n, h, w, oh, ow, lay, dt, esz, dev)
+                    skip.add(i + 1)
+                    continue
                 if weights_ohwi and nchw and dt != c2d.DTYPE_F32 and c % 8 == 0 and not pooled:
                     # weight residency: converted to channel-last once here, so a call copies
                     # only its input
@@ -204,16 +213,57 @@ class Net:
         # the stack's own need is below it for these workloads)
         self.ws = None
         if workspace:
-            need = c2d.stack_workspace_size([L["op"] for L in self.layers], layout=["nhwc", "nchw"][lay], dtype=dt)
+            need = c2d.stack_workspace_size(self.ops(), layout=["nhwc", "nchw"][lay], dtype=dt)
             self.ws = torch.empty(max(need, c2d.DEFAULT_WORKSPACE_BYTES), dtype=torch.uint8, device=dev)
         # kernel variants of each layer run on its own with this workspace
         wsb = self.ws.numel() if self.ws is not None else 0
         for L in self.layers:
             o = L["op"]
+            if L.get("pair"):
+                continue  # planned as a stack pair above
             if o.kind in (c2d.OP_CONV, c2d.OP_CONV_MAXPOOL):
                 fn = c2d.plan if o.kind == c2d.OP_CONV else c2d.plan_maxpool
                 L["plan"] = fn(o.N, o.H, o.W, o.Cin, o.Cout, o.kh, o.kw, o.stride, o.pad, o.act, lay, dt,
                                workspace_bytes=wsb)
+
+    def _add_pair(self, s1, s2, src, mid, w1, b1, a1, act1, n, h, w, oh, ow, lay, dt, esz, dev):
+        """One layer entry for a stem conv and the stride-1 conv of its output, run as a
+        two-op stack with the first output marked transient (`mid` is never written)."""
+        import torch
+
+        c2d = self.c2d
+        w2, b2 = s2.w.to(dev), s2.bias.to(dev)
+        a2 = s2.alpha.to(dev) if s2.alpha is not None else None
+        act2 = {"none": 0, "relu": 1, "silu": 2, "prelu": 3}[s2.act]
+        out = torch.empty((n, oh, ow, s2.cout), dtype=src.dtype, device=dev)
+        ptr = lambda t: t.data_ptr() if t is not None else None
+        lib = self.lib
+
+        def mk(x, wa, ba, aa, wb, bb, ab, y):
+            return [c2d.Op(c2d.OP_CONV, x, wa, ba, aa, None, mid.data_ptr(), n, h, w, 3, 32, 3, 3, 2, 1,
+                           act1 | c2d.Y_TRANSIENT),
+                    c2d.Op(c2d.OP_CONV, mid.data_ptr(), wb, bb, ab, None, y, n, oh, ow, 32, s2.cout, 3, 3, 1, 1,
+                           act2)]
+
+        def fn(x, wa, ba, aa, wb, bb, ab, y, stream):
+            ops = mk(*[v.value if isinstance(v, ctypes.c_void_p) else v for v in (x, wa, ba, aa, wb, bb, ab, y)])
+            arr = (c2d.Op * 2)(*ops)
+            return lib.conv2d_stack_run(arr, 2, lay, dt, stream)
+
+        args = [ctypes.c_void_p(ptr(t)) if t is not None else None for t in (src, w1, b1, a1, w2, b2, a2, out)]
+        ops = mk(*[ptr(t) for t in (src, w1, b1, a1, w2, b2, a2, out)])
+        flops = 2 * n * oh * ow * 32 * 3 * 9 + 2 * n * oh * ow * s2.cout * 32 * 9
+        nbytes = esz * (src.numel() + w1.numel() + w2.numel() + out.numel()) + 4 * (32 + s2.cout) * (
+            2 if a2 is not None else 1)
+        plan = c2d.stack_plan(ops, 1, layout=["nhwc", "nchw"][lay], dtype=dt)
+        self.layers.append(dict(name=s1.name + "+" + s2.name, fn=fn, args=args, flops=flops, bytes=nbytes, plan=plan,
+                                keep=(w1, b1, a1, w2, b2, a2, mid), op=ops[1], pre_ops=[ops[0]], pair=True,
+                                tens={0: src, 1: w1, 2: b1, 3: a1, 4: w2, 5: b2, 6: a2, 7: out}, outs=(7,)))
+        self.t[s2.out] = out
+
+    def ops(self):
+        """The stack's ops in order (a stem pair contributes its two)."""
+        return [o for L in self.layers for o in L.get("pre_ops", []) + [L["op"]]]
 
     def use_workspace(self):
         self.c2d.set_workspace(self.ws)
@@ -242,7 +292,7 @@ def time_steps(torch, net, steps, warmup, mode):
         # the library's own stack graph: validated once, captured once, replayed per step
         net.step(stream)
         torch.cuda.synchronize()
-        graph = net.c2d.StackGraph([L["op"] for L in net.layers], layout=["nhwc", "nchw"][net.layout],
+        graph = net.c2d.StackGraph(net.ops(), layout=["nhwc", "nchw"][net.layout],
                                    dtype=net.dtype, workspace=net.ws if net.ws is not None else False)
         run = lambda: graph.launch(stream)
     elif mode == "graph":
@@ -343,7 +393,7 @@ def time_steps_cold(torch, nets, steps):
     graphs = []
     for net in nets:
         net.step(stream)
-        graphs.append(net.c2d.StackGraph([L["op"] for L in net.layers], layout=["nhwc", "nchw"][net.layout],
+        graphs.append(net.c2d.StackGraph(net.ops(), layout=["nhwc", "nchw"][net.layout],
                                          dtype=net.dtype, workspace=net.ws if net.ws is not None else False))
     for g in graphs:
         g.launch(stream)
@@ -368,7 +418,7 @@ KERNEL_SOURCES = [
     ("hgemmws3x3", ["conv_hgemm.hip", "igemm_common.hpp", "common.hpp"]),
     ("halo3x3ws", ["conv_halo_ws.hip", "igemm_common.hpp", "common.hpp"]),
     ("halo3x3", ["conv_halo.hip", "igemm_common.hpp", "common.hpp"]),
-    ("stem3x3", ["conv_stem.hip", "conv_stem_f32.hip", "igemm_common.hpp", "common.hpp"]),
+    ("stem3x3", ["conv_stem.hip", "conv_stem_f32.hip", "igemm_common.hpp", "common.hpp"]),  # also the stem pair
     ("igemm_", ["conv_igemm.hip", "igemm_common.hpp", "common.hpp"]),
     ("maxpool", ["pool.hip", "common.hpp"]),
     ("avgpool", ["pool.hip", "common.hpp"]),
@@ -382,6 +432,7 @@ KERNEL_SYMBOLS = [
     ("hgemmws3x3", "3c2d17hgemmws3x3_kernel"),
     ("halo3x3ws", "3c2d17halo3x3_ws_kernel"),
     ("halo3x3", "3c2d14halo3x3_kernel"),
+    ("stem3x3+halo3x3_pair", "stem_pair_kernel"),
     ("stem3x3", "stem3_"),  # stem3_kernel, stem3_pool_kernel
     ("igemm_", "3c2d12igemm_kernel"),
     ("maxpool", "maxpool_"),

@@ -27,7 +27,7 @@ __all__ = ["conv2d_fused", "conv2d_fused_maxpool3x3s2", "maxpool3x3s2", "avgpool
            "check_args", "plan", "plan_maxpool", "Op", "conv_op", "pool_op", "copy_op", "stack_check",
            "stack_plan", "stack_run", "StackGraph", "conv_transpose4x4s2", "plan_deconv",
            "upsample_nearest2x", "concat_channels", "upsample2x_concat", "deconv_op", "upsample_op",
-           "concat_op", "tune", "tune_save", "tune_load", "tune_clear", "deconv_pack", "conv_transpose4x4s2_prepacked", "weights_to_ohwi", "WEIGHTS_OHWI",
+           "concat_op", "tune", "tune_save", "tune_load", "tune_clear", "deconv_pack", "conv_transpose4x4s2_prepacked", "weights_to_ohwi", "WEIGHTS_OHWI", "Y_TRANSIENT",
            "last_error", "library_path", "Conv2dError", "ACT_NONE", "ACT_RELU", "ACT_SILU",
            "workspace_size", "stack_workspace_size", "set_workspace", "DEFAULT_WORKSPACE_BYTES",
            "ACT_PRELU", "RES_BEFORE_ACT", "LAYOUT_NHWC", "LAYOUT_NCHW", "DTYPE_F32",
@@ -39,6 +39,7 @@ DTYPE_F32, DTYPE_BF16, DTYPE_F16 = 0, 1, 2
 ACT_NONE, ACT_RELU, ACT_SILU, ACT_PRELU = 0, 1, 2, 3
 RES_BEFORE_ACT = 0x100
 WEIGHTS_OHWI = 0x200
+Y_TRANSIENT = 0x400
 OK, EINVAL, EUNSUPPORTED, EHIP = 0, -1, -2, -3
 
 _ACTS = {"none": ACT_NONE, "relu": ACT_RELU, "silu": ACT_SILU, "prelu": ACT_PRELU}
@@ -412,13 +413,16 @@ def _tensor_ptr(t):
 
 
 def conv_op(x, w, y, bias=None, alpha=None, residual=None, *, stride=1, pad=0, act="none",
-            res_before_act=False, layout="nhwc", pool=False, weights_ohwi=False):
+            res_before_act=False, layout="nhwc", pool=False, weights_ohwi=False, transient=False):
     """An Op for conv2d_fused (or, with pool=True, conv2d_fused_maxpool3x3s2) on these
-    tensors. The tensors must stay alive while the stack (or its graph) is in use."""
+    tensors. transient=True marks y as an intermediate only the next op reads
+    (CONV2D_Y_TRANSIENT): the stack may then leave it unwritten. The tensors must stay
+    alive while the stack (or its graph) is in use."""
     N, H, W, Cin, Cout, kh, kw = _dims(x, w, layout, weights_ohwi)
     return Op(OP_CONV_MAXPOOL if pool else OP_CONV, _tensor_ptr(x), _tensor_ptr(w), _tensor_ptr(bias),
               _tensor_ptr(alpha), _tensor_ptr(residual), _tensor_ptr(y), N, H, W, Cin, Cout, kh, kw, stride, pad,
-              _act_code(act, res_before_act) | (WEIGHTS_OHWI if weights_ohwi else 0))
+              _act_code(act, res_before_act) | (WEIGHTS_OHWI if weights_ohwi else 0) |
+              (Y_TRANSIENT if transient else 0))
 
 
 def _nhwc_dims(x, layout):

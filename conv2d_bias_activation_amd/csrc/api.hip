@@ -907,6 +907,13 @@ struct OpPlan {
     bool pool_by_next;
     bool pool_pw;
     PoolPwArgs pp;
+    // a conv whose output is marked transient (CONV2D_Y_TRANSIENT), and the stack fusion of
+    // a stem conv with the stride-1 conv that reads its output: the first launches nothing
+    // (pair_by_next), the second runs both (stem_pair, pa = the first conv's arguments)
+    bool y_transient;
+    bool pair_by_next;
+    bool stem_pair;
+    ConvArgs pa;
 };
 
 // Bytes of workspace the launch of a planned op writes (0 for none).
@@ -940,8 +947,9 @@ int check_op(const conv2d_op &op, int layout, int dtype, size_t ws, OpPlan *o) {
     o->dtype = dtype;
     switch (op.kind) {
     case CONV2D_OP_CONV: {
+        o->y_transient = (op.act & CONV2D_Y_TRANSIENT) != 0;
         int rc = check_conv(op.x, op.w, op.bias, op.alpha, op.residual, op.y, op.N, op.H, op.W, op.Cin, op.Cout, op.kh,
-                            op.kw, op.stride, op.pad, op.act, layout, dtype, &o->a);
+                            op.kw, op.stride, op.pad, op.act & ~CONV2D_Y_TRANSIENT, layout, dtype, &o->a);
         if (rc) return rc;
         o->a.bias = op.bias;
         if ((op.act & 0xff) != CONV2D_ACT_PRELU) o->a.alpha = nullptr;
@@ -1086,6 +1094,25 @@ void link_pool_pw(std::vector<OpPlan> &plans) {
     }
 }
 
+// A stem conv (3 -> 32 channels, stride 2) whose output is marked transient, followed by
+// the stride-1 3x3 conv that reads it, runs as one kernel that never stores the first
+// output (bit-identical to the two launches when the second would run on the halo
+// kernel, its plan for such shapes).
+void link_stem_pair(std::vector<OpPlan> &plans) {
+    for (size_t i = 0; i + 1 < plans.size(); ++i) {
+        OpPlan &p = plans[i], &q = plans[i + 1];
+        if (p.kind != CONV2D_OP_CONV || q.kind != CONV2D_OP_CONV || !p.y_transient || p.pair_by_next || q.stem_pair)
+            continue;
+        if (p.layout != CONV2D_LAYOUT_NHWC || p.dtype != q.dtype || p.plan.family != FAM_STEM) continue;
+        if (q.plan.family != FAM_HALO || q.pool_pw || !stem_pair_fits(p.a, q.a, q.dtype)) continue;
+        const int eb = dtype_bytes(q.dtype);
+        if (overlap(q.a.y, (long long)q.a.M * q.a.Cout * eb, p.a.x, (long long)p.a.N * p.a.H * p.a.W * 3 * eb)) continue;
+        p.pair_by_next = true;
+        q.stem_pair = true;
+        q.pa = p.a;
+    }
+}
+
 int check_stack(const conv2d_op *ops, int n, int layout, int dtype, size_t ws, std::vector<OpPlan> *plans,
                 int *bad) {
     if (n < 0 || (n > 0 && !ops)) return set_error(CONV2D_EINVAL, "ops must hold n >= 0 entries");
@@ -1099,6 +1126,7 @@ int check_stack(const conv2d_op *ops, int n, int layout, int dtype, size_t ws, s
     }
     link_chains(*plans, ws);
     link_pool_pw(*plans);
+    link_stem_pair(*plans);
     return CONV2D_OK;
 }
 
@@ -1114,6 +1142,14 @@ int launch_op(const OpPlan &o, const Workspace &ws, hipStream_t st) {
     const bool nchw = o.layout == CONV2D_LAYOUT_NCHW;
     switch (o.kind) {
     case CONV2D_OP_CONV:
+        if (o.pair_by_next) return CONV2D_OK;  // computed by the next op's kernel
+        if (o.stem_pair) {
+            int cus = 0;
+            int rc = device_cus(&cus);
+            if (rc) return rc;
+            e = launch_stem_pair(o.pa, o.a, o.dtype, 3 * cus, st);
+            return e == hipSuccess ? CONV2D_OK : hip_fail(e, "stem conv pair launch");
+        }
         if (o.pool_pw) {
             e = launch_poolpw(o.pp, o.dtype, st);
             return e == hipSuccess ? CONV2D_OK : hip_fail(e, "avgpool2x2 + conv1x1 launch");
@@ -1196,6 +1232,15 @@ int describe_op(const OpPlan &o, char *buf, int cap) {
     char tmp[200];
     switch (o.kind) {
     case CONV2D_OP_CONV:
+        if (o.pair_by_next) {
+            snprintf(tmp, sizeof tmp, "stem3x3_mfma %s (in the next op's kernel, output not stored)",
+                     dtype_name(o.dtype));
+            break;
+        }
+        if (o.stem_pair) {
+            snprintf(tmp, sizeof tmp, "stem3x3+halo3x3_pair %s th8 co32 w4 (with the previous op)", dtype_name(o.dtype));
+            break;
+        }
         if (o.pool_pw) {
             snprintf(tmp, sizeof tmp, "avgpool2x2+conv1x1_nhwc %s %dx128 (with the previous op)",
                      dtype_name(o.dtype), o.a.Cin == 64 ? 64 : 32);
@@ -1415,7 +1460,7 @@ int tune_run(int N, int H, int W, int Cin, int Cout, int kh, int kw, int stride,
 
 extern "C" {
 
-int conv2d_abi_version(void) { return 9; }
+int conv2d_abi_version(void) { return 10; }
 
 const char *conv2d_last_error(void) { return g_err.c_str(); }
 

@@ -143,6 +143,14 @@ hipError_t launch_halo3x3_maxpool(const ConvArgs &a, void *y, int dtype, int gri
 // fp32 storage (dtype CONV2D_DTYPE_F32) goes to launch_stem3_f32.
 hipError_t launch_stem3(const ConvArgs &a, int dtype, hipStream_t st);
 
+// Two 3x3 convs, only the second one's output written: a1 = the stem conv (3 -> 32
+// channels, stride 2, pad 1, no residual, W % 8 == 0), a2 = a stride-1 pad-1 conv of a1's
+// output (a2.x == a1.y, Cin 32, Cout <= 32 with Cout % 8 == 0, no residual, y 16-byte
+// aligned); 16-bit storage, channel-last. Bit-identical to the stem kernel followed by
+// the halo kernel. grid_cap: persistent workgroups (three per CU).
+bool stem_pair_fits(const ConvArgs &a1, const ConvArgs &a2, int dtype);
+hipError_t launch_stem_pair(const ConvArgs &a1, const ConvArgs &a2, int dtype, int grid_cap, hipStream_t st);
+
 // The same for fp32 storage (32x32x2 fp32 products): Cout <= 64 with Cout % 4 == 0,
 // W % 4 == 0 and W <= 1700, same alignment and size limits.
 hipError_t launch_stem3_f32(const ConvArgs &a, hipStream_t st);

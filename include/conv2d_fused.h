@@ -90,6 +90,16 @@ extern "C" {
  * conv2d_fused_maxpool3x3s2 (CONV2D_EINVAL). */
 #define CONV2D_WEIGHTS_OHWI 0x200
 
+/* OR-ed into `act` of a stack's CONV2D_OP_CONV op (not accepted by the single calls): the
+ * op's output is only an intermediate read by the next op, so the stack need not store
+ * it. A 16-bit channel-last stem conv (Cin 3 -> Cout 32, 3x3, stride 2, pad 1, W % 8 == 0)
+ * so marked, followed by the 3x3 stride-1 pad-1 conv of its output (Cout <= 32, Cout % 8
+ * == 0, no residual; the second conv of inferencelayer's `encoder_maps` stem) then runs as
+ * one kernel that writes only the second output, bit-identical to the two launches; y of
+ * the marked op is left as it was. Any other marked op runs and stores its output as
+ * usual. */
+#define CONV2D_Y_TRANSIENT 0x400
+
 /* Status codes. */
 #define CONV2D_OK 0
 #define CONV2D_EINVAL (-1)      /* bad argument: null required pointer, size <= 0, stride
@@ -478,7 +488,7 @@ int conv2d_tune_clear(void);
  * valid until the thread's next call into the library. */
 const char *conv2d_last_error(void);
 
-/* ABI version of this header: 9 (conv2d_fused_noalloc; 8: caller-owned workspace: conv2d_set_workspace and the
+/* ABI version of this header: 10 (CONV2D_Y_TRANSIENT for stack ops; 9: conv2d_fused_noalloc; 8: caller-owned workspace: conv2d_set_workspace and the
  * size queries replace the library's own scratch; conv2d_avgpool2x2_conv1x1 and its op
  * kind are gone; 7 added CONV2D_WEIGHTS_OHWI and conv2d_weights_to_ohwi; 6
  * added the transposed conv's weight packing calls; 5
