@@ -440,14 +440,23 @@ KERNEL_SYMBOLS = [
 ]
 
 
+def kernel_family(plan):
+    """The plan name of the kernel that does a layer's products: the last of the kernels a
+    plan chains with "+" ("x_to_nhwc+<kernel>", "chained+<kernel>", "deconv4x4s2_pack+..."),
+    except the stem pair ("stem3x3+halo3x3_pair ..."), which is one kernel."""
+    head, _, rest = plan.partition(" ")
+    if not head.startswith("stem3x3+halo3x3_pair"):
+        head = head.split("+")[-1]
+    return head + (" " + rest if rest else "")
+
+
 def kernel_source_hash(plan=None):
     csrc = os.path.join(ROOT, "conv2d_bias_activation_amd", "csrc")
     files = sorted(f for f in os.listdir(csrc) if f.endswith((".hip", ".hpp")))
     if plan:
         # a channel-first plan runs the channel-last kernel after (or without) the layout
         # copy: "x_to_nhwc+<kernel> ...", "chained+<kernel> ..."
-        head, _, rest = plan.partition(" ")
-        plan = head.split("+")[-1] + (" " + rest if rest else "")
+        plan = kernel_family(plan)
     for prefix, fs in KERNEL_SOURCES:
         if plan and plan.startswith(prefix):
             files = fs
@@ -621,8 +630,7 @@ def write_traffic(src, copy_mib, plan):
         name = max(names, key=lambda k: d[k][0])  # the one launched most often in that run
         return name, d[name][1]
     # a channel-first plan's kernel is the channel-last one after the copy ("to_nhwc+...")
-    head, _, rest = plan.partition(" ")
-    family = head.split("+")[-1] + (" " + rest if rest else "")
+    family = kernel_family(plan)
     symbol = next((s for prefix, s in KERNEL_SYMBOLS if family.startswith(prefix)), "")
     _, cf = busiest(os.path.join(src, "copy_fetch"), "FETCH_SIZE")
     _, cw = busiest(os.path.join(src, "copy_write"), "WRITE_SIZE")
