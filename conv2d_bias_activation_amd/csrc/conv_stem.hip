@@ -419,13 +419,29 @@ __global__ __launch_bounds__(256) void stem3_pool_kernel(ConvArgs a, int PH, int
 // one rounding; pixels outside the first conv's map are the second conv's zero padding)
 // and write them to a halo buffer in the layout of the halo kernel; then the second
 // conv's products read the halo (weights in registers, the same k order and
-// accumulation as the halo kernel), while the next tile's image rows are loaded into
-// registers. Both convs round exactly as the two kernels do, so the output equals the
-// two launches bit for bit. Three workgroups per CU (measured on MI355X at 4 x 640 x 640:
-// 22.2 us against 23.8 with two, and 27.8 for the two launches).
+// accumulation as the halo kernel), while the next tile's image rows go straight from
+// memory into the staging buffer (direct-to-LDS loads, which hold no registers; the
+// first tile's go out before the weights are read, so the two latencies overlap). Both
+// convs round exactly as the two kernels do, so the output equals the two launches bit
+// for bit. Three workgroups per CU (measured on MI355X at 4 x 640 x 640: 22.2 us against
+// 23.8 with two, and 27.8 for the two launches, when the rows went through registers).
 struct StemPairGeo {
     int tiles_w, tiles_h, ntiles;
 };
+
+template <int N> __device__ __forceinline__ void pair_wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier after this wave's LDS accesses have completed; direct-to-LDS loads
+// are published by the explicit vmcnt waits before it.
+__device__ __forceinline__ void pair_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
 
 template <typename T>
 __global__ __launch_bounds__(256, 3) void stem_pair_kernel(ConvArgs a1, ConvArgs a2, StemPairGeo tg) {
@@ -438,7 +454,10 @@ __global__ __launch_bounds__(256, 3) void stem_pair_kernel(ConvArgs a1, ConvArgs
     constexpr int CPR = RSTR / 16;                    // 16-byte chunks per staged row
     constexpr int NSL = (RSW * CPR + 255) / 256;      // staging loads per thread
     constexpr int KSW = 18;                           // second conv: 9 taps x 2 chunks of 16 channels
-    constexpr int SBYTES = RSW * RSTR, HBYTES = NQ * PSTR;
+    // the staged window takes whole 4 KiB rounds of direct-to-LDS loads (the slots past
+    // its RSW rows hold zeros that nothing reads)
+    constexpr int SBYTES = NSL * 256 * 16, HBYTES = NQ * PSTR;
+    static_assert(SBYTES >= RSW * RSTR && RSTR == CPR * 16, "staged rows are contiguous 16-byte slots");
     static_assert(HBYTES >= KSW * 1024, "the weight staging fits the halo buffer");
     __shared__ __attribute__((aligned(16))) char srow[SBYTES];
     __shared__ __attribute__((aligned(1024))) char halo[HBYTES];
@@ -450,6 +469,44 @@ __global__ __launch_bounds__(256, 3) void stem_pair_kernel(ConvArgs a1, ConvArgs
     const int rl = lane & 31, hi = lane >> 5;
     const int H = a1.H, W = a1.W, OH = a1.OH, OW = a1.OW;  // image; the first conv's map
     const int C2 = a2.Cout;
+
+    // tiles t = k*G + r, the workgroups of one XCD taking a contiguous run of each round
+    const int G = gridDim.x;
+    const int r = (G % 8) == 0 ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
+    struct Geo {
+        int n, oy0, ox0;
+        bool live;
+    };
+    auto geo = [&](int k) -> Geo {
+        const int t = k * G + r;
+        const bool live = t < tg.ntiles;
+        const int tt = live ? t : 0;
+        const int tx = tt % tg.tiles_w, rr = tt / tg.tiles_w;
+        return Geo{rr / tg.tiles_h, (rr % tg.tiles_h) * TH, tx * TW, live};
+    };
+    // Image window of a tile: rows 2*oy0 - 3 + j (j < RSW), the row bytes from win0 on
+    // (16-byte aligned, at or before column 2*ox0 - 3), chunks outside the image zero.
+    // It goes straight into srow (direct-to-LDS loads: slot i = 16-byte chunk i % CPR of
+    // row i / CPR); every thread issues NSL loads, so each wave's count is the same.
+    const int row_bytes = W * 6;
+    const i32x4 rx = rsrc_words(a1.x, (uint32_t)((size_t)a1.N * H * row_bytes));
+    auto win0 = [](int ox0) {  // byte of column 2*ox0 - 3 rounded down to 16 (floor for negatives)
+        const int b = 6 * (2 * ox0 - 3);
+        return b >= 0 ? b & ~15 : -((-b + 15) & ~15);
+    };
+    auto stage = [&](const Geo &g) {
+#pragma unroll
+        for (int d = 0; d < NSL; ++d) {
+            const int i = threadIdx.x + 256 * d;
+            const int j = i / CPR, c = i - j * CPR;
+            const int iy = 2 * g.oy0 - 3 + j, b = win0(g.ox0) + 16 * c;
+            const bool ok = g.live && i < RSW * CPR && (unsigned)iy < (unsigned)H && b >= 0 && b < row_bytes;
+            dma_b128(rx, ok ? (uint32_t)((size_t)(g.n * H + iy) * row_bytes + b) : kOOB,
+                     lds_addr(srow + (256 * d + 64 * wave) * 16));
+        }
+    };
+    // the first tile's window goes out before the weights, so the two latencies overlap
+    stage(geo(0));
 
     // first conv's weights as A operands (the stem kernel's layout: step 0 values 0..7 of
     // patch row hi, step 1 values 0..7 of row 2 or value 8 of rows 0..2)
@@ -493,42 +550,6 @@ __global__ __launch_bounds__(256, 3) void stem_pair_kernel(ConvArgs a1, ConvArgs
 #pragma unroll
     for (int sw = 0; sw < KSW; ++sw) bw[sw] = *reinterpret_cast<const vec *>(halo + (sw * 64 + lane) * 16);
 
-    // tiles t = k*G + r, the workgroups of one XCD taking a contiguous run of each round
-    const int G = gridDim.x;
-    const int r = (G % 8) == 0 ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
-    struct Geo {
-        int n, oy0, ox0;
-        bool live;
-    };
-    auto geo = [&](int k) -> Geo {
-        const int t = k * G + r;
-        const bool live = t < tg.ntiles;
-        const int tt = live ? t : 0;
-        const int tx = tt % tg.tiles_w, rr = tt / tg.tiles_w;
-        return Geo{rr / tg.tiles_h, (rr % tg.tiles_h) * TH, tx * TW, live};
-    };
-    // image window of a tile: rows 2*oy0 - 3 + j (j < RSW), the row bytes from gstart on
-    // (16-byte aligned, at or before column 2*ox0 - 3), chunks outside the image zero
-    const int row_bytes = W * 6;
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(a1.x, (uint32_t)((size_t)a1.N * H * row_bytes));
-    auto win0 = [](int ox0) {  // byte of column 2*ox0 - 3 rounded down to 16 (floor for negatives)
-        const int b = 6 * (2 * ox0 - 3);
-        return b >= 0 ? b & ~15 : -((-b + 15) & ~15);
-    };
-    auto stage_load = [&](const Geo &g, int i) -> u32x4 {
-        const int j = i / CPR, c = i - j * CPR;
-        const int iy = 2 * g.oy0 - 3 + j, b = win0(g.ox0) + 16 * c;
-        const bool ok = g.live && i < RSW * CPR && (unsigned)iy < (unsigned)H && b >= 0 && b < row_bytes;
-        return __builtin_amdgcn_raw_buffer_load_b128(rx, ok ? (int)((size_t)(g.n * H + iy) * row_bytes + b) : (int)kOOB,
-                                                     0, 0);
-    };
-    auto commit = [&](const u32x4 (&v)[NSL]) {
-#pragma unroll
-        for (int d = 0; d < NSL; ++d) {
-            const int i = threadIdx.x + 256 * d;
-            if (i < RSW * CPR) *reinterpret_cast<u32x4 *>(srow + (i / CPR) * RSTR + (i % CPR) * 16) = v[d];
-        }
-    };
 
     const uint32_t out_bytes = (uint32_t)((size_t)a2.M * C2 * sizeof(T));
     const __amdgpu_buffer_rsrc_t ry = make_rsrc(a2.y, out_bytes);
@@ -586,9 +607,13 @@ __global__ __launch_bounds__(256, 3) void stem_pair_kernel(ConvArgs a1, ConvArgs
                     if constexpr (decltype(act_tag)::value == CONV2D_ACT_PRELU)
                         al = *reinterpret_cast<const f32x4 *>(&bal[1][8 * gq + 4 * hi]);
                     T o4[4];
+                    // rounded on every lane, then zeroed outside the map (a select, not a
+                    // branch per value around the rounding's fence)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        o4[e] = inmap ? round_fp32<T>(act1_of(act_tag, acc[4 * gq + e], al[e])) : from_f32<T>(0.0f);
+                    for (int e = 0; e < 4; ++e) {
+                        const T v = round_fp32<T>(act1_of(act_tag, acc[4 * gq + e], al[e]));
+                        o4[e] = inmap ? v : from_f32<T>(0.0f);
+                    }
                     __builtin_memcpy(&qv[h], o4, 8);
                 }
                 swap_halves(qv[0], qv[1]);
@@ -662,26 +687,27 @@ __global__ __launch_bounds__(256, 3) void stem_pair_kernel(ConvArgs a1, ConvArgs
         }
     };
 
+    // The second conv's epilogue issues FM * 2 stores per lane after the next window's
+    // loads; waiting until no more than those are outstanding leaves the window landed.
+    constexpr int NSTORE = FM * 2;
     auto run = [&](auto act1_tag, auto act2_tag) {
-        u32x4 v[NSL];
         Geo g = geo(0);
-#pragma unroll
-        for (int d = 0; d < NSL; ++d) v[d] = stage_load(g, threadIdx.x + 256 * d);
-        // the weight fragments are in registers (lgkmcnt(0) in the barrier) before the
-        // first tile's halo overwrites their staging
-        commit(v);
-        __syncthreads();
+        // the first window has landed (this wave's loads; the barrier: every wave's),
+        // and the weight fragments are in registers (lgkmcnt(0) in the barrier) before
+        // the first tile's halo overwrites their staging
+        pair_wait_vmcnt<0>();
+        pair_barrier();
         for (int k = 0; g.live; ++k) {
             first_conv(act1_tag, g);
-            __syncthreads();  // halo complete; every wave done with the staged window
+            pair_barrier();  // halo complete; every wave done with the staged window
             const Geo gn = geo(k + 1);
-#pragma unroll
-            for (int d = 0; d < NSL; ++d) v[d] = stage_load(gn, threadIdx.x + 256 * d);
+            stage(gn);
             second_conv(act2_tag, g);
-            commit(v);
-            __syncthreads();  // next window staged; every wave done reading the halo
+            pair_wait_vmcnt<NSTORE>();
+            pair_barrier();  // next window staged; every wave done reading the halo
             g = gn;
         }
+        pair_wait_vmcnt<0>();  // no direct-to-LDS load outlives the workgroup
     };
     auto with_act2 = [&](auto act1_tag) {
         switch (a2.act) {
