@@ -470,7 +470,10 @@ __global__ __launch_bounds__(256, 3) void stem_pair_kernel(ConvArgs a1, ConvArgs
     const int H = a1.H, W = a1.W, OH = a1.OH, OW = a1.OW;  // image; the first conv's map
     const int C2 = a2.Cout;
 
-    // tiles t = k*G + r, the workgroups of one XCD taking a contiguous run of each round
+    // tiles t = k*G + r, the workgroups of one XCD taking a contiguous run of each whole
+    // round; the tiles of a last, partial round go to workgroups by launch order instead
+    // (blockIdx % 8 round-robins the XCDs), so its few tiles spread over all XCDs and
+    // CUs rather than doubling up on the CUs of one
     const int G = gridDim.x;
     const int r = (G % 8) == 0 ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
     struct Geo {
@@ -478,7 +481,7 @@ __global__ __launch_bounds__(256, 3) void stem_pair_kernel(ConvArgs a1, ConvArgs
         bool live;
     };
     auto geo = [&](int k) -> Geo {
-        const int t = k * G + r;
+        const int t = k * G + ((k + 1) * G > tg.ntiles ? (int)blockIdx.x : r);
         const bool live = t < tg.ntiles;
         const int tt = live ? t : 0;
         const int tx = tt % tg.tiles_w, rr = tt / tg.tiles_w;
