@@ -429,9 +429,14 @@ struct StemPairGeo {
     int tiles_w, tiles_h, ntiles;
 };
 
+// Waits until at most N of this wave's vector-memory operations are outstanding. The
+// count is only meaningful if every store written before the wait is issued before it,
+// so the compiler may not move memory operations across it.
 template <int N> __device__ __forceinline__ void pair_wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
+    asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+    asm volatile("" ::: "memory");
 }
 
 // Workgroup barrier after this wave's LDS accesses have completed; direct-to-LDS loads
